@@ -1,0 +1,230 @@
+/*
+ * fp8moe.h -- C ABI of the MI355X (gfx950) FP8 MoE quantization and grouped-GEMM library.
+ *
+ * What the library computes
+ *   Dynamic FP8 quantization as one fused pass (absolute max -> scale -> apply ->
+ *   clip -> cast) in rowwise, colwise and MXFP8 (1x32 blocks, e8m0 scales)
+ *   forms, over the e4m3fn (max 448) and e4m3fnuz (max 240) codecs, feeding an
+ *   offset-routed grouped GEMM for the forward, dgrad and wgrad products of an
+ *   MoE expert layer.  Sources (cited by page and section):
+ *     [P1] AI Trends summary (aitrends.kr/articles/95981) of the PyTorch post
+ *          "FP8 Training on AMD GPUs with TorchTitan and TorchAO".
+ *     [P2] AI Trends summary (aitrends.kr/articles/16888) of the TorchAO MXFP8
+ *          MoE training post on Llama4 Scout.
+ *     [P3] aihirek.info, "Az AMD GPU-kon is gyorsult az FP8-as PyTorch-tréning".
+ *     [P4] aixai.ru blog post on FP8 training on AMD with TorchTitan.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer allocated by the caller; the
+ *     library allocates no device memory, keeps no per-call state and never
+ *     takes ownership of a buffer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on that stream; none synchronizes it.  Results are
+ *     visible once the caller synchronizes the stream.
+ *   - Layouts are row-major ("phys [a][b]": b contiguous).  bf16 inputs are
+ *     passed as their 16-bit patterns; FP8 data and e8m0 scales are bytes.
+ *   - Every argument check the host can do (null pointers, enums, negative
+ *     sizes, alignment, divisibility) runs BEFORE any HIP call and returns a
+ *     non-zero status; nothing is then enqueued.  FP8MOE_ERR_LAUNCH reports a
+ *     failed launch.  Device-resident data (the offsets) is not validated; it is
+ *     read with the clamping rule below, so malformed offsets cannot cause an
+ *     out-of-bounds access.  Device faults surface at the caller's synchronize.
+ *   - Group offsets `offs[n_groups]` (int32, device) are the inclusive
+ *     cumulative row counts of the groups (experts).  Group e covers rows
+ *     [hi(e-1), hi(e)), hi(e) = max(hi(e-1), clamp(offs[e], 0, rows)),
+ *     hi(-1) = 0: groups are disjoint, a decreasing entry gives an empty group,
+ *     and rows at or past hi(n_groups-1) belong to no group.  The host never
+ *     reads the offsets.  [P1 Details, MoE paragraph: tokens placed per expert
+ *     by offsets; P4 "MoE: почему DeepSeek-V3 ломал пайплайн".]
+ *   - Scales.  fp32 scales are multipliers: q ~= x * s with s = fmax / max(amax,
+ *     1e-12f), computed with an IEEE fp32 division; dequantized value = dec(q)/s.
+ *     e8m0 scales are dequantization factors 2^(code-127): dequantized value =
+ *     dec(q) * 2^(code-127).
+ *   - Rounding: y = fp32(x * s) (round to nearest even), clamp to
+ *     [-fmax, fmax], then round to the nearest FP8 value, ties to the even code.
+ *     e4m3fn keeps the sign of a zero result (0x80); e4m3fnuz has one unsigned
+ *     zero and never emits 0x80.  No subnormal is flushed.
+ *   - Calls on different streams may run concurrently from several host
+ *     threads; they share no mutable library state.
+ */
+#ifndef FP8MOE_H
+#define FP8MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FP8MOE_OK 0
+#define FP8MOE_ERR_NULL 1          /* a required pointer is NULL */
+#define FP8MOE_ERR_SHAPE 2         /* a size is negative or sizes are inconsistent */
+#define FP8MOE_ERR_ENUM 3          /* an enum argument is out of range */
+#define FP8MOE_ERR_ALIGN 4         /* a pointer, leading dimension or size violates its alignment */
+#define FP8MOE_ERR_UNSUPPORTED 5   /* a valid combination this library does not implement */
+#define FP8MOE_ERR_LAUNCH 6        /* the HIP runtime rejected a launch */
+#define FP8MOE_ERR_DEVICE 7        /* a HIP device query failed */
+
+/* FP8 codecs.  e4m3fn: OCP, bias 7, max 448, NaN 0x7F/0xFF, signed zero.
+ * e4m3fnuz: bias 8, max 240, no NaN/Inf among finite codes, unsigned zero.
+ * [P1 Details, e4m3fnuz property table; P1 glossary "FNUZ"; P3 "Az AMD
+ * FP8-formátumának támogatása"; P4 "Тихая порча градиентов: проблема формата FNUZ".] */
+#define FP8MOE_E4M3FN 0
+#define FP8MOE_E4M3FNUZ 1
+
+/* MX shared-exponent rule X for a 1x32 block with |x| max `amax` (e8m0 code X+127):
+ * FLOOR_OCP: X = floor(log2 amax) - 8 (OCP MX rule for e4m3; values above
+ *            448*2^X saturate in the clamp).   CEIL: the smallest X with
+ * amax*2^-X <= 448.  amax == 0 gives X = -127.  X is clamped to [-127, 127].
+ * [P2 Details, MXFP8 data/scale layout diagram: e4m3 data, one e8m0 scale per 1x32 block.] */
+#define FP8MOE_MX_FLOOR_OCP 0
+#define FP8MOE_MX_CEIL 1
+
+/* grouped GEMM modes */
+#define FP8MOE_GROUPED_M 0         /* 2D x 3D -> 2D: forward and dgrad */
+#define FP8MOE_GROUPED_K 1         /* 2D x 2D -> 3D: wgrad, contracting over tokens */
+
+/* operand formats */
+#define FP8MOE_OPD_E4M3FN 0
+#define FP8MOE_OPD_E4M3FNUZ 1
+#define FP8MOE_OPD_BF16 2
+
+/* scale kinds */
+#define FP8MOE_SCALE_F32 0         /* fp32 multipliers (divide in the epilogue) */
+#define FP8MOE_SCALE_E8M0 1        /* e8m0 per 32-block along the contraction (MXFP8) */
+#define FP8MOE_SCALE_NONE 2        /* unscaled bf16 operands */
+
+/* output dtypes */
+#define FP8MOE_OUT_BF16 0          /* round to nearest even */
+#define FP8MOE_OUT_F32 1
+
+/*
+ * quantize_rowwise -- one fp32 scale per row, over the last dimension.
+ *   [P1 Details: rowwise FP8 recipe and fused quantization kernels; P4 "Скейлы:
+ *   от тензора до микроблока" (rowwise granularity); P4 "Три уровня оптимизации
+ *   Triton-ядер" (one fused absmax/scale/clip/cast pass; expert weights quantized
+ *   by one kernel parallel over experts and output-dimension blocks).]
+ *   Expert weights W[E][N][K] are passed as rows = E*N, giving the per-expert
+ *   output-column scales [E][N] the grouped GEMM takes.
+ *   x      bf16 [rows][ld_x] (only the first `cols` of each row are read)
+ *   q      u8   [rows][cols]   FP8 codes (written)
+ *   scale  f32  [rows]         s = fmax/max(amax, 1e-12f) (written)
+ *   Requires: rows, cols >= 0; ld_x >= cols; cols % 8 == 0; ld_x % 8 == 0;
+ *   x and q 16-byte aligned, scale 4-byte aligned.
+ */
+int quantize_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                     int codec, void *q, float *scale, void *stream);
+
+/*
+ * quantize_colwise -- one fp32 scale per (group, column), reduced over the
+ * group's rows, with the FP8 output written transposed (contraction-contiguous)
+ * so the backward GEMMs read it directly, with no separate transpose copy.
+ *   [P1 Details: colwise scales kernel, output tile transposed through LDS
+ *   before the store, single-pass variant without the second HBM read; P4 "Три
+ *   уровня оптимизации Triton-ядер" (removal of the .t().contiguous().t() copy,
+ *   fused scale-and-cast for backward); P2 Details, wgrad layout along the
+ *   contracting dimension.]
+ *   Grouped 2D form (batch == 1, offs != NULL):
+ *     x     bf16 [rows][cols], offs int32 [n_groups]
+ *     q_t   u8   phys [cols][ld_q]   q_t[c][r] = code of x[r][c] (rows of no group untouched)
+ *     scale f32  [n_groups][cols]    empty group: fmax/1e-12f
+ *   Batched 3D form (offs == NULL, n_groups ignored):
+ *     x     bf16 [batch][rows][cols]
+ *     q_t   u8   phys [batch][cols][ld_q]
+ *     scale f32  [batch][cols]
+ *   Requires: batch >= 1 (== 1 with offs), n_groups >= 1 with offs, rows, cols >= 0,
+ *   ld_q >= rows, cols % 8 == 0, ld_q % 16 == 0, x and q_t 16-byte aligned.
+ *   The call enqueues up to three kernels (amax reset, partial amax, cast).
+ */
+int quantize_colwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
+                     const int32_t *offs, int32_t n_groups, int codec,
+                     void *q_t, int64_t ld_q, float *scale, void *stream);
+
+/*
+ * quantize_mx -- MXFP8: e4m3fn codes with one e8m0 scale per 1x32 block.
+ *   [P2 Details: _to_mxfp8_then_scaled_grouped_mm quantizes activations and
+ *   weights dynamically; MXFP8 data/scale layout diagram; wgrad quantized along
+ *   the contracting (token) dimension.  P4 "Скейлы: от тензора до микроблока".]
+ *   axis == 1 (blocks along cols; offs must be NULL):
+ *     x [batch*rows][cols] -> q [batch*rows][cols], scale [batch*rows][cols/32]; cols % 32 == 0.
+ *   axis == 0, offs == NULL (blocks along rows, per batch item):
+ *     x [batch][rows][cols] -> q phys [batch][cols][rows], scale [batch][cols][rows/32];
+ *     rows % 32 == 0.
+ *   axis == 0, offs != NULL (batch == 1; blocks restart at every group):
+ *     x [rows][cols] -> q phys [cols][rows_pad], scale [cols][rows_pad/32],
+ *     offs_pad_out int32 [n_groups] = inclusive cumsum of ceil(M_e/32)*32.
+ *     Each group is zero-padded to a multiple of 32 rows (pad counted as +0);
+ *     columns past the last padded group are written as data 0 and scale 0.
+ *     rows_pad % 32 == 0 and rows_pad >= quantize_mx_rows_bound(rows, n_groups).
+ *   Requires cols % 8 == 0 for axis == 0; x and q 16-byte aligned.
+ *   MX is defined for e4m3fn only (there is no codec argument).
+ */
+int quantize_mx(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis,
+                const int32_t *offs, int32_t n_groups, int rule,
+                void *q, void *scale_e8m0, int64_t rows_pad, int32_t *offs_pad_out,
+                void *stream);
+
+/* Host-side allocation bound for quantize_mx's padded rows: round_up(rows + 31*n_groups, 32).
+ * Returns -1 for negative arguments. */
+int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups);
+
+/*
+ * grouped_mm_scaled -- offset-routed grouped GEMM with the quantization scales
+ * applied in the epilogue (fp32) or per 32-block (e8m0).
+ *   [P1 Details, MoE paragraph: variable-size expert batches, per-expert weight
+ *   column scales, per-row activation scales, routing offsets, one launch;
+ *   P4 "MoE: почему DeepSeek-V3 ломал пайплайн"; P3 and P4 on the three GEMMs of a
+ *   linear layer (forward, input gradient, weight gradient); P2 Details, MoE
+ *   forward diagram (2D activations x 3D expert weights grouped by offsets) and
+ *   scaled MXFP8 grouped GEMM; P1 Details, Figure 1 "+GW" run with the weight
+ *   gradient kept in BF16.]
+ *   mode GROUPED_M (fwd/dgrad):  out[m][n] = sum_k A(m,k) B(e,n,k), m in group e
+ *     a [M][K], b [E][N][K] (E = n_groups), out [M][N]; rows of no group untouched.
+ *     SCALE_F32:  a_scale f32 [M], b_scale f32 [E][N]; A = dec(a)/sa, B = dec(b)/sb.
+ *     SCALE_E8M0: a_scale u8 [M][K/32], b_scale u8 [E][N][K/32]; K % 32 == 0.
+ *   mode GROUPED_K (wgrad):  out[e][n][k] = sum_{m in group e} A(n,m) B(k,m)
+ *     a phys [N][M], b phys [K][M] (token-contiguous), out [E][N][K]; empty group -> 0.
+ *     SCALE_F32:  a_scale f32 [E][N], b_scale f32 [E][K].
+ *     SCALE_E8M0: a_scale u8 [N][M/32], b_scale u8 [K][M/32]; M = padded rows and
+ *                 offs = padded offsets from quantize_mx (multiples of 32).
+ *     SCALE_NONE with OPD_BF16 operands: a bf16 [M][N], b bf16 [M][K] (token-major).
+ *   offs may be NULL only when n_groups == 1 (one group of all M rows).
+ *   Formats: both operands FP8 (e4m3fn or e4m3fnuz, mixed allowed; e8m0 needs
+ *   e4m3fn) or both BF16 (GROUPED_K with SCALE_NONE only).
+ *   Accumulation is fp32; out is bf16 (round to nearest even) or fp32.
+ *   Requires: M, N, K >= 0; K % 16 == 0 (GROUPED_M) or M % 16 == 0 (GROUPED_K);
+ *   all pointers 16-byte aligned.
+ */
+int grouped_mm_scaled(int mode, const void *a, int a_fmt, const void *a_scale,
+                      const void *b, int b_fmt, const void *b_scale, int scale_kind,
+                      const int32_t *offs, int32_t n_groups, int64_t M, int64_t N, int64_t K,
+                      void *out, int out_dtype, void *stream);
+
+/*
+ * fp8moe_encode_f32 -- the device FP8 encoder alone: q[i] = enc(y[i]) for
+ * values already inside [-fmax, fmax] (round to nearest, ties to the even
+ * code; e4m3fn keeps the sign of zero, e4m3fnuz has one unsigned zero).  The
+ * same encoder the quantization kernels use; exposed so the codec can be
+ * checked on the device over whole value ranges.  Values outside the range or
+ * NaN give unspecified codes.  y f32 [n] (4-byte aligned), q u8 [n].
+ */
+int fp8moe_encode_f32(const float *y, int64_t n, int codec, void *q, void *stream);
+
+/* Static string for a status code (never NULL). */
+const char *fp8moe_status_string(int status);
+
+/* FP8 codec native to a device: gfx950 -> E4M3FN, gfx942 -> E4M3FNUZ.  Queries
+ * the device (a HIP call).  Returns FP8MOE_ERR_UNSUPPORTED for other architectures.
+ * [P1 Details and P4 "Тихая порча градиентов": the FP8 dtype and its maximum are
+ * chosen from the hardware.] */
+int fp8moe_default_codec(int hip_device, int *codec_out);
+
+/* Library ABI version (major*100 + minor). */
+int fp8moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MOE_H */

@@ -1,0 +1,144 @@
+"""MI355X-native FP8 MoE quantization + grouped GEMM (thin Python binding).
+
+Every function here marshals torch tensors to device pointers and calls the
+C ABI of libfp8moe.so (include/fp8moe.h) on the current HIP stream; every step
+of the computation runs in the library's HIP kernels.  Outputs not supplied
+by the caller are allocated with torch (device memory plumbing only).  There is
+no CPU or eager fallback: a missing library or a rejected argument raises.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (E4M3FN, E4M3FNUZ, MX_FLOOR_OCP, MX_CEIL, GROUPED_M, GROUPED_K, OPD_E4M3FN,
+                   OPD_E4M3FNUZ, OPD_BF16, SCALE_F32, SCALE_E8M0, SCALE_NONE, OUT_BF16, OUT_F32,
+                   Fp8MoeError)
+
+__all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_rows_bound",
+           "grouped_mm_scaled", "encode_f32", "default_codec", "E4M3FN", "E4M3FNUZ", "MX_FLOOR_OCP",
+           "MX_CEIL", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ", "OPD_BF16", "SCALE_F32",
+           "SCALE_E8M0", "SCALE_NONE", "OUT_BF16", "OUT_F32", "Fp8MoeError"]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bits(x: torch.Tensor) -> torch.Tensor:
+    """bf16 tensors pass as their 16-bit patterns; int16/uint16 pass through."""
+    if x.dtype == torch.bfloat16:
+        return x
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError(f"expected bf16 (or its 16-bit pattern), got {x.dtype}")
+
+
+def quantize_rowwise(x, codec=E4M3FN, q=None, scale=None, stream=None):
+    """x [R, C] bf16 (row stride may exceed C) -> (q uint8 [R, C], scale f32 [R])."""
+    x = _bits(x)
+    R, C = x.shape
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("quantize_rowwise needs unit stride along the last dim")
+    ld_x = x.stride(0) if x.numel() else C
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((R,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _lib.check("quantize_rowwise", _lib.lib().quantize_rowwise(
+        _ptr(x), R, C, ld_x, codec, _ptr(q), _ptr(scale), _stream(stream)))
+    return q, scale
+
+
+def quantize_colwise(x, offs=None, codec=E4M3FN, q_t=None, scale=None, ld_q=None, stream=None):
+    """Grouped 2D: x [M, C] + offs [E] -> (q_t uint8 phys [C, ld_q], scale [E, C]).
+    Batched 3D: x [B, R, C] -> (q_t uint8 phys [B, C, ld_q], scale [B, C]).
+    ld_q defaults to the row count rounded up to a multiple of 16 (the ABI's alignment)."""
+    x = _bits(x).contiguous()
+    if offs is not None:
+        M, C = x.shape
+        B, R, E = 1, M, offs.numel()
+        ld_q = ld_q or (M + 15) // 16 * 16
+        q_t = torch.empty((C, ld_q), dtype=torch.uint8, device=x.device) if q_t is None else q_t
+        scale = torch.empty((E, C), dtype=torch.float32, device=x.device) if scale is None else scale
+    else:
+        B, R, C = x.shape
+        E = 0
+        ld_q = ld_q or (R + 15) // 16 * 16
+        q_t = torch.empty((B, C, ld_q), dtype=torch.uint8, device=x.device) if q_t is None else q_t
+        scale = torch.empty((B, C), dtype=torch.float32, device=x.device) if scale is None else scale
+    _lib.check("quantize_colwise", _lib.lib().quantize_colwise(
+        _ptr(x), B, R, C, _ptr(offs), E, codec, _ptr(q_t), ld_q, _ptr(scale), _stream(stream)))
+    return q_t, scale
+
+
+def quantize_mx_rows_bound(rows: int, n_groups: int) -> int:
+    return int(_lib.lib().quantize_mx_rows_bound(rows, n_groups))
+
+
+def quantize_mx(x, axis=1, offs=None, rule=MX_FLOOR_OCP, rows_pad=None, q=None, scale=None,
+                offs_pad=None, stream=None):
+    """MXFP8.  axis=1: x [R, C] -> (q [R, C], e8m0 [R, C/32], None).
+    axis=0 without offs: x [B, R, C] -> (q phys [B, C, R], e8m0 [B, C, R/32], None).
+    axis=0 with offs: x [M, C] -> (q phys [C, rows_pad], e8m0 [C, rows_pad/32], offs_pad [E])."""
+    x = _bits(x).contiguous()
+    dev = x.device
+    if axis == 1:
+        C = x.shape[-1]
+        R = x.numel() // max(C, 1)
+        q = torch.empty(tuple(x.shape), dtype=torch.uint8, device=dev) if q is None else q
+        scale = torch.empty(tuple(x.shape[:-1]) + (C // 32,), dtype=torch.uint8, device=dev) if scale is None else scale
+        st = _lib.lib().quantize_mx(_ptr(x), 1, R, C, 1, None, 0, rule, _ptr(q), _ptr(scale), 0, None,
+                                    _stream(stream))
+        _lib.check("quantize_mx", st)
+        return q, scale, None
+    if offs is None:
+        B, R, C = x.shape
+        q = torch.empty((B, C, R), dtype=torch.uint8, device=dev) if q is None else q
+        scale = torch.empty((B, C, R // 32), dtype=torch.uint8, device=dev) if scale is None else scale
+        st = _lib.lib().quantize_mx(_ptr(x), B, R, C, 0, None, 0, rule, _ptr(q), _ptr(scale), R, None,
+                                    _stream(stream))
+        _lib.check("quantize_mx", st)
+        return q, scale, None
+    M, C = x.shape
+    E = offs.numel()
+    rows_pad = rows_pad or quantize_mx_rows_bound(M, E)
+    q = torch.empty((C, rows_pad), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty((C, rows_pad // 32), dtype=torch.uint8, device=dev) if scale is None else scale
+    offs_pad = torch.empty((E,), dtype=torch.int32, device=dev) if offs_pad is None else offs_pad
+    st = _lib.lib().quantize_mx(_ptr(x), 1, M, C, 0, _ptr(offs), E, rule, _ptr(q), _ptr(scale), rows_pad,
+                                _ptr(offs_pad), _stream(stream))
+    _lib.check("quantize_mx", st)
+    return q, scale, offs_pad
+
+
+def grouped_mm_scaled(mode, a, a_fmt, a_scale, b, b_fmt, b_scale, scale_kind, offs, n_groups, M, N, K,
+                      out=None, out_dtype=OUT_BF16, stream=None):
+    """See include/fp8moe.h.  GROUPED_M -> out [M, N]; GROUPED_K -> out [E, N, K]."""
+    dev = a.device
+    if out is None:
+        shape = (M, N) if mode == GROUPED_M else (n_groups, N, K)
+        out = torch.empty(shape, dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device=dev)
+    st = _lib.lib().grouped_mm_scaled(mode, _ptr(a), a_fmt, _ptr(a_scale), _ptr(b), b_fmt, _ptr(b_scale),
+                                      scale_kind, _ptr(offs), n_groups, M, N, K, _ptr(out), out_dtype,
+                                      _stream(stream))
+    _lib.check("grouped_mm_scaled", st)
+    return out
+
+
+def encode_f32(y, codec=E4M3FN, q=None, stream=None):
+    """The device FP8 encoder on fp32 values already inside [-fmax, fmax]."""
+    q = torch.empty(y.shape, dtype=torch.uint8, device=y.device) if q is None else q
+    _lib.check("fp8moe_encode_f32", _lib.lib().fp8moe_encode_f32(_ptr(y), y.numel(), codec, _ptr(q),
+                                                                 _stream(stream)))
+    return q
+
+
+def default_codec(device: int = 0) -> int:
+    import ctypes
+    out = ctypes.c_int(-1)
+    _lib.check("fp8moe_default_codec", _lib.lib().fp8moe_default_codec(device, ctypes.byref(out)))
+    return out.value

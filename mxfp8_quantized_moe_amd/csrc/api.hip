@@ -1,0 +1,107 @@
+// C ABI entry points (include/fp8moe.h): validate on the host, then enqueue.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "../../include/fp8moe.h"
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+using namespace fp8moe;
+
+namespace fp8moe {
+
+__global__ __launch_bounds__(256) void encode_f32_kernel(const float* __restrict__ y, int64_t n, int codec,
+                                                         uint8_t* __restrict__ q) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    q[i] = (uint8_t)(codec == 0 ? enc_fp8<0>(y[i]) : enc_fp8<1>(y[i]));
+}
+
+hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1 << 16);
+  hipLaunchKernelGGL(encode_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, y, n, codec, q);
+  return hipGetLastError();
+}
+
+}  // namespace fp8moe
+
+static int launch_status(hipError_t e) { return e == hipSuccess ? FP8MOE_OK : FP8MOE_ERR_LAUNCH; }
+static hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+extern "C" {
+
+int quantize_rowwise(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, int codec, void* q, float* scale,
+                     void* stream) {
+  const int st = check_quantize_rowwise(x_bf16, rows, cols, ld_x, codec, q, scale);
+  if (st) return st;
+  return launch_status(launch_quantize_rowwise(static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, codec,
+                                               static_cast<uint8_t*>(q), scale, as_stream(stream)));
+}
+
+int quantize_colwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+                     int32_t n_groups, int codec, void* q_t, int64_t ld_q, float* scale, void* stream) {
+  const int st = check_quantize_colwise(x_bf16, batch, rows, cols, offs, n_groups, codec, q_t, ld_q, scale);
+  if (st) return st;
+  return launch_status(launch_quantize_colwise(static_cast<const uint16_t*>(x_bf16), batch, rows, cols, offs,
+                                               n_groups, codec, static_cast<uint8_t*>(q_t), ld_q, scale,
+                                               as_stream(stream)));
+}
+
+int quantize_mx(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,
+                int32_t n_groups, int rule, void* q, void* scale_e8m0, int64_t rows_pad, int32_t* offs_pad_out,
+                void* stream) {
+  const int st = check_quantize_mx(x_bf16, batch, rows, cols, axis, offs, n_groups, rule, q, scale_e8m0,
+                                   rows_pad, offs_pad_out);
+  if (st) return st;
+  return launch_status(launch_quantize_mx(static_cast<const uint16_t*>(x_bf16), batch, rows, cols, axis, offs,
+                                          n_groups, rule, static_cast<uint8_t*>(q),
+                                          static_cast<uint8_t*>(scale_e8m0), rows_pad, offs_pad_out,
+                                          as_stream(stream)));
+}
+
+int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups) { return mx_rows_bound(rows, n_groups); }
+
+int grouped_mm_scaled(int mode, const void* a, int a_fmt, const void* a_scale, const void* b, int b_fmt,
+                      const void* b_scale, int scale_kind, const int32_t* offs, int32_t n_groups, int64_t M,
+                      int64_t N, int64_t K, void* out, int out_dtype, void* stream) {
+  const int st = check_grouped_mm(mode, a, a_fmt, a_scale, b, b_fmt, b_scale, scale_kind, offs, n_groups, M, N,
+                                  K, out, out_dtype);
+  if (st) return st;
+  GemmArgs g{mode, a_fmt, b_fmt, scale_kind, out_dtype, a, b, a_scale, b_scale, offs, n_groups, M, N, K, out};
+  return launch_status(launch_grouped_mm(g, as_stream(stream)));
+}
+
+int fp8moe_encode_f32(const float* y, int64_t n, int codec, void* q, void* stream) {
+  const int st = check_encode_f32(y, n, codec, q);
+  if (st) return st;
+  return launch_status(launch_encode_f32(y, n, codec, static_cast<uint8_t*>(q), as_stream(stream)));
+}
+
+const char* fp8moe_status_string(int status) {
+  switch (status) {
+    case FP8MOE_OK: return "ok";
+    case FP8MOE_ERR_NULL: return "null pointer";
+    case FP8MOE_ERR_SHAPE: return "invalid shape";
+    case FP8MOE_ERR_ENUM: return "invalid enum value";
+    case FP8MOE_ERR_ALIGN: return "alignment or divisibility violated";
+    case FP8MOE_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP8MOE_ERR_LAUNCH: return "kernel launch failed";
+    case FP8MOE_ERR_DEVICE: return "device query failed";
+    default: return "unknown status";
+  }
+}
+
+int fp8moe_default_codec(int hip_device, int* codec_out) {
+  if (codec_out == nullptr) return FP8MOE_ERR_NULL;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, hip_device) != hipSuccess) return FP8MOE_ERR_DEVICE;
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) { *codec_out = FP8MOE_E4M3FN; return FP8MOE_OK; }
+  if (std::strncmp(p.gcnArchName, "gfx942", 6) == 0) { *codec_out = FP8MOE_E4M3FNUZ; return FP8MOE_OK; }
+  return FP8MOE_ERR_UNSUPPORTED;
+}
+
+int fp8moe_version(void) { return 100; }
+
+}  // extern "C"

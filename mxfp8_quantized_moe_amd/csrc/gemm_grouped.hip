@@ -1,0 +1,372 @@
+// Offset-routed grouped GEMM on gfx950 FP8 MFMA, for the forward, dgrad and
+// wgrad products of an MoE expert layer.
+// [P1 Details, MoE paragraph: variable-size expert batches through one grouped
+// GEMM launch with per-row activation scales, per-expert weight column scales
+// and routing offsets; P4 "MoE: почему DeepSeek-V3 ломал пайплайн"; P3/P4 on
+// the three GEMMs of a linear layer; P2 Details: 2D activations x 3D expert
+// weights grouped by offsets, and the MXFP8 scaled grouped GEMM.]
+//
+// Both operands are read contraction-contiguous ("row operand" P: tile rows
+// are output rows; "column operand" Q: tile rows are output columns):
+//   GROUPED_M (fwd/dgrad): P = A[m][K] rows of group e, Q = B[e][n][K].
+//   GROUPED_K (wgrad):     P = A phys [n][M], Q = B phys [k][M], contraction
+//                          over the token range [lo(e), hi(e)) of group e.
+//
+// Tiling, derived from the hardware rather than searched:
+//  * v_mfma_scale_f32_32x32x64_f8f6f4: each lane holds one row (lane & 31) and
+//    two 16-byte halves of the 64-wide contraction at byte offsets 16*g and
+//    32 + 16*g (g = lane >> 5); the e8m0 scale of (row i, 32-block b) comes
+//    from lane i + 32*b.  The 32x32 fp32 result sits in 16 registers: column
+//    lane & 31, row 8*(v/4) + 4*(lane>>5) + v%4.
+//  * 256 threads = 2x2 waves; a wave owns (BM/2) x (BN/2) outputs.  BM = BN =
+//    256 gives 4x4 MFMA tiles per wave = 256 fp32 accumulators per lane, the
+//    largest tile that fits one wave per SIMD (512 registers) and makes each
+//    byte read from LDS feed 128 flops per wave.
+//  * 128 contraction bytes per stage: (BM + BN) x 128 B = 64 KiB, double
+//    buffered = 128 KiB of the 160 KiB LDS.  Global loads of stage k+1 are in
+//    flight while stage k runs on the matrix cores.
+//  * LDS rows are 128 B (8 chunks of 16 B); chunk c of row r is stored at chunk
+//    c ^ ((r >> 1) & 7), so 16 consecutive lanes reading the same logical chunk
+//    of 16 consecutive rows, and 16 lanes writing 8 chunks of 2 rows, both
+//    touch 16 distinct 16-byte bank groups.
+//  * Small groups (average rows per group below 512) use BM = 128 to waste
+//    less of each tile on padding rows.
+//  * Workgroups are numbered so that each XCD (round-robin dispatch over 8)
+//    gets a contiguous range of tiles, ordered in bands of 8 row tiles, so the
+//    tiles running together on one XCD share operand rows in its L2.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace fp8moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kStageK = 128;   // contraction bytes per stage
+constexpr int kBandRows = 8;   // row tiles per band in the tile order
+
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+struct KParams {
+  const uint8_t* a;
+  const uint8_t* b;
+  const void* sa;
+  const void* sb;
+  const int32_t* offs;
+  void* out;
+  int E, M, N, K;
+  int row_units;   // GROUPED_M: bound on row tiles over all groups; GROUPED_K: E * ceil(N / BM)
+  int col_tiles;   // GROUPED_M: ceil(N / BN); GROUPED_K: ceil(K / BN)
+};
+
+// Each XCD gets a contiguous range of logical tile ids (dispatch is round-robin).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int x = bid % 8, i = bid / 8;
+  return x * per + min(x, rem) + i;
+}
+
+// Zero the bytes of a 16-byte chunk at contraction position pos outside [lo, hi).
+__device__ __forceinline__ u32x4 mask_chunk(u32x4 v, int pos, int lo, int hi) {
+  const int s = lo - pos, e = hi - pos;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int a = min(max(s - 4 * i, 0), 4), b = min(max(e - 4 * i, 0), 4);
+    const uint32_t keep_hi = b >= 4 ? 0xFFFFFFFFu : ((1u << (8 * b)) - 1u);
+    const uint32_t drop_lo = a >= 4 ? 0xFFFFFFFFu : ((1u << (8 * a)) - 1u);
+    w[i] &= keep_hi & ~drop_lo;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int BM, int BN, int MODE, int SK, int OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_fp8_kernel(KParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int A_BYTES = BM * kStageK, STAGE = (BM + BN) * kStageK;
+  constexpr int LA = BM / 32, LB = BN / 32;         // 16-byte global loads per thread per stage
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ uint32_t s_sc[SK == 1 ? 2 * (BM + BN) : 1];   // e8m0 bytes of 4 blocks per tile row
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---------------------------------------------------------------- tile -> work
+  const int total = gridDim.x;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int band = L / (kBandRows * p.col_tiles);
+  const int first = band * kBandRows;
+  const int gsz = min(p.row_units - first, kBandRows);
+  const int inband = L % (kBandRows * p.col_tiles);
+  const int ru = first + inband % gsz;
+  const int ct = inband / gsz;
+
+  const uint8_t* P;
+  const uint8_t* Q;
+  int64_t p_ld, q_ld;
+  int p_valid, q_valid, c_lo, c_hi, e;
+  int64_t out_base, out_ld;
+  const uint8_t* psc = nullptr;   // e8m0 rows
+  const uint8_t* qsc = nullptr;
+  int64_t sc_ld = 0;
+  const float* psf = nullptr;     // fp32 scales of the tile's rows / columns
+  const float* qsf = nullptr;
+  if constexpr (MODE == 0) {
+    struct Ch {
+      __device__ int operator()(int lo, int hi) const { return (hi - lo + BM - 1) / BM; }
+    };
+    struct NoPad {
+      __device__ int operator()(int, int) const { return 0; }
+    };
+    const Unit un = find_unit<256>(p.offs, p.E, p.M, ru, Ch{}, NoPad{});
+    if (un.e < 0) return;
+    e = un.e;
+    const int m0 = un.lo + un.j * BM, n0 = ct * BN;
+    p_valid = min(BM, un.hi - m0);
+    q_valid = min(BN, p.N - n0);
+    P = p.a + (int64_t)m0 * p.K;
+    Q = p.b + ((int64_t)e * p.N + n0) * p.K;
+    p_ld = q_ld = p.K;
+    c_lo = 0;
+    c_hi = p.K;
+    out_ld = p.N;
+    out_base = (int64_t)m0 * p.N + n0;
+    if constexpr (SK == 1) {
+      sc_ld = p.K / 32;
+      psc = static_cast<const uint8_t*>(p.sa) + (int64_t)m0 * sc_ld;
+      qsc = static_cast<const uint8_t*>(p.sb) + ((int64_t)e * p.N + n0) * sc_ld;
+    } else {
+      psf = static_cast<const float*>(p.sa) + m0;
+      qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.N + n0;
+    }
+  } else {
+    const int ntn = (p.N + BM - 1) / BM;
+    e = ru / ntn;
+    const int n0 = (ru % ntn) * BM, k0 = ct * BN;
+    // group range of e: lo = max over j < e of clamp(offs[j]); hi = max(lo, clamp(offs[e]))
+    __shared__ int s_red[4];
+    int m = 0;
+    if (p.offs != nullptr)
+      for (int jj = t; jj < e; jj += 256) m = max(m, clamp_off(p.offs[jj], p.M));
+    m = (int)wave_max_u32((uint32_t)m);
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    const int lo = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+    const int hi = p.offs != nullptr ? max(lo, clamp_off(p.offs[e], p.M)) : p.M;
+    p_valid = min(BM, p.N - n0);
+    q_valid = min(BN, p.K - k0);
+    P = p.a + (int64_t)n0 * p.M;
+    Q = p.b + (int64_t)k0 * p.M;
+    p_ld = q_ld = p.M;
+    c_lo = lo;
+    c_hi = hi;
+    out_ld = p.K;
+    out_base = ((int64_t)e * p.N + n0) * p.K + k0;
+    if constexpr (SK == 1) {
+      sc_ld = p.M / 32;
+      psc = static_cast<const uint8_t*>(p.sa) + (int64_t)n0 * sc_ld;
+      qsc = static_cast<const uint8_t*>(p.sb) + (int64_t)k0 * sc_ld;
+    } else {
+      psf = static_cast<const float*>(p.sa) + (int64_t)e * p.N + n0;
+      qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.K + k0;
+    }
+  }
+
+  const int c_start = c_lo & ~15;
+  const int nk = c_hi > c_lo ? (c_hi - c_start + kStageK - 1) / kStageK : 0;
+
+  // ---------------------------------------------------------------- global -> LDS
+  const int lc = t & 7, lr = t >> 3;   // this thread's chunk and first row in a stage
+  u32x4 ra[LA], rb[LB];
+  uint32_t rsc[SK == 1 ? 2 : 1];
+
+  auto load_stage = [&](int kt) {
+    const int pos = c_start + kt * kStageK + 16 * lc;
+    const bool in = pos < c_hi;
+    const bool partial = in && (pos < c_lo || pos + 16 > c_hi);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int r = min(lr + 32 * i, p_valid - 1);
+      ra[i] = in ? *reinterpret_cast<const u32x4*>(P + r * p_ld + pos) : u32x4{0, 0, 0, 0};
+      if (partial) ra[i] = mask_chunk(ra[i], pos, c_lo, c_hi);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int r = min(lr + 32 * i, q_valid - 1);
+      rb[i] = in ? *reinterpret_cast<const u32x4*>(Q + r * q_ld + pos) : u32x4{0, 0, 0, 0};
+      if (partial) rb[i] = mask_chunk(rb[i], pos, c_lo, c_hi);
+    }
+    if constexpr (SK == 1) {
+      // 4 e8m0 bytes (the stage's 32-blocks) for tile rows t and t + 256
+      const int blk0 = (c_start + kt * kStageK) >> 5, nblk = c_hi >> 5;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = t + 256 * h;
+        uint32_t w = 0;
+        if (r < BM + BN) {
+          const bool isp = r < BM;
+          const int rr = isp ? min(r, p_valid - 1) : min(r - BM, q_valid - 1);
+          const uint8_t* src = (isp ? psc : qsc) + rr * sc_ld;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (blk0 + j < nblk) w |= (uint32_t)src[blk0 + j] << (8 * j);
+        }
+        rsc[h] = w;
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint8_t* sa_ = smem + buf * STAGE;
+    uint8_t* sb_ = sa_ + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(sa_ + lds_off(lr + 32 * i, lc)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(sb_ + lds_off(lr + 32 * i, lc)) = rb[i];
+    if constexpr (SK == 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (t + 256 * h < BM + BN) s_sc[buf * (BM + BN) + t + 256 * h] = rsc[h];
+    }
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int g = lane >> 5, lrow = lane & 31;
+  if (nk > 0) {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_stage(kt + 1);
+    const uint8_t* sa_ = smem + buf * STAGE;
+    const uint8_t* sb_ = sa_ + A_BYTES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8i af[TM], bf[TN];
+      int scA[TM], scB[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + 32 * i + lrow;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + lds_off(r, 4 * h + g));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + lds_off(r, 4 * h + 2 + g));
+        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if constexpr (SK == 1) scA[i] = (int)((s_sc[buf * (BM + BN) + r] >> (8 * (2 * h + g))) & 0xFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WN + 32 * j + lrow;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + lds_off(r, 4 * h + g));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + lds_off(r, 4 * h + 2 + g));
+        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if constexpr (SK == 1) scB[j] = (int)((s_sc[buf * (BM + BN) + BM + r] >> (8 * (2 * h + g))) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (SK == 1)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, scA[i], 0,
+                                                                        scB[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nk) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // fp32 scales are multipliers of the quantized operands: divide by both.
+  const bool empty = c_hi <= c_lo;
+  float inv_q[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int cidx = min(wn * WN + 32 * j + lrow, q_valid - 1);
+    inv_q[j] = SK == 0 ? __frcp_rn(qsf[cidx]) : 1.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (r >= p_valid) continue;
+      const float inv_p = SK == 0 ? __frcp_rn(psf[r]) : 1.0f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int c = wn * WN + 32 * j + lrow;
+        if (c >= q_valid) continue;
+        const float val = empty ? 0.0f : acc[i][j][v] * inv_p * inv_q[j];
+        const int64_t o = out_base + (int64_t)r * out_ld + c;
+        if constexpr (OUT == 0)
+          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(val);
+        else
+          static_cast<float*>(p.out)[o] = val;
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int MODE, int SK, int OUT>
+static hipError_t launch_fp8(const GemmArgs& g, hipStream_t st) {
+  KParams p;
+  p.a = static_cast<const uint8_t*>(g.a);
+  p.b = static_cast<const uint8_t*>(g.b);
+  p.sa = g.sa;
+  p.sb = g.sb;
+  p.offs = g.offs;
+  p.out = g.out;
+  p.E = g.n_groups;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  if (MODE == 0) {
+    p.row_units = (int)((g.M + BM - 1) / BM + g.n_groups);
+    p.col_tiles = (int)((g.N + BN - 1) / BN);
+  } else {
+    p.row_units = (int)(g.n_groups * ((g.N + BM - 1) / BM));
+    p.col_tiles = (int)((g.K + BN - 1) / BN);
+  }
+  const int64_t total = (int64_t)p.row_units * p.col_tiles;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, MODE, SK, OUT>), dim3((unsigned)total), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int MODE, int SK, int OUT>
+static hipError_t pick_tile(const GemmArgs& g, hipStream_t st) {
+  // GROUPED_M with small average groups wastes less of a 128-row tile.
+  const bool small = MODE == 0 && g.n_groups > 1 && g.M / g.n_groups < 512;
+  return small ? launch_fp8<128, 256, MODE, SK, OUT>(g, st) : launch_fp8<256, 256, MODE, SK, OUT>(g, st);
+}
+
+template <int MODE>
+static hipError_t dispatch_fp8(const GemmArgs& g, hipStream_t st) {
+  if (g.scale_kind == 1)
+    return g.out_dtype == 0 ? pick_tile<MODE, 1, 0>(g, st) : pick_tile<MODE, 1, 1>(g, st);
+  return g.out_dtype == 0 ? pick_tile<MODE, 0, 0>(g, st) : pick_tile<MODE, 0, 1>(g, st);
+}
+
+hipError_t launch_grouped_mm_bf16(const GemmArgs& g, hipStream_t st);
+
+hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st) {
+  const bool fn = g.a_fmt == 0 && g.b_fmt == 0;
+  if (g.a_fmt == 2 || !fn) return launch_grouped_mm_bf16(g, st);
+  if (g.M == 0 && g.mode == 0) return hipSuccess;
+  return g.mode == 0 ? dispatch_fp8<0>(g, st) : dispatch_fp8<1>(g, st);
+}
+
+}  // namespace fp8moe

@@ -1,0 +1,40 @@
+// Internal launchers: one per operation, called by the C ABI after validation.
+// Each enqueues kernels on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+namespace fp8moe {
+
+hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int codec,
+                                   uint8_t* q, float* scale, hipStream_t st);
+
+hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                   const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,
+                                   int64_t ld_q, float* scale, hipStream_t st);
+
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int axis,
+                              const int32_t* offs, int32_t n_groups, int rule, uint8_t* q, uint8_t* sc,
+                              int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st);
+
+struct GemmArgs {
+  int mode, a_fmt, b_fmt, scale_kind, out_dtype;
+  const void* a;
+  const void* b;
+  const void* sa;
+  const void* sb;
+  const int32_t* offs;
+  int n_groups;
+  int64_t M, N, K;
+  void* out;
+};
+
+hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st);
+
+hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st);
+
+}  // namespace fp8moe

@@ -1,0 +1,246 @@
+// Colwise dynamic FP8 quantization for the backward GEMMs: one fp32 scale per
+// (group, column) over the group's rows, FP8 output written transposed
+// (phys [C][rows]) so the wgrad/dgrad GEMMs read contraction-contiguous
+// operands with no separate transpose copy.
+// [P1 Details (colwise scales kernel: LDS-transposed output tile, single-pass
+// variant without the second HBM read; relaxed atomics on AMD); P4 "Три уровня
+// оптимизации Triton-ядер" (removal of the .t().contiguous().t() copy; fused
+// scale-and-cast; relaxed atomic ordering for commutative reductions).]
+//
+// Work units: a 64-column strip x a chunk of up to 512 rows of one group.
+// Chunks of group e are anchored at floor16(lo(e)) so every 16-row output
+// segment is 16-byte aligned; the (rare) segments shared with a neighbouring
+// group are stored byte by byte.
+//   * A group that fits one chunk is done in one pass by the cast kernel: the
+//     chunk is loaded once into registers, reduced, scaled, cast, transposed
+//     through LDS and stored (2 B read + 1 B written per element).
+//   * A taller group first gets its per-column maxima from the partial-max
+//     kernel: every chunk reduces its rows and merges them into the scale
+//     buffer with a relaxed device-scope atomic max on the fp32 bit pattern,
+//     tagged with the sign bit (order independent, exact).  The cast kernel
+//     then turns the tag into the scale; a reader sees either the tagged max or
+//     the final scale, and both give the same scale.  The cast kernel visits
+//     units in reverse order so its second read starts with the data the
+//     partial-max kernel touched last (still in the last-level cache).
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "tile_lds.hpp"
+
+namespace fp8moe {
+
+constexpr int kCwThreads = 256;
+constexpr int kCwIters = kTileRows / 128;   // 4 iterations of 128 rows
+constexpr uint32_t kTag = 0x80000000u;      // marks a merged |x| max (not yet a scale)
+
+__device__ __forceinline__ int cw_chunks(int lo, int hi) {
+  if (hi <= lo) return 1;                    // an empty group still owns one unit: its scale
+  const int a = lo & ~15;
+  return (hi - a + kTileRows - 1) / kTileRows;
+}
+struct CwChunks {
+  __device__ int operator()(int lo, int hi) const { return cw_chunks(lo, hi); }
+};
+struct NoPad {
+  __device__ int operator()(int, int) const { return 0; }
+};
+
+__global__ __launch_bounds__(256) void colwise_reset_kernel(uint32_t* __restrict__ s, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) s[i] = kTag;   // tagged zero max
+}
+
+struct CwGeom {
+  int e, j, olo, ohi;      // group, chunk, output row range of the group
+  int64_t in_base;         // input row of output row 0 of this group's output space
+  uint8_t* q;              // output base of the group: q[c * ld_q + r]
+  float* s;                // scale base of the group: s[c]
+  bool ok;
+};
+
+template <bool GROUPED>
+__device__ __forceinline__ CwGeom cw_geom(int u, int64_t batch, int rows, int cols,
+                                          const int32_t* offs, int n_groups, uint8_t* q_t,
+                                          int64_t ld_q, float* scale) {
+  CwGeom g;
+  if constexpr (GROUPED) {
+    const Unit un = find_unit<kCwThreads>(offs, n_groups, rows, u, CwChunks{}, NoPad{});
+    g.ok = un.e >= 0;
+    g.e = un.e; g.j = un.j; g.olo = un.lo; g.ohi = un.hi;
+    g.in_base = 0;
+    g.q = q_t;
+    g.s = scale + (int64_t)max(un.e, 0) * cols;
+  } else {
+    const int upb = cw_chunks(0, rows);
+    const int64_t b = u / upb;
+    g.ok = b < batch;
+    g.e = (int)b; g.j = u % upb; g.olo = 0; g.ohi = rows;
+    g.in_base = b * rows;
+    g.q = q_t + b * cols * ld_q;
+    g.s = scale + b * cols;
+  }
+  return g;
+}
+
+// Reduce the per-thread packed maxima (4 u32 = 8 columns) over the 32 row
+// slots; returns the bf16 |x| max bit pattern of column t (t < 64) in `out`.
+__device__ __forceinline__ void cw_reduce_cols(uint32_t m[4], uint32_t* red /* [4][8][4] */, uint32_t* out) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, cc = t & 7;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int off = 8; off <= 32; off <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)m[p], off, 64);
+      m[p] = (max(m[p] & 0xFFFFu, o & 0xFFFFu)) | (max(m[p] >> 16, o >> 16) << 16);
+    }
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) red[(w * 8 + cc) * 4 + p] = m[p];
+  }
+  __syncthreads();
+  if (t < 64) {
+    const int c8 = t >> 3, p = (t & 7) >> 1, half = t & 1;
+    uint32_t r = 0;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) r = max(r, (red[(ww * 8 + c8) * 4 + p] >> (16 * half)) & 0xFFFFu);
+    out[t] = r;
+  }
+  __syncthreads();
+}
+
+// PHASE 0: partial maxima of multi-chunk groups.  PHASE 1: cast (and the whole
+// job for single-chunk and empty groups).
+template <int CODEC, bool GROUPED, int PHASE>
+__global__ __launch_bounds__(256) void colwise_kernel(const uint16_t* __restrict__ x, int64_t batch,
+                                                      int rows, int cols, const int32_t* __restrict__ offs,
+                                                      int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
+                                                      float* __restrict__ scale, int n_strips, int units) {
+  __shared__ uint32_t red[4 * 8 * 4];
+  __shared__ uint32_t s_amax[64];
+  __shared__ float s_scale[64];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[PHASE == 1 ? kTileBytes : 16];
+
+  const int strip = blockIdx.x % n_strips;
+  int u = blockIdx.x / n_strips;
+  if (PHASE == 1) u = units - 1 - u;
+  const CwGeom g = cw_geom<GROUPED>(u, batch, rows, cols, offs, n_groups, q_t, ld_q, scale);
+  if (!g.ok) return;
+
+  const int t = threadIdx.x, cc = t & 7, rs = t >> 3;
+  const int c0 = strip * kTileCols;
+  const bool empty = g.ohi <= g.olo;
+  const int nch = cw_chunks(g.olo, g.ohi);
+  if (PHASE == 0 && (empty || nch == 1)) return;
+  if (empty) {   // PHASE 1: the scale of an empty group (no rows, no data)
+    if (t < 64 && c0 + t < cols) g.s[c0 + t] = scale_from_amax(0.0f, CODEC);
+    return;
+  }
+
+  const int A = (g.olo & ~15) + g.j * kTileRows;          // output row of tile row 0
+  const int r_begin = max(A, g.olo), r_end = min(A + kTileRows, g.ohi);
+  const int col = c0 + cc * 8;
+  const bool col_ok = col < cols;
+
+  u32x4 v[kCwIters][4];
+  uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kCwIters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = A + 128 * i + 4 * rs + k;
+      const bool ok = col_ok && r >= r_begin && r < r_end;
+      v[i][k] = ok ? *reinterpret_cast<const u32x4*>(x + (g.in_base + r) * cols + col) : u32x4{0, 0, 0, 0};
+      m[0] = pk_absmax_bf16(m[0], v[i][k].x);
+      m[1] = pk_absmax_bf16(m[1], v[i][k].y);
+      m[2] = pk_absmax_bf16(m[2], v[i][k].z);
+      m[3] = pk_absmax_bf16(m[3], v[i][k].w);
+    }
+  }
+
+  if (PHASE == 0) {
+    cw_reduce_cols(m, red, s_amax);
+    if (t < 64 && c0 + t < cols)
+      __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(g.s) + c0 + t, kTag | (s_amax[t] << 16),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  } else {
+    if (nch == 1) {
+      cw_reduce_cols(m, red, s_amax);
+      if (t < 64) s_scale[t] = scale_from_amax(__uint_as_float(s_amax[t] << 16), CODEC);
+    } else if (t < 64) {
+      float sc = 0.0f;
+      if (c0 + t < cols) {
+        const uint32_t b = __hip_atomic_load(reinterpret_cast<uint32_t*>(g.s) + c0 + t, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        sc = (b & kTag) ? scale_from_amax(__uint_as_float(b & ~kTag), CODEC) : __uint_as_float(b);
+      }
+      s_scale[t] = sc;
+    }
+    __syncthreads();
+    if (g.j == 0 && t < 64 && c0 + t < cols) g.s[c0 + t] = s_scale[t];
+
+    // cast: per column, the 4 rows of a slot become one little-endian word
+    float sc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sc[k] = s_scale[cc * 8 + k];
+#pragma unroll
+    for (int i = 0; i < kCwIters; ++i) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t w = quant4<CODEC>(col_of(v[i][0], k), col_of(v[i][1], k), col_of(v[i][2], k),
+                                         col_of(v[i][3], k), sc[k]);
+        tile_put4(tile, cc * 8 + k, 128 * i + 4 * rs, w);
+      }
+    }
+    __syncthreads();
+
+    // transposed store: each pass writes 8 columns x 32 segments of 16 rows
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int ci = p * 8 + (t >> 5), sg = t & 31;
+      const int c = c0 + ci, R0 = A + 16 * sg;
+      if (c < cols && R0 < r_end && R0 + 16 > r_begin) {
+        const u32x4 d = tile_get16(tile, ci, 16 * sg);
+        store_segment(g.q + (int64_t)c * ld_q + R0, R0, r_begin, r_end, d);
+      }
+    }
+  }
+}
+
+int64_t colwise_units_bound(int64_t batch, int64_t rows, const int32_t* offs, int32_t n_groups) {
+  if (offs) return (rows + 16LL * n_groups + kTileRows - 1) / kTileRows + n_groups;
+  const int64_t upb = rows > 0 ? (rows + kTileRows - 1) / kTileRows : 1;
+  return batch * upb;
+}
+
+template <int CODEC, bool GROUPED>
+static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                            const int32_t* offs, int32_t n_groups, uint8_t* q_t, int64_t ld_q, float* scale,
+                            hipStream_t st) {
+  const int64_t n_scale = (GROUPED ? n_groups : batch) * cols;
+  if (n_scale == 0) return hipSuccess;
+  const int n_strips = (int)((cols + kTileCols - 1) / kTileCols);
+  const int64_t units = colwise_units_bound(batch, rows, offs, n_groups);
+  hipLaunchKernelGGL(colwise_reset_kernel, dim3((unsigned)((n_scale + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(scale), n_scale);
+  const dim3 grid((unsigned)(units * n_strips));
+  hipLaunchKernelGGL((colwise_kernel<CODEC, GROUPED, 0>), grid, dim3(256), 0, st, x, batch, (int)rows,
+                     (int)cols, offs, n_groups, q_t, ld_q, scale, n_strips, (int)units);
+  hipLaunchKernelGGL((colwise_kernel<CODEC, GROUPED, 1>), grid, dim3(256), 0, st, x, batch, (int)rows,
+                     (int)cols, offs, n_groups, q_t, ld_q, scale, n_strips, (int)units);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                   const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,
+                                   int64_t ld_q, float* scale, hipStream_t st) {
+  if (cols == 0) return hipSuccess;
+  if (offs) {
+    return codec == 0 ? launch_cw<0, true>(x, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st)
+                      : launch_cw<1, true>(x, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st);
+  }
+  return codec == 0 ? launch_cw<0, false>(x, batch, rows, cols, nullptr, 0, q_t, ld_q, scale, st)
+                    : launch_cw<1, false>(x, batch, rows, cols, nullptr, 0, q_t, ld_q, scale, st);
+}
+
+}  // namespace fp8moe

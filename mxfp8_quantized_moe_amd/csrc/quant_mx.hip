@@ -1,0 +1,227 @@
+// MXFP8 dynamic quantization: e4m3fn codes with one e8m0 scale per 1x32 block.
+// [P2 Details: MXFP8 data/scale layout diagram (e4m3 data, e8m0 scale per 1x32
+// block); activations and weights quantized on the fly before the scaled
+// grouped GEMM; wgrad blocks run along the contracting (token) dimension.
+// P4 "Скейлы: от тензора до микроблока".]
+//
+// The scale factor 2^-X is a power of two, so x * 2^-X is exact in fp32 (bf16
+// inputs); the clamp to +-448 and the round-to-nearest-even encode follow.
+//
+// Two layouts:
+//  * blocks along the last dim (fwd/dgrad operands, K-contiguous): 4 lanes per
+//    block, 16 bytes each, a 2-step shuffle reduction.
+//  * blocks along rows (wgrad operands; weights for dgrad): the colwise tile
+//    (64 columns x 512 rows) with the output transposed through LDS.  A
+//    32-row block is exactly the 8 row-slots of one wave in one iteration, so
+//    its reduction is three lane shuffles.  With group offsets, blocks restart
+//    at every group, each group is padded to a multiple of 32 rows with +0,
+//    groups sit back to back at padded offsets, and the columns past the last
+//    padded group are written with zero codes and zero scales.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "tile_lds.hpp"
+
+namespace fp8moe {
+
+// ------------------------------------------------------------ last-dim blocks
+
+template <int RULE>
+__global__ __launch_bounds__(256) void mx_lastdim_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  // chunk = 8 consecutive elements; 4 chunks = one block; rows are multiples of 32
+  for (int64_t ci = (int64_t)blockIdx.x * 256 + threadIdx.x; ci < n_chunks; ci += (int64_t)gridDim.x * 256) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(x)[ci];
+    uint32_t m = pk_absmax_bf16(pk_absmax_bf16(0u, v.x), v.y);
+    m = pk_fold(pk_absmax_bf16(pk_absmax_bf16(m, v.z), v.w));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+    const int X = mx_exponent(m << 16, RULE);
+    const float s = exp2_neg(X);
+    reinterpret_cast<u32x2*>(q)[ci] = u32x2{quant_bf16x4<0>(v.x, v.y, s), quant_bf16x4<0>(v.z, v.w, s)};
+    if ((ci & 3) == 0) sc[ci >> 2] = (uint8_t)(X + 127);
+  }
+}
+
+// ------------------------------------------------------------ row blocks
+
+constexpr int kMxIters = kTileRows / 128;
+
+__device__ __forceinline__ int mx_chunks(int lo, int hi) {
+  const int mp = (hi - lo + 31) & ~31;
+  return (mp + kTileRows - 1) / kTileRows;   // an empty group owns no unit
+}
+struct MxChunks {
+  __device__ int operator()(int lo, int hi) const { return mx_chunks(lo, hi); }
+};
+struct MxPad {
+  __device__ int operator()(int lo, int hi) const { return (hi - lo + 31) & ~31; }
+};
+
+template <int RULE, bool GROUPED>
+__global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t batch, int rows,
+                                                      int cols, const int32_t* __restrict__ offs, int n_groups,
+                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                      int64_t rows_pad, int32_t* __restrict__ offs_pad_out,
+                                                      int n_strips) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
+  __shared__ uint8_t s_x[64 * 16];       // e8m0 codes: [column][block of the tile]
+
+  const int strip = blockIdx.x % n_strips;
+  const int u = blockIdx.x / n_strips;
+  const int t = threadIdx.x, cc = t & 7, rs = t >> 3, lane = t & 63, w = t >> 6;
+
+  // geometry: input rows [lo, hi) -> padded output rows [plo, phi) of the output space
+  int lo, hi, plo, phi, j;
+  int64_t ld_q, ld_s;
+  uint8_t* qb;
+  uint8_t* sb;
+  if constexpr (GROUPED) {
+    if (blockIdx.x == 0 && offs_pad_out != nullptr) {
+      // padded offsets: inclusive cumulative sum of ceil32 of each group's rows
+      __shared__ int tmp[4];
+      __shared__ int s_hi[256];
+      __shared__ int s_tot[2];
+      int carry = 0, pbase = 0;
+      for (int g0 = 0; g0 < n_groups; g0 += 256) {
+        const int e = g0 + t;
+        const int vv = e < n_groups ? clamp_off(offs[e], rows) : 0;
+        const int h = max(block_scan_max<256>(vv, tmp), carry);
+        s_hi[t] = h;
+        __syncthreads();
+        const int l = t == 0 ? carry : s_hi[t - 1];
+        const int pd = e < n_groups ? ((h - l + 31) & ~31) : 0;
+        const int pincl = block_scan_sum<256>(pd, tmp) + pbase;
+        if (e < n_groups) offs_pad_out[e] = pincl;
+        if (t == 255) { s_tot[0] = pincl; s_tot[1] = h; }
+        __syncthreads();
+        pbase = s_tot[0];
+        carry = s_tot[1];
+        __syncthreads();
+      }
+    }
+    const Unit un = find_unit<256>(offs, n_groups, rows, u, MxChunks{}, MxPad{});
+    if (un.e >= 0) {
+      lo = un.lo; hi = un.hi; plo = un.pbase; phi = plo + ((hi - lo + 31) & ~31); j = un.j;
+    } else {
+      // tail: columns [padded total, rows_pad) get zero codes and zero scales
+      lo = hi = 0; plo = un.pbase; phi = (int)rows_pad; j = un.j;
+      if (plo + j * kTileRows >= phi) return;
+    }
+    ld_q = rows_pad; ld_s = rows_pad / 32; qb = q; sb = sc;
+  } else {
+    const int upb = mx_chunks(0, rows);
+    const int64_t b = upb ? u / upb : batch;
+    if (b >= batch) return;
+    j = u % upb;
+    lo = (int)0; hi = rows; plo = 0; phi = rows;
+    ld_q = rows; ld_s = rows / 32;
+    qb = q + b * cols * (int64_t)rows;
+    sb = sc + b * cols * (int64_t)(rows / 32);
+    x += b * (int64_t)rows * cols;
+  }
+
+  const int A = plo + j * kTileRows;                 // output row of tile row 0 (multiple of 32)
+  const int r_end = min(A + kTileRows, phi);         // output rows of this unit: [A, r_end)
+  const int c0 = strip * kTileCols;
+  const int col = c0 + cc * 8;
+  const bool col_ok = col < cols;
+
+#pragma unroll
+  for (int i = 0; i < kMxIters; ++i) {
+    u32x4 v[4];
+    uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = A + 128 * i + 4 * rs + k;       // output row
+      const int in = lo + (r - plo);                 // input row (pad rows: in >= hi)
+      const bool ok = col_ok && r < r_end && in < hi;
+      v[k] = ok ? *reinterpret_cast<const u32x4*>(x + (int64_t)in * cols + col) : u32x4{0, 0, 0, 0};
+      m[0] = pk_absmax_bf16(m[0], v[k].x);
+      m[1] = pk_absmax_bf16(m[1], v[k].y);
+      m[2] = pk_absmax_bf16(m[2], v[k].z);
+      m[3] = pk_absmax_bf16(m[3], v[k].w);
+    }
+    // the 32-row block of this wave: reduce over the 8 row slots (lanes 8 apart)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int off = 8; off <= 32; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)m[p], off, 64);
+        m[p] = (max(m[p] & 0xFFFFu, o & 0xFFFFu)) | (max(m[p] >> 16, o >> 16) << 16);
+      }
+    }
+    float s[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t a16 = (m[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+      const int X = mx_exponent(a16 << 16, RULE);
+      s[k] = exp2_neg(X);
+      if (lane < 8) s_x[(cc * 8 + k) * 16 + 4 * i + w] = (uint8_t)(X + 127);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t word = quant4<0>(col_of(v[0], k), col_of(v[1], k), col_of(v[2], k), col_of(v[3], k), s[k]);
+      tile_put4(tile, cc * 8 + k, 128 * i + 4 * rs, word);
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int ci = p * 8 + (t >> 5), sg = t & 31;
+    const int c = c0 + ci, R0 = A + 16 * sg;
+    if (c < cols && R0 < r_end)
+      *reinterpret_cast<u32x4*>(qb + (int64_t)c * ld_q + R0) = tile_get16(tile, ci, 16 * sg);
+  }
+  // scales: column t/4, blocks 4*(t%4) .. +3 of this tile
+  {
+    const int ci = t >> 2, c = c0 + ci;
+    const int nb = (r_end - A) >> 5;
+    if (c < cols) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int b = 4 * (t & 3) + b4;
+        if (b < nb) sb[(int64_t)c * ld_s + (A >> 5) + b] = s_x[ci * 16 + b];
+      }
+    }
+  }
+}
+
+int64_t mx_rows_units_bound(int64_t batch, int64_t rows, const int32_t* offs, int32_t n_groups, int64_t rows_pad) {
+  if (offs) return (rows_pad + kTileRows - 1) / kTileRows + n_groups + 1;
+  return batch * ((rows + kTileRows - 1) / kTileRows);
+}
+
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int axis,
+                              const int32_t* offs, int32_t n_groups, int rule, uint8_t* q, uint8_t* sc,
+                              int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st) {
+  if (axis == 1) {
+    const int64_t n_chunks = batch * rows * cols / 8;
+    if (n_chunks == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n_chunks + 255) / 256, 1 << 20);
+    if (rule == 0)
+      hipLaunchKernelGGL(mx_lastdim_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, x, n_chunks, q, sc);
+    else
+      hipLaunchKernelGGL(mx_lastdim_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, x, n_chunks, q, sc);
+    return hipGetLastError();
+  }
+  if (cols == 0) {
+    if (offs == nullptr || offs_pad_out == nullptr) return hipSuccess;
+  }
+  const int n_strips = (int)std::max<int64_t>((cols + kTileCols - 1) / kTileCols, 1);
+  const int64_t units = mx_rows_units_bound(batch, rows, offs, n_groups, rows_pad);
+  if (units == 0) return hipSuccess;
+  const dim3 grid((unsigned)(units * n_strips));
+  if (offs) {
+    auto k = rule == 0 ? mx_rows_kernel<0, true> : mx_rows_kernel<1, true>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, (int64_t)1, (int)rows, (int)cols, offs, n_groups, q, sc,
+                       rows_pad, offs_pad_out, n_strips);
+  } else {
+    auto k = rule == 0 ? mx_rows_kernel<0, false> : mx_rows_kernel<1, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, batch, (int)rows, (int)cols, nullptr, 0, q, sc, rows,
+                       nullptr, n_strips);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8moe

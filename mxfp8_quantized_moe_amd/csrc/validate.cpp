@@ -1,0 +1,147 @@
+// Host-only validation of the C ABI arguments (see include/fp8moe.h for the
+// contract of each entry point).  No HIP header, no HIP call.
+#include "validate.hpp"
+
+#include <stdint.h>
+
+#include "../../include/fp8moe.h"
+
+namespace fp8moe {
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool need(const void* p, int64_t elems) { return elems == 0 || p != nullptr; }
+
+// a*b without overflow for non-negative operands; -1 if it would exceed int64.
+int64_t mul(int64_t a, int64_t b) {
+  if (a == 0 || b == 0) return 0;
+  if (a > INT64_MAX / b) return -1;
+  return a * b;
+}
+
+}  // namespace
+
+int64_t mx_rows_bound(int64_t rows, int32_t n_groups) {
+  if (rows < 0 || n_groups < 0) return -1;
+  return (rows + 31LL * n_groups + 31) / 32 * 32;
+}
+
+int check_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int codec, const void* q,
+                           const void* scale) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (rows < 0 || cols < 0 || ld_x < cols || rows > kI32Max * 256LL || cols > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t n = mul(rows, cols);
+  if (n < 0 || mul(rows, ld_x) < 0) return FP8MOE_ERR_SHAPE;
+  if (!need(x, n) || !need(q, n) || !need(scale, rows)) return FP8MOE_ERR_NULL;
+  if (cols % 8 || ld_x % 8 || !aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_quantize_colwise(const void* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+                           int32_t n_groups, int codec, const void* q_t, int64_t ld_q, const void* scale) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (batch < 1 || rows < 0 || cols < 0 || ld_q < rows) return FP8MOE_ERR_SHAPE;
+  if (offs && (batch != 1 || n_groups < 1)) return FP8MOE_ERR_SHAPE;
+  if (rows > kI32Max / 2 || cols > kI32Max / 2 || n_groups > (1 << 20)) return FP8MOE_ERR_SHAPE;
+  const int64_t groups = offs ? n_groups : batch;
+  const int64_t n_in = mul(mul(batch, rows), cols);
+  const int64_t n_out = mul(mul(batch, cols), ld_q);
+  if (n_in < 0 || n_out < 0 || mul(groups, cols) < 0) return FP8MOE_ERR_SHAPE;
+  // grid: units x 64-column strips must fit a 1D launch
+  const int64_t units = offs ? (rows + 16LL * n_groups + 511) / 512 + n_groups : batch * ((rows + 511) / 512 + 1);
+  if (mul(units, (cols + 63) / 64) < 0 || mul(units, (cols + 63) / 64) > kI32Max) return FP8MOE_ERR_SHAPE;
+  if (!need(x, n_in) || !need(q_t, mul(mul(batch, cols), rows)) || !need(scale, mul(groups, cols)))
+    return FP8MOE_ERR_NULL;
+  if (cols % 8 || ld_q % 16 || !aligned(x, 16) || !aligned(q_t, 16) || !aligned(scale, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,
+                      int32_t n_groups, int rule, const void* q, const void* sc, int64_t rows_pad,
+                      const int32_t* offs_pad_out) {
+  if (rule != FP8MOE_MX_FLOOR_OCP && rule != FP8MOE_MX_CEIL) return FP8MOE_ERR_ENUM;
+  if (axis != 0 && axis != 1) return FP8MOE_ERR_ENUM;
+  if (batch < 1 || rows < 0 || cols < 0) return FP8MOE_ERR_SHAPE;
+  if (rows > kI32Max / 2 || cols > kI32Max / 2) return FP8MOE_ERR_SHAPE;
+  const int64_t n_in = mul(mul(batch, rows), cols);
+  if (n_in < 0) return FP8MOE_ERR_SHAPE;
+  if (axis == 1) {
+    if (offs) return FP8MOE_ERR_UNSUPPORTED;
+    if (!need(x, n_in) || !need(q, n_in) || !need(sc, n_in)) return FP8MOE_ERR_NULL;
+    if (cols % 32 || !aligned(x, 16) || !aligned(q, 16)) return FP8MOE_ERR_ALIGN;
+    return FP8MOE_OK;
+  }
+  if (cols % 8 || !aligned(x, 16) || !aligned(q, 16)) return FP8MOE_ERR_ALIGN;
+  if (offs == nullptr) {
+    if (rows % 32) return FP8MOE_ERR_ALIGN;
+    if (mul(batch * ((rows + 511) / 512), (cols + 63) / 64) > kI32Max) return FP8MOE_ERR_SHAPE;
+    if (!need(x, n_in) || !need(q, n_in) || !need(sc, n_in)) return FP8MOE_ERR_NULL;
+    return FP8MOE_OK;
+  }
+  if (batch != 1 || n_groups < 1 || n_groups > (1 << 20)) return FP8MOE_ERR_SHAPE;
+  if (rows_pad % 32) return FP8MOE_ERR_ALIGN;
+  if (rows_pad < mx_rows_bound(rows, n_groups) || rows_pad > kI32Max / 2) return FP8MOE_ERR_SHAPE;
+  const int64_t n_out = mul(cols, rows_pad);
+  if (n_out < 0) return FP8MOE_ERR_SHAPE;
+  const int64_t units = (rows_pad + 511) / 512 + n_groups + 1;
+  if (mul(units, (cols + 63) / 64 + 1) > kI32Max) return FP8MOE_ERR_SHAPE;
+  if (!need(x, n_in) || !need(q, n_out) || !need(sc, n_out)) return FP8MOE_ERR_NULL;
+  return FP8MOE_OK;
+}
+
+int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const void* b, int b_fmt,
+                     const void* sb, int scale_kind, const int32_t* offs, int32_t n_groups, int64_t M,
+                     int64_t N, int64_t K, const void* out, int out_dtype) {
+  if (mode != FP8MOE_GROUPED_M && mode != FP8MOE_GROUPED_K) return FP8MOE_ERR_ENUM;
+  if (a_fmt < 0 || a_fmt > 2 || b_fmt < 0 || b_fmt > 2) return FP8MOE_ERR_ENUM;
+  if (scale_kind < 0 || scale_kind > 2) return FP8MOE_ERR_ENUM;
+  if (out_dtype != FP8MOE_OUT_BF16 && out_dtype != FP8MOE_OUT_F32) return FP8MOE_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || n_groups < 1 || n_groups > (1 << 20)) return FP8MOE_ERR_SHAPE;
+  if (M > kI32Max / 2 || N > kI32Max / 2 || K > kI32Max / 2) return FP8MOE_ERR_SHAPE;
+  if (offs == nullptr && n_groups != 1) return FP8MOE_ERR_NULL;
+  const bool a_bf16 = a_fmt == FP8MOE_OPD_BF16, b_bf16 = b_fmt == FP8MOE_OPD_BF16;
+  if (a_bf16 != b_bf16) return FP8MOE_ERR_UNSUPPORTED;
+  if (a_bf16 && (scale_kind != FP8MOE_SCALE_NONE || mode != FP8MOE_GROUPED_K)) return FP8MOE_ERR_UNSUPPORTED;
+  if (!a_bf16 && scale_kind == FP8MOE_SCALE_NONE) return FP8MOE_ERR_UNSUPPORTED;
+  if (scale_kind == FP8MOE_SCALE_E8M0 && (a_fmt != FP8MOE_OPD_E4M3FN || b_fmt != FP8MOE_OPD_E4M3FN))
+    return FP8MOE_ERR_UNSUPPORTED;
+  const int64_t E = n_groups;
+  int64_t na, nb, no, nsa, nsb;
+  if (mode == FP8MOE_GROUPED_M) {
+    na = mul(M, K); nb = mul(mul(E, N), K); no = mul(M, N);
+    nsa = scale_kind == FP8MOE_SCALE_E8M0 ? mul(M, K / 32) : M;
+    nsb = scale_kind == FP8MOE_SCALE_E8M0 ? mul(mul(E, N), K / 32) : mul(E, N);
+  } else {
+    na = mul(N, M); nb = mul(K, M); no = mul(mul(E, N), K);
+    nsa = scale_kind == FP8MOE_SCALE_E8M0 ? mul(N, M / 32) : mul(E, N);
+    nsb = scale_kind == FP8MOE_SCALE_E8M0 ? mul(K, M / 32) : mul(E, K);
+  }
+  if (na < 0 || nb < 0 || no < 0 || nsa < 0 || nsb < 0 || mul(no, 4) < 0) return FP8MOE_ERR_SHAPE;
+  if (!need(a, na) || !need(b, nb) || !need(out, no)) return FP8MOE_ERR_NULL;
+  if (scale_kind != FP8MOE_SCALE_NONE && (!need(sa, nsa) || !need(sb, nsb))) return FP8MOE_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16)) return FP8MOE_ERR_ALIGN;
+  if (scale_kind == FP8MOE_SCALE_F32 && (!aligned(sa, 4) || !aligned(sb, 4))) return FP8MOE_ERR_ALIGN;
+  if (a_bf16) {
+    if (N % 8 || K % 8 || M % 8) return FP8MOE_ERR_ALIGN;
+  } else if (mode == FP8MOE_GROUPED_M) {
+    if (K % 16) return FP8MOE_ERR_ALIGN;
+    if (scale_kind == FP8MOE_SCALE_E8M0 && K % 32) return FP8MOE_ERR_ALIGN;
+  } else {
+    if (M % 16) return FP8MOE_ERR_ALIGN;
+    if (scale_kind == FP8MOE_SCALE_E8M0 && M % 32) return FP8MOE_ERR_ALIGN;
+  }
+  return FP8MOE_OK;
+}
+
+int check_encode_f32(const void* y, int64_t n, int codec, const void* q) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (n < 0 || n > kI32Max * 64LL) return FP8MOE_ERR_SHAPE;
+  if (!need(y, n) || !need(q, n)) return FP8MOE_ERR_NULL;
+  if (!aligned(y, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+}  // namespace fp8moe

@@ -37,6 +37,6 @@ from .quant import (EPS, bf16_to_f32, quantize_rowwise, quantize_colwise_grouped
                     mx_rows_bound)
 from .gemm import (group_bounds, mm_grouped_m, mm_grouped_k, mm_grouped_m_mx,
                    mm_grouped_k_mx, mm_grouped_k_bf16, error_bounds_m,
-                   error_bounds_k)
+                   error_bounds_k, ACC_FP32, ACC_FP8_MFMA)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -38,7 +38,8 @@ from .codec import decode, e8m0_decode
 from .quant import bf16_to_f32, group_bounds
 
 __all__ = ["group_bounds", "mm_grouped_m", "mm_grouped_k", "mm_grouped_m_mx",
-           "mm_grouped_k_mx", "mm_grouped_k_bf16", "error_bounds_m", "error_bounds_k"]
+           "mm_grouped_k_mx", "mm_grouped_k_bf16", "error_bounds_m", "error_bounds_k",
+           "ACC_FP32", "ACC_FP8_MFMA"]
 
 
 def mm_grouped_m(qa, sa, qb, sb, offs, a_codec: int, b_codec: int) -> np.ndarray:
@@ -151,19 +152,32 @@ def mm_grouped_k_bf16(a_bits, b_bits, offs) -> np.ndarray:
 
 # ------------------------------------------------------------ acceptance bounds
 
-def _bounds(Ad, Bd, K_eff):
+# Relative accumulation error allowed by the diagnostic bound, per unit of sum|a*b|:
+#  * "fp32": sequential IEEE fp32 accumulation of exact products, K * 2**-23.
+#  * "fp8_mfma": 2**-10.  The FP8 matrix-core instructions add the products of
+#    one instruction with less than fp32 precision (measured on gfx950 over
+#    these tests: |err| / sum|a*b| at most about 1.4e-4 = 2**-12.8); 2**-10
+#    leaves a margin and is still about 1000x below the error of a dropped
+#    term or a wrong scale.  By Cauchy-Schwarz, sum|a*b| <= |a||b|, so this
+#    diagnostic is always tighter than the 1e-2 |a||b| contract bound.
+ACC_FP32 = "fp32"
+ACC_FP8_MFMA = "fp8_mfma"
+
+
+def _bounds(Ad, Bd, K_eff, acc):
     """Contract bound 1e-2*|a_row|*|b_col| and the tighter diagnostic
-    2**-8*|ref| + K*2**-23*sum|a*b| for dense dequantized Ad [m, K], Bd [n, K]."""
+    2**-8*|ref| + rel_acc*sum|a*b| for dense dequantized Ad [m, K], Bd [n, K]."""
     na = np.sqrt((Ad * Ad).sum(axis=1))
     nb = np.sqrt((Bd * Bd).sum(axis=1))
     contract = 1e-2 * na[:, None] * nb[None, :]
     absdot = np.abs(Ad) @ np.abs(Bd).T
     ref = Ad @ Bd.T
-    tight = 2.0 ** -8 * np.abs(ref) + max(K_eff, 1) * 2.0 ** -23 * absdot
+    rel = max(K_eff, 1) * 2.0 ** -23 if acc == ACC_FP32 else 2.0 ** -10
+    tight = 2.0 ** -8 * np.abs(ref) + rel * absdot
     return contract, tight
 
 
-def error_bounds_m(A_deq, B_deq, offs):
+def error_bounds_m(A_deq, B_deq, offs, acc=ACC_FP32):
     """Per-element bounds for GROUPED_M given dequantized A [M, K] and B [E, N, K]."""
     M, K = A_deq.shape
     E, N, _ = B_deq.shape
@@ -173,13 +187,13 @@ def error_bounds_m(A_deq, B_deq, offs):
     for e in range(E):
         if hi[e] == lo[e]:
             continue
-        c, t = _bounds(A_deq[lo[e]:hi[e]], B_deq[e], K)
+        c, t = _bounds(A_deq[lo[e]:hi[e]], B_deq[e], K, acc)
         contract[lo[e]:hi[e]] = c
         tight[lo[e]:hi[e]] = t
     return contract, tight
 
 
-def error_bounds_k(A_deq_t, B_deq_t, offs):
+def error_bounds_k(A_deq_t, B_deq_t, offs, acc=ACC_FP32):
     """Per-element bounds for GROUPED_K given dequantized A phys [N, M] and B phys [K, M]
     (group scales already applied per column range)."""
     N, M = A_deq_t.shape
@@ -191,7 +205,7 @@ def error_bounds_k(A_deq_t, B_deq_t, offs):
     for e in range(E):
         if hi[e] == lo[e]:
             continue
-        c, t = _bounds(A_deq_t[:, lo[e]:hi[e]], B_deq_t[:, lo[e]:hi[e]], int(hi[e] - lo[e]))
+        c, t = _bounds(A_deq_t[:, lo[e]:hi[e]], B_deq_t[:, lo[e]:hi[e]], int(hi[e] - lo[e]), acc)
         contract[e] = c
         tight[e] = t
     return contract, tight

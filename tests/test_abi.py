@@ -1,0 +1,137 @@
+"""C ABI tests that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+Only argument combinations that fail validation are passed here; a call that
+passes validation would enqueue GPU work.  Fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp8_quantized_moe_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8moe.h")
+
+P = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+MIS = 0x10001        # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n)
+    nm = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf" T {n}$", nm, flags=re.M), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.fp8moe_status_string(0) == b"ok"
+    for s in range(1, 8):
+        assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.fp8moe_status_string(99) == b"unknown status"
+    assert lib.fp8moe_version() == 100
+
+
+def test_rows_bound(lib):
+    assert lib.quantize_mx_rows_bound(75, 4) == 224
+    assert lib.quantize_mx_rows_bound(16384, 16) == 16896
+    assert lib.quantize_mx_rows_bound(0, 1) == 32
+    assert lib.quantize_mx_rows_bound(-1, 1) == -1
+
+
+def test_rowwise_rejections(lib):
+    f = lib.quantize_rowwise
+    assert f(P, 4, 16, 16, 7, P, P, None) == L.ERR_ENUM
+    assert f(P, -1, 16, 16, 0, P, P, None) == L.ERR_SHAPE
+    assert f(P, 4, 16, 8, 0, P, P, None) == L.ERR_SHAPE            # ld_x < cols
+    assert f(None, 4, 16, 16, 0, P, P, None) == L.ERR_NULL
+    assert f(P, 4, 16, 16, 0, None, P, None) == L.ERR_NULL
+    assert f(P, 4, 16, 16, 0, P, None, None) == L.ERR_NULL
+    assert f(P, 4, 12, 16, 0, P, P, None) == L.ERR_ALIGN            # cols % 8
+    assert f(P, 4, 16, 20, 0, P, P, None) == L.ERR_ALIGN            # ld_x % 8
+    assert f(MIS, 4, 16, 16, 0, P, P, None) == L.ERR_ALIGN
+    assert f(P, 4, 16, 16, 0, MIS, P, None) == L.ERR_ALIGN
+    assert f(P, 4, 16, 16, 0, P, P + 2, None) == L.ERR_ALIGN
+
+
+def test_colwise_rejections(lib):
+    f = lib.quantize_colwise
+    assert f(P, 1, 64, 16, P, 4, 3, P, 64, P, None) == L.ERR_ENUM
+    assert f(P, 0, 64, 16, None, 0, 0, P, 64, P, None) == L.ERR_SHAPE      # batch 0
+    assert f(P, 2, 64, 16, P, 4, 0, P, 64, P, None) == L.ERR_SHAPE         # offs needs batch 1
+    assert f(P, 1, 64, 16, P, 0, 0, P, 64, P, None) == L.ERR_SHAPE         # no groups
+    assert f(P, 1, 64, 16, P, 4, 0, P, 32, P, None) == L.ERR_SHAPE         # ld_q < rows
+    assert f(None, 1, 64, 16, P, 4, 0, P, 64, P, None) == L.ERR_NULL
+    assert f(P, 1, 64, 12, P, 4, 0, P, 64, P, None) == L.ERR_ALIGN         # cols % 8
+    assert f(P, 1, 64, 16, P, 4, 0, P, 72, P, None) == L.ERR_ALIGN         # ld_q % 16
+    assert f(P, 1, 64, 16, P, 4, 0, MIS, 64, P, None) == L.ERR_ALIGN
+
+
+def test_mx_rejections(lib):
+    f = lib.quantize_mx
+    assert f(P, 1, 64, 64, 1, None, 0, 5, P, P, 0, None, None) == L.ERR_ENUM       # rule
+    assert f(P, 1, 64, 64, 2, None, 0, 0, P, P, 0, None, None) == L.ERR_ENUM       # axis
+    assert f(P, 1, 64, 48, 1, None, 0, 0, P, P, 0, None, None) == L.ERR_ALIGN      # cols % 32
+    assert f(P, 1, 64, 64, 1, P, 4, 0, P, P, 0, None, None) == L.ERR_UNSUPPORTED   # offs on axis 1
+    assert f(P, 1, 40, 64, 0, None, 0, 0, P, P, 0, None, None) == L.ERR_ALIGN      # rows % 32
+    assert f(P, 1, 75, 64, 0, P, 4, 0, P, P, 192, P, None) == L.ERR_SHAPE          # rows_pad < bound
+    assert f(P, 1, 75, 64, 0, P, 4, 0, P, P, 230, P, None) == L.ERR_ALIGN          # rows_pad % 32
+    assert f(P, 2, 75, 64, 0, P, 4, 0, P, P, 224, P, None) == L.ERR_SHAPE          # batch with offs
+    assert f(P, 1, 75, 64, 0, P, 4, 0, None, P, 224, P, None) == L.ERR_NULL
+
+
+def test_gemm_rejections(lib):
+    f = lib.grouped_mm_scaled
+    ok = dict(mode=0, a=P, af=0, sa=P, b=P, bf=0, sb=P, sk=0, offs=P, E=4, M=64, N=64, K=64, out=P, od=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["mode"], a["a"], a["af"], a["sa"], a["b"], a["bf"], a["sb"], a["sk"], a["offs"], a["E"],
+                 a["M"], a["N"], a["K"], a["out"], a["od"], None)
+
+    assert call(mode=2) == L.ERR_ENUM
+    assert call(af=3) == L.ERR_ENUM
+    assert call(sk=4) == L.ERR_ENUM
+    assert call(od=2) == L.ERR_ENUM
+    assert call(M=-1) == L.ERR_SHAPE
+    assert call(E=0) == L.ERR_SHAPE
+    assert call(offs=None) == L.ERR_NULL                  # several groups need offsets
+    assert call(a=None) == L.ERR_NULL
+    assert call(sa=None) == L.ERR_NULL
+    assert call(af=2) == L.ERR_UNSUPPORTED                # bf16 x fp8
+    assert call(af=2, bf=2, sk=2) == L.ERR_UNSUPPORTED    # bf16 only for GROUPED_K
+    assert call(sk=2) == L.ERR_UNSUPPORTED                # fp8 without scales
+    assert call(sk=1, af=1) == L.ERR_UNSUPPORTED          # e8m0 needs e4m3fn
+    assert call(K=40) == L.ERR_ALIGN                      # K % 16 (GROUPED_M)
+    assert call(sk=1, K=48) == L.ERR_ALIGN                # K % 32 for e8m0
+    assert call(mode=1, M=40) == L.ERR_ALIGN              # M % 16 (GROUPED_K)
+    assert call(out=MIS) == L.ERR_ALIGN
+
+
+def test_encode_rejections(lib):
+    assert lib.fp8moe_encode_f32(P, 16, 2, P, None) == L.ERR_ENUM
+    assert lib.fp8moe_encode_f32(P, -1, 0, P, None) == L.ERR_SHAPE
+    assert lib.fp8moe_encode_f32(None, 16, 0, P, None) == L.ERR_NULL
+    assert lib.fp8moe_encode_f32(P + 2, 16, 0, P, None) == L.ERR_ALIGN
+
+
+def test_python_binding_raises_on_bad_arguments():
+    import mxfp8_quantized_moe_amd as fm
+    with pytest.raises(fm.Fp8MoeError):
+        L.check("quantize_rowwise", L.lib().quantize_rowwise(P, 4, 12, 16, 0, P, P, None))

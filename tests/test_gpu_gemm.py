@@ -1,0 +1,317 @@
+"""GPU parity of the grouped GEMMs against the fp64 oracle.
+
+Operands are the GPU's own quantized tensors (their bytes are checked
+bit-exactly by test_gpu_quant), fed to both sides, so GEMM and quantization
+are tested independently.  Acceptance per element:
+  contract:   |out - ref| <= 1e-2 * ||a_row|| * ||b_col||   (dequantized operands)
+  diagnostic: |out - ref| <= 2^-8 |ref| + K * 2^-23 * sum|a*b|
+Rows of GROUPED_M outside every group must keep their sentinel; empty groups
+of GROUPED_K must be exact zeros.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp8_quantized_moe_amd as fm
+from mxfp8_quantized_moe_amd import synth
+from gpu_helpers import DEV, note, bf16_dev, i32_dev, host, bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+SENT_BF16 = 0x7FC1      # a NaN pattern the kernel never writes
+
+
+def _out_host(t):
+    h = host(t)
+    if t.dtype == torch.bfloat16:
+        return h, bf16_bits_to_f64(h)
+    return h.view(np.uint32), h.astype(np.float64)
+
+
+def check(got, ref, contract, tight, what):
+    """got/ref/bounds float64; NaN in ref marks positions that are not compared."""
+    fin = ~np.isnan(ref)
+    err = np.abs(got[fin] - ref[fin])
+    assert not np.any(np.isnan(got[fin])), f"{what}: NaN in output"
+    bad_c = err > contract[fin]
+    bad_t = err > tight[fin]
+    assert not bad_c.any(), f"{what}: {bad_c.sum()} elements beyond the contract bound (max err {err.max():.3e})"
+    assert not bad_t.any(), f"{what}: {bad_t.sum()} elements beyond the diagnostic bound (max err {err.max():.3e})"
+
+
+def gm_case(x_bits, w_bits, offs, codec_a=0, codec_b=0, out_dtype=0, name=""):
+    """Quantize on the GPU (rowwise), run GROUPED_M, compare with the oracle."""
+    M, K = x_bits.shape
+    E, N, _ = w_bits.shape
+    note(f"GROUPED_M {name} M={M} N={N} K={K} E={E} codecs={codec_a},{codec_b} out={out_dtype}")
+    qa, sa = fm.quantize_rowwise(bf16_dev(x_bits), codec_a)
+    qb, sb = fm.quantize_rowwise(bf16_dev(w_bits.reshape(E * N, K)), codec_b)
+    odt = torch.bfloat16 if out_dtype == 0 else torch.float32
+    out = torch.empty((M, N), dtype=odt, device=DEV)
+    if out_dtype == 0:
+        out.view(torch.int16).fill_(SENT_BF16)
+    else:
+        out.fill_(float("nan"))
+    fmt = {0: fm.OPD_E4M3FN, 1: fm.OPD_E4M3FNUZ}
+    fm.grouped_mm_scaled(fm.GROUPED_M, qa, fmt[codec_a], sa, qb, fmt[codec_b], sb, fm.SCALE_F32,
+                         i32_dev(offs), E, M, N, K, out=out, out_dtype=out_dtype)
+    raw, got = _out_host(out)
+    qa_h, sa_h, qb_h, sb_h = host(qa), host(sa), host(qb).reshape(E, N, K), host(sb).reshape(E, N)
+    ref = oracle.mm_grouped_m(qa_h, sa_h, qb_h, sb_h, offs, codec_a, codec_b)
+    A = oracle.decode(qa_h, codec_a) / sa_h[:, None].astype(np.float64)
+    B = oracle.decode(qb_h, codec_b) / sb_h[..., None].astype(np.float64)
+    acc = oracle.ACC_FP8_MFMA if codec_a == 0 and codec_b == 0 else oracle.ACC_FP32
+    contract, tight = oracle.error_bounds_m(A, B, offs, acc)
+    check(got, ref, contract, tight, f"GROUPED_M {name}")
+    rows_out = np.isnan(ref[:, 0]) if N else np.zeros(M, bool)
+    if out_dtype == 0:
+        assert np.all(raw[rows_out] == SENT_BF16), "wrote rows outside every group"
+    else:
+        assert np.all(np.isnan(got[rows_out])), "wrote rows outside every group"
+
+
+GM_CASES = {
+    "cfg1": lambda: (synth.make_x(synth.WORKLOADS[1]), synth.make_w1(synth.WORKLOADS[1]), synth.WORKLOADS[1].offs),
+    "ragged": lambda: (synth.normal_bf16(11, (700, 384), 1.0, 0.01, 50.0), synth.normal_bf16(12, (9, 320, 384), 0.02),
+                       synth.offsets_from_counts(synth.random_counts(13, 680, 9))),
+    "dense": lambda: (synth.normal_bf16(14, (600, 512), 1.0), synth.normal_bf16(15, (1, 300, 512), 0.02),
+                      np.array([600], np.int32)),
+    "malformed": lambda: (synth.normal_bf16(16, (300, 128), 1.0), synth.normal_bf16(17, (4, 64, 128), 0.02),
+                          np.array([100, 40, 250, 999], np.int32)),
+}
+
+
+@pytest.mark.parametrize("case", list(GM_CASES))
+def test_grouped_m_fp8(case):
+    x, w, offs = GM_CASES[case]()
+    gm_case(x, w, offs, name=case)
+
+
+@pytest.mark.parametrize("codecs", [(1, 1), (0, 1), (1, 0)])
+def test_grouped_m_fnuz(codecs):
+    x, w, offs = GM_CASES["ragged"]()
+    gm_case(x, w, offs, *codecs, name="fnuz")
+
+
+def test_grouped_m_f32_out():
+    x, w, offs = GM_CASES["cfg1"]()
+    gm_case(x, w, offs, out_dtype=1, name="f32out")
+
+
+def test_grouped_m_zero_rows():
+    note("GROUPED_M M=0")
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, torch.empty(0, 64, dtype=torch.uint8, device=DEV), 0,
+                               torch.empty(0, device=DEV), torch.zeros(2, 16, 64, dtype=torch.uint8, device=DEV), 0,
+                               torch.ones(2, 16, device=DEV), fm.SCALE_F32, i32_dev([0, 0]), 2, 0, 16, 64)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 16)
+
+
+# ------------------------------------------------------------------ GROUPED_K
+
+def gk_case(dy_bits, x_bits, offs, codec_a=0, codec_b=0, out_dtype=0, name=""):
+    M, N = dy_bits.shape
+    K = x_bits.shape[1]
+    E = len(offs)
+    note(f"GROUPED_K {name} M={M} N={N} K={K} E={E} codecs={codec_a},{codec_b}")
+    qa, sa = fm.quantize_colwise(bf16_dev(dy_bits), i32_dev(offs), codec_a)
+    qb, sb = fm.quantize_colwise(bf16_dev(x_bits), i32_dev(offs), codec_b)
+    fmt = {0: fm.OPD_E4M3FN, 1: fm.OPD_E4M3FNUZ}
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, fmt[codec_a], sa, qb, fmt[codec_b], sb, fm.SCALE_F32,
+                               i32_dev(offs), E, M, N, K, out_dtype=out_dtype)
+    _, got = _out_host(out)
+    qa_h, sa_h, qb_h, sb_h = host(qa), host(sa), host(qb), host(sb)
+    ref = oracle.mm_grouped_k(qa_h, sa_h, qb_h, sb_h, offs, codec_a, codec_b)
+    lo, hi = oracle.group_bounds(offs, M)
+    A = np.zeros((N, M))
+    B = np.zeros((K, M))
+    for e in range(E):
+        A[:, lo[e]:hi[e]] = oracle.decode(qa_h[:, lo[e]:hi[e]], codec_a) / sa_h[e][:, None].astype(np.float64)
+        B[:, lo[e]:hi[e]] = oracle.decode(qb_h[:, lo[e]:hi[e]], codec_b) / sb_h[e][:, None].astype(np.float64)
+    acc = oracle.ACC_FP8_MFMA if codec_a == 0 and codec_b == 0 else oracle.ACC_FP32
+    contract, tight = oracle.error_bounds_k(A, B, offs, acc)
+    check(got, ref, contract, tight, f"GROUPED_K {name}")
+    for e in range(E):
+        if hi[e] == lo[e]:
+            assert not np.any(got[e]), "empty group must be exact zeros"
+
+
+GK_CASES = {
+    "cfg1": lambda: (synth.normal_bf16(21, (512, 512), 1e-3), synth.make_x(synth.WORKLOADS[1]),
+                     synth.WORKLOADS[1].offs),
+    "ragged": lambda: (synth.normal_bf16(22, (1200, 320), 1e-3), synth.normal_bf16(23, (1200, 272), 1.0, 0.01, 50.0),
+                       synth.offsets_from_counts(synth.random_counts(24, 1150, 7))),
+    "dense": lambda: (synth.normal_bf16(25, (1024, 256), 1e-3), synth.normal_bf16(26, (1024, 512), 1.0),
+                      np.array([1024], np.int32)),
+}
+
+
+@pytest.mark.parametrize("case", list(GK_CASES))
+def test_grouped_k_fp8(case):
+    dy, x, offs = GK_CASES[case]()
+    gk_case(dy, x, offs, name=case)
+
+
+def test_grouped_k_fnuz():
+    dy, x, offs = GK_CASES["ragged"]()
+    gk_case(dy, x, offs, 1, 1, name="fnuz")
+
+
+def test_grouped_k_bf16_plus_gw():
+    dy, x, offs = GK_CASES["ragged"]()
+    M, N = dy.shape
+    K = x.shape[1]
+    E = len(offs)
+    note(f"GROUPED_K bf16 M={M} N={N} K={K}")
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, bf16_dev(dy), fm.OPD_BF16, None, bf16_dev(x), fm.OPD_BF16, None,
+                               fm.SCALE_NONE, i32_dev(offs), E, M, N, K)
+    _, got = _out_host(out)
+    ref = oracle.mm_grouped_k_bf16(dy, x, offs)
+    lo, hi = oracle.group_bounds(offs, M)
+    A = bf16_bits_to_f64(np.ascontiguousarray(dy.T))
+    B = bf16_bits_to_f64(np.ascontiguousarray(x.T))
+    contract, tight = oracle.error_bounds_k(A, B, offs)
+    check(got, ref, contract, tight, "GROUPED_K bf16")
+
+
+# ------------------------------------------------------------------ MXFP8
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_grouped_m_mx(rule):
+    x = synth.normal_bf16(31, (900, 512), 1.0, 0.01, 30.0)
+    w = synth.normal_bf16(32, (5, 288, 512), 0.02)
+    offs = synth.offsets_from_counts(synth.random_counts(33, 880, 5))
+    M, K = x.shape
+    E, N, _ = w.shape
+    note(f"GROUPED_M MX rule={rule}")
+    qa, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(w.reshape(E * N, K)), axis=1, rule=rule)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(SENT_BF16)
+    fm.grouped_mm_scaled(fm.GROUPED_M, qa, fm.OPD_E4M3FN, xa, qb, fm.OPD_E4M3FN, xb, fm.SCALE_E8M0, i32_dev(offs),
+                         E, M, N, K, out=out)
+    raw, got = _out_host(out)
+    qa_h, xa_h = host(qa), host(xa)
+    qb_h, xb_h = host(qb).reshape(E, N, K), host(xb).reshape(E, N, K // 32)
+    ref = oracle.mm_grouped_m_mx(qa_h, xa_h, qb_h, xb_h, offs)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, "GROUPED_M MX")
+    assert np.all(raw[np.isnan(ref[:, 0])] == SENT_BF16)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_grouped_k_mx(rule):
+    dy = synth.normal_bf16(34, (1000, 320), 1e-3)
+    x = synth.normal_bf16(35, (1000, 288), 1.0, 0.01, 30.0)
+    offs = synth.offsets_from_counts(synth.random_counts(36, 990, 6))
+    M, N = dy.shape
+    K = x.shape[1]
+    E = len(offs)
+    Mp = fm.quantize_mx_rows_bound(M, E)
+    note(f"GROUPED_K MX rule={rule} Mp={Mp}")
+    qa, xa, op = fm.quantize_mx(bf16_dev(dy), axis=0, offs=i32_dev(offs), rule=rule, rows_pad=Mp)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=rule, rows_pad=Mp)
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, fm.OPD_E4M3FN, xa, qb, fm.OPD_E4M3FN, xb, fm.SCALE_E8M0, op, E,
+                               Mp, N, K)
+    _, got = _out_host(out)
+    qa_h, xa_h, qb_h, xb_h, op_h = host(qa), host(xa), host(qb), host(xb), host(op)
+    ref = oracle.mm_grouped_k_mx(qa_h, xa_h, qb_h, xb_h, op_h)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_k(A, B, op_h, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, "GROUPED_K MX")
+
+
+# ------------------------------------------------------------------ full size, sampled rows
+
+def _rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(k, n), replace=False)]))
+
+
+def _check_rows_by_expert(got, rows, offs, M, per_expert_ref, what):
+    """Compare sampled output rows, one oracle call per expert that owns sampled rows."""
+    lo, hi = oracle.group_bounds(offs, M)
+    grp = np.searchsorted(hi, rows, side="right")
+    for e in np.unique(grp):
+        sel = rows[grp == e]
+        ref, contract, tight = per_expert_ref(e, sel)
+        check(got[sel], ref, contract, tight, f"{what} expert {e}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_grouped_m_full_size_sampled(cfg):
+    w = synth.WORKLOADS[cfg]
+    x = synth.make_x(w)
+    wt = synth.make_w1(w)
+    offs = w.offs
+    M, K = x.shape
+    E, N, _ = wt.shape
+    note(f"GROUPED_M full cfg={cfg} M={M} N={N} K={K}")
+    qa, sa = fm.quantize_rowwise(bf16_dev(x), 0)
+    qb, sb = fm.quantize_rowwise(bf16_dev(wt.reshape(E * N, K)), 0)
+    del wt
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, sa, qb, 0, sb, fm.SCALE_F32, i32_dev(offs), E, M, N, K)
+    _, got = _out_host(out)
+    qa_h, sa_h = host(qa), host(sa)
+    qb_h, sb_h = host(qb).reshape(E, N, K), host(sb).reshape(E, N)
+
+    def ref_for(e, sel):
+        one = np.array([len(sel)], np.int32)
+        ref = oracle.mm_grouped_m(qa_h[sel], sa_h[sel], qb_h[e:e + 1], sb_h[e:e + 1], one, 0, 0)
+        A = oracle.decode(qa_h[sel], 0) / sa_h[sel][:, None].astype(np.float64)
+        B = oracle.decode(qb_h[e:e + 1], 0) / sb_h[e][None, :, None].astype(np.float64)
+        return (ref,) + oracle.error_bounds_m(A, B, one, oracle.ACC_FP8_MFMA)
+
+    _check_rows_by_expert(got, _rows(M, 24, cfg), offs, M, ref_for, f"cfg{cfg}")
+
+
+def test_grouped_k_full_size_sampled():
+    w = synth.WORKLOADS[2]
+    dy = synth.make_dy(w)             # [8192, 14336]
+    x = synth.make_x(w)               # [8192, 4096]
+    offs = np.array([8192], np.int32)
+    M, N = dy.shape
+    K = x.shape[1]
+    note("GROUPED_K full cfg=2")
+    qa, sa = fm.quantize_colwise(bf16_dev(dy), i32_dev(offs), 0)
+    qb, sb = fm.quantize_colwise(bf16_dev(x), i32_dev(offs), 0)
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, sa, qb, 0, sb, fm.SCALE_F32, i32_dev(offs), 1, M, N, K)
+    rows = _rows(N, 12, 7)
+    _, got = _out_host(out)
+    qa_h, sa_h = host(qa)[rows], host(sa)[:, rows]
+    qb_h, sb_h = host(qb), host(sb)
+    ref = oracle.mm_grouped_k(qa_h, sa_h, qb_h, sb_h, offs, 0, 0)
+    A = oracle.decode(qa_h, 0) / sa_h[0][:, None]
+    B = oracle.decode(qb_h, 0) / sb_h[0][:, None]
+    contract, tight = oracle.error_bounds_k(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got[:, rows], ref, contract, tight, "cfg2 wgrad")
+
+
+def test_grouped_m_mx_full_size_sampled():
+    w = synth.WORKLOADS[5]
+    x = synth.make_x(w)               # [16384, 5120]
+    # a 2048-row slice of every expert's W1 keeps the host-side check small
+    E, N, K = 16, 2048, 5120
+    wt = np.stack([synth.normal_bf16(1000 * synth.tensor_seed(5, synth.T_W1) + e, (N, K), 0.02) for e in range(E)])
+    offs = w.offs
+    M = x.shape[0]
+    note(f"GROUPED_M MX full cfg=5 M={M} N={N} K={K}")
+    qa, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(wt.reshape(E * N, K)), axis=1, rule=0)
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, xa, qb, 0, xb, fm.SCALE_E8M0, i32_dev(offs), E, M, N, K)
+    _, got = _out_host(out)
+    qa_h, xa_h = host(qa), host(xa)
+    qb_h, xb_h = host(qb).reshape(E, N, K), host(xb).reshape(E, N, K // 32)
+
+    def ref_for(e, sel):
+        one = np.array([len(sel)], np.int32)
+        ref = oracle.mm_grouped_m_mx(qa_h[sel], xa_h[sel], qb_h[e:e + 1], xb_h[e:e + 1], one)
+        A = oracle.decode(qa_h[sel], 0) * np.repeat(oracle.e8m0_decode(xa_h[sel]), 32, axis=-1)
+        B = oracle.decode(qb_h[e:e + 1], 0) * np.repeat(oracle.e8m0_decode(xb_h[e:e + 1]), 32, axis=-1)
+        return (ref,) + oracle.error_bounds_m(A, B, one, oracle.ACC_FP8_MFMA)
+
+    _check_rows_by_expert(got, _rows(M, 16, 55), offs, M, ref_for, "cfg5 MX")

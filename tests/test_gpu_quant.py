@@ -1,0 +1,250 @@
+"""GPU parity of the quantization kernels against the CPU oracle: bit-exact
+codes and scales, through the C ABI (via the thin Python binding).
+
+Small cases span several tiles and ragged tails; full-size cases use the
+workloads' real shapes and compare sampled rows/columns (each row's or
+column's result depends only on its own reduction set, so the oracle can
+compute a sample independently).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp8_quantized_moe_amd as fm
+from mxfp8_quantized_moe_amd import synth
+from gpu_helpers import (DEV, note, bf16_dev, i32_dev, filled_u8, filled_f32, host, assert_bytes_equal,
+                         assert_f32_bits_equal)
+
+pytestmark = pytest.mark.gpu
+
+CODECS = [fm.E4M3FN, fm.E4M3FNUZ]
+
+
+def special_input(seed, shape, frac=0.02, factor=60.0, sigma=1.0):
+    x = synth.normal_bf16(seed, shape, sigma, frac, factor)
+    flat = x.reshape(-1)
+    n = flat.size
+    if n >= 8:
+        flat[:4] = synth.f32_to_bf16_bits(np.float32([0.0, 2.0 ** -130, -(2.0 ** -133), -0.0]))
+        flat[n // 2] = synth.f32_to_bf16_bits(np.float32([1e30]))[0]
+    return x
+
+
+# ------------------------------------------------------------------- codec
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_device_encoder_matches_oracle(codec):
+    fmax = oracle.FMAX[codec]
+    mags = oracle.decode_table(codec)[: (0x7E if codec == 0 else 0x7F) + 1]
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    probes = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+                             mags.astype(np.float32)])
+    fm_bits = int(np.float32(fmax).view(np.uint32))
+    sweep = np.arange(0, fm_bits + 1, 4099, dtype=np.uint32).view(np.float32)
+    y = np.concatenate([probes, sweep, np.float32([fmax, 0.0, -0.0, 1e-45, 2.0 ** -126])])
+    y = np.concatenate([y, -y]).astype(np.float32)
+    y = y[np.abs(y) <= fmax]
+    note(f"encode_f32 codec={codec} n={y.size}")
+    q = host(fm.encode_f32(torch.from_numpy(y).to(DEV), codec))
+    assert_bytes_equal(q, oracle.encode(y, codec), f"encode codec {codec}")
+
+
+# ------------------------------------------------------------------- rowwise
+
+ROW_SHAPES = [(512, 256), (2048, 256), (7, 8), (33, 24), (5, 4104), (3, 16400), (100, 4096), (2, 131072),
+              (257, 520), (0, 64), (3, 0)]
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_rowwise_parity(codec, shape):
+    R, C = shape
+    x = special_input(1000 + R + C, shape)
+    if R > 4:
+        x[R // 3] = 0                                      # an all-zero row
+    note(f"rowwise codec={codec} shape={shape}")
+    q, s = fm.quantize_rowwise(bf16_dev(x), codec)
+    qr, sr = oracle.quantize_rowwise(x, codec)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_f32_bits_equal(host(s), sr, "scales")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_rowwise_strided_rows(codec):
+    x = special_input(77, (129, 392))
+    xd = bf16_dev(x)[:, :264]                             # row stride 392 > cols 264
+    note(f"rowwise strided codec={codec}")
+    q, s = fm.quantize_rowwise(xd, codec)
+    qr, sr = oracle.quantize_rowwise(np.ascontiguousarray(x[:, :264]), codec)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_f32_bits_equal(host(s), sr, "scales")
+
+
+# ------------------------------------------------------------------- colwise
+
+GROUP_CASES = {
+    "cfg1": (512, 256, synth.offsets_from_counts(synth.routing_counts(1))),
+    "ragged": (3000, 136, synth.offsets_from_counts(synth.random_counts(5, 2950, 9))),
+    "tall": (2100, 64, np.array([2100], np.int32)),
+    "malformed": (700, 72, np.array([100, 50, 650, 900, -3], np.int32)),
+    "tiny": (37, 8, np.array([0, 5, 5, 36], np.int32)),
+}
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("case", list(GROUP_CASES))
+def test_colwise_grouped_parity(codec, case):
+    M, C, offs = GROUP_CASES[case]
+    x = special_input(2000 + M, (M, C))
+    ld_q = (M + 16 + 15) // 16 * 16
+    note(f"colwise grouped codec={codec} case={case}")
+    q_t = filled_u8((C, ld_q))
+    sc = filled_f32((len(offs), C))
+    fm.quantize_colwise(bf16_dev(x), i32_dev(offs), codec, q_t=q_t, scale=sc, ld_q=ld_q)
+    sentinel = np.full((C, ld_q), 0xA5, np.uint8)
+    qr, sr = oracle.quantize_colwise_grouped(x, offs, codec, q_init=sentinel, ld_q=ld_q)
+    assert_bytes_equal(host(q_t), qr, "codes")
+    assert_f32_bits_equal(host(sc), sr, "scales")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("shape", [(3, 700, 72), (4, 100, 64), (2, 1, 8), (1, 1030, 136)])
+def test_colwise_batched_parity(codec, shape):
+    x = special_input(3000 + sum(shape), shape)
+    B, R, C = shape
+    ld_q = (R + 15) // 16 * 16 + 16
+    note(f"colwise batched codec={codec} shape={shape}")
+    q_t = filled_u8((B, C, ld_q))
+    sc = filled_f32((B, C))
+    fm.quantize_colwise(bf16_dev(x), None, codec, q_t=q_t, scale=sc, ld_q=ld_q)
+    qr, sr = oracle.quantize_colwise_batched(x, codec)
+    got = host(q_t)
+    assert_bytes_equal(got[:, :, :R], qr, "codes")
+    assert np.all(got[:, :, R:] == 0xA5), "wrote past the rows"
+    assert_f32_bits_equal(host(sc), sr, "scales")
+
+
+def test_colwise_deterministic_across_runs():
+    M, C, offs = GROUP_CASES["ragged"]
+    x = bf16_dev(special_input(99, (M, C)))
+    o = i32_dev(offs)
+    note("colwise determinism")
+    a = [host(t) for t in fm.quantize_colwise(x, o, fm.E4M3FN)]
+    b = [host(t) for t in fm.quantize_colwise(x, o, fm.E4M3FN)]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+# ------------------------------------------------------------------- MXFP8
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("shape", [(64, 96), (1000, 5120), (3, 32), (0, 64)])
+def test_mx_lastdim_parity(rule, shape):
+    x = special_input(4000 + shape[0], shape, 0.01, 30.0)
+    note(f"mx lastdim rule={rule} shape={shape}")
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule)
+    qr, sr = oracle.quantize_mx_lastdim(x, rule)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), sr, "e8m0")
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("shape", [(2, 544, 72), (3, 32, 8), (1, 1024, 128)])
+def test_mx_rows_batched_parity(rule, shape):
+    x = special_input(5000 + sum(shape), shape, 0.01, 30.0)
+    note(f"mx rows batched rule={rule} shape={shape}")
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=0, rule=rule)
+    qr, sr = oracle.quantize_mx_rows_batched(x, rule)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), sr, "e8m0")
+
+
+MX_GROUP_CASES = {
+    "ragged": (1300, 136, synth.offsets_from_counts(synth.random_counts(8, 1290, 7))),
+    "cfg1": (512, 256, synth.offsets_from_counts(synth.routing_counts(1))),
+    "malformed": (300, 64, np.array([40, 20, 300, 500], np.int32)),
+    "one_row": (1, 8, np.array([1], np.int32)),
+}
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("case", list(MX_GROUP_CASES))
+def test_mx_rows_grouped_parity(rule, case):
+    M, C, offs = MX_GROUP_CASES[case]
+    x = special_input(6000 + M, (M, C), 0.01, 30.0)
+    rows_pad = fm.quantize_mx_rows_bound(M, len(offs)) + 64      # extra tail beyond the bound
+    note(f"mx rows grouped rule={rule} case={case} rows_pad={rows_pad}")
+    q = filled_u8((C, rows_pad))
+    sc = filled_u8((C, rows_pad // 32))
+    q, sc, op = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=rule, rows_pad=rows_pad,
+                               q=q, scale=sc)
+    qr, sr, opr = oracle.quantize_mx_rows_grouped(x, offs, rule, rows_pad)
+    assert_bytes_equal(host(op), opr, "padded offsets")
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), sr, "e8m0")
+
+
+# ------------------------------------------------------------------- full-size, sampled
+
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(k, n), replace=False)]))
+
+
+@pytest.mark.parametrize("cfg,tensor", [(2, "dy"), (2, "w1"), (3, "w1"), (4, "x")])
+def test_rowwise_full_size_sampled(cfg, tensor):
+    w = synth.WORKLOADS[cfg]
+    x = {"dy": synth.make_dy, "x": synth.make_x, "w1": synth.make_w1}[tensor](w)
+    x = x.reshape(-1, x.shape[-1])
+    note(f"rowwise full cfg={cfg} {tensor} {x.shape}")
+    q, s = fm.quantize_rowwise(bf16_dev(x), fm.E4M3FN)
+    rows = _sample(x.shape[0], 48, cfg)
+    qh, sh = host(q), host(s)
+    qr, sr = oracle.quantize_rowwise(x[rows], fm.E4M3FN)
+    assert_bytes_equal(qh[rows], qr, "codes")
+    assert_f32_bits_equal(sh[rows], sr, "scales")
+
+
+@pytest.mark.parametrize("cfg,tensor", [(2, "dy"), (3, "x"), (4, "dy"), (4, "a2")])
+def test_colwise_grouped_full_size_sampled(cfg, tensor):
+    w = synth.WORKLOADS[cfg]
+    x = {"dy": synth.make_dy, "x": synth.make_x, "a2": synth.make_a2}[tensor](w)
+    offs = w.offs
+    note(f"colwise full cfg={cfg} {tensor} {x.shape}")
+    q_t, sc = fm.quantize_colwise(bf16_dev(x), i32_dev(offs), fm.E4M3FN)
+    cols = _sample(x.shape[1], 12, cfg + 10)
+    qh, sh = host(q_t), host(sc)
+    qr, sr = oracle.quantize_colwise_grouped(np.ascontiguousarray(x[:, cols]), offs, fm.E4M3FN)
+    assert_bytes_equal(qh[cols], qr, "codes")
+    assert_f32_bits_equal(sh[:, cols], sr, "scales")
+
+
+def test_colwise_batched_full_size_sampled():
+    w = synth.WORKLOADS[4]
+    x = synth.make_w2(w)                                          # [32, 7168, 2048]
+    note(f"colwise batched full cfg=4 w2 {x.shape}")
+    q_t, sc = fm.quantize_colwise(bf16_dev(x), None, fm.E4M3FN)
+    cols = _sample(x.shape[2], 8, 44)
+    qh, sh = host(q_t), host(sc)
+    qr, sr = oracle.quantize_colwise_batched(np.ascontiguousarray(x[:, :, cols]), fm.E4M3FN)
+    assert_bytes_equal(qh[:, cols], qr, "codes")
+    assert_f32_bits_equal(sh[:, cols], sr, "scales")
+
+
+def test_mx_full_size_sampled():
+    w = synth.WORKLOADS[5]
+    x = synth.make_dy(w)                                          # [16384, 5120]
+    offs = w.offs
+    note(f"mx full cfg=5 dy {x.shape}")
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0)
+    rows = _sample(x.shape[0], 32, 5)
+    qr, sr = oracle.quantize_mx_lastdim(x[rows], 0)
+    assert_bytes_equal(host(q)[rows], qr, "codes lastdim")
+    assert_bytes_equal(host(sc)[rows], sr, "e8m0 lastdim")
+    rows_pad = fm.quantize_mx_rows_bound(x.shape[0], len(offs))
+    q, sc, op = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=0, rows_pad=rows_pad)
+    cols = _sample(x.shape[1], 8, 6)
+    qr, sr, opr = oracle.quantize_mx_rows_grouped(np.ascontiguousarray(x[:, cols]), offs, 0, rows_pad)
+    assert_bytes_equal(host(op), opr, "padded offsets")
+    assert_bytes_equal(host(q)[cols], qr, "codes rows")
+    assert_bytes_equal(host(sc)[cols], sr, "e8m0 rows")
