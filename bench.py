@@ -1,0 +1,392 @@
+"""Benchmark: one MoE/linear layer step (quantization + grouped GEMMs) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic inputs
+already resident in HBM: every quantization call and grouped GEMM of the
+layer's forward, dgrad and wgrad, in the order a training step issues them,
+on preallocated buffers (no allocation, no host sync inside the step).
+
+Default workload: the dense Llama3-8B-shaped linear (X [8192, 4096], W [14336,
+4096], dY [8192, 14336]; E = 1), FP8 rowwise recipe with colwise-quantized
+backward operands and FP8 wgrad.  --config selects the other workloads:
+1 tiny MoE (fwd only), 3 DeepSeek-MoE-16B-shaped layer, 4 DeepSeek-V3-shaped
+one-GPU expert share, 5 Llama4-Scout-shaped MXFP8 layer; --gw adds the BF16
+weight-gradient variant of config 2 as its own line item.
+
+Prints ONE JSON line.  `value` is microseconds per layer step (lower is
+better).  Also reported: aggregate quantization GB/s (algorithmic bytes: 2 B
+read + 1 B written per element + scale bytes), aggregate GEMM TFLOP/s
+(2 * sum_e M_e * N * K), per-kernel averages from HIP events on the launch
+stream, the roofline of the dominant kernel, and the CPU oracle timed on a
+bounded sample of the same workload (a reported baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # dense FP8 / MXFP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--gw", action="store_true", help="config 2: add the BF16 wgrad variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------- layer plan
+
+class Step:
+    """A list of launches; each item: (name, kind, fn, work) with kind 'quant' (work = bytes)
+    or 'gemm' (work = flops) or 'gemm_bf16'."""
+
+    def __init__(self):
+        self.items = []
+
+    def add(self, name, kind, fn, work):
+        self.items.append((name, kind, fn, work))
+
+
+def build_step(cfg: int, gw: bool):
+    import torch
+    import mxfp8_quantized_moe_amd as fm
+    from mxfp8_quantized_moe_amd import synth
+
+    dev = "cuda:0"
+    w = synth.WORKLOADS[cfg]
+
+    def dv(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
+    step = Step()
+    host = {}
+
+    E, M, H = w.E, w.M, w.H
+    offs_np = w.offs
+    offs = torch.from_numpy(offs_np.astype(np.int32)).to(dev)
+    counts = np.diff(np.concatenate([[0], offs_np]))
+    nonempty = int((counts > 0).sum())
+
+    def qbytes(n_elem, n_scale, scale_bytes=4):
+        return 3 * n_elem + scale_bytes * n_scale
+
+    def q_row(name, x, rows, cols):
+        q, s = u8(rows, cols), f32(rows)
+        step.add(name, "quant", lambda: fm.quantize_rowwise(x.view(rows, cols), 0, q=q, scale=s),
+                 qbytes(rows * cols, rows))
+        return q, s
+
+    def q_col_grouped(name, x, rows, cols):
+        ld = (rows + 15) // 16 * 16
+        q, s = u8(cols, ld), f32(E, cols)
+        step.add(name, "quant", lambda: fm.quantize_colwise(x, offs, 0, q_t=q, scale=s, ld_q=ld),
+                 qbytes(rows * cols, E * cols))
+        return q, s, ld
+
+    def q_col_batched(name, x, B, R, C):
+        q, s = u8(B, C, R), f32(B, C)
+        step.add(name, "quant", lambda: fm.quantize_colwise(x, None, 0, q_t=q, scale=s, ld_q=R),
+                 qbytes(B * R * C, B * C))
+        return q, s
+
+    def g_m(name, qa, sa, qb, sb, Mr, N, K, sk=fm.SCALE_F32, offs_t=None, n_groups=None):
+        o = bf(Mr, N)
+        og = offs if offs_t is None else offs_t
+        ng = E if n_groups is None else n_groups
+        step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, sa, qb, 0, sb, sk, og, ng,
+                                                            Mr, N, K, out=o), 2.0 * M * N * K)
+        return o
+
+    def g_k(name, qa, sa, qb, sb, Mc, N, K, sk=fm.SCALE_F32, offs_t=None):
+        o = bf(E, N, K)
+        og = offs if offs_t is None else offs_t
+        step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, sa, qb, 0, sb, sk, og, E,
+                                                            Mc, N, K, out=o), 2.0 * M * N * K)
+        return o
+
+    if cfg in (1, 2):
+        F2 = w.F2
+        X, W1 = synth.make_x(w), synth.make_w1(w)
+        host.update(X=X, W=W1.reshape(E * F2, H))
+        Xd, Wd = dv(X), dv(W1)
+        qx, sx = q_row("q_row X", Xd, M, H)
+        qw, sw = q_row("q_row W", Wd, E * F2, H)
+        g_m("gemm fwd", qx, sx, qw, sw, M, F2, H)
+        if cfg == 2:
+            DY = synth.make_dy(w)
+            host.update(DY=DY)
+            DYd = dv(DY)
+            qdy, sdy = q_row("q_row dY", DYd, M, F2)
+            qwt, swt = q_col_batched("q_col W", Wd, 1, F2, H)
+            g_m("gemm dgrad", qdy, sdy, qwt, swt, M, H, F2)
+            qdyt, sdyt, ld = q_col_grouped("q_col dY", DYd, M, F2)
+            qxt, sxt, _ = q_col_grouped("q_col X", Xd, M, H)
+            g_k("gemm wgrad", qdyt, sdyt, qxt, sxt, ld, F2, H)
+            if gw:
+                o = bf(1, F2, H)
+                step.add("gemm wgrad bf16", "gemm_bf16",
+                         lambda: fm.grouped_mm_scaled(fm.GROUPED_K, DYd, fm.OPD_BF16, None, Xd, fm.OPD_BF16, None,
+                                                      fm.SCALE_NONE, offs, 1, M, F2, H, out=o), 2.0 * M * F2 * H)
+        return step, host
+
+    F, F2 = w.F, w.F2
+    X, A2, DY, DH1 = synth.make_x(w), synth.make_a2(w), synth.make_dy(w), synth.make_dh1(w)
+    W1, W2 = synth.make_w1(w), synth.make_w2(w)
+    host.update(X=X, W=W1.reshape(E * F2, H), DY=DY)
+    Xd, A2d, DYd, DH1d, W1d, W2d = dv(X), dv(A2), dv(DY), dv(DH1), dv(W1), dv(W2)
+    del W1, W2
+    if cfg in (3, 4):
+        qx, sx = q_row("q_row X", Xd, M, H)
+        qw1, sw1 = q_row("q_row W1", W1d, E * F2, H)
+        g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H)
+        qa2, sa2 = q_row("q_row A2", A2d, M, F)
+        qw2, sw2 = q_row("q_row W2", W2d, E * H, F)
+        g_m("gemm fwd W2", qa2, sa2, qw2, sw2, M, H, F)
+        qdy, sdy = q_row("q_row dY", DYd, M, H)
+        qw2t, sw2t = q_col_batched("q_col W2", W2d, E, H, F)
+        g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, M, F, H)
+        qdyt, sdyt, ld = q_col_grouped("q_col dY", DYd, M, H)
+        qa2t, sa2t, _ = q_col_grouped("q_col A2", A2d, M, F)
+        g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, ld, H, F)
+        qdh, sdh = q_row("q_row dH1", DH1d, M, F2)
+        qw1t, sw1t = q_col_batched("q_col W1", W1d, E, F2, H)
+        g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, M, H, F2)
+        qdht, sdht, _ = q_col_grouped("q_col dH1", DH1d, M, F2)
+        qxt, sxt, _ = q_col_grouped("q_col X", Xd, M, H)
+        g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, ld, F2, H)
+        return step, host
+
+    # cfg 5: MXFP8
+    rule = fm.MX_FLOOR_OCP
+    Mp = fm.quantize_mx_rows_bound(M, E)
+
+    def mx_last(name, x, rows, cols):
+        q, s = u8(rows, cols), u8(rows, cols // 32)
+        step.add(name, "quant", lambda: fm.quantize_mx(x.view(rows, cols), axis=1, rule=rule, q=q, scale=s),
+                 qbytes(rows * cols, rows * cols // 32, 1))
+        return q, s
+
+    def mx_rows_b(name, x, B, R, C):
+        q, s = u8(B, C, R), u8(B, C, R // 32)
+        step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, rule=rule, q=q, scale=s),
+                 qbytes(B * R * C, B * C * R // 32, 1))
+        return q, s
+
+    op = torch.empty(E, dtype=torch.int32, device=dev)
+
+    def mx_rows_g(name, x, rows, cols):
+        q, s = u8(cols, Mp), u8(cols, Mp // 32)
+        step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
+                                                       offs_pad=op),
+                 qbytes(rows * cols, cols * rows // 32, 1))
+        return q, s
+
+    qx, sx = mx_last("mx X", Xd, M, H)
+    qw1, sw1 = mx_last("mx W1", W1d, E * F2, H)
+    g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H, sk=fm.SCALE_E8M0)
+    qa2, sa2 = mx_last("mx A2", A2d, M, F)
+    qw2, sw2 = mx_last("mx W2", W2d, E * H, F)
+    g_m("gemm fwd W2", qa2, sa2, qw2, sw2, M, H, F, sk=fm.SCALE_E8M0)
+    qdy, sdy = mx_last("mx dY", DYd, M, H)
+    qw2t, sw2t = mx_rows_b("mx W2^T", W2d, E, H, F)
+    g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, M, F, H, sk=fm.SCALE_E8M0)
+    qdyt, sdyt = mx_rows_g("mx dY^T", DYd, M, H)
+    qa2t, sa2t = mx_rows_g("mx A2^T", A2d, M, F)
+    g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0, offs_t=op)
+    qdh, sdh = mx_last("mx dH1", DH1d, M, F2)
+    qw1t, sw1t = mx_rows_b("mx W1^T", W1d, E, F2, H)
+    g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, M, H, F2, sk=fm.SCALE_E8M0)
+    qdht, sdht = mx_rows_g("mx dH1^T", DH1d, M, F2)
+    qxt, sxt = mx_rows_g("mx X^T", Xd, M, H)
+    g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0, offs_t=op)
+    return step, host
+
+
+# ---------------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(cfg: int, host: dict):
+    """The oracle timed on a bounded sample of the dense layer's work, scaled
+    linearly to the whole layer (us per layer): the rowwise and colwise
+    quantization of X, W and dY and the fwd/dgrad/wgrad GEMMs on row x column
+    samples (E = 1)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    X, W = host["X"], host["W"]
+    DY = host.get("DY")
+    total_us = 0.0
+    pieces = []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    def add(name, secs, factor):
+        nonlocal total_us
+        total_us += secs * factor * 1e6
+        pieces.append(f"{name} x{factor:.0f}")
+
+    rs = 128
+    for name, T in [("q_row X", X), ("q_row W", W)] + ([("q_row dY", DY)] if DY is not None else []):
+        (_, t) = timed(lambda: oracle.quantize_rowwise(T[:rs], 0))
+        add(name, t, T.shape[0] / rs)
+    cs = 32
+    offs1 = np.array([X.shape[0]], np.int32)
+    if DY is not None:
+        for name, T in [("q_col X", X), ("q_col dY", DY), ("q_col W", W)]:
+            (_, t) = timed(lambda: oracle.quantize_colwise_grouped(np.ascontiguousarray(T[:, :cs]),
+                                                                   np.array([T.shape[0]], np.int32), 0))
+            add(name, t, T.shape[1] / cs)
+    gm, gn = 32, 512
+    qa, sa = oracle.quantize_rowwise(X[:gm], 0)
+    qb, sb = oracle.quantize_rowwise(W[:gn], 0)
+    (_, t) = timed(lambda: oracle.mm_grouped_m(qa, sa, qb[None], sb[None], np.array([gm], np.int32), 0, 0))
+    n_gemm = 1
+    add("gemm fwd", t, (X.shape[0] / gm) * (W.shape[0] / gn))
+    if DY is not None:
+        qd, sd = oracle.quantize_rowwise(DY[:gm], 0)
+        qwt, swt = oracle.quantize_colwise_batched(np.ascontiguousarray(W[:, :gn])[None], 0)
+        (_, t) = timed(lambda: oracle.mm_grouped_m(qd, sd, qwt, swt, np.array([gm], np.int32), 0, 0))
+        add("gemm dgrad", t, (DY.shape[0] / gm) * (W.shape[1] / gn))
+        qdt, sdt = oracle.quantize_colwise_grouped(np.ascontiguousarray(DY[:, :gm]), offs1, 0)
+        qxt, sxt = oracle.quantize_colwise_grouped(np.ascontiguousarray(X[:, :gn]), offs1, 0)
+        (_, t) = timed(lambda: oracle.mm_grouped_k(qdt, sdt, qxt, sxt, offs1, 0, 0))
+        add("gemm wgrad", t, (DY.shape[1] / gm) * (X.shape[1] / gn))
+        n_gemm = 3
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(total_us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy oracle on row/column samples scaled linearly to the full layer "
+                      f"(quant: {rs} rows or {cs} columns per tensor, single-threaded; GEMM: {gm} x {gn} output "
+                      f"samples, fp64 BLAS with {threads} threads); {n_gemm} GEMMs + "
+                      f"{len(pieces) - n_gemm} quant calls: " + ", ".join(pieces)}
+
+
+# ---------------------------------------------------------------------- traffic evidence
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp8_quantized_moe_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_item: str, cfg: int):
+    """HBM bytes per launch measured by rocprofv3 PMC (profiles/traffic.json), or None
+    if absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("source_digest") != kernel_source_digest():
+        return None
+    return d.get("per_launch_bytes", {}).get(f"cfg{cfg}:{kernel_item}")
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    import mxfp8_quantized_moe_amd  # noqa: F401  (fails loudly if the HIP library is missing)
+    from mxfp8_quantized_moe_amd import synth
+
+    step, host = build_step(args.config, args.gw)
+    stream = torch.cuda.current_stream()
+    names = [it[0] for it in step.items]
+    for _ in range(args.warmup):
+        for it in step.items:
+            it[2]()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in step.items]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, it in enumerate(step.items):
+            ev[s][i][0].record(stream)
+            it[2]()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per = {}
+    for i, (name, kind, _, work) in enumerate(step.items):
+        us = float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])) * 1e3
+        per[name] = (kind, work, us)
+    q_bytes = sum(v[1] for v in per.values() if v[0] == "quant")
+    q_us = sum(v[2] for v in per.values() if v[0] == "quant")
+    g_flops = sum(v[1] for v in per.values() if v[0] == "gemm")
+    g_us = sum(v[2] for v in per.values() if v[0] == "gemm")
+    dom = max(per, key=lambda k: per[k][2])
+    kind, work, us = per[dom]
+    if kind == "quant":
+        achieved, peak, unit, bound = work / us / 1e3, PEAK_HBM_GBPS, "GB/s", "hbm"
+    else:
+        achieved = work / us / 1e6
+        peak = PEAK_BF16_TFLOPS if kind == "gemm_bf16" else PEAK_FP8_TFLOPS
+        unit, bound = "TFLOP/s", "mfma"
+
+    w = synth.WORKLOADS[args.config]
+    out = {
+        "metric": "quant HBM GB/s + grouped-GEMM TFLOP/s; us per MoE layer (quant+GEMM)",
+        "value": round(ms_per_step * 1e3, 1),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8" if w.mx else "fp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "experts": w.E, "routed_rows": w.M, "hidden": w.H,
+                   "w1_out": w.F2, "w2_in": w.F,
+                   "step": ("fwd" if args.config == 1 else "fwd+dgrad+wgrad") + ("+bf16 wgrad" if args.gw else ""),
+                   "recipe": "mxfp8 (e8m0 per 1x32)" if w.mx else "fp8 e4m3fn rowwise + colwise backward"},
+        "quant_GBps": round(q_bytes / q_us / 1e3, 1) if q_us else None,
+        "quant_us": round(q_us, 1),
+        "gemm_TFLOPs": round(g_flops / g_us / 1e6, 1) if g_us else None,
+        "gemm_us": round(g_us, 1),
+        "kernels_us": {k: round(v[2], 1) for k, v in per.items()},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, args.config)},
+    }
+    if not args.no_cpu_baseline and args.config == 2:
+        out["cpu_baseline"] = cpu_baseline(args.config, host)
+    else:
+        out["cpu_baseline"] = None      # sampled oracle timing is defined for the default workload
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
