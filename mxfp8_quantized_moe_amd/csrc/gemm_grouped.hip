@@ -22,13 +22,16 @@
 //    256 gives 4x4 MFMA tiles per wave = 256 fp32 accumulators per lane, the
 //    largest tile that fits one wave per SIMD (512 registers) and makes each
 //    byte read from LDS feed 128 flops per wave.
-//  * 128 contraction bytes per stage: (BM + BN) x 128 B = 64 KiB, double
-//    buffered = 128 KiB of the 160 KiB LDS.  Global loads of stage k+1 are in
-//    flight while stage k runs on the matrix cores.
-//  * LDS rows are 128 B (8 chunks of 16 B); chunk c of row r is stored at chunk
-//    c ^ ((r >> 1) & 7), so 16 consecutive lanes reading the same logical chunk
-//    of 16 consecutive rows, and 16 lanes writing 8 chunks of 2 rows, both
-//    touch 16 distinct 16-byte bank groups.
+//  * With one wave per SIMD nothing else hides memory latency, so operands
+//    stream through a 4-slot LDS ring of 64-byte contraction stages
+//    ((BM + BN) x 64 B = 32 KiB per stage, 128 KiB in all) with 3 stages in
+//    flight: gfx950's direct global->LDS loads (global_load_lds_dwordx4) move
+//    the data without staging registers, one barrier per stage.
+//  * LDS rows are 64 B (4 chunks of 16 B); chunk c of row r is stored at chunk
+//    c ^ ((r >> 2) & 3), so 16 consecutive lanes reading one logical chunk of
+//    16 consecutive rows touch 16 distinct 16-byte bank groups.  A wave's
+//    DMA fills 1 KiB contiguously (16 rows); each lane fetches the global chunk
+//    that belongs at its LDS slot, which realises the swizzle for free.
 //  * Small groups (average rows per group below 512) use BM = 128 to waste
 //    less of each tile on padding rows.
 //  * Workgroups are numbered so that each XCD (round-robin dispatch over 8)
@@ -42,10 +45,7 @@ namespace fp8moe {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kStageK = 128;   // contraction bytes per stage
 constexpr int kBandRows = 8;   // row tiles per band in the tile order
-
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 struct KParams {
   const uint8_t* a;
@@ -85,14 +85,69 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+constexpr int kBK = 64;          // contraction bytes per pipeline stage (one MFMA K step)
+constexpr int kSlots = 4;        // LDS ring slots
+constexpr int kAhead = 3;        // stages in flight ahead of the one being computed
+
+// Swizzled offset of 16-byte chunk c (0..3) of tile row r in a stage (64-byte rows):
+// 16 lanes reading one logical chunk of 16 consecutive rows hit 16 distinct
+// 16-byte bank groups, and a DMA of 16 rows x 64 B stays contiguous.
+__device__ __forceinline__ int stage_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]).  The builtin is visible to the compiler's own wait
+// insertion, which then knows which direct-to-LDS loads have landed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+// Direct global->LDS loads (a wave fills 64 consecutive 16-byte or 1-byte LDS
+// slots, one per lane, from per-lane global addresses).  Wrapped in plain
+// device functions: clang drops a kernel's host launch stub when this builtin
+// is called straight from a generic lambda in the kernel body.
+__device__ __forceinline__ void dma_16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+// A 1-byte DMA still gives each lane a dword of LDS: lane l's byte lands at dst + 4 l.
+__device__ __forceinline__ void dma_1(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 1, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// in-flight global load, draining the pipeline); the empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int BM, int BN, int MODE, int SK, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_kernel(KParams p) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-  constexpr int A_BYTES = BM * kStageK, STAGE = (BM + BN) * kStageK;
-  constexpr int LA = BM / 32, LB = BN / 32;         // 16-byte global loads per thread per stage
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ uint32_t s_sc[SK == 1 ? 2 * (BM + BN) : 1];   // e8m0 bytes of 4 blocks per tile row
+  constexpr int A_BYTES = BM * kBK, STAGE = (BM + BN) * kBK;
+  constexpr int BLOCKS = (BM + BN) / 16;               // 1 KiB DMA blocks per stage
+  constexpr int BPW = BLOCKS / 4;                      // per wave
+  constexpr int SROWS = BM + BN;                       // e8m0 bytes per stage and 32-block
+  constexpr int SC_DMA = SK == 1 ? (2 * SROWS) / 64 / 4 : 0;   // byte DMAs per wave per stage
+  constexpr int LPS = BPW + SC_DMA;                    // vector-memory ops per wave per stage
+  // One array per ring slot, each accessed with a compile-time slot index, so the
+  // compiler can tell a load landing in one slot from reads of another.
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[STAGE];
+  constexpr int SRB = SK == 1 ? 4 * 2 * SROWS : 16;   // byte DMAs land one lane per dword
+  __shared__ __attribute__((aligned(16))) uint8_t sring0[SRB];
+  __shared__ __attribute__((aligned(16))) uint8_t sring1[SRB];
+  __shared__ __attribute__((aligned(16))) uint8_t sring2[SRB];
+  __shared__ __attribute__((aligned(16))) uint8_t sring3[SRB];
+  uint8_t* const slot_data[kSlots] = {ring0, ring1, ring2, ring3};
+  uint8_t* const slot_scale[kSlots] = {sring0, sring1, sring2, sring3};
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -179,59 +234,55 @@ void gemm_fp8_kernel(KParams p) {
   }
 
   const int c_start = c_lo & ~15;
-  const int nk = c_hi > c_lo ? (c_hi - c_start + kStageK - 1) / kStageK : 0;
+  const int nk = c_hi > c_lo ? (c_hi - c_start + kBK - 1) / kBK : 0;
 
-  // ---------------------------------------------------------------- global -> LDS
-  const int lc = t & 7, lr = t >> 3;   // this thread's chunk and first row in a stage
-  u32x4 ra[LA], rb[LB];
-  uint32_t rsc[SK == 1 ? 2 : 1];
+  // ---------------------------------------------------------------- DMA global -> LDS
+  // Wave `wave` moves blocks wave + 4*i (i < BPW) of each stage.  In a block,
+  // lane l fills LDS bytes [16 l, 16 l + 16): tile row 16*blk + l/4, physical
+  // chunk l%4, i.e. logical chunk (l%4) ^ ((l/16)%4) of that row.
+  const int dma_c = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint8_t* rowp[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + 4 * i;
+    const int r = 16 * blk + (lane >> 2);           // row in the concatenated [A; B] tile
+    rowp[i] = r < BM ? P + (int64_t)min(r, p_valid - 1) * p_ld
+                     : Q + (int64_t)min(r - BM, q_valid - 1) * q_ld;
+  }
+  // e8m0: byte DMA d of a stage covers (block half d/(SROWS/64), rows 64*(d%(SROWS/64)) + lane)
+  const uint8_t* srow[SK == 1 ? SC_DMA : 1];
+  if constexpr (SK == 1) {
+#pragma unroll
+    for (int i = 0; i < SC_DMA; ++i) {
+      const int d = wave + 4 * i;
+      const int r = 64 * (d % (SROWS / 64)) + lane;
+      srow[i] = r < BM ? psc + (int64_t)min(r, p_valid - 1) * sc_ld : qsc + (int64_t)min(r - BM, q_valid - 1) * sc_ld;
+    }
+  }
 
-  auto load_stage = [&](int kt) {
-    const int pos = c_start + kt * kStageK + 16 * lc;
-    const bool in = pos < c_hi;
-    const bool partial = in && (pos < c_lo || pos + 16 > c_hi);
+  // Issue the DMAs of stage kt into ring slot SLOT (== kt % kSlots).  Every lane
+  // issues exactly one load per block (the per-stage wait counts rely on it):
+  // positions outside [c_lo, c_hi) are clamped to a valid chunk of the same row
+  // and zeroed in LDS by the boundary-stage fix-up.
+  const int pos_max = max((c_hi - 1) & ~15, 0);   // the last chunk overlapping the range
+  auto issue_stage = [&](auto slot_tag, int kt) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    uint8_t* dst = slot_data[SLOT];
+    const int pos = min(c_start + kt * kBK + 16 * dma_c, pos_max);
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = min(lr + 32 * i, p_valid - 1);
-      ra[i] = in ? *reinterpret_cast<const u32x4*>(P + r * p_ld + pos) : u32x4{0, 0, 0, 0};
-      if (partial) ra[i] = mask_chunk(ra[i], pos, c_lo, c_hi);
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int r = min(lr + 32 * i, q_valid - 1);
-      rb[i] = in ? *reinterpret_cast<const u32x4*>(Q + r * q_ld + pos) : u32x4{0, 0, 0, 0};
-      if (partial) rb[i] = mask_chunk(rb[i], pos, c_lo, c_hi);
-    }
+    for (int i = 0; i < BPW; ++i)
+      dma_16(rowp[i] + pos, dst + (wave + 4 * i) * 1024);
     if constexpr (SK == 1) {
-      // 4 e8m0 bytes (the stage's 32-blocks) for tile rows t and t + 256
-      const int blk0 = (c_start + kt * kStageK) >> 5, nblk = c_hi >> 5;
+      // e8m0 bytes past the range come from the row's last valid block; the
+      // data they scale is zeroed, and the quantizer never emits the NaN code.
+      uint8_t* sdst = slot_scale[SLOT];
+      const int blk0 = (c_start + kt * kBK) >> 5, nblk = c_hi >> 5;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = t + 256 * h;
-        uint32_t w = 0;
-        if (r < BM + BN) {
-          const bool isp = r < BM;
-          const int rr = isp ? min(r, p_valid - 1) : min(r - BM, q_valid - 1);
-          const uint8_t* src = (isp ? psc : qsc) + rr * sc_ld;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (blk0 + j < nblk) w |= (uint32_t)src[blk0 + j] << (8 * j);
-        }
-        rsc[h] = w;
+      for (int i = 0; i < SC_DMA; ++i) {
+        const int d = wave + 4 * i;
+        const int half = d / (SROWS / 64);
+        dma_1(srow[i] + max(min(blk0 + half, nblk - 1), 0), sdst + 256 * d);
       }
-    }
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* sa_ = smem + buf * STAGE;
-    uint8_t* sb_ = sa_ + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(sa_ + lds_off(lr + 32 * i, lc)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4*>(sb_ + lds_off(lr + 32 * i, lc)) = rb[i];
-    if constexpr (SK == 1) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (t + 256 * h < BM + BN) s_sc[buf * (BM + BN) + t + 256 * h] = rsc[h];
     }
   };
 
@@ -244,49 +295,75 @@ void gemm_fp8_kernel(KParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int g = lane >> 5, lrow = lane & 31;
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
-    const uint8_t* sa_ = smem + buf * STAGE;
-    const uint8_t* sb_ = sa_ + A_BYTES;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v8i af[TM], bf[TN];
-      int scA[TM], scB[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + 32 * i + lrow;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + lds_off(r, 4 * h + g));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + lds_off(r, 4 * h + 2 + g));
-        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        if constexpr (SK == 1) scA[i] = (int)((s_sc[buf * (BM + BN) + r] >> (8 * (2 * h + g))) & 0xFFu);
+
+  // One pipeline step: wait for stage kt (in slot SLOT), refill the slot that
+  // was computed last step with stage kt + kAhead, then run stage kt's MFMAs.
+  auto step = [&](auto slot_tag, int kt) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int NEXT = (SLOT + kAhead) % kSlots;
+    // stage kt has landed once at most the later stages' loads are outstanding
+    const int later = min(kAhead - 1, nk - 1 - kt);
+    if (later >= 2) wait_vmcnt<2 * LPS>();
+    else if (later == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    raw_barrier();
+    uint8_t* st = slot_data[SLOT];
+    const int base = c_start + kt * kBK;
+    if (base < c_lo || base + kBK > c_hi) {          // boundary stage (uniform)
+      // zero the bytes of every chunk outside or straddling [c_lo, c_hi)
+      for (int idx = t; idx < SROWS * 4; idx += 256) {
+        const int r = idx >> 2, c = idx & 3, pos = base + 16 * c;
+        if (pos < c_lo || pos + 16 > c_hi) {
+          u32x4* q = reinterpret_cast<u32x4*>(st + stage_off(r, c));
+          *q = mask_chunk(*q, pos, c_lo, c_hi);
+        }
       }
+      wait_lgkmcnt0();
+      raw_barrier();
+    }
+    if (kt + kAhead < nk) issue_stage(std::integral_constant<int, NEXT>{}, kt + kAhead);
+
+    const uint8_t* sa_ = st;
+    const uint8_t* sb_ = st + A_BYTES;
+    const uint8_t* sc_ = slot_scale[SLOT];
+    v8i af[TM], bf[TN];
+    int scA[TM], scB[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + 32 * i + lrow;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + stage_off(r, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + stage_off(r, 2 + g));
+      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (SK == 1) scA[i] = sc_[4 * (g * SROWS + r)];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WN + 32 * j + lrow;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + stage_off(r, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + stage_off(r, 2 + g));
+      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (SK == 1) scB[j] = sc_[4 * (g * SROWS + BM + r)];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + 32 * j + lrow;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + lds_off(r, 4 * h + g));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + lds_off(r, 4 * h + 2 + g));
-        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        if constexpr (SK == 1) scB[j] = (int)((s_sc[buf * (BM + BN) + BM + r] >> (8 * (2 * h + g))) & 0xFFu);
+        if constexpr (SK == 1)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, scA[i], 0,
+                                                                      scB[j]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          if constexpr (SK == 1)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, scA[i], 0,
-                                                                        scB[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-        }
-    }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
+  };
+
+  if (0 < nk) issue_stage(std::integral_constant<int, 0>{}, 0);
+  if (1 < nk) issue_stage(std::integral_constant<int, 1>{}, 1);
+  if (2 < nk) issue_stage(std::integral_constant<int, 2>{}, 2);
+  for (int kt = 0; kt < nk; kt += kSlots) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+    if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
   // ---------------------------------------------------------------- epilogue

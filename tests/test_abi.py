@@ -135,3 +135,9 @@ def test_python_binding_raises_on_bad_arguments():
     import mxfp8_quantized_moe_amd as fm
     with pytest.raises(fm.Fp8MoeError):
         L.check("quantize_rowwise", L.lib().quantize_rowwise(P, 4, 12, 16, 0, P, P, None))
+
+
+def test_no_undefined_internal_symbols():
+    """Every kernel launch stub and internal function resolves inside the library."""
+    und = os.popen(f"nm -D --undefined-only {L.LIB_PATH}").read()
+    assert "fp8moe" not in und, [l for l in und.splitlines() if "fp8moe" in l][:5]
