@@ -193,7 +193,8 @@ int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups);
  *   Formats: both operands FP8 (e4m3fn or e4m3fnuz, mixed allowed; e8m0 needs
  *   e4m3fn) or both BF16 (GROUPED_K with SCALE_NONE only).
  *   Accumulation is fp32; out is bf16 (round to nearest even) or fp32.
- *   Requires: M, N, K >= 0; K % 16 == 0 (GROUPED_M) or M % 16 == 0 (GROUPED_K);
+ *   Requires: M, N, K >= 0; FP8 operands: K % 16 == 0 and K <= 2^23 (GROUPED_M) or
+ *   M % 16 == 0 and M <= 2^23 (GROUPED_K); BF16 operands: M, N, K % 8 == 0;
  *   all pointers 16-byte aligned.
  */
 int grouped_mm_scaled(int mode, const void *a, int a_fmt, const void *a_scale,

@@ -24,9 +24,11 @@
 //    byte read from LDS feed 128 flops per wave.
 //  * With one wave per SIMD nothing else hides memory latency, so operands
 //    stream through a 4-slot LDS ring of 64-byte contraction stages
-//    ((BM + BN) x 64 B = 32 KiB per stage, 128 KiB in all) with 3 stages in
+//    ((BM + BN) x 64 B = 32 KiB per stage, 128 KiB in all) with 4 stages in
 //    flight: gfx950's direct global->LDS loads (global_load_lds_dwordx4) move
-//    the data without staging registers, one barrier per stage.
+//    the data without staging registers, one barrier per stage.  MFMA
+//    fragments are double-buffered in registers: stage k's MFMAs issue while
+//    stage k+1's fragments are read, so LDS latency stays off the MFMA path.
 //  * LDS rows are 64 B (4 chunks of 16 B); chunk c of row r is stored at chunk
 //    c ^ ((r >> 2) & 3), so 16 consecutive lanes reading one logical chunk of
 //    16 consecutive rows touch 16 distinct 16-byte bank groups.  A wave's
@@ -46,6 +48,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBandRows = 8;   // row tiles per band in the tile order
+constexpr int kGemmStageBytes = 64;   // contraction bytes per pipeline stage
 
 struct KParams {
   const uint8_t* a;
@@ -85,14 +88,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-constexpr int kBK = 64;          // contraction bytes per pipeline stage (one MFMA K step)
-constexpr int kSlots = 4;        // LDS ring slots
-constexpr int kAhead = 3;        // stages in flight ahead of the one being computed
-
-// Swizzled offset of 16-byte chunk c (0..3) of tile row r in a stage (64-byte rows):
-// 16 lanes reading one logical chunk of 16 consecutive rows hit 16 distinct
-// 16-byte bank groups, and a DMA of 16 rows x 64 B stays contiguous.
-__device__ __forceinline__ int stage_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// Pipeline shape: stages of BK = 64 contraction bytes (one MFMA K step) in a
+// 4-slot LDS ring (4 x (BM + BN) x 64 B = 128 KiB for 256 x 256 tiles).
+template <int BK>
+struct Ring {
+  static_assert(BK == 64, "64-byte stages (128-byte stages spill registers at 256 x 256)");
+  static constexpr int CH = BK / 16;                  // 16-byte chunks per tile row
+  static constexpr int SH = 2;                        // swizzle shift: log2(16 / CH)
+  static constexpr int SLOTS = 4;
+  static constexpr int RPB = 1024 / BK;               // tile rows per 1 KiB DMA block
+  // Swizzled offset of chunk c of tile row r: 16 lanes reading one logical chunk
+  // of 16 consecutive rows hit 16 distinct 16-byte bank groups.
+  static __device__ __forceinline__ int off(int r, int c) { return r * BK + ((c ^ ((r >> SH) & (CH - 1))) << 4); }
+};
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]).  The builtin is visible to the compiler's own wait
@@ -125,29 +133,32 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int MODE, int SK, int OUT>
+template <int BM, int BN, int BK, int MODE, int SK, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_kernel(KParams p) {
+  using R = Ring<BK>;
+  constexpr int kBK = BK, kSlots = R::SLOTS, CH = R::CH;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * kBK, STAGE = (BM + BN) * kBK;
-  constexpr int BLOCKS = (BM + BN) / 16;               // 1 KiB DMA blocks per stage
+  constexpr int BLOCKS = STAGE / 1024;                 // 1 KiB DMA blocks per stage
   constexpr int BPW = BLOCKS / 4;                      // per wave
   constexpr int SROWS = BM + BN;                       // e8m0 bytes per stage and 32-block
-  constexpr int SC_DMA = SK == 1 ? (2 * SROWS) / 64 / 4 : 0;   // byte DMAs per wave per stage
+  constexpr int NB = kBK / 32;                         // e8m0 blocks per row per stage
+  constexpr int SC_DMA = SK == 1 ? (NB * SROWS) / 64 / 4 : 0;   // byte DMAs per wave per stage
   constexpr int LPS = BPW + SC_DMA;                    // vector-memory ops per wave per stage
   // One array per ring slot, each accessed with a compile-time slot index, so the
   // compiler can tell a load landing in one slot from reads of another.
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[STAGE];
-  constexpr int SRB = SK == 1 ? 4 * 2 * SROWS : 16;   // byte DMAs land one lane per dword
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kSlots > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[kSlots > 2 ? STAGE : 16];
+  constexpr int SRB = SK == 1 ? 4 * NB * SROWS : 16;  // byte DMAs land one lane per dword
   __shared__ __attribute__((aligned(16))) uint8_t sring0[SRB];
   __shared__ __attribute__((aligned(16))) uint8_t sring1[SRB];
-  __shared__ __attribute__((aligned(16))) uint8_t sring2[SRB];
-  __shared__ __attribute__((aligned(16))) uint8_t sring3[SRB];
-  uint8_t* const slot_data[kSlots] = {ring0, ring1, ring2, ring3};
-  uint8_t* const slot_scale[kSlots] = {sring0, sring1, sring2, sring3};
+  __shared__ __attribute__((aligned(16))) uint8_t sring2[kSlots > 2 ? SRB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sring3[kSlots > 2 ? SRB : 16];
+  uint8_t* const slot_data[4] = {ring0, ring1, ring2, ring3};
+  uint8_t* const slot_scale[4] = {sring0, sring1, sring2, sring3};
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -237,19 +248,21 @@ void gemm_fp8_kernel(KParams p) {
   const int nk = c_hi > c_lo ? (c_hi - c_start + kBK - 1) / kBK : 0;
 
   // ---------------------------------------------------------------- DMA global -> LDS
-  // Wave `wave` moves blocks wave + 4*i (i < BPW) of each stage.  In a block,
-  // lane l fills LDS bytes [16 l, 16 l + 16): tile row 16*blk + l/4, physical
-  // chunk l%4, i.e. logical chunk (l%4) ^ ((l/16)%4) of that row.
-  const int dma_c = (lane & 3) ^ ((lane >> 4) & 3);
-  const uint8_t* rowp[BPW];
+  // Wave `wave` moves blocks wave + 4*i (i < BPW) of each stage; the first
+  // BPW_A of them lie in the A tile, the rest in the B tile.  In a block, lane l
+  // fills LDS bytes [16 l, 16 l + 16): tile row RPB*blk + l/CH, physical chunk
+  // l%CH, i.e. logical chunk (l%CH) ^ ((row >> SH) & (CH-1)), which is the same
+  // for every block of a wave.  Rows are 32-bit offsets from the uniform A/B
+  // tile bases (host validation bounds the row strides).
+  constexpr int BPW_A = BM / R::RPB / 4;
+  const int dma_c = (lane % CH) ^ (((R::RPB * wave + lane / CH) >> R::SH) & (CH - 1));
+  uint32_t roff[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
-    const int blk = wave + 4 * i;
-    const int r = 16 * blk + (lane >> 2);           // row in the concatenated [A; B] tile
-    rowp[i] = r < BM ? P + (int64_t)min(r, p_valid - 1) * p_ld
-                     : Q + (int64_t)min(r - BM, q_valid - 1) * q_ld;
+    const int r = R::RPB * (wave + 4 * i) + lane / CH;   // row in the concatenated [A; B] tile
+    roff[i] = i < BPW_A ? (uint32_t)(min(r, p_valid - 1) * p_ld) : (uint32_t)(min(r - BM, q_valid - 1) * q_ld);
   }
-  // e8m0: byte DMA d of a stage covers (block half d/(SROWS/64), rows 64*(d%(SROWS/64)) + lane)
+  // e8m0: byte DMA d of a stage covers (block d/(SROWS/64) of the stage, rows 64*(d%(SROWS/64)) + lane)
   const uint8_t* srow[SK == 1 ? SC_DMA : 1];
   if constexpr (SK == 1) {
 #pragma unroll
@@ -268,10 +281,11 @@ void gemm_fp8_kernel(KParams p) {
   auto issue_stage = [&](auto slot_tag, int kt) {
     constexpr int SLOT = decltype(slot_tag)::value;
     uint8_t* dst = slot_data[SLOT];
-    const int pos = min(c_start + kt * kBK + 16 * dma_c, pos_max);
+    const int base = c_start + kt * kBK;
+    const uint32_t pos = (uint32_t)min(base + 16 * dma_c, pos_max);
 #pragma unroll
     for (int i = 0; i < BPW; ++i)
-      dma_16(rowp[i] + pos, dst + (wave + 4 * i) * 1024);
+      dma_16((i < BPW_A ? P : Q) + (roff[i] + pos), dst + (wave + 4 * i) * 1024);
     if constexpr (SK == 1) {
       // e8m0 bytes past the range come from the row's last valid block; the
       // data they scale is zeroed, and the quantizer never emits the NaN code.
@@ -280,8 +294,8 @@ void gemm_fp8_kernel(KParams p) {
 #pragma unroll
       for (int i = 0; i < SC_DMA; ++i) {
         const int d = wave + 4 * i;
-        const int half = d / (SROWS / 64);
-        dma_1(srow[i] + max(min(blk0 + half, nblk - 1), 0), sdst + 256 * d);
+        const int b = d / (SROWS / 64);
+        dma_1(srow[i] + max(min(blk0 + b, nblk - 1), 0), sdst + 256 * d);
       }
     }
   };
@@ -296,69 +310,97 @@ void gemm_fp8_kernel(KParams p) {
 
   const int g = lane >> 5, lrow = lane & 31;
 
-  // One pipeline step: wait for stage kt (in slot SLOT), refill the slot that
-  // was computed last step with stage kt + kAhead, then run stage kt's MFMAs.
-  auto step = [&](auto slot_tag, int kt) {
-    constexpr int SLOT = decltype(slot_tag)::value;
-    constexpr int NEXT = (SLOT + kAhead) % kSlots;
-    // stage kt has landed once at most the later stages' loads are outstanding
-    const int later = min(kAhead - 1, nk - 1 - kt);
-    if (later >= 2) wait_vmcnt<2 * LPS>();
-    else if (later == 1) wait_vmcnt<LPS>();
+  // Wait until at most n later stages' loads are still outstanding.
+  auto wait_stages = [&](int n) {
+    if (n >= 3) wait_vmcnt<3 * LPS>();
+    else if (n == 2) wait_vmcnt<2 * LPS>();
+    else if (n == 1) wait_vmcnt<LPS>();
     else wait_vmcnt<0>();
-    raw_barrier();
-    uint8_t* st = slot_data[SLOT];
+  };
+  // Zero the bytes of every chunk of stage kt (in LDS `st`) outside or straddling
+  // [c_lo, c_hi).  Only the first and last stage of a range can hold such chunks.
+  auto fix_boundary = [&](uint8_t* st, int kt) {
     const int base = c_start + kt * kBK;
-    if (base < c_lo || base + kBK > c_hi) {          // boundary stage (uniform)
-      // zero the bytes of every chunk outside or straddling [c_lo, c_hi)
-      for (int idx = t; idx < SROWS * 4; idx += 256) {
-        const int r = idx >> 2, c = idx & 3, pos = base + 16 * c;
-        if (pos < c_lo || pos + 16 > c_hi) {
-          u32x4* q = reinterpret_cast<u32x4*>(st + stage_off(r, c));
-          *q = mask_chunk(*q, pos, c_lo, c_hi);
-        }
+    if (base >= c_lo && base + kBK <= c_hi) return;    // uniform
+    for (int idx = t; idx < SROWS * CH; idx += 256) {
+      const int r = idx / CH, c = idx % CH, pos = base + 16 * c;
+      if (pos < c_lo || pos + 16 > c_hi) {
+        u32x4* q = reinterpret_cast<u32x4*>(st + R::off(r, c));
+        *q = mask_chunk(*q, pos, c_lo, c_hi);
       }
-      wait_lgkmcnt0();
-      raw_barrier();
     }
-    if (kt + kAhead < nk) issue_stage(std::integral_constant<int, NEXT>{}, kt + kAhead);
+    wait_lgkmcnt0();
+    raw_barrier();
+  };
 
-    const uint8_t* sa_ = st;
-    const uint8_t* sb_ = st + A_BYTES;
-    const uint8_t* sc_ = slot_scale[SLOT];
-    v8i af[TM], bf[TN];
-    int scA[TM], scB[TN];
+  // Two register sets of MFMA fragments: stage k's MFMAs run from one while
+  // stage k+1's fragments are read from LDS into the other.
+  v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  int ea0[TM], eb0[TN], ea1[TM], eb1[TN];      // e8m0 scale operands
+  auto read_frags = [&](v8i (&fa)[TM], v8i (&fb)[TN], int (&ea)[TM], int (&eb)[TN], const uint8_t* st,
+                        const uint8_t* sc) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * WM + 32 * i + lrow;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + stage_off(r, g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + stage_off(r, 2 + g));
-      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (SK == 1) scA[i] = sc_[4 * (g * SROWS + r)];
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + R::off(r, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + R::off(r, 2 + g));
+      fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (SK == 1) ea[i] = sc[4 * (g * SROWS + r)];
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * WN + 32 * j + lrow;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + stage_off(r, g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + stage_off(r, 2 + g));
-      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (SK == 1) scB[j] = sc_[4 * (g * SROWS + BM + r)];
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 2 + g));
+      fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (SK == 1) eb[j] = sc[4 * (g * SROWS + BM + r)];
     }
+  };
+  auto mma = [&](v8i (&fa)[TM], v8i (&fb)[TN], int (&ea)[TM], int (&eb)[TN]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if constexpr (SK == 1)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, scA[i], 0,
-                                                                      scB[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, ea[i], 0,
+                                                                      eb[j]);
         else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
       }
   };
 
-  if (0 < nk) issue_stage(std::integral_constant<int, 0>{}, 0);
-  if (1 < nk) issue_stage(std::integral_constant<int, 1>{}, 1);
-  if (2 < nk) issue_stage(std::integral_constant<int, 2>{}, 2);
+  // One pipeline step for stage kt, held in ring slot SLOT (== kt % 4), whose
+  // fragments are already in register set SLOT % 2:
+  //  1. wait for stage kt+1 and for this wave's reads of slot SLOT, barrier
+  //     (stage kt+1 is visible; no wave still reads slot SLOT);
+  //  2. refill slot SLOT with stage kt+4;
+  //  3. read stage kt+1's fragments into the other set, then run stage kt's MFMAs.
+  auto step = [&](auto slot_tag, int kt) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int NS = (SLOT + 1) % kSlots;
+    wait_lgkmcnt0();   // on every path, so the MFMAs below never wait on the reads issued next
+    if (kt + 1 < nk) {
+      wait_stages(min(2, nk - 2 - kt));
+      raw_barrier();
+      fix_boundary(slot_data[NS], kt + 1);
+      if (kt + kSlots < nk) issue_stage(slot_tag, kt + kSlots);
+      if constexpr (SLOT % 2 == 0) read_frags(fa1, fb1, ea1, eb1, slot_data[NS], slot_scale[NS]);
+      else read_frags(fa0, fb0, ea0, eb0, slot_data[NS], slot_scale[NS]);
+    }
+    if constexpr (SLOT % 2 == 0) mma(fa0, fb0, ea0, eb0);
+    else mma(fa1, fb1, ea1, eb1);
+  };
+
+  if (nk > 0) {
+    issue_stage(std::integral_constant<int, 0>{}, 0);
+    if (1 < nk) issue_stage(std::integral_constant<int, 1>{}, 1);
+    if (2 < nk) issue_stage(std::integral_constant<int, 2>{}, 2);
+    if (3 < nk) issue_stage(std::integral_constant<int, 3>{}, 3);
+    wait_stages(min(3, nk - 1));
+    raw_barrier();
+    fix_boundary(slot_data[0], 0);
+    read_frags(fa0, fb0, ea0, eb0, slot_data[0], slot_scale[0]);
+  }
   for (int kt = 0; kt < nk; kt += kSlots) {
     step(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
@@ -419,7 +461,7 @@ static hipError_t launch_fp8(const GemmArgs& g, hipStream_t st) {
   }
   const int64_t total = (int64_t)p.row_units * p.col_tiles;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, MODE, SK, OUT>), dim3((unsigned)total), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, kGemmStageBytes, MODE, SK, OUT>), dim3((unsigned)total), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -127,9 +127,11 @@ int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const v
   if (a_bf16) {
     if (N % 8 || K % 8 || M % 8) return FP8MOE_ERR_ALIGN;
   } else if (mode == FP8MOE_GROUPED_M) {
+    if (K > (1 << 23)) return FP8MOE_ERR_SHAPE;     // tile-row offsets are 32-bit in the kernel
     if (K % 16) return FP8MOE_ERR_ALIGN;
     if (scale_kind == FP8MOE_SCALE_E8M0 && K % 32) return FP8MOE_ERR_ALIGN;
   } else {
+    if (M > (1 << 23)) return FP8MOE_ERR_SHAPE;     // tile-row offsets are 32-bit in the kernel
     if (M % 16) return FP8MOE_ERR_ALIGN;
     if (scale_kind == FP8MOE_SCALE_E8M0 && M % 32) return FP8MOE_ERR_ALIGN;
   }
