@@ -439,9 +439,569 @@ void gemm_fp8_kernel(KParams p) {
   }
 }
 
-template <int BM, int BN, int MODE, int SK, int OUT>
-static hipError_t launch_fp8(const GemmArgs& g, hipStream_t st) {
-  KParams p;
+// ============================================================================
+// Interleaved pipeline: 128-byte contraction stages.
+//
+// Measured on gfx950 (one workgroup per CU, operands resident in L2):
+//  * a direct global->LDS load moving 64-byte row segments delivers about half
+//    the bytes per clock of one moving whole 128-byte lines, so a stage spans
+//    BK = 128 contraction bytes (whole lines of K-contiguous operands);
+//  * issuing a stage's loads and LDS fragment reads as one burst ahead of its
+//    MFMAs stalls instruction issue and leaves the matrix cores idle for about
+//    a third of the loop; spreading them between the MFMAs of the same
+//    scheduling region (sched_group_barrier) keeps the matrix cores at ~95%.
+// A stage is (BM + BN) x 128 B: 64 KiB for 256 x 256 tiles, so the ring holds
+// two stages (one computing, one landing); 128 x 256 tiles hold three.  Each
+// stage runs as two 64-byte MFMA k steps; fragments of the next k step are read
+// from LDS while the current one's MFMAs issue.  The steady-state step is
+// branch-free so the interleave spans it; the first and last stages (which may
+// straddle the contraction range) go through a checked path.
+//
+// Swizzle of a 128-byte LDS row: logical chunk c of row r sits at physical
+// chunk c ^ ((r >> 1) & 7).  A 16-byte read serves 16 lanes per clock from 64
+// banks (256 bytes, two 128-byte rows): 16 consecutive rows reading one logical
+// chunk land on 16 distinct (row parity, chunk) slots.  The XOR term depends
+// on the row only through bits 1..3, so a fragment's address is affine in its
+// 32-row tile index and the compiler folds it into immediate offsets.
+template <int BK>
+struct PipeRing {
+  static_assert(BK == 64 || BK == 128, "stage width");
+  static constexpr int CH = BK / 16;          // 16-byte chunks per tile row
+  static constexpr int RPB = 1024 / BK;       // tile rows per 1 KiB DMA block
+  static __device__ __forceinline__ int phys(int r, int c) {
+    if constexpr (BK == 64) return c ^ ((r >> 2) & 3);
+    else return c ^ ((r >> 1) & 7);
+  }
+  static __device__ __forceinline__ int off(int r, int c) { return r * BK + (phys(r, c) << 4); }
+};
+
+__device__ __forceinline__ void dma_4(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// Place NM MFMAs of the current scheduling region with ND LDS reads and NV
+// global loads spread evenly between them.
+template <int NM, int ND, int NV, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NM) {
+    constexpr int d = ((I + 1) * ND) / NM - (I * ND) / NM;
+    constexpr int v = ((I + 1) * NV) / NM - (I * NV) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    interleave<NM, ND, NV, I + 1>();
+  }
+}
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices
+// for builtins that take immediates).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+template <int BM, int BN, int BK, int SLOTS, int MODE, int SK, int OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_fp8_pipe(KParams p) {
+  using R = PipeRing<BK>;
+  constexpr int CH = R::CH, KS = BK / 64;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  constexpr int BPW = STAGE / 1024 / 4, BPW_A = A_BYTES / 1024 / 4;   // 1 KiB DMA blocks per wave
+  constexpr int SROWS = BM + BN;
+  // e8m0: one 4-byte load per tile row and stage (the stage's four 32-blocks),
+  // 64 rows per wave-wide load, every wave issuing the same count.
+  constexpr int SC_DMA = SK == 1 ? (SROWS / 64 + 3) / 4 : 0;
+  constexpr int LPS = BPW + SC_DMA;                   // vector-memory ops per wave per stage
+  constexpr int SCB = SK == 1 ? SC_DMA * 4 * 256 : 16;
+  constexpr int NM = TM * TN;                         // MFMAs per k step
+  constexpr int ND = 2 * (TM + TN) + (SK == 1 ? TM + TN : 0);   // LDS reads per k step
+  static_assert(STAGE % 4096 == 0 && BPW_A * 4096 == A_BYTES, "stage must split into 4 waves of 1 KiB blocks");
+  static_assert(SK == 0 || BK == 128, "e8m0 scales need 128-byte stages");
+  static_assert((SLOTS * KS) % 2 == 0 && SLOTS >= 2 && SLOTS <= 4, "fragment sets alternate across the ring");
+  static_assert(SLOTS * (STAGE + SCB) <= 150 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[SLOTS > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[SLOTS > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sring0[SCB];
+  __shared__ __attribute__((aligned(16))) uint8_t sring1[SCB];
+  __shared__ __attribute__((aligned(16))) uint8_t sring2[SLOTS > 2 ? SCB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sring3[SLOTS > 3 ? SCB : 16];
+  uint8_t* const slot_data[4] = {ring0, ring1, ring2, ring3};
+  uint8_t* const slot_scale[4] = {sring0, sring1, sring2, sring3};
+
+  // ---------------------------------------------------------------- tile loop
+  // Persistent: the grid is at most one workgroup per CU and each walks the
+  // tiles with a stride of the grid.  Round k gives XCD x (dispatch is
+  // round-robin over 8) the contiguous logical tiles [G k + G/8 x, + G/8), so
+  // the tiles one XCD runs together share operand rows in its L2; logical
+  // tiles run in bands of kBandRows row tiles.  GROUPED_M counts its real row
+  // tiles on the device (the host knows only a bound), so no round is spent
+  // on empty tiles.
+  struct Ch {
+    __device__ int operator()(int lo, int hi) const { return (hi - lo + BM - 1) / BM; }
+  };
+  struct NoPad {
+    __device__ int operator()(int, int) const { return 0; }
+  };
+  int row_units = p.row_units;
+  if constexpr (MODE == 0) {
+    constexpr int kFar = 1 << 30;
+    row_units = kFar - find_unit<256>(p.offs, p.E, p.M, kFar, Ch{}, NoPad{}).j;
+  }
+  const int ntiles = row_units * p.col_tiles;
+  const int G = gridDim.x;
+  for (int it = 0;; ++it) {
+  const int L = (G & 7) == 0 ? G * it + (G >> 3) * (blockIdx.x & 7) + (blockIdx.x >> 3) : G * it + blockIdx.x;
+  if (L >= ntiles) break;
+  if (it > 0) {
+    wait_lgkmcnt0();
+    raw_barrier();   // the previous tile's epilogue is done with LDS
+  }
+  // Thread indices pass through an opaque copy each tile, so the compiler
+  // derives per-lane addresses inside the tile instead of hoisting (and
+  // spilling) all of them across the tile loop.
+  int t_opq = threadIdx.x;
+  asm volatile("" : "+v"(t_opq));
+  const int t = t_opq, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: scalar registers
+  const int wm = wave >> 1, wn = wave & 1;
+  const int band = L / (kBandRows * p.col_tiles);
+  const int first = band * kBandRows;
+  const int gsz = min(row_units - first, kBandRows);
+  const int inband = L % (kBandRows * p.col_tiles);
+  const int ru = first + inband % gsz;
+  const int ct = inband / gsz;
+
+  const uint8_t* P;
+  const uint8_t* Q;
+  int64_t p_ld, q_ld;
+  int p_valid, q_valid, c_lo, c_hi;
+  int64_t out_base, out_ld;
+  const uint8_t* psc = nullptr;   // e8m0 rows
+  const uint8_t* qsc = nullptr;
+  int64_t sc_ld = 0;
+  const float* psf = nullptr;     // fp32 scales of the tile's rows / columns
+  const float* qsf = nullptr;
+  if constexpr (MODE == 0) {
+    const Unit un = find_unit<256>(p.offs, p.E, p.M, ru, Ch{}, NoPad{});
+    if (un.e < 0) continue;   // not reached: ru < row_units
+    const int e = un.e;
+    const int m0 = un.lo + un.j * BM, n0 = ct * BN;
+    p_valid = min(BM, un.hi - m0);
+    q_valid = min(BN, p.N - n0);
+    P = p.a + (int64_t)m0 * p.K;
+    Q = p.b + ((int64_t)e * p.N + n0) * p.K;
+    p_ld = q_ld = p.K;
+    c_lo = 0;
+    c_hi = p.K;
+    out_ld = p.N;
+    out_base = (int64_t)m0 * p.N + n0;
+    if constexpr (SK == 1) {
+      sc_ld = p.K / 32;
+      psc = static_cast<const uint8_t*>(p.sa) + (int64_t)m0 * sc_ld;
+      qsc = static_cast<const uint8_t*>(p.sb) + ((int64_t)e * p.N + n0) * sc_ld;
+    } else {
+      psf = static_cast<const float*>(p.sa) + m0;
+      qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.N + n0;
+    }
+  } else {
+    const int ntn = (p.N + BM - 1) / BM;
+    const int e = ru / ntn;
+    const int n0 = (ru % ntn) * BM, k0 = ct * BN;
+    // group range of e: lo = max over j < e of clamp(offs[j]); hi = max(lo, clamp(offs[e]))
+    __shared__ int s_red[4];
+    int m = 0;
+    if (p.offs != nullptr)
+      for (int jj = t; jj < e; jj += 256) m = max(m, clamp_off(p.offs[jj], p.M));
+    m = (int)wave_max_u32((uint32_t)m);
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    const int lo = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+    const int hi = p.offs != nullptr ? max(lo, clamp_off(p.offs[e], p.M)) : p.M;
+    p_valid = min(BM, p.N - n0);
+    q_valid = min(BN, p.K - k0);
+    P = p.a + (int64_t)n0 * p.M;
+    Q = p.b + (int64_t)k0 * p.M;
+    p_ld = q_ld = p.M;
+    c_lo = lo;
+    c_hi = hi;
+    out_ld = p.K;
+    out_base = ((int64_t)e * p.N + n0) * p.K + k0;
+    if constexpr (SK == 1) {
+      sc_ld = p.M / 32;
+      psc = static_cast<const uint8_t*>(p.sa) + (int64_t)n0 * sc_ld;
+      qsc = static_cast<const uint8_t*>(p.sb) + (int64_t)k0 * sc_ld;
+    } else {
+      psf = static_cast<const float*>(p.sa) + (int64_t)e * p.N + n0;
+      qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.K + k0;
+    }
+  }
+
+  // Stages start on BK-aligned contraction positions (whole cache lines when
+  // the row stride is a multiple of 128); stage 0 may begin below c_lo and the
+  // last may end past c_hi: those bytes are zeroed in LDS before use.
+  // Reciprocals of the tile's row and column scales, for the epilogue (loaded
+  // now, so their latency hides behind the main loop).
+  __shared__ __attribute__((aligned(16))) float s_inv[SK == 0 ? BM + BN : 4];
+  if constexpr (SK == 0) {
+    for (int idx = t; idx < BM + BN; idx += 256)
+      s_inv[idx] = idx < BM ? __frcp_rn(psf[min(idx, p_valid - 1)]) : __frcp_rn(qsf[min(idx - BM, q_valid - 1)]);
+  }
+
+  const int c_start = c_lo & ~(BK - 1);
+  const int nk = c_hi > c_lo ? (c_hi - c_start + BK - 1) / BK : 0;
+
+  // ---------------------------------------------------------------- DMA global -> LDS
+  // Wave `wave` moves 1 KiB blocks wave + 4 i (i < BPW) of each stage (the
+  // first BPW_A lie in the A tile).  In a block, lane l fills LDS bytes
+  // [16 l, 16 l + 16): tile row RPB * blk + l / CH at physical chunk l % CH,
+  // i.e. logical chunk phys(row, l % CH) (the swizzle is an involution).  The
+  // swizzle term depends on row bits that a block step of 4 * RPB rows never
+  // changes, so the logical chunk is one per lane for all blocks.
+  // Block i covers rows r0 + 4 RPB i; its 32-bit offset (host validation
+  // bounds the row strides) is rebuilt in every step from a copy of r0 that the
+  // compiler cannot hoist, which keeps BPW loop-invariant offsets out of the
+  // register file at the cost of a few VALU ops between MFMAs.
+  const int lc16 = 16 * R::phys(R::RPB * wave + lane / CH, lane % CH);
+  const int r0 = R::RPB * wave + lane / CH;
+  const int pv1 = p_valid - 1, qv1 = q_valid - 1, pld = (int)p_ld, qld = (int)q_ld;
+  auto row_off = [&](int rr, int i) -> uint32_t {
+    return i < BPW_A ? (uint32_t)(min(rr + 4 * R::RPB * i, pv1) * pld + lc16)
+                     : (uint32_t)(min(rr + 4 * R::RPB * (i - BPW_A), qv1) * qld + lc16);
+  };
+  // e8m0: load d (< SC_DMA per wave, global index wave + 4 d) covers tile rows
+  // 64 (wave + 4 d) + lane; loads past the tile fetch row 0 into spare LDS.
+  const uint8_t* srow[SK == 1 ? SC_DMA : 1];
+  if constexpr (SK == 1) {
+#pragma unroll
+    for (int i = 0; i < SC_DMA; ++i) {
+      const int r = 64 * (wave + 4 * i) + lane;
+      srow[i] = r < BM ? psc + (int64_t)min(r, p_valid - 1) * sc_ld
+                       : (r < SROWS ? qsc + (int64_t)min(r - BM, q_valid - 1) * sc_ld : psc);
+    }
+  }
+  auto issue_scales = [&](uint8_t* sdst, int kt) {
+    if constexpr (SK == 1) {
+      const int blk0 = (c_start + kt * BK) >> 5;
+#pragma unroll
+      for (int i = 0; i < SC_DMA; ++i) dma_4(srow[i] + blk0, sdst + 256 * (wave + 4 * i));
+    }
+  };
+  // Steady-state stage: every position lies inside [c_lo, c_hi).
+  auto issue_main = [&](auto slot_tag, int kt) {
+    constexpr int S = decltype(slot_tag)::value;
+    uint8_t* dst = slot_data[S];
+    const uint32_t base = (uint32_t)(c_start + kt * BK);
+    int rr = r0;
+    asm volatile("" : "+v"(rr));
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) dma_16((i < BPW_A ? P : Q) + (row_off(rr, i) + base), dst + (wave + 4 * i) * 1024);
+    issue_scales(slot_scale[S], kt);
+  };
+  // Checked stage: positions past the range are clamped to the last chunk that
+  // overlaps it (zeroed in LDS later), so every lane still issues one load per
+  // block (the wait counts rely on it).
+  const int pos_max = max((c_hi - 1) & ~15, 0);
+  auto issue_checked = [&](auto slot_tag, int kt) {
+    constexpr int S = decltype(slot_tag)::value;
+    uint8_t* dst = slot_data[S];
+    const int base = c_start + kt * BK;
+    const uint32_t pos = (uint32_t)min(base + lc16, pos_max) - (uint32_t)lc16;
+    int rr = r0;
+    asm volatile("" : "+v"(rr));
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) dma_16((i < BPW_A ? P : Q) + (row_off(rr, i) + pos), dst + (wave + 4 * i) * 1024);
+    issue_scales(slot_scale[S], kt);
+  };
+
+  // Wait until at most n later stages' loads are still outstanding.
+  auto wait_stages = [&](int n) {
+    if (n >= 3) wait_vmcnt<3 * LPS>();
+    else if (n == 2) wait_vmcnt<2 * LPS>();
+    else if (n == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+  };
+  // Zero the bytes of every chunk of stage kt (in LDS `st`) outside or
+  // straddling [c_lo, c_hi).  Only the first and last stage can hold such chunks.
+  auto fix_boundary = [&](uint8_t* st, int kt) {
+    const int base = c_start + kt * BK;
+    if (base >= c_lo && base + BK <= c_hi) return;    // uniform
+    for (int idx = t; idx < SROWS * CH; idx += 256) {
+      const int r = idx / CH, c = idx % CH, pos = base + 16 * c;
+      if (pos < c_lo || pos + 16 > c_hi) {
+        u32x4* q = reinterpret_cast<u32x4*>(st + R::off(r, c));
+        *q = mask_chunk(*q, pos, c_lo, c_hi);
+      }
+    }
+    wait_lgkmcnt0();
+    raw_barrier();
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int g = lane >> 5, lrow = lane & 31;
+  // Two register sets of MFMA fragments (one 64-byte k step each).
+  v8i fa[2][TM], fb[2][TN];
+  // e8m0 scale operands: byte i of ea[set] is fragment i's scale (the MFMA
+  // picks it with op_sel), likewise eb.
+  static_assert(TM <= 4 && TN <= 4, "four scale bytes per register");
+  int ea[2], eb[2];
+  // Fragments of k step h of the stage in LDS `st` (scales in `sc`) into set SET.
+  auto rd = [&](auto set_tag, const uint8_t* st, const uint8_t* sc, int h) {
+    constexpr int SET = decltype(set_tag)::value;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + 32 * i + lrow;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + 2 + g));
+      fa[SET][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (SK == 1) {
+        const int s = sc[4 * r + 2 * h + g];
+        ea[SET] = i == 0 ? s : (ea[SET] | (s << (8 * i)));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WN + 32 * j + lrow;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + 2 + g));
+      fb[SET][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (SK == 1) {
+        const int s = sc[4 * (BM + r) + 2 * h + g];
+        eb[SET] = j == 0 ? s : (eb[SET] | (s << (8 * j)));
+      }
+    }
+  };
+  auto mma = [&](auto set_tag) {
+    constexpr int SET = decltype(set_tag)::value;
+    static_for<TM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      static_for<TN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (SK == 1)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[SET][i], fb[SET][j], acc[i][j], 0, 0, i,
+                                                                      ea[SET], j, eb[SET]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[SET][i], fb[SET][j], acc[i][j], 0, 0, 0, 0,
+                                                                      0, 0);
+      });
+    });
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // k steps of stage kt (ring slot S) before its last: read the next k step of
+  // the same stage into the other set while this one's MFMAs issue.
+  auto inner_halves = [&](auto slot_tag) {
+    constexpr int S = decltype(slot_tag)::value;
+    if constexpr (KS == 2) {
+      constexpr int CUR = (S * KS) & 1;
+      rd(std::integral_constant<int, 1 - CUR>{}, slot_data[S], slot_scale[S], 1);
+      mma(std::integral_constant<int, CUR>{});
+      interleave<NM, ND, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Steady-state step for stage kt in slot S (kt + SLOTS <= nk - 2):
+  //  1. k steps of stage kt but the last;
+  //  2. wait for stage kt+1 and this wave's reads of slot S, barrier (stage
+  //     kt+1 visible everywhere; no wave still reads slot S);
+  //  3. refill slot S with stage kt+SLOTS, read stage kt+1's first k step into
+  //     the other set and run the last k step's MFMAs, all interleaved.
+  auto step_main = [&](auto slot_tag, int kt) {
+    constexpr int S = decltype(slot_tag)::value, NS = (S + 1) % SLOTS;
+    constexpr int CUR = (S * KS + KS - 1) & 1;
+    inner_halves(slot_tag);
+    wait_lgkmcnt0();
+    wait_vmcnt<(SLOTS - 2) * LPS>();
+    raw_barrier();
+    issue_main(slot_tag, kt + SLOTS);
+    rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
+    mma(std::integral_constant<int, CUR>{});
+    interleave<NM, ND, LPS>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Checked step: the last SLOTS + 1 stages (boundary fix-ups, no refill past nk).
+  auto step_tail = [&](auto slot_tag, int kt) {
+    constexpr int S = decltype(slot_tag)::value, NS = (S + 1) % SLOTS;
+    constexpr int CUR = (S * KS + KS - 1) & 1;
+    inner_halves(slot_tag);
+    wait_lgkmcnt0();
+    if (kt + 1 < nk) {
+      wait_stages(min(SLOTS - 2, nk - 2 - kt));
+      raw_barrier();
+      fix_boundary(slot_data[NS], kt + 1);
+      if (kt + SLOTS < nk) issue_checked(slot_tag, kt + SLOTS);
+      rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
+    }
+    mma(std::integral_constant<int, CUR>{});
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nk > 0) {
+    issue_checked(I0{}, 0);
+    if (1 < nk) issue_checked(I1{}, 1);
+    if constexpr (SLOTS > 2) if (2 < nk) issue_checked(std::integral_constant<int, 2>{}, 2);
+    if constexpr (SLOTS > 3) if (3 < nk) issue_checked(std::integral_constant<int, 3>{}, 3);
+    wait_stages(min(SLOTS - 1, nk - 1));
+    raw_barrier();
+    fix_boundary(slot_data[0], 0);
+    rd(I0{}, slot_data[0], slot_scale[0], 0);
+  }
+  // Two loops (a per-step choice between the two step kinds inside one loop
+  // defeats register allocation): whole rounds of steady-state steps, then
+  // checked steps to the end.
+  const int nmain = max(nk - SLOTS - 1, 0);
+  int kt = 0;
+  for (; kt + SLOTS <= nmain; kt += SLOTS) {
+    step_main(I0{}, kt);
+    step_main(I1{}, kt + 1);
+    if constexpr (SLOTS > 2) step_main(std::integral_constant<int, 2>{}, kt + 2);
+    if constexpr (SLOTS > 3) step_main(std::integral_constant<int, 3>{}, kt + 3);
+  }
+  for (; kt < nk; kt += SLOTS) {
+    step_tail(I0{}, kt);
+    if (kt + 1 < nk) step_tail(I1{}, kt + 1);
+    if constexpr (SLOTS > 2) if (kt + 2 < nk) step_tail(std::integral_constant<int, 2>{}, kt + 2);
+    if constexpr (SLOTS > 3) if (kt + 3 < nk) step_tail(std::integral_constant<int, 3>{}, kt + 3);
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // fp32 scales are multipliers of the quantized operands: divide by both.
+  // (s_inv was written before the main loop's first barrier.)
+  const bool empty = c_hi <= c_lo;
+  float inv_q[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) inv_q[j] = SK == 0 ? s_inv[BM + wn * WN + 32 * j + lrow] : 1.0f;
+  auto inv_row = [&](int r) { return SK == 0 ? s_inv[min(r, BM - 1)] : 1.0f; };
+  constexpr int ELEM = OUT == 0 ? 2 : 4;
+  if (((int64_t)out_ld * ELEM) % 16 == 0) {
+    // Stage each wave's (BM/2) x (BN/2) results through LDS (the ring is free
+    // now) and write whole 16-byte pieces of output rows.  bf16: neighbouring
+    // lanes (adjacent columns) swap one value per row pair so that each lane
+    // writes a 4-byte word; fp32 takes two passes over the rows.  Staged rows
+    // are WN * ELEM bytes; 16-byte chunk k of staged row r sits at chunk
+    // k ^ sw(r), which spreads the rows one write instruction touches (row
+    // parity x lane half) over distinct banks, while a 16-lane read of one
+    // whole row stays conflict-free.
+    constexpr int PASSES = (OUT == 0 || TM < 2) ? 1 : 2;
+    constexpr int TMP = TM / PASSES;            // 32-row blocks per pass
+    constexpr int RB = WN * ELEM;               // staged row bytes
+    constexpr int NCH = RB / 16;                // 16-byte chunks per staged row
+    constexpr int WBYTES = TMP * 32 * RB;
+    constexpr int VEC = 16 / ELEM;              // elements per 16-byte piece
+    static_assert(2 * WBYTES <= STAGE, "staging fits in two ring slots");
+    uint8_t* const stg = (wave < 2 ? ring0 : ring1) + (wave & 1) * WBYTES;
+    auto sw = [](int r) { return OUT == 0 ? ((r & 1) * 4 + ((r >> 2) & 1) * 8) : (((r >> 2) & 1) * 8); };
+    wait_lgkmcnt0();
+    raw_barrier();   // every wave is past its last fragment read of the ring
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      if (pass > 0) wait_lgkmcnt0();   // this wave's reads of the previous pass are done
+#pragma unroll
+      for (int ii = 0; ii < TMP; ++ii) {
+        const int i = pass * TMP + ii;
+        float inv_p[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (SK == 0) {
+            const float4 f = *reinterpret_cast<const float4*>(&s_inv[wm * WM + 32 * i + 8 * q + 4 * g]);
+            inv_p[4 * q] = f.x; inv_p[4 * q + 1] = f.y; inv_p[4 * q + 2] = f.z; inv_p[4 * q + 3] = f.w;
+          } else {
+            inv_p[4 * q] = inv_p[4 * q + 1] = inv_p[4 * q + 2] = inv_p[4 * q + 3] = 1.0f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = 32 * j + lrow;                // column within the wave's staged row
+          if constexpr (OUT == 0) {
+            const bool odd = lane & 1;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int v0 = 2 * k, v1 = 2 * k + 1;     // rows rho(v0), rho(v0) + 1
+              const float a = empty ? 0.0f : acc[i][j][v0] * inv_p[v0] * inv_q[j];
+              const float b = empty ? 0.0f : acc[i][j][v1] * inv_p[v1] * inv_q[j];
+              const float send = odd ? a : b;
+              const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+              const float lo = odd ? recv : a, hi = odd ? b : recv;
+              const uint32_t word = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+              const int lr = 32 * ii + 8 * (v0 >> 2) + 4 * g + (v0 & 3) + (odd ? 1 : 0);
+              const int dw = (c & ~1) >> 1;             // word index in the staged row
+              *reinterpret_cast<uint32_t*>(stg + lr * RB + (((dw >> 2) ^ sw(lr)) << 4) + ((dw & 3) << 2)) = word;
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float val = empty ? 0.0f : acc[i][j][v] * inv_p[v] * inv_q[j];
+              const int lr = 32 * ii + 8 * (v >> 2) + 4 * g + (v & 3);
+              *reinterpret_cast<float*>(stg + lr * RB + (((c >> 2) ^ sw(lr)) << 4) + ((c & 3) << 2)) = val;
+            }
+          }
+        }
+      }
+      wait_lgkmcnt0();   // a wave reads back only its own staging area
+      constexpr int RPI = 64 / NCH;                 // staged rows per read instruction
+#pragma unroll
+      for (int it = 0; it < TMP * 32 / RPI; ++it) {
+        const int lr = it * RPI + lane / NCH, k = lane % NCH;
+        const u32x4 d = *reinterpret_cast<const u32x4*>(stg + lr * RB + ((k ^ sw(lr)) << 4));
+        const int r = wm * WM + pass * TMP * 32 + lr, c = wn * WN + k * VEC;
+        if (r >= p_valid) continue;
+        uint8_t* dst = static_cast<uint8_t*>(p.out) + (out_base + (int64_t)r * out_ld + c) * ELEM;
+        if (c + VEC <= q_valid) {
+          *reinterpret_cast<u32x4*>(dst) = d;
+        } else {
+          const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            if (c + e >= q_valid) break;
+            if constexpr (OUT == 0)
+              reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            else
+              reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+          }
+        }
+      }
+    }
+    continue;
+  }
+  // Output rows not 16-byte aligned: element stores straight from registers.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (r >= p_valid) continue;
+      const float inv_p = inv_row(r);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int c = wn * WN + 32 * j + lrow;
+        if (c >= q_valid) continue;
+        const float val = empty ? 0.0f : acc[i][j][v] * inv_p * inv_q[j];
+        const int64_t o = out_base + (int64_t)r * out_ld + c;
+        if constexpr (OUT == 0)
+          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(val);
+        else
+          static_cast<float*>(p.out)[o] = val;
+      }
+    }
+  }
+  }   // tile loop
+}
+
+static void fill_params(KParams& p, const GemmArgs& g, int BM, int BN) {
   p.a = static_cast<const uint8_t*>(g.a);
   p.b = static_cast<const uint8_t*>(g.b);
   p.sa = g.sa;
@@ -452,16 +1012,49 @@ static hipError_t launch_fp8(const GemmArgs& g, hipStream_t st) {
   p.M = (int)g.M;
   p.N = (int)g.N;
   p.K = (int)g.K;
-  if (MODE == 0) {
+  if (g.mode == 0) {
     p.row_units = (int)((g.M + BM - 1) / BM + g.n_groups);
     p.col_tiles = (int)((g.N + BN - 1) / BN);
   } else {
     p.row_units = (int)(g.n_groups * ((g.N + BM - 1) / BM));
     p.col_tiles = (int)((g.K + BN - 1) / BN);
   }
+}
+
+// 64-byte-stage kernel with byte-wise e8m0 loads: MX operands whose scale rows
+// are not 4-byte aligned per 128-byte stage.
+template <int BM, int BN, int MODE, int OUT>
+static hipError_t launch_mx_bytewise(const GemmArgs& g, hipStream_t st) {
+  KParams p;
+  fill_params(p, g, BM, BN);
   const int64_t total = (int64_t)p.row_units * p.col_tiles;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, kGemmStageBytes, MODE, SK, OUT>), dim3((unsigned)total), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, kGemmStageBytes, MODE, 1, OUT>), dim3((unsigned)total), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int BM, int BN, int BK, int SLOTS, int MODE, int SK, int OUT>
+static hipError_t launch_pipe(const GemmArgs& g, hipStream_t st) {
+  KParams p;
+  fill_params(p, g, BM, BN);
+  const int64_t total = (int64_t)p.row_units * p.col_tiles;   // GROUPED_M: a bound
+  if (total == 0) return hipSuccess;
+  // One workgroup fits per CU (LDS); a persistent grid of at most one per CU.
+  const int64_t grid = std::min<int64_t>(total, cu_count());
+  hipLaunchKernelGGL((gemm_fp8_pipe<BM, BN, BK, SLOTS, MODE, SK, OUT>), dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -469,7 +1062,16 @@ template <int MODE, int SK, int OUT>
 static hipError_t pick_tile(const GemmArgs& g, hipStream_t st) {
   // GROUPED_M with small average groups wastes less of a 128-row tile.
   const bool small = MODE == 0 && g.n_groups > 1 && g.M / g.n_groups < 512;
-  return small ? launch_fp8<128, 256, MODE, SK, OUT>(g, st) : launch_fp8<256, 256, MODE, SK, OUT>(g, st);
+  if constexpr (SK == 1) {
+    // Each 128-byte stage takes one aligned 4-byte word of every e8m0 row.
+    const int64_t clen = MODE == 0 ? g.K : g.M;
+    const bool aligned = clen % 128 == 0 && (reinterpret_cast<uintptr_t>(g.sa) & 3) == 0 &&
+                         (reinterpret_cast<uintptr_t>(g.sb) & 3) == 0;
+    if (!aligned)
+      return small ? launch_mx_bytewise<128, 256, MODE, OUT>(g, st) : launch_mx_bytewise<256, 256, MODE, OUT>(g, st);
+  }
+  return small ? launch_pipe<128, 256, 128, 3, MODE, SK, OUT>(g, st)
+               : launch_pipe<256, 256, 128, 2, MODE, SK, OUT>(g, st);
 }
 
 template <int MODE>
