@@ -48,6 +48,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--only", default=None, metavar="ITEM",
+                    help="profiling aid: warm up the whole step, then time only launch ITEM (e.g. 'gemm fwd'), "
+                         "after a marker kernel so counter passes can isolate its dispatches")
+    ap.add_argument("--write-traffic", nargs=4, default=None,
+                    metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="write profiles/traffic.json for --only ITEM of --config from rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE databases of an --only run and of a --copy-probe run")
+    ap.add_argument("--copy-mib", type=int, default=512, help="size of the --copy-probe run behind the calibration")
     return ap.parse_args()
 
 
@@ -291,6 +299,67 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def _dispatch_counters(db: str, counter: str):
+    """[(dispatch_id, kernel_name, value)] of one PMC counter, in dispatch order (value summed
+    over the counter's instances)."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    acc = {}
+    for name, cn, val, disp in cur.execute(
+            "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+        if cn != counter:
+            continue
+        k = acc.setdefault(disp, [name, 0.0])
+        k[1] += val
+    return [(d, acc[d][0], acc[d][1]) for d in sorted(acc)]
+
+
+def _item_kib(db: str, counter: str, steps: int) -> float:
+    """Counter KiB per launch of the --only item: the run of library dispatches after the last
+    dispatch of any other kernel (the marker), divided by the number of timed launches."""
+    rows = _dispatch_counters(db, counter)
+    tail = []
+    for d, name, v in reversed(rows):
+        if "fp8moe::" not in name:
+            break
+        tail.append(v)
+    if not tail:
+        raise SystemExit(f"{db}: no library dispatches after the marker")
+    return sum(tail) / steps
+
+
+def _copy_factor(db: str, counter: str, nbytes: int) -> float:
+    rows = _dispatch_counters(db, counter)
+    vals = sorted((v for _, _, v in rows), reverse=True)[:3]
+    return nbytes / (float(np.mean(vals)) * 1024.0)
+
+
+def write_traffic(args):
+    fdb, wdb, cfdb, cwdb = args.write_traffic
+    if not args.only:
+        raise SystemExit("--write-traffic needs --only ITEM (the item the databases were taken for)")
+    nbytes = args.copy_mib << 20
+    ff, fw = _copy_factor(cfdb, "FETCH_SIZE", nbytes), _copy_factor(cwdb, "WRITE_SIZE", nbytes)
+    fetch = _item_kib(fdb, "FETCH_SIZE", args.steps) * 1024.0 * ff
+    write = _item_kib(wdb, "WRITE_SIZE", args.steps) * 1024.0 * fw
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(p)) if os.path.exists(p) else {}
+    if d.get("source_digest") != kernel_source_digest():
+        d = {"source_digest": kernel_source_digest(), "per_launch_bytes": {}, "detail": {}}
+    key = f"cfg{args.config}:{args.only}"
+    d["per_launch_bytes"][key] = round(fetch + write)
+    d["detail"][key] = {"fetch_bytes": round(fetch), "write_bytes": round(write),
+                        "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
+                        "timed_launches": args.steps,
+                        "counter_runs": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python bench.py --config "
+                                        f"{args.config} --only '{args.only}' --steps {args.steps} --warmup 1 "
+                                        f"--no-cpu-baseline; calibration: the same counters on "
+                                        f"python bench.py --copy-probe {args.copy_mib}"}
+    with open(p, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+    print(json.dumps({key: d["detail"][key], "per_launch_bytes": d["per_launch_bytes"][key]}))
+
+
 def traffic_for(kernel_item: str, cfg: int):
     """HBM bytes per launch measured by rocprofv3 PMC (profiles/traffic.json), or None
     if absent or taken on a different kernel source."""
@@ -310,6 +379,9 @@ def traffic_for(kernel_item: str, cfg: int):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
@@ -335,6 +407,13 @@ def main():
         for it in step.items:
             it[2]()
     torch.cuda.synchronize()
+    if args.only is not None:
+        sel = [it for it in step.items if it[0] == args.only]
+        if not sel:
+            raise SystemExit(f"--only: no launch named {args.only!r}; launches: {names}")
+        step.items = sel
+        torch.zeros(1, device="cuda:0").add_(1)      # marker dispatch for counter passes
+        torch.cuda.synchronize()
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in step.items]
           for _ in range(args.steps)]
@@ -383,7 +462,8 @@ def main():
         "config": {"workload": w.name, "experts": w.E, "routed_rows": w.M, "hidden": w.H,
                    "w1_out": w.F2, "w2_in": w.F,
                    "step": ("fwd" if args.config == 1 else "fwd+dgrad+wgrad") + ("+bf16 wgrad" if args.gw else ""),
-                   "recipe": "mxfp8 (e8m0 per 1x32)" if w.mx else "fp8 e4m3fn rowwise + colwise backward"},
+                   "recipe": "mxfp8 (e8m0 per 1x32)" if w.mx else "fp8 e4m3fn rowwise + colwise backward",
+                   **({"only": args.only} if args.only else {})},
         "quant_GBps": round(q_bytes / q_us / 1e3, 1) if q_us else None,
         "quant_us": round(q_us, 1),
         "gemm_TFLOPs": round(g_flops / g_us / 1e6, 1) if g_us else None,
