@@ -46,6 +46,9 @@ namespace fp8moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBandRows = 8;   // row tiles per band in the tile order
 constexpr int kGemmStageBytes = 64;   // contraction bytes per pipeline stage
@@ -493,6 +496,17 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// A wave-uniform value moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  return reinterpret_cast<T*>(uniform_i64(reinterpret_cast<int64_t>(p)));
+}
+
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices
 // for builtins that take immediates).
 template <int N, int I = 0, typename F>
@@ -535,7 +549,7 @@ void gemm_fp8_pipe(KParams p) {
   uint8_t* const slot_data[4] = {ring0, ring1, ring2, ring3};
   uint8_t* const slot_scale[4] = {sring0, sring1, sring2, sring3};
 
-  // ---------------------------------------------------------------- tile loop
+  // ---------------------------------------------------------------- tiles
   // Persistent: the grid is at most one workgroup per CU and each walks the
   // tiles with a stride of the grid.  Round k gives XCD x (dispatch is
   // round-robin over 8) the contiguous logical tiles [G k + G/8 x, + G/8), so
@@ -543,119 +557,182 @@ void gemm_fp8_pipe(KParams p) {
   // tiles run in bands of kBandRows row tiles.  GROUPED_M counts its real row
   // tiles on the device (the host knows only a bound), so no round is spent
   // on empty tiles.
+  //
+  // Consecutive tiles of a workgroup overlap: once a tile's last stage has
+  // been read, the next tile's stage 0 is loaded into ring slot 0 while the
+  // epilogue stages results through the last slot.  (Loads and stores share
+  // one counter on gfx9 and may complete out of order with respect to each
+  // other, so the next tile starts with a full drain before using stage 0.)
   struct Ch {
     __device__ int operator()(int lo, int hi) const { return (hi - lo + BM - 1) / BM; }
   };
   struct NoPad {
     __device__ int operator()(int, int) const { return 0; }
   };
+  // Group table (up to kTableGroups groups): g_hi[e] = hi(e) and, for
+  // GROUPED_M, g_pre[e] = row tiles of groups before e (g_pre[E] = all), built
+  // once per launch so a tile finds its group by a binary search in LDS.
+  // More groups: the block-wide scan per tile (find_unit).
+  constexpr int kTableGroups = 256;
+  __shared__ int g_hi[kTableGroups];
+  __shared__ int g_pre[kTableGroups + 1];
+  const bool table = p.E <= kTableGroups;
+  if (table) {
+    __shared__ int s_tmp[4];
+    const int t = threadIdx.x;
+    const int v = t < p.E ? (p.offs != nullptr ? clamp_off(p.offs[t], p.M) : p.M) : 0;
+    const int hi = block_scan_max<256>(v, s_tmp);
+    if (t < p.E) g_hi[t] = hi;
+    __syncthreads();
+    if constexpr (MODE == 0) {
+      const int lo = t == 0 ? 0 : g_hi[t - 1];
+      const int cnt = t < p.E ? (hi - lo + BM - 1) / BM : 0;
+      const int incl = block_scan_sum<256>(cnt, s_tmp);
+      if (t < p.E) g_pre[t + 1] = incl;
+      if (t == 0) g_pre[0] = 0;
+      __syncthreads();
+    }
+  }
   int row_units = p.row_units;
   if constexpr (MODE == 0) {
     constexpr int kFar = 1 << 30;
-    row_units = kFar - find_unit<256>(p.offs, p.E, p.M, kFar, Ch{}, NoPad{}).j;
+    row_units = table ? g_pre[p.E] : kFar - find_unit<256>(p.offs, p.E, p.M, kFar, Ch{}, NoPad{}).j;
+    row_units = __builtin_amdgcn_readfirstlane(row_units);
   }
   const int ntiles = row_units * p.col_tiles;
   const int G = gridDim.x;
-  for (int it = 0;; ++it) {
-  const int L = (G & 7) == 0 ? G * it + (G >> 3) * (blockIdx.x & 7) + (blockIdx.x >> 3) : G * it + blockIdx.x;
-  if (L >= ntiles) break;
-  if (it > 0) {
-    wait_lgkmcnt0();
-    raw_barrier();   // the previous tile's epilogue is done with LDS
-  }
-  // Thread indices pass through an opaque copy each tile, so the compiler
-  // derives per-lane addresses inside the tile instead of hoisting (and
-  // spilling) all of them across the tile loop.
-  int t_opq = threadIdx.x;
-  asm volatile("" : "+v"(t_opq));
-  const int t = t_opq, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: scalar registers
-  const int wm = wave >> 1, wn = wave & 1;
-  const int band = L / (kBandRows * p.col_tiles);
-  const int first = band * kBandRows;
-  const int gsz = min(row_units - first, kBandRows);
-  const int inband = L % (kBandRows * p.col_tiles);
-  const int ru = first + inband % gsz;
-  const int ct = inband / gsz;
+  auto tile_of = [&](int it) {
+    return (G & 7) == 0 ? G * it + (G >> 3) * (blockIdx.x & 7) + (blockIdx.x >> 3) : G * it + blockIdx.x;
+  };
+  // Contraction-contiguous row stride of both operands, output row stride and
+  // e8m0 row length: fixed per launch.
+  const int ld = MODE == 0 ? p.K : p.M;
+  const int64_t out_ld = MODE == 0 ? p.N : p.K;
+  const int sc_ld = MODE == 0 ? p.K / 32 : p.M / 32;
 
-  const uint8_t* P;
-  const uint8_t* Q;
-  int64_t p_ld, q_ld;
-  int p_valid, q_valid, c_lo, c_hi;
-  int64_t out_base, out_ld;
-  const uint8_t* psc = nullptr;   // e8m0 rows
-  const uint8_t* qsc = nullptr;
-  int64_t sc_ld = 0;
-  const float* psf = nullptr;     // fp32 scales of the tile's rows / columns
-  const float* qsf = nullptr;
-  if constexpr (MODE == 0) {
-    const Unit un = find_unit<256>(p.offs, p.E, p.M, ru, Ch{}, NoPad{});
-    if (un.e < 0) continue;   // not reached: ru < row_units
-    const int e = un.e;
-    const int m0 = un.lo + un.j * BM, n0 = ct * BN;
-    p_valid = min(BM, un.hi - m0);
-    q_valid = min(BN, p.N - n0);
-    P = p.a + (int64_t)m0 * p.K;
-    Q = p.b + ((int64_t)e * p.N + n0) * p.K;
-    p_ld = q_ld = p.K;
-    c_lo = 0;
-    c_hi = p.K;
-    out_ld = p.N;
-    out_base = (int64_t)m0 * p.N + n0;
-    if constexpr (SK == 1) {
-      sc_ld = p.K / 32;
-      psc = static_cast<const uint8_t*>(p.sa) + (int64_t)m0 * sc_ld;
-      qsc = static_cast<const uint8_t*>(p.sb) + ((int64_t)e * p.N + n0) * sc_ld;
-    } else {
+  // Everything a tile needs, from its logical index.
+  struct Tile {
+    const uint8_t* P;       // first row of the row operand (A rows / output rows)
+    const uint8_t* Q;       // first row of the column operand (B rows / output columns)
+    const uint8_t* psc;     // e8m0 rows of P and Q
+    const uint8_t* qsc;
+    int64_t out_base;
+    int pv, qv;             // valid rows of P and Q in the tile
+    int c_lo, c_hi;         // contraction range
+    int c_start, nk;        // first stage position (BK-aligned) and stage count
+  };
+  __shared__ __attribute__((aligned(16))) float s_inv[2][SK == 0 ? BM + BN : 4];
+  constexpr int SPT = (BM + BN + 255) / 256;   // fp32 scales per thread
+  // Fill `tl` for logical tile L and start loading its fp32 scales into `sv`
+  // (scale_commit turns them into reciprocals in LDS).  Every thread calls it
+  // (without a group table it synchronizes the workgroup).
+  auto setup = [&](int L, Tile& tl, float (&sv)[SPT]) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int band = L / (kBandRows * p.col_tiles);
+    const int first = band * kBandRows;
+    const int gsz = min(row_units - first, kBandRows);
+    const int inband = L % (kBandRows * p.col_tiles);
+    const int ru = first + inband % gsz;
+    const int ct = inband / gsz;
+    const float* psf = nullptr;   // fp32 scales of the tile's rows / columns
+    const float* qsf = nullptr;
+    if constexpr (MODE == 0) {
+      Unit un;
+      if (table) {
+        int a = 0, b = p.E;   // g_pre[a] <= ru < g_pre[b]
+        while (b - a > 1) {
+          const int mid = (a + b) >> 1;
+          if (g_pre[mid] <= ru) a = mid;
+          else b = mid;
+        }
+        un = Unit{a, ru - g_pre[a], a == 0 ? 0 : g_hi[a - 1], g_hi[a], 0};
+      } else {
+        un = find_unit<256>(p.offs, p.E, p.M, ru, Ch{}, NoPad{});
+      }
+      const int e = max(un.e, 0);   // un.e >= 0: ru < row_units
+      const int m0 = un.e < 0 ? 0 : un.lo + un.j * BM, n0 = ct * BN;
+      tl.pv = un.e < 0 ? 0 : min(BM, un.hi - m0);
+      tl.qv = min(BN, p.N - n0);
+      tl.P = p.a + (int64_t)m0 * p.K;
+      tl.Q = p.b + ((int64_t)e * p.N + n0) * p.K;
+      tl.c_lo = 0;
+      tl.c_hi = tl.pv > 0 ? p.K : 0;
+      tl.out_base = (int64_t)m0 * p.N + n0;
+      tl.psc = static_cast<const uint8_t*>(p.sa) + (int64_t)m0 * sc_ld;
+      tl.qsc = static_cast<const uint8_t*>(p.sb) + ((int64_t)e * p.N + n0) * sc_ld;
       psf = static_cast<const float*>(p.sa) + m0;
       qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.N + n0;
-    }
-  } else {
-    const int ntn = (p.N + BM - 1) / BM;
-    const int e = ru / ntn;
-    const int n0 = (ru % ntn) * BM, k0 = ct * BN;
-    // group range of e: lo = max over j < e of clamp(offs[j]); hi = max(lo, clamp(offs[e]))
-    __shared__ int s_red[4];
-    int m = 0;
-    if (p.offs != nullptr)
-      for (int jj = t; jj < e; jj += 256) m = max(m, clamp_off(p.offs[jj], p.M));
-    m = (int)wave_max_u32((uint32_t)m);
-    if (lane == 0) s_red[wave] = m;
-    __syncthreads();
-    const int lo = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
-    const int hi = p.offs != nullptr ? max(lo, clamp_off(p.offs[e], p.M)) : p.M;
-    p_valid = min(BM, p.N - n0);
-    q_valid = min(BN, p.K - k0);
-    P = p.a + (int64_t)n0 * p.M;
-    Q = p.b + (int64_t)k0 * p.M;
-    p_ld = q_ld = p.M;
-    c_lo = lo;
-    c_hi = hi;
-    out_ld = p.K;
-    out_base = ((int64_t)e * p.N + n0) * p.K + k0;
-    if constexpr (SK == 1) {
-      sc_ld = p.M / 32;
-      psc = static_cast<const uint8_t*>(p.sa) + (int64_t)n0 * sc_ld;
-      qsc = static_cast<const uint8_t*>(p.sb) + (int64_t)k0 * sc_ld;
     } else {
+      const int ntn = (p.N + BM - 1) / BM;
+      const int e = ru / ntn;
+      const int n0 = (ru % ntn) * BM, k0 = ct * BN;
+      // group range of e: lo = max over j < e of clamp(offs[j]); hi = max(lo, clamp(offs[e]))
+      int lo, hi;
+      if (table) {
+        lo = e == 0 ? 0 : g_hi[e - 1];
+        hi = g_hi[e];
+      } else {
+        __shared__ int s_red[4];
+        int m = 0;
+        if (p.offs != nullptr)
+          for (int jj = t; jj < e; jj += 256) m = max(m, clamp_off(p.offs[jj], p.M));
+        m = (int)wave_max_u32((uint32_t)m);
+        if (lane == 0) s_red[wave] = m;
+        __syncthreads();
+        lo = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+        hi = p.offs != nullptr ? max(lo, clamp_off(p.offs[e], p.M)) : p.M;
+        __syncthreads();   // s_red is reused by the next tile's setup
+      }
+      tl.pv = min(BM, p.N - n0);
+      tl.qv = min(BN, p.K - k0);
+      tl.P = p.a + (int64_t)n0 * p.M;
+      tl.Q = p.b + (int64_t)k0 * p.M;
+      tl.c_lo = lo;
+      tl.c_hi = hi;
+      tl.out_base = ((int64_t)e * p.N + n0) * p.K + k0;
+      tl.psc = static_cast<const uint8_t*>(p.sa) + (int64_t)n0 * sc_ld;
+      tl.qsc = static_cast<const uint8_t*>(p.sb) + (int64_t)k0 * sc_ld;
       psf = static_cast<const float*>(p.sa) + (int64_t)e * p.N + n0;
       qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.K + k0;
     }
-  }
+    // Stages start on BK-aligned contraction positions (whole cache lines when
+    // the row stride is a multiple of 128); stage 0 may begin below c_lo and
+    // the last may end past c_hi: those bytes are zeroed in LDS before use.
+    tl.c_start = tl.c_lo & ~(BK - 1);
+    tl.nk = tl.c_hi > tl.c_lo ? (tl.c_hi - tl.c_start + BK - 1) / BK : 0;
+    // The description is workgroup-uniform (part of it came through LDS):
+    // keep it in scalar registers.
+    tl.P = uniform_ptr(tl.P);
+    tl.Q = uniform_ptr(tl.Q);
+    tl.psc = uniform_ptr(tl.psc);
+    tl.qsc = uniform_ptr(tl.qsc);
+    tl.out_base = uniform_i64(tl.out_base);
+    tl.pv = __builtin_amdgcn_readfirstlane(tl.pv);
+    tl.qv = __builtin_amdgcn_readfirstlane(tl.qv);
+    tl.c_lo = __builtin_amdgcn_readfirstlane(tl.c_lo);
+    tl.c_hi = __builtin_amdgcn_readfirstlane(tl.c_hi);
+    tl.c_start = __builtin_amdgcn_readfirstlane(tl.c_start);
+    tl.nk = __builtin_amdgcn_readfirstlane(tl.nk);
+    if constexpr (SK == 0) {
+      const int pv1 = max(tl.pv, 1) - 1, qv1 = max(tl.qv, 1) - 1;
+#pragma unroll
+      for (int s = 0; s < SPT; ++s) {
+        const int idx = min(t + 256 * s, BM + BN - 1);
+        sv[s] = idx < BM ? psf[min(idx, pv1)] : qsf[min(idx - BM, qv1)];
+      }
+    }
+  };
 
-  // Stages start on BK-aligned contraction positions (whole cache lines when
-  // the row stride is a multiple of 128); stage 0 may begin below c_lo and the
-  // last may end past c_hi: those bytes are zeroed in LDS before use.
-  // Reciprocals of the tile's row and column scales, for the epilogue (loaded
-  // now, so their latency hides behind the main loop).
-  __shared__ __attribute__((aligned(16))) float s_inv[SK == 0 ? BM + BN : 4];
-  if constexpr (SK == 0) {
-    for (int idx = t; idx < BM + BN; idx += 256)
-      s_inv[idx] = idx < BM ? __frcp_rn(psf[min(idx, p_valid - 1)]) : __frcp_rn(qsf[min(idx - BM, q_valid - 1)]);
-  }
-
-  const int c_start = c_lo & ~(BK - 1);
-  const int nk = c_hi > c_lo ? (c_hi - c_start + BK - 1) / BK : 0;
+  // Reciprocals of the scales loaded by setup, into `sinv`.
+  auto scale_commit = [&](const float (&sv)[SPT], float* sinv) {
+    if constexpr (SK == 0) {
+#pragma unroll
+      for (int s = 0; s < SPT; ++s) {
+        const int idx = threadIdx.x + 256 * s;
+        if (idx < BM + BN) sinv[idx] = __frcp_rn(sv[s]);
+      }
+    }
+  };
 
   // ---------------------------------------------------------------- DMA global -> LDS
   // Wave `wave` moves 1 KiB blocks wave + 4 i (i < BPW) of each stage (the
@@ -665,60 +742,57 @@ void gemm_fp8_pipe(KParams p) {
   // swizzle term depends on row bits that a block step of 4 * RPB rows never
   // changes, so the logical chunk is one per lane for all blocks.
   // Block i covers rows r0 + 4 RPB i; its 32-bit offset (host validation
-  // bounds the row strides) is rebuilt in every step from a copy of r0 that the
-  // compiler cannot hoist, which keeps BPW loop-invariant offsets out of the
-  // register file at the cost of a few VALU ops between MFMAs.
-  const int lc16 = 16 * R::phys(R::RPB * wave + lane / CH, lane % CH);
-  const int r0 = R::RPB * wave + lane / CH;
-  const int pv1 = p_valid - 1, qv1 = q_valid - 1, pld = (int)p_ld, qld = (int)q_ld;
-  auto row_off = [&](int rr, int i) -> uint32_t {
-    return i < BPW_A ? (uint32_t)(min(rr + 4 * R::RPB * i, pv1) * pld + lc16)
-                     : (uint32_t)(min(rr + 4 * R::RPB * (i - BPW_A), qv1) * qld + lc16);
+  // bounds the row strides) is rebuilt for every stage from a copy of r0 that
+  // the compiler cannot hoist, which keeps BPW loop-invariant offsets out of
+  // the register file at the cost of a few VALU ops between MFMAs.  Checked
+  // stages clamp positions past the range to the last chunk that overlaps it
+  // (zeroed in LDS later), so every lane still issues one load per block (the
+  // wait counts rely on it).
+  // e8m0: load d (global index wave + 4 d) covers tile rows 64 (wave + 4 d)
+  // + lane, one 4-byte word (the stage's four 32-blocks) per row; loads past
+  // the tile fetch row 0 into spare LDS.  Row offsets are 32-bit from the
+  // tile's (uniform) scale-row bases.
+  auto scale_row_off = [&](const Tile& tl, int wave, int lane, int i) -> uint32_t {
+    const int rb = 64 * (wave + 4 * i);                    // wave-uniform
+    const bool in_a = rb < BM, in_b = !in_a && rb < SROWS;
+    const int rr = in_a ? min(rb + lane, tl.pv - 1) : (in_b ? min(rb - BM + lane, tl.qv - 1) : 0);
+    return (uint32_t)(rr * sc_ld);
   };
-  // e8m0: load d (< SC_DMA per wave, global index wave + 4 d) covers tile rows
-  // 64 (wave + 4 d) + lane; loads past the tile fetch row 0 into spare LDS.
-  const uint8_t* srow[SK == 1 ? SC_DMA : 1];
-  if constexpr (SK == 1) {
+  auto issue_stage = [&](const Tile& tl, auto slot_tag, int kt, auto checked_tag, const uint32_t* soff = nullptr) {
+    constexpr int S = decltype(slot_tag)::value;
+    constexpr bool CHECKED = decltype(checked_tag)::value;
+    int t_opq = threadIdx.x;
+    asm volatile("" : "+v"(t_opq));
+    const int lane = t_opq & 63, wave = __builtin_amdgcn_readfirstlane(t_opq >> 6);
+    const int r0 = R::RPB * wave + lane / CH;
+    const int lc16 = 16 * R::phys(r0, lane % CH);
+    const int pv1 = tl.pv - 1, qv1 = tl.qv - 1;
+    const int base = tl.c_start + kt * BK;
+    uint32_t pos = (uint32_t)base;
+    if constexpr (CHECKED) pos = (uint32_t)min(base + lc16, max((tl.c_hi - 1) & ~15, 0)) - (uint32_t)lc16;
+    uint8_t* dst = slot_data[S];
 #pragma unroll
-    for (int i = 0; i < SC_DMA; ++i) {
-      const int r = 64 * (wave + 4 * i) + lane;
-      srow[i] = r < BM ? psc + (int64_t)min(r, p_valid - 1) * sc_ld
-                       : (r < SROWS ? qsc + (int64_t)min(r - BM, q_valid - 1) * sc_ld : psc);
+    for (int i = 0; i < BPW; ++i) {
+      const uint32_t ro = i < BPW_A ? (uint32_t)(min(r0 + 4 * R::RPB * i, pv1) * ld + lc16)
+                                    : (uint32_t)(min(r0 + 4 * R::RPB * (i - BPW_A), qv1) * ld + lc16);
+      dma_16((i < BPW_A ? tl.P : tl.Q) + (ro + pos), dst + (wave + 4 * i) * 1024);
     }
-  }
-  auto issue_scales = [&](uint8_t* sdst, int kt) {
     if constexpr (SK == 1) {
-      const int blk0 = (c_start + kt * BK) >> 5;
+      const int blk0 = base >> 5;
+      uint8_t* sdst = slot_scale[S];
 #pragma unroll
-      for (int i = 0; i < SC_DMA; ++i) dma_4(srow[i] + blk0, sdst + 256 * (wave + 4 * i));
+      for (int i = 0; i < SC_DMA; ++i) {
+        const int rb = 64 * (wave + 4 * i);
+        const uint8_t* sbase = (rb >= BM && rb < SROWS) ? tl.qsc : tl.psc;
+        const uint32_t so = soff != nullptr ? soff[i] : scale_row_off(tl, wave, lane, i);
+        dma_4(sbase + (so + (uint32_t)blk0), sdst + 256 * (wave + 4 * i));
+      }
     }
   };
-  // Steady-state stage: every position lies inside [c_lo, c_hi).
-  auto issue_main = [&](auto slot_tag, int kt) {
-    constexpr int S = decltype(slot_tag)::value;
-    uint8_t* dst = slot_data[S];
-    const uint32_t base = (uint32_t)(c_start + kt * BK);
-    int rr = r0;
-    asm volatile("" : "+v"(rr));
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) dma_16((i < BPW_A ? P : Q) + (row_off(rr, i) + base), dst + (wave + 4 * i) * 1024);
-    issue_scales(slot_scale[S], kt);
-  };
-  // Checked stage: positions past the range are clamped to the last chunk that
-  // overlaps it (zeroed in LDS later), so every lane still issues one load per
-  // block (the wait counts rely on it).
-  const int pos_max = max((c_hi - 1) & ~15, 0);
-  auto issue_checked = [&](auto slot_tag, int kt) {
-    constexpr int S = decltype(slot_tag)::value;
-    uint8_t* dst = slot_data[S];
-    const int base = c_start + kt * BK;
-    const uint32_t pos = (uint32_t)min(base + lc16, pos_max) - (uint32_t)lc16;
-    int rr = r0;
-    asm volatile("" : "+v"(rr));
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) dma_16((i < BPW_A ? P : Q) + (row_off(rr, i) + pos), dst + (wave + 4 * i) * 1024);
-    issue_scales(slot_scale[S], kt);
-  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using Checked = std::true_type;
+  using Unchecked = std::false_type;
 
   // Wait until at most n later stages' loads are still outstanding.
   auto wait_stages = [&](int n) {
@@ -727,6 +801,36 @@ void gemm_fp8_pipe(KParams p) {
     else if (n == 1) wait_vmcnt<LPS>();
     else wait_vmcnt<0>();
   };
+
+  Tile cur, nxt;
+  float sv[SPT];
+  if (tile_of(0) >= ntiles) return;
+  setup(tile_of(0), cur, sv);
+  scale_commit(sv, s_inv[0]);
+  if (cur.nk > 0) {
+    issue_stage(cur, I0{}, 0, Checked{});
+    if (1 < cur.nk) issue_stage(cur, I1{}, 1, Checked{});
+    if constexpr (SLOTS > 2) if (2 < cur.nk) issue_stage(cur, std::integral_constant<int, 2>{}, 2, Checked{});
+    if constexpr (SLOTS > 3) if (3 < cur.nk) issue_stage(cur, std::integral_constant<int, 3>{}, 3, Checked{});
+  }
+
+  for (int it = 0;; ++it) {
+  // Thread indices pass through an opaque copy each tile, so the compiler
+  // derives per-lane addresses inside the tile instead of hoisting (and
+  // spilling) all of them across the tile loop.
+  int t_opq = threadIdx.x;
+  asm volatile("" : "+v"(t_opq));
+  const int t = t_opq, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: scalar registers
+  const int wm = wave >> 1, wn = wave & 1;
+  const int c_lo = cur.c_lo, c_hi = cur.c_hi, c_start = cur.c_start, nk = cur.nk;
+  const float* const sinv = s_inv[it & 1];
+  uint32_t soff[SK == 1 ? SC_DMA : 1];
+  if constexpr (SK == 1) {
+#pragma unroll
+    for (int i = 0; i < SC_DMA; ++i) soff[i] = scale_row_off(cur, wave, lane, i);
+  }
+
   // Zero the bytes of every chunk of stage kt (in LDS `st`) outside or
   // straddling [c_lo, c_hi).  Only the first and last stage can hold such chunks.
   auto fix_boundary = [&](uint8_t* st, int kt) {
@@ -790,17 +894,18 @@ void gemm_fp8_pipe(KParams p) {
       constexpr int i = decltype(ic)::value;
       static_for<TN>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
+        // B fragment first: the 32x32 result then holds output row (lane & 31)
+        // and output columns 8 (v / 4) + 4 (lane >> 5) + v % 4 in register v,
+        // i.e. four consecutive columns per register quad (the epilogue packs them).
         if constexpr (SK == 1)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[SET][i], fb[SET][j], acc[i][j], 0, 0, i,
-                                                                      ea[SET], j, eb[SET]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[SET][j], fa[SET][i], acc[i][j], 0, 0, j,
+                                                                      eb[SET], i, ea[SET]);
         else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[SET][i], fb[SET][j], acc[i][j], 0, 0, 0, 0,
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[SET][j], fa[SET][i], acc[i][j], 0, 0, 0, 0,
                                                                       0, 0);
       });
     });
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
 
   // k steps of stage kt (ring slot S) before its last: read the next k step of
   // the same stage into the other set while this one's MFMAs issue.
@@ -827,7 +932,7 @@ void gemm_fp8_pipe(KParams p) {
     wait_lgkmcnt0();
     wait_vmcnt<(SLOTS - 2) * LPS>();
     raw_barrier();
-    issue_main(slot_tag, kt + SLOTS);
+    issue_stage(cur, slot_tag, kt + SLOTS, Unchecked{}, soff);
     rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
     mma(std::integral_constant<int, CUR>{});
     interleave<NM, ND, LPS>();
@@ -843,20 +948,29 @@ void gemm_fp8_pipe(KParams p) {
       wait_stages(min(SLOTS - 2, nk - 2 - kt));
       raw_barrier();
       fix_boundary(slot_data[NS], kt + 1);
-      if (kt + SLOTS < nk) issue_checked(slot_tag, kt + SLOTS);
+      if (kt + SLOTS < nk) issue_stage(cur, slot_tag, kt + SLOTS, Checked{});
       rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
     }
     mma(std::integral_constant<int, CUR>{});
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // ---- start of the tile.  First tile: stages 0 .. SLOTS-1 are in flight;
+  // wait for stage 0.  Later tiles: every wave already waited for its part of
+  // stage 0 inside the previous epilogue (before that epilogue's stores, which
+  // may complete in any order with respect to loads); refill slots 1 .. SLOTS-1.
+  if (it == 0) wait_stages(max(min(SLOTS - 1, nk - 1), 0));
+  raw_barrier();
+  // The next tile's description now, and its scale loads (issued before this
+  // tile's later stages, so they land first and never delay a stage wait).
+  const bool has_next = tile_of(it + 1) < ntiles;
+  if (has_next) setup(tile_of(it + 1), nxt, sv);
+  if (it > 0 && nk > 1) {
+    issue_stage(cur, I1{}, 1, Checked{});
+    if constexpr (SLOTS > 2) if (2 < nk) issue_stage(cur, std::integral_constant<int, 2>{}, 2, Checked{});
+    if constexpr (SLOTS > 3) if (3 < nk) issue_stage(cur, std::integral_constant<int, 3>{}, 3, Checked{});
+  }
   if (nk > 0) {
-    issue_checked(I0{}, 0);
-    if (1 < nk) issue_checked(I1{}, 1);
-    if constexpr (SLOTS > 2) if (2 < nk) issue_checked(std::integral_constant<int, 2>{}, 2);
-    if constexpr (SLOTS > 3) if (3 < nk) issue_checked(std::integral_constant<int, 3>{}, 3);
-    wait_stages(min(SLOTS - 1, nk - 1));
-    raw_barrier();
     fix_boundary(slot_data[0], 0);
     rd(I0{}, slot_data[0], slot_scale[0], 0);
   }
@@ -878,88 +992,116 @@ void gemm_fp8_pipe(KParams p) {
     if constexpr (SLOTS > 3) if (kt + 3 < nk) step_tail(std::integral_constant<int, 3>{}, kt + 3);
   }
 
+  // ---- the next tile: its scale reciprocals, then (once no wave reads the
+  // ring any more) its stage 0, which lands during the epilogue.
+  if (has_next) scale_commit(sv, s_inv[(it + 1) & 1]);
+  wait_lgkmcnt0();
+  raw_barrier();
+  if (has_next && nxt.nk > 0) issue_stage(nxt, I0{}, 0, Checked{});
+
   // ---------------------------------------------------------------- epilogue
-  // fp32 scales are multipliers of the quantized operands: divide by both.
-  // (s_inv was written before the main loop's first barrier.)
-  const bool empty = c_hi <= c_lo;
-  float inv_q[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) inv_q[j] = SK == 0 ? s_inv[BM + wn * WN + 32 * j + lrow] : 1.0f;
-  auto inv_row = [&](int r) { return SK == 0 ? s_inv[min(r, BM - 1)] : 1.0f; };
+  // fp32 scales are multipliers of the quantized operands: divide by both
+  // (reciprocals were loaded with the tile's description).  An empty
+  // contraction range gives zeros (its reciprocals are zeroed too, so no
+  // 0 * inf appears).
+  const int p_valid = cur.pv, q_valid = cur.qv;
+  const int64_t out_base = cur.out_base;
+  const float keep = c_hi > c_lo ? 1.0f : 0.0f;
   constexpr int ELEM = OUT == 0 ? 2 : 4;
-  if (((int64_t)out_ld * ELEM) % 16 == 0) {
-    // Stage each wave's (BM/2) x (BN/2) results through LDS (the ring is free
-    // now) and write whole 16-byte pieces of output rows.  bf16: neighbouring
-    // lanes (adjacent columns) swap one value per row pair so that each lane
-    // writes a 4-byte word; fp32 takes two passes over the rows.  Staged rows
-    // are WN * ELEM bytes; 16-byte chunk k of staged row r sits at chunk
-    // k ^ sw(r), which spreads the rows one write instruction touches (row
-    // parity x lane half) over distinct banks, while a 16-lane read of one
-    // whole row stays conflict-free.
-    constexpr int PASSES = (OUT == 0 || TM < 2) ? 1 : 2;
-    constexpr int TMP = TM / PASSES;            // 32-row blocks per pass
-    constexpr int RB = WN * ELEM;               // staged row bytes
+  constexpr int RB = WN * ELEM;                 // staged row bytes
+  // 32-row blocks per staging pass: four waves share the last ring slot.
+  constexpr int TMP_FIT = STAGE / (4 * 32 * RB);
+  constexpr int TMP = TMP_FIT >= TM ? TM : (TMP_FIT >= 2 ? 2 : TMP_FIT);
+  // Four consecutive output columns of one row, scaled: register quad q of acc[i][j].
+  auto quad = [&](int i, int j, int q, float inv_p, const float* inv_q) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * inv_p * inv_q[4 * q + e];
+    return v;
+  };
+  if (TMP > 0 && (out_ld * ELEM) % 16 == 0) {
+    // Stage each wave's results through LDS and write whole 16-byte pieces of
+    // output rows.  A lane holds four consecutive columns of one row per
+    // register quad: bf16 packs them into 8 bytes (fp32: 16 bytes), written
+    // to staged row r at unit u ^ (r & 31) (units of 8 bytes for bf16, 16 for
+    // fp32): the 32 rows one write instruction touches land on distinct banks.
+    // A 16-lane read of a whole staged row stays conflict-free; a bf16 read
+    // of logical 16-byte chunk k finds its two halves in physical chunk
+    // k ^ ((r & 31) >> 1), swapped when r is odd.
+    constexpr int PASSES = TMP > 0 ? TM / TMP : 1;
     constexpr int NCH = RB / 16;                // 16-byte chunks per staged row
     constexpr int WBYTES = TMP * 32 * RB;
     constexpr int VEC = 16 / ELEM;              // elements per 16-byte piece
-    static_assert(2 * WBYTES <= STAGE, "staging fits in two ring slots");
-    uint8_t* const stg = (wave < 2 ? ring0 : ring1) + (wave & 1) * WBYTES;
-    auto sw = [](int r) { return OUT == 0 ? ((r & 1) * 4 + ((r >> 2) & 1) * 8) : (((r >> 2) & 1) * 8); };
-    wait_lgkmcnt0();
-    raw_barrier();   // every wave is past its last fragment read of the ring
+    static_assert(TMP == 0 || (TM % TMP == 0 && 4 * WBYTES <= STAGE), "staging fits in the last ring slot");
+    uint8_t* const stg = slot_data[SLOTS - 1] + wave * WBYTES;
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
       if (pass > 0) wait_lgkmcnt0();   // this wave's reads of the previous pass are done
 #pragma unroll
-      for (int ii = 0; ii < TMP; ++ii) {
-        const int i = pass * TMP + ii;
-        float inv_p[16];
+      for (int j = 0; j < TN; ++j) {
+        float inv_q[16];                           // columns 32 j + 8 q + 4 g + e
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if constexpr (SK == 0) {
-            const float4 f = *reinterpret_cast<const float4*>(&s_inv[wm * WM + 32 * i + 8 * q + 4 * g]);
-            inv_p[4 * q] = f.x; inv_p[4 * q + 1] = f.y; inv_p[4 * q + 2] = f.z; inv_p[4 * q + 3] = f.w;
-          } else {
-            inv_p[4 * q] = inv_p[4 * q + 1] = inv_p[4 * q + 2] = inv_p[4 * q + 3] = 1.0f;
-          }
+          f32x4 f = {1.0f, 1.0f, 1.0f, 1.0f};
+          if constexpr (SK == 0) f = *reinterpret_cast<const f32x4*>(&sinv[BM + wn * WN + 32 * j + 8 * q + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) inv_q[4 * q + e] = f[e] * keep;
         }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int c = 32 * j + lrow;                // column within the wave's staged row
-          if constexpr (OUT == 0) {
-            const bool odd = lane & 1;
+        for (int ii = 0; ii < TMP; ++ii) {
+          const int i = pass * TMP + ii;
+          const int lr = 32 * ii + lrow;             // staged row
+          const float inv_p = (SK == 0 ? sinv[wm * WM + 32 * i + lrow] : 1.0f) * keep;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const int v0 = 2 * k, v1 = 2 * k + 1;     // rows rho(v0), rho(v0) + 1
-              const float a = empty ? 0.0f : acc[i][j][v0] * inv_p[v0] * inv_q[j];
-              const float b = empty ? 0.0f : acc[i][j][v1] * inv_p[v1] * inv_q[j];
-              const float send = odd ? a : b;
-              const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-              const float lo = odd ? recv : a, hi = odd ? b : recv;
-              const uint32_t word = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-              const int lr = 32 * ii + 8 * (v0 >> 2) + 4 * g + (v0 & 3) + (odd ? 1 : 0);
-              const int dw = (c & ~1) >> 1;             // word index in the staged row
-              *reinterpret_cast<uint32_t*>(stg + lr * RB + (((dw >> 2) ^ sw(lr)) << 4) + ((dw & 3) << 2)) = word;
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float val = empty ? 0.0f : acc[i][j][v] * inv_p[v] * inv_q[j];
-              const int lr = 32 * ii + 8 * (v >> 2) + 4 * g + (v & 3);
-              *reinterpret_cast<float*>(stg + lr * RB + (((c >> 2) ^ sw(lr)) << 4) + ((c & 3) << 2)) = val;
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = quad(i, j, q, inv_p, inv_q);
+            const int u = 8 * j + 2 * q + g;         // logical unit of 4 columns
+            if constexpr (OUT == 0) {
+              const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
+              const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
+              *reinterpret_cast<u32x2*>(stg + lr * RB + ((u ^ (lr & 31)) << 3)) =
+                  u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            } else {
+              *reinterpret_cast<f32x4*>(stg + lr * RB + ((u ^ (lr & 31)) << 4)) = v;
             }
           }
         }
       }
       wait_lgkmcnt0();   // a wave reads back only its own staging area
+      if (pass == 0) wait_vmcnt<0>();   // the next tile's stage 0 (older than any store below)
       constexpr int RPI = 64 / NCH;                 // staged rows per read instruction
+      constexpr int NRD = TMP > 0 ? TMP * 32 / RPI : 1;   // read instructions per pass
+      const int k = lane % NCH, c = wn * WN + k * VEC;
+      u32x4 dv[NRD];
 #pragma unroll
-      for (int it = 0; it < TMP * 32 / RPI; ++it) {
-        const int lr = it * RPI + lane / NCH, k = lane % NCH;
-        const u32x4 d = *reinterpret_cast<const u32x4*>(stg + lr * RB + ((k ^ sw(lr)) << 4));
-        const int r = wm * WM + pass * TMP * 32 + lr, c = wn * WN + k * VEC;
+      for (int itr = 0; itr < NRD; ++itr) {
+        const int lr = itr * RPI + lane / NCH;
+        const int pc = OUT == 0 ? (k ^ ((lr & 31) >> 1)) : (k ^ (lr & 31));
+        dv[itr] = *reinterpret_cast<const u32x4*>(stg + lr * RB + (pc << 4));
+      }
+      if constexpr (OUT == 0) {
+#pragma unroll
+        for (int itr = 0; itr < NRD; ++itr) {
+          const bool odd = (itr * RPI + lane / NCH) & 1;
+          const u32x4 d = dv[itr];
+          dv[itr] = u32x4{odd ? d.z : d.x, odd ? d.w : d.y, odd ? d.x : d.z, odd ? d.y : d.w};
+        }
+      }
+      uint8_t* const row0 = static_cast<uint8_t*>(p.out) +
+                            (out_base + (int64_t)(wm * WM + pass * TMP * 32 + lane / NCH) * out_ld + c) * ELEM;
+      if (p_valid == BM && q_valid == BN) {
+#pragma unroll
+        for (int itr = 0; itr < NRD; ++itr)
+          *reinterpret_cast<u32x4*>(row0 + (int64_t)itr * RPI * out_ld * ELEM) = dv[itr];
+        continue;
+      }
+#pragma unroll
+      for (int itr = 0; itr < NRD; ++itr) {
+        const int lr = itr * RPI + lane / NCH;
+        const u32x4 d = dv[itr];
+        const int r = wm * WM + pass * TMP * 32 + lr;
         if (r >= p_valid) continue;
-        uint8_t* dst = static_cast<uint8_t*>(p.out) + (out_base + (int64_t)r * out_ld + c) * ELEM;
+        uint8_t* dst = row0 + (int64_t)itr * RPI * out_ld * ELEM;
         if (c + VEC <= q_valid) {
           *reinterpret_cast<u32x4*>(dst) = d;
         } else {
@@ -975,29 +1117,42 @@ void gemm_fp8_pipe(KParams p) {
         }
       }
     }
-    continue;
-  }
-  // Output rows not 16-byte aligned: element stores straight from registers.
+  } else {
+    // Output rows not 16-byte aligned: element stores straight from registers.
+    wait_vmcnt<0>();   // the next tile's stage 0 (older than any store below)
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < TN; ++j) {
+      float inv_q[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (r >= p_valid) continue;
-      const float inv_p = inv_row(r);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int c = wn * WN + 32 * j + lrow;
-        if (c >= q_valid) continue;
-        const float val = empty ? 0.0f : acc[i][j][v] * inv_p * inv_q[j];
-        const int64_t o = out_base + (int64_t)r * out_ld + c;
-        if constexpr (OUT == 0)
-          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(val);
-        else
-          static_cast<float*>(p.out)[o] = val;
+        for (int e = 0; e < 4; ++e) {
+          const int cc = min(wn * WN + 32 * j + 8 * q + 4 * g + e, BN - 1);
+          inv_q[4 * q + e] = (SK == 0 ? sinv[BM + cc] : 1.0f) * keep;
+        }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + 32 * i + lrow;
+        const float inv_p = (SK == 0 ? sinv[r] : 1.0f) * keep;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = quad(i, j, q, inv_p, inv_q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = wn * WN + 32 * j + 8 * q + 4 * g + e;
+            if (r >= p_valid || c >= q_valid) continue;
+            const int64_t o = out_base + (int64_t)r * out_ld + c;
+            if constexpr (OUT == 0)
+              static_cast<__bf16*>(p.out)[o] = (__bf16)v[e];
+            else
+              static_cast<float*>(p.out)[o] = v[e];
+          }
+        }
       }
     }
   }
+  if (!has_next) break;
+  cur = nxt;
   }   // tile loop
 }
 
