@@ -807,11 +807,15 @@ void gemm_fp8_pipe(KParams p) {
   if (tile_of(0) >= ntiles) return;
   setup(tile_of(0), cur, sv);
   scale_commit(sv, s_inv[0]);
+  // Stage of step s in the processing order nk-1, 0, 1, ..., nk-2 (see below).
+  auto first_stage = [](const Tile& tl, int s) { return s == 0 ? tl.nk - 1 : s - 1; };
   if (cur.nk > 0) {
-    issue_stage(cur, I0{}, 0, Checked{});
-    if (1 < cur.nk) issue_stage(cur, I1{}, 1, Checked{});
-    if constexpr (SLOTS > 2) if (2 < cur.nk) issue_stage(cur, std::integral_constant<int, 2>{}, 2, Checked{});
-    if constexpr (SLOTS > 3) if (3 < cur.nk) issue_stage(cur, std::integral_constant<int, 3>{}, 3, Checked{});
+    issue_stage(cur, I0{}, first_stage(cur, 0), Checked{});
+    issue_stage(cur, I1{}, first_stage(cur, min(1, cur.nk - 1)), Checked{});
+    if constexpr (SLOTS > 2)
+      issue_stage(cur, std::integral_constant<int, 2>{}, first_stage(cur, min(2, cur.nk - 1)), Checked{});
+    if constexpr (SLOTS > 3)
+      issue_stage(cur, std::integral_constant<int, 3>{}, first_stage(cur, min(3, cur.nk - 1)), Checked{});
   }
 
   for (int it = 0;; ++it) {
@@ -835,7 +839,7 @@ void gemm_fp8_pipe(KParams p) {
   // straddling [c_lo, c_hi).  Only the first and last stage can hold such chunks.
   auto fix_boundary = [&](uint8_t* st, int kt) {
     const int base = c_start + kt * BK;
-    if (base >= c_lo && base + BK <= c_hi) return;    // uniform
+    if (kt >= nk || (base >= c_lo && base + BK <= c_hi)) return;    // uniform
     for (int idx = t; idx < SROWS * CH; idx += 256) {
       const int r = idx / CH, c = idx % CH, pos = base + 16 * c;
       if (pos < c_lo || pos + 16 > c_hi) {
@@ -919,39 +923,34 @@ void gemm_fp8_pipe(KParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Steady-state step for stage kt in slot S (kt + SLOTS <= nk - 2):
-  //  1. k steps of stage kt but the last;
-  //  2. wait for stage kt+1 and this wave's reads of slot S, barrier (stage
-  //     kt+1 visible everywhere; no wave still reads slot S);
-  //  3. refill slot S with stage kt+SLOTS, read stage kt+1's first k step into
+  // Stages are processed in the order nk-1, 0, 1, ..., nk-2: the two that can
+  // straddle the contraction range (the last and the first) come first and
+  // are fixed up before the uniform steps start.
+  auto stage_of = [&](int s) { return s == 0 ? nk - 1 : s - 1; };
+  // Step s of the order, stage stage_of(s) in ring slot S (== s % SLOTS), the
+  // same code for the whole range so it stays branch-free and interleaved:
+  //  1. k steps of the stage but the last;
+  //  2. wait for step s+1's stage and this wave's reads of slot S, barrier
+  //     (that stage visible everywhere; no wave still reads slot S); the
+  //     first step also zeroes the out-of-range bytes of the next stage;
+  //  3. refill slot S with the stage of step min(s+SLOTS, nk-1) (past the end a
+  //     reload that nothing reads, so every step issues the same loads and
+  //     every wait count is static), read the next stage's first k step into
   //     the other set and run the last k step's MFMAs, all interleaved.
-  auto step_main = [&](auto slot_tag, int kt) {
+  auto step = [&](auto slot_tag, int kt, auto fix_tag) {
     constexpr int S = decltype(slot_tag)::value, NS = (S + 1) % SLOTS;
     constexpr int CUR = (S * KS + KS - 1) & 1;
     inner_halves(slot_tag);
     wait_lgkmcnt0();
     wait_vmcnt<(SLOTS - 2) * LPS>();
     raw_barrier();
-    issue_stage(cur, slot_tag, kt + SLOTS, Unchecked{}, soff);
+    if constexpr (decltype(fix_tag)::value) {
+      if (kt + 1 < nk) fix_boundary(slot_data[NS], stage_of(kt + 1));
+    }
+    issue_stage(cur, slot_tag, stage_of(min(kt + SLOTS, nk - 1)), Checked{}, soff);
     rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
     mma(std::integral_constant<int, CUR>{});
     interleave<NM, ND, LPS>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Checked step: the last SLOTS + 1 stages (boundary fix-ups, no refill past nk).
-  auto step_tail = [&](auto slot_tag, int kt) {
-    constexpr int S = decltype(slot_tag)::value, NS = (S + 1) % SLOTS;
-    constexpr int CUR = (S * KS + KS - 1) & 1;
-    inner_halves(slot_tag);
-    wait_lgkmcnt0();
-    if (kt + 1 < nk) {
-      wait_stages(min(SLOTS - 2, nk - 2 - kt));
-      raw_barrier();
-      fix_boundary(slot_data[NS], kt + 1);
-      if (kt + SLOTS < nk) issue_stage(cur, slot_tag, kt + SLOTS, Checked{});
-      rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
-    }
-    mma(std::integral_constant<int, CUR>{});
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -959,45 +958,48 @@ void gemm_fp8_pipe(KParams p) {
   // wait for stage 0.  Later tiles: every wave already waited for its part of
   // stage 0 inside the previous epilogue (before that epilogue's stores, which
   // may complete in any order with respect to loads); refill slots 1 .. SLOTS-1.
-  if (it == 0) wait_stages(max(min(SLOTS - 1, nk - 1), 0));
+  if (it == 0) wait_vmcnt<(SLOTS - 1) * LPS>();
   raw_barrier();
   // The next tile's description now, and its scale loads (issued before this
   // tile's later stages, so they land first and never delay a stage wait).
   const bool has_next = tile_of(it + 1) < ntiles;
   if (has_next) setup(tile_of(it + 1), nxt, sv);
-  if (it > 0 && nk > 1) {
-    issue_stage(cur, I1{}, 1, Checked{});
-    if constexpr (SLOTS > 2) if (2 < nk) issue_stage(cur, std::integral_constant<int, 2>{}, 2, Checked{});
-    if constexpr (SLOTS > 3) if (3 < nk) issue_stage(cur, std::integral_constant<int, 3>{}, 3, Checked{});
+  if (it > 0 && nk > 0) {
+    issue_stage(cur, I1{}, first_stage(cur, min(1, nk - 1)), Checked{});
+    if constexpr (SLOTS > 2)
+      issue_stage(cur, std::integral_constant<int, 2>{}, first_stage(cur, min(2, nk - 1)), Checked{});
+    if constexpr (SLOTS > 3)
+      issue_stage(cur, std::integral_constant<int, 3>{}, first_stage(cur, min(3, nk - 1)), Checked{});
   }
   if (nk > 0) {
-    fix_boundary(slot_data[0], 0);
+    fix_boundary(slot_data[0], nk - 1);
     rd(I0{}, slot_data[0], slot_scale[0], 0);
   }
-  // Two loops (a per-step choice between the two step kinds inside one loop
-  // defeats register allocation): whole rounds of steady-state steps, then
-  // checked steps to the end.
-  const int nmain = max(nk - SLOTS - 1, 0);
-  int kt = 0;
-  for (; kt + SLOTS <= nmain; kt += SLOTS) {
-    step_main(I0{}, kt);
-    step_main(I1{}, kt + 1);
-    if constexpr (SLOTS > 2) step_main(std::integral_constant<int, 2>{}, kt + 2);
-    if constexpr (SLOTS > 3) step_main(std::integral_constant<int, 3>{}, kt + 3);
+  // Step 0 (with the fix-up of the next stage), then whole rounds of SLOTS
+  // steps (static slots 1, 2, ..., 0), then the partial round.
+  using Fix = std::true_type;
+  using NoFix = std::false_type;
+  if (nk > 0) step(I0{}, 0, Fix{});
+  int kt = 1;
+  for (; kt + SLOTS <= nk; kt += SLOTS) {
+    step(I1{}, kt, NoFix{});
+    if constexpr (SLOTS > 2) step(std::integral_constant<int, 2>{}, kt + 1, NoFix{});
+    if constexpr (SLOTS > 3) step(std::integral_constant<int, 3>{}, kt + 2, NoFix{});
+    step(I0{}, kt + SLOTS - 1, NoFix{});
   }
-  for (; kt < nk; kt += SLOTS) {
-    step_tail(I0{}, kt);
-    if (kt + 1 < nk) step_tail(I1{}, kt + 1);
-    if constexpr (SLOTS > 2) if (kt + 2 < nk) step_tail(std::integral_constant<int, 2>{}, kt + 2);
-    if constexpr (SLOTS > 3) if (kt + 3 < nk) step_tail(std::integral_constant<int, 3>{}, kt + 3);
+  if (kt < nk) {
+    step(I1{}, kt, NoFix{});
+    if constexpr (SLOTS > 2) if (kt + 1 < nk) step(std::integral_constant<int, 2>{}, kt + 1, NoFix{});
+    if constexpr (SLOTS > 3) if (kt + 2 < nk) step(std::integral_constant<int, 3>{}, kt + 2, NoFix{});
   }
+  wait_vmcnt<0>();   // the reloads past the end land before their slots are reused
 
   // ---- the next tile: its scale reciprocals, then (once no wave reads the
   // ring any more) its stage 0, which lands during the epilogue.
   if (has_next) scale_commit(sv, s_inv[(it + 1) & 1]);
   wait_lgkmcnt0();
   raw_barrier();
-  if (has_next && nxt.nk > 0) issue_stage(nxt, I0{}, 0, Checked{});
+  if (has_next && nxt.nk > 0) issue_stage(nxt, I0{}, first_stage(nxt, 0), Checked{});
 
   // ---------------------------------------------------------------- epilogue
   // fp32 scales are multipliers of the quantized operands: divide by both
