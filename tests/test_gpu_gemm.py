@@ -315,3 +315,100 @@ def test_grouped_m_mx_full_size_sampled():
         return (ref,) + oracle.error_bounds_m(A, B, one, oracle.ACC_FP8_MFMA)
 
     _check_rows_by_expert(got, _rows(M, 16, 55), offs, M, ref_for, "cfg5 MX")
+
+
+# ------------------------------------------------------------------ pipeline edge cases
+# The FP8/MX kernel streams 128-byte contraction stages through a 2-slot (256-row
+# tiles) or 3-slot (128-row tiles, small groups) ring, processes the last stage
+# first, and reloads past the end: cover 1..5 stages, lengths that are not a
+# multiple of 128, both tile shapes, and the staged fp32 epilogue.
+
+@pytest.mark.parametrize("K", [48, 144, 400, 640])
+@pytest.mark.parametrize("tiles", ["wide", "small"])
+def test_grouped_m_contraction_lengths(K, tiles):
+    if tiles == "wide":     # one group: 256-row tiles
+        x = synth.normal_bf16(41, (600, K), 1.0)
+        w = synth.normal_bf16(42, (1, 272, K), 0.02)
+        offs = np.array([600], np.int32)
+    else:                   # small groups: 128-row tiles
+        x = synth.normal_bf16(43, (700, K), 1.0, 0.01, 50.0)
+        w = synth.normal_bf16(44, (8, 272, K), 0.02)
+        offs = synth.offsets_from_counts(synth.random_counts(45, 690, 8))
+    gm_case(x, w, offs, name=f"K{K}-{tiles}")
+
+
+def test_grouped_m_f32_out_wide_tiles():
+    x, w, offs = GM_CASES["dense"]()
+    w = np.concatenate([w, w[:, :212]], axis=1)       # N = 512: 16-byte aligned fp32 rows
+    gm_case(x, w, offs, out_dtype=1, name="f32out-wide")
+
+
+def test_grouped_k_small_and_empty_groups():
+    counts = np.array([1, 0, 2, 17, 128, 0, 255, 300, 3], np.int64)
+    M = (int(counts.sum()) + 20 + 15) // 16 * 16       # a multiple of 16; rows past the last group are ignored
+    dy = synth.normal_bf16(46, (M, 264), 1e-3)
+    x = synth.normal_bf16(47, (M, 200), 1.0, 0.01, 30.0)
+    gk_case(dy, x, synth.offsets_from_counts(counts), name="small-groups")
+
+
+def test_grouped_k_f32_out():
+    dy, x, offs = GK_CASES["ragged"]()
+    gk_case(dy, x, offs, out_dtype=1, name="f32out")
+
+
+def _gk_mx(dy, x, offs, rule, what):
+    M, N = dy.shape
+    K = x.shape[1]
+    E = len(offs)
+    Mp = fm.quantize_mx_rows_bound(M, E)
+    note(f"GROUPED_K MX {what} rule={rule} Mp={Mp}")
+    qa, xa, op = fm.quantize_mx(bf16_dev(dy), axis=0, offs=i32_dev(offs), rule=rule, rows_pad=Mp)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=rule, rows_pad=Mp)
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, fm.OPD_E4M3FN, xa, qb, fm.OPD_E4M3FN, xb, fm.SCALE_E8M0, op, E,
+                               Mp, N, K)
+    _, got = _out_host(out)
+    qa_h, xa_h, qb_h, xb_h, op_h = host(qa), host(xa), host(qb), host(xb), host(op)
+    ref = oracle.mm_grouped_k_mx(qa_h, xa_h, qb_h, xb_h, op_h)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_k(A, B, op_h, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, f"GROUPED_K MX {what}")
+    return Mp
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_grouped_k_mx_aligned_rows(rule):
+    # rows_pad = round_up(960 + 31 * 2, 32) = 1024, a multiple of 128: the 128-byte-stage kernel
+    dy = synth.normal_bf16(48, (960, 320), 1e-3)
+    x = synth.normal_bf16(49, (960, 288), 1.0, 0.01, 30.0)
+    offs = synth.offsets_from_counts(np.array([517, 443]))
+    assert _gk_mx(dy, x, offs, rule, "aligned") % 128 == 0
+
+
+def test_grouped_k_mx_aligned_many_groups():
+    counts = np.array([40, 0, 300, 1, 127, 129, 200, 103], np.int64)   # sum 900, bound = 1152
+    M = int(counts.sum())
+    dy = synth.normal_bf16(50, (M, 256), 1e-3)
+    x = synth.normal_bf16(51, (M, 320), 1.0)
+    assert _gk_mx(dy, x, synth.offsets_from_counts(counts), 0, "groups") % 128 == 0
+
+
+def test_grouped_m_mx_unaligned_k():
+    # K = 288 is not a multiple of 128: e8m0 rows take the byte-wise stage kernel
+    x = synth.normal_bf16(52, (500, 288), 1.0, 0.01, 30.0)
+    w = synth.normal_bf16(53, (3, 200, 288), 0.02)
+    offs = synth.offsets_from_counts(synth.random_counts(54, 480, 3))
+    M, K = x.shape
+    E, N, _ = w.shape
+    note("GROUPED_M MX K=288")
+    qa, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(w.reshape(E * N, K)), axis=1, rule=0)
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, xa, qb, 0, xb, fm.SCALE_E8M0, i32_dev(offs), E, M, N, K)
+    _, got = _out_host(out)
+    qa_h, xa_h = host(qa), host(xa)
+    qb_h, xb_h = host(qb).reshape(E, N, K), host(xb).reshape(E, N, K // 32)
+    ref = oracle.mm_grouped_m_mx(qa_h, xa_h, qb_h, xb_h, offs)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, "GROUPED_M MX K=288")
