@@ -62,14 +62,15 @@ def parse():
 # ---------------------------------------------------------------------- layer plan
 
 class Step:
-    """A list of launches; each item: (name, kind, fn, work) with kind 'quant' (work = bytes)
-    or 'gemm' (work = flops) or 'gemm_bf16'."""
+    """A list of launches; each item: (name, kind, fn, work, hbm) with kind 'quant' (work = hbm =
+    algorithmic bytes) or 'gemm' / 'gemm_bf16' (work = flops, hbm = algorithmic bytes: operands and
+    scales read once, output written once)."""
 
     def __init__(self):
         self.items = []
 
-    def add(self, name, kind, fn, work):
-        self.items.append((name, kind, fn, work))
+    def add(self, name, kind, fn, work, hbm=None):
+        self.items.append((name, kind, fn, work, work if hbm is None else hbm))
 
 
 def build_step(cfg: int, gw: bool):
@@ -117,19 +118,27 @@ def build_step(cfg: int, gw: bool):
                  qbytes(B * R * C, B * C))
         return q, s
 
+    def gemm_bytes(a_elems, b_elems, out_elems, a_rows, b_rows, sk):
+        # fp8 operands + bf16 output; fp32 scales per row (per group row for the weight side) or
+        # one e8m0 byte per 32 operand bytes
+        sc = (a_elems + b_elems) / 32 if sk == fm.SCALE_E8M0 else 4 * (a_rows + b_rows)
+        return a_elems + b_elems + 2 * out_elems + sc
+
     def g_m(name, qa, sa, qb, sb, Mr, N, K, sk=fm.SCALE_F32, offs_t=None, n_groups=None):
         o = bf(Mr, N)
         og = offs if offs_t is None else offs_t
         ng = E if n_groups is None else n_groups
         step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, sa, qb, 0, sb, sk, og, ng,
-                                                            Mr, N, K, out=o), 2.0 * M * N * K)
+                                                            Mr, N, K, out=o), 2.0 * M * N * K,
+                 gemm_bytes(M * K, ng * N * K, M * N, M, ng * N, sk))
         return o
 
     def g_k(name, qa, sa, qb, sb, Mc, N, K, sk=fm.SCALE_F32, offs_t=None):
         o = bf(E, N, K)
         og = offs if offs_t is None else offs_t
         step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, sa, qb, 0, sb, sk, og, E,
-                                                            Mc, N, K, out=o), 2.0 * M * N * K)
+                                                            Mc, N, K, out=o), 2.0 * M * N * K,
+                 gemm_bytes(N * M, K * M, E * N * K, E * N, E * K, sk))
         return o
 
     if cfg in (1, 2):
@@ -154,7 +163,8 @@ def build_step(cfg: int, gw: bool):
                 o = bf(1, F2, H)
                 step.add("gemm wgrad bf16", "gemm_bf16",
                          lambda: fm.grouped_mm_scaled(fm.GROUPED_K, DYd, fm.OPD_BF16, None, Xd, fm.OPD_BF16, None,
-                                                      fm.SCALE_NONE, offs, 1, M, F2, H, out=o), 2.0 * M * F2 * H)
+                                                      fm.SCALE_NONE, offs, 1, M, F2, H, out=o), 2.0 * M * F2 * H,
+                         2 * (M * F2 + M * H + F2 * H))
         return step, host
 
     F, F2 = w.F, w.F2
@@ -429,21 +439,30 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     per = {}
-    for i, (name, kind, _, work) in enumerate(step.items):
+    for i, (name, kind, _, work, hbm) in enumerate(step.items):
         us = float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])) * 1e3
-        per[name] = (kind, work, us)
+        per[name] = (kind, work, us, hbm)
     q_bytes = sum(v[1] for v in per.values() if v[0] == "quant")
     q_us = sum(v[2] for v in per.values() if v[0] == "quant")
     g_flops = sum(v[1] for v in per.values() if v[0] == "gemm")
     g_us = sum(v[2] for v in per.values() if v[0] == "gemm")
+
+    def roof(kind, work, us, hbm):
+        """(bound, achieved, peak, unit): a GEMM is HBM-bound when moving its algorithmic bytes at
+        peak bandwidth takes longer than its flops at peak MFMA rate."""
+        if kind == "quant":
+            return "hbm", work / us / 1e3, PEAK_HBM_GBPS, "GB/s"
+        peak_f = PEAK_BF16_TFLOPS if kind == "gemm_bf16" else PEAK_FP8_TFLOPS
+        if hbm / PEAK_HBM_GBPS / 1e3 > work / peak_f / 1e6:
+            return "hbm", hbm / us / 1e3, PEAK_HBM_GBPS, "GB/s"
+        return "mfma", work / us / 1e6, peak_f, "TFLOP/s"
+
     dom = max(per, key=lambda k: per[k][2])
-    kind, work, us = per[dom]
-    if kind == "quant":
-        achieved, peak, unit, bound = work / us / 1e3, PEAK_HBM_GBPS, "GB/s", "hbm"
-    else:
-        achieved = work / us / 1e6
-        peak = PEAK_BF16_TFLOPS if kind == "gemm_bf16" else PEAK_FP8_TFLOPS
-        unit, bound = "TFLOP/s", "mfma"
+    bound, achieved, peak, unit = roof(*per[dom])
+    fracs = {}
+    for k, v in per.items():
+        b, a, pk, _ = roof(*v)
+        fracs[k] = {"bound": b, "frac": round(a / pk, 4)}
 
     w = synth.WORKLOADS[args.config]
     out = {
@@ -471,6 +490,7 @@ def main():
         "kernels_us": {k: round(v[2], 1) for k, v in per.items()},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, args.config)},
+        "kernels_roofline": fracs,
     }
     if not args.no_cpu_baseline and args.config == 2:
         out["cpu_baseline"] = cpu_baseline(args.config, host)

@@ -109,7 +109,8 @@ def test_colwise_grouped_parity(codec, case):
 
 
 @pytest.mark.parametrize("codec", CODECS)
-@pytest.mark.parametrize("shape", [(3, 700, 72), (4, 100, 64), (2, 1, 8), (1, 1030, 136)])
+@pytest.mark.parametrize("shape", [(3, 700, 72), (4, 100, 64), (2, 1, 8), (1, 1030, 136),
+                                   (2, 4096, 72), (2, 4097, 72), (5, 1536, 200)])
 def test_colwise_batched_parity(codec, shape):
     x = special_input(3000 + sum(shape), shape)
     B, R, C = shape
@@ -123,6 +124,21 @@ def test_colwise_batched_parity(codec, shape):
     assert_bytes_equal(got[:, :, :R], qr, "codes")
     assert np.all(got[:, :, R:] == 0xA5), "wrote past the rows"
     assert_f32_bits_equal(host(sc), sr, "scales")
+
+
+def test_colwise_batched_back_to_back_calls():
+    # The batched single pass exchanges column maxima between chunks through
+    # memory the library keeps across calls: a call must see none of the
+    # previous call's maxima, here larger than its own by 2^10.
+    shape = (3, 1800, 136)
+    big = special_input(4100, shape, sigma=1024.0)
+    small = special_input(4101, shape)
+    for k, x in enumerate([big, small, big[:2, :900], small[:2, :900]]):
+        note(f"colwise batched back-to-back call {k} shape={x.shape}")
+        q_t, sc = fm.quantize_colwise(bf16_dev(x), None, fm.E4M3FN)
+        qr, sr = oracle.quantize_colwise_batched(x, fm.E4M3FN)
+        assert_bytes_equal(host(q_t)[:, :, :x.shape[1]], qr, f"codes call {k}")
+        assert_f32_bits_equal(host(sc), sr, f"scales call {k}")
 
 
 def test_colwise_deterministic_across_runs():
@@ -219,10 +235,11 @@ def test_colwise_grouped_full_size_sampled(cfg, tensor):
     assert_f32_bits_equal(sh[:, cols], sr, "scales")
 
 
-def test_colwise_batched_full_size_sampled():
+@pytest.mark.parametrize("tensor", ["w1", "w2"])
+def test_colwise_batched_full_size_sampled(tensor):
     w = synth.WORKLOADS[4]
-    x = synth.make_w2(w)                                          # [32, 7168, 2048]
-    note(f"colwise batched full cfg=4 w2 {x.shape}")
+    x = synth.make_w1(w) if tensor == "w1" else synth.make_w2(w)  # [32, 4096, 7168] / [32, 7168, 2048]
+    note(f"colwise batched full cfg=4 {tensor} {x.shape}")
     q_t, sc = fm.quantize_colwise(bf16_dev(x), None, fm.E4M3FN)
     cols = _sample(x.shape[2], 8, 44)
     qh, sh = host(q_t), host(sc)
