@@ -121,7 +121,7 @@ def build_step(cfg: int, gw: bool):
     def gemm_bytes(a_elems, b_elems, out_elems, a_rows, b_rows, sk):
         # fp8 operands + bf16 output; fp32 scales per row (per group row for the weight side) or
         # one e8m0 byte per 32 operand bytes
-        sc = (a_elems + b_elems) / 32 if sk == fm.SCALE_E8M0 else 4 * (a_rows + b_rows)
+        sc = (a_elems + b_elems) / 32 if sk in (fm.SCALE_E8M0, fm.SCALE_E8M0_K4) else 4 * (a_rows + b_rows)
         return a_elems + b_elems + 2 * out_elems + sc
 
     def g_m(name, qa, sa, qb, sb, Mr, N, K, sk=fm.SCALE_F32, offs_t=None, n_groups=None):
@@ -194,49 +194,51 @@ def build_step(cfg: int, gw: bool):
         g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, ld, F2, H)
         return step, host
 
-    # cfg 5: MXFP8
+    # cfg 5: MXFP8, e8m0 scales written by the quantizer in the K4 layout the GEMM reads per stage
     rule = fm.MX_FLOOR_OCP
     Mp = fm.quantize_mx_rows_bound(M, E)
+    K4 = fm.MX_LAYOUT_K4
 
     def mx_last(name, x, rows, cols):
-        q, s = u8(rows, cols), u8(rows, cols // 32)
-        step.add(name, "quant", lambda: fm.quantize_mx(x.view(rows, cols), axis=1, rule=rule, q=q, scale=s),
+        q, s = u8(rows, cols), u8(*fm.mx_k4_shape(rows, cols // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx(x.view(rows, cols), axis=1, rule=rule, q=q, scale=s,
+                                                       layout=K4),
                  qbytes(rows * cols, rows * cols // 32, 1))
         return q, s
 
     def mx_rows_b(name, x, B, R, C):
-        q, s = u8(B, C, R), u8(B, C, R // 32)
-        step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, rule=rule, q=q, scale=s),
+        q, s = u8(B, C, R), u8(*fm.mx_k4_shape(B * C, R // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, rule=rule, q=q, scale=s, layout=K4),
                  qbytes(B * R * C, B * C * R // 32, 1))
         return q, s
 
     op = torch.empty(E, dtype=torch.int32, device=dev)
 
     def mx_rows_g(name, x, rows, cols):
-        q, s = u8(cols, Mp), u8(cols, Mp // 32)
+        q, s = u8(cols, Mp), u8(*fm.mx_k4_shape(cols, Mp // 32))
         step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
-                                                       offs_pad=op),
+                                                       offs_pad=op, layout=K4),
                  qbytes(rows * cols, cols * rows // 32, 1))
         return q, s
 
     qx, sx = mx_last("mx X", Xd, M, H)
     qw1, sw1 = mx_last("mx W1", W1d, E * F2, H)
-    g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H, sk=fm.SCALE_E8M0)
+    g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H, sk=fm.SCALE_E8M0_K4)
     qa2, sa2 = mx_last("mx A2", A2d, M, F)
     qw2, sw2 = mx_last("mx W2", W2d, E * H, F)
-    g_m("gemm fwd W2", qa2, sa2, qw2, sw2, M, H, F, sk=fm.SCALE_E8M0)
+    g_m("gemm fwd W2", qa2, sa2, qw2, sw2, M, H, F, sk=fm.SCALE_E8M0_K4)
     qdy, sdy = mx_last("mx dY", DYd, M, H)
     qw2t, sw2t = mx_rows_b("mx W2^T", W2d, E, H, F)
-    g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, M, F, H, sk=fm.SCALE_E8M0)
+    g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, M, F, H, sk=fm.SCALE_E8M0_K4)
     qdyt, sdyt = mx_rows_g("mx dY^T", DYd, M, H)
     qa2t, sa2t = mx_rows_g("mx A2^T", A2d, M, F)
-    g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0, offs_t=op)
+    g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0_K4, offs_t=op)
     qdh, sdh = mx_last("mx dH1", DH1d, M, F2)
     qw1t, sw1t = mx_rows_b("mx W1^T", W1d, E, F2, H)
-    g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, M, H, F2, sk=fm.SCALE_E8M0)
+    g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, M, H, F2, sk=fm.SCALE_E8M0_K4)
     qdht, sdht = mx_rows_g("mx dH1^T", DH1d, M, F2)
     qxt, sxt = mx_rows_g("mx X^T", Xd, M, H)
-    g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0, offs_t=op)
+    g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0_K4, offs_t=op)
     return step, host
 
 

@@ -81,6 +81,19 @@ extern "C" {
 #define FP8MOE_MX_FLOOR_OCP 0
 #define FP8MOE_MX_CEIL 1
 
+/* e8m0 scale layouts of quantize_mx.  A scale matrix has R rows (the rows of
+ * the operand that a GEMM contracts along) and NB = L / 32 blocks per row:
+ *   ROWS: row-major, byte (r, b) at r * NB + b.
+ *   K4:   the four blocks of one 128-wide contraction stage of all rows
+ *         together: byte (r, b) at ((b / 4) * R + r) * 4 + b % 4, size
+ *         4 * R * ceil(NB / 4); bytes of blocks NB .. 4 ceil(NB / 4) - 1 are
+ *         written as 0.  One GEMM stage then reads its scales as one
+ *         contiguous run per operand tile instead of one word per row.
+ * [P2 Details, MXFP8 data/scale layout diagram: one e8m0 scale per 1x32 block;
+ * the K4 arrangement is this library's choice for its GEMM.] */
+#define FP8MOE_MX_LAYOUT_ROWS 0
+#define FP8MOE_MX_LAYOUT_K4 1
+
 /* grouped GEMM modes */
 #define FP8MOE_GROUPED_M 0         /* 2D x 3D -> 2D: forward and dgrad */
 #define FP8MOE_GROUPED_K 1         /* 2D x 2D -> 3D: wgrad, contracting over tokens */
@@ -94,6 +107,7 @@ extern "C" {
 #define FP8MOE_SCALE_F32 0         /* fp32 multipliers (divide in the epilogue) */
 #define FP8MOE_SCALE_E8M0 1        /* e8m0 per 32-block along the contraction (MXFP8) */
 #define FP8MOE_SCALE_NONE 2        /* unscaled bf16 operands */
+#define FP8MOE_SCALE_E8M0_K4 3     /* e8m0 as SCALE_E8M0, in the K4 layout of quantize_mx */
 
 /* output dtypes */
 #define FP8MOE_OUT_BF16 0          /* round to nearest even */
@@ -157,11 +171,15 @@ int quantize_colwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t co
  *     Each group is zero-padded to a multiple of 32 rows (pad counted as +0);
  *     columns past the last padded group are written as data 0 and scale 0.
  *     rows_pad % 32 == 0 and rows_pad >= quantize_mx_rows_bound(rows, n_groups).
+ *   scale_layout: FP8MOE_MX_LAYOUT_ROWS gives the row-major scale shapes above;
+ *     FP8MOE_MX_LAYOUT_K4 the K4 layout of the same matrices, with
+ *     R = batch*rows, NB = cols/32 (axis 1); R = batch*cols, NB = rows/32
+ *     (axis 0 without offs); R = cols, NB = rows_pad/32 (axis 0 with offs).
  *   Requires cols % 8 == 0 for axis == 0; x and q 16-byte aligned.
  *   MX is defined for e4m3fn only (there is no codec argument).
  */
 int quantize_mx(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis,
-                const int32_t *offs, int32_t n_groups, int rule,
+                const int32_t *offs, int32_t n_groups, int rule, int scale_layout,
                 void *q, void *scale_e8m0, int64_t rows_pad, int32_t *offs_pad_out,
                 void *stream);
 
@@ -188,10 +206,13 @@ int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups);
  *     SCALE_F32:  a_scale f32 [E][N], b_scale f32 [E][K].
  *     SCALE_E8M0: a_scale u8 [N][M/32], b_scale u8 [K][M/32]; M = padded rows and
  *                 offs = padded offsets from quantize_mx (multiples of 32).
+ *   SCALE_E8M0_K4: the same e8m0 scales in quantize_mx's K4 layout, the operand's
+ *     scale rows being R = M and E*N (GROUPED_M: a, b) or N and K (GROUPED_K);
+ *     4-byte aligned, 4 * R * ceil(L/128) bytes each (L = K or M) and below 2^31.
  *     SCALE_NONE with OPD_BF16 operands: a bf16 [M][N], b bf16 [M][K] (token-major).
  *   offs may be NULL only when n_groups == 1 (one group of all M rows).
- *   Formats: both operands FP8 (e4m3fn or e4m3fnuz, mixed allowed; e8m0 needs
- *   e4m3fn) or both BF16 (GROUPED_K with SCALE_NONE only).
+ *   Formats: both operands FP8 (e4m3fn or e4m3fnuz, mixed allowed; e8m0 scales
+ *   need e4m3fn) or both BF16 (GROUPED_K with SCALE_NONE only).
  *   Accumulation is fp32; out is bf16 (round to nearest even) or fp32.
  *   Requires: M, N, K >= 0; FP8 operands: K % 16 == 0 and K <= 2^23 (GROUPED_M) or
  *   M % 16 == 0 and M <= 2^23 (GROUPED_K); BF16 operands: M, N, K % 8 == 0;

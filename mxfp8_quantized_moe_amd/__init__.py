@@ -11,14 +11,16 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (E4M3FN, E4M3FNUZ, MX_FLOOR_OCP, MX_CEIL, GROUPED_M, GROUPED_K, OPD_E4M3FN,
-                   OPD_E4M3FNUZ, OPD_BF16, SCALE_F32, SCALE_E8M0, SCALE_NONE, OUT_BF16, OUT_F32,
+from ._lib import (E4M3FN, E4M3FNUZ, MX_FLOOR_OCP, MX_CEIL, MX_LAYOUT_ROWS, MX_LAYOUT_K4, GROUPED_M, GROUPED_K,
+                   OPD_E4M3FN, OPD_E4M3FNUZ, OPD_BF16, SCALE_F32, SCALE_E8M0, SCALE_NONE, SCALE_E8M0_K4,
+                   OUT_BF16, OUT_F32,
                    Fp8MoeError)
 
 __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_rows_bound",
            "grouped_mm_scaled", "encode_f32", "default_codec", "E4M3FN", "E4M3FNUZ", "MX_FLOOR_OCP",
-           "MX_CEIL", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ", "OPD_BF16", "SCALE_F32",
-           "SCALE_E8M0", "SCALE_NONE", "OUT_BF16", "OUT_F32", "Fp8MoeError"]
+           "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
+           "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
+           "mx_k4_shape", "Fp8MoeError"]
 
 
 def _ptr(t):
@@ -79,27 +81,41 @@ def quantize_mx_rows_bound(rows: int, n_groups: int) -> int:
     return int(_lib.lib().quantize_mx_rows_bound(rows, n_groups))
 
 
+def mx_k4_shape(rows: int, n_blocks: int):
+    """Shape of an e8m0 scale matrix of `rows` rows and `n_blocks` 32-blocks per row in the K4
+    layout: [ceil(n_blocks / 4), rows, 4]."""
+    return ((n_blocks + 3) // 4, rows, 4)
+
+
 def quantize_mx(x, axis=1, offs=None, rule=MX_FLOOR_OCP, rows_pad=None, q=None, scale=None,
-                offs_pad=None, stream=None):
+                offs_pad=None, layout=MX_LAYOUT_ROWS, stream=None):
     """MXFP8.  axis=1: x [R, C] -> (q [R, C], e8m0 [R, C/32], None).
     axis=0 without offs: x [B, R, C] -> (q phys [B, C, R], e8m0 [B, C, R/32], None).
-    axis=0 with offs: x [M, C] -> (q phys [C, rows_pad], e8m0 [C, rows_pad/32], offs_pad [E])."""
+    axis=0 with offs: x [M, C] -> (q phys [C, rows_pad], e8m0 [C, rows_pad/32], offs_pad [E]).
+    layout=MX_LAYOUT_K4: e8m0 in the K4 layout instead, shape mx_k4_shape(scale rows, blocks) with
+    scale rows R (axis 1), B*C (axis 0 without offs), C (axis 0 with offs)."""
     x = _bits(x).contiguous()
     dev = x.device
+    k4 = layout == MX_LAYOUT_K4
+
+    def sc_empty(rows_major_shape, n_rows, n_blocks):
+        shape = mx_k4_shape(n_rows, n_blocks) if k4 else rows_major_shape
+        return torch.empty(shape, dtype=torch.uint8, device=dev)
+
     if axis == 1:
         C = x.shape[-1]
         R = x.numel() // max(C, 1)
         q = torch.empty(tuple(x.shape), dtype=torch.uint8, device=dev) if q is None else q
-        scale = torch.empty(tuple(x.shape[:-1]) + (C // 32,), dtype=torch.uint8, device=dev) if scale is None else scale
-        st = _lib.lib().quantize_mx(_ptr(x), 1, R, C, 1, None, 0, rule, _ptr(q), _ptr(scale), 0, None,
+        scale = sc_empty(tuple(x.shape[:-1]) + (C // 32,), R, C // 32) if scale is None else scale
+        st = _lib.lib().quantize_mx(_ptr(x), 1, R, C, 1, None, 0, rule, layout, _ptr(q), _ptr(scale), 0, None,
                                     _stream(stream))
         _lib.check("quantize_mx", st)
         return q, scale, None
     if offs is None:
         B, R, C = x.shape
         q = torch.empty((B, C, R), dtype=torch.uint8, device=dev) if q is None else q
-        scale = torch.empty((B, C, R // 32), dtype=torch.uint8, device=dev) if scale is None else scale
-        st = _lib.lib().quantize_mx(_ptr(x), B, R, C, 0, None, 0, rule, _ptr(q), _ptr(scale), R, None,
+        scale = sc_empty((B, C, R // 32), B * C, R // 32) if scale is None else scale
+        st = _lib.lib().quantize_mx(_ptr(x), B, R, C, 0, None, 0, rule, layout, _ptr(q), _ptr(scale), R, None,
                                     _stream(stream))
         _lib.check("quantize_mx", st)
         return q, scale, None
@@ -107,9 +123,9 @@ def quantize_mx(x, axis=1, offs=None, rule=MX_FLOOR_OCP, rows_pad=None, q=None, 
     E = offs.numel()
     rows_pad = rows_pad or quantize_mx_rows_bound(M, E)
     q = torch.empty((C, rows_pad), dtype=torch.uint8, device=dev) if q is None else q
-    scale = torch.empty((C, rows_pad // 32), dtype=torch.uint8, device=dev) if scale is None else scale
+    scale = sc_empty((C, rows_pad // 32), C, rows_pad // 32) if scale is None else scale
     offs_pad = torch.empty((E,), dtype=torch.int32, device=dev) if offs_pad is None else offs_pad
-    st = _lib.lib().quantize_mx(_ptr(x), 1, M, C, 0, _ptr(offs), E, rule, _ptr(q), _ptr(scale), rows_pad,
+    st = _lib.lib().quantize_mx(_ptr(x), 1, M, C, 0, _ptr(offs), E, rule, layout, _ptr(q), _ptr(scale), rows_pad,
                                 _ptr(offs_pad), _stream(stream))
     _lib.check("quantize_mx", st)
     return q, scale, offs_pad

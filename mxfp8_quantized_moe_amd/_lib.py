@@ -14,9 +14,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8moe.s
 OK, ERR_NULL, ERR_SHAPE, ERR_ENUM, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE = range(8)
 E4M3FN, E4M3FNUZ = 0, 1
 MX_FLOOR_OCP, MX_CEIL = 0, 1
+MX_LAYOUT_ROWS, MX_LAYOUT_K4 = 0, 1
 GROUPED_M, GROUPED_K = 0, 1
 OPD_E4M3FN, OPD_E4M3FNUZ, OPD_BF16 = 0, 1, 2
-SCALE_F32, SCALE_E8M0, SCALE_NONE = 0, 1, 2
+SCALE_F32, SCALE_E8M0, SCALE_NONE, SCALE_E8M0_K4 = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_rows_bound",
@@ -30,7 +31,7 @@ _vp, _i64, _i32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.
 _SIGS = {
     "quantize_rowwise": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),
     "quantize_colwise": (_int, [_vp, _i64, _i64, _i64, _vp, _i32, _int, _vp, _i64, _vp, _vp]),
-    "quantize_mx": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i32, _int, _vp, _vp, _i64, _vp, _vp]),
+    "quantize_mx": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i32, _int, _int, _vp, _vp, _i64, _vp, _vp]),
     "quantize_mx_rows_bound": (_i64, [_i64, _i32]),
     "grouped_mm_scaled": (_int, [_int, _vp, _int, _vp, _vp, _int, _vp, _int, _vp, _i32, _i64, _i64, _i64,
                                  _vp, _int, _vp]),

@@ -50,13 +50,13 @@ int quantize_colwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t co
 }
 
 int quantize_mx(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,
-                int32_t n_groups, int rule, void* q, void* scale_e8m0, int64_t rows_pad, int32_t* offs_pad_out,
-                void* stream) {
-  const int st = check_quantize_mx(x_bf16, batch, rows, cols, axis, offs, n_groups, rule, q, scale_e8m0,
-                                   rows_pad, offs_pad_out);
+                int32_t n_groups, int rule, int scale_layout, void* q, void* scale_e8m0, int64_t rows_pad,
+                int32_t* offs_pad_out, void* stream) {
+  const int st = check_quantize_mx(x_bf16, batch, rows, cols, axis, offs, n_groups, rule, scale_layout, q,
+                                   scale_e8m0, rows_pad, offs_pad_out);
   if (st) return st;
   return launch_status(launch_quantize_mx(static_cast<const uint16_t*>(x_bf16), batch, rows, cols, axis, offs,
-                                          n_groups, rule, static_cast<uint8_t*>(q),
+                                          n_groups, rule, scale_layout, static_cast<uint8_t*>(q),
                                           static_cast<uint8_t*>(scale_e8m0), rows_pad, offs_pad_out,
                                           as_stream(stream)));
 }
@@ -102,6 +102,6 @@ int fp8moe_default_codec(int hip_device, int* codec_out) {
   return FP8MOE_ERR_UNSUPPORTED;
 }
 
-int fp8moe_version(void) { return 100; }
+int fp8moe_version(void) { return 101; }
 
 }  // extern "C"

@@ -536,13 +536,14 @@ void gemm_fp8_pipe(KParams p) {
   constexpr int SROWS = BM + BN;
   // e8m0: one 4-byte load per tile row and stage (the stage's four 32-blocks),
   // 64 rows per wave-wide load, every wave issuing the same count.
-  constexpr int SC_DMA = SK == 1 ? (SROWS / 64 + 3) / 4 : 0;
+  constexpr bool E8 = SK != 0;                        // e8m0 scales (SK 1: row-major, SK 2: K4 layout)
+  constexpr int SC_DMA = E8 ? (SROWS / 64 + 3) / 4 : 0;
   constexpr int LPS = BPW + SC_DMA;                   // vector-memory ops per wave per stage
-  constexpr int SCB = SK == 1 ? SC_DMA * 4 * 256 : 16;
+  constexpr int SCB = E8 ? SC_DMA * 4 * 256 : 16;
   constexpr int NM = TM * TN;                         // MFMAs per k step
-  constexpr int ND = 2 * (TM + TN) + (SK == 1 ? TM + TN : 0);   // LDS reads per k step
+  constexpr int ND = 2 * (TM + TN) + (E8 ? TM + TN : 0);   // LDS reads per k step
   static_assert(STAGE % 4096 == 0 && BPW_A * 4096 == A_BYTES, "stage must split into 4 waves of 1 KiB blocks");
-  static_assert(SK == 0 || BK == 128, "e8m0 scales need 128-byte stages");
+  static_assert(!E8 || BK == 128, "e8m0 scales need 128-byte stages");
   static_assert((SLOTS * KS) % 2 == 0 && SLOTS >= 2 && SLOTS <= 4, "fragment sets alternate across the ring");
   static_assert(SLOTS * (STAGE + SCB) <= 150 * 1024, "LDS budget");
 
@@ -616,7 +617,11 @@ void gemm_fp8_pipe(KParams p) {
   // e8m0 row length: fixed per launch.
   const int ld = MODE == 0 ? p.K : p.M;
   const int64_t out_ld = MODE == 0 ? p.N : p.K;
-  const int sc_ld = MODE == 0 ? p.K / 32 : p.M / 32;
+  // e8m0 row stride: a row's blocks (row-major), or one stage's four blocks (K4,
+  // where the next stage of the same rows lies 4 * rows further on).
+  const int sc_ld = SK == 2 ? 4 : (MODE == 0 ? p.K / 32 : p.M / 32);
+  const uint32_t k4_p = SK == 2 ? (uint32_t)(4 * (MODE == 0 ? p.M : p.N)) : 0u;          // K4 stage stride, P
+  const uint32_t k4_q = SK == 2 ? (uint32_t)(4 * (MODE == 0 ? (int64_t)p.E * p.N : p.K)) : 0u;   // and Q
 
   // Everything a tile needs, from its logical index.
   struct Tile {
@@ -785,15 +790,17 @@ void gemm_fp8_pipe(KParams p) {
                                     : (uint32_t)(min(r0 + 4 * R::RPB * (i - BPW_A), qv1) * ld + lc16);
       dma_16((i < BPW_A ? tl.P : tl.Q) + (ro + pos), dst + (wave + 4 * i) * 1024);
     }
-    if constexpr (SK == 1) {
-      const int blk0 = base >> 5;
+    if constexpr (E8) {
+      const uint32_t blk0 = (uint32_t)(base >> 5);
       uint8_t* sdst = slot_scale[S];
 #pragma unroll
       for (int i = 0; i < SC_DMA; ++i) {
         const int rb = 64 * (wave + 4 * i);
-        const uint8_t* sbase = (rb >= BM && rb < SROWS) ? tl.qsc : tl.psc;
+        const bool in_q = rb >= BM && rb < SROWS;
+        const uint8_t* sbase = in_q ? tl.qsc : tl.psc;
         const uint32_t so = soff != nullptr ? soff[i] : scale_row_off(tl, wave, lane, i);
-        dma_4(sbase + (so + (uint32_t)blk0), sdst + 256 * (wave + 4 * i));
+        const uint32_t st_off = SK == 2 ? (blk0 >> 2) * (in_q ? k4_q : k4_p) : blk0;
+        dma_4(sbase + (so + st_off), sdst + 256 * (wave + 4 * i));
       }
     }
   };
@@ -837,8 +844,8 @@ void gemm_fp8_pipe(KParams p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int c_lo = cur.c_lo, c_hi = cur.c_hi, c_start = cur.c_start, nk = cur.nk;
   const float* const sinv = s_inv[it & 1];
-  uint32_t soff[SK == 1 ? SC_DMA : 1];
-  if constexpr (SK == 1) {
+  uint32_t soff[E8 ? SC_DMA : 1];
+  if constexpr (E8) {
 #pragma unroll
     for (int i = 0; i < SC_DMA; ++i) soff[i] = scale_row_off(cur, wave, lane, i);
   }
@@ -883,7 +890,7 @@ void gemm_fp8_pipe(KParams p) {
       const u32x4 lo = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + g));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + 2 + g));
       fa[SET][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (SK == 1) {
+      if constexpr (E8) {
         const int s = sc[4 * r + 2 * h + g];
         ea[SET] = i == 0 ? s : (ea[SET] | (s << (8 * i)));
       }
@@ -894,7 +901,7 @@ void gemm_fp8_pipe(KParams p) {
       const u32x4 lo = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + g));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + 2 + g));
       fb[SET][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (SK == 1) {
+      if constexpr (E8) {
         const int s = sc[4 * (BM + r) + 2 * h + g];
         eb[SET] = j == 0 ? s : (eb[SET] | (s << (8 * j)));
       }
@@ -909,7 +916,7 @@ void gemm_fp8_pipe(KParams p) {
         // B fragment first: the 32x32 result then holds output row (lane & 31)
         // and output columns 8 (v / 4) + 4 (lane >> 5) + v % 4 in register v,
         // i.e. four consecutive columns per register quad (the epilogue packs them).
-        if constexpr (SK == 1)
+        if constexpr (E8)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[SET][j], fa[SET][i], acc[i][j], 0, 0, j,
                                                                       eb[SET], i, ea[SET]);
         else
@@ -1243,6 +1250,8 @@ template <int MODE>
 static hipError_t dispatch_fp8(const GemmArgs& g, hipStream_t st) {
   if (g.scale_kind == 1)
     return g.out_dtype == 0 ? pick_tile<MODE, 1, 0>(g, st) : pick_tile<MODE, 1, 1>(g, st);
+  if (g.scale_kind == 3)   // e8m0 in the K4 layout: every contraction length takes the pipeline
+    return g.out_dtype == 0 ? pick_tile<MODE, 2, 0>(g, st) : pick_tile<MODE, 2, 1>(g, st);
   return g.out_dtype == 0 ? pick_tile<MODE, 0, 0>(g, st) : pick_tile<MODE, 0, 1>(g, st);
 }
 

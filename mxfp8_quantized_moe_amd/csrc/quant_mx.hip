@@ -17,17 +17,47 @@
 //    at every group, each group is padded to a multiple of 32 rows with +0,
 //    groups sit back to back at padded offsets, and the columns past the last
 //    padded group are written with zero codes and zero scales.
+//
+// Scales go out row-major ([R][NB], NB blocks per row) or in the K4 layout
+// the GEMM reads one 128-wide stage at a time from: byte (r, b) at
+// ((b / 4) R + r) 4 + b % 4, with the bytes past the last block of a row
+// (up to the next multiple of four) written as 0.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "tile_lds.hpp"
 
 namespace fp8moe {
 
+// Division of 32-bit unsigned values by a fixed divisor d >= 1 with a
+// multiply-high and a shift (the round-up multiplier method): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the quotient is
+// (mulhi(n, m) + n) >> l for every n < 2^32.
+struct DivU32 {
+  uint32_t m;
+  int l;
+  uint32_t d;
+};
+static DivU32 make_div(uint32_t d) {
+  int l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return DivU32{(uint32_t)m, l, d};
+}
+__device__ __forceinline__ uint32_t div_u32(uint32_t n, const DivU32& q) {
+  return (uint32_t)(((uint64_t)__umulhi(n, q.m) + n) >> q.l);
+}
+
+// Byte offset of scale (row r, block b) in the K4 layout with R rows.
+__device__ __forceinline__ int64_t k4_index(int64_t r, int b, int64_t R) {
+  return ((int64_t)(b >> 2) * R + r) * 4 + (b & 3);
+}
+
 // ------------------------------------------------------------ last-dim blocks
 
-template <int RULE>
+template <int RULE, bool K4>
 __global__ __launch_bounds__(256) void mx_lastdim_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
-                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                         DivU32 nb, int64_t n_rows) {
   // chunk = 8 consecutive elements; 4 chunks = one block; rows are multiples of 32
   for (int64_t ci = (int64_t)blockIdx.x * 256 + threadIdx.x; ci < n_chunks; ci += (int64_t)gridDim.x * 256) {
     const u32x4 v = reinterpret_cast<const u32x4*>(x)[ci];
@@ -38,7 +68,33 @@ __global__ __launch_bounds__(256) void mx_lastdim_kernel(const uint16_t* __restr
     const int X = mx_exponent(m << 16, RULE);
     const float s = exp2_neg(X);
     reinterpret_cast<u32x2*>(q)[ci] = u32x2{quant_bf16x4<0>(v.x, v.y, s), quant_bf16x4<0>(v.z, v.w, s)};
-    if ((ci & 3) == 0) sc[ci >> 2] = (uint8_t)(X + 127);
+    if constexpr (K4) {
+      // 16 lanes hold one stage's four blocks of one row when rows have whole
+      // stages (chunks start at multiples of 256, rows at multiples of 16):
+      // their first lane writes the four codes as one word.  Otherwise a
+      // block's first lane writes its byte (and the row's padding).
+      const uint32_t blk = (uint32_t)(ci >> 2);          // < 2^31: the K4 tensor is bounded by the host
+      if ((nb.d & 3) == 0) {
+        const int lane = threadIdx.x & 63;
+        const uint32_t e = (uint32_t)(X + 127);
+        const uint32_t w = e | ((uint32_t)__shfl((int)e, lane + 4, 64) << 8) |
+                           ((uint32_t)__shfl((int)e, lane + 8, 64) << 16) |
+                           ((uint32_t)__shfl((int)e, lane + 12, 64) << 24);
+        if ((ci & 15) == 0) {
+          const uint32_t r = div_u32(blk, nb);
+          *reinterpret_cast<uint32_t*>(sc + k4_index(r, (int)(blk - r * nb.d), n_rows)) = w;
+        }
+      } else if ((ci & 3) == 0) {
+        const uint32_t r = div_u32(blk, nb);
+        const int b = (int)(blk - r * nb.d);
+        uint8_t* d = sc + k4_index(r, b, n_rows);
+        d[0] = (uint8_t)(X + 127);
+        if (b == (int)nb.d - 1)
+          for (int e = 1; (b + e) & 3; ++e) d[e] = 0;   // pad to the stage's four blocks
+      }
+    } else if ((ci & 3) == 0) {
+      sc[ci >> 2] = (uint8_t)(X + 127);
+    }
   }
 }
 
@@ -57,7 +113,7 @@ struct MxPad {
   __device__ int operator()(int lo, int hi) const { return (hi - lo + 31) & ~31; }
 };
 
-template <int RULE, bool GROUPED>
+template <int RULE, bool GROUPED, bool K4>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t batch, int rows,
                                                       int cols, const int32_t* __restrict__ offs, int n_groups,
                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
@@ -72,9 +128,10 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
 
   // geometry: input rows [lo, hi) -> padded output rows [plo, phi) of the output space
   int lo, hi, plo, phi, j;
-  int64_t ld_q, ld_s;
+  int64_t ld_q;
   uint8_t* qb;
-  uint8_t* sb;
+  int64_t srow0, s_rows;   // scale row of column 0 and scale rows in all
+  int s_nb;                // blocks per scale row
   if constexpr (GROUPED) {
     if (blockIdx.x == 0 && offs_pad_out != nullptr) {
       // padded offsets: inclusive cumulative sum of ceil32 of each group's rows
@@ -107,16 +164,17 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
       lo = hi = 0; plo = un.pbase; phi = (int)rows_pad; j = un.j;
       if (plo + j * kTileRows >= phi) return;
     }
-    ld_q = rows_pad; ld_s = rows_pad / 32; qb = q; sb = sc;
+    ld_q = rows_pad; qb = q;
+    srow0 = 0; s_rows = cols; s_nb = (int)(rows_pad / 32);
   } else {
     const int upb = mx_chunks(0, rows);
     const int64_t b = upb ? u / upb : batch;
     if (b >= batch) return;
     j = u % upb;
     lo = (int)0; hi = rows; plo = 0; phi = rows;
-    ld_q = rows; ld_s = rows / 32;
+    ld_q = rows;
     qb = q + b * cols * (int64_t)rows;
-    sb = sc + b * cols * (int64_t)(rows / 32);
+    srow0 = b * cols; s_rows = batch * cols; s_nb = rows / 32;
     x += b * (int64_t)rows * cols;
   }
 
@@ -178,10 +236,21 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
     const int ci = t >> 2, c = c0 + ci;
     const int nb = (r_end - A) >> 5;
     if (c < cols) {
+      const int64_t srow = srow0 + c;
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
         const int b = 4 * (t & 3) + b4;
-        if (b < nb) sb[(int64_t)c * ld_s + (A >> 5) + b] = s_x[ci * 16 + b];
+        if (b < nb) {
+          const int blk = (A >> 5) + b;
+          if constexpr (K4) {
+            uint8_t* d = sc + k4_index(srow, blk, s_rows);
+            d[0] = s_x[ci * 16 + b];
+            if (blk == s_nb - 1)
+              for (int e = 1; (blk + e) & 3; ++e) d[e] = 0;   // pad to the stage's four blocks
+          } else {
+            sc[srow * s_nb + blk] = s_x[ci * 16 + b];
+          }
+        }
       }
     }
   }
@@ -192,17 +261,35 @@ int64_t mx_rows_units_bound(int64_t batch, int64_t rows, const int32_t* offs, in
   return batch * ((rows + kTileRows - 1) / kTileRows);
 }
 
+template <int RULE>
+static hipError_t launch_rows(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+                              int32_t n_groups, bool k4, uint8_t* q, uint8_t* sc, int64_t rows_pad,
+                              int32_t* offs_pad_out, dim3 grid, int n_strips, hipStream_t st) {
+  if (offs) {
+    auto k = k4 ? mx_rows_kernel<RULE, true, true> : mx_rows_kernel<RULE, true, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, (int64_t)1, (int)rows, (int)cols, offs, n_groups, q, sc,
+                       rows_pad, offs_pad_out, n_strips);
+  } else {
+    auto k = k4 ? mx_rows_kernel<RULE, false, true> : mx_rows_kernel<RULE, false, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, batch, (int)rows, (int)cols, nullptr, 0, q, sc, rows,
+                       nullptr, n_strips);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int axis,
-                              const int32_t* offs, int32_t n_groups, int rule, uint8_t* q, uint8_t* sc,
-                              int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st) {
+                              const int32_t* offs, int32_t n_groups, int rule, int scale_layout, uint8_t* q,
+                              uint8_t* sc, int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st) {
+  const bool k4 = scale_layout == 1;
   if (axis == 1) {
     const int64_t n_chunks = batch * rows * cols / 8;
     if (n_chunks == 0) return hipSuccess;
     const int64_t blocks = std::min<int64_t>((n_chunks + 255) / 256, 1 << 20);
-    if (rule == 0)
-      hipLaunchKernelGGL(mx_lastdim_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, x, n_chunks, q, sc);
-    else
-      hipLaunchKernelGGL(mx_lastdim_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, x, n_chunks, q, sc);
+    const DivU32 nb = make_div((uint32_t)(cols / 32));
+    const int64_t n_rows = batch * rows;
+    auto k = rule == 0 ? (k4 ? mx_lastdim_kernel<0, true> : mx_lastdim_kernel<0, false>)
+                       : (k4 ? mx_lastdim_kernel<1, true> : mx_lastdim_kernel<1, false>);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, st, x, n_chunks, q, sc, nb, n_rows);
     return hipGetLastError();
   }
   if (cols == 0) {
@@ -212,16 +299,10 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, in
   const int64_t units = mx_rows_units_bound(batch, rows, offs, n_groups, rows_pad);
   if (units == 0) return hipSuccess;
   const dim3 grid((unsigned)(units * n_strips));
-  if (offs) {
-    auto k = rule == 0 ? mx_rows_kernel<0, true> : mx_rows_kernel<1, true>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, (int64_t)1, (int)rows, (int)cols, offs, n_groups, q, sc,
-                       rows_pad, offs_pad_out, n_strips);
-  } else {
-    auto k = rule == 0 ? mx_rows_kernel<0, false> : mx_rows_kernel<1, false>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, batch, (int)rows, (int)cols, nullptr, 0, q, sc, rows,
-                       nullptr, n_strips);
-  }
-  return hipGetLastError();
+  return rule == 0 ? launch_rows<0>(x, batch, rows, cols, offs, n_groups, k4, q, sc, rows_pad, offs_pad_out, grid,
+                                    n_strips, st)
+                   : launch_rows<1>(x, batch, rows, cols, offs, n_groups, k4, q, sc, rows_pad, offs_pad_out, grid,
+                                    n_strips, st);
 }
 
 }  // namespace fp8moe

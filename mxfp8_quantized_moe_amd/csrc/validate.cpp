@@ -59,18 +59,24 @@ int check_quantize_colwise(const void* x, int64_t batch, int64_t rows, int64_t c
   return FP8MOE_OK;
 }
 
+int64_t mx_k4_bytes(int64_t rows, int64_t nb) { return mul(mul(rows, (nb + 3) / 4), 4); }
+
 int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,
-                      int32_t n_groups, int rule, const void* q, const void* sc, int64_t rows_pad,
-                      const int32_t* offs_pad_out) {
+                      int32_t n_groups, int rule, int scale_layout, const void* q, const void* sc,
+                      int64_t rows_pad, const int32_t* offs_pad_out) {
   if (rule != FP8MOE_MX_FLOOR_OCP && rule != FP8MOE_MX_CEIL) return FP8MOE_ERR_ENUM;
   if (axis != 0 && axis != 1) return FP8MOE_ERR_ENUM;
+  if (scale_layout != FP8MOE_MX_LAYOUT_ROWS && scale_layout != FP8MOE_MX_LAYOUT_K4) return FP8MOE_ERR_ENUM;
+  const bool k4 = scale_layout == FP8MOE_MX_LAYOUT_K4;
   if (batch < 1 || rows < 0 || cols < 0) return FP8MOE_ERR_SHAPE;
   if (rows > kI32Max / 2 || cols > kI32Max / 2) return FP8MOE_ERR_SHAPE;
   const int64_t n_in = mul(mul(batch, rows), cols);
   if (n_in < 0) return FP8MOE_ERR_SHAPE;
   if (axis == 1) {
     if (offs) return FP8MOE_ERR_UNSUPPORTED;
-    if (!need(x, n_in) || !need(q, n_in) || !need(sc, n_in)) return FP8MOE_ERR_NULL;
+    const int64_t nsc = k4 ? mx_k4_bytes(mul(batch, rows), cols / 32) : n_in / 32;
+    if (nsc < 0 || (k4 && nsc > kI32Max)) return FP8MOE_ERR_SHAPE;
+    if (!need(x, n_in) || !need(q, n_in) || !need(sc, nsc)) return FP8MOE_ERR_NULL;
     if (cols % 32 || !aligned(x, 16) || !aligned(q, 16)) return FP8MOE_ERR_ALIGN;
     return FP8MOE_OK;
   }
@@ -78,7 +84,9 @@ int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, 
   if (offs == nullptr) {
     if (rows % 32) return FP8MOE_ERR_ALIGN;
     if (mul(batch * ((rows + 511) / 512), (cols + 63) / 64) > kI32Max) return FP8MOE_ERR_SHAPE;
-    if (!need(x, n_in) || !need(q, n_in) || !need(sc, n_in)) return FP8MOE_ERR_NULL;
+    const int64_t nsc = k4 ? mx_k4_bytes(mul(batch, cols), rows / 32) : n_in / 32;
+    if (nsc < 0 || (k4 && nsc > kI32Max)) return FP8MOE_ERR_SHAPE;
+    if (!need(x, n_in) || !need(q, n_in) || !need(sc, nsc)) return FP8MOE_ERR_NULL;
     return FP8MOE_OK;
   }
   if (batch != 1 || n_groups < 1 || n_groups > (1 << 20)) return FP8MOE_ERR_SHAPE;
@@ -88,7 +96,9 @@ int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, 
   if (n_out < 0) return FP8MOE_ERR_SHAPE;
   const int64_t units = (rows_pad + 511) / 512 + n_groups + 1;
   if (mul(units, (cols + 63) / 64 + 1) > kI32Max) return FP8MOE_ERR_SHAPE;
-  if (!need(x, n_in) || !need(q, n_out) || !need(sc, n_out)) return FP8MOE_ERR_NULL;
+  const int64_t nsc = k4 ? mx_k4_bytes(cols, rows_pad / 32) : n_out / 32;
+  if (nsc < 0 || (k4 && nsc > kI32Max)) return FP8MOE_ERR_SHAPE;
+  if (!need(x, n_in) || !need(q, n_out) || !need(sc, nsc)) return FP8MOE_ERR_NULL;
   return FP8MOE_OK;
 }
 
@@ -97,7 +107,7 @@ int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const v
                      int64_t N, int64_t K, const void* out, int out_dtype) {
   if (mode != FP8MOE_GROUPED_M && mode != FP8MOE_GROUPED_K) return FP8MOE_ERR_ENUM;
   if (a_fmt < 0 || a_fmt > 2 || b_fmt < 0 || b_fmt > 2) return FP8MOE_ERR_ENUM;
-  if (scale_kind < 0 || scale_kind > 2) return FP8MOE_ERR_ENUM;
+  if (scale_kind < 0 || scale_kind > 3) return FP8MOE_ERR_ENUM;
   if (out_dtype != FP8MOE_OUT_BF16 && out_dtype != FP8MOE_OUT_F32) return FP8MOE_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || n_groups < 1 || n_groups > (1 << 20)) return FP8MOE_ERR_SHAPE;
   if (M > kI32Max / 2 || N > kI32Max / 2 || K > kI32Max / 2) return FP8MOE_ERR_SHAPE;
@@ -106,34 +116,35 @@ int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const v
   if (a_bf16 != b_bf16) return FP8MOE_ERR_UNSUPPORTED;
   if (a_bf16 && (scale_kind != FP8MOE_SCALE_NONE || mode != FP8MOE_GROUPED_K)) return FP8MOE_ERR_UNSUPPORTED;
   if (!a_bf16 && scale_kind == FP8MOE_SCALE_NONE) return FP8MOE_ERR_UNSUPPORTED;
-  if (scale_kind == FP8MOE_SCALE_E8M0 && (a_fmt != FP8MOE_OPD_E4M3FN || b_fmt != FP8MOE_OPD_E4M3FN))
-    return FP8MOE_ERR_UNSUPPORTED;
+  const bool e8 = scale_kind == FP8MOE_SCALE_E8M0, k4 = scale_kind == FP8MOE_SCALE_E8M0_K4;
+  if ((e8 || k4) && (a_fmt != FP8MOE_OPD_E4M3FN || b_fmt != FP8MOE_OPD_E4M3FN)) return FP8MOE_ERR_UNSUPPORTED;
   const int64_t E = n_groups;
   int64_t na, nb, no, nsa, nsb;
   if (mode == FP8MOE_GROUPED_M) {
     na = mul(M, K); nb = mul(mul(E, N), K); no = mul(M, N);
-    nsa = scale_kind == FP8MOE_SCALE_E8M0 ? mul(M, K / 32) : M;
-    nsb = scale_kind == FP8MOE_SCALE_E8M0 ? mul(mul(E, N), K / 32) : mul(E, N);
+    nsa = e8 ? mul(M, K / 32) : k4 ? mx_k4_bytes(M, K / 32) : M;
+    nsb = e8 ? mul(mul(E, N), K / 32) : k4 ? mx_k4_bytes(mul(E, N), K / 32) : mul(E, N);
   } else {
     na = mul(N, M); nb = mul(K, M); no = mul(mul(E, N), K);
-    nsa = scale_kind == FP8MOE_SCALE_E8M0 ? mul(N, M / 32) : mul(E, N);
-    nsb = scale_kind == FP8MOE_SCALE_E8M0 ? mul(K, M / 32) : mul(E, K);
+    nsa = e8 ? mul(N, M / 32) : k4 ? mx_k4_bytes(N, M / 32) : mul(E, N);
+    nsb = e8 ? mul(K, M / 32) : k4 ? mx_k4_bytes(K, M / 32) : mul(E, K);
   }
   if (na < 0 || nb < 0 || no < 0 || nsa < 0 || nsb < 0 || mul(no, 4) < 0) return FP8MOE_ERR_SHAPE;
+  if (k4 && (nsa > kI32Max || nsb > kI32Max)) return FP8MOE_ERR_SHAPE;   // 32-bit offsets in the kernel
   if (!need(a, na) || !need(b, nb) || !need(out, no)) return FP8MOE_ERR_NULL;
   if (scale_kind != FP8MOE_SCALE_NONE && (!need(sa, nsa) || !need(sb, nsb))) return FP8MOE_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16)) return FP8MOE_ERR_ALIGN;
-  if (scale_kind == FP8MOE_SCALE_F32 && (!aligned(sa, 4) || !aligned(sb, 4))) return FP8MOE_ERR_ALIGN;
+  if ((scale_kind == FP8MOE_SCALE_F32 || k4) && (!aligned(sa, 4) || !aligned(sb, 4))) return FP8MOE_ERR_ALIGN;
   if (a_bf16) {
     if (N % 8 || K % 8 || M % 8) return FP8MOE_ERR_ALIGN;
   } else if (mode == FP8MOE_GROUPED_M) {
     if (K > (1 << 23)) return FP8MOE_ERR_SHAPE;     // tile-row offsets are 32-bit in the kernel
     if (K % 16) return FP8MOE_ERR_ALIGN;
-    if (scale_kind == FP8MOE_SCALE_E8M0 && K % 32) return FP8MOE_ERR_ALIGN;
+    if ((e8 || k4) && K % 32) return FP8MOE_ERR_ALIGN;
   } else {
     if (M > (1 << 23)) return FP8MOE_ERR_SHAPE;     // tile-row offsets are 32-bit in the kernel
     if (M % 16) return FP8MOE_ERR_ALIGN;
-    if (scale_kind == FP8MOE_SCALE_E8M0 && M % 32) return FP8MOE_ERR_ALIGN;
+    if ((e8 || k4) && M % 32) return FP8MOE_ERR_ALIGN;
   }
   return FP8MOE_OK;
 }

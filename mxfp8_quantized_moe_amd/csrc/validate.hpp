@@ -11,8 +11,11 @@ int check_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ld
 int check_quantize_colwise(const void* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                            int32_t n_groups, int codec, const void* q_t, int64_t ld_q, const void* scale);
 int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,
-                      int32_t n_groups, int rule, const void* q, const void* sc, int64_t rows_pad,
-                      const int32_t* offs_pad_out);
+                      int32_t n_groups, int rule, int scale_layout, const void* q, const void* sc,
+                      int64_t rows_pad, const int32_t* offs_pad_out);
+// Bytes of an e8m0 scale matrix of `rows` rows and `nb` 32-blocks per row in
+// the K4 layout (nb rounded up to whole 128-wide stages), or -1 on overflow.
+int64_t mx_k4_bytes(int64_t rows, int64_t nb);
 int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const void* b, int b_fmt,
                      const void* sb, int scale_kind, const int32_t* offs, int32_t n_groups, int64_t M,
                      int64_t N, int64_t K, const void* out, int out_dtype);

@@ -54,3 +54,13 @@ def assert_bytes_equal(got: np.ndarray, ref: np.ndarray, what: str) -> None:
 def assert_f32_bits_equal(got: np.ndarray, ref: np.ndarray, what: str) -> None:
     assert_bytes_equal(np.asarray(got, np.float32).view(np.uint32), np.asarray(ref, np.float32).view(np.uint32),
                        what)
+
+
+def e8m0_rows_to_k4(sc: np.ndarray) -> np.ndarray:
+    """Row-major e8m0 scales [R, NB] in the K4 layout of include/fp8moe.h: [ceil(NB/4), R, 4], byte
+    (r, b) at [b // 4, r, b % 4], the bytes past block NB - 1 of a row zero."""
+    R, NB = sc.shape
+    G = (NB + 3) // 4
+    padded = np.zeros((R, 4 * G), np.uint8)
+    padded[:, :NB] = sc
+    return np.ascontiguousarray(padded.reshape(R, G, 4).transpose(1, 0, 2))

@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 8):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 100
+    assert lib.fp8moe_version() == 101
 
 
 def test_rows_bound(lib):
@@ -85,15 +85,20 @@ def test_colwise_rejections(lib):
 
 def test_mx_rejections(lib):
     f = lib.quantize_mx
-    assert f(P, 1, 64, 64, 1, None, 0, 5, P, P, 0, None, None) == L.ERR_ENUM       # rule
-    assert f(P, 1, 64, 64, 2, None, 0, 0, P, P, 0, None, None) == L.ERR_ENUM       # axis
-    assert f(P, 1, 64, 48, 1, None, 0, 0, P, P, 0, None, None) == L.ERR_ALIGN      # cols % 32
-    assert f(P, 1, 64, 64, 1, P, 4, 0, P, P, 0, None, None) == L.ERR_UNSUPPORTED   # offs on axis 1
-    assert f(P, 1, 40, 64, 0, None, 0, 0, P, P, 0, None, None) == L.ERR_ALIGN      # rows % 32
-    assert f(P, 1, 75, 64, 0, P, 4, 0, P, P, 192, P, None) == L.ERR_SHAPE          # rows_pad < bound
-    assert f(P, 1, 75, 64, 0, P, 4, 0, P, P, 230, P, None) == L.ERR_ALIGN          # rows_pad % 32
-    assert f(P, 2, 75, 64, 0, P, 4, 0, P, P, 224, P, None) == L.ERR_SHAPE          # batch with offs
-    assert f(P, 1, 75, 64, 0, P, 4, 0, None, P, 224, P, None) == L.ERR_NULL
+    assert f(P, 1, 64, 64, 1, None, 0, 5, 0, P, P, 0, None, None) == L.ERR_ENUM       # rule
+    assert f(P, 1, 64, 64, 2, None, 0, 0, 0, P, P, 0, None, None) == L.ERR_ENUM       # axis
+    assert f(P, 1, 64, 64, 1, None, 0, 0, 2, P, P, 0, None, None) == L.ERR_ENUM       # scale layout
+    assert f(P, 1, 64, 48, 1, None, 0, 0, 0, P, P, 0, None, None) == L.ERR_ALIGN      # cols % 32
+    assert f(P, 1, 64, 48, 1, None, 0, 0, 1, P, P, 0, None, None) == L.ERR_ALIGN      # cols % 32 (K4)
+    assert f(P, 1, 64, 64, 1, P, 4, 0, 0, P, P, 0, None, None) == L.ERR_UNSUPPORTED   # offs on axis 1
+    assert f(P, 1, 40, 64, 0, None, 0, 0, 0, P, P, 0, None, None) == L.ERR_ALIGN      # rows % 32
+    assert f(P, 1, 75, 64, 0, P, 4, 0, 0, P, P, 192, P, None) == L.ERR_SHAPE          # rows_pad < bound
+    assert f(P, 1, 75, 64, 0, P, 4, 0, 0, P, P, 230, P, None) == L.ERR_ALIGN          # rows_pad % 32
+    assert f(P, 2, 75, 64, 0, P, 4, 0, 0, P, P, 224, P, None) == L.ERR_SHAPE          # batch with offs
+    assert f(P, 1, 75, 64, 0, P, 4, 0, 0, None, P, 224, P, None) == L.ERR_NULL
+    assert f(P, 1, 75, 64, 0, P, 4, 0, 1, P, None, 224, P, None) == L.ERR_NULL        # K4 scales missing
+    # K4 scale tensors are addressed with 32-bit offsets: at most 2^31 - 1 bytes
+    assert f(P, 1, 1 << 29, 2048, 1, None, 0, 0, 1, P, P, 0, None, None) == L.ERR_SHAPE
 
 
 def test_gemm_rejections(lib):
@@ -107,7 +112,7 @@ def test_gemm_rejections(lib):
 
     assert call(mode=2) == L.ERR_ENUM
     assert call(af=3) == L.ERR_ENUM
-    assert call(sk=4) == L.ERR_ENUM
+    assert call(sk=5) == L.ERR_ENUM
     assert call(od=2) == L.ERR_ENUM
     assert call(M=-1) == L.ERR_SHAPE
     assert call(E=0) == L.ERR_SHAPE
@@ -118,6 +123,10 @@ def test_gemm_rejections(lib):
     assert call(af=2, bf=2, sk=2) == L.ERR_UNSUPPORTED    # bf16 only for GROUPED_K
     assert call(sk=2) == L.ERR_UNSUPPORTED                # fp8 without scales
     assert call(sk=1, af=1) == L.ERR_UNSUPPORTED          # e8m0 needs e4m3fn
+    assert call(sk=3, bf=1) == L.ERR_UNSUPPORTED          # also in the K4 layout
+    assert call(sk=3, K=48) == L.ERR_ALIGN                # K % 32 for e8m0 (K4)
+    assert call(sk=3, sa=P + 2) == L.ERR_ALIGN            # K4 scales are read as 4-byte words
+    assert call(sk=3, M=1 << 26, N=64, K=1024, E=1, offs=None) == L.ERR_SHAPE   # K4 a_scale of 2^31 B
     assert call(K=40) == L.ERR_ALIGN                      # K % 16 (GROUPED_M)
     assert call(sk=1, K=48) == L.ERR_ALIGN                # K % 32 for e8m0
     assert call(mode=1, M=40) == L.ERR_ALIGN              # M % 16 (GROUPED_K)

@@ -15,7 +15,7 @@ import torch
 import oracle
 import mxfp8_quantized_moe_amd as fm
 from mxfp8_quantized_moe_amd import synth
-from gpu_helpers import DEV, note, bf16_dev, i32_dev, host, bf16_bits_to_f64
+from gpu_helpers import DEV, note, bf16_dev, i32_dev, host, bf16_bits_to_f64, e8m0_rows_to_k4
 
 pytestmark = pytest.mark.gpu
 
@@ -291,7 +291,8 @@ def test_grouped_k_full_size_sampled():
     check(got[:, rows], ref, contract, tight, "cfg2 wgrad")
 
 
-def test_grouped_m_mx_full_size_sampled():
+@pytest.mark.parametrize("layout", ["rows", "k4"])
+def test_grouped_m_mx_full_size_sampled(layout):
     w = synth.WORKLOADS[5]
     x = synth.make_x(w)               # [16384, 5120]
     # a 2048-row slice of every expert's W1 keeps the host-side check small
@@ -299,10 +300,15 @@ def test_grouped_m_mx_full_size_sampled():
     wt = np.stack([synth.normal_bf16(1000 * synth.tensor_seed(5, synth.T_W1) + e, (N, K), 0.02) for e in range(E)])
     offs = w.offs
     M = x.shape[0]
-    note(f"GROUPED_M MX full cfg=5 M={M} N={N} K={K}")
+    note(f"GROUPED_M MX full cfg=5 M={M} N={N} K={K} scales={layout}")
     qa, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0)
     qb, xb, _ = fm.quantize_mx(bf16_dev(wt.reshape(E * N, K)), axis=1, rule=0)
-    out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, xa, qb, 0, xb, fm.SCALE_E8M0, i32_dev(offs), E, M, N, K)
+    if layout == "k4":
+        _, ya, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0, layout=fm.MX_LAYOUT_K4)
+        _, yb, _ = fm.quantize_mx(bf16_dev(wt.reshape(E * N, K)), axis=1, rule=0, layout=fm.MX_LAYOUT_K4)
+        out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, ya, qb, 0, yb, fm.SCALE_E8M0_K4, i32_dev(offs), E, M, N, K)
+    else:
+        out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, xa, qb, 0, xb, fm.SCALE_E8M0, i32_dev(offs), E, M, N, K)
     _, got = _out_host(out)
     qa_h, xa_h = host(qa), host(xa)
     qb_h, xb_h = host(qb).reshape(E, N, K), host(xb).reshape(E, N, K // 32)
@@ -412,3 +418,94 @@ def test_grouped_m_mx_unaligned_k():
     B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
     contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
     check(got, ref, contract, tight, "GROUPED_M MX K=288")
+
+
+# ------------------------------------------------------------------ e8m0 scales in the K4 layout
+# The same products with the scales in the layout whose stage words are contiguous per tile:
+# the pipeline reads them with other addresses but the same MFMA sequence, so where the
+# row-major scales take the pipeline too the outputs are bit-identical; elsewhere (contraction
+# lengths that are not a multiple of 128) they are checked against the oracle.
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("K", [512, 288])
+def test_grouped_m_mx_k4(rule, K):
+    x = synth.normal_bf16(61, (900, K), 1.0, 0.01, 30.0)
+    w = synth.normal_bf16(62, (5, 288, K), 0.02)
+    offs = synth.offsets_from_counts(synth.random_counts(63, 880, 5))
+    M = x.shape[0]
+    E, N, _ = w.shape
+    note(f"GROUPED_M MX K4 rule={rule} K={K}")
+    qa, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(w.reshape(E * N, K)), axis=1, rule=rule)
+    _, ya, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule, layout=fm.MX_LAYOUT_K4)
+    _, yb, _ = fm.quantize_mx(bf16_dev(w.reshape(E * N, K)), axis=1, rule=rule, layout=fm.MX_LAYOUT_K4)
+    xa_h, xb_h = host(xa), host(xb)
+    assert np.array_equal(host(ya), e8m0_rows_to_k4(xa_h)) and np.array_equal(host(yb), e8m0_rows_to_k4(xb_h))
+    ref_rows = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, xa, qb, 0, xb, fm.SCALE_E8M0, i32_dev(offs), E, M, N, K)
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, ya, qb, 0, yb, fm.SCALE_E8M0_K4, i32_dev(offs), E, M, N, K)
+    raw, got = _out_host(out)
+    if K % 128 == 0:       # rows outside every group are left untouched: compare the routed ones
+        used = int(offs[-1])
+        assert np.array_equal(raw[:used], _out_host(ref_rows)[0][:used]), "K4 and row-major scales differ"
+    qa_h = host(qa)
+    qb_h, xb3 = host(qb).reshape(E, N, K), xb_h.reshape(E, N, K // 32)
+    ref = oracle.mm_grouped_m_mx(qa_h, xa_h, qb_h, xb3, offs)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb3), 32, axis=-1)
+    contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, f"GROUPED_M MX K4 K={K}")
+
+
+@pytest.mark.parametrize("case", ["unaligned", "aligned", "small-groups"])
+def test_grouped_k_mx_k4(case):
+    if case == "unaligned":       # rows_pad = 1216: the last stage holds one real 32-block
+        counts = synth.random_counts(64, 990, 6)
+    elif case == "aligned":       # rows_pad = 1024
+        counts = np.array([517, 443])
+    else:
+        counts = np.array([40, 0, 300, 1, 127, 129, 200, 103], np.int64)
+    offs = synth.offsets_from_counts(counts)
+    M = int(np.sum(counts)) + 10
+    dy = synth.normal_bf16(65, (M, 320), 1e-3)
+    x = synth.normal_bf16(66, (M, 288), 1.0, 0.01, 30.0)
+    N, K, E = dy.shape[1], x.shape[1], len(offs)
+    Mp = fm.quantize_mx_rows_bound(M, E)
+    note(f"GROUPED_K MX K4 {case} Mp={Mp}")
+    qa, xa, op = fm.quantize_mx(bf16_dev(dy), axis=0, offs=i32_dev(offs), rule=0, rows_pad=Mp)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=0, rows_pad=Mp)
+    _, ya, _ = fm.quantize_mx(bf16_dev(dy), axis=0, offs=i32_dev(offs), rule=0, rows_pad=Mp, layout=fm.MX_LAYOUT_K4)
+    _, yb, _ = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=0, rows_pad=Mp, layout=fm.MX_LAYOUT_K4)
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, ya, qb, 0, yb, fm.SCALE_E8M0_K4, op, E, Mp, N, K)
+    raw, got = _out_host(out)
+    if Mp % 128 == 0:
+        ref_rows = fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, xa, qb, 0, xb, fm.SCALE_E8M0, op, E, Mp, N, K)
+        assert np.array_equal(raw, _out_host(ref_rows)[0]), "K4 and row-major scales differ"
+    qa_h, xa_h, qb_h, xb_h, op_h = host(qa), host(xa), host(qb), host(xb), host(op)
+    ref = oracle.mm_grouped_k_mx(qa_h, xa_h, qb_h, xb_h, op_h)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_k(A, B, op_h, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, f"GROUPED_K MX K4 {case}")
+
+
+def test_grouped_m_mx_k4_batched_weights():
+    # dgrad-style B operand: weights quantized along their rows (batched axis 0), scale rows E * N
+    x = synth.normal_bf16(67, (700, 384), 1.0, 0.01, 30.0)
+    w = synth.normal_bf16(68, (4, 384, 160), 0.02)             # [E][K][N] -> B phys [E][N][K]
+    offs = synth.offsets_from_counts(synth.random_counts(69, 690, 4))
+    M, K = x.shape
+    E, _, N = w.shape
+    note("GROUPED_M MX K4 batched weights")
+    qa, ya, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0, layout=fm.MX_LAYOUT_K4)
+    qb, yb, _ = fm.quantize_mx(bf16_dev(w), axis=0, rule=0, layout=fm.MX_LAYOUT_K4)
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, ya, qb, 0, yb, fm.SCALE_E8M0_K4, i32_dev(offs), E, M, N, K)
+    _, got = _out_host(out)
+    _, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0)
+    _, xb, _ = fm.quantize_mx(bf16_dev(w), axis=0, rule=0)
+    qa_h, xa_h = host(qa), host(xa)
+    qb_h, xb_h = host(qb), host(xb)                               # [E][N][K], [E][N][K/32]
+    ref = oracle.mm_grouped_m_mx(qa_h, xa_h, qb_h, xb_h, offs)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, "GROUPED_M MX K4 batched weights")

@@ -13,7 +13,7 @@ import torch
 import oracle
 import mxfp8_quantized_moe_amd as fm
 from mxfp8_quantized_moe_amd import synth
-from gpu_helpers import (DEV, note, bf16_dev, i32_dev, filled_u8, filled_f32, host, assert_bytes_equal,
+from gpu_helpers import (DEV, note, bf16_dev, i32_dev, filled_u8, filled_f32, host, assert_bytes_equal, e8m0_rows_to_k4,
                          assert_f32_bits_equal)
 
 pytestmark = pytest.mark.gpu
@@ -175,6 +175,30 @@ def test_mx_rows_batched_parity(rule, shape):
     assert_bytes_equal(host(sc), sr, "e8m0")
 
 
+@pytest.mark.parametrize("shape", [(64, 96), (1000, 5120), (3, 32), (0, 64), (40, 288)])
+def test_mx_lastdim_k4_layout(shape):
+    x = special_input(4100 + shape[0], shape, 0.01, 30.0)
+    R, C = shape
+    note(f"mx lastdim K4 shape={shape}")
+    sc = filled_u8(fm.mx_k4_shape(R, C // 32))
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=0, scale=sc, layout=fm.MX_LAYOUT_K4)
+    qr, sr = oracle.quantize_mx_lastdim(x, 0)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), e8m0_rows_to_k4(sr.reshape(R, C // 32)), "e8m0 K4")
+
+
+@pytest.mark.parametrize("shape", [(2, 544, 72), (3, 32, 8), (1, 1024, 128)])
+def test_mx_rows_batched_k4_layout(shape):
+    x = special_input(5100 + sum(shape), shape, 0.01, 30.0)
+    B, R, C = shape
+    note(f"mx rows batched K4 shape={shape}")
+    sc = filled_u8(fm.mx_k4_shape(B * C, R // 32))
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=0, rule=1, scale=sc, layout=fm.MX_LAYOUT_K4)
+    qr, sr = oracle.quantize_mx_rows_batched(x, 1)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), e8m0_rows_to_k4(sr.reshape(B * C, R // 32)), "e8m0 K4")
+
+
 MX_GROUP_CASES = {
     "ragged": (1300, 136, synth.offsets_from_counts(synth.random_counts(8, 1290, 7))),
     "cfg1": (512, 256, synth.offsets_from_counts(synth.routing_counts(1))),
@@ -198,6 +222,21 @@ def test_mx_rows_grouped_parity(rule, case):
     assert_bytes_equal(host(op), opr, "padded offsets")
     assert_bytes_equal(host(q), qr, "codes")
     assert_bytes_equal(host(sc), sr, "e8m0")
+
+
+@pytest.mark.parametrize("case", list(MX_GROUP_CASES))
+def test_mx_rows_grouped_k4_layout(case):
+    M, C, offs = MX_GROUP_CASES[case]
+    x = special_input(6100 + M, (M, C), 0.01, 30.0)
+    rows_pad = fm.quantize_mx_rows_bound(M, len(offs)) + 32      # a tail, and NB not a multiple of 4
+    note(f"mx rows grouped K4 case={case} rows_pad={rows_pad}")
+    sc = filled_u8(fm.mx_k4_shape(C, rows_pad // 32))
+    q, sc, op = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=0, rows_pad=rows_pad, scale=sc,
+                               layout=fm.MX_LAYOUT_K4)
+    qr, sr, opr = oracle.quantize_mx_rows_grouped(x, offs, 0, rows_pad)
+    assert_bytes_equal(host(op), opr, "padded offsets")
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), e8m0_rows_to_k4(sr), "e8m0 K4")
 
 
 # ------------------------------------------------------------------- full-size, sampled
