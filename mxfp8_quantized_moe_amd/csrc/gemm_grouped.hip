@@ -1230,6 +1230,33 @@ static hipError_t launch_pipe(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// GROUPED_K with one group and fp32 scales (a dense weight gradient): when the
+// 256x256 tiles leave the last round of the persistent grid at most half full,
+// that round would cost as much as a full one.  The output rows then split into
+// whole rounds of 256-row tiles and a tail of 128-row tiles, a second launch
+// that fills the CUs again with tiles of half the work.  Returns false when the
+// shape does not call for it (nothing launched).
+template <int OUT>
+static bool launch_k_round_split(const GemmArgs& g, hipStream_t st, hipError_t* err) {
+  const int64_t G = cu_count();
+  const int64_t rt = (g.N + 255) / 256, ct = (g.K + 255) / 256, tiles = rt * ct;
+  const int64_t rem = tiles % G;
+  if (g.n_groups != 1 || tiles < 2 * G || rem == 0 || rem > G / 2) return false;
+  const int64_t r1 = tiles / G * G / ct;   // 256-row units that make whole rounds
+  if (r1 <= 0 || r1 >= rt) return false;
+  const int64_t n0 = r1 * 256;
+  constexpr int64_t ELEM = OUT == 0 ? 2 : 4;
+  GemmArgs head = g, tail = g;
+  head.N = n0;
+  tail.N = g.N - n0;
+  tail.a = static_cast<const uint8_t*>(g.a) + n0 * g.M;          // A phys [N][M]
+  tail.sa = static_cast<const float*>(g.sa) + n0;                  // fp32 [1][N]
+  tail.out = static_cast<uint8_t*>(g.out) + n0 * g.K * ELEM;       // out [1][N][K]
+  *err = launch_pipe<256, 256, 128, 2, 1, 0, OUT>(head, st);
+  if (*err == hipSuccess) *err = launch_pipe<128, 256, 128, 3, 1, 0, OUT>(tail, st);
+  return true;
+}
+
 template <int MODE, int SK, int OUT>
 static hipError_t pick_tile(const GemmArgs& g, hipStream_t st) {
   // GROUPED_M with small average groups wastes less of a 128-row tile.
@@ -1241,6 +1268,10 @@ static hipError_t pick_tile(const GemmArgs& g, hipStream_t st) {
                          (reinterpret_cast<uintptr_t>(g.sb) & 3) == 0;
     if (!aligned)
       return small ? launch_mx_bytewise<128, 256, MODE, OUT>(g, st) : launch_mx_bytewise<256, 256, MODE, OUT>(g, st);
+  }
+  if constexpr (MODE == 1 && SK == 0) {
+    hipError_t err = hipSuccess;
+    if (launch_k_round_split<OUT>(g, st, &err)) return err;
   }
   return small ? launch_pipe<128, 256, 128, 3, MODE, SK, OUT>(g, st)
                : launch_pipe<256, 256, 128, 2, MODE, SK, OUT>(g, st);

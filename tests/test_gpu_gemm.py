@@ -509,3 +509,17 @@ def test_grouped_m_mx_k4_batched_weights():
     B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
     contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
     check(got, ref, contract, tight, "GROUPED_M MX K4 batched weights")
+
+
+# ------------------------------------------------------------------ dense wgrad split into rounds
+# One group, fp32 scales: with 256 CUs, N = 33 x 256 and K = 16 x 256 make 528 tiles of 256x256,
+# two full rounds and a 16-tile remainder, so the output rows split into a 256-row-tile launch
+# (N = 8192) and a 128-row-tile tail (N = 256). The full-size Llama3-8B weight gradient takes
+# the same path (896 tiles). Checked element by element against the oracle.
+
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_grouped_k_dense_round_split(out_dtype):
+    M, N, K = 256, 33 * 256, 16 * 256
+    dy = synth.normal_bf16(71, (M, N), 1e-3)
+    x = synth.normal_bf16(72, (M, K), 1.0, 0.01, 30.0)
+    gk_case(dy, x, np.array([M], np.int32), out_dtype=out_dtype, name=f"round-split out={out_dtype}")
