@@ -149,7 +149,13 @@ int quantize_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_
  *     scale f32  [batch][cols]
  *   Requires: batch >= 1 (== 1 with offs), n_groups >= 1 with offs, rows, cols >= 0,
  *   ld_q >= rows, cols % 8 == 0, ld_q % 16 == 0, x and q_t 16-byte aligned.
- *   The call enqueues up to three kernels (amax reset, partial amax, cast).
+ *   The call enqueues up to three kernels (amax reset, partial amax, cast), or,
+ *   for a batched matrix 2 to 8 tiles of 512 rows tall, one cooperative kernel
+ *   whose tiles exchange column maxima through fixed library-owned device
+ *   arrays (4096 jobs; no allocation).  Values in those arrays carry a per-call
+ *   tag, so calls need no reset and leave nothing behind.  Calls overlapping on
+ *   one device (other streams) stay correct: a tile that cannot complete the
+ *   exchange recomputes the maxima from x itself, at the cost of a second read.
  */
 int quantize_colwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
                      const int32_t *offs, int32_t n_groups, int codec,
