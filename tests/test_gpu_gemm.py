@@ -523,3 +523,70 @@ def test_grouped_k_dense_round_split(out_dtype):
     dy = synth.normal_bf16(71, (M, N), 1e-3)
     x = synth.normal_bf16(72, (M, K), 1.0, 0.01, 30.0)
     gk_case(dy, x, np.array([M], np.int32), out_dtype=out_dtype, name=f"round-split out={out_dtype}")
+
+
+# ------------------------------------------------------------------ MoE weight gradients at full size, sampled
+# The launches the bench times for the W1 weight gradient of the MoE workloads: every expert's
+# [N, K] output, checked on sampled output rows n (all experts, all k) against the oracle.
+
+def _dequant_groups(q_t, s, lo, hi, codec=0):
+    out = np.zeros(q_t.shape)
+    for e in range(len(lo)):
+        if hi[e] > lo[e]:
+            out[:, lo[e]:hi[e]] = oracle.decode(q_t[:, lo[e]:hi[e]], codec) / s[e][:, None].astype(np.float64)
+    return out
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_grouped_k_moe_full_size_sampled(cfg):
+    w = synth.WORKLOADS[cfg]
+    dh = synth.make_dh1(w)            # [M, 2F]
+    x = synth.make_x(w)               # [M, H]
+    offs = w.offs
+    M, N = dh.shape
+    K, E = x.shape[1], w.E
+    note(f"GROUPED_K full cfg={cfg} M={M} N={N} K={K} E={E}")
+    o = i32_dev(offs)
+    qa, sa = fm.quantize_colwise(bf16_dev(dh), o, 0)
+    qb, sb = fm.quantize_colwise(bf16_dev(x), o, 0)
+    del dh, x
+    ld = qa.shape[1]
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, sa, qb, 0, sb, fm.SCALE_F32, o, E, ld, N, K)
+    rows = _rows(N, 8, 70 + cfg)
+    got = bf16_bits_to_f64(host(out[:, torch.from_numpy(rows).to(DEV)]))
+    del out
+    qa_h, sa_h = host(qa)[rows], host(sa)[:, rows]
+    qb_h, sb_h = host(qb), host(sb)
+    ref = oracle.mm_grouped_k(qa_h, sa_h, qb_h, sb_h, offs, 0, 0)
+    lo, hi = oracle.group_bounds(offs, ld)
+    A, B = _dequant_groups(qa_h, sa_h, lo, hi), _dequant_groups(qb_h, sb_h, lo, hi)
+    contract, tight = oracle.error_bounds_k(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, f"cfg{cfg} wgrad W1")
+
+
+def test_grouped_k_mx_k4_full_size_sampled():
+    w = synth.WORKLOADS[5]
+    dh = synth.make_dh1(w)            # [16384, 16384]
+    x = synth.make_x(w)               # [16384, 5120]
+    offs = w.offs
+    M, N = dh.shape
+    K, E = x.shape[1], w.E
+    Mp = fm.quantize_mx_rows_bound(M, E)
+    note(f"GROUPED_K MX K4 full cfg=5 Mp={Mp} N={N} K={K}")
+    o = i32_dev(offs)
+    qa, ya, op = fm.quantize_mx(bf16_dev(dh), axis=0, offs=o, rule=0, rows_pad=Mp, layout=fm.MX_LAYOUT_K4)
+    qb, yb, _ = fm.quantize_mx(bf16_dev(x), axis=0, offs=o, rule=0, rows_pad=Mp, layout=fm.MX_LAYOUT_K4)
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, ya, qb, 0, yb, fm.SCALE_E8M0_K4, op, E, Mp, N, K)
+    rows = _rows(N, 6, 77)
+    got = bf16_bits_to_f64(host(out[:, torch.from_numpy(rows).to(DEV)]))
+    del out
+    # the row-major scales of the same tensors for the oracle (the K4 bytes are checked against them elsewhere)
+    _, xa, _ = fm.quantize_mx(bf16_dev(dh), axis=0, offs=o, rule=0, rows_pad=Mp)
+    _, xb, _ = fm.quantize_mx(bf16_dev(x), axis=0, offs=o, rule=0, rows_pad=Mp)
+    del dh, x
+    qa_h, xa_h, qb_h, xb_h, op_h = host(qa)[rows], host(xa)[rows], host(qb), host(xb), host(op)
+    ref = oracle.mm_grouped_k_mx(qa_h, xa_h, qb_h, xb_h, op_h)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb_h), 32, axis=-1)
+    contract, tight = oracle.error_bounds_k(A, B, op_h, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, "cfg5 MX wgrad W1 (K4)")
