@@ -149,13 +149,16 @@ int quantize_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_
  *     scale f32  [batch][cols]
  *   Requires: batch >= 1 (== 1 with offs), n_groups >= 1 with offs, rows, cols >= 0,
  *   ld_q >= rows, cols % 8 == 0, ld_q % 16 == 0, x and q_t 16-byte aligned.
- *   The call enqueues up to three kernels (amax reset, partial amax, cast), or,
- *   for a batched matrix 2 to 8 tiles of 512 rows tall, one cooperative kernel
- *   whose tiles exchange column maxima through fixed library-owned device
- *   arrays (4096 jobs; no allocation).  Values in those arrays carry a per-call
- *   tag, so calls need no reset and leave nothing behind.  Calls overlapping on
- *   one device (other streams) stay correct: a tile that cannot complete the
- *   exchange recomputes the maxima from x itself, at the cost of a second read.
+ *   Normally the call enqueues one kernel: every 512-row x 64-column chunk is
+ *   read once into registers, and the chunks of a group exchange their column
+ *   maxima through a fixed library-owned device array (32768 chunk slots, no
+ *   allocation) before casting from registers.  Values in that array carry a
+ *   per-call tag, so calls need no reset and leave nothing behind.  Calls that
+ *   overlap on one device (other streams) stay correct: a chunk that cannot
+ *   complete the exchange recomputes the maxima from x itself, at the cost of
+ *   a second read.  A group taller than 128 chunks, or a call with more than
+ *   32768 chunks, instead takes three kernels (amax reset, partial amax, cast)
+ *   and reads x twice.
  */
 int quantize_colwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
                      const int32_t *offs, int32_t n_groups, int codec,

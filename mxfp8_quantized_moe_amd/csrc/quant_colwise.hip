@@ -11,21 +11,19 @@
 // Chunks of group e are anchored at floor16(lo(e)) so every 16-row output
 // segment is 16-byte aligned; the (rare) segments shared with a neighbouring
 // group are stored byte by byte.
-//   * A group that fits one chunk is done in one pass by the cast kernel: the
-//     chunk is loaded once into registers, reduced, scaled, cast, transposed
-//     through LDS and stored (2 B read + 1 B written per element).
-//   * A taller group first gets its per-column maxima from the partial-max
-//     kernel: every chunk reduces its rows and merges them into the scale
-//     buffer with a relaxed device-scope atomic max on the fp32 bit pattern,
-//     tagged with the sign bit (order independent, exact).  The cast kernel
-//     then turns the tag into the scale; a reader sees either the tagged max or
-//     the final scale, and both give the same scale.  The cast kernel visits
-//     units in reverse order so its second read starts with the data the
-//     partial-max kernel touched last (still in the last-level cache).
-//   * A weight matrix of the batched form that is 2 to 8 chunks tall is done
-//     in one pass by a cooperative kernel (below): its chunks run at the same
-//     time, exchange column maxima through device-scope atomics and cast from
-//     registers.
+//   * Normally one single-pass kernel does everything (below): every chunk is
+//     loaded once into registers and reduced; a group that spans several
+//     chunks exchanges its column maxima between them through tagged slots in
+//     device memory; then each chunk casts from registers, transposes through
+//     LDS and stores (2 B read + 1 B written per element).
+//   * Groups taller than 128 chunks, or calls with more chunks than there are
+//     slots, take two passes: a partial-max kernel where every chunk merges its
+//     column maxima into the scale buffer with a relaxed device-scope atomic
+//     max on the fp32 bit pattern, tagged with the sign bit (order
+//     independent, exact), then a cast kernel that turns the tag into the
+//     scale (a reader sees either the tagged max or the final scale, and both
+//     give the same scale).  The cast kernel visits units in reverse order so
+//     its second read starts with the data the partial-max kernel touched last.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "tile_lds.hpp"
@@ -215,34 +213,25 @@ __global__ __launch_bounds__(256) void colwise_kernel(const uint16_t* __restrict
 
 
 // ---------------------------------------------------------------- single pass
-// Cooperative single pass for the batched (3D, weight) form when a matrix is a
-// few chunks tall.  A persistent grid (at most as many workgroups as fit on the
-// device at once) gives every column strip to one XCD (workgroups are
-// dispatched round-robin over the 8 XCDs) and walks that XCD's items
-// strip-major, so the chunks of one (strip, matrix) job are consecutive items
-// running at the same time.  Each chunk keeps its data in registers, merges its column maxima into
-// the job's slots of a library-owned array (atomic max), waits for those to
-// complete, and counts its arrival; once all chunks of the job have arrived it
-// reads the job's maxima and casts from registers: HBM sees 2 bytes read + 1
-// byte written per element.  The maxima and counters are device-scope atomics
-// and are polled with device-scope loads (one memory round trip per poll): the
-// wait is short when a job's chunks start together, which holds for the few
-// equal-height chunks of a weight matrix; taller or ragged (grouped) columns
-// spread their chunks' arrivals and keep the two-pass path, where measured
-// faster.
-//   Slots and counters hold the call's generation in their high 32 bits
-// (unique per call): values left by earlier calls lose every max and restart
-// the count, so no reset is needed and calls rely on no shared state.  The
-// wait is bounded: a chunk whose peers do not all arrive in time (not resident
-// together, or not sharing its L2, or another call's job on the same slot)
-// computes the job's column maxima itself by re-reading the group's rows,
-// which gives the same scale; every wave thus always finishes, and the
-// caller's buffers only ever receive final values.
-constexpr int kCoopJobs = 4096;             // job slots; more jobs take the two-pass path
-constexpr int kCoopPolls = 4096;            // sleeps of ~128 cycles before the fallback
-constexpr int kCoopMaxChunks = 8;           // taller matrices take the two-pass path
-__device__ unsigned long long g_cw_arrivals[kCoopJobs];
-__device__ unsigned long long g_cw_max[kCoopJobs][kTileCols];
+// One workgroup per chunk, numbered so that the chunks of one (group, strip)
+// job are consecutive workgroups, which the hardware dispatches together.  A
+// chunk keeps its 512 x 64 values in registers, reduces its column maxima and,
+// when its group spans several chunks, publishes them to its own slot of a
+// library-owned array (one 64-bit word per column: the call's generation in
+// the high half, the bf16 |x| max in the low bits).  It then reads the slots of
+// every chunk of its job until all carry this call's generation, takes the
+// maximum, and casts from registers: HBM sees 2 bytes read + 1 byte written
+// per element.  There are no read-modify-write atomics and no counters: every
+// slot is written once per call and validated by its tag, so calls need no
+// reset and rely on no state left by earlier calls.
+//   The wait is bounded.  A chunk whose peers do not all publish in time (not
+// resident together, or another call on the same slots) re-reads its group's
+// rows to compute the same maxima itself, so every wave finishes and the
+// result never depends on timing.
+constexpr int kSlotItems = 32768;           // chunk slots (16 MiB); more chunks take the two-pass path
+constexpr int kMaxChunks = 128;             // taller groups take the two-pass path
+constexpr int kPolls = 4096;                // sleeps of ~512 cycles (plus a load) before the fallback
+__device__ unsigned long long g_cw_part[kSlotItems][kTileCols];
 
 // Maxima of 64 columns over rows [lo, hi) of group rows in_base + r, read
 // again from global memory (the fallback of a wait that ran out).
@@ -263,128 +252,120 @@ __device__ __forceinline__ void cw_column_max(const uint16_t* __restrict__ x, in
   cw_reduce_cols(m, red, out);
 }
 
+// Wave 0 (64 lanes, one per column): the maximum over the published slots of
+// the nch chunks starting at item0, 8 slots per round trip.  Returns whether
+// all arrived within the poll budget (then out[t] holds the maximum).
+__device__ __forceinline__ bool cw_gather(const unsigned long long* __restrict__ part, int item0, int nch,
+                                          uint32_t gen, uint32_t* out) {
+  const int t = threadIdx.x;
+  uint32_t mx = 0;
+  int k = 0;
+  for (int polls = 0; k < nch && polls < kPolls;) {
+    unsigned long long b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      b[i] = k + i < nch ? __hip_atomic_load(part + (int64_t)(item0 + k + i) * kTileCols + t, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : (unsigned long long)gen << 32;
+    int have = 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) have &= (uint32_t)(b[i] >> 32) == gen;
+    if (__all(have)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = max(mx, (uint32_t)b[i] & 0xFFFFu);
+      k += 8;
+    } else {
+      ++polls;
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  out[t] = mx;
+  return k >= nch;
+}
+
 template <int CODEC, bool GROUPED>
-__global__ __launch_bounds__(256) void colwise_coop_kernel(const uint16_t* __restrict__ x, int64_t batch,
-                                                           int rows, int cols, const int32_t* __restrict__ offs,
-                                                           int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
-                                                           float* __restrict__ scale, int n_strips, int units,
-                                                           uint32_t gen) {
+__global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __restrict__ x, int64_t batch,
+                                                             int rows, int cols, const int32_t* __restrict__ offs,
+                                                             int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
+                                                             float* __restrict__ scale, int units, uint32_t gen) {
   __shared__ uint32_t red[4 * 8 * 4];
   __shared__ uint32_t s_amax[64];
   __shared__ float s_scale[64];
-  __shared__ int s_done;
+  __shared__ int s_ok;
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
   const int t = threadIdx.x, cc = t & 7, rs = t >> 3;
-  // XCD x = blockIdx % 8 owns strips x, x + 8, ...; its workgroups take its
-  // items i = strip-local index * units + unit with a stride of their count.
-  const int xcd = blockIdx.x & 7, nloc = gridDim.x >> 3;
-  const int my_strips = n_strips > xcd ? (n_strips - 1 - xcd) / 8 + 1 : 0;
-  const int items = my_strips * units;
-  const unsigned long long tagged = (unsigned long long)gen << 32;
-  for (int item = blockIdx.x >> 3; item < items; item += nloc) {
-    const int strip = xcd + 8 * (item / units), u = item % units;
-    const CwGeom g = cw_geom<GROUPED>(u, batch, rows, cols, offs, n_groups, q_t, ld_q, scale);
-    if (!g.ok) continue;   // uniform
-    const int c0 = strip * kTileCols;
-    if (g.ohi <= g.olo) {   // the scale of an empty group (no rows, no data)
-      if (t < 64 && c0 + t < cols) g.s[c0 + t] = scale_from_amax(0.0f, CODEC);
-      continue;
-    }
-    const int nch = cw_chunks(g.olo, g.ohi);
-    const int A = (g.olo & ~15) + g.j * kTileRows;          // output row of tile row 0
-    const int r_begin = max(A, g.olo), r_end = min(A + kTileRows, g.ohi);
-    const int col = c0 + cc * 8;
-    const bool col_ok = col < cols;
+  const int strip = blockIdx.x / units, u = blockIdx.x % units;
+  const CwGeom g = cw_geom<GROUPED>(u, batch, rows, cols, offs, n_groups, q_t, ld_q, scale);
+  if (!g.ok) return;
+  const int c0 = strip * kTileCols;
+  if (g.ohi <= g.olo) {   // the scale of an empty group (no rows, no data)
+    if (t < 64 && c0 + t < cols) g.s[c0 + t] = scale_from_amax(0.0f, CODEC);
+    return;
+  }
+  const int nch = cw_chunks(g.olo, g.ohi);
+  const int A = (g.olo & ~15) + g.j * kTileRows;          // output row of tile row 0
+  const int r_begin = max(A, g.olo), r_end = min(A + kTileRows, g.ohi);
+  const int col = c0 + cc * 8;
+  const bool col_ok = col < cols;
 
-    u32x4 v[kCwIters][4];
-    uint32_t m[4] = {0, 0, 0, 0};
+  u32x4 v[kCwIters][4];
+  uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < kCwIters; ++i) {
+  for (int i = 0; i < kCwIters; ++i) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = A + 128 * i + 4 * rs + k;
-        const bool ok = col_ok && r >= r_begin && r < r_end;
-        v[i][k] = ok ? *reinterpret_cast<const u32x4*>(x + (g.in_base + r) * cols + col) : u32x4{0, 0, 0, 0};
-        m[0] = pk_absmax_bf16(m[0], v[i][k].x);
-        m[1] = pk_absmax_bf16(m[1], v[i][k].y);
-        m[2] = pk_absmax_bf16(m[2], v[i][k].z);
-        m[3] = pk_absmax_bf16(m[3], v[i][k].w);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int r = A + 128 * i + 4 * rs + k;
+      const bool ok = col_ok && r >= r_begin && r < r_end;
+      v[i][k] = ok ? *reinterpret_cast<const u32x4*>(x + (g.in_base + r) * cols + col) : u32x4{0, 0, 0, 0};
+      m[0] = pk_absmax_bf16(m[0], v[i][k].x);
+      m[1] = pk_absmax_bf16(m[1], v[i][k].y);
+      m[2] = pk_absmax_bf16(m[2], v[i][k].z);
+      m[3] = pk_absmax_bf16(m[3], v[i][k].w);
     }
-    cw_reduce_cols(m, red, s_amax);
-    if (nch == 1) {
-      if (t < 64) s_scale[t] = scale_from_amax(__uint_as_float(s_amax[t] << 16), CODEC);
-    } else {
-      const int job = g.e * n_strips + strip;   // group (or batch) major, < kCoopJobs
-      unsigned long long* jmax = g_cw_max[job];
-      if (t < 64) __hip_atomic_fetch_max(jmax + t, tagged | s_amax[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);   // the maxima are performed before the arrival below
-      __syncthreads();
-      if (t == 0) {
-        unsigned long long* ctr = &g_cw_arrivals[job];
-        unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (;;) {
-          const unsigned long long want = (old >> 32) == gen ? old + 1 : tagged | 1ull;
-          if (__hip_atomic_compare_exchange_strong(ctr, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT))
-            break;
-        }
-        int done = 0;
-        for (int poll = 0; poll < kCoopPolls; ++poll) {
-          const unsigned long long now = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((now >> 32) == gen && (int)(now & 0xFFFFFFFFull) >= nch) {
-            done = 1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        s_done = done;
-      }
-      __syncthreads();
-      int ok = s_done;
-      if (ok && t < 64) {
-        const unsigned long long b = __hip_atomic_load(jmax + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((b >> 32) == gen) s_amax[t] = (uint32_t)b & 0xFFFFu;
-        else s_done = 0;   // not this call's value: take the fallback
-      }
-      __syncthreads();
-      ok = s_done;
-      if (!ok) cw_column_max(x, g.in_base, g.olo, g.ohi, cols, c0, red, s_amax);
-      if (t < 64) s_scale[t] = scale_from_amax(__uint_as_float(s_amax[t] << 16), CODEC);
+  }
+  cw_reduce_cols(m, red, s_amax);
+  if (nch > 1) {
+    unsigned long long* part = &g_cw_part[0][0];
+    if (t < 64) {
+      __hip_atomic_store(part + (int64_t)blockIdx.x * kTileCols + t, ((unsigned long long)gen << 32) | s_amax[t],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool ok = cw_gather(part, (int)blockIdx.x - g.j, nch, gen, s_amax);
+      if (t == 0) s_ok = ok;
     }
     __syncthreads();
-    if (g.j == 0 && t < 64 && c0 + t < cols) g.s[c0 + t] = s_scale[t];
+    if (!s_ok) cw_column_max(x, g.in_base, g.olo, g.ohi, cols, c0, red, s_amax);
+  }
+  if (t < 64) s_scale[t] = scale_from_amax(__uint_as_float(s_amax[t] << 16), CODEC);
+  __syncthreads();
+  if (g.j == 0 && t < 64 && c0 + t < cols) g.s[c0 + t] = s_scale[t];
 
-    // cast: per column, the 4 rows of a slot become one little-endian word
-    float sc[8];
+  // cast: per column, the 4 rows of a slot become one little-endian word
+  float sc[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) sc[k] = s_scale[cc * 8 + k];
+  for (int k = 0; k < 8; ++k) sc[k] = s_scale[cc * 8 + k];
 #pragma unroll
-    for (int i = 0; i < kCwIters; ++i) {
+  for (int i = 0; i < kCwIters; ++i) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t w = quant4<CODEC>(col_of(v[i][0], k), col_of(v[i][1], k), col_of(v[i][2], k),
-                                         col_of(v[i][3], k), sc[k]);
-        tile_put4(tile, cc * 8 + k, 128 * i + 4 * rs, w);
-      }
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t w = quant4<CODEC>(col_of(v[i][0], k), col_of(v[i][1], k), col_of(v[i][2], k),
+                                       col_of(v[i][3], k), sc[k]);
+      tile_put4(tile, cc * 8 + k, 128 * i + 4 * rs, w);
     }
-    __syncthreads();
-    // transposed store: each pass writes 8 columns x 32 segments of 16 rows
+  }
+  __syncthreads();
+  // transposed store: each pass writes 8 columns x 32 segments of 16 rows
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-      const int ci = pp * 8 + (t >> 5), sg = t & 31;
-      const int c = c0 + ci, R0 = A + 16 * sg;
-      if (c < cols && R0 < r_end && R0 + 16 > r_begin) {
-        const u32x4 d = tile_get16(tile, ci, 16 * sg);
-        store_segment(g.q + (int64_t)c * ld_q + R0, R0, r_begin, r_end, d);
-      }
+  for (int pp = 0; pp < 8; ++pp) {
+    const int ci = pp * 8 + (t >> 5), sg = t & 31;
+    const int c = c0 + ci, R0 = A + 16 * sg;
+    if (c < cols && R0 < r_end && R0 + 16 > r_begin) {
+      const u32x4 d = tile_get16(tile, ci, 16 * sg);
+      store_segment(g.q + (int64_t)c * ld_q + R0, R0, r_begin, r_end, d);
     }
-    __syncthreads();   // the tile and s_scale are reused by the next item
   }
 }
 
-// One generation per call of the single-pass kernel, shared by every
-// instantiation (0 never names a call).
+// One generation per call of the single-pass kernel (0 never names a call).
 static std::atomic<uint32_t> g_generation{0};
 static uint32_t next_generation() {
   uint32_t g = g_generation.fetch_add(1) + 1;
@@ -406,29 +387,13 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
   if (n_scale == 0) return hipSuccess;
   const int n_strips = (int)((cols + kTileCols - 1) / kTileCols);
   const int64_t units = colwise_units_bound(batch, rows, offs, n_groups);
-  const int64_t jobs = (GROUPED ? n_groups : batch) * (int64_t)n_strips;
   const int64_t items = units * n_strips;
-  const int64_t chunks = rows > 0 ? (rows + kTileRows - 1) / kTileRows : 1;
-  if constexpr (!GROUPED) if (chunks <= kCoopMaxChunks && jobs <= kCoopJobs && items < (1LL << 31)) {
-    // Single pass: a persistent grid of at most the co-resident workgroups.
-    static int per_cu[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (per_cu[dev] == 0) {
-      int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, colwise_coop_kernel<CODEC, GROUPED>, 256, 0) !=
-              hipSuccess || n <= 0)
-        n = 1;
-      per_cu[dev] = n;
-    }
-    int n_cu = 0;
-    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-      n_cu = 1;
-    const uint32_t gen = next_generation();
-    // a multiple of 8 (the XCD count) workgroups, at most what is co-resident
-    const int64_t grid = std::max<int64_t>(8, std::min<int64_t>((items + 7) / 8 * 8, (int64_t)per_cu[dev] * n_cu / 8 * 8));
-    hipLaunchKernelGGL((colwise_coop_kernel<CODEC, GROUPED>), dim3((unsigned)grid), dim3(256), 0, st, x, batch,
-                       (int)rows, (int)cols, offs, n_groups, q_t, ld_q, scale, n_strips, (int)units, gen);
+  // most chunks one group can span: a grouped group may start 15 rows past a 16-row anchor
+  const int64_t nch_bound = ((GROUPED ? rows + 15 : rows) + kTileRows - 1) / kTileRows;
+  if (nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
+    hipLaunchKernelGGL((colwise_single_kernel<CODEC, GROUPED>), dim3((unsigned)items), dim3(256), 0, st, x,
+                       batch, (int)rows, (int)cols, offs, n_groups, q_t, ld_q, scale, (int)units,
+                       next_generation());
     return hipGetLastError();
   }
   hipLaunchKernelGGL(colwise_reset_kernel, dim3((unsigned)((n_scale + 255) / 256)), dim3(256), 0, st,

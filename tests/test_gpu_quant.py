@@ -89,6 +89,10 @@ GROUP_CASES = {
     "tall": (2100, 64, np.array([2100], np.int32)),
     "malformed": (700, 72, np.array([100, 50, 650, 900, -3], np.int32)),
     "tiny": (37, 8, np.array([0, 5, 5, 36], np.int32)),
+    # more than 128 chunks of 512 rows in one group: the two-pass kernels
+    "very_tall": (70000, 64, np.array([70000], np.int32)),
+    # more chunk slots than the single pass holds (2000 mostly empty groups): the two-pass kernels
+    "many_groups": (1024, 1024, synth.offsets_from_counts(synth.random_counts(6, 1024, 2000, 0.5))),
 }
 
 
@@ -110,7 +114,7 @@ def test_colwise_grouped_parity(codec, case):
 
 @pytest.mark.parametrize("codec", CODECS)
 @pytest.mark.parametrize("shape", [(3, 700, 72), (4, 100, 64), (2, 1, 8), (1, 1030, 136),
-                                   (2, 4096, 72), (2, 4097, 72), (5, 1536, 200)])
+                                   (2, 4096, 72), (2, 4097, 72), (5, 1536, 200), (1, 65600, 16)])
 def test_colwise_batched_parity(codec, shape):
     x = special_input(3000 + sum(shape), shape)
     B, R, C = shape
