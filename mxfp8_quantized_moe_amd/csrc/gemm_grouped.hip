@@ -63,6 +63,9 @@ struct KParams {
   int E, M, N, K;
   int row_units;   // GROUPED_M: bound on row tiles over all groups; GROUPED_K: E * ceil(N / BM)
   int col_tiles;   // GROUPED_M: ceil(N / BN); GROUPED_K: ceil(K / BN)
+  // ceil(2^32 / (kBandRows * col_tiles)): band = umulhi(L, band_magic) for
+  // every logical tile L (exact while L * kBandRows * col_tiles < 2^32).
+  uint32_t band_magic;
 };
 
 // Each XCD gets a contiguous range of logical tile ids (dispatch is round-robin).
@@ -84,6 +87,36 @@ __device__ __forceinline__ u32x4 mask_chunk(u32x4 v, int pos, int lo, int hi) {
     w[i] &= keep_hi & ~drop_lo;
   }
   return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Zero the bytes outside the contraction range [lo, hi) of one stage in LDS:
+// SROWS tile rows of CH 16-byte chunks at contraction positions base + 16 c
+// (chunk c of row r at R::off(r, c)).  Whether a chunk needs work depends only
+// on its column, a workgroup-uniform test: columns wholly outside the range
+// are written with zeros (no read), and only the chunk columns holding an end
+// of the range (at most two) are read, masked and written back.  Each thread
+// handles whole rows; the loops stay rolled to keep register use low.
+template <class R, int SROWS, int CH>
+__device__ __forceinline__ void zero_outside(uint8_t* st, int base, int lo, int hi) {
+  const int end = base + 16 * CH;
+  const int ca = (lo > base && lo < end && (lo & 15) != 0) ? (lo - base) >> 4 : -1;
+  const int cb = (hi > base && hi < end && (hi & 15) != 0) ? (hi - base) >> 4 : -1;
+#pragma unroll 1
+  for (int r = threadIdx.x; r < SROWS; r += 256) {
+#pragma unroll 1
+    for (int c = 0; c < CH; ++c) {
+      const int pos = base + 16 * c;
+      if (pos + 16 <= lo || pos >= hi) *reinterpret_cast<u32x4*>(st + R::off(r, c)) = u32x4{0, 0, 0, 0};
+    }
+    if (ca >= 0) {
+      u32x4* q = reinterpret_cast<u32x4*>(st + R::off(r, ca));
+      *q = mask_chunk(*q, base + 16 * ca, lo, hi);
+    }
+    if (cb >= 0 && cb != ca) {
+      u32x4* q = reinterpret_cast<u32x4*>(st + R::off(r, cb));
+      *q = mask_chunk(*q, base + 16 * cb, lo, hi);
+    }
+  }
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -333,13 +366,7 @@ void gemm_fp8_kernel(KParams p) {
   auto fix_boundary = [&](uint8_t* st, int kt) {
     const int base = c_start + kt * kBK;
     if (base >= c_lo && base + kBK <= c_hi) return;    // uniform
-    for (int idx = t; idx < SROWS * CH; idx += 256) {
-      const int r = idx / CH, c = idx % CH, pos = base + 16 * c;
-      if (pos < c_lo || pos + 16 > c_hi) {
-        u32x4* q = reinterpret_cast<u32x4*>(st + R::off(r, c));
-        *q = mask_chunk(*q, pos, c_lo, c_hi);
-      }
-    }
+    zero_outside<R, SROWS, CH>(st, base, c_lo, c_hi);
     wait_lgkmcnt0();
     raw_barrier();
   };
@@ -633,20 +660,31 @@ void gemm_fp8_pipe(KParams p) {
     int pv, qv;             // valid rows of P and Q in the tile
     int c_lo, c_hi;         // contraction range
     int c_start, nk;        // first stage position (BK-aligned) and stage count
+    const float* psf;       // fp32 scales of the tile's rows and columns
+    const float* qsf;
   };
   __shared__ __attribute__((aligned(16))) float s_inv[2][SK == 0 ? BM + BN : 4];
   constexpr int SPT = (BM + BN + 255) / 256;   // fp32 scales per thread
-  // Fill `tl` for logical tile L and start loading its fp32 scales into `sv`
-  // (scale_commit turns them into reciprocals in LDS).  Every thread calls it
-  // (without a group table it synchronizes the workgroup).
-  auto setup = [&](int L, Tile& tl, float (&sv)[SPT]) {
+  // Fill `tl` for logical tile L.  Every thread calls it (without a group
+  // table it synchronizes the workgroup).
+  auto setup = [&](int L, Tile& tl) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int band = L / (kBandRows * p.col_tiles);
+    // band, row unit and column tile of L without a division by a runtime
+    // value in the common case (a loop-invariant reciprocal would occupy a
+    // register across the whole tile loop)
+    static_assert((kBandRows & (kBandRows - 1)) == 0, "band rows: a power of two");
+    const int band = (int)__umulhi((uint32_t)L, p.band_magic);
     const int first = band * kBandRows;
     const int gsz = min(row_units - first, kBandRows);
-    const int inband = L % (kBandRows * p.col_tiles);
-    const int ru = first + inband % gsz;
-    const int ct = inband / gsz;
+    const int inband = L - band * (kBandRows * p.col_tiles);
+    int ru, ct;
+    if (gsz == kBandRows) {
+      ru = first + (inband & (kBandRows - 1));
+      ct = inband / kBandRows;
+    } else {
+      ru = first + inband % gsz;
+      ct = inband / gsz;
+    }
     const float* psf = nullptr;   // fp32 scales of the tile's rows / columns
     const float* qsf = nullptr;
     if constexpr (MODE == 0) {
@@ -726,23 +764,42 @@ void gemm_fp8_pipe(KParams p) {
     tl.c_hi = __builtin_amdgcn_readfirstlane(tl.c_hi);
     tl.c_start = __builtin_amdgcn_readfirstlane(tl.c_start);
     tl.nk = __builtin_amdgcn_readfirstlane(tl.nk);
-    if constexpr (SK == 0) {
-      const int pv1 = max(tl.pv, 1) - 1, qv1 = max(tl.qv, 1) - 1;
-#pragma unroll
-      for (int s = 0; s < SPT; ++s) {
-        const int idx = min(t + 256 * s, BM + BN - 1);
-        sv[s] = idx < BM ? psf[min(idx, pv1)] : qsf[min(idx - BM, qv1)];
-      }
-    }
+    tl.psf = psf;
+    tl.qsf = qsf;
   };
 
-  // Reciprocals of the scales loaded by setup, into `sinv`.
-  auto scale_commit = [&](const float (&sv)[SPT], float* sinv) {
+  // Start loading a tile's fp32 scales straight into LDS (s_raw) with
+  // direct-to-LDS loads, so no register holds them across the k loop (a
+  // spilled one would force a full wait, draining the previous tile's stores,
+  // right after its load).  Wave w loads entries 64 (w + 4 i) + lane, exactly
+  // the entries its own threads turn into reciprocals (scale_commit, after a
+  // full wait), so no barrier is needed in between.
+  __shared__ __attribute__((aligned(16))) float s_raw[SK == 0 ? BM + BN : 4];
+  auto load_scales = [&](const Tile& tl) {
+    if constexpr (SK == 0) {
+      int t_opq = threadIdx.x;
+      asm volatile("" : "+v"(t_opq));
+      const int lane = t_opq & 63, wave = __builtin_amdgcn_readfirstlane(t_opq >> 6);
+      const int pv1 = max(tl.pv, 1) - 1, qv1 = max(tl.qv, 1) - 1;
+      constexpr int NB = (BM + BN) / 64;   // 64-entry blocks
+      static_for<(NB + 3) / 4>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int blk = wave + 4 * i;
+        if (blk < NB) {
+          const int idx = 64 * blk + lane;
+          const float* src = idx < BM ? tl.psf + min(idx, pv1) : tl.qsf + min(idx - BM, qv1);
+          dma_4(reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint8_t*>(s_raw) + 256 * blk);
+        }
+      });
+    }
+  };
+  // Reciprocals of the scales in s_raw, into `sinv`.
+  auto scale_commit = [&](float* sinv) {
     if constexpr (SK == 0) {
 #pragma unroll
       for (int s = 0; s < SPT; ++s) {
         const int idx = threadIdx.x + 256 * s;
-        if (idx < BM + BN) sinv[idx] = __frcp_rn(sv[s]);
+        if (idx < BM + BN) sinv[idx] = __frcp_rn(s_raw[idx]);
       }
     }
   };
@@ -818,10 +875,11 @@ void gemm_fp8_pipe(KParams p) {
   };
 
   Tile cur, nxt;
-  float sv[SPT];
   if (tile_of(0) >= ntiles) return;
-  setup(tile_of(0), cur, sv);
-  scale_commit(sv, s_inv[0]);
+  setup(tile_of(0), cur);
+  load_scales(cur);
+  wait_vmcnt<0>();
+  scale_commit(s_inv[0]);
   // Stage of step s in the processing order nk-1, 0, 1, ..., nk-2 (see below).
   auto first_stage = [](const Tile& tl, int s) { return s == 0 ? tl.nk - 1 : s - 1; };
   if (cur.nk > 0) {
@@ -855,13 +913,7 @@ void gemm_fp8_pipe(KParams p) {
   auto fix_boundary = [&](uint8_t* st, int kt) {
     const int base = c_start + kt * BK;
     if (kt >= nk || (base >= c_lo && base + BK <= c_hi)) return;    // uniform
-    for (int idx = t; idx < SROWS * CH; idx += 256) {
-      const int r = idx / CH, c = idx % CH, pos = base + 16 * c;
-      if (pos < c_lo || pos + 16 > c_hi) {
-        u32x4* q = reinterpret_cast<u32x4*>(st + R::off(r, c));
-        *q = mask_chunk(*q, pos, c_lo, c_hi);
-      }
-    }
+    zero_outside<R, SROWS, CH>(st, base, c_lo, c_hi);
     wait_lgkmcnt0();
     raw_barrier();
   };
@@ -978,7 +1030,10 @@ void gemm_fp8_pipe(KParams p) {
   // The next tile's description now, and its scale loads (issued before this
   // tile's later stages, so they land first and never delay a stage wait).
   const bool has_next = tile_of(it + 1) < ntiles;
-  if (has_next) setup(tile_of(it + 1), nxt, sv);
+  if (has_next) {
+    setup(tile_of(it + 1), nxt);
+    load_scales(nxt);
+  }
   if (it > 0 && nk > 0) {
     issue_stage(cur, I1{}, first_stage(cur, min(1, nk - 1)), Checked{});
     if constexpr (SLOTS > 2)
@@ -1011,7 +1066,7 @@ void gemm_fp8_pipe(KParams p) {
 
   // ---- the next tile: its scale reciprocals, then (once no wave reads the
   // ring any more) its stage 0, which lands during the epilogue.
-  if (has_next) scale_commit(sv, s_inv[(it + 1) & 1]);
+  if (has_next) scale_commit(s_inv[(it + 1) & 1]);
   wait_lgkmcnt0();
   raw_barrier();
   if (has_next && nxt.nk > 0) issue_stage(nxt, I0{}, first_stage(nxt, 0), Checked{});
@@ -1191,6 +1246,13 @@ static void fill_params(KParams& p, const GemmArgs& g, int BM, int BN) {
     p.row_units = (int)(g.n_groups * ((g.N + BM - 1) / BM));
     p.col_tiles = (int)((g.K + BN - 1) / BN);
   }
+  const uint64_t band_tiles = (uint64_t)kBandRows * (uint64_t)std::max(p.col_tiles, 1);
+  p.band_magic = (uint32_t)(((1ull << 32) + band_tiles - 1) / band_tiles);
+}
+
+// The band magic is exact for every tile index below 2^32 / (kBandRows * col_tiles).
+static bool band_magic_exact(const KParams& p) {
+  return (uint64_t)p.row_units * (uint64_t)p.col_tiles * (uint64_t)kBandRows * (uint64_t)p.col_tiles < (1ull << 32);
 }
 
 // 64-byte-stage kernel with byte-wise e8m0 loads: MX operands whose scale rows
@@ -1224,6 +1286,7 @@ static hipError_t launch_pipe(const GemmArgs& g, hipStream_t st) {
   fill_params(p, g, BM, BN);
   const int64_t total = (int64_t)p.row_units * p.col_tiles;   // GROUPED_M: a bound
   if (total == 0) return hipSuccess;
+  if (!band_magic_exact(p)) return hipErrorInvalidValue;   // far beyond any expert layer
   // One workgroup fits per CU (LDS); a persistent grid of at most one per CU.
   const int64_t grid = std::min<int64_t>(total, cu_count());
   hipLaunchKernelGGL((gemm_fp8_pipe<BM, BN, BK, SLOTS, MODE, SK, OUT>), dim3((unsigned)grid), dim3(256), 0, st, p);
