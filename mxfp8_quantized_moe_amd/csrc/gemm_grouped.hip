@@ -40,6 +40,7 @@
 //    gets a contiguous range of tiles, ordered in bands of 8 row tiles, so the
 //    tiles running together on one XCD share operand rows in its L2.
 #include "device_common.hpp"
+#include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace fp8moe {
@@ -137,45 +138,6 @@ struct Ring {
   // of 16 consecutive rows hit 16 distinct 16-byte bank groups.
   static __device__ __forceinline__ int off(int r, int c) { return r * BK + ((c ^ ((r >> SH) & (CH - 1))) << 4); }
 };
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4],
-// lgkmcnt [11:8]).  The builtin is visible to the compiler's own wait
-// insertion, which then knows which direct-to-LDS loads have landed.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
-
-// Direct global->LDS loads (a wave fills 64 consecutive 16-byte or 1-byte LDS
-// slots, one per lane, from per-lane global addresses).  Wrapped in plain
-// device functions: clang drops a kernel's host launch stub when this builtin
-// is called straight from a generic lambda in the kernel body.
-__device__ __forceinline__ void dma_16(const uint8_t* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-// A 1-byte DMA still gives each lane a dword of LDS: lane l's byte lands at dst + 4 l.
-__device__ __forceinline__ void dma_1(const uint8_t* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 1, 0, 0);
-}
-
-// 16-byte store of output the kernel never reads back: streamed (non-temporal),
-// so finished tiles do not displace operand lines in L2 and leave less dirty
-// data behind for the kernels that follow.
-__device__ __forceinline__ void store_stream16(uint8_t* dst, u32x4 v) {
-  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
-}
-
-// Workgroup barrier without a memory fence (a fence would wait for every
-// in-flight global load, draining the pipeline); the empty asm statements keep
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int BM, int BN, int BK, int MODE, int SK, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -517,20 +479,6 @@ __device__ __forceinline__ void dma_4(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
-// Place NM MFMAs of the current scheduling region with ND LDS reads and NV
-// global loads spread evenly between them.
-template <int NM, int ND, int NV, int I = 0>
-__device__ __forceinline__ void interleave() {
-  if constexpr (I < NM) {
-    constexpr int d = ((I + 1) * ND) / NM - (I * ND) / NM;
-    constexpr int v = ((I + 1) * NV) / NM - (I * NV) / NM;
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
-    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
-    interleave<NM, ND, NV, I + 1>();
-  }
-}
-
 // A wave-uniform value moved to scalar registers.
 __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -540,16 +488,6 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
 template <typename T>
 __device__ __forceinline__ T* uniform_ptr(T* p) {
   return reinterpret_cast<T*>(uniform_i64(reinterpret_cast<int64_t>(p)));
-}
-
-// Calls f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices
-// for builtins that take immediates).
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
 }
 
 template <int BM, int BN, int BK, int SLOTS, int MODE, int SK, int OUT>

@@ -175,6 +175,76 @@ def test_grouped_k_bf16_plus_gw():
     check(got, ref, contract, tight, "GROUPED_K bf16")
 
 
+def gw_case(dy, x, offs, out_dtype=0, name=""):
+    """bf16 "+GW" GROUPED_K on token-major operands against the fp64 oracle; every
+    output element (exact zeros for empty groups) must be written."""
+    M, N = dy.shape
+    K, E = x.shape[1], len(offs)
+    note(f"GROUPED_K bf16 {name} M={M} N={N} K={K} E={E} out={out_dtype}")
+    odt = torch.bfloat16 if out_dtype == 0 else torch.float32
+    out = torch.empty((E, N, K), dtype=odt, device=DEV)
+    if out_dtype == 0:
+        out.view(torch.int16).fill_(SENT_BF16)
+    else:
+        out.fill_(float("nan"))
+    fm.grouped_mm_scaled(fm.GROUPED_K, bf16_dev(dy), fm.OPD_BF16, None, bf16_dev(x), fm.OPD_BF16, None,
+                         fm.SCALE_NONE, i32_dev(offs), E, M, N, K, out=out, out_dtype=out_dtype)
+    _, got = _out_host(out)
+    ref = oracle.mm_grouped_k_bf16(dy, x, offs)
+    A = bf16_bits_to_f64(np.ascontiguousarray(dy.T))
+    B = bf16_bits_to_f64(np.ascontiguousarray(x.T))
+    contract, tight = oracle.error_bounds_k(A, B, offs)
+    check(got, ref, contract, tight, f"GROUPED_K bf16 {name}")
+
+
+GW_CASES = {
+    # one group whose token count leaves a partial last stage; tiles past N and K
+    "tail": lambda: (synth.normal_bf16(40, (1000, 264), 1e-3), synth.normal_bf16(41, (1000, 520), 1.0, 0.01, 30.0),
+                     np.array([1000], np.int32)),
+    # tiny, single-token and empty groups
+    "small": lambda: (synth.normal_bf16(42, (480, 136), 1e-3), synth.normal_bf16(43, (480, 72), 1.0),
+                      np.cumsum([0, 1, 7, 16, 0, 63, 64, 65, 1, 0, 150, 113]).astype(np.int32)),
+    # decreasing and out-of-range offsets
+    "malformed": lambda: (synth.normal_bf16(44, (600, 64), 1e-3), synth.normal_bf16(45, (600, 96), 1.0),
+                          np.array([100, 50, 650, 900, -3], np.int32)),
+    # more groups than the kernel's group table (the scan path)
+    "many_groups": lambda: (synth.normal_bf16(46, (2048, 64), 1e-3), synth.normal_bf16(47, (2048, 64), 1.0),
+                            synth.offsets_from_counts(synth.random_counts(48, 2048, 300))),
+}
+
+
+@pytest.mark.parametrize("case", list(GW_CASES))
+def test_grouped_k_bf16_gw(case):
+    dy, x, offs = GW_CASES[case]()
+    gw_case(dy, x, offs, name=case)
+
+
+def test_grouped_k_bf16_gw_f32_out():
+    dy, x, offs = GW_CASES["tail"]()
+    gw_case(dy, x, offs, out_dtype=1, name="tail f32")
+
+
+def test_grouped_k_bf16_gw_full_size_sampled():
+    # the Llama3-8B linear's weight gradient kept in BF16: dY [8192, 14336], X [8192, 4096]
+    w = synth.WORKLOADS[2]
+    dy, x = synth.make_dy(w), synth.make_x(w)
+    M, N = dy.shape
+    K = x.shape[1]
+    offs = np.array([M], np.int32)
+    note(f"GROUPED_K bf16 full M={M} N={N} K={K}")
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, bf16_dev(dy), fm.OPD_BF16, None, bf16_dev(x), fm.OPD_BF16, None,
+                               fm.SCALE_NONE, i32_dev(offs), 1, M, N, K)
+    rows = _rows(N, 10, 81)
+    got = bf16_bits_to_f64(host(out[:, torch.from_numpy(rows).to(DEV)]))
+    del out
+    dyr = np.ascontiguousarray(dy[:, rows])
+    ref = oracle.mm_grouped_k_bf16(dyr, x, offs)
+    A = bf16_bits_to_f64(np.ascontiguousarray(dyr.T))
+    B = bf16_bits_to_f64(np.ascontiguousarray(x.T))
+    contract, tight = oracle.error_bounds_k(A, B, offs)
+    check(got, ref, contract, tight, "GROUPED_K bf16 full")
+
+
 # ------------------------------------------------------------------ MXFP8
 
 @pytest.mark.parametrize("rule", [0, 1])
