@@ -18,6 +18,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
+}
 
 // Direct global->LDS loads (a wave fills 64 consecutive 16-byte or 1-byte LDS
 // slots, one per lane, from per-lane global addresses).  Wrapped in plain
@@ -37,6 +42,39 @@ __device__ __forceinline__ void dma_1(const uint8_t* src, uint8_t* dst) {
 __device__ __forceinline__ void store_stream16(uint8_t* dst, u32x4 v) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
+}
+
+// LDS accesses that the compiler's wait insertion does not see.  It cannot
+// tell an LDS buffer apart from the direct-to-LDS loads in flight into other
+// buffers, and before an ordinary LDS access it waits for all of them; with
+// these the caller orders accesses itself: lds_wait() and then lds_ready() on
+// each read result before it is used (the empty asm ties the result to the
+// wait, so no use is scheduled above it).  Addresses are LDS byte offsets.
+typedef unsigned int lds_u2 __attribute__((ext_vector_type(2)));
+typedef unsigned int lds_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);   // the low half of a shared-aperture address
+}
+__device__ __forceinline__ void lds_write8(uint32_t a, lds_u2 v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write16(uint32_t a, lds_u4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_read4(uint32_t a) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(a) : "memory");
+  return r;
+}
+__device__ __forceinline__ lds_u4 lds_read16(uint32_t a) {
+  lds_u4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ void lds_ready(T& r) {
+  asm volatile("" : "+v"(r));
 }
 
 // Workgroup barrier without a memory fence (a fence would wait for every

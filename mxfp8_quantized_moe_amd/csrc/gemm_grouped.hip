@@ -522,6 +522,14 @@ void gemm_fp8_pipe(KParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sring3[SLOTS > 3 ? SCB : 16];
   uint8_t* const slot_data[4] = {ring0, ring1, ring2, ring3};
   uint8_t* const slot_scale[4] = {sring0, sring1, sring2, sring3};
+  // Epilogue staging, 4 KiB per wave: its own buffer beside a 2-slot ring (so
+  // both slots can take the next tile's first stages meanwhile), else the
+  // last ring slot.
+  constexpr int kStgWave = 4096;
+  __shared__ __attribute__((aligned(16))) uint8_t stg_own[SLOTS == 2 ? 4 * kStgWave : 16];
+  // Ring slots refilled with the next tile's first stages before the
+  // epilogue; any others (the staging slot) after it.
+  constexpr int NPRE = SLOTS == 2 ? 2 : SLOTS - 1;
 
   // ---------------------------------------------------------------- tiles
   // Persistent: the grid is at most one workgroup per CU and each walks the
@@ -533,10 +541,11 @@ void gemm_fp8_pipe(KParams p) {
   // on empty tiles.
   //
   // Consecutive tiles of a workgroup overlap: once a tile's last stage has
-  // been read, the next tile's stage 0 is loaded into ring slot 0 while the
-  // epilogue stages results through the last slot.  (Loads and stores share
-  // one counter on gfx9 and may complete out of order with respect to each
-  // other, so the next tile starts with a full drain before using stage 0.)
+  // been read, the ring slots not used for staging are refilled with the next
+  // tile's first stages, which land while the epilogue runs.  (Loads and
+  // stores share one counter on gfx9 and may complete out of order with
+  // respect to each other, so each wave waits for its part of the next stage
+  // 0 before its first store.)
   struct Ch {
     __device__ int operator()(int lo, int hi) const { return (hi - lo + BM - 1) / BM; }
   };
@@ -947,7 +956,10 @@ void gemm_fp8_pipe(KParams p) {
     constexpr int CUR = (S * KS + KS - 1) & 1;
     inner_halves(slot_tag);
     wait_lgkmcnt0();
-    wait_vmcnt<(SLOTS - 2) * LPS>();
+    // The tile's first step needs no stage wait: every wave waited for its
+    // part of the next stage before the tile-start barrier (in the prologue or
+    // in the previous epilogue), so the epilogue's stores are not drained here.
+    if constexpr (!decltype(fix_tag)::value) wait_vmcnt<(SLOTS - 2) * LPS>();
     raw_barrier();
     if constexpr (decltype(fix_tag)::value) {
       if (kt + 1 < nk) fix_boundary(slot_data[NS], stage_of(kt + 1));
@@ -960,10 +972,11 @@ void gemm_fp8_pipe(KParams p) {
   };
 
   // ---- start of the tile.  First tile: stages 0 .. SLOTS-1 are in flight;
-  // wait for stage 0.  Later tiles: every wave already waited for its part of
-  // stage 0 inside the previous epilogue (before that epilogue's stores, which
-  // may complete in any order with respect to loads); refill slots 1 .. SLOTS-1.
-  if (it == 0) wait_vmcnt<(SLOTS - 1) * LPS>();
+  // wait for stages 0 and 1.  Later tiles: stages 0 .. NPRE-1 were issued
+  // before the previous epilogue, and every wave already waited for its part
+  // of them there (before that epilogue's stores, which may complete in any
+  // order with respect to loads); refill the staging slot, if the ring has one.
+  if (it == 0) wait_vmcnt<(SLOTS - 2) * LPS>();
   raw_barrier();
   // The next tile's description now, and its scale loads (issued before this
   // tile's later stages, so they land first and never delay a stage wait).
@@ -973,11 +986,10 @@ void gemm_fp8_pipe(KParams p) {
     load_scales(nxt);
   }
   if (it > 0 && nk > 0) {
-    issue_stage(cur, I1{}, first_stage(cur, min(1, nk - 1)), Checked{});
-    if constexpr (SLOTS > 2)
-      issue_stage(cur, std::integral_constant<int, 2>{}, first_stage(cur, min(2, nk - 1)), Checked{});
-    if constexpr (SLOTS > 3)
-      issue_stage(cur, std::integral_constant<int, 3>{}, first_stage(cur, min(3, nk - 1)), Checked{});
+    static_for<SLOTS - NPRE>([&](auto sc) {
+      constexpr int S = NPRE + decltype(sc)::value;
+      issue_stage(cur, std::integral_constant<int, S>{}, first_stage(cur, min(S, nk - 1)), Checked{});
+    });
   }
   if (nk > 0) {
     fix_boundary(slot_data[0], nk - 1);
@@ -1003,11 +1015,16 @@ void gemm_fp8_pipe(KParams p) {
   wait_vmcnt<0>();   // the reloads past the end land before their slots are reused
 
   // ---- the next tile: its scale reciprocals, then (once no wave reads the
-  // ring any more) its stage 0, which lands during the epilogue.
+  // ring any more) its first stages, which land during the epilogue.
   if (has_next) scale_commit(s_inv[(it + 1) & 1]);
   wait_lgkmcnt0();
   raw_barrier();
-  if (has_next && nxt.nk > 0) issue_stage(nxt, I0{}, first_stage(nxt, 0), Checked{});
+  if (has_next && nxt.nk > 0) {
+    static_for<NPRE>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      issue_stage(nxt, std::integral_constant<int, S>{}, first_stage(nxt, min(S, nxt.nk - 1)), Checked{});
+    });
+  }
 
   // ---------------------------------------------------------------- epilogue
   // fp32 scales are multipliers of the quantized operands: divide by both
@@ -1018,102 +1035,64 @@ void gemm_fp8_pipe(KParams p) {
   const int64_t out_base = cur.out_base;
   const float keep = c_hi > c_lo ? 1.0f : 0.0f;
   constexpr int ELEM = OUT == 0 ? 2 : 4;
-  constexpr int RB = WN * ELEM;                 // staged row bytes
-  // 32-row blocks per staging pass: four waves share the last ring slot.
-  constexpr int TMP_FIT = STAGE / (4 * 32 * RB);
-  constexpr int TMP = TMP_FIT >= TM ? TM : (TMP_FIT >= 2 ? 2 : TMP_FIT);
-  // Four consecutive output columns of one row, scaled: register quad q of acc[i][j].
-  auto quad = [&](int i, int j, int q, float inv_p, const float* inv_q) {
-    f32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * inv_p * inv_q[4 * q + e];
-    return v;
-  };
-  if (TMP > 0 && (out_ld * ELEM) % 16 == 0) {
-    // Stage each wave's results through LDS and write whole 16-byte pieces of
-    // output rows.  A lane holds four consecutive columns of one row per
-    // register quad: bf16 packs them into 8 bytes (fp32: 16 bytes), written
-    // to staged row r at unit u ^ (r & 31) (units of 8 bytes for bf16, 16 for
-    // fp32): the 32 rows one write instruction touches land on distinct banks.
-    // A 16-lane read of a whole staged row stays conflict-free; a bf16 read
-    // of logical 16-byte chunk k finds its two halves in physical chunk
-    // k ^ ((r & 31) >> 1), swapped when r is odd.
-    constexpr int PASSES = TMP > 0 ? TM / TMP : 1;
-    constexpr int NCH = RB / 16;                // 16-byte chunks per staged row
-    constexpr int WBYTES = TMP * 32 * RB;
+  if ((out_ld * ELEM) % 16 == 0) {
+    // Lane indices from a fresh opaque copy of the thread index: values kept
+    // across the k loop may be spilled, and a reload would wait for the
+    // stages now in flight.
+    int t_epi = threadIdx.x;
+    asm volatile("" : "+v"(t_epi));
+    const int lane = t_epi & 63, g = lane >> 5, lrow = lane & 31;
+    // Each pass stages one 32-row block of a wave's results, PC columns wide
+    // (128 bytes per row), and writes whole 128-byte row segments.  A lane
+    // holds four consecutive columns of one row per register quad: bf16
+    // packs them into 8 bytes, written at unit u ^ (row & 15) of its staged
+    // row (fp32: 16 bytes at unit u ^ (row & 7)), so the rows one write
+    // instruction touches land on distinct banks; 8 lanes read back one whole
+    // row.  A bf16 read of logical 16-byte chunk k finds its two halves in
+    // physical chunk k ^ ((row & 15) >> 1), swapped when the row is odd.
+    // LDS accesses go through lds_* while the next tile's stages land.
+    constexpr int PC = 128 / ELEM;              // output columns per pass
+    constexpr int JPP = PC / 32;                // 32-column blocks per pass
     constexpr int VEC = 16 / ELEM;              // elements per 16-byte piece
-    static_assert(TMP == 0 || (TM % TMP == 0 && 4 * WBYTES <= STAGE), "staging fits in the last ring slot");
-    uint8_t* const stg = slot_data[SLOTS - 1] + wave * WBYTES;
+    uint8_t* const stg = (SLOTS == 2 ? stg_own : slot_data[SLOTS - 1]) + wave * kStgWave;
+    const uint32_t stg_l = lds_off(stg), sinv_l = lds_off(sinv);
+    const bool full = p_valid == BM && q_valid == BN;
+    const int rr = lane >> 3, k = lane & 7;     // read-back: staged row 8 itr + rr, chunk k
+    lds_u4 dv[2][4];                            // read-back pieces of the last two passes
+    // Stores of pass n (32-row block n % TM, columns PC (n / TM) ..), once its
+    // read-back has landed.
+    auto store_pass = [&](auto nc) {
+      constexpr int n = decltype(nc)::value, i = n % TM, jp = n / TM;
 #pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      if (pass > 0) wait_lgkmcnt0();   // this wave's reads of the previous pass are done
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        float inv_q[16];                           // columns 32 j + 8 q + 4 g + e
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 f = {1.0f, 1.0f, 1.0f, 1.0f};
-          if constexpr (SK == 0) f = *reinterpret_cast<const f32x4*>(&sinv[BM + wn * WN + 32 * j + 8 * q + 4 * g]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) inv_q[4 * q + e] = f[e] * keep;
-        }
-#pragma unroll
-        for (int ii = 0; ii < TMP; ++ii) {
-          const int i = pass * TMP + ii;
-          const int lr = 32 * ii + lrow;             // staged row
-          const float inv_p = (SK == 0 ? sinv[wm * WM + 32 * i + lrow] : 1.0f) * keep;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = quad(i, j, q, inv_p, inv_q);
-            const int u = 8 * j + 2 * q + g;         // logical unit of 4 columns
-            if constexpr (OUT == 0) {
-              const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
-              const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
-              *reinterpret_cast<u32x2*>(stg + lr * RB + ((u ^ (lr & 31)) << 3)) =
-                  u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-            } else {
-              *reinterpret_cast<f32x4*>(stg + lr * RB + ((u ^ (lr & 31)) << 4)) = v;
-            }
-          }
+      for (int itr = 0; itr < 4; ++itr) {
+        lds_ready(dv[n & 1][itr]);
+        if constexpr (OUT == 0) {
+          const bool odd = rr & 1;   // (8 itr + rr) & 1
+          const lds_u4 d = dv[n & 1][itr];
+          dv[n & 1][itr] = lds_u4{odd ? d.z : d.x, odd ? d.w : d.y, odd ? d.x : d.z, odd ? d.y : d.w};
         }
       }
-      wait_lgkmcnt0();   // a wave reads back only its own staging area
-      if (pass == 0) wait_vmcnt<0>();   // the next tile's stage 0 (older than any store below)
-      constexpr int RPI = 64 / NCH;                 // staged rows per read instruction
-      constexpr int NRD = TMP > 0 ? TMP * 32 / RPI : 1;   // read instructions per pass
-      const int k = lane % NCH, c = wn * WN + k * VEC;
-      u32x4 dv[NRD];
-#pragma unroll
-      for (int itr = 0; itr < NRD; ++itr) {
-        const int lr = itr * RPI + lane / NCH;
-        const int pc = OUT == 0 ? (k ^ ((lr & 31) >> 1)) : (k ^ (lr & 31));
-        dv[itr] = *reinterpret_cast<const u32x4*>(stg + lr * RB + (pc << 4));
-      }
-      if constexpr (OUT == 0) {
-#pragma unroll
-        for (int itr = 0; itr < NRD; ++itr) {
-          const bool odd = (itr * RPI + lane / NCH) & 1;
-          const u32x4 d = dv[itr];
-          dv[itr] = u32x4{odd ? d.z : d.x, odd ? d.w : d.y, odd ? d.x : d.z, odd ? d.y : d.w};
-        }
-      }
+      // All pre-issued stages of the next tile (this wave's part) land before
+      // the first store: until then only loads are in flight, and they
+      // complete in order.
+      if constexpr (n == 0) wait_vmcnt<0>();
+      const int c = wn * WN + PC * jp + VEC * k;
       uint8_t* const row0 = static_cast<uint8_t*>(p.out) +
-                            (out_base + (int64_t)(wm * WM + pass * TMP * 32 + lane / NCH) * out_ld + c) * ELEM;
-      if (p_valid == BM && q_valid == BN) {
+                            (out_base + (int64_t)(wm * WM + 32 * i + rr) * out_ld + c) * ELEM;
+      if (full) {
 #pragma unroll
-        for (int itr = 0; itr < NRD; ++itr)
-          store_stream16(row0 + (int64_t)itr * RPI * out_ld * ELEM, dv[itr]);
-        continue;
+        for (int itr = 0; itr < 4; ++itr)
+          store_stream16(row0 + (int64_t)itr * 8 * out_ld * ELEM, __builtin_bit_cast(u32x4, dv[n & 1][itr]));
+        return;
       }
 #pragma unroll
-      for (int itr = 0; itr < NRD; ++itr) {
-        const int lr = itr * RPI + lane / NCH;
-        const u32x4 d = dv[itr];
-        const int r = wm * WM + pass * TMP * 32 + lr;
+      for (int itr = 0; itr < 4; ++itr) {
+        const int r = wm * WM + 32 * i + 8 * itr + rr;
         if (r >= p_valid) continue;
-        uint8_t* dst = row0 + (int64_t)itr * RPI * out_ld * ELEM;
+        uint8_t* dst = row0 + (int64_t)itr * 8 * out_ld * ELEM;
+        const lds_u4 d = dv[n & 1][itr];
         if (c + VEC <= q_valid) {
-          store_stream16(dst, d);
+          store_stream16(dst, __builtin_bit_cast(u32x4, d));
         } else {
           const uint32_t w[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
@@ -1126,10 +1105,92 @@ void gemm_fp8_pipe(KParams p) {
           }
         }
       }
-    }
+    };
+    static_for<TN / JPP>([&](auto jpc) {
+      constexpr int jp = decltype(jpc)::value;
+      // reciprocals of the lane's columns in this pass (register quad q of
+      // block jj: columns 32 jj + 8 q + 4 g + e of the pass) and of its rows
+      f32x4 inv_q[JPP][4];
+      float inv_p[TM];
+      if constexpr (SK == 0) {
+        lds_u4 rq[JPP][4];
+        uint32_t rp[TM];
+#pragma unroll
+        for (int jj = 0; jj < JPP; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            rq[jj][q] = lds_read16(sinv_l + 4 * (BM + wn * WN + 32 * (JPP * jp + jj) + 8 * q + 4 * g));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) rp[i] = lds_read4(sinv_l + 4 * (wm * WM + 32 * i + lrow));
+        lds_wait();
+#pragma unroll
+        for (int jj = 0; jj < JPP; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            lds_ready(rq[jj][q]);
+            inv_q[jj][q] = __builtin_bit_cast(f32x4, rq[jj][q]) * keep;
+          }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          lds_ready(rp[i]);
+          inv_p[i] = __builtin_bit_cast(float, rp[i]) * keep;
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < JPP; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) inv_q[jj][q] = f32x4{keep, keep, keep, keep};
+#pragma unroll
+        for (int i = 0; i < TM; ++i) inv_p[i] = 1.0f;
+      }
+      static_for<TM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, n = TM * jp + i;   // pass n
+        // stage: block (i, JPP jp + jj), quad q -> staged row lrow
+#pragma unroll
+        for (int jj = 0; jj < JPP; ++jj) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][JPP * jp + jj][4 * q + e] * inv_p[i] * inv_q[jj][q][e];
+            const int u = 8 * jj + 2 * q + g;
+            if constexpr (OUT == 0) {
+              const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
+              const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
+              lds_write8(stg_l + lrow * 128 + ((u ^ (lrow & 15)) << 3),
+                         lds_u2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
+            } else {
+              lds_write16(stg_l + lrow * 128 + ((u ^ (lrow & 7)) << 4), __builtin_bit_cast(lds_u4, v));
+            }
+          }
+        }
+        // read back whole 16-byte pieces: 8 lanes per staged row.  (A wave's
+        // LDS accesses execute in order, so these reads see this pass's
+        // writes and the previous pass's reads saw its own.)
+#pragma unroll
+        for (int itr = 0; itr < 4; ++itr) {
+          const int lr = 8 * itr + rr;
+          const int pc = OUT == 0 ? (k ^ ((lr & 15) >> 1)) : (k ^ (lr & 7));
+          dv[n & 1][itr] = lds_read16(stg_l + lr * 128 + (pc << 4));
+        }
+        // the previous pass's pieces leave now, behind this pass's LDS work
+        if constexpr (n > 0) {
+          wait_lgkmcnt<4 * JPP + 4>();
+          store_pass(std::integral_constant<int, n - 1>{});
+        }
+      });
+    });
+    wait_lgkmcnt<0>();
+    store_pass(std::integral_constant<int, TM * (TN / JPP) - 1>{});
   } else {
     // Output rows not 16-byte aligned: element stores straight from registers.
-    wait_vmcnt<0>();   // the next tile's stage 0 (older than any store below)
+    wait_vmcnt<0>();   // the next tile's pre-issued stages (older than any store below)
+    auto quad = [&](int i, int j, int q, float inv_p, const float* inv_q) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * inv_p * inv_q[4 * q + e];
+      return v;
+    };
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       float inv_q[16];
