@@ -475,6 +475,47 @@ struct PipeRing {
   static __device__ __forceinline__ int off(int r, int c) { return r * BK + (phys(r, c) << 4); }
 };
 
+// Zero the bytes outside the contraction range [lo, hi) of one ring stage
+// (SROWS tile rows of CH 16-byte chunks at contraction positions base + 16 c).
+// Wave w takes chunk columns w, w + 4, ..., so the test of a column is
+// wave-uniform: a column wholly outside the range is overwritten with zeros,
+// a column holding an end of the range is read, masked with one mask for all
+// its rows and written back, and any other column is left alone.  Lane l
+// takes rows l, l + 64, ...: the swizzle term of a row repeats every 16 rows,
+// so a lane's chunks of one column lie 64 BK bytes apart.
+template <class R, int SROWS, int CH>
+__device__ __forceinline__ void zero_outside_ring(uint8_t* st, int base, int lo, int hi) {
+  static_assert(SROWS % 64 == 0 && CH % 4 == 0, "whole row groups and column sets per wave");
+  constexpr int RPL = SROWS / 64;               // rows per lane
+  constexpr int STEP = 64 * R::CH * 16;         // bytes between a lane's rows
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint32_t st_l = lds_off(st);
+#pragma unroll
+  for (int cc = 0; cc < CH / 4; ++cc) {
+    const int c = wave + 4 * cc;                // wave-uniform column
+    const int pos = base + 16 * c;
+    const uint32_t a0 = st_l + R::off(lane, c);
+    if (pos + 16 <= lo || pos >= hi) {
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) lds_write16(a0 + k * STEP, lds_u4{0u, 0u, 0u, 0u});
+    } else if (pos < lo || pos + 16 > hi) {
+      const u32x4 m = mask_chunk(u32x4{~0u, ~0u, ~0u, ~0u}, pos, lo, hi);
+      const lds_u4 mv = lds_u4{m.x, m.y, m.z, m.w};
+      lds_u4 v[RPL];
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) v[k] = lds_read16(a0 + k * STEP);
+      lds_wait();
+#pragma unroll
+      for (int k = 0; k < RPL; ++k) {
+        lds_ready(v[k]);
+        lds_write16(a0 + k * STEP, v[k] & mv);
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ void dma_4(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
@@ -860,7 +901,7 @@ void gemm_fp8_pipe(KParams p) {
   auto fix_boundary = [&](uint8_t* st, int kt) {
     const int base = c_start + kt * BK;
     if (kt >= nk || (base >= c_lo && base + BK <= c_hi)) return;    // uniform
-    zero_outside<R, SROWS, CH>(st, base, c_lo, c_hi);
+    zero_outside_ring<R, SROWS, CH>(st, base, c_lo, c_hi);
     wait_lgkmcnt0();
     raw_barrier();
   };
