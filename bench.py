@@ -13,11 +13,16 @@ one-GPU expert share, 5 Llama4-Scout-shaped MXFP8 layer; --gw adds the BF16
 weight-gradient variant of config 2 as its own line item.
 
 Prints ONE JSON line.  `value` is microseconds per layer step (lower is
-better).  Also reported: aggregate quantization GB/s (algorithmic bytes: 2 B
-read + 1 B written per element + scale bytes), aggregate GEMM TFLOP/s
-(2 * sum_e M_e * N * K), per-kernel averages from HIP events on the launch
-stream, the roofline of the dominant kernel, and the CPU oracle timed on a
-bounded sample of the same workload (a reported baseline, not a target).
+better).  Every input has 4 device copies and step s reads copy s % 4, so no
+step finds its inputs in the 256 MB last-level cache (reuse between launches
+inside a step stays).  Also reported: aggregate quantization GB/s (algorithmic
+bytes: 2 B read + 1 B written per element + scale bytes), aggregate GEMM
+TFLOP/s (2 * sum_e M_e * N * K), per-kernel averages from HIP events on the
+launch stream over the timed steps, the roofline of the dominant kernel, each
+launch alone after a 1 GiB cache-evicting read (median, p10, p90 of 20
+repeats after 5 warm-ups), the peaks used, the shader clock rocm-smi reports
+while untimed steps run, and the CPU oracle timed on a bounded sample of the
+same workload (a reported baseline, not a target).
 """
 from __future__ import annotations
 
@@ -61,13 +66,18 @@ def parse():
 
 # ---------------------------------------------------------------------- layer plan
 
+N_ROTATE = 4   # device copies of every input; step s reads copy s % N_ROTATE
+
+
 class Step:
     """A list of launches; each item: (name, kind, fn, work, hbm) with kind 'quant' (work = hbm =
     algorithmic bytes) or 'gemm' / 'gemm_bf16' (work = flops, hbm = algorithmic bytes: operands and
-    scales read once, output written once)."""
+    scales read once, output written once).  Launches read their inputs through getters that pick
+    copy `rot[0]`, so consecutive steps read inputs that the caches do not hold."""
 
     def __init__(self):
         self.items = []
+        self.rot = [0]
 
     def add(self, name, kind, fn, work, hbm=None):
         self.items.append((name, kind, fn, work, work if hbm is None else hbm))
@@ -82,7 +92,10 @@ def build_step(cfg: int, gw: bool):
     w = synth.WORKLOADS[cfg]
 
     def dv(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+        """N_ROTATE device copies of a bf16 input; returns a getter of the current one."""
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+        copies = [t] + [t.clone() for _ in range(N_ROTATE - 1)]
+        return lambda: copies[step.rot[0]]
 
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
     f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
@@ -101,20 +114,20 @@ def build_step(cfg: int, gw: bool):
 
     def q_row(name, x, rows, cols):
         q, s = u8(rows, cols), f32(rows)
-        step.add(name, "quant", lambda: fm.quantize_rowwise(x.view(rows, cols), 0, q=q, scale=s),
+        step.add(name, "quant", lambda: fm.quantize_rowwise(x().view(rows, cols), 0, q=q, scale=s),
                  qbytes(rows * cols, rows))
         return q, s
 
     def q_col_grouped(name, x, rows, cols):
         ld = (rows + 15) // 16 * 16
         q, s = u8(cols, ld), f32(E, cols)
-        step.add(name, "quant", lambda: fm.quantize_colwise(x, offs, 0, q_t=q, scale=s, ld_q=ld),
+        step.add(name, "quant", lambda: fm.quantize_colwise(x(), offs, 0, q_t=q, scale=s, ld_q=ld),
                  qbytes(rows * cols, E * cols))
         return q, s, ld
 
     def q_col_batched(name, x, B, R, C):
         q, s = u8(B, C, R), f32(B, C)
-        step.add(name, "quant", lambda: fm.quantize_colwise(x, None, 0, q_t=q, scale=s, ld_q=R),
+        step.add(name, "quant", lambda: fm.quantize_colwise(x(), None, 0, q_t=q, scale=s, ld_q=R),
                  qbytes(B * R * C, B * C))
         return q, s
 
@@ -162,7 +175,7 @@ def build_step(cfg: int, gw: bool):
             if gw:
                 o = bf(1, F2, H)
                 step.add("gemm wgrad bf16", "gemm_bf16",
-                         lambda: fm.grouped_mm_scaled(fm.GROUPED_K, DYd, fm.OPD_BF16, None, Xd, fm.OPD_BF16, None,
+                         lambda: fm.grouped_mm_scaled(fm.GROUPED_K, DYd(), fm.OPD_BF16, None, Xd(), fm.OPD_BF16, None,
                                                       fm.SCALE_NONE, offs, 1, M, F2, H, out=o), 2.0 * M * F2 * H,
                          2 * (M * F2 + M * H + F2 * H))
         return step, host
@@ -201,14 +214,14 @@ def build_step(cfg: int, gw: bool):
 
     def mx_last(name, x, rows, cols):
         q, s = u8(rows, cols), u8(*fm.mx_k4_shape(rows, cols // 32))
-        step.add(name, "quant", lambda: fm.quantize_mx(x.view(rows, cols), axis=1, rule=rule, q=q, scale=s,
+        step.add(name, "quant", lambda: fm.quantize_mx(x().view(rows, cols), axis=1, rule=rule, q=q, scale=s,
                                                        layout=K4),
                  qbytes(rows * cols, rows * cols // 32, 1))
         return q, s
 
     def mx_rows_b(name, x, B, R, C):
         q, s = u8(B, C, R), u8(*fm.mx_k4_shape(B * C, R // 32))
-        step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, rule=rule, q=q, scale=s, layout=K4),
+        step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, rule=rule, q=q, scale=s, layout=K4),
                  qbytes(B * R * C, B * C * R // 32, 1))
         return q, s
 
@@ -216,7 +229,7 @@ def build_step(cfg: int, gw: bool):
 
     def mx_rows_g(name, x, rows, cols):
         q, s = u8(cols, Mp), u8(*fm.mx_k4_shape(cols, Mp // 32))
-        step.add(name, "quant", lambda: fm.quantize_mx(x, axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
+        step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
                                                        offs_pad=op, layout=K4),
                  qbytes(rows * cols, cols * rows // 32, 1))
         return q, s
@@ -243,6 +256,19 @@ def build_step(cfg: int, gw: bool):
 
 
 # ---------------------------------------------------------------------- CPU oracle baseline
+
+def cpu_model():
+    """The host CPU's model name (lscpu), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=30)
+        for line in r.stdout.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        return None
+    return None
+
 
 def cpu_baseline(cfg: int, host: dict):
     """The oracle timed on a bounded sample of the dense layer's work, scaled
@@ -295,6 +321,7 @@ def cpu_baseline(cfg: int, host: dict):
         n_gemm = 3
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(total_us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "cpu_count": os.cpu_count(),
             "sample": f"numpy oracle on row/column samples scaled linearly to the full layer "
                       f"(quant: {rs} rows or {cs} columns per tensor, single-threaded; GEMM: {gm} x {gn} output "
                       f"samples, fp64 BLAS with {threads} threads); {n_gemm} GEMMs + "
@@ -387,6 +414,77 @@ def traffic_for(kernel_item: str, cfg: int):
     return d.get("per_launch_bytes", {}).get(f"cfg{cfg}:{kernel_item}")
 
 
+# ---------------------------------------------------------------------- per-kernel protocol
+
+FLUSH_BYTES = 1 << 30   # read before each flushed repeat: more than the 256 MB last-level cache and the L2s
+
+
+def per_kernel_flushed(step, stream, warmup=5, repeats=20):
+    """Each launch of the step alone: `warmup` untimed launches, then `repeats` timed ones, each after
+    a 1 GiB device read that evicts the last-level cache and the L2s (outside the timed events).  A
+    read, not a write: a write would leave up to 256 MB of dirty lines whose write-back then falls
+    inside the timed launch.  Returns {name: (median, p10, p90)} in microseconds."""
+    import torch
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    res = {}
+    step.rot[0] = 0
+    for name, _, fn, _, _ in step.items:
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(repeats)]
+        for r in range(repeats):
+            flush.sum()
+            ev[r][0].record(stream)
+            fn()
+            ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        res[name] = tuple(round(float(np.percentile(t, p)), 1) for p in (50, 10, 90))
+    del flush
+    return res
+
+
+def _smi_sclk():
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+        for card in d.values():
+            for k, v in card.items():
+                if "sclk" in k.lower() and "speed" in k.lower():
+                    digits = "".join(ch for ch in str(v).split("Mhz")[0] if ch.isdigit() or ch == ".")
+                    return float(digits) if digits else None
+    except Exception:
+        return None
+    return None
+
+
+def observed_sclk(step, seconds=1.5):
+    """Shader clock (MHz) that rocm-smi reports while untimed steps run back to back, or None."""
+    import threading
+    import torch
+    box = {}
+
+    def sample():
+        time.sleep(seconds / 3)
+        box["mhz"] = _smi_sclk()
+
+    th = threading.Thread(target=sample)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    k = 0
+    while time.perf_counter() < t_end or th.is_alive():
+        step.rot[0] = k % N_ROTATE
+        for it in step.items:
+            it[2]()
+        torch.cuda.synchronize()
+        k += 1
+        if k > 100000:
+            break
+    th.join()
+    return box.get("mhz")
+
+
 # ---------------------------------------------------------------------- main
 
 def main():
@@ -415,7 +513,8 @@ def main():
     step, host = build_step(args.config, args.gw)
     stream = torch.cuda.current_stream()
     names = [it[0] for it in step.items]
-    for _ in range(args.warmup):
+    for w_i in range(args.warmup):
+        step.rot[0] = w_i % N_ROTATE
         for it in step.items:
             it[2]()
     torch.cuda.synchronize()
@@ -432,6 +531,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        step.rot[0] = s % N_ROTATE
         for i, it in enumerate(step.items):
             ev[s][i][0].record(stream)
             it[2]()
@@ -466,6 +566,7 @@ def main():
         b, a, pk, _ = roof(*v)
         fracs[k] = {"bound": b, "frac": round(a / pk, 4)}
 
+    flushed = {} if args.only is not None else per_kernel_flushed(step, stream)
     w = synth.WORKLOADS[args.config]
     out = {
         "metric": "quant HBM GB/s + grouped-GEMM TFLOP/s; us per MoE layer (quant+GEMM)",
@@ -493,6 +594,13 @@ def main():
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, args.config)},
         "kernels_roofline": fracs,
+        "kernels_flushed": {k: {"median_us": v[0], "p10_us": v[1], "p90_us": v[2],
+                                "frac": round(roof(per[k][0], per[k][1], v[0], per[k][3])[1]
+                                              / roof(per[k][0], per[k][1], v[0], per[k][3])[2], 4)}
+                            for k, v in flushed.items()},
+        "peaks": {"hbm_GBps": PEAK_HBM_GBPS, "fp8_TFLOPs": PEAK_FP8_TFLOPS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
+        "sclk_MHz_under_load": observed_sclk(step) if args.only is None else None,
+        "inputs": f"{N_ROTATE} device copies of every input, step s reads copy s % {N_ROTATE}",
     }
     if not args.no_cpu_baseline and args.config == 2:
         out["cpu_baseline"] = cpu_baseline(args.config, host)
