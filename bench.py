@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--gw", action="store_true", help="config 2: add the BF16 wgrad variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-kernel", action="store_true",
+                    help="skip the flushed per-kernel pass and the clock sample (kernel traces of the steps alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--only", default=None, metavar="ITEM",
@@ -566,7 +568,8 @@ def main():
         b, a, pk, _ = roof(*v)
         fracs[k] = {"bound": b, "frac": round(a / pk, 4)}
 
-    flushed = {} if args.only is not None else per_kernel_flushed(step, stream)
+    extras = args.only is None and not args.no_per_kernel
+    flushed = per_kernel_flushed(step, stream) if extras else {}
     w = synth.WORKLOADS[args.config]
     out = {
         "metric": "quant HBM GB/s + grouped-GEMM TFLOP/s; us per MoE layer (quant+GEMM)",
@@ -599,7 +602,7 @@ def main():
                                               / roof(per[k][0], per[k][1], v[0], per[k][3])[2], 4)}
                             for k, v in flushed.items()},
         "peaks": {"hbm_GBps": PEAK_HBM_GBPS, "fp8_TFLOPs": PEAK_FP8_TFLOPS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
-        "sclk_MHz_under_load": observed_sclk(step) if args.only is None else None,
+        "sclk_MHz_under_load": observed_sclk(step) if extras else None,
         "inputs": f"{N_ROTATE} device copies of every input, step s reads copy s % {N_ROTATE}",
     }
     if not args.no_cpu_baseline and args.config == 2:
