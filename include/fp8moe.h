@@ -131,6 +131,40 @@ int quantize_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_
                      int codec, void *q, float *scale, void *stream);
 
 /*
+ * swiglu_quantize_rowwise -- the SwiGLU activation between the two expert
+ * GEMMs, fused with the rowwise quantization of its output for the W2 GEMM.
+ *   [P1 Details: the MoE layer's grouped GEMMs on dynamically quantized
+ *   operands, fused quantization kernels; P4 "MoE" (routed experts between two
+ *   grouped GEMMs) and "Три уровня оптимизации Triton-ядер" (quantization fused
+ *   into the kernel that produces the tensor).]
+ *   h1     bf16 [rows][ld_h1]  W1's output: gate in columns [0, F), up in [F, 2F)
+ *   a2     bf16 [rows][F]      bf16(silu(gate) * up), silu(g) = g / (1 + e^-g),
+ *                              fp32 arithmetic, round to nearest even (written)
+ *   q      u8   [rows][F]      FP8 codes of a2, as quantize_rowwise(a2) (written)
+ *   scale  f32  [rows]         as quantize_rowwise(a2) (written)
+ *   Requires: rows, F >= 0; ld_h1 >= 2F; F % 8 == 0; ld_h1 % 8 == 0; h1, a2 and
+ *   q 16-byte aligned, scale 4-byte aligned.  The caller owns every buffer.
+ */
+int swiglu_quantize_rowwise(const void *h1_bf16, int64_t rows, int64_t F, int64_t ld_h1,
+                            int codec, void *a2_bf16, void *q, float *scale, void *stream);
+
+/*
+ * swiglu_backward_quantize_rowwise -- the gradient of W1's output through the
+ * SwiGLU, fused with its rowwise quantization for the W1 dgrad GEMM.
+ *   [as swiglu_quantize_rowwise]
+ *   da2    bf16 [rows][F]      gradient of a2 (the W2 dgrad output)
+ *   h1     bf16 [rows][ld_h1]  as above
+ *   dh1    bf16 [rows][2F]     [bf16(da2 up s (1 + g (1 - s))) | bf16(da2 g s)],
+ *                              s = sigmoid(gate), fp32 arithmetic (written)
+ *   q      u8   [rows][2F]     FP8 codes of dh1, as quantize_rowwise(dh1) (written)
+ *   scale  f32  [rows]         as quantize_rowwise(dh1) (written)
+ *   Requires: as swiglu_quantize_rowwise, and da2 16-byte aligned.
+ */
+int swiglu_backward_quantize_rowwise(const void *da2_bf16, const void *h1_bf16, int64_t rows,
+                                     int64_t F, int64_t ld_h1, int codec, void *dh1_bf16,
+                                     void *q, float *scale, void *stream);
+
+/*
  * quantize_colwise -- one fp32 scale per (group, column), reduced over the
  * group's rows, with the FP8 output written transposed (contraction-contiguous)
  * so the backward GEMMs read it directly, with no separate transpose copy.

@@ -20,7 +20,8 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "grouped_mm_scaled", "encode_f32", "default_codec", "E4M3FN", "E4M3FNUZ", "MX_FLOOR_OCP",
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
-           "mx_k4_shape", "Fp8MoeError"]
+           "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
+           "swiglu_backward_quantize_rowwise"]
 
 
 def _ptr(t):
@@ -143,6 +144,39 @@ def grouped_mm_scaled(mode, a, a_fmt, a_scale, b, b_fmt, b_scale, scale_kind, of
                                       _stream(stream))
     _lib.check("grouped_mm_scaled", st)
     return out
+
+
+def swiglu_quantize_rowwise(h1, codec=E4M3FN, a2=None, q=None, scale=None, stream=None):
+    """h1 [R, 2F] bf16 (gate | up; row stride may exceed 2F) -> (a2 bf16 [R, F], q uint8 [R, F], scale f32 [R])."""
+    h1 = _bits(h1)
+    R, F2 = h1.shape
+    if F2 % 2 or (h1.numel() and h1.stride(1) != 1):
+        raise ValueError("swiglu_quantize_rowwise needs an even column count and unit column stride")
+    F = F2 // 2
+    ld = h1.stride(0) if h1.numel() else F2
+    a2 = torch.empty((R, F), dtype=torch.bfloat16, device=h1.device) if a2 is None else a2
+    q = torch.empty((R, F), dtype=torch.uint8, device=h1.device) if q is None else q
+    scale = torch.empty((R,), dtype=torch.float32, device=h1.device) if scale is None else scale
+    _lib.check("swiglu_quantize_rowwise", _lib.lib().swiglu_quantize_rowwise(
+        _ptr(h1), R, F, ld, codec, _ptr(a2), _ptr(q), _ptr(scale), _stream(stream)))
+    return a2, q, scale
+
+
+def swiglu_backward_quantize_rowwise(da2, h1, codec=E4M3FN, dh1=None, q=None, scale=None, stream=None):
+    """da2 [R, F] bf16 and h1 [R, 2F] bf16 -> (dh1 bf16 [R, 2F], q uint8 [R, 2F], scale f32 [R])."""
+    h1 = _bits(h1)
+    da2 = _bits(da2).contiguous()
+    R, F2 = h1.shape
+    if F2 % 2 or (h1.numel() and h1.stride(1) != 1) or tuple(da2.shape) != (R, F2 // 2):
+        raise ValueError("swiglu_backward_quantize_rowwise: h1 [R, 2F] with unit column stride, da2 [R, F]")
+    F = F2 // 2
+    ld = h1.stride(0) if h1.numel() else F2
+    dh1 = torch.empty((R, F2), dtype=torch.bfloat16, device=h1.device) if dh1 is None else dh1
+    q = torch.empty((R, F2), dtype=torch.uint8, device=h1.device) if q is None else q
+    scale = torch.empty((R,), dtype=torch.float32, device=h1.device) if scale is None else scale
+    _lib.check("swiglu_backward_quantize_rowwise", _lib.lib().swiglu_backward_quantize_rowwise(
+        _ptr(da2), _ptr(h1), R, F, ld, codec, _ptr(dh1), _ptr(q), _ptr(scale), _stream(stream)))
+    return dh1, q, scale
 
 
 def encode_f32(y, codec=E4M3FN, q=None, stream=None):

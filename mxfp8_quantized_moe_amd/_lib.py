@@ -22,7 +22,7 @@ OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_rows_bound",
            "grouped_mm_scaled", "fp8moe_encode_f32", "fp8moe_status_string", "fp8moe_default_codec",
-           "fp8moe_version"]
+           "fp8moe_version", "swiglu_quantize_rowwise", "swiglu_backward_quantize_rowwise"]
 
 _lib = None
 
@@ -39,6 +39,8 @@ _SIGS = {
     "fp8moe_status_string": (ctypes.c_char_p, [_int]),
     "fp8moe_default_codec": (_int, [_int, ctypes.POINTER(_int)]),
     "fp8moe_version": (_int, []),
+    "swiglu_quantize_rowwise": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
+    "swiglu_backward_quantize_rowwise": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
 }
 
 

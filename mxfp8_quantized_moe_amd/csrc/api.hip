@@ -40,6 +40,24 @@ int quantize_rowwise(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_
                                                static_cast<uint8_t*>(q), scale, as_stream(stream)));
 }
 
+int swiglu_quantize_rowwise(const void* h1_bf16, int64_t rows, int64_t F, int64_t ld_h1, int codec, void* a2_bf16,
+                            void* q, float* scale, void* stream) {
+  const int st = check_swiglu(h1_bf16, rows, F, ld_h1, codec, a2_bf16, q, scale, nullptr, false);
+  if (st) return st;
+  return launch_status(launch_swiglu_quantize_rowwise(static_cast<const uint16_t*>(h1_bf16), rows, F, ld_h1, codec,
+                                                      static_cast<uint16_t*>(a2_bf16), static_cast<uint8_t*>(q),
+                                                      scale, as_stream(stream)));
+}
+
+int swiglu_backward_quantize_rowwise(const void* da2_bf16, const void* h1_bf16, int64_t rows, int64_t F, int64_t ld_h1,
+                                     int codec, void* dh1_bf16, void* q, float* scale, void* stream) {
+  const int st = check_swiglu(h1_bf16, rows, F, ld_h1, codec, dh1_bf16, q, scale, da2_bf16, true);
+  if (st) return st;
+  return launch_status(launch_swiglu_backward_quantize_rowwise(
+      static_cast<const uint16_t*>(da2_bf16), static_cast<const uint16_t*>(h1_bf16), rows, F, ld_h1, codec,
+      static_cast<uint16_t*>(dh1_bf16), static_cast<uint8_t*>(q), scale, as_stream(stream)));
+}
+
 int quantize_colwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                      int32_t n_groups, int codec, void* q_t, int64_t ld_q, float* scale, void* stream) {
   const int st = check_quantize_colwise(x_bf16, batch, rows, cols, offs, n_groups, codec, q_t, ld_q, scale);

@@ -36,5 +36,10 @@ struct GemmArgs {
 hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st);
 
 hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st);
+hipError_t launch_swiglu_quantize_rowwise(const uint16_t* h1, int64_t rows, int64_t F, int64_t ld_h1, int codec,
+                                          uint16_t* a2, uint8_t* q, float* scale, hipStream_t st);
+hipError_t launch_swiglu_backward_quantize_rowwise(const uint16_t* da2, const uint16_t* h1, int64_t rows, int64_t F,
+                                                   int64_t ld_h1, int codec, uint16_t* dh1, uint8_t* q, float* scale,
+                                                   hipStream_t st);
 
 }  // namespace fp8moe

@@ -149,6 +149,20 @@ int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const v
   return FP8MOE_OK;
 }
 
+int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int codec, const void* out_bf16,
+                 const void* q, const void* scale, const void* da2, bool backward) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (rows < 0 || F < 0 || rows > kI32Max * 256LL || F > kI32Max / 2 || ld_h1 < 2 * F) return FP8MOE_ERR_SHAPE;
+  const int64_t n = mul(rows, 2 * F);
+  if (n < 0 || mul(rows, ld_h1) < 0) return FP8MOE_ERR_SHAPE;
+  if (!need(h1, n) || !need(out_bf16, n) || !need(q, n) || !need(scale, rows) || (backward && !need(da2, n)))
+    return FP8MOE_ERR_NULL;
+  if (F % 8 || ld_h1 % 8 || !aligned(h1, 16) || !aligned(out_bf16, 16) || !aligned(q, 16) || !aligned(scale, 4) ||
+      (backward && !aligned(da2, 16)))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_encode_f32(const void* y, int64_t n, int codec, const void* q) {
   if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
   if (n < 0 || n > kI32Max * 64LL) return FP8MOE_ERR_SHAPE;

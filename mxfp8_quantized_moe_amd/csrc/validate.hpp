@@ -20,6 +20,8 @@ int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const v
                      const void* sb, int scale_kind, const int32_t* offs, int32_t n_groups, int64_t M,
                      int64_t N, int64_t K, const void* out, int out_dtype);
 int check_encode_f32(const void* y, int64_t n, int codec, const void* q);
+int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int codec, const void* out_bf16,
+                 const void* q, const void* scale, const void* da2, bool backward);
 
 int64_t mx_rows_bound(int64_t rows, int32_t n_groups);
 

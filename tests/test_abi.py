@@ -70,6 +70,34 @@ def test_rowwise_rejections(lib):
     assert f(P, 4, 16, 16, 0, P, P + 2, None) == L.ERR_ALIGN
 
 
+def test_swiglu_rejections(lib):
+    f = lib.swiglu_quantize_rowwise          # (h1, rows, F, ld_h1, codec, a2, q, scale, stream)
+    assert f(P, 4, 16, 32, 7, P, P, P, None) == L.ERR_ENUM
+    assert f(P, -1, 16, 32, 0, P, P, P, None) == L.ERR_SHAPE
+    assert f(P, 4, 16, 24, 0, P, P, P, None) == L.ERR_SHAPE          # ld_h1 < 2F
+    assert f(None, 4, 16, 32, 0, P, P, P, None) == L.ERR_NULL
+    assert f(P, 4, 16, 32, 0, None, P, P, None) == L.ERR_NULL
+    assert f(P, 4, 16, 32, 0, P, None, P, None) == L.ERR_NULL
+    assert f(P, 4, 16, 32, 0, P, P, None, None) == L.ERR_NULL
+    assert f(P, 4, 12, 32, 0, P, P, P, None) == L.ERR_ALIGN           # F % 8
+    assert f(P, 4, 16, 36, 0, P, P, P, None) == L.ERR_ALIGN           # ld_h1 % 8
+    assert f(MIS, 4, 16, 32, 0, P, P, P, None) == L.ERR_ALIGN
+    assert f(P, 4, 16, 32, 0, MIS, P, P, None) == L.ERR_ALIGN
+    assert f(P, 4, 16, 32, 0, P, MIS, P, None) == L.ERR_ALIGN
+    assert f(P, 4, 16, 32, 0, P, P, P + 2, None) == L.ERR_ALIGN
+    b = lib.swiglu_backward_quantize_rowwise  # (da2, h1, rows, F, ld_h1, codec, dh1, q, scale, stream)
+    assert b(P, P, 4, 16, 32, 7, P, P, P, None) == L.ERR_ENUM
+    assert b(P, P, 4, 16, 24, 0, P, P, P, None) == L.ERR_SHAPE
+    assert b(None, P, 4, 16, 32, 0, P, P, P, None) == L.ERR_NULL
+    assert b(P, None, 4, 16, 32, 0, P, P, P, None) == L.ERR_NULL
+    assert b(P, P, 4, 16, 32, 0, None, P, P, None) == L.ERR_NULL
+    assert b(MIS, P, 4, 16, 32, 0, P, P, P, None) == L.ERR_ALIGN
+    assert b(P, P, 4, 12, 32, 0, P, P, P, None) == L.ERR_ALIGN
+    # nothing to do: zero rows is accepted without touching any pointer
+    assert f(None, 0, 16, 32, 0, None, None, None, None) == L.OK
+    assert b(None, None, 0, 16, 32, 0, None, None, None, None) == L.OK
+
+
 def test_colwise_rejections(lib):
     f = lib.quantize_colwise
     assert f(P, 1, 64, 16, P, 4, 3, P, 64, P, None) == L.ERR_ENUM

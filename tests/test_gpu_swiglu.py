@@ -1,0 +1,139 @@
+"""GPU parity of the fused SwiGLU + rowwise quantization (forward and backward)
+against the oracle (oracle/swiglu.py).
+
+The bf16 activation and gradients are compared with the exact values rounded
+once to bf16: the kernels compute in fp32 with their own exponential, so an
+element whose exact value lies within a few fp32 ulps of a bf16 rounding
+boundary may land one bf16 ulp away (bound: 1 ulp, and such elements must be
+rare).  The FP8 codes and scales are an integer decision, taken on the same
+bf16 values on both sides: they must equal the oracle's rowwise quantizer
+applied to the kernel's own bf16 output, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_quantized_moe_amd as fm
+import oracle
+from oracle import swiglu as sw
+from gpu_helpers import DEV, note, bf16_dev, host, assert_bytes_equal, assert_f32_bits_equal
+
+pytestmark = pytest.mark.gpu
+
+CODECS = [fm.E4M3FN, fm.E4M3FNUZ]
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make_h1(seed: int, R: int, F: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((R, F)).astype(np.float32) * 3
+    u = rng.standard_normal((R, F)).astype(np.float32)
+    if R and F:
+        # exact zeros, both signs of up, the exponential's overflow region, tiny gates
+        sp = np.float32([0.0, -0.0, 100.0, -100.0, 89.5, -89.5, 88.0, -88.0, 1e-30, -1e-30, 20.0, -20.0])
+        k = min(F, len(sp))
+        g[0, :k] = sp[:k]
+        u[0, :k] = np.float32([3.0, -3.0] * 6)[:k]
+    if R > 2:
+        g[2] = 0.0                                   # an all-zero activation row
+    return np.concatenate([bf16_bits(g), bf16_bits(u)], axis=1)
+
+
+def make_da2(seed: int, R: int, F: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.standard_normal((R, F)).astype(np.float32) * 1e-3)
+
+
+def ulp_key(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> integers ordered like the values (both zeros -> 0)."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def assert_within_one_ulp(got: np.ndarray, ref: np.ndarray, what: str) -> None:
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    d = np.abs(ulp_key(got) - ulp_key(ref))
+    if d.size:
+        i = np.unravel_index(np.argmax(d), d.shape)
+        assert d.max() <= 1, f"{what}: {int((d > 1).sum())} elements beyond 1 bf16 ulp; worst at {i}: " \
+                             f"got {got[i]:#06x} ref {ref[i]:#06x}"
+        assert (d > 0).mean() < 0.01, f"{what}: {(d > 0).mean():.2%} of elements off by one ulp"
+
+
+SHAPES = [(7, 8), (33, 64), (129, 1408), (64, 2048), (17, 8192), (3, 16384), (2, 24576), (300, 520), (0, 64)]
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_swiglu_forward_parity(codec, shape):
+    R, F = shape
+    h1 = make_h1(10 + R + F, R, F)
+    note(f"swiglu fwd codec={codec} rows={R} F={F}")
+    a2, q, s = fm.swiglu_quantize_rowwise(bf16_dev(h1), codec)
+    a2h = host(a2)
+    assert_within_one_ulp(a2h, sw.swiglu_fwd(h1, F), "a2")
+    qr, sr = oracle.quantize_rowwise(a2h, codec)
+    assert_bytes_equal(host(q), qr, "a2 codes")
+    assert_f32_bits_equal(host(s), sr, "a2 scales")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_swiglu_backward_parity(codec, shape):
+    R, F = shape
+    h1 = make_h1(20 + R + F, R, F)
+    da2 = make_da2(30 + R + F, R, F)
+    note(f"swiglu bwd codec={codec} rows={R} F={F}")
+    dh1, q, s = fm.swiglu_backward_quantize_rowwise(bf16_dev(da2), bf16_dev(h1), codec)
+    dh1h = host(dh1)
+    assert_within_one_ulp(dh1h, sw.swiglu_bwd(da2, h1, F), "dh1")
+    qr, sr = oracle.quantize_rowwise(dh1h, codec)
+    assert_bytes_equal(host(q), qr, "dh1 codes")
+    assert_f32_bits_equal(host(s), sr, "dh1 scales")
+
+
+def test_swiglu_strided_h1():
+    R, F, LD = 65, 1408, 2 * 1408 + 40
+    rng = np.random.default_rng(6)
+    wide = bf16_bits(rng.standard_normal((R, LD)).astype(np.float32) * 2)
+    h1 = np.ascontiguousarray(wide[:, :2 * F])
+    da2 = make_da2(7, R, F)
+    wd = bf16_dev(wide)[:, :2 * F]                  # row stride LD > 2F
+    note("swiglu strided h1")
+    a2, q, s = fm.swiglu_quantize_rowwise(wd, fm.E4M3FN)
+    assert_within_one_ulp(host(a2), sw.swiglu_fwd(h1, F), "a2 (strided)")
+    qr, sr = oracle.quantize_rowwise(host(a2), fm.E4M3FN)
+    assert_bytes_equal(host(q), qr, "a2 codes (strided)")
+    dh1, q2, s2 = fm.swiglu_backward_quantize_rowwise(bf16_dev(da2), wd, fm.E4M3FN)
+    assert_within_one_ulp(host(dh1), sw.swiglu_bwd(da2, h1, F), "dh1 (strided)")
+    qr2, sr2 = oracle.quantize_rowwise(host(dh1), fm.E4M3FN)
+    assert_bytes_equal(host(q2), qr2, "dh1 codes (strided)")
+    assert_f32_bits_equal(host(s2), sr2, "dh1 scales (strided)")
+
+
+def test_swiglu_full_size_sampled():
+    """DeepSeek-V3-share shape (8192 routed rows, F = 2048) in the launch the
+    bench times; rows sampled for the oracle."""
+    R, F = 8192, 2048
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    h1 = (torch.randn(R, 2 * F, device=DEV, generator=gen) * 2).to(torch.bfloat16)
+    da2 = (torch.randn(R, F, device=DEV, generator=gen) * 1e-3).to(torch.bfloat16)
+    note("swiglu full size")
+    a2, q, s = fm.swiglu_quantize_rowwise(h1, fm.E4M3FN)
+    dh1, qb, sb = fm.swiglu_backward_quantize_rowwise(da2, h1, fm.E4M3FN)
+    rows = np.random.default_rng(12).choice(R, 96, replace=False)
+    h1h, dah = host(h1)[rows], host(da2)[rows]
+    a2h, dh1h = host(a2)[rows], host(dh1)[rows]
+    assert_within_one_ulp(a2h, sw.swiglu_fwd(h1h, F), "a2 sampled")
+    assert_within_one_ulp(dh1h, sw.swiglu_bwd(dah, h1h, F), "dh1 sampled")
+    qr, sr = oracle.quantize_rowwise(a2h, fm.E4M3FN)
+    assert_bytes_equal(host(q)[rows], qr, "a2 codes sampled")
+    assert_f32_bits_equal(host(s)[rows], sr, "a2 scales sampled")
+    qr, sr = oracle.quantize_rowwise(dh1h, fm.E4M3FN)
+    assert_bytes_equal(host(qb)[rows], qr, "dh1 codes sampled")
+    assert_f32_bits_equal(host(sb)[rows], sr, "dh1 scales sampled")
