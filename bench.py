@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--gw", action="store_true", help="config 2: add the BF16 wgrad variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swiglu", action="store_true",
+                    help="configs 3/4: also time the fused SwiGLU + rowwise quantization (forward and backward) "
+                         "on the layer's A2/dH1 shapes, outside the layer step")
     ap.add_argument("--no-per-kernel", action="store_true",
                     help="skip the flushed per-kernel pass and the clock sample (kernel traces of the steps alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -487,6 +490,40 @@ def observed_sclk(step, seconds=1.5):
     return box.get("mhz")
 
 
+def swiglu_extras(cfg: int, stream):
+    """The fused SwiGLU kernels on the layer's shapes (H1 [M, 2F], dA2 [M, F]; seeded normal inputs),
+    timed like kernels_flushed.  Not part of the layer step's call list."""
+    import torch
+    import mxfp8_quantized_moe_amd as fm
+    from mxfp8_quantized_moe_amd import synth
+    w = synth.WORKLOADS[cfg]
+    M, F = w.M, w.F
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(1000 * cfg + 7)
+    h1 = (torch.randn(M, 2 * F, device="cuda:0", generator=gen) * 2).to(torch.bfloat16)
+    da2 = (torch.randn(M, F, device="cuda:0", generator=gen) * 1e-3).to(torch.bfloat16)
+    a2 = torch.empty(M, F, dtype=torch.bfloat16, device="cuda:0")
+    qa = torch.empty(M, F, dtype=torch.uint8, device="cuda:0")
+    sa = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    dh1 = torch.empty(M, 2 * F, dtype=torch.bfloat16, device="cuda:0")
+    qd = torch.empty(M, 2 * F, dtype=torch.uint8, device="cuda:0")
+    sd = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    st = Step()
+    # algorithmic bytes: inputs read once, bf16 result and FP8 codes written once, one fp32 scale per row
+    st.add("swiglu+q A2", "quant", lambda: fm.swiglu_quantize_rowwise(h1, 0, a2=a2, q=qa, scale=sa),
+           M * (4 * F + 2 * F + F) + 4 * M)
+    st.add("swiglu bwd+q dH1", "quant", lambda: fm.swiglu_backward_quantize_rowwise(da2, h1, 0, dh1=dh1, q=qd,
+                                                                                    scale=sd),
+           M * (2 * F + 4 * F + 4 * F + 2 * F) + 4 * M)
+    t = per_kernel_flushed(st, stream)
+    out = {}
+    for name, _, _, work, _ in st.items:
+        med, p10, p90 = t[name]
+        out[name] = {"median_us": med, "p10_us": p10, "p90_us": p90, "GBps": round(work / med / 1e3, 1),
+                     "frac": round(work / med / 1e3 / PEAK_HBM_GBPS, 4), "rows": M, "F": F}
+    return out
+
+
 # ---------------------------------------------------------------------- main
 
 def main():
@@ -605,6 +642,8 @@ def main():
         "sclk_MHz_under_load": observed_sclk(step) if extras else None,
         "inputs": f"{N_ROTATE} device copies of every input, step s reads copy s % {N_ROTATE}",
     }
+    if args.swiglu and args.config in (3, 4):
+        out["swiglu_fused"] = swiglu_extras(args.config, stream)
     if not args.no_cpu_baseline and args.config == 2:
         out["cpu_baseline"] = cpu_baseline(args.config, host)
     else:
