@@ -89,6 +89,26 @@ def routing_counts(cfg: int) -> np.ndarray:
     raise ValueError(f"unknown workload {cfg}")
 
 
+def routing_ids(cfg: int):
+    """Per-token expert ids [tokens, topk] (int32) whose per-expert counts are
+    routing_counts(cfg): config 3 keeps its Gumbel top-6 draw; config 4 places
+    its multinomial counts on 8192 tokens with one expert each, in a seeded
+    random token order."""
+    if cfg == 3:
+        rng = np.random.Generator(np.random.PCG64(cfg))
+        rank = rng.permutation(64) + 1
+        p = rank.astype(np.float64) ** -1.1
+        p /= p.sum()
+        g = rng.gumbel(size=(8192, 64))
+        return np.argsort(-(np.log(p)[None, :] + g), axis=1)[:, :6].astype(np.int32)
+    if cfg == 4:
+        counts = routing_counts(4)
+        ids = np.repeat(np.arange(32, dtype=np.int32), counts)
+        rng = np.random.Generator(np.random.PCG64(10_000 + cfg))
+        return rng.permutation(ids).reshape(-1, 1).astype(np.int32)
+    raise ValueError(f"per-token routing is generated for configs 3 and 4, not {cfg}")
+
+
 def offsets_from_counts(counts) -> np.ndarray:
     return np.cumsum(np.asarray(counts, dtype=np.int64)).astype(np.int32)
 

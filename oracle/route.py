@@ -1,0 +1,78 @@
+"""MoE routing around the grouped GEMMs: token slots grouped by expert into
+offsets (optionally padded per group), the rows gathered into that grouped
+layout, and the expert outputs combined back per token.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The grouped GEMMs take their rows already grouped by expert, with an
+offsets tensor splitting them [P1 Details (the grouped GEMM over an offsets
+tensor); P4 "MoE" (tokens routed to experts, grouped GEMMs over the routed
+rows); P2 Details (groups padded to the MX block size)].  Readings the pages
+leave open, stated here and in the design notes:
+  * Slot i = t * topk + j is token t's j-th expert choice.  Within an expert
+    the slots keep their slot order (a stable grouping).
+  * Each group's row count may be rounded up to a multiple of `pad` (1: no
+    padding); padding rows hold zeros and come after the group's rows.
+  * An expert id outside [0, E) drops the slot: it is not counted, its
+    destination is -1 and it contributes nothing to the combine.
+  * combine: y[t] = sum over j = 0 .. topk-1, in that order, of
+    w[t, j] * yg[dest[t, j]], each product and each sum an IEEE fp32
+    operation (round to nearest), then rounded once to bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .quant import bf16_to_f32
+from .swiglu import round_bf16
+
+
+def rows_bound(slots: int, n_experts: int, pad: int) -> int:
+    """Most grouped rows a routing can need: every slot plus pad - 1 per group."""
+    return slots + n_experts * (pad - 1)
+
+
+def route(expert_ids: np.ndarray, n_experts: int, pad: int = 1):
+    """expert_ids [T, k] -> (counts [E], offs [E] inclusive padded cumsum, dest [T*k], src [rows_bound]).
+    src[r] is the slot whose row lands at grouped row r, -1 for padding and unused rows."""
+    ids = np.asarray(expert_ids, dtype=np.int64).ravel()
+    S = ids.size
+    valid = (ids >= 0) & (ids < n_experts)
+    counts = np.bincount(ids[valid], minlength=n_experts).astype(np.int64)
+    padded = (counts + pad - 1) // pad * pad
+    offs = np.cumsum(padded)
+    start = offs - padded
+    dest = np.full(S, -1, dtype=np.int64)
+    order = np.argsort(np.where(valid, ids, n_experts), kind="stable")   # valid slots by expert, slot order kept
+    first = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(n_experts):
+        slots = order[first[e]:first[e + 1]]
+        dest[slots] = start[e] + np.arange(counts[e])
+    src = np.full(rows_bound(S, n_experts, pad), -1, dtype=np.int64)
+    src[dest[valid]] = np.nonzero(valid)[0]
+    return (counts.astype(np.int32), offs.astype(np.int32), dest.astype(np.int32), src.astype(np.int32))
+
+
+def permute(x_bits: np.ndarray, src: np.ndarray, topk: int) -> np.ndarray:
+    """x [T, C] bf16 -> xg [len(src), C] bf16: row r is x[src[r] // topk], zeros where src[r] < 0."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    src = np.asarray(src, dtype=np.int64)
+    out = np.zeros((src.size, x.shape[1]), dtype=np.uint16)
+    used = src >= 0
+    out[used] = x[src[used] // topk]
+    return out
+
+
+def combine(yg_bits: np.ndarray, dest: np.ndarray, weights: np.ndarray, tokens: int, topk: int) -> np.ndarray:
+    """yg [rows, C] bf16, dest [T*k], weights [T, k] fp32 -> y [T, C] bf16 (the fp32 order above)."""
+    yg = bf16_to_f32(np.asarray(yg_bits, dtype=np.uint16))
+    dest = np.asarray(dest, dtype=np.int64).reshape(tokens, topk)
+    w = np.asarray(weights, dtype=np.float32).reshape(tokens, topk)
+    acc = np.zeros((tokens, yg.shape[1]), dtype=np.float32)
+    for j in range(topk):
+        d = dest[:, j]
+        ok = d >= 0
+        term = np.zeros_like(acc)
+        term[ok] = w[ok, j][:, None] * yg[d[ok]]          # fp32 products (numpy: IEEE, round to nearest)
+        acc = np.where(ok[:, None], acc + term, acc)       # fp32 sums in slot order
+    return round_bf16(acc.astype(np.float64))
