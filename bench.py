@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--swiglu", action="store_true",
                     help="configs 3/4: also time the fused SwiGLU + rowwise quantization (forward and backward) "
                          "on the layer's A2/dH1 shapes, outside the layer step")
+    ap.add_argument("--route", action="store_true",
+                    help="configs 3/4: also time the routing kernels (route, permute of X into the grouped layout, "
+                         "combine of the grouped output) on the layer's routing and hidden size, outside the layer step")
     ap.add_argument("--no-per-kernel", action="store_true",
                     help="skip the flushed per-kernel pass and the clock sample (kernel traces of the steps alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -524,6 +527,44 @@ def swiglu_extras(cfg: int, stream):
     return out
 
 
+def route_extras(cfg: int, stream):
+    """The routing kernels on the layer's per-token routing (tokens x topk ids over E experts, no
+    padding) and hidden size H: route, permute of X [T, H] into the grouped rows, combine of a grouped
+    output [rows, H] back to [T, H]; timed like kernels_flushed.  Not part of the layer step."""
+    import torch
+    import mxfp8_quantized_moe_amd as fm
+    from mxfp8_quantized_moe_amd import synth
+    w = synth.WORKLOADS[cfg]
+    ids_h = synth.routing_ids(cfg)
+    T, k = ids_h.shape
+    S, H, E = T * k, w.H, w.E
+    ids = torch.from_numpy(ids_h).to("cuda:0")
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(1000 * cfg + 11)
+    x = torch.randn(T, H, device="cuda:0", generator=gen).to(torch.bfloat16)
+    wts = torch.rand(T, k, device="cuda:0", generator=gen)
+    counts, offs, dest, src = fm.moe_route(ids, E, 1)
+    R = src.numel()
+    ws = torch.empty(max(int(fm._lib.lib().moe_route_workspace_bytes(S, E)), 4), dtype=torch.uint8, device="cuda:0")
+    xg = fm.moe_permute(x, src, k)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda:0")
+    st = Step()
+    # algorithmic bytes: ids read once, dest and src written once (plus counts and offsets)
+    st.add("route", "route", lambda: fm.moe_route(ids, E, 1, out=(counts, offs, dest, src), workspace=ws),
+           4 * S + 4 * S + 4 * R + 8 * E)
+    # X read once, the grouped rows and src once
+    st.add("permute X", "route", lambda: fm.moe_permute(x, src, k, xg=xg), 2 * T * H + 2 * R * H + 4 * R)
+    # every grouped row read once, dest and weights once, Y written once
+    st.add("combine Y", "route", lambda: fm.moe_combine(xg, dest, wts, k, y=y), 2 * R * H + 8 * S + 2 * T * H)
+    t = per_kernel_flushed(st, stream)
+    out = {}
+    for name, _, _, work, _ in st.items:
+        med, p10, p90 = t[name]
+        out[name] = {"median_us": med, "p10_us": p10, "p90_us": p90, "GBps": round(work / med / 1e3, 1),
+                     "frac": round(work / med / 1e3 / PEAK_HBM_GBPS, 4), "tokens": T, "topk": k, "E": E, "H": H}
+    return out
+
+
 # ---------------------------------------------------------------------- main
 
 def main():
@@ -644,6 +685,8 @@ def main():
     }
     if args.swiglu and args.config in (3, 4):
         out["swiglu_fused"] = swiglu_extras(args.config, stream)
+    if args.route and args.config in (3, 4):
+        out["routing"] = route_extras(args.config, stream)
     if not args.no_cpu_baseline and args.config == 2:
         out["cpu_baseline"] = cpu_baseline(args.config, host)
     else:

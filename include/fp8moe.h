@@ -165,6 +165,69 @@ int swiglu_backward_quantize_rowwise(const void *da2_bf16, const void *h1_bf16, 
                                      void *q, float *scale, void *stream);
 
 /*
+ * moe_route -- group the token slots of a top-k routing by expert: per-expert
+ * counts, the offsets tensor the grouped GEMMs take, and for every slot the
+ * grouped row it lands in (and the inverse map).
+ *   [P1 Details (the grouped GEMM over token groups split by an offsets
+ *   tensor); P4 "MoE" (tokens routed to experts, grouped GEMMs over the routed
+ *   rows); P2 Details (groups padded to the MX block size).]
+ *   Slot i = t*topk + j is token t's j-th choice.  Within an expert the slots
+ *   keep their order (a stable grouping); each group's row count is rounded up
+ *   to a multiple of `pad` (1: no padding), its padding rows after its slots.
+ *   An id outside [0, n_experts) drops its slot: not counted, dest -1.
+ *   expert_ids  int32 [tokens][topk]
+ *   counts      int32 [n_experts]   valid slots per expert (written)
+ *   offs        int32 [n_experts]   inclusive cumsum of the padded counts (written)
+ *   dest        int32 [tokens*topk] grouped row of each slot, or -1 (written)
+ *   src         int32 [moe_route_rows_bound(...)]  slot whose row lands at each
+ *               grouped row; -1 for padding and for rows past offs[n_experts-1] (written)
+ *   workspace   device memory of moe_route_workspace_bytes(tokens*topk, n_experts)
+ *               bytes, owned by the caller; contents on entry do not matter
+ *   Requires: tokens >= 0, topk >= 1, 1 <= n_experts, pad >= 1, tokens*topk and
+ *   the rows bound within int32; int32 pointers 4-byte aligned.  More than
+ *   1024 experts: FP8MOE_ERR_UNSUPPORTED.  Three kernels, no allocation.
+ */
+int moe_route(const int32_t *expert_ids, int64_t tokens, int32_t topk, int32_t n_experts,
+              int32_t pad, int32_t *counts, int32_t *offs, int32_t *dest, int32_t *src,
+              void *workspace, void *stream);
+
+/* Workspace bytes moe_route needs for `slots` = tokens*topk slots (-1: invalid sizes). */
+int64_t moe_route_workspace_bytes(int64_t slots, int32_t n_experts);
+
+/* Most grouped rows a routing of `slots` slots can need: slots + n_experts*(pad-1)
+ * (-1: invalid sizes or beyond int32).  The length of moe_route's src. */
+int64_t moe_route_rows_bound(int64_t slots, int32_t n_experts, int32_t pad);
+
+/*
+ * moe_permute -- gather token rows into the grouped layout.
+ *   [as moe_route]
+ *   x      bf16 [tokens][cols]
+ *   src    int32 [rows_out]   as written by moe_route
+ *   xg     bf16 [rows_out][cols]  row r = x[src[r] / topk], zeros where src[r] < 0
+ *          or src[r] >= tokens*topk (written)
+ *   Requires: cols % 8 == 0; x and xg 16-byte aligned, src 4-byte aligned.
+ */
+int moe_permute(const void *x_bf16, int64_t tokens, int64_t cols, int32_t topk,
+                const int32_t *src, int64_t rows_out, void *xg_bf16, void *stream);
+
+/*
+ * moe_combine -- weighted sum of each token's expert outputs.
+ *   [P4 "MoE" (the routed experts' outputs summed per token with the router's
+ *   weights).]
+ *   yg       bf16 [rows_in][cols]  expert outputs in the grouped layout
+ *   dest     int32 [tokens*topk]   as written by moe_route; a slot whose dest
+ *                                  is < 0 or >= rows_in contributes nothing
+ *   weights  f32 [tokens][topk]
+ *   y        bf16 [tokens][cols]   y[t] = sum over j in order 0..topk-1 of
+ *            weights[t][j] * yg[dest[t*topk+j]], each product and sum one fp32
+ *            operation rounded to nearest, then rounded to bf16 (nearest even) (written)
+ *   Requires: cols % 8 == 0; yg and y 16-byte aligned, dest and weights 4-byte aligned.
+ */
+int moe_combine(const void *yg_bf16, int64_t rows_in, const int32_t *dest,
+                const float *weights, int64_t tokens, int32_t topk, int64_t cols,
+                void *y_bf16, void *stream);
+
+/*
  * quantize_colwise -- one fp32 scale per (group, column), reduced over the
  * group's rows, with the FP8 output written transposed (contraction-contiguous)
  * so the backward GEMMs read it directly, with no separate transpose copy.

@@ -21,7 +21,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
-           "swiglu_backward_quantize_rowwise"]
+           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine"]
 
 
 def _ptr(t):
@@ -177,6 +177,56 @@ def swiglu_backward_quantize_rowwise(da2, h1, codec=E4M3FN, dh1=None, q=None, sc
     _lib.check("swiglu_backward_quantize_rowwise", _lib.lib().swiglu_backward_quantize_rowwise(
         _ptr(da2), _ptr(h1), R, F, ld, codec, _ptr(dh1), _ptr(q), _ptr(scale), _stream(stream)))
     return dh1, q, scale
+
+
+def moe_route_rows_bound(slots: int, n_experts: int, pad: int = 1) -> int:
+    return int(_lib.lib().moe_route_rows_bound(slots, n_experts, pad))
+
+
+def moe_route(expert_ids, n_experts, pad=1, out=None, workspace=None, stream=None):
+    """expert_ids int32 [T, k] -> (counts [E], offs [E], dest [T*k], src [rows bound]), all int32."""
+    ids = expert_ids.contiguous()
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("moe_route needs int32 expert ids of shape [tokens, topk]")
+    T, k = ids.shape
+    rows = moe_route_rows_bound(T * k, n_experts, pad)
+    ws = int(_lib.lib().moe_route_workspace_bytes(T * k, n_experts))
+    if rows < 0 or ws < 0:
+        raise ValueError(f"moe_route: invalid sizes tokens={T} topk={k} experts={n_experts} pad={pad}")
+    dev = ids.device
+    if out is None:
+        out = (torch.empty(n_experts, dtype=torch.int32, device=dev), torch.empty(n_experts, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev), torch.empty(rows, dtype=torch.int32, device=dev))
+    counts, offs, dest, src = out
+    if workspace is None:
+        workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=dev)
+    _lib.check("moe_route", _lib.lib().moe_route(_ptr(ids), T, k, n_experts, pad, _ptr(counts), _ptr(offs),
+                                                  _ptr(dest), _ptr(src), _ptr(workspace), _stream(stream)))
+    return counts, offs, dest, src
+
+
+def moe_permute(x, src, topk, xg=None, stream=None):
+    """x bf16 [T, C], src int32 [R] -> xg bf16 [R, C]: row r = x[src[r] // topk], zeros where src[r] < 0."""
+    x = _bits(x).contiguous()
+    T, C = x.shape
+    R = src.numel()
+    xg = torch.empty((R, C), dtype=x.dtype, device=x.device) if xg is None else xg
+    _lib.check("moe_permute", _lib.lib().moe_permute(_ptr(x), T, C, topk, _ptr(src), R, _ptr(xg), _stream(stream)))
+    return xg
+
+
+def moe_combine(yg, dest, weights, topk, y=None, stream=None):
+    """yg bf16 [R, C], dest int32 [T*k], weights f32 [T, k] -> y bf16 [T, C]."""
+    yg = _bits(yg).contiguous()
+    R, C = yg.shape
+    weights = weights.contiguous()
+    T = weights.shape[0]
+    if weights.dtype != torch.float32 or tuple(weights.shape) != (T, topk) or dest.numel() != T * topk:
+        raise ValueError("moe_combine: weights f32 [T, topk] and dest [T*topk]")
+    y = torch.empty((T, C), dtype=yg.dtype, device=yg.device) if y is None else y
+    _lib.check("moe_combine", _lib.lib().moe_combine(_ptr(yg), R, _ptr(dest), _ptr(weights), T, topk, C, _ptr(y),
+                                                     _stream(stream)))
+    return y
 
 
 def encode_f32(y, codec=E4M3FN, q=None, stream=None):

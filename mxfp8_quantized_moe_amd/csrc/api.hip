@@ -58,6 +58,40 @@ int swiglu_backward_quantize_rowwise(const void* da2_bf16, const void* h1_bf16, 
       static_cast<uint16_t*>(dh1_bf16), static_cast<uint8_t*>(q), scale, as_stream(stream)));
 }
 
+int64_t moe_route_workspace_bytes(int64_t slots, int32_t n_experts) {
+  return route_workspace_bytes(slots, n_experts);
+}
+
+int64_t moe_route_rows_bound(int64_t slots, int32_t n_experts, int32_t pad) {
+  return route_rows_bound(slots, n_experts, pad);
+}
+
+int moe_route(const int32_t* expert_ids, int64_t tokens, int32_t topk, int32_t n_experts, int32_t pad,
+              int32_t* counts, int32_t* offs, int32_t* dest, int32_t* src, void* workspace, void* stream) {
+  const int st = check_moe_route(expert_ids, tokens, topk, n_experts, pad, counts, offs, dest, src, workspace);
+  if (st) return st;
+  const int64_t S = tokens * topk;
+  return launch_status(launch_moe_route(expert_ids, S, n_experts, pad, counts, offs, dest, src,
+                                        route_rows_bound(S, n_experts, pad), static_cast<int32_t*>(workspace),
+                                        as_stream(stream)));
+}
+
+int moe_permute(const void* x_bf16, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src, int64_t rows_out,
+                void* xg_bf16, void* stream) {
+  const int st = check_moe_permute(x_bf16, tokens, cols, topk, src, rows_out, xg_bf16);
+  if (st) return st;
+  return launch_status(launch_moe_permute(static_cast<const uint16_t*>(x_bf16), tokens, cols, topk, src, rows_out,
+                                          static_cast<uint16_t*>(xg_bf16), as_stream(stream)));
+}
+
+int moe_combine(const void* yg_bf16, int64_t rows_in, const int32_t* dest, const float* weights, int64_t tokens,
+                int32_t topk, int64_t cols, void* y_bf16, void* stream) {
+  const int st = check_moe_combine(yg_bf16, rows_in, dest, weights, tokens, topk, cols, y_bf16);
+  if (st) return st;
+  return launch_status(launch_moe_combine(static_cast<const uint16_t*>(yg_bf16), rows_in, dest, weights, tokens, topk,
+                                          cols, static_cast<uint16_t*>(y_bf16), as_stream(stream)));
+}
+
 int quantize_colwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                      int32_t n_groups, int codec, void* q_t, int64_t ld_q, float* scale, void* stream) {
   const int st = check_quantize_colwise(x_bf16, batch, rows, cols, offs, n_groups, codec, q_t, ld_q, scale);

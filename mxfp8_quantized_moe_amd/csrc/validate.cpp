@@ -163,6 +163,54 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
   return FP8MOE_OK;
 }
 
+int64_t route_rows_bound(int64_t slots, int32_t n_experts, int32_t pad) {
+  if (slots < 0 || n_experts < 1 || pad < 1) return -1;
+  const int64_t r = slots + (int64_t)n_experts * (pad - 1);
+  return r > kI32Max ? -1 : r;
+}
+
+int64_t route_workspace_bytes(int64_t slots, int32_t n_experts) {
+  if (slots < 0 || slots > kI32Max || n_experts < 1) return -1;
+  return route_blocks(slots) * n_experts * 4;
+}
+
+int check_moe_route(const int32_t* ids, int64_t tokens, int32_t topk, int32_t E, int32_t pad, const int32_t* counts,
+                    const int32_t* offs, const int32_t* dest, const int32_t* src, const void* workspace) {
+  if (tokens < 0 || topk < 1 || E < 1 || pad < 1) return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk);
+  if (S < 0 || S > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t rows = route_rows_bound(S, E, pad);
+  if (rows < 0) return FP8MOE_ERR_SHAPE;   // grouped rows must fit int32
+  if (E > kRouteMaxExperts) return FP8MOE_ERR_UNSUPPORTED;
+  if (!need(ids, S) || !counts || !offs || !need(dest, S) || !need(src, rows) || !need(workspace, S))
+    return FP8MOE_ERR_NULL;
+  if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offs, 4) || !aligned(dest, 4) || !aligned(src, 4) ||
+      !aligned(workspace, 4))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_moe_permute(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                      int64_t rows_out, const void* xg) {
+  if (tokens < 0 || cols < 0 || topk < 1 || rows_out < 0 || rows_out > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk), nx = mul(tokens, cols), ng = mul(rows_out, cols);
+  if (S < 0 || S > kI32Max || nx < 0 || ng < 0) return FP8MOE_ERR_SHAPE;
+  if (!need(x, nx) || !need(src, rows_out) || !need(xg, ng)) return FP8MOE_ERR_NULL;
+  if (cols % 8 || !aligned(x, 16) || !aligned(xg, 16) || !aligned(src, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_moe_combine(const void* yg, int64_t rows_in, const int32_t* dest, const float* w, int64_t tokens,
+                      int32_t topk, int64_t cols, const void* y) {
+  if (tokens < 0 || cols < 0 || topk < 1 || rows_in < 0 || rows_in > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk), ny = mul(tokens, cols), ng = mul(rows_in, cols);
+  if (S < 0 || S > kI32Max || ny < 0 || ng < 0) return FP8MOE_ERR_SHAPE;
+  const int64_t work = cols ? S : 0;   // nothing is read when there are no columns
+  if (!need(yg, cols ? ng : 0) || !need(dest, work) || !need(w, work) || !need(y, ny)) return FP8MOE_ERR_NULL;
+  if (cols % 8 || !aligned(yg, 16) || !aligned(y, 16) || !aligned(dest, 4) || !aligned(w, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_encode_f32(const void* y, int64_t n, int codec, const void* q) {
   if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
   if (n < 0 || n > kI32Max * 64LL) return FP8MOE_ERR_SHAPE;

@@ -25,4 +25,19 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
 
 int64_t mx_rows_bound(int64_t rows, int32_t n_groups);
 
+// Routing: slots per block of the histogram and rank launches, and the most
+// experts one route call takes (one workgroup scans them).
+constexpr int kRouteSlots = 256;
+constexpr int kRouteMaxExperts = 1024;
+inline int64_t route_blocks(int64_t slots) { return (slots + kRouteSlots - 1) / kRouteSlots; }
+// Workspace bytes of a route call, rows of its grouped layout; -1 for invalid sizes.
+int64_t route_workspace_bytes(int64_t slots, int32_t n_experts);
+int64_t route_rows_bound(int64_t slots, int32_t n_experts, int32_t pad);
+int check_moe_route(const int32_t* ids, int64_t tokens, int32_t topk, int32_t E, int32_t pad, const int32_t* counts,
+                    const int32_t* offs, const int32_t* dest, const int32_t* src, const void* workspace);
+int check_moe_permute(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                      int64_t rows_out, const void* xg);
+int check_moe_combine(const void* yg, int64_t rows_in, const int32_t* dest, const float* w, int64_t tokens,
+                      int32_t topk, int64_t cols, const void* y);
+
 }  // namespace fp8moe

@@ -98,6 +98,55 @@ def test_swiglu_rejections(lib):
     assert b(None, None, 0, 16, 32, 0, None, None, None, None) == L.OK
 
 
+def test_route_rejections(lib):
+    r = lib.moe_route        # (ids, tokens, topk, E, pad, counts, offs, dest, src, workspace, stream)
+    assert r(P, -1, 2, 8, 1, P, P, P, P, P, None) == L.ERR_SHAPE
+    assert r(P, 4, 0, 8, 1, P, P, P, P, P, None) == L.ERR_SHAPE     # topk 0
+    assert r(P, 4, 2, 0, 1, P, P, P, P, P, None) == L.ERR_SHAPE     # no experts
+    assert r(P, 4, 2, 8, 0, P, P, P, P, P, None) == L.ERR_SHAPE     # pad 0
+    assert r(P, 1 << 30, 4, 8, 1, P, P, P, P, P, None) == L.ERR_SHAPE  # slots beyond int32
+    assert r(P, 4, 2, 8, 1 << 29, P, P, P, P, P, None) == L.ERR_SHAPE  # rows bound beyond int32
+    assert r(P, 4, 2, 1025, 1, P, P, P, P, P, None) == L.ERR_UNSUPPORTED
+    assert r(None, 4, 2, 8, 1, P, P, P, P, P, None) == L.ERR_NULL
+    assert r(P, 4, 2, 8, 1, None, P, P, P, P, None) == L.ERR_NULL
+    assert r(P, 4, 2, 8, 1, P, None, P, P, P, None) == L.ERR_NULL
+    assert r(P, 4, 2, 8, 1, P, P, None, P, P, None) == L.ERR_NULL
+    assert r(P, 4, 2, 8, 1, P, P, P, None, P, None) == L.ERR_NULL
+    assert r(P, 4, 2, 8, 1, P, P, P, P, None, None) == L.ERR_NULL
+    assert r(P + 2, 4, 2, 8, 1, P, P, P, P, P, None) == L.ERR_ALIGN
+    assert r(P, 4, 2, 8, 1, P, P, P + 2, P, P, None) == L.ERR_ALIGN
+    assert r(P, 4, 2, 8, 1, P, P, P, P, P + 1, None) == L.ERR_ALIGN
+    assert lib.moe_route_rows_bound(100, 8, 32) == 100 + 8 * 31
+    assert lib.moe_route_rows_bound(100, 0, 1) == -1 and lib.moe_route_rows_bound(-1, 8, 1) == -1
+    assert lib.moe_route_rows_bound((1 << 31) - 8, 8, 2) == -1
+    assert lib.moe_route_workspace_bytes(0, 8) == 0
+    assert lib.moe_route_workspace_bytes(1, 8) == lib.moe_route_workspace_bytes(256, 8) > 0
+    assert lib.moe_route_workspace_bytes(257, 8) == 2 * lib.moe_route_workspace_bytes(256, 8)
+    p = lib.moe_permute      # (x, tokens, cols, topk, src, rows_out, xg, stream)
+    assert p(P, -1, 16, 2, P, 8, P, None) == L.ERR_SHAPE
+    assert p(P, 4, 16, 0, P, 8, P, None) == L.ERR_SHAPE
+    assert p(P, 4, 16, 2, P, -1, P, None) == L.ERR_SHAPE
+    assert p(None, 4, 16, 2, P, 8, P, None) == L.ERR_NULL
+    assert p(P, 4, 16, 2, None, 8, P, None) == L.ERR_NULL
+    assert p(P, 4, 16, 2, P, 8, None, None) == L.ERR_NULL
+    assert p(P, 4, 12, 2, P, 8, P, None) == L.ERR_ALIGN             # cols % 8
+    assert p(MIS, 4, 16, 2, P, 8, P, None) == L.ERR_ALIGN
+    assert p(P, 4, 16, 2, P, 8, MIS, None) == L.ERR_ALIGN
+    assert p(None, 0, 16, 2, None, 0, None, None) == L.OK          # nothing to do
+    c = lib.moe_combine      # (yg, rows_in, dest, weights, tokens, topk, cols, y, stream)
+    assert c(P, 8, P, P, -1, 2, 16, P, None) == L.ERR_SHAPE
+    assert c(P, -1, P, P, 4, 2, 16, P, None) == L.ERR_SHAPE
+    assert c(P, 8, P, P, 4, 0, 16, P, None) == L.ERR_SHAPE
+    assert c(None, 8, P, P, 4, 2, 16, P, None) == L.ERR_NULL
+    assert c(P, 8, None, P, 4, 2, 16, P, None) == L.ERR_NULL
+    assert c(P, 8, P, None, 4, 2, 16, P, None) == L.ERR_NULL
+    assert c(P, 8, P, P, 4, 2, 16, None, None) == L.ERR_NULL
+    assert c(P, 8, P, P, 4, 2, 12, P, None) == L.ERR_ALIGN
+    assert c(MIS, 8, P, P, 4, 2, 16, P, None) == L.ERR_ALIGN
+    assert c(P, 8, P, P + 2, 4, 2, 16, P, None) == L.ERR_ALIGN
+    assert c(None, 0, None, None, 0, 2, 16, None, None) == L.OK    # nothing to do
+
+
 def test_colwise_rejections(lib):
     f = lib.quantize_colwise
     assert f(P, 1, 64, 16, P, 4, 3, P, 64, P, None) == L.ERR_ENUM
