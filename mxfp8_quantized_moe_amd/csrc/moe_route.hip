@@ -12,13 +12,14 @@
 // product and sum one fp32 operation rounded to nearest, then rounds to bf16.
 //
 // route: three launches on the caller's workspace (one int per block of
-// kRouteSlots slots and expert): per-block expert histograms (LDS atomics);
-// one workgroup turns them into running counts over blocks (the rows of each
-// expert in earlier blocks), the counts, the padded inclusive scan over
-// experts (offs), and sets every source entry to -1; one wave per block then
-// ranks its slots stably (lanes by shuffles, earlier passes by a per-expert
-// running count in LDS) and writes destinations and sources, a slot's row
-// being its group's start + the earlier blocks' rows + its rank in the block.
+// kRouteSlots slots and expert): per-block expert histograms (LDS atomics;
+// the same grid sets every source entry to -1); one workgroup turns them into
+// running counts over blocks (the rows of each expert in earlier blocks), the
+// counts and the padded inclusive scan over experts (offs); one wave per block
+// then ranks its slots stably (same-expert lanes found by ballots over the
+// id's bits, earlier passes by a per-expert running row in LDS) and writes
+// destinations and sources, a slot's row being its group's start + the
+// earlier blocks' rows + its rank in the block.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -26,9 +27,12 @@
 namespace fp8moe {
 
 static_assert(kRouteSlots % 64 == 0, "the rank kernel walks a block in whole waves");
+static_assert(kRouteMaxExperts == 1024, "the scan kernel runs one thread per (expert, range) in 1024");
 
+// Per-block histograms; the grid also sets every source entry to -1.
 __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
-                                                         int32_t* __restrict__ hist) {
+                                                         int32_t* __restrict__ hist, int32_t* __restrict__ src,
+                                                         int64_t rows_bound) {
   __shared__ int h[kRouteMaxExperts];
   const int t = threadIdx.x;
   for (int e = t; e < E; e += 256) h[e] = 0;
@@ -41,78 +45,122 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restri
       if (e >= 0 && e < E) atomicAdd(&h[e], 1);
     }
   }
+  for (int64_t r = (int64_t)blockIdx.x * 256 + t; r < rows_bound; r += (int64_t)gridDim.x * 256) src[r] = -1;
   __syncthreads();
   for (int e = t; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nb, int E, int pad,
+// One workgroup: P threads per expert (P a power of two, P * E <= 1024) each
+// take a range of blocks; hist[b][e] becomes the rows of e in blocks before b.
+// Then counts, and offs = the inclusive scan of the padded counts.  With no
+// slots (nb == 0) the histogram launch did not run and src is filled here.
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nb, int E, int P, int pad,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offs,
                                                           int32_t* __restrict__ src, int64_t rows_bound) {
+  __shared__ int part[kRouteMaxExperts];
   __shared__ int sc[kRouteMaxExperts];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    int b = 0;
-    for (; b + 4 <= nb; b += 4) {   // four independent loads in flight
+  const int t = threadIdx.x;
+  const int e = t / P, q = t % P;
+  const bool mine = e < E;
+  const int chunk = (nb + P - 1) / P;
+  const int b0 = min(q * chunk, nb), b1 = min(b0 + chunk, nb);
+  int sum = 0;
+  if (mine) {
+    int b = b0;
+    for (; b + 4 <= b1; b += 4) {
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = hist[(int64_t)(b + u) * E + e];
+      sum += c[0] + c[1] + c[2] + c[3];
+    }
+    for (; b < b1; ++b) sum += hist[(int64_t)b * E + e];
+  }
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < P; off <<= 1) {   // inclusive scan within each expert's P ranges
+    const int v = q >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  if (mine) {
+    int run = part[t] - sum;   // rows of e in blocks before b0
+    int b = b0;
+    for (; b + 4 <= b1; b += 4) {
       int c[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) c[u] = hist[(int64_t)(b + u) * E + e];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        hist[(int64_t)(b + u) * E + e] = run;   // rows of e in blocks before b + u
+        hist[(int64_t)(b + u) * E + e] = run;
         run += c[u];
       }
     }
-    for (; b < nb; ++b) {
+    for (; b < b1; ++b) {
       const int c = hist[(int64_t)b * E + e];
       hist[(int64_t)b * E + e] = run;
       run += c;
     }
   }
-  const int padded = e < E ? (run + pad - 1) / pad * pad : 0;
-  sc[e] = padded;
+  const int total = t < E ? part[t * P + P - 1] : 0;
+  const int padded = (total + pad - 1) / pad * pad;
+  __syncthreads();
+  sc[t] = padded;
   __syncthreads();
   for (int off = 1; off < kRouteMaxExperts; off <<= 1) {   // inclusive scan over experts
-    const int v = e >= off ? sc[e - off] : 0;
+    const int v = t >= off ? sc[t - off] : 0;
     __syncthreads();
-    sc[e] += v;
+    sc[t] += v;
     __syncthreads();
   }
-  if (e < E) {
-    counts[e] = run;
-    offs[e] = sc[e];
+  if (t < E) {
+    counts[t] = total;
+    offs[t] = sc[t];
   }
-  for (int64_t r = e; r < rows_bound; r += kRouteMaxExperts) src[r] = -1;
+  if (nb == 0)
+    for (int64_t r = t; r < rows_bound; r += kRouteMaxExperts) src[r] = -1;
 }
 
-// One wave per block of kRouteSlots slots.
-__global__ __launch_bounds__(64) void route_rank_kernel(const int32_t* __restrict__ ids, int64_t S, int E, int pad,
-                                                        const int32_t* __restrict__ base,
+// One wave per block of kRouteSlots slots, in passes of 64.  In a pass, the
+// lanes holding the same expert are found from `nbits` ballots over the bits
+// of the id; a slot's rank is the number of such lanes below it, and the last
+// of them advances the expert's running row in LDS.
+__global__ __launch_bounds__(64) void route_rank_kernel(const int32_t* __restrict__ ids, int64_t S, int E, int nbits,
+                                                        int pad, const int32_t* __restrict__ base,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offs,
                                                         int32_t* __restrict__ dest, int32_t* __restrict__ src,
                                                         int64_t rows_bound) {
+  constexpr int NP = kRouteSlots / 64;
   __shared__ int run[kRouteMaxExperts];   // group start + earlier blocks' rows + this block's earlier passes
   const int lane = threadIdx.x;
+  const int64_t s0 = (int64_t)blockIdx.x * kRouteSlots;
+  int ev[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t s = s0 + p * 64 + lane;
+    ev[p] = s < S ? ids[s] : -1;
+  }
   const int32_t* __restrict__ bb = base + (int64_t)blockIdx.x * E;
   for (int e = lane; e < E; e += 64) run[e] = offs[e] - (counts[e] + pad - 1) / pad * pad + bb[e];
   __syncthreads();
-  const int64_t s0 = (int64_t)blockIdx.x * kRouteSlots;
-  for (int p = 0; p < kRouteSlots / 64; ++p) {
-    const int64_t s = s0 + p * 64 + lane;
-    const int e = s < S ? ids[s] : -1;
+  const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int e = ev[p];
     const bool valid = e >= 0 && e < E;
-    // earlier and later lanes of this pass with the same expert
-    int before = 0, after = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j, 64);
-      before += (j < lane && ej == e) ? 1 : 0;
-      after += (j > lane && ej == e) ? 1 : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
     }
-    int d = -1;
-    if (valid) d = run[e] + before;   // every lane reads run[] before any lane updates it
+    const int before = __popcll(peers & below);
+    const bool last = ((peers >> lane) >> 1) == 0;
+    const int d = valid ? run[e] + before : -1;   // every lane reads run[] before any lane updates it
     __syncthreads();
-    if (valid && after == 0) run[e] += before + 1;
+    if (valid && last) run[e] = d + 1;
+    const int64_t s = s0 + p * 64 + lane;
     if (s < S) dest[s] = d;
     if (valid && d < rows_bound) src[d] = (int32_t)s;   // always true when ids do not change under the call
     __syncthreads();
@@ -125,60 +173,95 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint16_t* __restrict
                                                       int topk, const int32_t* __restrict__ src,
                                                       uint16_t* __restrict__ xg) {
   const int64_t r = blockIdx.x;
+  const int64_t nc = cols >> 3;
   const int s = src[r];
   u32x4* __restrict__ out = reinterpret_cast<u32x4*>(xg + r * cols);
   if (s >= 0 && (int64_t)s < tokens * topk) {
     const u32x4* __restrict__ in = reinterpret_cast<const u32x4*>(x + (int64_t)(s / topk) * cols);
-    for (int64_t c = threadIdx.x; c < (cols >> 3); c += 256) out[c] = in[c];
+    int64_t c = threadIdx.x;
+    for (; c + 768 < nc; c += 1024) {   // four 16-byte loads in flight per thread on long rows
+      const u32x4 v0 = in[c], v1 = in[c + 256], v2 = in[c + 512], v3 = in[c + 768];
+      out[c] = v0;
+      out[c + 256] = v1;
+      out[c + 512] = v2;
+      out[c + 768] = v3;
+    }
+    for (; c < nc; c += 256) out[c] = in[c];
   } else {
-    for (int64_t c = threadIdx.x; c < (cols >> 3); c += 256) out[c] = u32x4{0, 0, 0, 0};
+    for (int64_t c = threadIdx.x; c < nc; c += 256) out[c] = u32x4{0, 0, 0, 0};
   }
 }
 
 typedef float rt_f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 rt_bf16x2 __attribute__((ext_vector_type(2)));
 
-// One workgroup per token: y[t] = sum_j w[t, j] * yg[dest[t, j]] in slot order.
+// One workgroup per token: y[t] = sum_j w[t, j] * yg[dest[t, j]] in slot
+// order.  A thread loads its chunk of up to eight rows before summing (a
+// dropped slot loads row 0 and its result is not taken).
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ yg, int64_t rows_in,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ w, int topk, int64_t cols,
                                                       uint16_t* __restrict__ y) {
 #pragma clang fp contract(off)   // a product and the sum it enters round separately (no FMA)
+  constexpr int KB = 8;          // slots per batch of loads
   const int64_t t = blockIdx.x;
+  const int64_t nc = cols >> 3;
   const int32_t* __restrict__ dt = dest + t * topk;
   const float* __restrict__ wt = w + t * topk;
-  for (int64_t c = threadIdx.x; c < (cols >> 3); c += 256) {
+  u32x4* __restrict__ out = reinterpret_cast<u32x4*>(y + t * cols);
+  for (int64_t c = threadIdx.x; c < nc; c += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < topk; ++j) {
-      const int d = dt[j];
-      if (d < 0 || (int64_t)d >= rows_in) continue;   // a dropped slot
-      const float wj = wt[j];
-      const u32x4 v = reinterpret_cast<const u32x4*>(yg + (int64_t)d * cols)[c];
-      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    for (int j0 = 0; j0 < topk; j0 += KB) {
+      u32x4 v[KB];
+      bool ok[KB];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[2 * k] = acc[2 * k] + wj * bf16_lo(vw[k]);
-        acc[2 * k + 1] = acc[2 * k + 1] + wj * bf16_hi(vw[k]);
+      for (int u = 0; u < KB; ++u) {   // the guards are uniform over the wave
+        const int j = j0 + u;
+        ok[u] = false;
+        v[u] = u32x4{0, 0, 0, 0};
+        if (j < topk) {
+          const int d = dt[j];
+          ok[u] = d >= 0 && (int64_t)d < rows_in;
+          if (rows_in > 0) v[u] = reinterpret_cast<const u32x4*>(yg + (int64_t)(ok[u] ? d : 0) * cols)[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (j0 + u >= topk) break;
+        const float wj = wt[j0 + u];
+        const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float s0 = acc[2 * k] + wj * bf16_lo(vw[k]);
+          const float s1 = acc[2 * k + 1] + wj * bf16_hi(vw[k]);
+          acc[2 * k] = ok[u] ? s0 : acc[2 * k];
+          acc[2 * k + 1] = ok[u] ? s1 : acc[2 * k + 1];
+        }
       }
     }
     uint32_t o[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rt_f32x2{acc[2 * k], acc[2 * k + 1]}, rt_bf16x2));
-    reinterpret_cast<u32x4*>(y + t * cols)[c] = u32x4{o[0], o[1], o[2], o[3]};
+    out[c] = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t S, int E, int pad, int32_t* counts, int32_t* offs,
                             int32_t* dest, int32_t* src, int64_t rows_bound, int32_t* workspace, hipStream_t st) {
   const int64_t nb = route_blocks(S);
+  int P = 1;
+  while (P * 2 * E <= kRouteMaxExperts) P *= 2;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
   if (nb > 0)
-    hipLaunchKernelGGL(route_hist_kernel, dim3((unsigned)nb), dim3(256), 0, st, ids, S, E, workspace);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteMaxExperts), 0, st, workspace, (int)nb, E, pad, counts,
+    hipLaunchKernelGGL(route_hist_kernel, dim3((unsigned)nb), dim3(256), 0, st, ids, S, E, workspace, src,
+                       rows_bound);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteMaxExperts), 0, st, workspace, (int)nb, E, P, pad, counts,
                      offs, src, rows_bound);
   if (nb > 0)
-    hipLaunchKernelGGL(route_rank_kernel, dim3((unsigned)nb), dim3(64), 0, st, ids, S, E, pad, workspace, counts,
-                       offs, dest, src, rows_bound);
+    hipLaunchKernelGGL(route_rank_kernel, dim3((unsigned)nb), dim3(64), 0, st, ids, S, E, nbits, pad, workspace,
+                       counts, offs, dest, src, rows_bound);
   return hipGetLastError();
 }
 
