@@ -338,10 +338,14 @@ def cpu_baseline(cfg: int, host: dict):
 
 # ---------------------------------------------------------------------- traffic evidence
 
+# The sources the grouped-GEMM launches whose counters profiles/traffic.json holds are built from.
+TRAFFIC_SOURCES = ("gemm_grouped.hip", "gemm_common.hpp", "device_common.hpp", "kernels.hpp", "api.hip")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mxfp8_quantized_moe_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in TRAFFIC_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
