@@ -165,6 +165,36 @@ int swiglu_backward_quantize_rowwise(const void *da2_bf16, const void *h1_bf16, 
                                      void *q, float *scale, void *stream);
 
 /*
+ * quantize_tensorwise -- one fp32 scale for the whole tensor: the coarsest and
+ * fastest scaling granularity, next to rowwise, blockwise and MXFP8.
+ *   [P4 "Скейлы: от тензора до микроблока" (one scale per tensor); P4 FAQ
+ *   (tensorwise is faster and coarser than rowwise); P3, the four scaling
+ *   strategies TorchAO and TorchTitan support.]
+ *   The rowwise recipe with every element as the one reduction set:
+ *   s = fmax/max(amax, 1e-12f), codes = enc(clamp(fp32(x*s))).
+ *   x       bf16 [batch][rows][cols], contiguous
+ *   q       u8   [batch*rows][cols]    row-major codes, or NULL (written)
+ *   q_t     u8   phys [batch][cols][ld_q]  the same codes transposed, as
+ *           quantize_colwise lays them out for the backward GEMMs, or NULL;
+ *           bytes [rows, ld_q) of each output row untouched (written)
+ *   scale   f32  [n_scale]  every entry s (written).  Size it as the fp32 scale
+ *           vector grouped_mm_scaled takes for this operand (rows of A, E*N of
+ *           3D weights, n_groups*cols of a transposed operand): the grouped GEMM
+ *           then runs tensorwise with no change.
+ *   workspace  device memory of quantize_tensorwise_workspace_bytes() bytes,
+ *           owned by the caller; contents on entry do not matter
+ *   Requires: batch >= 1, rows, cols >= 0, n_scale >= 1, cols % 8 == 0; x, q,
+ *   q_t 16-byte aligned; with q_t: ld_q >= rows, ld_q % 16 == 0.  Two or three
+ *   kernels (maxima, row-major cast + broadcast, transposed cast), no allocation.
+ */
+int quantize_tensorwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, int codec,
+                        void *q, void *q_t, int64_t ld_q, float *scale, int64_t n_scale,
+                        void *workspace, void *stream);
+
+/* Workspace bytes quantize_tensorwise needs (a fixed size). */
+int64_t quantize_tensorwise_workspace_bytes(void);
+
+/*
  * moe_route -- group the token slots of a top-k routing by expert: per-expert
  * counts, the offsets tensor the grouped GEMMs take, and for every slot the
  * grouped row it lands in (and the inverse map).

@@ -21,7 +21,8 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
-           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine"]
+           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine",
+           "quantize_tensorwise"]
 
 
 def _ptr(t):
@@ -177,6 +178,30 @@ def swiglu_backward_quantize_rowwise(da2, h1, codec=E4M3FN, dh1=None, q=None, sc
     _lib.check("swiglu_backward_quantize_rowwise", _lib.lib().swiglu_backward_quantize_rowwise(
         _ptr(da2), _ptr(h1), R, F, ld, codec, _ptr(dh1), _ptr(q), _ptr(scale), _stream(stream)))
     return dh1, q, scale
+
+
+def quantize_tensorwise(x, codec=E4M3FN, rowmajor=True, transposed=False, ld_q=None, n_scale=None, q=None,
+                        q_t=None, scale=None, workspace=None, stream=None):
+    """x bf16 [R, C] or [B, R, C] -> (q u8 [B*R, C] or None, q_t u8 [B, C, ld_q] or None, scale f32 [n_scale]).
+    One scale for the whole tensor, repeated n_scale times (default: B*R, the row count); ld_q defaults to R
+    rounded up to 16."""
+    x = _bits(x).contiguous()
+    B, R, C = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+    dev = x.device
+    if rowmajor and q is None:
+        q = torch.empty((B * R, C), dtype=torch.uint8, device=dev)
+    if transposed:
+        ld_q = (R + 15) // 16 * 16 if ld_q is None else ld_q   # rows of q_t start 16-byte aligned
+        if q_t is None:
+            q_t = torch.empty((B, C, ld_q), dtype=torch.uint8, device=dev)
+    n_scale = max(B * R, 1) if n_scale is None else n_scale
+    scale = torch.empty((n_scale,), dtype=torch.float32, device=dev) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(int(_lib.lib().quantize_tensorwise_workspace_bytes()), dtype=torch.uint8, device=dev)
+    _lib.check("quantize_tensorwise", _lib.lib().quantize_tensorwise(
+        _ptr(x), B, R, C, codec, _ptr(q) if rowmajor else None, _ptr(q_t) if transposed else None,
+        ld_q if transposed else 0, _ptr(scale), n_scale, _ptr(workspace), _stream(stream)))
+    return (q if rowmajor else None), (q_t if transposed else None), scale
 
 
 def moe_route_rows_bound(slots: int, n_experts: int, pad: int = 1) -> int:

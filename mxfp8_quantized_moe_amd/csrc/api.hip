@@ -58,6 +58,17 @@ int swiglu_backward_quantize_rowwise(const void* da2_bf16, const void* h1_bf16, 
       static_cast<uint16_t*>(dh1_bf16), static_cast<uint8_t*>(q), scale, as_stream(stream)));
 }
 
+int64_t quantize_tensorwise_workspace_bytes(void) { return kTwPartials * 4; }
+
+int quantize_tensorwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int codec, void* q, void* q_t,
+                        int64_t ld_q, float* scale, int64_t n_scale, void* workspace, void* stream) {
+  const int st = check_quantize_tensorwise(x_bf16, batch, rows, cols, codec, q, q_t, ld_q, scale, n_scale, workspace);
+  if (st) return st;
+  return launch_status(launch_quantize_tensorwise(static_cast<const uint16_t*>(x_bf16), batch, rows, cols, codec,
+                                                  static_cast<uint8_t*>(q), static_cast<uint8_t*>(q_t), ld_q, scale,
+                                                  n_scale, static_cast<uint32_t*>(workspace), as_stream(stream)));
+}
+
 int64_t moe_route_workspace_bytes(int64_t slots, int32_t n_experts) {
   return route_workspace_bytes(slots, n_experts);
 }

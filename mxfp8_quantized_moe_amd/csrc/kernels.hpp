@@ -36,6 +36,9 @@ struct GemmArgs {
 hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st);
 
 hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st);
+hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int codec,
+                                      uint8_t* q, uint8_t* q_t, int64_t ld_q, float* scale, int64_t n_scale,
+                                      uint32_t* part, hipStream_t st);
 hipError_t launch_moe_route(const int32_t* ids, int64_t S, int E, int pad, int32_t* counts, int32_t* offs,
                             int32_t* dest, int32_t* src, int64_t rows_bound, int32_t* workspace, hipStream_t st);
 hipError_t launch_moe_permute(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,

@@ -163,6 +163,26 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
   return FP8MOE_OK;
 }
 
+int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int codec, const void* q,
+                              const void* q_t, int64_t ld_q, const void* scale, int64_t n_scale,
+                              const void* workspace) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (batch < 1 || rows < 0 || cols < 0 || n_scale < 1 || rows > kI32Max || cols > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t per = mul(rows, cols), n = mul(batch, per);
+  if (per < 0 || n < 0) return FP8MOE_ERR_SHAPE;
+  if (q_t != nullptr) {
+    if (ld_q < rows) return FP8MOE_ERR_SHAPE;
+    const int64_t nt = mul(mul(batch, cols), ld_q);
+    const int64_t tiles = mul(batch, mul((rows + 127) / 128, (cols + 63) / 64));
+    if (nt < 0 || tiles < 0 || tiles > kI32Max) return FP8MOE_ERR_SHAPE;
+  }
+  if (!need(x, n) || !scale || !need(workspace, n)) return FP8MOE_ERR_NULL;
+  if (cols % 8 || !aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || !aligned(workspace, 4))
+    return FP8MOE_ERR_ALIGN;
+  if (q_t != nullptr && (ld_q % 16 || !aligned(q_t, 16))) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int64_t route_rows_bound(int64_t slots, int32_t n_experts, int32_t pad) {
   if (slots < 0 || n_experts < 1 || pad < 1) return -1;
   const int64_t r = slots + (int64_t)n_experts * (pad - 1);

@@ -25,6 +25,12 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
 
 int64_t mx_rows_bound(int64_t rows, int32_t n_groups);
 
+// Tensorwise quantization: partial maxima (one u32 each) of the first pass.
+constexpr int kTwPartials = 1024;
+int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int codec, const void* q,
+                              const void* q_t, int64_t ld_q, const void* scale, int64_t n_scale,
+                              const void* workspace);
+
 // Routing: slots per block of the histogram and rank launches, and the most
 // experts one route call takes (one workgroup scans them).
 constexpr int kRouteSlots = 256;

@@ -98,6 +98,25 @@ def test_swiglu_rejections(lib):
     assert b(None, None, 0, 16, 32, 0, None, None, None, None) == L.OK
 
 
+def test_tensorwise_rejections(lib):
+    f = lib.quantize_tensorwise   # (x, batch, rows, cols, codec, q, q_t, ld_q, scale, n_scale, workspace, stream)
+    assert lib.quantize_tensorwise_workspace_bytes() == 4096
+    assert f(P, 1, 4, 16, 7, P, P, 16, P, 4, P, None) == L.ERR_ENUM
+    assert f(P, 0, 4, 16, 0, P, P, 16, P, 4, P, None) == L.ERR_SHAPE       # batch 0
+    assert f(P, 1, -1, 16, 0, P, P, 16, P, 4, P, None) == L.ERR_SHAPE
+    assert f(P, 1, 4, 16, 0, P, P, 16, P, 0, P, None) == L.ERR_SHAPE       # no scale entry
+    assert f(P, 1, 20, 16, 0, P, P, 16, P, 4, P, None) == L.ERR_SHAPE      # ld_q < rows
+    assert f(None, 1, 4, 16, 0, P, P, 16, P, 4, P, None) == L.ERR_NULL
+    assert f(P, 1, 4, 16, 0, P, P, 16, None, 4, P, None) == L.ERR_NULL
+    assert f(P, 1, 4, 16, 0, P, P, 16, P, 4, None, None) == L.ERR_NULL
+    assert f(P, 1, 4, 12, 0, P, P, 16, P, 4, P, None) == L.ERR_ALIGN       # cols % 8
+    assert f(MIS, 1, 4, 16, 0, P, P, 16, P, 4, P, None) == L.ERR_ALIGN
+    assert f(P, 1, 4, 16, 0, MIS, P, 16, P, 4, P, None) == L.ERR_ALIGN
+    assert f(P, 1, 4, 16, 0, P, MIS, 16, P, 4, P, None) == L.ERR_ALIGN
+    assert f(P, 1, 4, 16, 0, P, P, 24, P, 4, P, None) == L.ERR_ALIGN       # ld_q % 16
+    assert f(P, 1, 4, 16, 0, P, P, 16, P + 2, 4, P, None) == L.ERR_ALIGN
+
+
 def test_route_rejections(lib):
     r = lib.moe_route        # (ids, tokens, topk, E, pad, counts, offs, dest, src, workspace, stream)
     assert r(P, -1, 2, 8, 1, P, P, P, P, P, None) == L.ERR_SHAPE
