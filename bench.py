@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--swiglu", action="store_true",
                     help="configs 3/4: also time the fused SwiGLU + rowwise quantization (forward and backward) "
                          "on the layer's A2/dH1 shapes, outside the layer step")
+    ap.add_argument("--tensorwise", action="store_true",
+                    help="config 2: the tensorwise recipe (one scale per tensor for X, W and dY) in place of "
+                         "rowwise + colwise")
     ap.add_argument("--route", action="store_true",
                     help="configs 3/4: also time the routing kernels (route, permute of X into the grouped layout, "
                          "combine of the grouped output) on the layer's routing and hidden size, outside the layer step")
@@ -91,7 +94,7 @@ class Step:
         self.items.append((name, kind, fn, work, work if hbm is None else hbm))
 
 
-def build_step(cfg: int, gw: bool):
+def build_step(cfg: int, gw: bool, tensorwise: bool = False):
     import torch
     import mxfp8_quantized_moe_amd as fm
     from mxfp8_quantized_moe_amd import synth
@@ -161,6 +164,31 @@ def build_step(cfg: int, gw: bool):
                                                             Mc, N, K, out=o), 2.0 * M * N * K,
                  gemm_bytes(N * M, K * M, E * N * K, E * N, E * K, sk))
         return o
+
+    if cfg == 2 and tensorwise:
+        # one scale per tensor: each of X, W, dY quantized once into both layouts, its scale broadcast
+        # into a vector long enough for both of its GEMM uses; the GEMM launches are the rowwise ones
+        F2 = w.F2
+        X, W1, DY = synth.make_x(w), synth.make_w1(w), synth.make_dy(w)
+        host.update(X=X, W=W1.reshape(F2, H), DY=DY)
+        Xd, Wd, DYd = dv(X), dv(W1), dv(DY)
+
+        def q_tw(name, x, R, C):
+            ld = (R + 15) // 16 * 16
+            q, qt, sc, ws = u8(R, C), u8(1, C, ld), f32(max(R, C)), u8(4096)
+            step.add(name, "quant", lambda: fm.quantize_tensorwise(x().view(R, C), 0, rowmajor=True, transposed=True,
+                                                                   ld_q=ld, n_scale=max(R, C), q=q, q_t=qt, scale=sc,
+                                                                   workspace=ws),
+                     4 * R * C + 4 * max(R, C))   # read once, both layouts written, the scale vector
+            return q, qt.view(C, ld), sc, ld
+
+        qx, qxt, sx, ld = q_tw("q_tw X", Xd, M, H)
+        qw, qwt, sw, _ = q_tw("q_tw W", Wd, F2, H)
+        g_m("gemm fwd", qx, sx, qw, sw, M, F2, H)
+        qdy, qdyt, sdy, _ = q_tw("q_tw dY", DYd, M, F2)
+        g_m("gemm dgrad", qdy, sdy, qwt.view(1, H, F2), sw, M, H, F2)
+        g_k("gemm wgrad", qdyt, sdy, qxt, sx, ld, F2, H)
+        return step, host
 
     if cfg in (1, 2):
         F2 = w.F2
@@ -338,8 +366,9 @@ def cpu_baseline(cfg: int, host: dict):
 
 # ---------------------------------------------------------------------- traffic evidence
 
-# The sources the grouped-GEMM launches whose counters profiles/traffic.json holds are built from.
-TRAFFIC_SOURCES = ("gemm_grouped.hip", "gemm_common.hpp", "device_common.hpp", "kernels.hpp", "api.hip")
+# The sources that define the grouped-GEMM kernels and their launch configuration, whose counters
+# profiles/traffic.json holds (the entry-point and declaration files change with every new entry point).
+TRAFFIC_SOURCES = ("gemm_grouped.hip", "gemm_common.hpp", "device_common.hpp")
 
 
 def kernel_source_digest() -> str:
@@ -594,7 +623,9 @@ def main():
     import mxfp8_quantized_moe_amd  # noqa: F401  (fails loudly if the HIP library is missing)
     from mxfp8_quantized_moe_amd import synth
 
-    step, host = build_step(args.config, args.gw)
+    if args.tensorwise and args.config != 2:
+        raise SystemExit("--tensorwise is built for config 2 (the Llama3-8B linear layer)")
+    step, host = build_step(args.config, args.gw, args.tensorwise)
     stream = torch.cuda.current_stream()
     names = [it[0] for it in step.items]
     for w_i in range(args.warmup):
@@ -669,7 +700,9 @@ def main():
         "config": {"workload": w.name, "experts": w.E, "routed_rows": w.M, "hidden": w.H,
                    "w1_out": w.F2, "w2_in": w.F,
                    "step": ("fwd" if args.config == 1 else "fwd+dgrad+wgrad") + ("+bf16 wgrad" if args.gw else ""),
-                   "recipe": "mxfp8 (e8m0 per 1x32)" if w.mx else "fp8 e4m3fn rowwise + colwise backward",
+                   "recipe": "mxfp8 (e8m0 per 1x32)" if w.mx else
+                   "fp8 e4m3fn tensorwise (one scale per tensor)" if args.tensorwise else
+                   "fp8 e4m3fn rowwise + colwise backward",
                    **({"only": args.only} if args.only else {})},
         "quant_GBps": round(q_bytes / q_us / 1e3, 1) if q_us else None,
         "quant_us": round(q_us, 1),
@@ -691,7 +724,7 @@ def main():
         out["swiglu_fused"] = swiglu_extras(args.config, stream)
     if args.route and args.config in (3, 4):
         out["routing"] = route_extras(args.config, stream)
-    if not args.no_cpu_baseline and args.config == 2:
+    if not args.no_cpu_baseline and args.config == 2 and not args.tensorwise:
         out["cpu_baseline"] = cpu_baseline(args.config, host)
     else:
         out["cpu_baseline"] = None      # sampled oracle timing is defined for the default workload

@@ -9,8 +9,10 @@
 // entry equal (the call broadcasts s into a vector of the caller's length).
 //
 // Launches: partial |x| maxima (one per block, grid-strided over 16-byte
-// chunks) into the caller's workspace; then the row-major cast and/or the
-// transposed cast, each of whose blocks folds the partials into s itself.
+// chunks) into the caller's workspace; then the row-major cast (or, with a
+// transposed copy asked for, only the broadcast of s) and the transposed cast,
+// which writes the row-major codes from the same tile; each block folds the
+// partials into s itself.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -91,14 +93,15 @@ __global__ __launch_bounds__(256) void tw_cast_kernel(const u32x4* __restrict__ 
 }
 
 // Transposed cast: tile of 128 rows x 64 columns of batch item b; thread
-// (rq, cc) casts rows 4rq..4rq+3 x columns 8cc..8cc+7 and writes, per column,
+// (rq, cc) casts rows 4rq..4rq+3 x columns 8cc..8cc+7, stores them row-major
+// when q is given (one read of x serves both layouts), and writes, per column,
 // the four codes as one word of the [column][row] LDS tile; then each thread
 // stores two 16-row segments of output rows (columns).
 template <int CODEC>
 __global__ __launch_bounds__(256) void tw_cast_t_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                         const uint32_t* __restrict__ part, int np,
-                                                        uint8_t* __restrict__ q_t, int64_t ld_q, int tiles_r,
-                                                        int tiles_c) {
+                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ q_t,
+                                                        int64_t ld_q, int tiles_r, int tiles_c) {
   __shared__ uint32_t red[4];
   __shared__ uint32_t T[kTwCols][kTwRows / 4 + 2];   // [column][row/4], rows padded by 8 bytes
   const float s = tw_scale(part, np, CODEC, red);
@@ -112,10 +115,12 @@ __global__ __launch_bounds__(256) void tw_cast_t_kernel(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = r0 + 4 * rq + i, c = c0 + 8 * cc;
+    const bool in = r < rows && c < cols;
     u32x4 v = u32x4{0, 0, 0, 0};
-    if (r < rows && c < cols) v = *reinterpret_cast<const u32x4*>(xb + (int64_t)r * cols + c);
+    if (in) v = *reinterpret_cast<const u32x4*>(xb + (int64_t)r * cols + c);
     lo[i] = quant_bf16x4<CODEC>(v.x, v.y, s);
     hi[i] = quant_bf16x4<CODEC>(v.z, v.w, s);
+    if (q != nullptr && in) *reinterpret_cast<u32x2*>(q + (b * rows + r) * (int64_t)cols + c) = u32x2{lo[i], hi[i]};
   }
   // column j's bytes over the four rows -> one word (row 4rq in the low byte)
 #pragma unroll
@@ -151,23 +156,26 @@ hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t batch, int64_t 
   if (np > 0)
     hipLaunchKernelGGL(tw_amax_kernel, dim3((unsigned)np), dim3(256), 0, st, reinterpret_cast<const u32x4*>(x),
                        nchunk, part);
-  const int64_t work = std::max<int64_t>(q ? nchunk : 0, n_scale);
+  // with q_t, the transposed kernel also writes q; the plain cast then only broadcasts s
+  const bool fused = q_t != nullptr && rows > 0 && cols > 0;
+  uint8_t* q_rm = fused ? nullptr : q;
+  const int64_t work = std::max<int64_t>(q_rm ? nchunk : 0, n_scale);
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(4096, (work + 511) / 512));
   if (codec == 0)
     hipLaunchKernelGGL(tw_cast_kernel<0>, dim3(grid), dim3(256), 0, st, reinterpret_cast<const u32x4*>(x), nchunk,
-                       part, np, reinterpret_cast<u32x2*>(q), scale, n_scale);
+                       part, np, reinterpret_cast<u32x2*>(q_rm), scale, n_scale);
   else
     hipLaunchKernelGGL(tw_cast_kernel<1>, dim3(grid), dim3(256), 0, st, reinterpret_cast<const u32x4*>(x), nchunk,
-                       part, np, reinterpret_cast<u32x2*>(q), scale, n_scale);
-  if (q_t != nullptr && rows > 0 && cols > 0) {
+                       part, np, reinterpret_cast<u32x2*>(q_rm), scale, n_scale);
+  if (fused) {
     const int tiles_r = (int)((rows + kTwRows - 1) / kTwRows), tiles_c = (int)((cols + kTwCols - 1) / kTwCols);
     const int64_t tiles = batch * tiles_r * tiles_c;
     if (codec == 0)
       hipLaunchKernelGGL(tw_cast_t_kernel<0>, dim3((unsigned)tiles), dim3(256), 0, st, x, (int)rows, (int)cols, part,
-                         np, q_t, ld_q, tiles_r, tiles_c);
+                         np, q, q_t, ld_q, tiles_r, tiles_c);
     else
       hipLaunchKernelGGL(tw_cast_t_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, st, x, (int)rows, (int)cols, part,
-                         np, q_t, ld_q, tiles_r, tiles_c);
+                         np, q, q_t, ld_q, tiles_r, tiles_c);
   }
   return hipGetLastError();
 }

@@ -8,7 +8,7 @@ import torch
 import mxfp8_quantized_moe_amd as fm
 from oracle import tensorwise as tw
 from oracle.swiglu import round_bf16
-from gpu_helpers import DEV, note, bf16_dev, host, assert_bytes_equal, assert_f32_bits_equal
+from gpu_helpers import DEV, note, bf16_dev, i32_dev, host, assert_bytes_equal, assert_f32_bits_equal
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +92,87 @@ def test_tensorwise_full_size_llama3_x():
     """The Llama3-8B linear layer's activations [8192, 4096] with both layouts, compared in full."""
     x = make_x(11, (1, 8192, 4096), outlier=80.0)
     check(x, fm.E4M3FN, ld_pad=0, what="llama3 X")
+
+
+def _tw(x_bits, n_scale, transposed=False, ld_q=None):
+    B, R, C = (1, *x_bits.shape) if x_bits.ndim == 2 else x_bits.shape
+    return fm.quantize_tensorwise(bf16_dev(x_bits).view(B, R, C), fm.E4M3FN, rowmajor=True, transposed=transposed,
+                                  ld_q=ld_q, n_scale=n_scale)
+
+
+def test_tensorwise_recipe_dense_layer_gemms():
+    """fwd, dgrad and wgrad of a dense linear layer on tensorwise operands through the unchanged
+    grouped GEMM (scales broadcast into its fp32 vectors), against the oracle GEMMs and bounds."""
+    from oracle import gemm as og
+    from test_gpu_gemm import check, _out_host
+    M, H, F2 = 512, 256, 384
+    rng = np.random.default_rng(21)
+    X = round_bf16(rng.standard_normal((M, H)))
+    W = round_bf16(rng.standard_normal((F2, H)) * 0.02)
+    DY = round_bf16(rng.standard_normal((M, F2)) * 1e-3)
+    offs = np.array([M], np.int32)
+    note("tensorwise recipe: quantize X, W, dY")
+    qx, qxt, sx = _tw(X, max(M, H), transposed=True)
+    qw, qwt, sw = _tw(W, max(F2, H), transposed=True)
+    qdy, qdyt, sdy = _tw(DY, max(M, F2), transposed=True)
+    acc = og.ACC_FP8_MFMA
+    h = lambda t: host(t)
+    # forward: X [M, H] x W^T -> [M, F2]
+    note("tensorwise recipe: fwd")
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qx, fm.OPD_E4M3FN, sx, qw.view(1, F2, H), fm.OPD_E4M3FN, sw,
+                               fm.SCALE_F32, i32_dev(offs), 1, M, F2, H)
+    qa, sa, qb, sb = h(qx), h(sx)[:M], h(qw).reshape(1, F2, H), h(sw)[:F2].reshape(1, F2)
+    ref = og.mm_grouped_m(qa, sa, qb, sb, offs, 0, 0)
+    A = oracle_dec(qa) / sa[:, None].astype(np.float64)
+    Bm = oracle_dec(qb) / sb[..., None].astype(np.float64)
+    check(_out_host(out)[1], ref, *og.error_bounds_m(A, Bm, offs, acc), "tensorwise fwd")
+    # dgrad: dY [M, F2] x W -> [M, H]; W's transposed codes [1, H, F2]
+    note("tensorwise recipe: dgrad")
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qdy, fm.OPD_E4M3FN, sdy, qwt.view(1, H, F2), fm.OPD_E4M3FN, sw,
+                               fm.SCALE_F32, i32_dev(offs), 1, M, H, F2)
+    qa, sa, qb, sb = h(qdy), h(sdy)[:M], h(qwt).reshape(1, H, F2), h(sw)[:H].reshape(1, H)
+    ref = og.mm_grouped_m(qa, sa, qb, sb, offs, 0, 0)
+    A = oracle_dec(qa) / sa[:, None].astype(np.float64)
+    Bm = oracle_dec(qb) / sb[..., None].astype(np.float64)
+    check(_out_host(out)[1], ref, *og.error_bounds_m(A, Bm, offs, acc), "tensorwise dgrad")
+    # wgrad: dY^T [F2, M] x X^T [H, M] -> [1, F2, H]
+    note("tensorwise recipe: wgrad")
+    out = fm.grouped_mm_scaled(fm.GROUPED_K, qdyt.view(F2, M), fm.OPD_E4M3FN, sdy, qxt.view(H, M), fm.OPD_E4M3FN,
+                               sx, fm.SCALE_F32, i32_dev(offs), 1, M, F2, H)
+    qa, sa, qb, sb = h(qdyt).reshape(F2, M), h(sdy)[:F2].reshape(1, F2), h(qxt).reshape(H, M), h(sx)[:H].reshape(1, H)
+    ref = og.mm_grouped_k(qa, sa, qb, sb, offs, 0, 0)
+    A = oracle_dec(qa) / sa[0][:, None].astype(np.float64)
+    Bm = oracle_dec(qb) / sb[0][:, None].astype(np.float64)
+    check(_out_host(out)[1], ref, *og.error_bounds_k(A, Bm, offs, acc), "tensorwise wgrad")
+
+
+def test_tensorwise_recipe_moe_forward():
+    """A grouped forward whose 3D expert weights share one tensorwise scale."""
+    from oracle import gemm as og
+    from test_gpu_gemm import check, _out_host
+    from mxfp8_quantized_moe_amd import synth
+    E, N, K = 5, 192, 256
+    counts = synth.random_counts(31, 900, E)
+    offs = synth.offsets_from_counts(counts)
+    M = int(offs[-1])
+    rng = np.random.default_rng(22)
+    X = round_bf16(rng.standard_normal((M, K)))
+    W = round_bf16(rng.standard_normal((E, N, K)) * 0.02)
+    note("tensorwise recipe: MoE fwd")
+    qx, _, sx = _tw(X, M)
+    qw, _, sw = _tw(W, E * N)
+    out = fm.grouped_mm_scaled(fm.GROUPED_M, qx, fm.OPD_E4M3FN, sx, qw.view(E, N, K), fm.OPD_E4M3FN, sw,
+                               fm.SCALE_F32, i32_dev(offs), E, M, N, K)
+    qa, sa, qb, sb = host(qx), host(sx), host(qw).reshape(E, N, K), host(sw).reshape(E, N)
+    qr, sr = tw.quantize_tensorwise(W, fm.E4M3FN)
+    assert_bytes_equal(qb, qr, "3D weight codes")
+    assert np.all(sb == sr)
+    ref = og.mm_grouped_m(qa, sa, qb, sb, offs, 0, 0)
+    A = oracle_dec(qa) / sa[:, None].astype(np.float64)
+    Bm = oracle_dec(qb) / sb[..., None].astype(np.float64)
+    check(_out_host(out)[1], ref, *og.error_bounds_m(A, Bm, offs, og.ACC_FP8_MFMA), "tensorwise MoE fwd")
+
+
+def oracle_dec(q):
+    import oracle
+    return oracle.decode(q, fm.E4M3FN)
