@@ -50,72 +50,91 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restri
   for (int e = t; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
+// Inclusive sum over the lanes of each aligned segment of `seg` lanes (seg a
+// power of two <= 64) of a wave.
+__device__ __forceinline__ int seg_scan(int v, int seg) {
+  const int q = (threadIdx.x & 63) & (seg - 1);
+  for (int off = 1; off < seg; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (q >= off) v += u;
+  }
+  return v;
+}
+
 // One workgroup: P threads per expert (P a power of two, P * E <= 1024) each
 // take a range of blocks; hist[b][e] becomes the rows of e in blocks before b.
 // Then counts, and offs = the inclusive scan of the padded counts.  With no
 // slots (nb == 0) the histogram launch did not run and src is filled here.
+// A thread keeps up to kKeep of its blocks' counts in registers (one pass over
+// hist); the scans run on wave shuffles with one LDS exchange each.
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nb, int E, int P, int pad,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offs,
                                                           int32_t* __restrict__ src, int64_t rows_bound) {
-  __shared__ int part[kRouteMaxExperts];
-  __shared__ int sc[kRouteMaxExperts];
-  const int t = threadIdx.x;
+  constexpr int kKeep = 16;
+  __shared__ int part[kRouteMaxExperts];   // P > 64 only: per-thread sums
+  __shared__ int tot[kRouteMaxExperts];    // per-expert totals
+  __shared__ int wsum[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int e = t / P, q = t % P;
   const bool mine = e < E;
   const int chunk = (nb + P - 1) / P;
   const int b0 = min(q * chunk, nb), b1 = min(b0 + chunk, nb);
+  const bool keep = chunk <= kKeep;
+  int c[kKeep];
   int sum = 0;
   if (mine) {
-    int b = b0;
-    for (; b + 4 <= b1; b += 4) {
-      int c[4];
+    if (keep) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) c[u] = hist[(int64_t)(b + u) * E + e];
-      sum += c[0] + c[1] + c[2] + c[3];
+      for (int u = 0; u < kKeep; ++u) {
+        c[u] = b0 + u < b1 ? hist[(int64_t)(b0 + u) * E + e] : 0;
+        sum += c[u];
+      }
+    } else {
+      for (int b = b0; b < b1; ++b) sum += hist[(int64_t)b * E + e];
     }
-    for (; b < b1; ++b) sum += hist[(int64_t)b * E + e];
   }
-  part[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < P; off <<= 1) {   // inclusive scan within each expert's P ranges
-    const int v = q >= off ? part[t - off] : 0;
+  int incl;   // inclusive sum over this expert's ranges up to q
+  if (P <= 64) {
+    incl = seg_scan(sum, P);
+  } else {    // an expert spans several waves (E <= 8)
+    part[t] = sum;
     __syncthreads();
-    part[t] += v;
-    __syncthreads();
+    for (int off = 1; off < P; off <<= 1) {
+      const int v = q >= off ? part[t - off] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    incl = part[t];
   }
   if (mine) {
-    int run = part[t] - sum;   // rows of e in blocks before b0
-    int b = b0;
-    for (; b + 4 <= b1; b += 4) {
-      int c[4];
+    int run = incl - sum;   // rows of e in blocks before b0
+    if (keep) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) c[u] = hist[(int64_t)(b + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        hist[(int64_t)(b + u) * E + e] = run;
-        run += c[u];
+      for (int u = 0; u < kKeep; ++u)
+        if (b0 + u < b1) {
+          hist[(int64_t)(b0 + u) * E + e] = run;
+          run += c[u];
+        }
+    } else {
+      for (int b = b0; b < b1; ++b) {
+        const int cb = hist[(int64_t)b * E + e];
+        hist[(int64_t)b * E + e] = run;
+        run += cb;
       }
     }
-    for (; b < b1; ++b) {
-      const int c = hist[(int64_t)b * E + e];
-      hist[(int64_t)b * E + e] = run;
-      run += c;
-    }
+    if (q == P - 1) tot[e] = incl;
   }
-  const int total = t < E ? part[t * P + P - 1] : 0;
+  __syncthreads();
+  const int total = t < E ? tot[t] : 0;
   const int padded = (total + pad - 1) / pad * pad;
+  int x = seg_scan(padded, 64);   // inclusive scan over experts: within the wave, then across waves
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  sc[t] = padded;
-  __syncthreads();
-  for (int off = 1; off < kRouteMaxExperts; off <<= 1) {   // inclusive scan over experts
-    const int v = t >= off ? sc[t - off] : 0;
-    __syncthreads();
-    sc[t] += v;
-    __syncthreads();
-  }
+  for (int w = 0; w < wave; ++w) x += wsum[w];
   if (t < E) {
     counts[t] = total;
-    offs[t] = sc[t];
+    offs[t] = x;
   }
   if (nb == 0)
     for (int64_t r = t; r < rows_bound; r += kRouteMaxExperts) src[r] = -1;
