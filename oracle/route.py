@@ -23,7 +23,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quant import bf16_to_f32
+from .quant import EPS, bf16_to_f32
+from .codec import FMAX
 from .swiglu import round_bf16
 
 
@@ -61,6 +62,22 @@ def permute(x_bits: np.ndarray, src: np.ndarray, topk: int) -> np.ndarray:
     used = src >= 0
     out[used] = x[src[used] // topk]
     return out
+
+
+def permute_quantized(q: np.ndarray, s: np.ndarray, src: np.ndarray, topk: int, codec: int):
+    """Rowwise-quantized tokens q [T, C] u8, s [T] f32 -> (qg [len(src), C] u8, sg [len(src)] f32): row r
+    is token src[r] // topk's codes and scale; a padding row gets zero codes and the scale the rowwise
+    recipe gives an all-zero row, fmax / eps.  Quantizing before the gather moves one byte per element
+    instead of two, for the T token rows instead of the topk*T grouped rows; with the padding rows
+    defined this way it gives the same bits as quantizing the gathered bf16 rows."""
+    q = np.asarray(q, dtype=np.uint8)
+    src = np.asarray(src, dtype=np.int64)
+    used = src >= 0
+    qg = np.zeros((src.size, q.shape[1]), dtype=np.uint8)
+    qg[used] = q[src[used] // topk]
+    sg = np.full(src.size, np.float32(np.float32(FMAX[codec]) / EPS), dtype=np.float32)
+    sg[used] = np.asarray(s, dtype=np.float32)[src[used] // topk]
+    return qg, sg
 
 
 def combine(yg_bits: np.ndarray, dest: np.ndarray, weights: np.ndarray, tokens: int, topk: int) -> np.ndarray:

@@ -109,3 +109,21 @@ def test_permute_then_combine_round_trip():
     w[:, 0] = 0.5                                                           # 0.5 + 0.25 + 0.25, exact
     y = rt.combine(xg, dest, w, T, k)
     assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("codec", [oracle.E4M3FN, oracle.E4M3FNUZ])
+def test_permute_quantized_equals_quantize_after_permute(codec):
+    """Gathering rowwise codes and scales gives the bits of quantizing the gathered bf16 rows, padding
+    rows (zeros) included."""
+    rng = np.random.default_rng(4)
+    T, k, C, E = 60, 3, 48, 5
+    ids = rng.integers(0, E, size=(T, k))
+    ids[7, 2] = -1
+    x = round_bf16(rng.standard_normal((T, C)) * 3)
+    x[11] = 0.0                                                             # an all-zero token
+    _, _, _, src = rt.route(ids, E, 16)
+    q, s = oracle.quantize_rowwise(x, codec)
+    qg, sg = rt.permute_quantized(q, s, src, k, codec)
+    qr, sr = oracle.quantize_rowwise(rt.permute(x, src, k), codec)
+    assert np.array_equal(qg, qr)
+    assert np.array_equal(sg.view(np.uint32), sr.view(np.uint32))
