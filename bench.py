@@ -581,12 +581,24 @@ def route_extras(cfg: int, stream):
     ws = torch.empty(max(int(fm._lib.lib().moe_route_workspace_bytes(S, E)), 4), dtype=torch.uint8, device="cuda:0")
     xg = fm.moe_permute(x, src, k)
     y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda:0")
+    q_tok, s_tok = fm.quantize_rowwise(x, 0)
+    qg, sg = torch.empty(R, H, dtype=torch.uint8, device="cuda:0"), torch.empty(R, dtype=torch.float32,
+                                                                                 device="cuda:0")
+    q_rows, s_rows = torch.empty(R, H, dtype=torch.uint8, device="cuda:0"), torch.empty(R, dtype=torch.float32,
+                                                                                        device="cuda:0")
     st = Step()
     # algorithmic bytes: ids read once, dest and src written once (plus counts and offsets)
     st.add("route", "route", lambda: fm.moe_route(ids, E, 1, out=(counts, offs, dest, src), workspace=ws),
            4 * S + 4 * S + 4 * R + 8 * E)
     # X read once, the grouped rows and src once
     st.add("permute X", "route", lambda: fm.moe_permute(x, src, k, xg=xg), 2 * T * H + 2 * R * H + 4 * R)
+    # the two orders of gather and rowwise quantization for the first GEMM's operand:
+    # bf16 gather (above) then quantizing the R grouped rows, or quantizing the T tokens then gathering codes
+    st.add("q_row grouped X", "route", lambda: fm.quantize_rowwise(xg, 0, q=q_rows, scale=s_rows),
+           3 * R * H + 4 * R)
+    st.add("q_row tokens X", "route", lambda: fm.quantize_rowwise(x, 0, q=q_tok, scale=s_tok), 3 * T * H + 4 * T)
+    st.add("permute q(X)", "route", lambda: fm.moe_permute_quantized(q_tok, s_tok, src, k, 0, qg=qg, scale_g=sg),
+           T * H + R * H + 4 * R + 4 * T)
     # every grouped row read once, dest and weights once, Y written once
     st.add("combine Y", "route", lambda: fm.moe_combine(xg, dest, wts, k, y=y), 2 * R * H + 8 * S + 2 * T * H)
     t = per_kernel_flushed(st, stream)

@@ -241,6 +241,27 @@ int moe_permute(const void *x_bf16, int64_t tokens, int64_t cols, int32_t topk,
                 const int32_t *src, int64_t rows_out, void *xg_bf16, void *stream);
 
 /*
+ * moe_permute_quantized -- gather rowwise-quantized token rows (FP8 codes and
+ * their fp32 row scales) into the grouped layout: quantize the tokens once,
+ * then move one byte per element, instead of gathering bf16 rows and
+ * quantizing every routed copy.
+ *   [as moe_route; the rowwise recipe as quantize_rowwise]
+ *   q        u8  [tokens][cols]   codes of quantize_rowwise(x)
+ *   scale    f32 [tokens]         its row scales
+ *   src      int32 [rows_out]     as written by moe_route
+ *   qg       u8  [rows_out][cols] row r = q[src[r] / topk]; zero codes for a padding
+ *            row (src[r] < 0 or >= tokens*topk) (written)
+ *   scale_g  f32 [rows_out]       scale[src[r] / topk]; for a padding row the scale the
+ *            rowwise recipe gives an all-zero row, fmax/1e-12f (written)
+ *   With that padding rule the result has the bits of quantize_rowwise applied to
+ *   moe_permute(x).  Requires: cols % 16 == 0; q and qg 16-byte aligned; src,
+ *   scale, scale_g 4-byte aligned.
+ */
+int moe_permute_quantized(const void *q, const float *scale, int64_t tokens, int64_t cols,
+                          int32_t topk, const int32_t *src, int64_t rows_out, int codec,
+                          void *qg, float *scale_g, void *stream);
+
+/*
  * moe_combine -- weighted sum of each token's expert outputs.
  *   [P4 "MoE" (the routed experts' outputs summed per token with the router's
  *   weights).]

@@ -22,7 +22,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine",
-           "quantize_tensorwise"]
+           "quantize_tensorwise", "moe_permute_quantized"]
 
 
 def _ptr(t):
@@ -238,6 +238,18 @@ def moe_permute(x, src, topk, xg=None, stream=None):
     xg = torch.empty((R, C), dtype=x.dtype, device=x.device) if xg is None else xg
     _lib.check("moe_permute", _lib.lib().moe_permute(_ptr(x), T, C, topk, _ptr(src), R, _ptr(xg), _stream(stream)))
     return xg
+
+
+def moe_permute_quantized(q, scale, src, topk, codec=E4M3FN, qg=None, scale_g=None, stream=None):
+    """Rowwise codes q u8 [T, C] and scales f32 [T], src int32 [R] -> (qg u8 [R, C], scale_g f32 [R])."""
+    q = q.contiguous()
+    T, C = q.shape
+    R = src.numel()
+    qg = torch.empty((R, C), dtype=torch.uint8, device=q.device) if qg is None else qg
+    scale_g = torch.empty((R,), dtype=torch.float32, device=q.device) if scale_g is None else scale_g
+    _lib.check("moe_permute_quantized", _lib.lib().moe_permute_quantized(
+        _ptr(q), _ptr(scale), T, C, topk, _ptr(src), R, codec, _ptr(qg), _ptr(scale_g), _stream(stream)))
+    return qg, scale_g
 
 
 def moe_combine(yg, dest, weights, topk, y=None, stream=None):

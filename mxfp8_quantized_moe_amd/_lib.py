@@ -23,7 +23,7 @@ OUT_BF16, OUT_F32 = 0, 1
 EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_rows_bound",
            "grouped_mm_scaled", "fp8moe_encode_f32", "fp8moe_status_string", "fp8moe_default_codec",
            "fp8moe_version", "swiglu_quantize_rowwise", "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_workspace_bytes",
-           "moe_route_rows_bound", "moe_permute", "moe_combine", "quantize_tensorwise",
+           "moe_route_rows_bound", "moe_permute", "moe_combine", "quantize_tensorwise", "moe_permute_quantized",
            "quantize_tensorwise_workspace_bytes"]
 
 _lib = None
@@ -49,6 +49,7 @@ _SIGS = {
     "moe_route_workspace_bytes": (_i64, [_i64, _i32]),
     "moe_route_rows_bound": (_i64, [_i64, _i32, _i32]),
     "moe_permute": (_int, [_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp]),
+    "moe_permute_quantized": (_int, [_vp, _vp, _i64, _i64, _i32, _vp, _i64, _int, _vp, _vp, _vp]),
     "moe_combine": (_int, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
 }
 

@@ -95,6 +95,15 @@ int moe_permute(const void* x_bf16, int64_t tokens, int64_t cols, int32_t topk, 
                                           static_cast<uint16_t*>(xg_bf16), as_stream(stream)));
 }
 
+int moe_permute_quantized(const void* q, const float* scale, int64_t tokens, int64_t cols, int32_t topk,
+                          const int32_t* src, int64_t rows_out, int codec, void* qg, float* scale_g, void* stream) {
+  const int st = check_moe_permute_quantized(q, scale, tokens, cols, topk, src, rows_out, codec, qg, scale_g);
+  if (st) return st;
+  return launch_status(launch_moe_permute_quantized(static_cast<const uint8_t*>(q), scale, tokens, cols, topk, src,
+                                                    rows_out, codec, static_cast<uint8_t*>(qg), scale_g,
+                                                    as_stream(stream)));
+}
+
 int moe_combine(const void* yg_bf16, int64_t rows_in, const int32_t* dest, const float* weights, int64_t tokens,
                 int32_t topk, int64_t cols, void* y_bf16, void* stream) {
   const int st = check_moe_combine(yg_bf16, rows_in, dest, weights, tokens, topk, cols, y_bf16);

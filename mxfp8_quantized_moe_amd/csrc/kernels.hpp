@@ -43,6 +43,9 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t S, int E, int pad, int32
                             int32_t* dest, int32_t* src, int64_t rows_bound, int32_t* workspace, hipStream_t st);
 hipError_t launch_moe_permute(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
                               int64_t rows_out, uint16_t* xg, hipStream_t st);
+hipError_t launch_moe_permute_quantized(const uint8_t* q, const float* scale, int64_t tokens, int64_t cols, int topk,
+                                        const int32_t* src, int64_t rows_out, int codec, uint8_t* qg,
+                                        float* scale_g, hipStream_t st);
 hipError_t launch_moe_combine(const uint16_t* yg, int64_t rows_in, const int32_t* dest, const float* w,
                               int64_t tokens, int topk, int64_t cols, uint16_t* y, hipStream_t st);
 hipError_t launch_swiglu_quantize_rowwise(const uint16_t* h1, int64_t rows, int64_t F, int64_t ld_h1, int codec,

@@ -186,29 +186,39 @@ __global__ __launch_bounds__(64) void route_rank_kernel(const int32_t* __restric
   }
 }
 
-// One workgroup per grouped row: row r of xg is row src[r] / topk of x, zeros
-// where src[r] is -1 (or names no slot).
-__global__ __launch_bounds__(256) void permute_kernel(const uint16_t* __restrict__ x, int64_t tokens, int64_t cols,
-                                                      int topk, const int32_t* __restrict__ src,
-                                                      uint16_t* __restrict__ xg) {
-  const int64_t r = blockIdx.x;
-  const int64_t nc = cols >> 3;
+// Gather into the grouped layout: row r of xg is row src[r] / topk of x (rb
+// bytes per row, a multiple of 16), zeros where src[r] is -1 (or names no
+// slot).  With row scales (sg non-null), sg[r] is the token's scale, and a
+// padding row takes the scale the rowwise recipe gives an all-zero row.
+// RPB rows per workgroup (256 / RPB threads each), more when rows are short.
+template <int RPB>
+__global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict__ x, int64_t tokens, int64_t rb,
+                                                      int topk, const int32_t* __restrict__ src, int64_t rows_out,
+                                                      uint8_t* __restrict__ xg, const float* __restrict__ s_in,
+                                                      float* __restrict__ sg, int codec) {
+  constexpr int TPR = 256 / RPB;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (r >= rows_out) return;   // no barrier in this kernel
+  const int tid = threadIdx.x % TPR;
+  const int64_t nc = rb >> 4;
   const int s = src[r];
-  u32x4* __restrict__ out = reinterpret_cast<u32x4*>(xg + r * cols);
-  if (s >= 0 && (int64_t)s < tokens * topk) {
-    const u32x4* __restrict__ in = reinterpret_cast<const u32x4*>(x + (int64_t)(s / topk) * cols);
-    int64_t c = threadIdx.x;
-    for (; c + 768 < nc; c += 1024) {   // four 16-byte loads in flight per thread on long rows
-      const u32x4 v0 = in[c], v1 = in[c + 256], v2 = in[c + 512], v3 = in[c + 768];
+  const bool ok = s >= 0 && (int64_t)s < tokens * topk;
+  u32x4* __restrict__ out = reinterpret_cast<u32x4*>(xg + r * rb);
+  if (ok) {
+    const u32x4* __restrict__ in = reinterpret_cast<const u32x4*>(x + (int64_t)(s / topk) * rb);
+    int64_t c = tid;
+    for (; c + 3 * TPR < nc; c += 4 * TPR) {   // four 16-byte loads in flight per thread on long rows
+      const u32x4 v0 = in[c], v1 = in[c + TPR], v2 = in[c + 2 * TPR], v3 = in[c + 3 * TPR];
       out[c] = v0;
-      out[c + 256] = v1;
-      out[c + 512] = v2;
-      out[c + 768] = v3;
+      out[c + TPR] = v1;
+      out[c + 2 * TPR] = v2;
+      out[c + 3 * TPR] = v3;
     }
-    for (; c < nc; c += 256) out[c] = in[c];
+    for (; c < nc; c += TPR) out[c] = in[c];
   } else {
-    for (int64_t c = threadIdx.x; c < nc; c += 256) out[c] = u32x4{0, 0, 0, 0};
+    for (int64_t c = tid; c < nc; c += TPR) out[c] = u32x4{0, 0, 0, 0};
   }
+  if (sg != nullptr && tid == 0) sg[r] = ok ? s_in[s / topk] : scale_from_amax(0.0f, codec);
 }
 
 typedef float rt_f32x2 __attribute__((ext_vector_type(2)));
@@ -284,11 +294,36 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t S, int E, int pad, int32
   return hipGetLastError();
 }
 
+// Rows per workgroup: enough that most of the 256 threads have a 16-byte chunk.
+static hipError_t launch_permute(const uint8_t* x, int64_t tokens, int64_t rb, int topk, const int32_t* src,
+                                 int64_t rows_out, uint8_t* xg, const float* s_in, float* sg, int codec,
+                                 hipStream_t st) {
+  const int64_t nc = rb >> 4;
+  if (nc <= 64) {
+    hipLaunchKernelGGL(permute_kernel<4>, dim3((unsigned)((rows_out + 3) / 4)), dim3(256), 0, st, x, tokens, rb, topk,
+                       src, rows_out, xg, s_in, sg, codec);
+  } else if (nc <= 128) {
+    hipLaunchKernelGGL(permute_kernel<2>, dim3((unsigned)((rows_out + 1) / 2)), dim3(256), 0, st, x, tokens, rb, topk,
+                       src, rows_out, xg, s_in, sg, codec);
+  } else {
+    hipLaunchKernelGGL(permute_kernel<1>, dim3((unsigned)rows_out), dim3(256), 0, st, x, tokens, rb, topk, src,
+                       rows_out, xg, s_in, sg, codec);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_permute(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
                               int64_t rows_out, uint16_t* xg, hipStream_t st) {
   if (rows_out == 0 || cols == 0) return hipSuccess;
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)rows_out), dim3(256), 0, st, x, tokens, cols, topk, src, xg);
-  return hipGetLastError();
+  return launch_permute(reinterpret_cast<const uint8_t*>(x), tokens, 2 * cols, topk, src, rows_out,
+                        reinterpret_cast<uint8_t*>(xg), nullptr, nullptr, 0, st);
+}
+
+hipError_t launch_moe_permute_quantized(const uint8_t* q, const float* scale, int64_t tokens, int64_t cols, int topk,
+                                        const int32_t* src, int64_t rows_out, int codec, uint8_t* qg,
+                                        float* scale_g, hipStream_t st) {
+  if (rows_out == 0) return hipSuccess;
+  return launch_permute(q, tokens, cols, topk, src, rows_out, qg, scale, scale_g, codec, st);
 }
 
 hipError_t launch_moe_combine(const uint16_t* yg, int64_t rows_in, const int32_t* dest, const float* w,

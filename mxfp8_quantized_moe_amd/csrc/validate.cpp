@@ -220,6 +220,21 @@ int check_moe_permute(const void* x, int64_t tokens, int64_t cols, int32_t topk,
   return FP8MOE_OK;
 }
 
+int check_moe_permute_quantized(const void* q, const float* scale, int64_t tokens, int64_t cols, int32_t topk,
+                                const int32_t* src, int64_t rows_out, int codec, const void* qg,
+                                const float* scale_g) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (tokens < 0 || cols < 0 || topk < 1 || rows_out < 0 || rows_out > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk), nq = mul(tokens, cols), ng = mul(rows_out, cols);
+  if (S < 0 || S > kI32Max || nq < 0 || ng < 0) return FP8MOE_ERR_SHAPE;
+  if (!need(q, nq) || !need(scale, tokens) || !need(src, rows_out) || !need(qg, ng) || !need(scale_g, rows_out))
+    return FP8MOE_ERR_NULL;
+  if (cols % 16 || !aligned(q, 16) || !aligned(qg, 16) || !aligned(src, 4) || !aligned(scale, 4) ||
+      !aligned(scale_g, 4))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_moe_combine(const void* yg, int64_t rows_in, const int32_t* dest, const float* w, int64_t tokens,
                       int32_t topk, int64_t cols, const void* y) {
   if (tokens < 0 || cols < 0 || topk < 1 || rows_in < 0 || rows_in > kI32Max) return FP8MOE_ERR_SHAPE;

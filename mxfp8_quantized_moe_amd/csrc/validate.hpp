@@ -43,6 +43,9 @@ int check_moe_route(const int32_t* ids, int64_t tokens, int32_t topk, int32_t E,
                     const int32_t* offs, const int32_t* dest, const int32_t* src, const void* workspace);
 int check_moe_permute(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
                       int64_t rows_out, const void* xg);
+int check_moe_permute_quantized(const void* q, const float* scale, int64_t tokens, int64_t cols, int32_t topk,
+                                const int32_t* src, int64_t rows_out, int codec, const void* qg,
+                                const float* scale_g);
 int check_moe_combine(const void* yg, int64_t rows_in, const int32_t* dest, const float* w, int64_t tokens,
                       int32_t topk, int64_t cols, const void* y);
 

@@ -152,6 +152,17 @@ def test_route_rejections(lib):
     assert p(MIS, 4, 16, 2, P, 8, P, None) == L.ERR_ALIGN
     assert p(P, 4, 16, 2, P, 8, MIS, None) == L.ERR_ALIGN
     assert p(None, 0, 16, 2, None, 0, None, None) == L.OK          # nothing to do
+    pq = lib.moe_permute_quantized   # (q, scale, tokens, cols, topk, src, rows_out, codec, qg, scale_g, stream)
+    assert pq(P, P, 4, 32, 2, P, 8, 7, P, P, None) == L.ERR_ENUM
+    assert pq(P, P, -1, 32, 2, P, 8, 0, P, P, None) == L.ERR_SHAPE
+    assert pq(P, P, 4, 32, 0, P, 8, 0, P, P, None) == L.ERR_SHAPE
+    assert pq(None, P, 4, 32, 2, P, 8, 0, P, P, None) == L.ERR_NULL
+    assert pq(P, None, 4, 32, 2, P, 8, 0, P, P, None) == L.ERR_NULL
+    assert pq(P, P, 4, 32, 2, P, 8, 0, P, None, None) == L.ERR_NULL
+    assert pq(P, P, 4, 24, 2, P, 8, 0, P, P, None) == L.ERR_ALIGN          # cols % 16
+    assert pq(MIS, P, 4, 32, 2, P, 8, 0, P, P, None) == L.ERR_ALIGN
+    assert pq(P, P + 2, 4, 32, 2, P, 8, 0, P, P, None) == L.ERR_ALIGN
+    assert pq(None, None, 0, 32, 2, None, 0, 0, None, None, None) == L.OK
     c = lib.moe_combine      # (yg, rows_in, dest, weights, tokens, topk, cols, y, stream)
     assert c(P, 8, P, P, -1, 2, 16, P, None) == L.ERR_SHAPE
     assert c(P, -1, P, P, 4, 2, 16, P, None) == L.ERR_SHAPE

@@ -156,3 +156,30 @@ def test_workload_permute_combine_sampled(cfg, E, C):
     yg_sub = xgh[np.clip(d, 0, None).ravel()]
     dest_sub = np.where(d.ravel() >= 0, np.arange(d.size), -1).astype(np.int32)
     assert_bytes_equal(host(y)[toks], rt.combine(yg_sub, dest_sub, wh[toks], len(toks), k), "y sampled")
+
+
+@pytest.mark.parametrize("codec", [fm.E4M3FN, fm.E4M3FNUZ])
+@pytest.mark.parametrize("shape", [(9, 3, 5, 4, 32), (1000, 6, 64, 32, 2048), (300, 1, 16, 128, 7168), (0, 2, 4, 16, 64)])
+def test_permute_quantized(codec, shape):
+    """Gather of rowwise codes and scales: bit-exact against the oracle, and equal to quantizing the
+    gathered bf16 rows on the device."""
+    import oracle
+    T, k, E, pad, C = shape
+    rng = np.random.default_rng(T + C + codec)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 10:
+        ids[rng.random((T, k)) < 0.02] = -1
+    x = bf16_random(rng, (T, C), 2.0)
+    counts, offs, dest, src = fm.moe_route(i32_dev(ids), E, pad)
+    xd = bf16_dev(x)
+    note(f"moe_permute_quantized T={T} k={k} C={C} codec={codec}")
+    q, s = fm.quantize_rowwise(xd, codec)
+    qg, sg = fm.moe_permute_quantized(q, s, src, k, codec)
+    qr, sr = rt.permute_quantized(host(q), host(s), host(src), k, codec)
+    assert_bytes_equal(host(qg), qr, "qg")
+    assert_bytes_equal(host(sg).view(np.uint32), sr.view(np.uint32), "scale_g")
+    q2, s2 = fm.quantize_rowwise(fm.moe_permute(xd, src, k), codec)
+    assert_bytes_equal(host(qg), host(q2), "qg vs quantize after permute")
+    assert_bytes_equal(host(sg).view(np.uint32), host(s2).view(np.uint32), "scale_g vs quantize after permute")
+    q_or, s_or = oracle.quantize_rowwise(x, codec)
+    assert_bytes_equal(host(q), q_or, "token codes")
