@@ -35,7 +35,7 @@ from .quant import (EPS, bf16_to_f32, quantize_rowwise, quantize_colwise_grouped
                     quantize_colwise_batched, quantize_mx_lastdim,
                     quantize_mx_rows_grouped, quantize_mx_rows_batched,
                     mx_rows_bound)
-from . import route, swiglu, tensorwise
+from . import blockwise, route, swiglu, tensorwise
 from .gemm import (group_bounds, mm_grouped_m, mm_grouped_k, mm_grouped_m_mx,
                    mm_grouped_k_mx, mm_grouped_k_bf16, error_bounds_m,
                    error_bounds_k, ACC_FP32, ACC_FP8_MFMA)
