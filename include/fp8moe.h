@@ -195,6 +195,44 @@ int quantize_tensorwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t
 int64_t quantize_tensorwise_workspace_bytes(void);
 
 /*
+ * quantize_blockwise -- one fp32 scale per fixed tile: 1 x 128 (block_rows = 1)
+ * for activations, 128 x 128 (block_rows = 128) for weights.
+ *   [P4 "Скейлы: от тензора до микроблока" (a scale per fixed-size tile,
+ *   between rowwise and MXFP8; blockwise kernels for MI300 and MI350); P3, the
+ *   four scaling strategies.  The pages give no tile shape.]
+ *   Each tile (the last of a row or column range may be partial) follows the
+ *   rowwise recipe: s = fmax/max(amax, 1e-12f), codes = enc(clamp(fp32(x*s))).
+ *   x      bf16 [batch][rows][cols], contiguous
+ *   q      u8   [batch][rows][cols] (written)
+ *   scale  f32  [batch][ceil(rows/block_rows)][ceil(cols/128)] (written)
+ *   Requires: batch >= 1, rows, cols >= 0, block_rows 1 or 128, cols % 8 == 0;
+ *   x and q 16-byte aligned, scale 4-byte aligned.
+ */
+int quantize_blockwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
+                       int block_rows, int codec, void *q, float *scale, void *stream);
+
+/*
+ * grouped_mm_blockwise -- GROUPED_M (2D x 3D -> 2D) over blockwise-scaled FP8
+ * operands: out[m][n] = sum over 128-wide contraction blocks kb of
+ * (sum of a[m][k] b[e][n][k] over kb) / (a_scale[m][kb] * b_scale[e][n/128][kb]),
+ * e the group of row m.
+ *   [as quantize_blockwise; P1 Details (the grouped GEMM over an offsets tensor).]
+ *   a        e4m3fn [M][K]            from quantize_blockwise(block_rows = 1)
+ *   a_scale  f32 [M][ceil(K/128)]
+ *   b        e4m3fn [n_groups][N][K]  from quantize_blockwise(batch = n_groups, block_rows = 128)
+ *   b_scale  f32 [n_groups][ceil(N/128)][ceil(K/128)]
+ *   offs     int32 [n_groups], groups as in grouped_mm_scaled (rows of no group untouched)
+ *   out      bf16 (round to nearest even) or f32 [M][N] (written)
+ *   Per block, the FP8 products are summed in fp32 (MFMA), and the partial sum is
+ *   scaled and added to an fp32 running result.  Requires: a_fmt = b_fmt =
+ *   FP8MOE_OPD_E4M3FN (others: FP8MOE_ERR_UNSUPPORTED), K % 16 == 0, a and b
+ *   16-byte aligned.
+ */
+int grouped_mm_blockwise(const void *a, int a_fmt, const float *a_scale, const void *b, int b_fmt,
+                         const float *b_scale, const int32_t *offs, int32_t n_groups, int64_t M,
+                         int64_t N, int64_t K, void *out, int out_dtype, void *stream);
+
+/*
  * moe_route -- group the token slots of a top-k routing by expert: per-expert
  * counts, the offsets tensor the grouped GEMMs take, and for every slot the
  * grouped row it lands in (and the inverse map).

@@ -22,7 +22,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine",
-           "quantize_tensorwise", "moe_permute_quantized"]
+           "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise"]
 
 
 def _ptr(t):
@@ -202,6 +202,28 @@ def quantize_tensorwise(x, codec=E4M3FN, rowmajor=True, transposed=False, ld_q=N
         _ptr(x), B, R, C, codec, _ptr(q) if rowmajor else None, _ptr(q_t) if transposed else None,
         ld_q if transposed else 0, _ptr(scale), n_scale, _ptr(workspace), _stream(stream)))
     return (q if rowmajor else None), (q_t if transposed else None), scale
+
+
+def quantize_blockwise(x, block_rows, codec=E4M3FN, q=None, scale=None, stream=None):
+    """x bf16 [R, C] or [B, R, C] -> (q u8 of x's shape, scale f32 [B, ceil(R/block_rows), ceil(C/128)])."""
+    x = _bits(x).contiguous()
+    B, R, C = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    nr, nc = -(-R // block_rows), -(-C // 128)
+    scale = torch.empty((B, nr, nc), dtype=torch.float32, device=x.device) if scale is None else scale
+    _lib.check("quantize_blockwise", _lib.lib().quantize_blockwise(_ptr(x), B, R, C, block_rows, codec, _ptr(q),
+                                                                    _ptr(scale), _stream(stream)))
+    return q, scale
+
+
+def grouped_mm_blockwise(a, a_scale, b, b_scale, offs, n_groups, M, N, K, out=None, out_dtype=OUT_BF16, stream=None):
+    """GROUPED_M over blockwise e4m3fn operands -> out [M, N] (bf16 or f32)."""
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device=a.device)
+    _lib.check("grouped_mm_blockwise", _lib.lib().grouped_mm_blockwise(
+        _ptr(a), OPD_E4M3FN, _ptr(a_scale), _ptr(b), OPD_E4M3FN, _ptr(b_scale), _ptr(offs), n_groups, M, N, K,
+        _ptr(out), out_dtype, _stream(stream)))
+    return out
 
 
 def moe_route_rows_bound(slots: int, n_experts: int, pad: int = 1) -> int:

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libfp8moe.so")
 
 HIP_SOURCES = ["api.hip", "quant_rowwise.hip", "quant_colwise.hip", "quant_mx.hip", "gemm_grouped.hip", "gemm_bf16.hip",
                "swiglu_quant.hip", "moe_route.hip",
-               "quant_tensorwise.hip"]
+               "quant_tensorwise.hip", "blockwise.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

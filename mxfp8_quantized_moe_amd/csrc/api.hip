@@ -58,6 +58,25 @@ int swiglu_backward_quantize_rowwise(const void* da2_bf16, const void* h1_bf16, 
       static_cast<uint16_t*>(dh1_bf16), static_cast<uint8_t*>(q), scale, as_stream(stream)));
 }
 
+int quantize_blockwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int block_rows, int codec,
+                       void* q, float* scale, void* stream) {
+  const int st = check_quantize_blockwise(x_bf16, batch, rows, cols, block_rows, codec, q, scale);
+  if (st) return st;
+  return launch_status(launch_quantize_blockwise(static_cast<const uint16_t*>(x_bf16), batch, rows, cols, block_rows,
+                                                 codec, static_cast<uint8_t*>(q), scale, as_stream(stream)));
+}
+
+int grouped_mm_blockwise(const void* a, int a_fmt, const float* a_scale, const void* b, int b_fmt,
+                         const float* b_scale, const int32_t* offs, int32_t n_groups, int64_t M, int64_t N, int64_t K,
+                         void* out, int out_dtype, void* stream) {
+  const int st = check_grouped_mm_blockwise(a, a_fmt, a_scale, b, b_fmt, b_scale, offs, n_groups, M, N, K, out,
+                                            out_dtype);
+  if (st) return st;
+  return launch_status(launch_grouped_mm_blockwise(static_cast<const uint8_t*>(a), a_scale,
+                                                   static_cast<const uint8_t*>(b), b_scale, offs, n_groups, M, N, K,
+                                                   out, out_dtype, as_stream(stream)));
+}
+
 int64_t quantize_tensorwise_workspace_bytes(void) { return kTwPartials * 4; }
 
 int quantize_tensorwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int codec, void* q, void* q_t,

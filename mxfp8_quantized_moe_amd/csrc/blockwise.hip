@@ -1,0 +1,269 @@
+// Blockwise FP8 scaling: one fp32 scale per fixed tile (1 x 128 along the
+// contraction for activations, 128 x 128 for weights), and the grouped GEMM
+// over blockwise-scaled operands.  [P4 "Скейлы: от тензора до микроблока" (a
+// scale per fixed-size tile, between rowwise and MXFP8; blockwise kernels for
+// MI300 and MI350); P3, the four scaling strategies.]
+//
+// Each tile follows the rowwise recipe: s = fmax / max(amax, 1e-12f),
+// codes = enc(clamp(fp32(x * s))).  The GEMM (GROUPED_M) sums, per 128-wide
+// contraction block kb, the exact FP8 products of the block in fp32 (MFMA) and
+// adds that partial sum times 1 / (sa[m][kb] * sb[e][n / 128][kb]) to the
+// running fp32 result: the scale changes every block, so it cannot wait for
+// the epilogue as the rowwise scales do.
+//
+// GEMM tile 128 x 128 per workgroup, four waves of 64 x 64 (2 x 2 MFMA blocks
+// of 32 x 32), 64 running + 64 partial accumulator registers per lane.  Each
+// 128-wide block is staged through LDS (global -> registers -> LDS) between
+// two barriers.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+namespace fp8moe {
+
+namespace {
+
+typedef int bw_v8i __attribute__((ext_vector_type(8)));
+typedef float bw_v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kBwTile = 128;               // GEMM tile rows / columns and contraction block
+constexpr int kBwStride = kBwTile + 16;    // LDS row stride in bytes (16-byte aligned, spreads banks)
+
+__device__ __forceinline__ uint32_t chunk_absmax(const u32x4& v) {
+  uint32_t m = pk_absmax_bf16(0u, v.x);
+  m = pk_absmax_bf16(m, v.y);
+  m = pk_absmax_bf16(m, v.z);
+  return pk_fold(pk_absmax_bf16(m, v.w));
+}
+
+template <int CODEC>
+__device__ __forceinline__ u32x2 cast_chunk(const u32x4& v, float s) {
+  return u32x2{quant_bf16x4<CODEC>(v.x, v.y, s), quant_bf16x4<CODEC>(v.z, v.w, s)};
+}
+
+__device__ __forceinline__ uint16_t bw_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+}  // namespace
+
+// 1 x 128 tiles: 16 tiles per workgroup, 16 threads per tile, one 16-byte
+// chunk each.  x is [R][C] (all batch rows stacked); scale is [R][nc].
+template <int CODEC>
+__global__ __launch_bounds__(256) void bw_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t R, int cols,
+                                                            int nc, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  const int t = threadIdx.x;
+  const int64_t tile = (int64_t)blockIdx.x * 16 + (t >> 4);
+  const bool tv = tile < R * nc;
+  const int64_t row = tv ? tile / nc : 0;
+  const int cb = tv ? (int)(tile % nc) : 0;
+  const int c = cb * kBwTile + (t & 15) * 8;
+  const bool valid = tv && c < cols;
+  u32x4 v = u32x4{0, 0, 0, 0};
+  if (valid) v = *reinterpret_cast<const u32x4*>(x + row * cols + c);
+  uint32_t m = chunk_absmax(v);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));   // within 16 lanes
+  const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
+  if (valid) *reinterpret_cast<u32x2*>(q + row * cols + c) = cast_chunk<CODEC>(v, s);
+  if (tv && (t & 15) == 0) scale[row * nc + cb] = s;
+}
+
+// 128 x 128 tiles: one tile per workgroup; thread t takes chunk column t % 16
+// of rows t / 16 + 16 i (i < 8).  x is [B][R][C]; scale is [B][nr][nc].
+template <int CODEC>
+__global__ __launch_bounds__(256) void bw_quant_tiles_kernel(const uint16_t* __restrict__ x, int rows, int cols,
+                                                             int nr, int nc, uint8_t* __restrict__ q,
+                                                             float* __restrict__ scale) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x / (nr * nc);
+  const int rb = (blockIdx.x / nc) % nr, cb = blockIdx.x % nc;
+  const int c = cb * kBwTile + (t & 15) * 8;
+  const int64_t base = b * rows * (int64_t)cols;
+  u32x4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rb * kBwTile + (t >> 4) + 16 * i;
+    v[i] = u32x4{0, 0, 0, 0};
+    if (r < rows && c < cols) v[i] = *reinterpret_cast<const u32x4*>(x + base + (int64_t)r * cols + c);
+    m = max(m, chunk_absmax(v[i]));
+  }
+  m = wave_max_u32(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rb * kBwTile + (t >> 4) + 16 * i;
+    if (r < rows && c < cols) *reinterpret_cast<u32x2*>(q + base + (int64_t)r * cols + c) = cast_chunk<CODEC>(v[i], s);
+  }
+  if (t == 0) scale[blockIdx.x] = s;
+}
+
+struct BwGemm {
+  const uint8_t* a;      // [M][K] e4m3fn codes
+  const float* sa;       // [M][KB]
+  const uint8_t* b;      // [E][N][K]
+  const float* sb;       // [E][NB][KB]
+  const int32_t* offs;   // [E]
+  void* out;             // [M][N] bf16 or f32
+  int E, M, N, K, KB, NB, col_tiles;
+};
+
+template <int OUT>
+__global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm p) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[kBwTile * kBwStride];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[kBwTile * kBwStride];
+  __shared__ float inv_a[kBwTile];
+  __shared__ float inv_b;
+  struct Ch {
+    __device__ int operator()(int lo, int hi) const { return (hi - lo + kBwTile - 1) / kBwTile; }
+  };
+  struct NoPad {
+    __device__ int operator()(int, int) const { return 0; }
+  };
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, lrow = lane & 31;
+  const int ru = blockIdx.x / p.col_tiles, ct = blockIdx.x % p.col_tiles;
+  const Unit un = find_unit<256>(p.offs, p.E, p.M, ru, Ch{}, NoPad{});   // every thread: it synchronizes
+  if (un.e < 0) return;   // uniform
+  const int e = un.e;
+  const int m0 = un.lo + un.j * kBwTile, n0 = ct * kBwTile;
+  const int pv = min(kBwTile, un.hi - m0), qv = min(kBwTile, p.N - n0);
+  const int nb = n0 / kBwTile;
+
+  bw_v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  for (int kb = 0; kb < p.KB; ++kb) {
+    const int k0 = kb * kBwTile;
+    // stage the A and B blocks: 128 rows x 8 chunks of 16 bytes each, four chunks per thread
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = t + 256 * u, row = idx >> 3, ch = idx & 7;
+      const int k = k0 + ch * 16;
+      u32x4 va = u32x4{0, 0, 0, 0}, vb = u32x4{0, 0, 0, 0};
+      if (row < pv && k < p.K) va = *reinterpret_cast<const u32x4*>(p.a + (int64_t)(m0 + row) * p.K + k);
+      if (row < qv && k < p.K)
+        vb = *reinterpret_cast<const u32x4*>(p.b + ((int64_t)e * p.N + n0 + row) * p.K + k);
+      *reinterpret_cast<u32x4*>(As + row * kBwStride + ch * 16) = va;
+      *reinterpret_cast<u32x4*>(Bs + row * kBwStride + ch * 16) = vb;
+    }
+    if (t < kBwTile) inv_a[t] = t < pv ? __frcp_rn(p.sa[(int64_t)(m0 + t) * p.KB + kb]) : 0.0f;
+    if (t == kBwTile) inv_b = __frcp_rn(p.sb[((int64_t)e * p.NB + nb) * p.KB + kb]);
+    __syncthreads();
+
+    bw_v16f part[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {   // two 64-wide MFMA steps; lane half g holds 32 contiguous bytes
+      bw_v8i fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint8_t* pa = As + (wm * 64 + 32 * i + lrow) * kBwStride + ks * 64 + 32 * g;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(pa), hi = *reinterpret_cast<const u32x4*>(pa + 16);
+        fa[i] = bw_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint8_t* pb = Bs + (wn * 64 + 32 * i + lrow) * kBwStride + ks * 64 + 32 * g;
+        const u32x4 lb = *reinterpret_cast<const u32x4*>(pb), hb = *reinterpret_cast<const u32x4*>(pb + 16);
+        fb[i] = bw_v8i{(int)lb.x, (int)lb.y, (int)lb.z, (int)lb.w, (int)hb.x, (int)hb.y, (int)hb.z, (int)hb.w};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (ks == 0) {
+            bw_v16f z;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], z, 0, 0, 0, 0, 0, 0);
+          } else {
+            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], part[i][j], 0, 0, 0, 0, 0, 0);
+          }
+        }
+    }
+    // running result += partial / (sa * sb): element v of block (i, j) is row
+    // 32 i + 8 (v / 4) + 4 g + v % 4 and column 32 j + lrow of the wave's 64 x 64
+    const float ib = inv_b;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float f = inv_a[wm * 64 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3)] * ib;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j][v] += part[i][j][v] * f;
+      }
+    __syncthreads();   // the next block's staging overwrites As, Bs and the scales
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (r >= pv) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = wn * 64 + 32 * j + lrow;
+        if (c >= qv) continue;
+        const int64_t o = (int64_t)(m0 + r) * p.N + n0 + c;
+        if constexpr (OUT == 0)
+          static_cast<uint16_t*>(p.out)[o] = bw_bf16_rne(acc[i][j][v]);
+        else
+          static_cast<float*>(p.out)[o] = acc[i][j][v];
+      }
+    }
+}
+
+hipError_t launch_quantize_blockwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,
+                                     int codec, uint8_t* q, float* scale, hipStream_t st) {
+  if (batch * rows == 0 || cols == 0) return hipSuccess;
+  const int nc = (int)((cols + kBwTile - 1) / kBwTile);
+  if (block_rows == 1) {
+    const int64_t R = batch * rows;
+    const unsigned grid = (unsigned)((R * nc + 15) / 16);
+    if (codec == 0)
+      hipLaunchKernelGGL(bw_quant_rows_kernel<0>, dim3(grid), dim3(256), 0, st, x, R, (int)cols, nc, q, scale);
+    else
+      hipLaunchKernelGGL(bw_quant_rows_kernel<1>, dim3(grid), dim3(256), 0, st, x, R, (int)cols, nc, q, scale);
+  } else {
+    const int nr = (int)((rows + kBwTile - 1) / kBwTile);
+    const unsigned grid = (unsigned)(batch * nr * nc);
+    if (codec == 0)
+      hipLaunchKernelGGL(bw_quant_tiles_kernel<0>, dim3(grid), dim3(256), 0, st, x, (int)rows, (int)cols, nr, nc, q,
+                         scale);
+    else
+      hipLaunchKernelGGL(bw_quant_tiles_kernel<1>, dim3(grid), dim3(256), 0, st, x, (int)rows, (int)cols, nr, nc, q,
+                         scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_mm_blockwise(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                       const int32_t* offs, int n_groups, int64_t M, int64_t N, int64_t K, void* out,
+                                       int out_dtype, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  BwGemm p;
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.offs = offs; p.out = out;
+  p.E = n_groups; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.KB = (int)((K + kBwTile - 1) / kBwTile);
+  p.NB = (int)((N + kBwTile - 1) / kBwTile);
+  p.col_tiles = p.NB;
+  const int64_t row_units = (M + kBwTile - 1) / kBwTile + n_groups;   // bound on the groups' 128-row tiles
+  const unsigned grid = (unsigned)(row_units * p.col_tiles);
+  if (out_dtype == 0)
+    hipLaunchKernelGGL(bw_gemm_kernel<0>, dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(bw_gemm_kernel<1>, dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace fp8moe

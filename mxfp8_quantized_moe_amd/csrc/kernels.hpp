@@ -36,6 +36,11 @@ struct GemmArgs {
 hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st);
 
 hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st);
+hipError_t launch_quantize_blockwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,
+                                     int codec, uint8_t* q, float* scale, hipStream_t st);
+hipError_t launch_grouped_mm_blockwise(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                       const int32_t* offs, int n_groups, int64_t M, int64_t N, int64_t K, void* out,
+                                       int out_dtype, hipStream_t st);
 hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int codec,
                                       uint8_t* q, uint8_t* q_t, int64_t ld_q, float* scale, int64_t n_scale,
                                       uint32_t* part, hipStream_t st);

@@ -163,6 +163,41 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
   return FP8MOE_OK;
 }
 
+int check_quantize_blockwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int block_rows, int codec,
+                             const void* q, const void* scale) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (block_rows != 1 && block_rows != 128) return FP8MOE_ERR_ENUM;
+  if (batch < 1 || rows < 0 || cols < 0 || rows > kI32Max || cols > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t n = mul(batch, mul(rows, cols));
+  const int64_t tiles = mul(batch, mul((rows + block_rows - 1) / block_rows, (cols + 127) / 128));
+  if (n < 0 || tiles < 0 || tiles > (block_rows == 1 ? kI32Max * 16LL : kI32Max)) return FP8MOE_ERR_SHAPE;
+  if (!need(x, n) || !need(q, n) || !need(scale, cols ? tiles : 0)) return FP8MOE_ERR_NULL;
+  if (cols % 8 || !aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_grouped_mm_blockwise(const void* a, int a_fmt, const void* sa, const void* b, int b_fmt, const void* sb,
+                               const int32_t* offs, int32_t n_groups, int64_t M, int64_t N, int64_t K,
+                               const void* out, int out_dtype) {
+  if (a_fmt < FP8MOE_OPD_E4M3FN || a_fmt > FP8MOE_OPD_BF16 || b_fmt < FP8MOE_OPD_E4M3FN || b_fmt > FP8MOE_OPD_BF16 ||
+      (out_dtype != FP8MOE_OUT_BF16 && out_dtype != FP8MOE_OUT_F32))
+    return FP8MOE_ERR_ENUM;
+  if (a_fmt != FP8MOE_OPD_E4M3FN || b_fmt != FP8MOE_OPD_E4M3FN) return FP8MOE_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || n_groups < 1 || M > kI32Max || N > kI32Max || K > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t KB = (K + 127) / 128, NB = (N + 127) / 128;
+  const int64_t grid = mul((M + 127) / 128 + n_groups, NB);
+  const int64_t na = mul(M, K), nb = mul(mul(n_groups, N), K), no = mul(M, N);
+  if (na < 0 || nb < 0 || no < 0 || grid < 0 || grid > kI32Max || mul(mul(n_groups, NB), KB) < 0) return FP8MOE_ERR_SHAPE;
+  const bool work = M > 0 && N > 0;
+  if (!offs || (work && (!need(a, na) || !need(b, nb) || !need(sa, mul(M, KB)) || !need(sb, mul(n_groups, NB * KB)) ||
+                         !out)))
+    return FP8MOE_ERR_NULL;
+  if (K % 16 || !aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(offs, 4) ||
+      !aligned(out, out_dtype == FP8MOE_OUT_BF16 ? 2 : 4))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int codec, const void* q,
                               const void* q_t, int64_t ld_q, const void* scale, int64_t n_scale,
                               const void* workspace) {

@@ -25,6 +25,12 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
 
 int64_t mx_rows_bound(int64_t rows, int32_t n_groups);
 
+int check_quantize_blockwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int block_rows, int codec,
+                             const void* q, const void* scale);
+int check_grouped_mm_blockwise(const void* a, int a_fmt, const void* sa, const void* b, int b_fmt, const void* sb,
+                               const int32_t* offs, int32_t n_groups, int64_t M, int64_t N, int64_t K,
+                               const void* out, int out_dtype);
+
 // Tensorwise quantization: partial maxima (one u32 each) of the first pass.
 constexpr int kTwPartials = 1024;
 int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int codec, const void* q,

@@ -117,6 +117,29 @@ def test_tensorwise_rejections(lib):
     assert f(P, 1, 4, 16, 0, P, P, 16, P + 2, 4, P, None) == L.ERR_ALIGN
 
 
+def test_blockwise_rejections(lib):
+    f = lib.quantize_blockwise   # (x, batch, rows, cols, block_rows, codec, q, scale, stream)
+    assert f(P, 1, 4, 16, 1, 7, P, P, None) == L.ERR_ENUM
+    assert f(P, 1, 4, 16, 64, 0, P, P, None) == L.ERR_ENUM          # tile height 1 or 128 only
+    assert f(P, 0, 4, 16, 1, 0, P, P, None) == L.ERR_SHAPE
+    assert f(None, 1, 4, 16, 1, 0, P, P, None) == L.ERR_NULL
+    assert f(P, 1, 4, 16, 1, 0, P, None, None) == L.ERR_NULL
+    assert f(P, 1, 4, 12, 1, 0, P, P, None) == L.ERR_ALIGN
+    assert f(MIS, 1, 4, 16, 128, 0, P, P, None) == L.ERR_ALIGN
+    g = lib.grouped_mm_blockwise  # (a, a_fmt, sa, b, b_fmt, sb, offs, n_groups, M, N, K, out, out_dtype, stream)
+    assert g(P, 0, P, P, 0, P, P, 2, 64, 64, 128, P, 5, None) == L.ERR_ENUM
+    assert g(P, 1, P, P, 0, P, P, 2, 64, 64, 128, P, 0, None) == L.ERR_UNSUPPORTED   # fnuz codes
+    assert g(P, 0, P, P, 2, P, P, 2, 64, 64, 128, P, 0, None) == L.ERR_UNSUPPORTED   # bf16
+    assert g(P, 0, P, P, 0, P, P, 0, 64, 64, 128, P, 0, None) == L.ERR_SHAPE
+    assert g(P, 0, P, P, 0, P, P, 2, -1, 64, 128, P, 0, None) == L.ERR_SHAPE
+    assert g(P, 0, P, P, 0, P, None, 2, 64, 64, 128, P, 0, None) == L.ERR_NULL
+    assert g(P, 0, None, P, 0, P, P, 2, 64, 64, 128, P, 0, None) == L.ERR_NULL
+    assert g(P, 0, P, P, 0, P, P, 2, 64, 64, 128, None, 0, None) == L.ERR_NULL
+    assert g(P, 0, P, P, 0, P, P, 2, 64, 64, 120, P, 0, None) == L.ERR_ALIGN          # K % 16
+    assert g(MIS, 0, P, P, 0, P, P, 2, 64, 64, 128, P, 0, None) == L.ERR_ALIGN
+    assert g(P, 0, P, P, 0, P + 2, P, 2, 64, 64, 128, P, 0, None) == L.ERR_ALIGN
+
+
 def test_route_rejections(lib):
     r = lib.moe_route        # (ids, tokens, topk, E, pad, counts, offs, dest, src, workspace, stream)
     assert r(P, -1, 2, 8, 1, P, P, P, P, P, None) == L.ERR_SHAPE
