@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--tensorwise", action="store_true",
                     help="config 2: the tensorwise recipe (one scale per tensor for X, W and dY) in place of "
                          "rowwise + colwise")
+    ap.add_argument("--blockwise", action="store_true",
+                    help="config 2: also time the blockwise recipe's forward (1x128 / 128x128 tiles, blockwise "
+                         "grouped GEMM) outside the layer step")
     ap.add_argument("--route", action="store_true",
                     help="configs 3/4: also time the routing kernels (route, permute of X into the grouped layout, "
                          "combine of the grouped output) on the layer's routing and hidden size, outside the layer step")
@@ -560,6 +563,40 @@ def swiglu_extras(cfg: int, stream):
     return out
 
 
+def blockwise_extras(stream):
+    """The blockwise recipe's forward on the Llama3-8B linear shape: X [8192, 4096] in 1 x 128 tiles, W
+    [14336, 4096] in 128 x 128 tiles, the blockwise grouped GEMM; timed like kernels_flushed."""
+    import torch
+    import mxfp8_quantized_moe_amd as fm
+    M, N, K = 8192, 14336, 4096
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(2024)
+    x = torch.randn(M, K, device="cuda:0", generator=gen).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda:0", generator=gen) * 0.02).to(torch.bfloat16)
+    qa, sa = fm.quantize_blockwise(x, 1)
+    qb, sb = fm.quantize_blockwise(w.view(1, N, K), 128)
+    offs = torch.tensor([M], dtype=torch.int32, device="cuda:0")
+    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+    st = Step()
+    st.add("q_block X (1x128)", "quant", lambda: fm.quantize_blockwise(x, 1, q=qa, scale=sa),
+           3 * M * K + 4 * M * (K // 128))
+    st.add("q_block W (128x128)", "quant", lambda: fm.quantize_blockwise(w.view(1, N, K), 128, q=qb, scale=sb),
+           3 * N * K + 4 * (N // 128) * (K // 128))
+    st.add("gemm fwd blockwise", "gemm", lambda: fm.grouped_mm_blockwise(qa, sa.view(M, -1), qb, sb, offs, 1, M, N, K,
+                                                                          out=out), 2.0 * M * N * K)
+    t = per_kernel_flushed(st, stream)
+    res = {}
+    for name, kind, _, work, _ in st.items:
+        med, p10, p90 = t[name]
+        if kind == "gemm":
+            res[name] = {"median_us": med, "p10_us": p10, "p90_us": p90, "TFLOPs": round(work / med / 1e6, 1),
+                         "frac": round(work / med / 1e6 / PEAK_FP8_TFLOPS, 4)}
+        else:
+            res[name] = {"median_us": med, "p10_us": p10, "p90_us": p90, "GBps": round(work / med / 1e3, 1),
+                         "frac": round(work / med / 1e3 / PEAK_HBM_GBPS, 4)}
+    return res
+
+
 def route_extras(cfg: int, stream):
     """The routing kernels on the layer's per-token routing (tokens x topk ids over E experts, no
     padding) and hidden size H: route, permute of X [T, H] into the grouped rows, combine of a grouped
@@ -734,6 +771,8 @@ def main():
     }
     if args.swiglu and args.config in (3, 4):
         out["swiglu_fused"] = swiglu_extras(args.config, stream)
+    if args.blockwise and args.config == 2:
+        out["blockwise_forward"] = blockwise_extras(stream)
     if args.route and args.config in (3, 4):
         out["routing"] = route_extras(args.config, stream)
     if not args.no_cpu_baseline and args.config == 2 and not args.tensorwise:

@@ -14,7 +14,8 @@
 // GEMM tile 128 x 128 per workgroup, four waves of 64 x 64 (2 x 2 MFMA blocks
 // of 32 x 32), 64 running + 64 partial accumulator registers per lane.  Each
 // 128-wide block is staged through LDS (global -> registers -> LDS) between
-// two barriers.
+// two barriers, the next block's loads in flight during the current block's
+// MFMAs; registers capped for two workgroups per CU.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "validate.hpp"
@@ -116,7 +117,7 @@ struct BwGemm {
 };
 
 template <int OUT>
-__global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm p) {
+__global__ __launch_bounds__(256, 2) void bw_gemm_kernel(BwGemm p) {   // two workgroups per CU
   __shared__ __attribute__((aligned(16))) uint8_t As[kBwTile * kBwStride];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[kBwTile * kBwStride];
   __shared__ float inv_a[kBwTile];
@@ -145,23 +146,37 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(BwGemm p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  for (int kb = 0; kb < p.KB; ++kb) {
+  // Block kb + 1's operands and scales load into registers while block kb's
+  // MFMAs run; they go to LDS after the barrier that ends block kb.
+  u32x4 va[4], vb[4];
+  float ra = 0.0f, rb = 0.0f;
+  auto load_block = [&](int kb) {
     const int k0 = kb * kBwTile;
-    // stage the A and B blocks: 128 rows x 8 chunks of 16 bytes each, four chunks per thread
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = t + 256 * u, row = idx >> 3, ch = idx & 7;
       const int k = k0 + ch * 16;
-      u32x4 va = u32x4{0, 0, 0, 0}, vb = u32x4{0, 0, 0, 0};
-      if (row < pv && k < p.K) va = *reinterpret_cast<const u32x4*>(p.a + (int64_t)(m0 + row) * p.K + k);
+      va[u] = u32x4{0, 0, 0, 0};
+      vb[u] = u32x4{0, 0, 0, 0};
+      if (row < pv && k < p.K) va[u] = *reinterpret_cast<const u32x4*>(p.a + (int64_t)(m0 + row) * p.K + k);
       if (row < qv && k < p.K)
-        vb = *reinterpret_cast<const u32x4*>(p.b + ((int64_t)e * p.N + n0 + row) * p.K + k);
-      *reinterpret_cast<u32x4*>(As + row * kBwStride + ch * 16) = va;
-      *reinterpret_cast<u32x4*>(Bs + row * kBwStride + ch * 16) = vb;
+        vb[u] = *reinterpret_cast<const u32x4*>(p.b + ((int64_t)e * p.N + n0 + row) * p.K + k);
     }
-    if (t < kBwTile) inv_a[t] = t < pv ? __frcp_rn(p.sa[(int64_t)(m0 + t) * p.KB + kb]) : 0.0f;
-    if (t == kBwTile) inv_b = __frcp_rn(p.sb[((int64_t)e * p.NB + nb) * p.KB + kb]);
+    if (t < pv) ra = p.sa[(int64_t)(m0 + t) * p.KB + kb];
+    if (t == kBwTile) rb = p.sb[((int64_t)e * p.NB + nb) * p.KB + kb];
+  };
+  if (p.KB > 0) load_block(0);
+  for (int kb = 0; kb < p.KB; ++kb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = t + 256 * u, row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(As + row * kBwStride + ch * 16) = va[u];
+      *reinterpret_cast<u32x4*>(Bs + row * kBwStride + ch * 16) = vb[u];
+    }
+    if (t < kBwTile) inv_a[t] = t < pv ? __frcp_rn(ra) : 0.0f;
+    if (t == kBwTile) inv_b = __frcp_rn(rb);
     __syncthreads();
+    if (kb + 1 < p.KB) load_block(kb + 1);
 
     bw_v16f part[2][2];
 #pragma unroll
