@@ -87,3 +87,46 @@ def test_gemm_equals_dequantized_product():
     A = bw.dequantize_blockwise(qa, sa, 1, 0)[0]
     B = bw.dequantize_blockwise(qb, sb, 128, 0)[0]
     assert np.allclose(got, A @ B.T, rtol=1e-12, atol=1e-12)
+
+
+def test_token_blocks_restart_at_groups():
+    blocks = bw.token_blocks(np.array([130, 130, 400, 999], np.int32), 500)
+    assert blocks == [(0, 0, 128), (0, 128, 130), (2, 130, 258), (2, 258, 386), (2, 386, 400), (3, 400, 500)]
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_token_blocks_of_short_groups_are_colwise(codec):
+    """Groups of at most 128 tokens: one block per group, i.e. the colwise grouped quantizer."""
+    rng = np.random.default_rng(5)
+    offs = np.array([50, 50, 170, 290], np.int32)
+    x = bits(rng, (300, 64), 2.0)
+    init = np.full((64, 304), 0x5A, np.uint8)
+    q, s = bw.quantize_blockwise_tokens(x, offs, codec, ld_q=304, q_init=init)
+    qc, sc = oracle.quantize_colwise_grouped(x, offs, codec, q_init=init, ld_q=304)
+    assert np.array_equal(q, qc)
+    assert np.array_equal(s, sc[[0, 2, 3]])              # the empty group 1 has no block
+
+
+def test_grouped_k_one_block_per_group_matches_colwise_gemm():
+    rng = np.random.default_rng(6)
+    offs = np.array([100, 100, 228, 300], np.int32)
+    M, N, K = 300, 72, 40
+    qa, sa = bw.quantize_blockwise_tokens(bits(rng, (M, N), 1e-3), offs, 0)
+    qb, sb = bw.quantize_blockwise_tokens(bits(rng, (M, K)), offs, 0)
+    got = bw.mm_grouped_k_blockwise(qa, sa, qb, sb, offs, 0, 0)
+    full = lambda s: np.insert(s, 1, 1.0, axis=0)         # the empty group: any scale (no tokens)
+    want = oracle.mm_grouped_k(qa, full(sa), qb, full(sb), offs, 0, 0)
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+    assert not got[1].any()
+
+
+def test_grouped_k_blocks_sum_by_hand():
+    """One group of 256 tokens in two blocks with different scales; exact codes."""
+    a = np.zeros((256, 1))
+    b = np.zeros((256, 1))
+    a[3, 0], a[200, 0] = 2.0, 0.25
+    b[3, 0], b[200, 0] = 1.0, 8.0
+    qa, sa = bw.quantize_blockwise_tokens(round_bf16(a), np.array([256], np.int32), 0)
+    qb, sb = bw.quantize_blockwise_tokens(round_bf16(b), np.array([256], np.int32), 0)
+    out = bw.mm_grouped_k_blockwise(qa, sa, qb, sb, np.array([256], np.int32), 0, 0)
+    assert out[0, 0, 0] == 2.0 * 1.0 + 0.25 * 8.0
