@@ -233,6 +233,43 @@ int grouped_mm_blockwise(const void *a, int a_fmt, const float *a_scale, const v
                          int64_t N, int64_t K, void *out, int out_dtype, void *stream);
 
 /*
+ * quantize_blockwise_tokens -- the blockwise tiles of a token-major operand of
+ * the weight gradient (dY, X), which contracts over tokens: one fp32 scale per
+ * column and 128-token block, the blocks restarting at every group start (a
+ * block never spans two experts; a group's last block may be partial).
+ *   [as quantize_blockwise]
+ *   x      bf16 [tokens][cols]
+ *   offs   int32 [n_groups], groups as in quantize_colwise
+ *   q_t    u8 phys [cols][ld_q]: q_t[c][t] = code of x[t][c] (tokens of no group untouched) (written)
+ *   scale  f32 [blockwise_token_blocks_bound(tokens, n_groups)][cols]: row b = the b-th
+ *          block in group order; rows past the last block untouched (written)
+ *   Requires: cols % 8 == 0, ld_q >= tokens, ld_q % 16 == 0; x and q_t 16-byte aligned.
+ */
+int quantize_blockwise_tokens(const void *x_bf16, int64_t tokens, int64_t cols, const int32_t *offs,
+                              int32_t n_groups, int codec, void *q_t, int64_t ld_q, float *scale,
+                              void *stream);
+
+/* Most 128-token blocks a grouping of `tokens` tokens into n_groups groups can have
+ * (-1: invalid sizes). */
+int64_t blockwise_token_blocks_bound(int64_t tokens, int32_t n_groups);
+
+/*
+ * grouped_mm_blockwise_k -- GROUPED_K (2D x 2D -> 3D, the weight gradient) over
+ * blockwise e4m3fn operands from quantize_blockwise_tokens:
+ * out[e][n][k] = sum over the 128-token blocks b of group e of
+ * (sum of a_t[n][t] b_t[k][t] over b) / (a_scale[b][n] * b_scale[b][k]).
+ *   a_t phys [N][ld], b_t phys [K][ld], a_scale [blocks][N], b_scale [blocks][K];
+ *   out bf16 or f32 [n_groups][N][K] (written; an empty group gives zeros).
+ *   Blocks whose first token is 16-byte aligned in the transposed rows move 16
+ *   bytes at a time, others byte by byte.  Requires: ld >= tokens, ld % 16 == 0,
+ *   a_t and b_t 16-byte aligned.
+ */
+int grouped_mm_blockwise_k(const void *a_t, const float *a_scale, const void *b_t,
+                           const float *b_scale, const int32_t *offs, int32_t n_groups,
+                           int64_t tokens, int64_t ld, int64_t N, int64_t K, void *out,
+                           int out_dtype, void *stream);
+
+/*
  * moe_route -- group the token slots of a top-k routing by expert: per-expert
  * counts, the offsets tensor the grouped GEMMs take, and for every slot the
  * grouped row it lands in (and the inverse map).

@@ -22,7 +22,8 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine",
-           "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise"]
+           "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise",
+           "quantize_blockwise_tokens", "grouped_mm_blockwise_k"]
 
 
 def _ptr(t):
@@ -223,6 +224,34 @@ def grouped_mm_blockwise(a, a_scale, b, b_scale, offs, n_groups, M, N, K, out=No
     _lib.check("grouped_mm_blockwise", _lib.lib().grouped_mm_blockwise(
         _ptr(a), OPD_E4M3FN, _ptr(a_scale), _ptr(b), OPD_E4M3FN, _ptr(b_scale), _ptr(offs), n_groups, M, N, K,
         _ptr(out), out_dtype, _stream(stream)))
+    return out
+
+
+def quantize_blockwise_tokens(x, offs, codec=E4M3FN, ld_q=None, q_t=None, scale=None, stream=None):
+    """x bf16 [M, C], offs int32 [E] -> (q_t u8 [C, ld_q], scale f32 [block bound, C])."""
+    x = _bits(x).contiguous()
+    M, C = x.shape
+    E = offs.numel()
+    ld_q = (M + 15) // 16 * 16 if ld_q is None else ld_q
+    q_t = torch.empty((C, ld_q), dtype=torch.uint8, device=x.device) if q_t is None else q_t
+    nb = int(_lib.lib().blockwise_token_blocks_bound(M, E))
+    scale = torch.empty((nb, C), dtype=torch.float32, device=x.device) if scale is None else scale
+    _lib.check("quantize_blockwise_tokens", _lib.lib().quantize_blockwise_tokens(
+        _ptr(x), M, C, _ptr(offs), E, codec, _ptr(q_t), ld_q, _ptr(scale), _stream(stream)))
+    return q_t, scale
+
+
+def grouped_mm_blockwise_k(a_t, a_scale, b_t, b_scale, offs, tokens, out=None, out_dtype=OUT_BF16, stream=None):
+    """GROUPED_K over blockwise operands a_t [N, ld], b_t [K, ld] -> out [E, N, K]."""
+    N, ld = a_t.shape
+    K = b_t.shape[0]
+    E = offs.numel()
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32,
+                          device=a_t.device)
+    _lib.check("grouped_mm_blockwise_k", _lib.lib().grouped_mm_blockwise_k(
+        _ptr(a_t), _ptr(a_scale), _ptr(b_t), _ptr(b_scale), _ptr(offs), E, tokens, ld, N, K, _ptr(out), out_dtype,
+        _stream(stream)))
     return out
 
 

@@ -24,7 +24,8 @@ EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "grouped_mm_scaled", "fp8moe_encode_f32", "fp8moe_status_string", "fp8moe_default_codec",
            "fp8moe_version", "swiglu_quantize_rowwise", "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_workspace_bytes",
            "moe_route_rows_bound", "moe_permute", "moe_combine", "quantize_tensorwise", "moe_permute_quantized",
-           "quantize_blockwise", "grouped_mm_blockwise",
+           "quantize_blockwise", "grouped_mm_blockwise", "quantize_blockwise_tokens",
+           "blockwise_token_blocks_bound", "grouped_mm_blockwise_k",
            "quantize_tensorwise_workspace_bytes"]
 
 _lib = None
@@ -46,6 +47,9 @@ _SIGS = {
     "swiglu_backward_quantize_rowwise": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
     "quantize_tensorwise": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
     "quantize_tensorwise_workspace_bytes": (_i64, []),
+    "quantize_blockwise_tokens": (_int, [_vp, _i64, _i64, _vp, _i32, _int, _vp, _i64, _vp, _vp]),
+    "blockwise_token_blocks_bound": (_i64, [_i64, _i32]),
+    "grouped_mm_blockwise_k": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _vp, _int, _vp]),
     "quantize_blockwise": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "grouped_mm_blockwise": (_int, [_vp, _int, _vp, _vp, _int, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _int, _vp]),
     "moe_route": (_int, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),

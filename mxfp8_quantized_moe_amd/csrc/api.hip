@@ -77,6 +77,30 @@ int grouped_mm_blockwise(const void* a, int a_fmt, const float* a_scale, const v
                                                    out, out_dtype, as_stream(stream)));
 }
 
+int64_t blockwise_token_blocks_bound(int64_t tokens, int32_t n_groups) {
+  return fp8moe::blockwise_token_blocks_bound(tokens, n_groups);
+}
+
+int quantize_blockwise_tokens(const void* x_bf16, int64_t tokens, int64_t cols, const int32_t* offs, int32_t n_groups,
+                              int codec, void* q_t, int64_t ld_q, float* scale, void* stream) {
+  const int st = check_quantize_blockwise_tokens(x_bf16, tokens, cols, offs, n_groups, codec, q_t, ld_q, scale);
+  if (st) return st;
+  return launch_status(launch_quantize_blockwise_tokens(static_cast<const uint16_t*>(x_bf16), tokens, cols, offs,
+                                                        n_groups, codec, static_cast<uint8_t*>(q_t), ld_q, scale,
+                                                        as_stream(stream)));
+}
+
+int grouped_mm_blockwise_k(const void* a_t, const float* a_scale, const void* b_t, const float* b_scale,
+                           const int32_t* offs, int32_t n_groups, int64_t tokens, int64_t ld, int64_t N, int64_t K,
+                           void* out, int out_dtype, void* stream) {
+  const int st = check_grouped_mm_blockwise_k(a_t, a_scale, b_t, b_scale, offs, n_groups, tokens, ld, N, K, out,
+                                              out_dtype);
+  if (st) return st;
+  return launch_status(launch_grouped_mm_blockwise_k(static_cast<const uint8_t*>(a_t), a_scale,
+                                                     static_cast<const uint8_t*>(b_t), b_scale, offs, n_groups, tokens,
+                                                     ld, N, K, out, out_dtype, as_stream(stream)));
+}
+
 int64_t quantize_tensorwise_workspace_bytes(void) { return kTwPartials * 4; }
 
 int quantize_tensorwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int codec, void* q, void* q_t,

@@ -41,6 +41,11 @@ hipError_t launch_quantize_blockwise(const uint16_t* x, int64_t batch, int64_t r
 hipError_t launch_grouped_mm_blockwise(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                        const int32_t* offs, int n_groups, int64_t M, int64_t N, int64_t K, void* out,
                                        int out_dtype, hipStream_t st);
+hipError_t launch_quantize_blockwise_tokens(const uint16_t* x, int64_t M, int64_t C, const int32_t* offs, int n_groups,
+                                            int codec, uint8_t* q_t, int64_t ld_q, float* scale, hipStream_t st);
+hipError_t launch_grouped_mm_blockwise_k(const uint8_t* a_t, const float* sa, const uint8_t* b_t, const float* sb,
+                                         const int32_t* offs, int n_groups, int64_t M, int64_t ld, int64_t N,
+                                         int64_t K, void* out, int out_dtype, hipStream_t st);
 hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int codec,
                                       uint8_t* q, uint8_t* q_t, int64_t ld_q, float* scale, int64_t n_scale,
                                       uint32_t* part, hipStream_t st);

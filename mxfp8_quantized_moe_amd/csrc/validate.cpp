@@ -198,6 +198,44 @@ int check_grouped_mm_blockwise(const void* a, int a_fmt, const void* sa, const v
   return FP8MOE_OK;
 }
 
+int64_t blockwise_token_blocks_bound(int64_t M, int32_t n_groups) {
+  if (M < 0 || n_groups < 1) return -1;
+  return (M + 127) / 128 + n_groups;
+}
+
+int check_quantize_blockwise_tokens(const void* x, int64_t M, int64_t C, const int32_t* offs, int32_t n_groups,
+                                    int codec, const void* q_t, int64_t ld_q, const void* scale) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (M < 0 || C < 0 || n_groups < 1 || M > kI32Max || C > kI32Max || ld_q < M) return FP8MOE_ERR_SHAPE;
+  const int64_t tb = blockwise_token_blocks_bound(M, n_groups);
+  const int64_t grid = mul(tb, (C + 63) / 64);
+  if (mul(M, C) < 0 || mul(C, ld_q) < 0 || mul(tb, C) < 0 || grid < 0 || grid > kI32Max) return FP8MOE_ERR_SHAPE;
+  const bool work = M > 0 && C > 0;
+  if (!offs || (work && (!x || !q_t || !scale))) return FP8MOE_ERR_NULL;
+  if (C % 8 || ld_q % 16 || !aligned(x, 16) || !aligned(q_t, 16) || !aligned(scale, 4) || !aligned(offs, 4))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_grouped_mm_blockwise_k(const void* a_t, const void* sa, const void* b_t, const void* sb, const int32_t* offs,
+                                 int32_t n_groups, int64_t M, int64_t ld, int64_t N, int64_t K, const void* out,
+                                 int out_dtype) {
+  if (out_dtype != FP8MOE_OUT_BF16 && out_dtype != FP8MOE_OUT_F32) return FP8MOE_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || n_groups < 1 || ld < M || M > kI32Max || N > kI32Max || K > kI32Max)
+    return FP8MOE_ERR_SHAPE;
+  const int64_t tb = blockwise_token_blocks_bound(M, n_groups);
+  const int64_t grid = mul(n_groups, mul((N + 127) / 128, (K + 127) / 128));
+  if (mul(N, ld) < 0 || mul(K, ld) < 0 || mul(mul(n_groups, N), K) < 0 || mul(tb, N + K) < 0 || grid < 0 ||
+      grid > kI32Max)
+    return FP8MOE_ERR_SHAPE;
+  const bool work = N > 0 && K > 0;
+  if (!offs || (work && (!out || (M > 0 && (!a_t || !b_t || !sa || !sb))))) return FP8MOE_ERR_NULL;
+  if (ld % 16 || !aligned(a_t, 16) || !aligned(b_t, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(offs, 4) ||
+      !aligned(out, out_dtype == FP8MOE_OUT_BF16 ? 2 : 4))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int codec, const void* q,
                               const void* q_t, int64_t ld_q, const void* scale, int64_t n_scale,
                               const void* workspace) {

@@ -31,6 +31,13 @@ int check_grouped_mm_blockwise(const void* a, int a_fmt, const void* sa, const v
                                const int32_t* offs, int32_t n_groups, int64_t M, int64_t N, int64_t K,
                                const void* out, int out_dtype);
 
+int64_t blockwise_token_blocks_bound(int64_t M, int32_t n_groups);
+int check_quantize_blockwise_tokens(const void* x, int64_t M, int64_t C, const int32_t* offs, int32_t n_groups,
+                                    int codec, const void* q_t, int64_t ld_q, const void* scale);
+int check_grouped_mm_blockwise_k(const void* a_t, const void* sa, const void* b_t, const void* sb, const int32_t* offs,
+                                 int32_t n_groups, int64_t M, int64_t ld, int64_t N, int64_t K, const void* out,
+                                 int out_dtype);
+
 // Tensorwise quantization: partial maxima (one u32 each) of the first pass.
 constexpr int kTwPartials = 1024;
 int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int codec, const void* q,
