@@ -58,8 +58,8 @@ def parse():
                     help="config 2: the tensorwise recipe (one scale per tensor for X, W and dY) in place of "
                          "rowwise + colwise")
     ap.add_argument("--blockwise", action="store_true",
-                    help="config 2: also time the blockwise recipe's forward (1x128 / 128x128 tiles, blockwise "
-                         "grouped GEMM) outside the layer step")
+                    help="config 2: also time the blockwise recipe's launches (1x128 / 128x128 tiles, 128-token "
+                         "blocks for the weight gradient, the three blockwise GEMMs) outside the layer step")
     ap.add_argument("--route", action="store_true",
                     help="configs 3/4: also time the routing kernels (route, permute of X into the grouped layout, "
                          "combine of the grouped output) on the layer's routing and hidden size, outside the layer step")
@@ -564,26 +564,48 @@ def swiglu_extras(cfg: int, stream):
 
 
 def blockwise_extras(stream):
-    """The blockwise recipe's forward on the Llama3-8B linear shape: X [8192, 4096] in 1 x 128 tiles, W
-    [14336, 4096] in 128 x 128 tiles, the blockwise grouped GEMM; timed like kernels_flushed."""
+    """The blockwise recipe's launches on the Llama3-8B linear layer (M = 8192, H = 4096, F = 14336), timed
+    like kernels_flushed: X and dY in 1 x 128 tiles, W and W^T in 128 x 128 tiles, the token-major dY and X in
+    128-token blocks for the weight gradient, and the three blockwise GEMMs.  Not the layer step (its W^T is a
+    bf16 transpose made once outside the timing)."""
     import torch
     import mxfp8_quantized_moe_amd as fm
-    M, N, K = 8192, 14336, 4096
+    M, K, N = 8192, 4096, 14336
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(2024)
     x = torch.randn(M, K, device="cuda:0", generator=gen).to(torch.bfloat16)
     w = (torch.randn(N, K, device="cuda:0", generator=gen) * 0.02).to(torch.bfloat16)
-    qa, sa = fm.quantize_blockwise(x, 1)
-    qb, sb = fm.quantize_blockwise(w.view(1, N, K), 128)
+    dy = (torch.randn(M, N, device="cuda:0", generator=gen) * 1e-3).to(torch.bfloat16)
+    wt = w.t().contiguous()
     offs = torch.tensor([M], dtype=torch.int32, device="cuda:0")
-    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+    qx, sx = fm.quantize_blockwise(x, 1)
+    qw, sw = fm.quantize_blockwise(w.view(1, N, K), 128)
+    qdy, sdy = fm.quantize_blockwise(dy, 1)
+    qwt, swt = fm.quantize_blockwise(wt.view(1, K, N), 128)
+    qdyt, sdyt = fm.quantize_blockwise_tokens(dy, offs)
+    qxt, sxt = fm.quantize_blockwise_tokens(x, offs)
+    o_f = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+    o_d = torch.empty(M, K, dtype=torch.bfloat16, device="cuda:0")
+    o_w = torch.empty(1, N, K, dtype=torch.bfloat16, device="cuda:0")
+    qb = lambda n_elem, n_scale: 3 * n_elem + 4 * n_scale
     st = Step()
-    st.add("q_block X (1x128)", "quant", lambda: fm.quantize_blockwise(x, 1, q=qa, scale=sa),
-           3 * M * K + 4 * M * (K // 128))
-    st.add("q_block W (128x128)", "quant", lambda: fm.quantize_blockwise(w.view(1, N, K), 128, q=qb, scale=sb),
-           3 * N * K + 4 * (N // 128) * (K // 128))
-    st.add("gemm fwd blockwise", "gemm", lambda: fm.grouped_mm_blockwise(qa, sa.view(M, -1), qb, sb, offs, 1, M, N, K,
-                                                                          out=out), 2.0 * M * N * K)
+    st.add("q_block X (1x128)", "quant", lambda: fm.quantize_blockwise(x, 1, q=qx, scale=sx), qb(M * K, M * K // 128))
+    st.add("q_block W (128x128)", "quant", lambda: fm.quantize_blockwise(w.view(1, N, K), 128, q=qw, scale=sw),
+           qb(N * K, N * K // 16384))
+    st.add("gemm fwd blockwise", "gemm", lambda: fm.grouped_mm_blockwise(qx, sx.view(M, -1), qw, sw, offs, 1, M, N, K,
+                                                                          out=o_f), 2.0 * M * N * K)
+    st.add("q_block dY (1x128)", "quant", lambda: fm.quantize_blockwise(dy, 1, q=qdy, scale=sdy),
+           qb(M * N, M * N // 128))
+    st.add("q_block W^T (128x128)", "quant", lambda: fm.quantize_blockwise(wt.view(1, K, N), 128, q=qwt, scale=swt),
+           qb(N * K, N * K // 16384))
+    st.add("gemm dgrad blockwise", "gemm", lambda: fm.grouped_mm_blockwise(qdy, sdy.view(M, -1), qwt, swt, offs, 1, M,
+                                                                            K, N, out=o_d), 2.0 * M * N * K)
+    st.add("q_tokens dY", "quant", lambda: fm.quantize_blockwise_tokens(dy, offs, q_t=qdyt, scale=sdyt),
+           qb(M * N, M * N // 128))
+    st.add("q_tokens X", "quant", lambda: fm.quantize_blockwise_tokens(x, offs, q_t=qxt, scale=sxt),
+           qb(M * K, M * K // 128))
+    st.add("gemm wgrad blockwise", "gemm", lambda: fm.grouped_mm_blockwise_k(qdyt, sdyt, qxt, sxt, offs, M, out=o_w),
+           2.0 * M * N * K)
     t = per_kernel_flushed(st, stream)
     res = {}
     for name, kind, _, work, _ in st.items:
@@ -594,6 +616,7 @@ def blockwise_extras(stream):
         else:
             res[name] = {"median_us": med, "p10_us": p10, "p90_us": p90, "GBps": round(work / med / 1e3, 1),
                          "frac": round(work / med / 1e3 / PEAK_HBM_GBPS, 4)}
+    res["sum_of_medians_us"] = round(sum(t[name][0] for name, *_ in st.items), 1)
     return res
 
 
@@ -772,7 +795,7 @@ def main():
     if args.swiglu and args.config in (3, 4):
         out["swiglu_fused"] = swiglu_extras(args.config, stream)
     if args.blockwise and args.config == 2:
-        out["blockwise_forward"] = blockwise_extras(stream)
+        out["blockwise_recipe"] = blockwise_extras(stream)
     if args.route and args.config in (3, 4):
         out["routing"] = route_extras(args.config, stream)
     if not args.no_cpu_baseline and args.config == 2 and not args.tensorwise:

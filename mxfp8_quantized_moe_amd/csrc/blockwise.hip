@@ -354,7 +354,8 @@ __device__ __forceinline__ u32x4 bw_load_tokens(const uint8_t* __restrict__ row,
 }
 
 // Tile (expert e, 128 rows of N, 128 columns of K): the sum over e's token
-// blocks of the block's MFMA product times 1 / (sa[tb][n] * sb[tb][k]).
+// blocks of the block's MFMA product times 1 / (sa[tb][n] * sb[tb][k]); the
+// next block's loads in flight during the current block's MFMAs.
 template <int OUT>
 __global__ __launch_bounds__(256, 2) void bw_gemm_k_kernel(BwGemmK p) {
   __shared__ __attribute__((aligned(16))) uint8_t As[kBwTile * kBwStride];
@@ -378,19 +379,32 @@ __global__ __launch_bounds__(256, 2) void bw_gemm_k_kernel(BwGemmK p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  for (int jb = 0; jb < nblk; ++jb) {
+  // Block jb + 1's operands and scale load into registers while block jb's MFMAs run.
+  u32x4 va[4], vb[4];
+  float rs = 0.0f;
+  auto load_block = [&](int jb) {
     const int t0 = lo + kBwTile * jb, tl = min(kBwTile, hi - t0), tb = tb0 + jb;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = t + 256 * u, row = idx >> 3, ch = idx & 7;
-      const u32x4 va = row < nv ? bw_load_tokens(p.a + (int64_t)(n0 + row) * p.ld, t0, ch, tl) : u32x4{0, 0, 0, 0};
-      const u32x4 vb = row < kv ? bw_load_tokens(p.b + (int64_t)(k0 + row) * p.ld, t0, ch, tl) : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(As + row * kBwStride + ch * 16) = va;
-      *reinterpret_cast<u32x4*>(Bs + row * kBwStride + ch * 16) = vb;
+      va[u] = row < nv ? bw_load_tokens(p.a + (int64_t)(n0 + row) * p.ld, t0, ch, tl) : u32x4{0, 0, 0, 0};
+      vb[u] = row < kv ? bw_load_tokens(p.b + (int64_t)(k0 + row) * p.ld, t0, ch, tl) : u32x4{0, 0, 0, 0};
     }
-    if (t < kBwTile) inv_a[t] = t < nv ? __frcp_rn(p.sa[(int64_t)tb * p.N + n0 + t]) : 0.0f;
-    else inv_b[t - kBwTile] = t - kBwTile < kv ? __frcp_rn(p.sb[(int64_t)tb * p.K + k0 + t - kBwTile]) : 0.0f;
+    if (t < kBwTile) rs = t < nv ? p.sa[(int64_t)tb * p.N + n0 + t] : 1.0f;
+    else rs = t - kBwTile < kv ? p.sb[(int64_t)tb * p.K + k0 + t - kBwTile] : 1.0f;
+  };
+  if (nblk > 0) load_block(0);
+  for (int jb = 0; jb < nblk; ++jb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = t + 256 * u, row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(As + row * kBwStride + ch * 16) = va[u];
+      *reinterpret_cast<u32x4*>(Bs + row * kBwStride + ch * 16) = vb[u];
+    }
+    if (t < kBwTile) inv_a[t] = t < nv ? __frcp_rn(rs) : 0.0f;
+    else inv_b[t - kBwTile] = t - kBwTile < kv ? __frcp_rn(rs) : 0.0f;
     __syncthreads();
+    if (jb + 1 < nblk) load_block(jb + 1);
     bw_v16f part[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
