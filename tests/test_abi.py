@@ -140,6 +140,30 @@ def test_blockwise_rejections(lib):
     assert g(P, 0, P, P, 0, P + 2, P, 2, 64, 64, 128, P, 0, None) == L.ERR_ALIGN
 
 
+def test_blockwise_tokens_rejections(lib):
+    f = lib.quantize_blockwise_tokens   # (x, tokens, cols, offs, n_groups, codec, q_t, ld_q, scale, stream)
+    assert lib.blockwise_token_blocks_bound(300, 4) == 3 + 4
+    assert lib.blockwise_token_blocks_bound(-1, 4) == -1 and lib.blockwise_token_blocks_bound(10, 0) == -1
+    assert f(P, 64, 16, P, 2, 7, P, 64, P, None) == L.ERR_ENUM
+    assert f(P, 64, 16, P, 0, 0, P, 64, P, None) == L.ERR_SHAPE       # no groups
+    assert f(P, 64, 16, P, 2, 0, P, 48, P, None) == L.ERR_SHAPE       # ld_q < tokens
+    assert f(P, 64, 16, None, 2, 0, P, 64, P, None) == L.ERR_NULL
+    assert f(None, 64, 16, P, 2, 0, P, 64, P, None) == L.ERR_NULL
+    assert f(P, 64, 16, P, 2, 0, P, 64, None, None) == L.ERR_NULL
+    assert f(P, 64, 12, P, 2, 0, P, 64, P, None) == L.ERR_ALIGN       # cols % 8
+    assert f(P, 64, 16, P, 2, 0, P, 72, P, None) == L.ERR_ALIGN       # ld_q % 16
+    assert f(P, 64, 16, P, 2, 0, MIS, 64, P, None) == L.ERR_ALIGN
+    g = lib.grouped_mm_blockwise_k   # (a_t, sa, b_t, sb, offs, n_groups, tokens, ld, N, K, out, out_dtype, stream)
+    assert g(P, P, P, P, P, 2, 64, 64, 32, 32, P, 3, None) == L.ERR_ENUM
+    assert g(P, P, P, P, P, 0, 64, 64, 32, 32, P, 0, None) == L.ERR_SHAPE
+    assert g(P, P, P, P, P, 2, 64, 48, 32, 32, P, 0, None) == L.ERR_SHAPE   # ld < tokens
+    assert g(P, P, P, P, None, 2, 64, 64, 32, 32, P, 0, None) == L.ERR_NULL
+    assert g(None, P, P, P, P, 2, 64, 64, 32, 32, P, 0, None) == L.ERR_NULL
+    assert g(P, P, P, P, P, 2, 64, 64, 32, 32, None, 0, None) == L.ERR_NULL
+    assert g(P, P, P, P, P, 2, 64, 72, 32, 32, P, 0, None) == L.ERR_ALIGN   # ld % 16
+    assert g(P, P, MIS, P, P, 2, 64, 64, 32, 32, P, 0, None) == L.ERR_ALIGN
+
+
 def test_route_rejections(lib):
     r = lib.moe_route        # (ids, tokens, topk, E, pad, counts, offs, dest, src, workspace, stream)
     assert r(P, -1, 2, 8, 1, P, P, P, P, P, None) == L.ERR_SHAPE
