@@ -299,10 +299,10 @@ static hipError_t launch_permute(const uint8_t* x, int64_t tokens, int64_t rb, i
                                  int64_t rows_out, uint8_t* xg, const float* s_in, float* sg, int codec,
                                  hipStream_t st) {
   const int64_t nc = rb >> 4;
-  if (nc <= 64) {
+  if (nc <= 128) {
     hipLaunchKernelGGL(permute_kernel<4>, dim3((unsigned)((rows_out + 3) / 4)), dim3(256), 0, st, x, tokens, rb, topk,
                        src, rows_out, xg, s_in, sg, codec);
-  } else if (nc <= 128) {
+  } else if (nc <= 256) {
     hipLaunchKernelGGL(permute_kernel<2>, dim3((unsigned)((rows_out + 1) / 2)), dim3(256), 0, st, x, tokens, rb, topk,
                        src, rows_out, xg, s_in, sg, codec);
   } else {
