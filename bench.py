@@ -678,7 +678,7 @@ def main():
         write_traffic(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import torch
