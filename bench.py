@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--gw", action="store_true", help="config 2: add the BF16 wgrad variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--swiglu", action="store_true",
@@ -80,6 +80,11 @@ def parse():
 
 # ---------------------------------------------------------------------- layer plan
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 N_ROTATE = 4   # device copies of every input; step s reads copy s % N_ROTATE
 
 
@@ -87,28 +92,40 @@ class Step:
     """A list of launches; each item: (name, kind, fn, work, hbm) with kind 'quant' (work = hbm =
     algorithmic bytes) or 'gemm' / 'gemm_bf16' (work = flops, hbm = algorithmic bytes: operands and
     scales read once, output written once).  Launches read their inputs through getters that pick
-    copy `rot[0]`, so consecutive steps read inputs that the caches do not hold."""
+    copy `rot[0]`, so consecutive steps read inputs that the caches do not hold.  `specs[name]`
+    says what a launch computes (operation, named host inputs, device outputs), so a parity test
+    can check every launch of exactly this step against the oracle."""
 
     def __init__(self):
         self.items = []
         self.rot = [0]
+        self.specs = {}
 
-    def add(self, name, kind, fn, work, hbm=None):
+    def add(self, name, kind, fn, work, hbm=None, spec=None):
         self.items.append((name, kind, fn, work, work if hbm is None else hbm))
+        if spec is not None:
+            self.specs[name] = spec
+
+    def run(self):
+        for it in self.items:
+            it[2]()
 
 
-def build_step(cfg: int, gw: bool, tensorwise: bool = False):
+def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_ROTATE, keep_host: bool = False,
+               dev: str = "cuda:0"):
+    """The layer step of workload `cfg` on preallocated device buffers.  Returns (step, host): host
+    holds the bf16 inputs as numpy bit patterns (X, DY and W always; with keep_host every input,
+    named as in Step.specs)."""
     import torch
     import mxfp8_quantized_moe_amd as fm
     from mxfp8_quantized_moe_amd import synth
 
-    dev = "cuda:0"
     w = synth.WORKLOADS[cfg]
 
     def dv(bits):
-        """N_ROTATE device copies of a bf16 input; returns a getter of the current one."""
+        """n_rotate device copies of a bf16 input; returns a getter of the current one."""
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-        copies = [t] + [t.clone() for _ in range(N_ROTATE - 1)]
+        copies = [t] + [t.clone() for _ in range(n_rotate - 1)]
         return lambda: copies[step.rot[0]]
 
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
@@ -126,23 +143,23 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False):
     def qbytes(n_elem, n_scale, scale_bytes=4):
         return 3 * n_elem + scale_bytes * n_scale
 
-    def q_row(name, x, rows, cols):
+    def q_row(name, src, x, rows, cols):
         q, s = u8(rows, cols), f32(rows)
         step.add(name, "quant", lambda: fm.quantize_rowwise(x().view(rows, cols), 0, q=q, scale=s),
-                 qbytes(rows * cols, rows))
+                 qbytes(rows * cols, rows), spec=dict(op="q_row", src=src, shape=(rows, cols), q=q, s=s))
         return q, s
 
-    def q_col_grouped(name, x, rows, cols):
+    def q_col_grouped(name, src, x, rows, cols):
         ld = (rows + 15) // 16 * 16
         q, s = u8(cols, ld), f32(E, cols)
         step.add(name, "quant", lambda: fm.quantize_colwise(x(), offs, 0, q_t=q, scale=s, ld_q=ld),
-                 qbytes(rows * cols, E * cols))
+                 qbytes(rows * cols, E * cols), spec=dict(op="q_col_grouped", src=src, offs=offs_np, q=q, s=s))
         return q, s, ld
 
-    def q_col_batched(name, x, B, R, C):
+    def q_col_batched(name, src, x, B, R, C):
         q, s = u8(B, C, R), f32(B, C)
         step.add(name, "quant", lambda: fm.quantize_colwise(x(), None, 0, q_t=q, scale=s, ld_q=R),
-                 qbytes(B * R * C, B * C))
+                 qbytes(B * R * C, B * C), spec=dict(op="q_col_batched", src=src, shape=(B, R, C), q=q, s=s))
         return q, s
 
     def gemm_bytes(a_elems, b_elems, out_elems, a_rows, b_rows, sk):
@@ -151,13 +168,13 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False):
         sc = (a_elems + b_elems) / 32 if sk in (fm.SCALE_E8M0, fm.SCALE_E8M0_K4) else 4 * (a_rows + b_rows)
         return a_elems + b_elems + 2 * out_elems + sc
 
-    def g_m(name, qa, sa, qb, sb, Mr, N, K, sk=fm.SCALE_F32, offs_t=None, n_groups=None):
+    def g_m(name, qa, sa, qb, sb, Mr, N, K, sk=fm.SCALE_F32):
+        # the weight operand of an expert with no rows is never read: only non-empty experts count
         o = bf(Mr, N)
-        og = offs if offs_t is None else offs_t
-        ng = E if n_groups is None else n_groups
-        step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, sa, qb, 0, sb, sk, og, ng,
+        step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, sa, qb, 0, sb, sk, offs, E,
                                                             Mr, N, K, out=o), 2.0 * M * N * K,
-                 gemm_bytes(M * K, ng * N * K, M * N, M, ng * N, sk))
+                 gemm_bytes(M * K, nonempty * N * K, M * N, M, nonempty * N, sk),
+                 spec=dict(op="g_m", qa=qa, sa=sa, qb=qb, sb=sb, sk=sk, offs=offs_np, M=Mr, N=N, K=K, out=o))
         return o
 
     def g_k(name, qa, sa, qb, sb, Mc, N, K, sk=fm.SCALE_F32, offs_t=None):
@@ -165,7 +182,9 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False):
         og = offs if offs_t is None else offs_t
         step.add(name, "gemm", lambda: fm.grouped_mm_scaled(fm.GROUPED_K, qa, 0, sa, qb, 0, sb, sk, og, E,
                                                             Mc, N, K, out=o), 2.0 * M * N * K,
-                 gemm_bytes(N * M, K * M, E * N * K, E * N, E * K, sk))
+                 gemm_bytes(N * M, K * M, E * N * K, E * N, E * K, sk),
+                 spec=dict(op="g_k", qa=qa, sa=sa, qb=qb, sb=sb, sk=sk, offs=offs_np if offs_t is None else offs_t,
+                           M=Mc, N=N, K=K, out=o))
         return o
 
     if cfg == 2 and tensorwise:
@@ -196,53 +215,58 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False):
     if cfg in (1, 2):
         F2 = w.F2
         X, W1 = synth.make_x(w), synth.make_w1(w)
-        host.update(X=X, W=W1.reshape(E * F2, H))
+        host.update(X=X, W=W1.reshape(E * F2, H), W1=W1)
         Xd, Wd = dv(X), dv(W1)
-        qx, sx = q_row("q_row X", Xd, M, H)
-        qw, sw = q_row("q_row W", Wd, E * F2, H)
+        qx, sx = q_row("q_row X", "X", Xd, M, H)
+        qw, sw = q_row("q_row W", "W1", Wd, E * F2, H)
         g_m("gemm fwd", qx, sx, qw, sw, M, F2, H)
         if cfg == 2:
             DY = synth.make_dy(w)
             host.update(DY=DY)
             DYd = dv(DY)
-            qdy, sdy = q_row("q_row dY", DYd, M, F2)
-            qwt, swt = q_col_batched("q_col W", Wd, 1, F2, H)
+            qdy, sdy = q_row("q_row dY", "DY", DYd, M, F2)
+            qwt, swt = q_col_batched("q_col W", "W1", Wd, 1, F2, H)
             g_m("gemm dgrad", qdy, sdy, qwt, swt, M, H, F2)
-            qdyt, sdyt, ld = q_col_grouped("q_col dY", DYd, M, F2)
-            qxt, sxt, _ = q_col_grouped("q_col X", Xd, M, H)
+            qdyt, sdyt, ld = q_col_grouped("q_col dY", "DY", DYd, M, F2)
+            qxt, sxt, _ = q_col_grouped("q_col X", "X", Xd, M, H)
             g_k("gemm wgrad", qdyt, sdyt, qxt, sxt, ld, F2, H)
             if gw:
                 o = bf(1, F2, H)
                 step.add("gemm wgrad bf16", "gemm_bf16",
                          lambda: fm.grouped_mm_scaled(fm.GROUPED_K, DYd(), fm.OPD_BF16, None, Xd(), fm.OPD_BF16, None,
                                                       fm.SCALE_NONE, offs, 1, M, F2, H, out=o), 2.0 * M * F2 * H,
-                         2 * (M * F2 + M * H + F2 * H))
+                         2 * (M * F2 + M * H + F2 * H),
+                         spec=dict(op="g_k_bf16", a="DY", b="X", offs=offs_np, out=o))
         return step, host
 
     F, F2 = w.F, w.F2
-    X, A2, DY, DH1 = synth.make_x(w), synth.make_a2(w), synth.make_dy(w), synth.make_dh1(w)
-    W1, W2 = synth.make_w1(w), synth.make_w2(w)
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(6) as ex:      # independent seeded streams: the values do not depend on this
+        X, A2, DY, DH1, W1, W2 = ex.map(lambda f: f(w), [synth.make_x, synth.make_a2, synth.make_dy,
+                                                         synth.make_dh1, synth.make_w1, synth.make_w2])
     host.update(X=X, W=W1.reshape(E * F2, H), DY=DY)
+    if keep_host:
+        host.update(A2=A2, DH1=DH1, W1=W1, W2=W2)
     Xd, A2d, DYd, DH1d, W1d, W2d = dv(X), dv(A2), dv(DY), dv(DH1), dv(W1), dv(W2)
     del W1, W2
     if cfg in (3, 4):
-        qx, sx = q_row("q_row X", Xd, M, H)
-        qw1, sw1 = q_row("q_row W1", W1d, E * F2, H)
+        qx, sx = q_row("q_row X", "X", Xd, M, H)
+        qw1, sw1 = q_row("q_row W1", "W1", W1d, E * F2, H)
         g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H)
-        qa2, sa2 = q_row("q_row A2", A2d, M, F)
-        qw2, sw2 = q_row("q_row W2", W2d, E * H, F)
+        qa2, sa2 = q_row("q_row A2", "A2", A2d, M, F)
+        qw2, sw2 = q_row("q_row W2", "W2", W2d, E * H, F)
         g_m("gemm fwd W2", qa2, sa2, qw2, sw2, M, H, F)
-        qdy, sdy = q_row("q_row dY", DYd, M, H)
-        qw2t, sw2t = q_col_batched("q_col W2", W2d, E, H, F)
+        qdy, sdy = q_row("q_row dY", "DY", DYd, M, H)
+        qw2t, sw2t = q_col_batched("q_col W2", "W2", W2d, E, H, F)
         g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, M, F, H)
-        qdyt, sdyt, ld = q_col_grouped("q_col dY", DYd, M, H)
-        qa2t, sa2t, _ = q_col_grouped("q_col A2", A2d, M, F)
+        qdyt, sdyt, ld = q_col_grouped("q_col dY", "DY", DYd, M, H)
+        qa2t, sa2t, _ = q_col_grouped("q_col A2", "A2", A2d, M, F)
         g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, ld, H, F)
-        qdh, sdh = q_row("q_row dH1", DH1d, M, F2)
-        qw1t, sw1t = q_col_batched("q_col W1", W1d, E, F2, H)
+        qdh, sdh = q_row("q_row dH1", "DH1", DH1d, M, F2)
+        qw1t, sw1t = q_col_batched("q_col W1", "W1", W1d, E, F2, H)
         g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, M, H, F2)
-        qdht, sdht, _ = q_col_grouped("q_col dH1", DH1d, M, F2)
-        qxt, sxt, _ = q_col_grouped("q_col X", Xd, M, H)
+        qdht, sdht, _ = q_col_grouped("q_col dH1", "DH1", DH1d, M, F2)
+        qxt, sxt, _ = q_col_grouped("q_col X", "X", Xd, M, H)
         g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, ld, F2, H)
         return step, host
 
@@ -251,45 +275,48 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False):
     Mp = fm.quantize_mx_rows_bound(M, E)
     K4 = fm.MX_LAYOUT_K4
 
-    def mx_last(name, x, rows, cols):
+    def mx_last(name, src, x, rows, cols):
         q, s = u8(rows, cols), u8(*fm.mx_k4_shape(rows, cols // 32))
         step.add(name, "quant", lambda: fm.quantize_mx(x().view(rows, cols), axis=1, rule=rule, q=q, scale=s,
                                                        layout=K4),
-                 qbytes(rows * cols, rows * cols // 32, 1))
+                 qbytes(rows * cols, rows * cols // 32, 1),
+                 spec=dict(op="mx_last", src=src, shape=(rows, cols), rule=rule, q=q, s=s))
         return q, s
 
-    def mx_rows_b(name, x, B, R, C):
+    def mx_rows_b(name, src, x, B, R, C):
         q, s = u8(B, C, R), u8(*fm.mx_k4_shape(B * C, R // 32))
         step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, rule=rule, q=q, scale=s, layout=K4),
-                 qbytes(B * R * C, B * C * R // 32, 1))
+                 qbytes(B * R * C, B * C * R // 32, 1),
+                 spec=dict(op="mx_rows_b", src=src, shape=(B, R, C), rule=rule, q=q, s=s))
         return q, s
 
     op = torch.empty(E, dtype=torch.int32, device=dev)
 
-    def mx_rows_g(name, x, rows, cols):
+    def mx_rows_g(name, src, x, rows, cols):
         q, s = u8(cols, Mp), u8(*fm.mx_k4_shape(cols, Mp // 32))
         step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
                                                        offs_pad=op, layout=K4),
-                 qbytes(rows * cols, cols * rows // 32, 1))
+                 qbytes(rows * cols, cols * rows // 32, 1),
+                 spec=dict(op="mx_rows_g", src=src, offs=offs_np, rows_pad=Mp, rule=rule, q=q, s=s, offs_pad=op))
         return q, s
 
-    qx, sx = mx_last("mx X", Xd, M, H)
-    qw1, sw1 = mx_last("mx W1", W1d, E * F2, H)
+    qx, sx = mx_last("mx X", "X", Xd, M, H)
+    qw1, sw1 = mx_last("mx W1", "W1", W1d, E * F2, H)
     g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H, sk=fm.SCALE_E8M0_K4)
-    qa2, sa2 = mx_last("mx A2", A2d, M, F)
-    qw2, sw2 = mx_last("mx W2", W2d, E * H, F)
+    qa2, sa2 = mx_last("mx A2", "A2", A2d, M, F)
+    qw2, sw2 = mx_last("mx W2", "W2", W2d, E * H, F)
     g_m("gemm fwd W2", qa2, sa2, qw2, sw2, M, H, F, sk=fm.SCALE_E8M0_K4)
-    qdy, sdy = mx_last("mx dY", DYd, M, H)
-    qw2t, sw2t = mx_rows_b("mx W2^T", W2d, E, H, F)
+    qdy, sdy = mx_last("mx dY", "DY", DYd, M, H)
+    qw2t, sw2t = mx_rows_b("mx W2^T", "W2", W2d, E, H, F)
     g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, M, F, H, sk=fm.SCALE_E8M0_K4)
-    qdyt, sdyt = mx_rows_g("mx dY^T", DYd, M, H)
-    qa2t, sa2t = mx_rows_g("mx A2^T", A2d, M, F)
+    qdyt, sdyt = mx_rows_g("mx dY^T", "DY", DYd, M, H)
+    qa2t, sa2t = mx_rows_g("mx A2^T", "A2", A2d, M, F)
     g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0_K4, offs_t=op)
-    qdh, sdh = mx_last("mx dH1", DH1d, M, F2)
-    qw1t, sw1t = mx_rows_b("mx W1^T", W1d, E, F2, H)
+    qdh, sdh = mx_last("mx dH1", "DH1", DH1d, M, F2)
+    qw1t, sw1t = mx_rows_b("mx W1^T", "W1", W1d, E, F2, H)
     g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, M, H, F2, sk=fm.SCALE_E8M0_K4)
-    qdht, sdht = mx_rows_g("mx dH1^T", DH1d, M, F2)
-    qxt, sxt = mx_rows_g("mx X^T", Xd, M, H)
+    qdht, sdht = mx_rows_g("mx dH1^T", "DH1", DH1d, M, F2)
+    qxt, sxt = mx_rows_g("mx X^T", "X", Xd, M, H)
     g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0_K4, offs_t=op)
     return step, host
 
@@ -309,62 +336,128 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(cfg: int, host: dict):
-    """The oracle timed on a bounded sample of the dense layer's work, scaled
-    linearly to the whole layer (us per layer): the rowwise and colwise
-    quantization of X, W and dY and the fwd/dgrad/wgrad GEMMs on row x column
-    samples (E = 1)."""
+def _k4_rows(k4, R, NB):
+    """e8m0 scales in the K4 layout [ceil(NB/4), R, 4] as row-major [R, NB] (a layout change only)."""
+    return np.ascontiguousarray(k4.transpose(1, 0, 2).reshape(R, 4 * k4.shape[0])[:, :NB])
+
+
+def cpu_baseline(step, host: dict):
+    """The oracle timed on a bounded sample of every launch of the step, each scaled linearly to its
+    full size (us per layer step):
+      * quantization: a slice of whole rows (rowwise, MX last-dim blocks) or whole columns (colwise,
+        MX row blocks) of about 2M elements, single-threaded numpy;
+      * GEMMs: a block of up to 1024 output rows x 4096 output columns of the largest group, over the
+        whole contraction, on the step's own operands copied to the host, fp64 BLAS; scaled by flops.
+    """
     import oracle
-    from threadpoolctl import threadpool_info
-    X, W = host["X"], host["W"]
-    DY = host.get("DY")
+    from threadpoolctl import threadpool_info, threadpool_limits
     total_us = 0.0
     pieces = []
+    QS = 1 << 21
 
-    def timed(fn):
+    def timed(fn, threads=None):
+        if threads == 1:
+            with threadpool_limits(1):
+                t0 = time.perf_counter()
+                fn()
+                return time.perf_counter() - t0
         t0 = time.perf_counter()
-        r = fn()
-        return r, time.perf_counter() - t0
+        fn()
+        return time.perf_counter() - t0
 
     def add(name, secs, factor):
         nonlocal total_us
         total_us += secs * factor * 1e6
         pieces.append(f"{name} x{factor:.0f}")
 
-    rs = 128
-    for name, T in [("q_row X", X), ("q_row W", W)] + ([("q_row dY", DY)] if DY is not None else []):
-        (_, t) = timed(lambda: oracle.quantize_rowwise(T[:rs], 0))
-        add(name, t, T.shape[0] / rs)
-    cs = 32
-    offs1 = np.array([X.shape[0]], np.int32)
-    if DY is not None:
-        for name, T in [("q_col X", X), ("q_col dY", DY), ("q_col W", W)]:
-            (_, t) = timed(lambda: oracle.quantize_colwise_grouped(np.ascontiguousarray(T[:, :cs]),
-                                                                   np.array([T.shape[0]], np.int32), 0))
-            add(name, t, T.shape[1] / cs)
-    gm, gn = 32, 512
-    qa, sa = oracle.quantize_rowwise(X[:gm], 0)
-    qb, sb = oracle.quantize_rowwise(W[:gn], 0)
-    (_, t) = timed(lambda: oracle.mm_grouped_m(qa, sa, qb[None], sb[None], np.array([gm], np.int32), 0, 0))
-    n_gemm = 1
-    add("gemm fwd", t, (X.shape[0] / gm) * (W.shape[0] / gn))
-    if DY is not None:
-        qd, sd = oracle.quantize_rowwise(DY[:gm], 0)
-        qwt, swt = oracle.quantize_colwise_batched(np.ascontiguousarray(W[:, :gn])[None], 0)
-        (_, t) = timed(lambda: oracle.mm_grouped_m(qd, sd, qwt, swt, np.array([gm], np.int32), 0, 0))
-        add("gemm dgrad", t, (DY.shape[0] / gm) * (W.shape[1] / gn))
-        qdt, sdt = oracle.quantize_colwise_grouped(np.ascontiguousarray(DY[:, :gm]), offs1, 0)
-        qxt, sxt = oracle.quantize_colwise_grouped(np.ascontiguousarray(X[:, :gn]), offs1, 0)
-        (_, t) = timed(lambda: oracle.mm_grouped_k(qdt, sdt, qxt, sxt, offs1, 0, 0))
-        add("gemm wgrad", t, (DY.shape[1] / gm) * (X.shape[1] / gn))
-        n_gemm = 3
+    def h(t):
+        import torch
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    def src(name):
+        return host["W1"] if name == "W1" else host[name]
+
+    for name, kind, *_ in step.items:
+        sp = step.specs.get(name)
+        if sp is None:
+            continue
+        op = sp["op"]
+        if op in ("q_row", "mx_last"):
+            R, C = sp["shape"]
+            x = src(sp["src"]).reshape(R, C)
+            r = max(1, min(R, QS // max(C, 1)))
+            f = (lambda: oracle.quantize_rowwise(x[:r], 0)) if op == "q_row" else \
+                (lambda: oracle.quantize_mx_lastdim(x[:r], sp["rule"]))
+            add(name, timed(f, 1), R / r)
+        elif op in ("q_col_grouped", "mx_rows_g"):
+            x = src(sp["src"])
+            M, C = x.shape
+            c = max(8, min(C, QS // max(M, 1)) // 8 * 8)
+            xs = np.ascontiguousarray(x[:, :c])
+            f = (lambda: oracle.quantize_colwise_grouped(xs, sp["offs"], 0)) if op == "q_col_grouped" else \
+                (lambda: oracle.quantize_mx_rows_grouped(xs, sp["offs"], sp["rule"], sp["rows_pad"]))
+            add(name, timed(f, 1), C / c)
+        elif op in ("q_col_batched", "mx_rows_b"):
+            B, R, C = sp["shape"]
+            x = src(sp["src"]).reshape(B, R, C)
+            c = max(8, min(C, QS // max(B * R, 1)) // 8 * 8)
+            xs = np.ascontiguousarray(x[:, :, :c])
+            f = (lambda: oracle.quantize_colwise_batched(xs, 0)) if op == "q_col_batched" else \
+                (lambda: oracle.quantize_mx_rows_batched(xs, sp["rule"]))
+            add(name, timed(f, 1), C / c)
+        elif op == "g_m":
+            M, N, K = sp["M"], sp["N"], sp["K"]
+            offs = sp["offs"]
+            lo, hi = oracle.group_bounds(offs, M)
+            e = int(np.argmax(hi - lo))
+            m, n = min(1024, int(hi[e] - lo[e])), min(4096, N)
+            rows = slice(int(lo[e]), int(lo[e]) + m)
+            qa = h(sp["qa"][rows])
+            qb = h(sp["qb"].view(len(offs), N, K)[e, :n])[None]
+            one = np.array([m], np.int32)
+            if sp["sk"] == 0:
+                sa, sb = h(sp["sa"][rows]), h(sp["sb"].view(len(offs), N)[e, :n])[None]
+                f = lambda: oracle.mm_grouped_m(qa, sa, qb, sb, one, 0, 0)
+            else:
+                sa = _k4_rows(h(sp["sa"]), M, K // 32)[rows]
+                sb = _k4_rows(h(sp["sb"]), len(offs) * N, K // 32).reshape(len(offs), N, K // 32)[e:e + 1, :n]
+                f = lambda: oracle.mm_grouped_m_mx(qa, sa, qb, sb, one)
+            full = 2.0 * float((hi - lo).sum()) * N * K
+            add(name, timed(f), full / (2.0 * m * n * K))
+        elif op == "g_k":
+            Mc, N, K = sp["M"], sp["N"], sp["K"]
+            offs = sp["offs"] if isinstance(sp["offs"], np.ndarray) else h(sp["offs"])
+            lo, hi = oracle.group_bounds(offs, Mc)
+            e = int(np.argmax(hi - lo))
+            n, k = min(1024, N), min(4096, K)
+            cols = slice(int(lo[e]), int(hi[e]))
+            qa, qb = h(sp["qa"][:n])[:, cols], h(sp["qb"][:k])[:, cols]
+            one = np.array([int(hi[e] - lo[e])], np.int32)
+            if sp["sk"] == 0:
+                sa, sb = h(sp["sa"][e:e + 1, :n]), h(sp["sb"][e:e + 1, :k])
+                f = lambda: oracle.mm_grouped_k(np.ascontiguousarray(qa), sa, np.ascontiguousarray(qb), sb, one, 0, 0)
+            else:
+                sa = _k4_rows(h(sp["sa"]), N, Mc // 32)[:n, int(lo[e]) // 32:int(hi[e]) // 32]
+                sb = _k4_rows(h(sp["sb"]), K, Mc // 32)[:k, int(lo[e]) // 32:int(hi[e]) // 32]
+                f = lambda: oracle.mm_grouped_k_mx(np.ascontiguousarray(qa), sa, np.ascontiguousarray(qb), sb, one)
+            full = 2.0 * float((hi - lo).sum()) * N * K
+            add(name, timed(f), full / (2.0 * n * k * float(hi[e] - lo[e])))
+        elif op == "g_k_bf16":
+            a, b = host[sp["a"]], host[sp["b"]]
+            Mt, N = a.shape
+            K = b.shape[1]
+            n, k = min(1024, N), min(4096, K)
+            an, bk = np.ascontiguousarray(a[:, :n]), np.ascontiguousarray(b[:, :k])
+            add(name, timed(lambda: oracle.mm_grouped_k_bf16(an, bk, sp["offs"])), (N * K) / (n * k))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(total_us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(), "cpu_count": os.cpu_count(),
-            "sample": f"numpy oracle on row/column samples scaled linearly to the full layer "
-                      f"(quant: {rs} rows or {cs} columns per tensor, single-threaded; GEMM: {gm} x {gn} output "
-                      f"samples, fp64 BLAS with {threads} threads); {n_gemm} GEMMs + "
-                      f"{len(pieces) - n_gemm} quant calls: " + ", ".join(pieces)}
+            "sample": f"numpy oracle on a bounded sample of every launch of the step, each scaled linearly to its "
+                      f"full size (quantization: about {QS} elements of whole rows or columns, one thread; GEMMs: up "
+                      f"to 1024 x 4096 outputs of the largest group over the whole contraction, fp64 BLAS with "
+                      f"{threads} threads, scaled by flops): " + ", ".join(pieces)}
 
 
 # ---------------------------------------------------------------------- traffic evidence
@@ -697,7 +790,9 @@ def main():
 
     if args.tensorwise and args.config != 2:
         raise SystemExit("--tensorwise is built for config 2 (the Llama3-8B linear layer)")
-    step, host = build_step(args.config, args.gw, args.tensorwise)
+    progress(f"config {args.config}: inputs")
+    step, host = build_step(args.config, args.gw, args.tensorwise, keep_host=not args.no_cpu_baseline)
+    progress(f"config {args.config}: {len(step.items)} launches; warm-up")
     stream = torch.cuda.current_stream()
     names = [it[0] for it in step.items]
     for w_i in range(args.warmup):
@@ -753,8 +848,11 @@ def main():
         b, a, pk, _ = roof(*v)
         fracs[k] = {"bound": b, "frac": round(a / pk, 4)}
 
+    progress(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us per step")
     extras = args.only is None and not args.no_per_kernel
     flushed = per_kernel_flushed(step, stream) if extras else {}
+    if extras:
+        progress("per-kernel pass done")
     w = synth.WORKLOADS[args.config]
     out = {
         "metric": "quant HBM GB/s + grouped-GEMM TFLOP/s; us per MoE layer (quant+GEMM)",
@@ -798,10 +896,11 @@ def main():
         out["blockwise_recipe"] = blockwise_extras(stream)
     if args.route and args.config in (3, 4):
         out["routing"] = route_extras(args.config, stream)
-    if not args.no_cpu_baseline and args.config == 2 and not args.tensorwise:
-        out["cpu_baseline"] = cpu_baseline(args.config, host)
+    if not args.no_cpu_baseline and args.only is None and not args.tensorwise:
+        progress("oracle baseline on the host")
+        out["cpu_baseline"] = cpu_baseline(step, host)
     else:
-        out["cpu_baseline"] = None      # sampled oracle timing is defined for the default workload
+        out["cpu_baseline"] = None      # the tensorwise recipe's launches carry no oracle spec
     print(json.dumps(out), flush=True)
 
 

@@ -45,7 +45,12 @@
  *     e4m3fn keeps the sign of a zero result (0x80); e4m3fnuz has one unsigned
  *     zero and never emits 0x80.  No subnormal is flushed.
  *   - Calls on different streams may run concurrently from several host
- *     threads; they share no mutable library state.
+ *     threads.  The only mutable library state is the device array the
+ *     single-pass colwise quantizer exchanges column maxima through (see
+ *     quantize_colwise: its values are tagged per call, so overlapping calls
+ *     stay correct) and that quantizer's poll budget, a test hook
+ *     (fp8moe_set_colwise_poll_budget).  Everything else a call needs is in
+ *     its arguments.
  */
 #ifndef FP8MOE_H
 #define FP8MOE_H
@@ -376,12 +381,14 @@ int moe_combine(const void *yg_bf16, int64_t rows_in, const int32_t *dest,
  *   read once into registers, and the chunks of a group exchange their column
  *   maxima through a fixed library-owned device array (32768 chunk slots, no
  *   allocation) before casting from registers.  Values in that array carry a
- *   per-call tag, so calls need no reset and leave nothing behind.  Calls that
- *   overlap on one device (other streams) stay correct: a chunk that cannot
- *   complete the exchange recomputes the maxima from x itself, at the cost of
- *   a second read.  A group taller than 128 chunks, or a call with more than
- *   32768 chunks, instead takes three kernels (amax reset, partial amax, cast)
- *   and reads x twice.
+ *   per-call tag (a host counter), so calls need no reset and leave nothing
+ *   behind.  Calls that overlap on one device (other streams) stay correct: a
+ *   chunk whose peers do not all publish within a bounded number of polls
+ *   recomputes the maxima from x itself, at the cost of a second read.  A
+ *   group taller than 128 chunks, a call with more than 32768 chunks, or a
+ *   call made while `stream` is being captured into a graph (where a replay
+ *   would repeat the tag) instead takes three kernels (amax reset, partial
+ *   amax, cast): x is read twice, and no state carries between launches.
  */
 int quantize_colwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
                      const int32_t *offs, int32_t n_groups, int codec,
@@ -476,6 +483,16 @@ int fp8moe_default_codec(int hip_device, int *codec_out);
 
 /* Library ABI version (major*100 + minor). */
 int fp8moe_version(void);
+
+/*
+ * fp8moe_set_colwise_poll_budget -- test hook: the number of polls a chunk of
+ * the single-pass colwise quantizer makes for its peers' column maxima before
+ * it recomputes them from x (0: recompute at once; negative: restore the
+ * default, 4096).  Results do not depend on it, only the time a call takes;
+ * tests use 0 to run the recomputation path.  It applies to calls enqueued
+ * after it returns.  Returns the previous budget.  Host only, no HIP call.
+ */
+int fp8moe_set_colwise_poll_budget(int polls);
 
 #ifdef __cplusplus
 }

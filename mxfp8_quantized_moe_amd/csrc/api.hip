@@ -217,6 +217,8 @@ int fp8moe_default_codec(int hip_device, int* codec_out) {
   return FP8MOE_ERR_UNSUPPORTED;
 }
 
-int fp8moe_version(void) { return 101; }
+int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(polls); }
+
+int fp8moe_version(void) { return 102; }
 
 }  // extern "C"

@@ -35,6 +35,9 @@ struct GemmArgs {
 
 hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st);
 
+// Poll budget of the single-pass colwise exchange (negative: the default); returns the previous one.
+int set_colwise_poll_budget(int polls);
+
 hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st);
 hipError_t launch_quantize_blockwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,
                                      int codec, uint8_t* q, float* scale, hipStream_t st);

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void colwise_kernel(const uint16_t* __restrict
 // result never depends on timing.
 constexpr int kSlotItems = 32768;           // chunk slots (16 MiB); more chunks take the two-pass path
 constexpr int kMaxChunks = 128;             // taller groups take the two-pass path
-constexpr int kPolls = 4096;                // sleeps of ~512 cycles (plus a load) before the fallback
+constexpr int kPolls = 4096;                // default: sleeps of ~512 cycles (plus a load) before the fallback
 __device__ unsigned long long g_cw_part[kSlotItems][kTileCols];
 
 // Maxima of 64 columns over rows [lo, hi) of group rows in_base + r, read
@@ -256,11 +256,11 @@ __device__ __forceinline__ void cw_column_max(const uint16_t* __restrict__ x, in
 // the nch chunks starting at item0, 8 slots per round trip.  Returns whether
 // all arrived within the poll budget (then out[t] holds the maximum).
 __device__ __forceinline__ bool cw_gather(const unsigned long long* __restrict__ part, int item0, int nch,
-                                          uint32_t gen, uint32_t* out) {
+                                          uint32_t gen, int max_polls, uint32_t* out) {
   const int t = threadIdx.x;
   uint32_t mx = 0;
   int k = 0;
-  for (int polls = 0; k < nch && polls < kPolls;) {
+  for (int polls = 0; k < nch && polls < max_polls;) {
     unsigned long long b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -287,7 +287,8 @@ template <int CODEC, bool GROUPED>
 __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __restrict__ x, int64_t batch,
                                                              int rows, int cols, const int32_t* __restrict__ offs,
                                                              int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
-                                                             float* __restrict__ scale, int units, uint32_t gen) {
+                                                             float* __restrict__ scale, int units, uint32_t gen,
+                                                             int max_polls) {
   __shared__ uint32_t red[4 * 8 * 4];
   __shared__ uint32_t s_amax[64];
   __shared__ float s_scale[64];
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
     if (t < 64) {
       __hip_atomic_store(part + (int64_t)blockIdx.x * kTileCols + t, ((unsigned long long)gen << 32) | s_amax[t],
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool ok = cw_gather(part, (int)blockIdx.x - g.j, nch, gen, s_amax);
+      const bool ok = cw_gather(part, (int)blockIdx.x - g.j, nch, gen, max_polls, s_amax);
       if (t == 0) s_ok = ok;
     }
     __syncthreads();
@@ -366,7 +367,12 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
 }
 
 // One generation per call of the single-pass kernel (0 never names a call).
+// A generation is a kernel argument, so a launch captured into a graph would
+// replay with the same one and could accept a previous replay's slots: calls
+// made while their stream is capturing take the two-pass path instead, whose
+// reset is an ordinary kernel and which keeps no state between launches.
 static std::atomic<uint32_t> g_generation{0};
+static std::atomic<int> g_poll_budget{kPolls};
 static uint32_t next_generation() {
   uint32_t g = g_generation.fetch_add(1) + 1;
   if (g == 0) g = g_generation.fetch_add(1) + 1;
@@ -390,10 +396,13 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
   const int64_t items = units * n_strips;
   // most chunks one group can span: a grouped group may start 15 rows past a 16-row anchor
   const int64_t nch_bound = ((GROUPED ? rows + 15 : rows) + kTileRows - 1) / kTileRows;
-  if (nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess) return hipGetLastError();
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  if (!capturing && nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
     hipLaunchKernelGGL((colwise_single_kernel<CODEC, GROUPED>), dim3((unsigned)items), dim3(256), 0, st, x,
                        batch, (int)rows, (int)cols, offs, n_groups, q_t, ld_q, scale, (int)units,
-                       next_generation());
+                       next_generation(), g_poll_budget.load());
     return hipGetLastError();
   }
   hipLaunchKernelGGL(colwise_reset_kernel, dim3((unsigned)((n_scale + 255) / 256)), dim3(256), 0, st,
@@ -405,6 +414,8 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
                      (int)cols, offs, n_groups, q_t, ld_q, scale, n_strips, (int)units);
   return hipGetLastError();
 }
+
+int set_colwise_poll_budget(int polls) { return g_poll_budget.exchange(polls < 0 ? kPolls : polls); }
 
 hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                    const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,

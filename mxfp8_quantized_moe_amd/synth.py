@@ -51,10 +51,16 @@ def normal_bf16(seed: int, shape, sigma: float, outlier_frac: float = 0.0,
 
 def expert_weights_bf16(base_seed: int, n_experts: int, rows: int, cols: int,
                         sigma: float) -> np.ndarray:
-    """[E, rows, cols] bf16 bits; expert e is drawn from seed 1000*base_seed + e."""
+    """[E, rows, cols] bf16 bits; expert e is drawn from seed 1000*base_seed + e (experts are
+    independent streams, drawn on several host threads; the values do not depend on that)."""
+    import concurrent.futures as cf
     out = np.empty((n_experts, rows, cols), dtype=np.uint16)
-    for e in range(n_experts):
+
+    def one(e):
         out[e] = normal_bf16(1000 * base_seed + e, (rows, cols), sigma)
+
+    with cf.ThreadPoolExecutor(min(8, max(n_experts, 1))) as ex:
+        list(ex.map(one, range(n_experts)))
     return out
 
 

@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 8):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 101
+    assert lib.fp8moe_version() == 102
 
 
 def test_rows_bound(lib):
@@ -304,3 +304,15 @@ def test_no_undefined_internal_symbols():
     """Every kernel launch stub and internal function resolves inside the library."""
     und = os.popen(f"nm -D --undefined-only {L.LIB_PATH}").read()
     assert "fp8moe" not in und, [l for l in und.splitlines() if "fp8moe" in l][:5]
+
+
+def test_colwise_poll_budget_hook(lib):
+    """Host-only test hook: returns the previous budget; negative restores the default."""
+    f = lib.fp8moe_set_colwise_poll_budget
+    first = f(7)
+    try:
+        assert f(0) == 7
+        assert f(-1) == 0
+        assert f(-1) == 4096
+    finally:
+        f(first)

@@ -308,3 +308,147 @@ def test_mx_full_size_sampled():
     assert_bytes_equal(host(op), opr, "padded offsets")
     assert_bytes_equal(host(q)[cols], qr, "codes rows")
     assert_bytes_equal(host(sc)[cols], sr, "e8m0 rows")
+
+
+# ------------------------------------------------------------------- edge cases
+
+def _subnormal_bf16(seed, shape):
+    """bf16 patterns of nonzero subnormals only (exponent field 0), random signs."""
+    rng = np.random.default_rng(seed)
+    mant = rng.integers(1, 128, size=shape).astype(np.uint16)
+    sign = (rng.random(shape) < 0.5).astype(np.uint16) << np.uint16(15)
+    return (mant | sign).astype(np.uint16)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_mx_all_subnormal_blocks(rule):
+    """Blocks made only of bf16 subnormals: the shared exponent clamps at -127 (e8m0 code 0) and
+    x * 2^127 stays non-zero, so no code of a non-zero input may be zero (no flush to zero)."""
+    R, C = 64, 256
+    x = _subnormal_bf16(71, (R, C))
+    x[5, 32:64] = 0                  # one all-zero block beside them
+    x[9, :32] = 1                    # the smallest subnormal, 2^-133, everywhere in a block
+    note(f"mx all-subnormal rule={rule}")
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule)
+    qr, sr = oracle.quantize_mx_lastdim(x, rule)
+    assert_bytes_equal(host(q), qr, "codes")
+    assert_bytes_equal(host(sc), sr, "e8m0")
+    assert not host(sc).any(), "subnormal blocks take X = -127 (code 0)"
+    nz = x.reshape(R, C) & 0x7FFF != 0
+    assert np.all(host(q)[nz] & 0x7F != 0), "a subnormal input was flushed to a zero code"
+    _, sk, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule, layout=fm.MX_LAYOUT_K4)
+    assert_bytes_equal(host(sk), e8m0_rows_to_k4(sr), "e8m0 K4")
+    xb = x.reshape(2, 32, C)         # row blocks, batched
+    q, sc, _ = fm.quantize_mx(bf16_dev(xb), axis=0, rule=rule)
+    qr, sr = oracle.quantize_mx_rows_batched(xb, rule)
+    assert_bytes_equal(host(q), qr, "row-block codes")
+    assert_bytes_equal(host(sc), sr, "row-block e8m0")
+    offs = np.array([20, 20, 64], np.int32)          # grouped, with an empty group and padding
+    Mp = fm.quantize_mx_rows_bound(R, 3)
+    q, sc, op = fm.quantize_mx(bf16_dev(x), axis=0, offs=i32_dev(offs), rule=rule, rows_pad=Mp)
+    qr, sr, opr = oracle.quantize_mx_rows_grouped(x, offs, rule, Mp)
+    assert_bytes_equal(host(q), qr, "grouped codes")
+    assert_bytes_equal(host(sc), sr, "grouped e8m0")
+    assert_bytes_equal(host(op), opr, "padded offsets")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_colwise_wait_fallback_bit_exact(codec):
+    """With a poll budget of 0 every chunk of a multi-chunk group recomputes its group's column
+    maxima from x (the path a chunk takes when its peers do not publish in time); every kernel
+    still exits normally and the result is the same, bit for bit."""
+    lib = fm._lib.lib()
+    M, C = 3000, 200
+    x = special_input(7100 + codec, (M, C))
+    offs = np.array([1300, 1300, 2950], np.int32)    # groups of 1300 and 1650 rows (3-4 chunks), an empty one
+    qr, sr = oracle.quantize_colwise_grouped(x, offs, codec)
+    xb = special_input(7200 + codec, (2, 1100, 64))
+    qbr, sbr = oracle.quantize_colwise_batched(xb, codec)
+    prev = lib.fp8moe_set_colwise_poll_budget(0)
+    try:
+        note(f"colwise with no polls codec={codec}")
+        q, s = fm.quantize_colwise(bf16_dev(x), i32_dev(offs), codec)
+        qb, sb = fm.quantize_colwise(bf16_dev(xb), None, codec, ld_q=1104)
+        qh, qbh = host(q), host(qb)
+    finally:
+        lib.fp8moe_set_colwise_poll_budget(prev)
+    assert_bytes_equal(qh[:, :2950], qr[:, :2950], "codes")
+    assert_f32_bits_equal(host(s), sr, "scales")
+    assert_bytes_equal(qbh[:, :, :1100], qbr, "batched codes")
+    assert_f32_bits_equal(host(sb), sbr, "batched scales")
+
+
+def test_colwise_graph_replays():
+    """A call captured into a HIP graph and replayed with new inputs (eager calls in between, which
+    advance the single-pass kernel's tag) gives the oracle's result on every replay."""
+    M, C = 2000, 136
+    offs = np.array([700, 700, 1900], np.int32)
+    xs = bf16_dev(special_input(7300, (M, C)))
+    ws = bf16_dev(special_input(7301, (3, 640, 64)))
+    od = i32_dev(offs)
+    q, s = filled_u8((C, M)), filled_f32((3, C))
+    qw, sw = filled_u8((3, 64, 640)), filled_f32((3, 64))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up off the default stream, as capture requires
+        fm.quantize_colwise(xs, od, 0, q_t=q, scale=s)
+        fm.quantize_colwise(ws, None, 0, q_t=qw, scale=sw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("colwise graph capture")
+    with torch.cuda.graph(g):
+        fm.quantize_colwise(xs, od, 0, q_t=q, scale=s)
+        fm.quantize_colwise(ws, None, 0, q_t=qw, scale=sw)
+    for rep in range(4):
+        xh = special_input(7310 + rep, (M, C), sigma=4.0 ** rep)
+        wh = special_input(7320 + rep, (3, 640, 64), sigma=0.5 ** rep)
+        xs.copy_(bf16_dev(xh))
+        ws.copy_(bf16_dev(wh))
+        fm.quantize_colwise(bf16_dev(special_input(7330 + rep, (M, C))), od, 0)    # eager call in between
+        torch.cuda.synchronize()
+        note(f"colwise graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        qr, sr = oracle.quantize_colwise_grouped(xh, offs, 0)
+        assert_bytes_equal(host(q)[:, :1900], qr[:, :1900], f"replay {rep} codes")
+        assert_f32_bits_equal(host(s), sr, f"replay {rep} scales")
+        qwr, swr = oracle.quantize_colwise_batched(wh, 0)
+        assert_bytes_equal(host(qw), qwr, f"replay {rep} batched codes")
+        assert_f32_bits_equal(host(sw), swr, f"replay {rep} batched scales")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_device_encoder_monotone_exhaustive(codec):
+    """Every fp32 value in [0, fmax], encoded on the device: codes never decrease as the value
+    grows, and -y encodes as y with the sign bit (e4m3fnuz: a zero code stays 0x00).  With the
+    midpoint probes of test_device_encoder_matches_oracle (every rounding boundary +-1 ulp) this
+    fixes the encoder on every input: between two boundaries a monotone encoder is constant."""
+    fm_bits = int(np.float32(oracle.FMAX[codec]).view(np.uint32))
+    chunk = 1 << 27
+    last = -1
+    note(f"encoder sweep codec={codec} values={fm_bits + 1}")
+    for start in range(0, fm_bits + 1, chunk):
+        stop = min(start + chunk, fm_bits + 1)
+        y = torch.arange(start, stop, dtype=torch.int32, device=DEV).view(torch.float32)
+        qp = fm.encode_f32(y, codec).to(torch.int32)
+        qn = fm.encode_f32(-y, codec).to(torch.int32)
+        assert bool((qp[1:] >= qp[:-1]).all()), f"codes decrease inside [{start}, {stop})"
+        assert int(qp[0]) >= last, f"codes decrease at bit pattern {start}"
+        assert int(qp.max()) <= (0x7E if codec == 0 else 0x7F) and int(qp.min()) >= 0
+        want_n = qp | 0x80 if codec == 0 else torch.where(qp == 0, qp, qp | 0x80)
+        assert bool((qn == want_n).all()), f"negative values inside [{start}, {stop})"
+        last = int(qp[-1])
+        del y, qp, qn
+    assert last == (0x7E if codec == 0 else 0x7F)
+    torch.cuda.synchronize()
+
+
+def test_default_codec_on_gfx950():
+    """fp8moe_default_codec picks the OCP e4m3fn codec on gfx950 (its FP8 matrix cores take it)."""
+    import ctypes
+    out = ctypes.c_int(-1)
+    assert fm._lib.lib().fp8moe_default_codec(torch.cuda.current_device(), ctypes.byref(out)) == 0
+    assert out.value == fm.E4M3FN
+    assert fm.default_codec() == fm.E4M3FN
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName

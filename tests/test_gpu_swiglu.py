@@ -61,6 +61,7 @@ def assert_within_one_ulp(got: np.ndarray, ref: np.ndarray, what: str) -> None:
         i = np.unravel_index(np.argmax(d), d.shape)
         assert d.max() <= 1, f"{what}: {int((d > 1).sum())} elements beyond 1 bf16 ulp; worst at {i}: " \
                              f"got {got[i]:#06x} ref {ref[i]:#06x}"
+        note(f"{what}: {int((d > 0).sum())} of {d.size} elements one bf16 ulp off ({(d > 0).mean():.3e})")
         assert (d > 0).mean() < 0.01, f"{what}: {(d > 0).mean():.2%} of elements off by one ulp"
 
 

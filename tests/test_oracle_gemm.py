@@ -176,3 +176,69 @@ def test_bounds_reject_planted_mistakes():
     perm = rng.permutation(128)
     wrong_k = oracle.mm_grouped_m(qa[:, perm], sa, qb, sb, offs, E4M3FN, E4M3FN)   # mis-indexed K
     assert np.any(np.abs(wrong_k - ref) > contract)
+
+
+def _bounds_k_by_hand(A, B, lo, hi, acc):
+    """Pure-Python loops: the GROUPED_K contract bound 1e-2 * |a_row| * |b_col| and the diagnostic
+    2^-8 |ref| + rel * sum|a*b|, norms and sums over the group's tokens [lo, hi) only."""
+    N, K = A.shape[0], B.shape[0]
+    contract = [[0.0] * K for _ in range(N)]
+    tight = [[0.0] * K for _ in range(N)]
+    rel = max(hi - lo, 1) * 2.0 ** -23 if acc == oracle.ACC_FP32 else 2.0 ** -10
+    for n in range(N):
+        na = sum(float(A[n, m]) ** 2 for m in range(lo, hi)) ** 0.5
+        for k in range(K):
+            nb = sum(float(B[k, m]) ** 2 for m in range(lo, hi)) ** 0.5
+            ref = sum(Fraction(float(A[n, m])) * Fraction(float(B[k, m])) for m in range(lo, hi))
+            absdot = sum(abs(Fraction(float(A[n, m])) * Fraction(float(B[k, m]))) for m in range(lo, hi))
+            contract[n][k] = 1e-2 * na * nb
+            tight[n][k] = 2.0 ** -8 * abs(float(ref)) + rel * float(absdot)
+    return np.array(contract), np.array(tight)
+
+
+@pytest.mark.parametrize("acc", [oracle.ACC_FP32, oracle.ACC_FP8_MFMA])
+def test_error_bounds_k_brute_force_two_groups(acc):
+    """Per group, norms and |a*b| sums run over that group's tokens only; an empty group (and a
+    decreasing offset) gets zero bounds, so only exact zeros pass there."""
+    rng = np.random.default_rng(21)
+    N, K, M = 3, 4, 11
+    A = rng.standard_normal((N, M)) * np.array([10.0] * 4 + [0.01] * 7)   # group 0 tokens much larger
+    B = rng.standard_normal((K, M))
+    offs = np.array([4, 4, 11, 9], np.int32)                           # groups [0,4), [], [4,11), []
+    contract, tight = oracle.error_bounds_k(A, B, offs, acc)
+    assert contract.shape == tight.shape == (4, N, K)
+    for e, (lo, hi) in enumerate([(0, 4), (4, 4), (4, 11), (11, 11)]):
+        c, t = _bounds_k_by_hand(A, B, lo, hi, acc)
+        np.testing.assert_allclose(contract[e], c, rtol=1e-12, atol=0)
+        np.testing.assert_allclose(tight[e], t, rtol=1e-12, atol=0)
+    assert not contract[1].any() and not contract[3].any()
+
+
+def test_error_bounds_k_catches_slicing_mistakes():
+    """Planted mistakes about the group's token range.  (1) A bound that takes its norms over all M
+    tokens instead of the group's disagrees with the loops above.  (2) A weight gradient of group 1
+    that drops the group's last token (an off-by-one slicing mistake in a kernel) is outside the
+    real bound, but inside the loosened bound of mistake (1); so is (3) one that contracts group 1
+    over every token."""
+    rng = np.random.default_rng(22)
+    N, K, M = 5, 6, 40
+    scale = np.where(np.arange(M) < 24, 1.0, 1e-3)                    # group 0 dominates the norms
+    A = rng.standard_normal((N, M)) * scale
+    B = rng.standard_normal((K, M)) * scale
+    offs = np.array([24, 40], np.int32)
+
+    def bounds_over_all_tokens(A_t, B_t, offs_, acc=oracle.ACC_FP32):   # the planted mistake (1)
+        c, t = oracle.error_bounds_k(A_t, B_t, np.array([A_t.shape[1]], np.int32), acc)
+        return np.repeat(c, len(offs_), 0), np.repeat(t, len(offs_), 0)
+
+    c_bad, _ = bounds_over_all_tokens(A, B, offs)
+    c_hand, _ = _bounds_k_by_hand(A, B, 24, 40, oracle.ACC_FP32)
+    assert not np.allclose(c_bad[1], c_hand, rtol=1e-6)                 # the loops catch it
+    contract, _ = oracle.error_bounds_k(A, B, offs)
+    np.testing.assert_allclose(contract[1], c_hand, rtol=1e-12)
+    ref1 = A[:, 24:] @ B[:, 24:].T
+    short1 = A[:, 24:39] @ B[:, 24:39].T                                # mistake (2): last token dropped
+    assert np.any(np.abs(short1 - ref1) > contract[1])
+    assert np.all(np.abs(short1 - ref1) <= c_bad[1])                   # the mutant bound would pass it
+    wrong1 = A @ B.T                                                    # mistake (3): every token
+    assert np.any(np.abs(wrong1 - ref1) > contract[1])
