@@ -12,33 +12,36 @@
 //   GROUPED_K (wgrad):     P = A phys [n][M], Q = B phys [k][M], contraction
 //                          over the token range [lo(e), hi(e)) of group e.
 //
-// Tiling, derived from the hardware rather than searched:
+// Two kernels, tiling derived from the hardware rather than searched:
 //  * v_mfma_scale_f32_32x32x64_f8f6f4: each lane holds one row (lane & 31) and
 //    two 16-byte halves of the 64-wide contraction at byte offsets 16*g and
 //    32 + 16*g (g = lane >> 5); the e8m0 scale of (row i, 32-block b) comes
-//    from lane i + 32*b.  The 32x32 fp32 result sits in 16 registers: column
-//    lane & 31, row 8*(v/4) + 4*(lane>>5) + v%4.
+//    from lane i + 32*b.  FP8 operands pass scale 0 (2^0).
 //  * 256 threads = 2x2 waves; a wave owns (BM/2) x (BN/2) outputs.  BM = BN =
 //    256 gives 4x4 MFMA tiles per wave = 256 fp32 accumulators per lane, the
 //    largest tile that fits one wave per SIMD (512 registers) and makes each
 //    byte read from LDS feed 128 flops per wave.
-//  * With one wave per SIMD nothing else hides memory latency, so operands
-//    stream through a 4-slot LDS ring of 64-byte contraction stages
-//    ((BM + BN) x 64 B = 32 KiB per stage, 128 KiB in all) with 4 stages in
-//    flight: gfx950's direct global->LDS loads (global_load_lds_dwordx4) move
-//    the data without staging registers, one barrier per stage.  MFMA
-//    fragments are double-buffered in registers: stage k's MFMAs issue while
-//    stage k+1's fragments are read, so LDS latency stays off the MFMA path.
-//  * LDS rows are 64 B (4 chunks of 16 B); chunk c of row r is stored at chunk
-//    c ^ ((r >> 2) & 3), so 16 consecutive lanes reading one logical chunk of
-//    16 consecutive rows touch 16 distinct 16-byte bank groups.  A wave's
-//    DMA fills 1 KiB contiguously (16 rows); each lane fetches the global chunk
-//    that belongs at its LDS slot, which realises the swizzle for free.
+//  * gemm_fp8_pipe (every FP8 call, and MX calls with K4 scales or 4-byte
+//    aligned row-major scales): persistent, at most one workgroup per CU
+//    walking its tiles with a grid stride.  Operands stream through an LDS ring
+//    of 128-byte contraction stages (whole cache lines of the K-contiguous
+//    operands): two 64 KiB slots for 256 x 256 tiles, three 48 KiB slots for
+//    128 x 256 tiles, filled by gfx950's direct global->LDS loads
+//    (global_load_lds_dwordx4) with no staging registers.  The steady-state
+//    step is branch-free: one wait and barrier per stage, then the refill of
+//    the freed slot and the fragment reads of the next k step interleaved
+//    (sched_group_barrier) between the MFMAs of the current one.  Consecutive
+//    tiles overlap: the next tile's first stages land during the epilogue,
+//    which stages bf16 results through LDS so every store writes whole
+//    128-byte row segments.  Details at the kernel.
+//  * gemm_fp8_kernel (MX operands whose row-major e8m0 rows are not 4-byte
+//    aligned per stage): one workgroup per tile, 64-byte stages in a 4-slot
+//    ring, e8m0 scales loaded a byte at a time.
 //  * Small groups (average rows per group below 512) use BM = 128 to waste
 //    less of each tile on padding rows.
-//  * Workgroups are numbered so that each XCD (round-robin dispatch over 8)
-//    gets a contiguous range of tiles, ordered in bands of 8 row tiles, so the
-//    tiles running together on one XCD share operand rows in its L2.
+//  * Tiles are ordered in bands of 8 row tiles, and each XCD (dispatch is
+//    round-robin over 8) gets a contiguous range of them, so the tiles running
+//    together on one XCD share operand rows in its L2.
 #include "device_common.hpp"
 #include "gemm_common.hpp"
 #include "kernels.hpp"
@@ -547,7 +550,10 @@ void gemm_fp8_pipe(KParams p) {
   constexpr int LPS = BPW + SC_DMA;                   // vector-memory ops per wave per stage
   constexpr int SCB = E8 ? SC_DMA * 4 * 256 : 16;
   constexpr int NM = TM * TN;                         // MFMAs per k step
-  constexpr int ND = 2 * (TM + TN) + (E8 ? TM + TN : 0);   // LDS reads per k step
+  // LDS reads per k step: the fragments, plus (e8m0, a stage's first k step) one scale word per
+  // fragment row, which serves both k steps of the stage
+  constexpr int ND = 2 * (TM + TN);
+  constexpr int ND0 = ND + (E8 ? TM + TN : 0);
   static_assert(STAGE % 4096 == 0 && BPW_A * 4096 == A_BYTES, "stage must split into 4 waves of 1 KiB blocks");
   static_assert(!E8 || BK == 128, "e8m0 scales need 128-byte stages");
   static_assert((SLOTS * KS) % 2 == 0 && SLOTS >= 2 && SLOTS <= 4, "fragment sets alternate across the ring");
@@ -918,22 +924,48 @@ void gemm_fp8_pipe(KParams p) {
   // Two register sets of MFMA fragments (one 64-byte k step each).
   v8i fa[2][TM], fb[2][TN];
   // e8m0 scale operands: byte i of ea[set] is fragment i's scale (the MFMA
-  // picks it with op_sel), likewise eb.
-  static_assert(TM <= 4 && TN <= 4, "four scale bytes per register");
-  int ea[2], eb[2];
+  // picks it with op_sel), likewise eb.  In LDS a tile row's four scale bytes
+  // of a stage are one word, byte 2 h + b for 32-block b of k step h, and the
+  // lane supplies block b = g of its row.  A stage's first k step reads the
+  // word of each fragment row once (ahead of that step's fragment reads) and
+  // packs the bytes of both k steps with byte permutes; the second k step's
+  // operands wait in ea_n / eb_n.
+  static_assert(TM <= 4 && TN <= 4 && (TM == 4 || TM == 2) && TN == 4, "four scale bytes per register");
+  int ea[2], eb[2], ea_n = 0, eb_n = 0;
+  // byte selectors: t = [w0.b(g), w1.b(g), w0.b(2+g), w1.b(2+g)] from words w0 (low), w1
+  const uint32_t sel_pair = 0x06020400u + 0x01010101u * (uint32_t)g;
+  // Four words of one operand's fragment rows -> (k step 0 bytes, k step 1 bytes), byte i = row i.
+  auto pack4 = [&](const uint32_t (&w)[4], int& k0, int& k1) {
+    const uint32_t t01 = __builtin_amdgcn_perm(w[1], w[0], sel_pair);
+    const uint32_t t23 = __builtin_amdgcn_perm(w[3], w[2], sel_pair);
+    k0 = (int)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    k1 = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
+  };
+  auto pack2 = [&](const uint32_t (&w)[4], int& k0, int& k1) {
+    const uint32_t t01 = __builtin_amdgcn_perm(w[1], w[0], sel_pair);
+    k0 = (int)t01;
+    k1 = (int)(t01 >> 16);
+  };
   // Fragments of k step h of the stage in LDS `st` (scales in `sc`) into set SET.
   auto rd = [&](auto set_tag, const uint8_t* st, const uint8_t* sc, int h) {
     constexpr int SET = decltype(set_tag)::value;
+    uint32_t wa[4] = {0u, 0u, 0u, 0u}, wb[4] = {0u, 0u, 0u, 0u};
+    if constexpr (E8) {
+      if (h == 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          wa[i] = *reinterpret_cast<const uint32_t*>(sc + 4 * (wm * WM + 32 * i + lrow));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          wb[j] = *reinterpret_cast<const uint32_t*>(sc + 4 * (BM + wn * WN + 32 * j + lrow));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * WM + 32 * i + lrow;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + g));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + 2 + g));
       fa[SET][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (E8) {
-        const int s = sc[4 * r + 2 * h + g];
-        ea[SET] = i == 0 ? s : (ea[SET] | (s << (8 * i)));
-      }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -941,9 +973,15 @@ void gemm_fp8_pipe(KParams p) {
       const u32x4 lo = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + g));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + 2 + g));
       fb[SET][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (E8) {
-        const int s = sc[4 * (BM + r) + 2 * h + g];
-        eb[SET] = j == 0 ? s : (eb[SET] | (s << (8 * j)));
+    }
+    if constexpr (E8) {
+      if (h == 0) {
+        if constexpr (TM == 4) pack4(wa, ea[SET], ea_n);
+        else pack2(wa, ea[SET], ea_n);
+        pack4(wb, eb[SET], eb_n);
+      } else {
+        ea[SET] = ea_n;
+        eb[SET] = eb_n;
       }
     }
   };
@@ -1008,7 +1046,7 @@ void gemm_fp8_pipe(KParams p) {
     issue_stage(cur, slot_tag, stage_of(min(kt + SLOTS, nk - 1)), Checked{}, soff);
     rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
     mma(std::integral_constant<int, CUR>{});
-    interleave<NM, ND, LPS>();
+    interleave<NM, ND0, LPS>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
