@@ -18,6 +18,18 @@ __global__ __launch_bounds__(256) void encode_f32_kernel(const float* __restrict
     q[i] = (uint8_t)(codec == 0 ? enc_fp8<0>(y[i]) : enc_fp8<1>(y[i]));
 }
 
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1 << 16);

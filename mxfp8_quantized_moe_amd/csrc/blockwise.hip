@@ -65,8 +65,7 @@ __global__ __launch_bounds__(256) void bw_quant_rows_kernel(const uint16_t* __re
   u32x4 v = u32x4{0, 0, 0, 0};
   if (valid) v = *reinterpret_cast<const u32x4*>(x + row * cols + c);
   uint32_t m = chunk_absmax(v);
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));   // within 16 lanes
+  m = group_max_u32<16>(m);   // within 16 lanes
   const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
   if (valid) *reinterpret_cast<u32x2*>(q + row * cols + c) = cast_chunk<CODEC>(v, s);
   if (tv && (t & 15) == 0) scale[row * nc + cb] = s;
@@ -288,8 +287,7 @@ __global__ __launch_bounds__(256) void bw_quant_tokens_kernel(const uint16_t* __
       const uint32_t w = jj < 2 ? v[i].x : jj < 4 ? v[i].y : jj < 6 ? v[i].z : v[i].w;
       m[jj] = max(m[jj], ((jj & 1) ? (w >> 16) : w) & 0x7FFFu);
     }
-#pragma unroll
-    for (int off = 8; off <= 32; off <<= 1) m[jj] = max(m[jj], (uint32_t)__shfl_xor((int)m[jj], off, 64));
+    m[jj] = lane_max_xor<32, false>(lane_max_xor<16, false>(lane_max_xor<8, false>(m[jj])));
   }
   if (lane < 8) {
 #pragma unroll

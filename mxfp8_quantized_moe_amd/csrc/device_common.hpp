@@ -26,18 +26,64 @@ struct alignas(8) u32x2 { uint32_t x, y; };
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
+// Two independent 16-bit maxima packed in a u32 (v_pk_max_u16: one instruction).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
 // max(|a|,|b|) over each 16-bit half of two packed bf16 pairs, as magnitudes
 // compared by their bit patterns (valid for finite values: a larger bf16
 // magnitude has a larger 15-bit pattern).
 __device__ __forceinline__ uint32_t pk_absmax_bf16(uint32_t acc, uint32_t v) {
-  uint32_t a = v & 0x7FFF7FFFu;
-  uint32_t lo = max(acc & 0xFFFFu, a & 0xFFFFu);
-  uint32_t hi = max(acc >> 16, a >> 16);
-  return lo | (hi << 16);
+  return pk_max_u16(acc, v & 0x7FFF7FFFu);
 }
 __device__ __forceinline__ uint32_t pk_fold(uint32_t acc) { return max(acc & 0xFFFFu, acc >> 16); }
 
 // ------------------------------------------------------------------ reductions
+//
+// Lane exchanges on the VALU instead of the LDS crossbar (no LDS wait): lane l
+// meets lane l ^ 8 by a DPP rotation of its 16-lane row by 8, lane l ^ 16 and
+// l ^ 32 by gfx950's row swaps (v_permlane16_swap / v_permlane32_swap: the two
+// results hold, in every lane, the values of l and of its partner), and l ^ 1,
+// l ^ 2 by DPP quad permutations.
+
+// max over lanes {l, l ^ X} for X in {1, 2, 8, 16, 32}, unsigned 32-bit or packed 16-bit.
+template <int X, bool PK16>
+__device__ __forceinline__ uint32_t lane_max_xor(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return PK16 ? pk_max_u16(a, b) : max(a, b); };
+  if constexpr (X == 1) {
+    return mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  } else if constexpr (X == 2) {
+    return mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  } else if constexpr (X == 8) {
+    return mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else if constexpr (X == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return mx(p[0], p[1]);
+  } else {
+    static_assert(X == 32, "lane distance");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return mx(p[0], p[1]);
+  }
+}
+
+// Unsigned maximum over aligned groups of N lanes (N = 4, 16 or 64), in every
+// lane of the group.  Within a 16-lane row, DPP rotations by 8, 4, 2, 1 leave
+// every lane with the row maximum (after rotating by 2^k the value has period
+// 2^k along the row).
+template <int N>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(N == 4 || N == 16 || N == 64, "group size");
+  if constexpr (N == 4) return lane_max_xor<2, false>(lane_max_xor<1, false>(v));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x122, 0xF, 0xF, false));   // row_ror:2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x121, 0xF, 0xF, false));   // row_ror:1
+  if constexpr (N == 64) v = lane_max_xor<32, false>(lane_max_xor<16, false>(v));
+  return v;
+}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -135,6 +181,21 @@ __device__ __forceinline__ int mx_exponent(uint32_t amax_bits, int rule) {
   if (rule == 1 && sig_frac > 0x600000u) X += 1;   // significand > 1.75
   return max(-127, min(127, X));
 }
+
+// The same rule for a block maximum that is a bf16 value, given as its 16-bit
+// pattern a16 (finite): floor(log2 amax) is the exponent field minus 127 for a
+// normal value, and at most -127 for a subnormal one, so X = field - 135
+// (+1 under CEIL when the 7-bit significand exceeds 0x60, i.e. 1.75) clamped
+// below at -127; the largest finite bf16 gives X = 119, so the upper clamp
+// never acts.  Equal to mx_exponent(a16 << 16, rule) for every such a16.
+__device__ __forceinline__ int mx_exponent_bf16(uint32_t a16, int rule) {
+  int X = (int)(a16 >> 7) - 135;
+  if (rule == 1) X += (a16 & 0x7Fu) > 0x60u ? 1 : 0;
+  return max(X, -127);
+}
+
+// 2^-X for X in [-127, 119] (a normal fp32, no branch).
+__device__ __forceinline__ float exp2_neg_bf16(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
 
 // 2^-X as an fp32 for X in [-127, 127] (X = 127 gives the subnormal 2^-127 = 0x00400000).
 __device__ __forceinline__ float exp2_neg(int X) {

@@ -10,6 +10,9 @@
 
 namespace fp8moe {
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int codec,
                                    uint8_t* q, float* scale, hipStream_t st);
 

@@ -90,13 +90,8 @@ __device__ __forceinline__ CwGeom cw_geom(int u, int64_t batch, int rows, int co
 __device__ __forceinline__ void cw_reduce_cols(uint32_t m[4], uint32_t* red /* [4][8][4] */, uint32_t* out) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, cc = t & 7;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-#pragma unroll
-    for (int off = 8; off <= 32; off <<= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)m[p], off, 64);
-      m[p] = (max(m[p] & 0xFFFFu, o & 0xFFFFu)) | (max(m[p] >> 16, o >> 16) << 16);
-    }
-  }
+  for (int p = 0; p < 4; ++p)
+    m[p] = lane_max_xor<32, true>(lane_max_xor<16, true>(lane_max_xor<8, true>(m[p])));
   if (lane < 8) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) red[(w * 8 + cc) * 4 + p] = m[p];

@@ -63,10 +63,9 @@ __global__ __launch_bounds__(256) void mx_lastdim_kernel(const uint16_t* __restr
     const u32x4 v = reinterpret_cast<const u32x4*>(x)[ci];
     uint32_t m = pk_absmax_bf16(pk_absmax_bf16(0u, v.x), v.y);
     m = pk_fold(pk_absmax_bf16(pk_absmax_bf16(m, v.z), v.w));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
-    const int X = mx_exponent(m << 16, RULE);
-    const float s = exp2_neg(X);
+    m = lane_max_xor<2, false>(lane_max_xor<1, false>(m));
+    const int X = mx_exponent_bf16(m, RULE);
+    const float s = exp2_neg_bf16(X);
     reinterpret_cast<u32x2*>(q)[ci] = u32x2{quant_bf16x4<0>(v.x, v.y, s), quant_bf16x4<0>(v.z, v.w, s)};
     if constexpr (K4) {
       // 16 lanes hold one stage's four blocks of one row when rows have whole
@@ -100,11 +99,21 @@ __global__ __launch_bounds__(256) void mx_lastdim_kernel(const uint16_t* __restr
 
 // ------------------------------------------------------------ row blocks
 
-constexpr int kMxIters = kTileRows / 128;
+// Row-block work items are 64 columns x kMxRows rows: a 16 KiB LDS tile and 32
+// data registers per thread, so several workgroups share a CU and hide each
+// other's load latency.
+constexpr int kMxRows = 256;
+constexpr int kMxIters = kMxRows / 128;
+constexpr int kMxTileBytes = kTileCols * kMxRows;
+
+// Column c, row r of the codes tile (the colwise tile's swizzle over 16 segments).
+__device__ __forceinline__ int mx_tile_off(int c, int r) {
+  return c * kMxRows + ((((r >> 4) ^ (2 * (c >> 3))) & (kMxRows / 16 - 1)) << 4) + (r & 15);
+}
 
 __device__ __forceinline__ int mx_chunks(int lo, int hi) {
   const int mp = (hi - lo + 31) & ~31;
-  return (mp + kTileRows - 1) / kTileRows;   // an empty group owns no unit
+  return (mp + kMxRows - 1) / kMxRows;   // an empty group owns no unit
 }
 struct MxChunks {
   __device__ int operator()(int lo, int hi) const { return mx_chunks(lo, hi); }
@@ -119,8 +128,8 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
                                                       int64_t rows_pad, int32_t* __restrict__ offs_pad_out,
                                                       int n_strips) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
-  __shared__ uint8_t s_x[64 * 16];       // e8m0 codes: [column][block of the tile]
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kMxTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[64 * (kMxRows / 32)];   // e8m0 codes: [column][block of the tile]
 
   const int strip = blockIdx.x % n_strips;
   const int u = blockIdx.x / n_strips;
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
     } else {
       // tail: columns [padded total, rows_pad) get zero codes and zero scales
       lo = hi = 0; plo = un.pbase; phi = (int)rows_pad; j = un.j;
-      if (plo + j * kTileRows >= phi) return;
+      if (plo + j * kMxRows >= phi) return;
     }
     ld_q = rows_pad; qb = q;
     srow0 = 0; s_rows = cols; s_nb = (int)(rows_pad / 32);
@@ -178,77 +187,106 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
     x += b * (int64_t)rows * cols;
   }
 
-  const int A = plo + j * kTileRows;                 // output row of tile row 0 (multiple of 32)
-  const int r_end = min(A + kTileRows, phi);         // output rows of this unit: [A, r_end)
+  const int A = plo + j * kMxRows;                 // output row of tile row 0 (multiple of 32)
+  const int r_end = min(A + kMxRows, phi);         // output rows of this unit: [A, r_end)
   const int c0 = strip * kTileCols;
   const int col = c0 + cc * 8;
   const bool col_ok = col < cols;
+  // an interior tile (all 512 rows and 64 columns are input data) loads without checks
+  const bool full = c0 + kTileCols <= cols && A + kMxRows <= r_end && lo + (A + kMxRows - plo) <= hi;
+  u32x4 v[kMxIters][4];
+  if (full) {
+    const uint16_t* xr = x + (int64_t)(lo + A - plo + 4 * rs) * cols + col;   // this thread's first row
+#pragma unroll
+    for (int i = 0; i < kMxIters; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[i][k] = *reinterpret_cast<const u32x4*>(xr + (int64_t)(128 * i + k) * cols);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMxIters; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = A + 128 * i + 4 * rs + k;       // output row
+        const int in = lo + (r - plo);                 // input row (pad rows: in >= hi)
+        const bool ok = col_ok && r < r_end && in < hi;
+        v[i][k] = ok ? *reinterpret_cast<const u32x4*>(x + (int64_t)in * cols + col) : u32x4{0, 0, 0, 0};
+      }
+  }
 
 #pragma unroll
   for (int i = 0; i < kMxIters; ++i) {
-    u32x4 v[4];
     uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int r = A + 128 * i + 4 * rs + k;       // output row
-      const int in = lo + (r - plo);                 // input row (pad rows: in >= hi)
-      const bool ok = col_ok && r < r_end && in < hi;
-      v[k] = ok ? *reinterpret_cast<const u32x4*>(x + (int64_t)in * cols + col) : u32x4{0, 0, 0, 0};
-      m[0] = pk_absmax_bf16(m[0], v[k].x);
-      m[1] = pk_absmax_bf16(m[1], v[k].y);
-      m[2] = pk_absmax_bf16(m[2], v[k].z);
-      m[3] = pk_absmax_bf16(m[3], v[k].w);
+      m[0] = pk_absmax_bf16(m[0], v[i][k].x);
+      m[1] = pk_absmax_bf16(m[1], v[i][k].y);
+      m[2] = pk_absmax_bf16(m[2], v[i][k].z);
+      m[3] = pk_absmax_bf16(m[3], v[i][k].w);
     }
     // the 32-row block of this wave: reduce over the 8 row slots (lanes 8 apart)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-#pragma unroll
-      for (int off = 8; off <= 32; off <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)m[p], off, 64);
-        m[p] = (max(m[p] & 0xFFFFu, o & 0xFFFFu)) | (max(m[p] >> 16, o >> 16) << 16);
-      }
-    }
+    for (int p = 0; p < 4; ++p)
+      m[p] = lane_max_xor<32, true>(lane_max_xor<16, true>(lane_max_xor<8, true>(m[p])));
     float s[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t a16 = (m[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-      const int X = mx_exponent(a16 << 16, RULE);
-      s[k] = exp2_neg(X);
-      if (lane < 8) s_x[(cc * 8 + k) * 16 + 4 * i + w] = (uint8_t)(X + 127);
+      const int X = mx_exponent_bf16(a16, RULE);
+      s[k] = exp2_neg_bf16(X);
+      if (lane < 8) s_x[(cc * 8 + k) * (kMxRows / 32) + 4 * i + w] = (uint8_t)(X + 127);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t word = quant4<0>(col_of(v[0], k), col_of(v[1], k), col_of(v[2], k), col_of(v[3], k), s[k]);
-      tile_put4(tile, cc * 8 + k, 128 * i + 4 * rs, word);
+      const uint32_t word = quant4<0>(col_of(v[i][0], k), col_of(v[i][1], k), col_of(v[i][2], k),
+                                      col_of(v[i][3], k), s[k]);
+      *reinterpret_cast<uint32_t*>(tile + mx_tile_off(cc * 8 + k, 128 * i + 4 * rs)) = word;
     }
   }
   __syncthreads();
 
+  // transposed store: each pass writes 16 columns x 16 segments of 16 rows
+  constexpr int kSeg = kMxRows / 16, kColsPerPass = 256 / kSeg, kPasses = kTileCols / kColsPerPass;
+  if (full) {
+    uint8_t* qo = qb + (int64_t)(c0 + t / kSeg) * ld_q + A + 16 * (t % kSeg);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int ci = p * 8 + (t >> 5), sg = t & 31;
-    const int c = c0 + ci, R0 = A + 16 * sg;
-    if (c < cols && R0 < r_end)
-      *reinterpret_cast<u32x4*>(qb + (int64_t)c * ld_q + R0) = tile_get16(tile, ci, 16 * sg);
+    for (int p = 0; p < kPasses; ++p)
+      *reinterpret_cast<u32x4*>(qo + (int64_t)(kColsPerPass * p) * ld_q) =
+          *reinterpret_cast<const u32x4*>(tile + mx_tile_off(p * kColsPerPass + t / kSeg, 16 * (t % kSeg)));
+  } else {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int ci = p * kColsPerPass + t / kSeg, sg = t % kSeg;
+      const int c = c0 + ci, R0 = A + 16 * sg;
+      if (c < cols && R0 < r_end)
+        *reinterpret_cast<u32x4*>(qb + (int64_t)c * ld_q + R0) = *reinterpret_cast<const u32x4*>(tile + mx_tile_off(ci, 16 * sg));
+    }
   }
   // scales: column t/4, blocks 4*(t%4) .. +3 of this tile
   {
-    const int ci = t >> 2, c = c0 + ci;
+    constexpr int kBlk = kMxRows / 32, kThrPerCol = kBlk / 4;   // block quads per column
+    const int ci = t / kThrPerCol, c = c0 + ci;
     const int nb = (r_end - A) >> 5;
-    if (c < cols) {
+    if (ci < kTileCols && c < cols) {
       const int64_t srow = srow0 + c;
+      const int b0 = 4 * (t % kThrPerCol), blk0 = (A >> 5) + b0;
+      if (b0 + 4 <= nb && (blk0 & 3) == 0 && (K4 || (s_nb & 3) == 0)) {
+        // four whole blocks starting at a multiple of four: one aligned word
+        const uint32_t wv = *reinterpret_cast<const uint32_t*>(s_x + ci * kBlk + b0);
+        *reinterpret_cast<uint32_t*>(sc + (K4 ? k4_index(srow, blk0, s_rows) : srow * s_nb + blk0)) = wv;
+      } else {
 #pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const int b = 4 * (t & 3) + b4;
-        if (b < nb) {
-          const int blk = (A >> 5) + b;
-          if constexpr (K4) {
-            uint8_t* d = sc + k4_index(srow, blk, s_rows);
-            d[0] = s_x[ci * 16 + b];
-            if (blk == s_nb - 1)
-              for (int e = 1; (blk + e) & 3; ++e) d[e] = 0;   // pad to the stage's four blocks
-          } else {
-            sc[srow * s_nb + blk] = s_x[ci * 16 + b];
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int b = b0 + b4;
+          if (b < nb) {
+            const int blk = (A >> 5) + b;
+            if constexpr (K4) {
+              uint8_t* d = sc + k4_index(srow, blk, s_rows);
+              d[0] = s_x[ci * kBlk + b];
+              if (blk == s_nb - 1)
+                for (int e = 1; (blk + e) & 3; ++e) d[e] = 0;   // pad to the stage's four blocks
+            } else {
+              sc[srow * s_nb + blk] = s_x[ci * kBlk + b];
+            }
           }
         }
       }
@@ -257,8 +295,8 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
 }
 
 int64_t mx_rows_units_bound(int64_t batch, int64_t rows, const int32_t* offs, int32_t n_groups, int64_t rows_pad) {
-  if (offs) return (rows_pad + kTileRows - 1) / kTileRows + n_groups + 1;
-  return batch * ((rows + kTileRows - 1) / kTileRows);
+  if (offs) return (rows_pad + kMxRows - 1) / kMxRows + n_groups + 1;
+  return batch * ((rows + kMxRows - 1) / kMxRows);
 }
 
 template <int RULE>

@@ -19,12 +19,10 @@ namespace fp8moe {
 template <int TPR>
 __device__ __forceinline__ uint32_t row_group_max(uint32_t m, uint32_t* red) {
   if constexpr (TPR <= 64) {
-#pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    return m;
+    return group_max_u32<TPR>(m);
   } else {
     static_assert(TPR == 256, "row group is one workgroup");
-    m = wave_max_u32(m);
+    m = group_max_u32<64>(m);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = m;
     __syncthreads();
