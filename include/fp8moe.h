@@ -70,6 +70,7 @@ extern "C" {
 #define FP8MOE_ERR_UNSUPPORTED 5   /* a valid combination this library does not implement */
 #define FP8MOE_ERR_LAUNCH 6        /* the HIP runtime rejected a launch */
 #define FP8MOE_ERR_DEVICE 7        /* a HIP device query failed */
+#define FP8MOE_ERR_SCRATCH 8       /* the allocation-free entry point's fixed scratch is too small */
 
 /* FP8 codecs.  e4m3fn: OCP, bias 7, max 448, NaN 0x7F/0xFF, signed zero.
  * e4m3fnuz: bias 8, max 240, no NaN/Inf among finite codes, unsigned zero.
@@ -300,6 +301,23 @@ int grouped_mm_blockwise_k(const void *a_t, const float *a_scale, const void *b_
 int moe_route(const int32_t *expert_ids, int64_t tokens, int32_t topk, int32_t n_experts,
               int32_t pad, int32_t *counts, int32_t *offs, int32_t *dest, int32_t *src,
               void *workspace, void *stream);
+
+/*
+ * moe_route_noalloc -- moe_route for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, results and kernels, with the
+ * workspace replaced by a fixed scratch array the library owns on each GPU
+ * (4 MiB, held until the process ends; routings whose
+ * moe_route_workspace_bytes exceed it return FP8MOE_ERR_SCRATCH before any
+ * HIP call).  It calls no allocating routine.  Every call on a GPU shares
+ * that GPU's scratch, which keeps the last call's contents (a call rewrites
+ * all it uses, so nothing needs clearing): calls that overlap on one GPU race.
+ * The scratch's device address is looked up once per device, at the first
+ * call with that device current.
+ */
+int moe_route_noalloc(const int32_t *expert_ids, int64_t tokens, int32_t topk, int32_t n_experts,
+                      int32_t pad, int32_t *counts, int32_t *offs, int32_t *dest, int32_t *src,
+                      void *stream);
 
 /* Workspace bytes moe_route needs for `slots` = tokens*topk slots (-1: invalid sizes). */
 int64_t moe_route_workspace_bytes(int64_t slots, int32_t n_experts);

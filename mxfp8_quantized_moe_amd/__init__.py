@@ -21,7 +21,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
-           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_rows_bound", "moe_permute", "moe_combine",
+           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_permute", "moe_combine",
            "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise",
            "quantize_blockwise_tokens", "grouped_mm_blockwise_k"]
 
@@ -278,6 +278,19 @@ def moe_route(expert_ids, n_experts, pad=1, out=None, workspace=None, stream=Non
         workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=dev)
     _lib.check("moe_route", _lib.lib().moe_route(_ptr(ids), T, k, n_experts, pad, _ptr(counts), _ptr(offs),
                                                   _ptr(dest), _ptr(src), _ptr(workspace), _stream(stream)))
+    return counts, offs, dest, src
+
+
+def moe_route_noalloc(expert_ids, n_experts, out, pad=1, stream=None):
+    """moe_route on the library's fixed scratch: nothing is allocated, so the outputs
+    out = (counts [E], offs [E], dest [T*k], src [rows bound]) (int32) must be passed."""
+    ids = expert_ids
+    if ids.dtype != torch.int32 or ids.dim() != 2 or not ids.is_contiguous():
+        raise ValueError("moe_route_noalloc needs contiguous int32 expert ids of shape [tokens, topk]")
+    T, k = ids.shape
+    counts, offs, dest, src = out
+    _lib.check("moe_route_noalloc", _lib.lib().moe_route_noalloc(_ptr(ids), T, k, n_experts, pad, _ptr(counts),
+                                                                  _ptr(offs), _ptr(dest), _ptr(src), _stream(stream)))
     return counts, offs, dest, src
 
 

@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8moe.so")
 
 # status codes and enums (mirror include/fp8moe.h)
-OK, ERR_NULL, ERR_SHAPE, ERR_ENUM, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_ENUM, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_SCRATCH = range(9)
 E4M3FN, E4M3FNUZ = 0, 1
 MX_FLOOR_OCP, MX_CEIL = 0, 1
 MX_LAYOUT_ROWS, MX_LAYOUT_K4 = 0, 1
@@ -26,7 +26,7 @@ EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "moe_route_rows_bound", "moe_permute", "moe_combine", "quantize_tensorwise", "moe_permute_quantized",
            "quantize_blockwise", "grouped_mm_blockwise", "quantize_blockwise_tokens",
            "blockwise_token_blocks_bound", "grouped_mm_blockwise_k",
-           "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget"]
+           "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget", "moe_route_noalloc"]
 
 _lib = None
 
@@ -55,6 +55,7 @@ _SIGS = {
     "grouped_mm_blockwise": (_int, [_vp, _int, _vp, _vp, _int, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _int, _vp]),
     "moe_route": (_int, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_workspace_bytes": (_i64, [_i64, _i32]),
+    "moe_route_noalloc": (_int, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_rows_bound": (_i64, [_i64, _i32, _i32]),
     "moe_permute": (_int, [_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp]),
     "moe_permute_quantized": (_int, [_vp, _vp, _i64, _i64, _i32, _vp, _i64, _int, _vp, _vp, _vp]),

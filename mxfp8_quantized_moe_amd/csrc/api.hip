@@ -142,6 +142,18 @@ int moe_route(const int32_t* expert_ids, int64_t tokens, int32_t topk, int32_t n
                                         as_stream(stream)));
 }
 
+int moe_route_noalloc(const int32_t* expert_ids, int64_t tokens, int32_t topk, int32_t n_experts, int32_t pad,
+                      int32_t* counts, int32_t* offs, int32_t* dest, int32_t* src, void* stream) {
+  // the library's scratch stands in for the workspace (a non-null, aligned placeholder for the check)
+  const int st = check_moe_route(expert_ids, tokens, topk, n_experts, pad, counts, offs, dest, src,
+                                 reinterpret_cast<const void*>(uintptr_t{256}));
+  if (st) return st;
+  const int64_t S = tokens * topk;
+  if (route_workspace_bytes(S, n_experts) > kRouteScratchBytes) return FP8MOE_ERR_SCRATCH;
+  return launch_status(launch_moe_route_noalloc(expert_ids, S, n_experts, pad, counts, offs, dest, src,
+                                                route_rows_bound(S, n_experts, pad), as_stream(stream)));
+}
+
 int moe_permute(const void* x_bf16, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src, int64_t rows_out,
                 void* xg_bf16, void* stream) {
   const int st = check_moe_permute(x_bf16, tokens, cols, topk, src, rows_out, xg_bf16);
@@ -216,6 +228,7 @@ const char* fp8moe_status_string(int status) {
     case FP8MOE_ERR_UNSUPPORTED: return "unsupported combination";
     case FP8MOE_ERR_LAUNCH: return "kernel launch failed";
     case FP8MOE_ERR_DEVICE: return "device query failed";
+    case FP8MOE_ERR_SCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -231,6 +244,6 @@ int fp8moe_default_codec(int hip_device, int* codec_out) {
 
 int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(polls); }
 
-int fp8moe_version(void) { return 102; }
+int fp8moe_version(void) { return 103; }
 
 }  // extern "C"

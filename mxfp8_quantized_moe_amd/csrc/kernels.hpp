@@ -57,6 +57,8 @@ hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t batch, int64_t 
                                       uint32_t* part, hipStream_t st);
 hipError_t launch_moe_route(const int32_t* ids, int64_t S, int E, int pad, int32_t* counts, int32_t* offs,
                             int32_t* dest, int32_t* src, int64_t rows_bound, int32_t* workspace, hipStream_t st);
+hipError_t launch_moe_route_noalloc(const int32_t* ids, int64_t S, int E, int pad, int32_t* counts, int32_t* offs,
+                                    int32_t* dest, int32_t* src, int64_t rows_bound, hipStream_t st);
 hipError_t launch_moe_permute(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
                               int64_t rows_out, uint16_t* xg, hipStream_t st);
 hipError_t launch_moe_permute_quantized(const uint8_t* q, const float* scale, int64_t tokens, int64_t cols, int topk,

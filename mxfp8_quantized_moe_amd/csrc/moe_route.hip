@@ -24,6 +24,8 @@
 #include "kernels.hpp"
 #include "validate.hpp"
 
+#include <mutex>
+
 namespace fp8moe {
 
 static_assert(kRouteSlots % 64 == 0, "the rank kernel walks a block in whole waves");
@@ -292,6 +294,46 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t S, int E, int pad, int32
     hipLaunchKernelGGL(route_rank_kernel, dim3((unsigned)nb), dim3(64), 0, st, ids, S, E, nbits, pad, workspace,
                        counts, offs, dest, src, rows_bound);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ allocation-free routing
+//
+// The block histograms of moe_route_noalloc live in a fixed file-scope device
+// array owned by the library: each GPU the library runs on holds its own copy
+// until the process ends.  In host code the array's name is only a stand-in,
+// so its device address is taken once per device with hipGetSymbolAddress
+// (with that device current, at the entry point's first call on it) and only
+// that address is ever passed to kernels.  Every call on a GPU shares that
+// GPU's array (the histogram kernel rewrites all of it that a call uses, so
+// nothing needs clearing); calls that overlap on one GPU race.
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / 4];
+
+static int32_t* route_scratch(hipError_t* err) {
+  static std::mutex mu;
+  static int32_t* ptr[kMaxDevices] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  return ptr[dev];
+}
+
+hipError_t launch_moe_route_noalloc(const int32_t* ids, int64_t S, int E, int pad, int32_t* counts, int32_t* offs,
+                                    int32_t* dest, int32_t* src, int64_t rows_bound, hipStream_t st) {
+  hipError_t err = hipSuccess;
+  int32_t* ws = route_scratch(&err);
+  if (ws == nullptr) return err == hipSuccess ? hipErrorInvalidSymbol : err;
+  return launch_moe_route(ids, S, E, pad, counts, offs, dest, src, rows_bound, ws, st);
 }
 
 // Rows per workgroup: enough that most of the 256 threads have a 16-byte chunk.

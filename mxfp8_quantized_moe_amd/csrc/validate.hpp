@@ -48,6 +48,8 @@ int check_quantize_tensorwise(const void* x, int64_t batch, int64_t rows, int64_
 // experts one route call takes (one workgroup scans them).
 constexpr int kRouteSlots = 256;
 constexpr int kRouteMaxExperts = 1024;
+constexpr int64_t kRouteScratchBytes = 4 << 20;   // the fixed scratch of moe_route_noalloc
+constexpr int kMaxDevices = 64;
 inline int64_t route_blocks(int64_t slots) { return (slots + kRouteSlots - 1) / kRouteSlots; }
 // Workspace bytes of a route call, rows of its grouped layout; -1 for invalid sizes.
 int64_t route_workspace_bytes(int64_t slots, int32_t n_experts);

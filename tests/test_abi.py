@@ -42,10 +42,10 @@ def test_exports_every_declared_function(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.fp8moe_status_string(0) == b"ok"
-    for s in range(1, 8):
+    for s in range(1, 9):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 102
+    assert lib.fp8moe_version() == 103
 
 
 def test_rows_bound(lib):
@@ -316,3 +316,15 @@ def test_colwise_poll_budget_hook(lib):
         assert f(-1) == 4096
     finally:
         f(first)
+
+
+def test_route_noalloc_rejections(lib):
+    """Host-side checks of the allocation-free routing (no HIP call is reached)."""
+    r = lib.moe_route_noalloc   # (ids, tokens, topk, E, pad, counts, offs, dest, src, stream)
+    assert r(None, 4, 2, 8, 1, P, P, P, P, None) == L.ERR_NULL
+    assert r(P, 4, 2, 0, 1, P, P, P, P, None) == L.ERR_SHAPE
+    assert r(P, 4, 2, 2048, 1, P, P, P, P, None) == L.ERR_UNSUPPORTED
+    assert r(MIS, 4, 2, 8, 1, P, P, P, P, None) == L.ERR_ALIGN
+    # 2^20 slots x 1024 experts: 16 MiB of histograms, beyond the 4 MiB scratch
+    assert lib.moe_route_workspace_bytes(1 << 20, 1024) > 4 << 20
+    assert r(P, 1 << 18, 4, 1024, 1, P, P, P, P, None) == L.ERR_SCRATCH
