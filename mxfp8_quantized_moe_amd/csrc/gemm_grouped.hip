@@ -1124,11 +1124,13 @@ void gemm_fp8_pipe(KParams p) {
     // Each pass stages one 32-row block of a wave's results, PC columns wide
     // (128 bytes per row), and writes whole 128-byte row segments.  A lane
     // holds four consecutive columns of one row per register quad: bf16
-    // packs them into 8 bytes, written at unit u ^ (row & 15) of its staged
-    // row (fp32: 16 bytes at unit u ^ (row & 7)), so the rows one write
-    // instruction touches land on distinct banks; 8 lanes read back one whole
-    // row.  A bf16 read of logical 16-byte chunk k finds its two halves in
-    // physical chunk k ^ ((row & 15) >> 1), swapped when the row is odd.
+    // packs them into 8 bytes, written at unit u ^ (row & 14) of its staged
+    // row (fp32: 16 bytes at unit u ^ (row & 7)).  The even mask keeps the two
+    // 8-byte halves of a 16-byte chunk (lanes g = 0, 1 of one row) in order,
+    // and rows 0..15 of one write instruction still cover all 64 banks once
+    // (row parity picks the bank half, row & 14 the chunk), so the 512 bytes
+    // take the minimum two cycles; 8 lanes read back one whole row, logical
+    // chunk k at physical chunk k ^ ((row & 14) >> 1).
     // LDS accesses go through lds_* while the next tile's stages land.
     constexpr int PC = 128 / ELEM;              // output columns per pass
     constexpr int JPP = PC / 32;                // 32-column blocks per pass
@@ -1143,14 +1145,7 @@ void gemm_fp8_pipe(KParams p) {
     auto store_pass = [&](auto nc) {
       constexpr int n = decltype(nc)::value, i = n % TM, jp = n / TM;
 #pragma unroll
-      for (int itr = 0; itr < 4; ++itr) {
-        lds_ready(dv[n & 1][itr]);
-        if constexpr (OUT == 0) {
-          const bool odd = rr & 1;   // (8 itr + rr) & 1
-          const lds_u4 d = dv[n & 1][itr];
-          dv[n & 1][itr] = lds_u4{odd ? d.z : d.x, odd ? d.w : d.y, odd ? d.x : d.z, odd ? d.y : d.w};
-        }
-      }
+      for (int itr = 0; itr < 4; ++itr) lds_ready(dv[n & 1][itr]);
       // All pre-issued stages of the next tile (this wave's part) land before
       // the first store: until then only loads are in flight, and they
       // complete in order.
@@ -1230,13 +1225,17 @@ void gemm_fp8_pipe(KParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             f32x4 v;
+            // e8m0 scales were applied inside the MFMAs; an empty contraction
+            // range leaves the zero accumulators untouched
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[i][JPP * jp + jj][4 * q + e] * inv_p[i] * inv_q[jj][q][e];
+            for (int e = 0; e < 4; ++e)
+              v[e] = SK == 0 ? acc[i][JPP * jp + jj][4 * q + e] * inv_p[i] * inv_q[jj][q][e]
+                             : acc[i][JPP * jp + jj][4 * q + e];
             const int u = 8 * jj + 2 * q + g;
             if constexpr (OUT == 0) {
               const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
               const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
-              lds_write8(stg_l + lrow * 128 + ((u ^ (lrow & 15)) << 3),
+              lds_write8(stg_l + lrow * 128 + ((u ^ (lrow & 14)) << 3),
                          lds_u2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
             } else {
               lds_write16(stg_l + lrow * 128 + ((u ^ (lrow & 7)) << 4), __builtin_bit_cast(lds_u4, v));
@@ -1249,7 +1248,7 @@ void gemm_fp8_pipe(KParams p) {
 #pragma unroll
         for (int itr = 0; itr < 4; ++itr) {
           const int lr = 8 * itr + rr;
-          const int pc = OUT == 0 ? (k ^ ((lr & 15) >> 1)) : (k ^ (lr & 7));
+          const int pc = OUT == 0 ? (k ^ ((lr & 14) >> 1)) : (k ^ (lr & 7));
           dv[n & 1][itr] = lds_read16(stg_l + lr * 128 + (pc << 4));
         }
         // the previous pass's pieces leave now, behind this pass's LDS work
