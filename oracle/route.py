@@ -17,7 +17,16 @@ leave open, stated here and in the design notes:
     destination is -1 and it contributes nothing to the combine.
   * combine: y[t] = sum over j = 0 .. topk-1, in that order, of
     w[t, j] * yg[dest[t, j]], each product and each sum an IEEE fp32
-    operation (round to nearest), then rounded once to bf16.
+    operation (round to nearest), then rounded once to bf16.  Without
+    weights every weight is 1 (the backward's sum of the routed copies'
+    input gradients).
+  * combine's backward, for the loss gradient dy [T, C]: a grouped row r
+    holding slot s = src[r] of token t = s // topk receives
+    dyg[r] = w[s] * dy[t] (one fp32 product rounded to bf16, as the
+    forward's products; zeros for padding rows), and the router weight
+    receives dw[s] = <dy[t], yg[dest[s]]> (0 for a dropped slot).  The pages
+    fix no precision for dw; it is an fp32 accumulation in the kernel and the
+    exact sum here, and tests accept it within fp32 summation error.
 """
 from __future__ import annotations
 
@@ -80,10 +89,13 @@ def permute_quantized(q: np.ndarray, s: np.ndarray, src: np.ndarray, topk: int, 
     return qg, sg
 
 
-def combine(yg_bits: np.ndarray, dest: np.ndarray, weights: np.ndarray, tokens: int, topk: int) -> np.ndarray:
-    """yg [rows, C] bf16, dest [T*k], weights [T, k] fp32 -> y [T, C] bf16 (the fp32 order above)."""
+def combine(yg_bits: np.ndarray, dest: np.ndarray, weights, tokens: int, topk: int) -> np.ndarray:
+    """yg [rows, C] bf16, dest [T*k], weights [T, k] fp32 or None (all 1) -> y [T, C] bf16 (the fp32 order
+    above)."""
     yg = bf16_to_f32(np.asarray(yg_bits, dtype=np.uint16))
     dest = np.asarray(dest, dtype=np.int64).reshape(tokens, topk)
+    if weights is None:
+        weights = np.ones((tokens, topk), dtype=np.float32)
     w = np.asarray(weights, dtype=np.float32).reshape(tokens, topk)
     acc = np.zeros((tokens, yg.shape[1]), dtype=np.float32)
     for j in range(topk):
@@ -93,3 +105,26 @@ def combine(yg_bits: np.ndarray, dest: np.ndarray, weights: np.ndarray, tokens: 
         term[ok] = w[ok, j][:, None] * yg[d[ok]]          # fp32 products (numpy: IEEE, round to nearest)
         acc = np.where(ok[:, None], acc + term, acc)       # fp32 sums in slot order
     return round_bf16(acc.astype(np.float64))
+
+
+def combine_backward(dy_bits: np.ndarray, yg_bits: np.ndarray, src: np.ndarray, dest: np.ndarray,
+                     weights: np.ndarray, tokens: int, topk: int):
+    """Backward of combine (the reading above).  dy [T, C] bf16, yg [rows, C] bf16 (the forward's expert
+    outputs), src [rows_out] and dest [T*k] from route, weights [T, k] fp32 ->
+    (dyg [rows_out, C] bf16 bits, dw [T*k] fp64)."""
+    dy = bf16_to_f32(np.asarray(dy_bits, dtype=np.uint16))
+    yg = bf16_to_f32(np.asarray(yg_bits, dtype=np.uint16)).astype(np.float64)
+    src = np.asarray(src, dtype=np.int64)
+    dest = np.asarray(dest, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float32).reshape(-1)
+    S = tokens * topk
+    used = (src >= 0) & (src < S)
+    s = src[used]
+    prod = np.zeros((src.size, dy.shape[1]), dtype=np.float32)
+    prod[used] = w[s][:, None] * dy[s // topk]             # fp32 products, round to nearest
+    dyg = round_bf16(prod.astype(np.float64))
+    dw = np.zeros(S, dtype=np.float64)
+    ok = (dest >= 0) & (dest < yg.shape[0])
+    slots = np.nonzero(ok)[0]
+    dw[slots] = np.einsum("sc,sc->s", dy[slots // topk].astype(np.float64), yg[dest[slots]])
+    return dyg, dw

@@ -4,10 +4,18 @@ against the oracle (oracle/swiglu.py).
 The bf16 activation and gradients are compared with the exact values rounded
 once to bf16: the kernels compute in fp32 with their own exponential, so an
 element whose exact value lies within a few fp32 ulps of a bf16 rounding
-boundary may land one bf16 ulp away (bound: 1 ulp, and such elements must be
-rare).  The FP8 codes and scales are an integer decision, taken on the same
+boundary may land one bf16 ulp away.  Bound: 1 ulp, on at most a fraction
+2^-11 of the elements (at least one allowed).  The fraction: the fp32
+evaluation (exponential, add, divide and up to six products and sums) stays
+within a relative error eps = 2^-20 of the exact value; an element flips only
+if its exact value v lies within eps*v of a bf16 rounding midpoint, and with the
+bf16 spacing h > v*2^-8 that happens for a fraction at most 2*eps*v/h < 2^-11
+of values spread over the spacing.  Measured rates stay near 1e-5 to 3e-5.
+The FP8 codes and scales are an integer decision, taken on the same
 bf16 values on both sides: they must equal the oracle's rowwise quantizer
 applied to the kernel's own bf16 output, bit for bit."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -62,7 +70,9 @@ def assert_within_one_ulp(got: np.ndarray, ref: np.ndarray, what: str) -> None:
         assert d.max() <= 1, f"{what}: {int((d > 1).sum())} elements beyond 1 bf16 ulp; worst at {i}: " \
                              f"got {got[i]:#06x} ref {ref[i]:#06x}"
         note(f"{what}: {int((d > 0).sum())} of {d.size} elements one bf16 ulp off ({(d > 0).mean():.3e})")
-        assert (d > 0).mean() < 0.01, f"{what}: {(d > 0).mean():.2%} of elements off by one ulp"
+        allowed = math.ceil(d.size * 2.0 ** -11)
+        assert int((d > 0).sum()) <= allowed, \
+            f"{what}: {int((d > 0).sum())} elements off by one ulp, more than {allowed} ({d.size} * 2^-11)"
 
 
 SHAPES = [(7, 8), (33, 64), (129, 1408), (64, 2048), (17, 8192), (3, 16384), (2, 24576), (300, 520), (0, 64)]

@@ -127,3 +127,88 @@ def test_permute_quantized_equals_quantize_after_permute(codec):
     qr, sr = oracle.quantize_rowwise(rt.permute(x, src, k), codec)
     assert np.array_equal(qg, qr)
     assert np.array_equal(sg.view(np.uint32), sr.view(np.uint32))
+
+
+def test_combine_without_weights_sums_the_copies():
+    """No weights means weight 1 for every slot: the sum of a token's routed copies.  With 4 copies of
+    a bf16 row the sum is 4x the row, exact in fp32 and in bf16."""
+    rng = np.random.default_rng(5)
+    T, k, C, E = 20, 4, 16, 6
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    x = round_bf16(rng.standard_normal((T, C)))
+    _, _, dest, src = rt.route(ids, E, 1)
+    y = rt.combine(rt.permute(x, src, k), dest, None, T, k)
+    assert np.array_equal(oracle.bf16_to_f32(y), 4.0 * oracle.bf16_to_f32(x))
+
+
+def test_combine_backward_worked_example():
+    """Two tokens, two choices each, values chosen so every product and sum is exact.
+    Token 0 -> experts (1, 0) with weights (0.5, 0.25); token 1 -> (1, 1) with (1.0, 2.0).
+    Grouping (stable, pad 1): expert 0 holds slot 1 (row 0); expert 1 holds slots 0, 2, 3 (rows 1, 2, 3)."""
+    ids = np.array([[1, 0], [1, 1]])
+    _, _, dest, src = rt.route(ids, 2, 1)
+    assert dest.tolist() == [1, 0, 2, 3] and src.tolist() == [1, 0, 2, 3]
+    dy = round_bf16(np.array([[1.0, -2.0], [4.0, 0.5]]))
+    yg = round_bf16(np.array([[3.0, 1.0],      # row 0: token 0's expert-0 output
+                              [2.0, 2.0],      # row 1: token 0's expert-1 output
+                              [-1.0, 8.0],     # row 2: token 1, first choice
+                              [0.5, 0.25]]))   # row 3: token 1, second choice
+    w = np.array([[0.5, 0.25], [1.0, 2.0]], np.float32)
+    dyg, dw = rt.combine_backward(dy, yg, src, dest, w, 2, 2)
+    assert oracle.bf16_to_f32(dyg).tolist() == [[0.25, -0.5], [0.5, -1.0], [4.0, 0.5], [8.0, 1.0]]
+    # dw[s] = <dy[token], yg[dest[s]]>: slot 0 -> row 1, 1 -> row 0, 2 -> row 2, 3 -> row 3
+    assert dw.tolist() == [1.0 * 2 - 2.0 * 2, 1.0 * 3 - 2.0 * 1, 4.0 * -1 + 0.5 * 8, 4.0 * 0.5 + 0.5 * 0.25]
+
+
+def test_combine_backward_is_the_gradient_of_combine():
+    """torch autograd (fp64) differentiates the weighted sum of the routed rows: the rows' gradient,
+    rounded as the reading states (fp32 product, then bf16), is dyg bit for bit, and the weights'
+    gradient is dw.  Padding rows and a dropped slot get zeros."""
+    import torch
+    rng = np.random.default_rng(6)
+    T, k, C, E, pad = 40, 3, 24, 5, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    ids[5, 1] = -1                                                          # dropped slot
+    _, offs, dest, src = rt.route(ids, E, pad)
+    rows = src.size
+    dy = round_bf16(rng.standard_normal((T, C)))
+    yg = round_bf16(rng.standard_normal((rows, C)))
+    w = (rng.random((T, k)) + 0.1).astype(np.float32)
+    dyg, dw = rt.combine_backward(dy, yg, src, dest, w, T, k)
+
+    ygt = torch.tensor(oracle.bf16_to_f32(yg), dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    d = torch.tensor(dest.astype(np.int64)).reshape(T, k)
+    ok = (d >= 0).to(torch.float64)
+    y = (wt[:, :, None] * ygt[d.clamp(min=0)] * ok[:, :, None]).sum(1)
+    (y * torch.tensor(oracle.bf16_to_f32(dy), dtype=torch.float64)).sum().backward()
+    want_rows = round_bf16(ygt.grad.numpy().astype(np.float32).astype(np.float64))
+    assert np.array_equal(dyg, want_rows)
+    assert np.allclose(dw, wt.grad.numpy().ravel(), rtol=1e-13, atol=0.0)
+    assert dw[5 * k + 1] == 0.0
+    assert np.all(dyg[src < 0] == 0)
+
+
+def test_combine_backward_catches_index_mistakes():
+    """Two plausible slips, planted in copies of the oracle's arithmetic (each a one-token slip: the
+    slot's token taken as src // 1, or the weight of the token's first choice for every choice), fail
+    the autograd comparison above on the same inputs."""
+    import torch
+    rng = np.random.default_rng(7)
+    T, k, C, E = 12, 2, 8, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    _, _, dest, src = rt.route(ids, E, 1)
+    dy = round_bf16(rng.standard_normal((T, C)))
+    w = (rng.random((T, k)) + 0.1).astype(np.float32)
+    dyf = oracle.bf16_to_f32(dy)
+    wt = torch.tensor(w, dtype=torch.float64)
+    ygt = torch.zeros((src.size, C), dtype=torch.float64, requires_grad=True)
+    d = torch.tensor(dest.astype(np.int64)).reshape(T, k)
+    ((wt[:, :, None] * ygt[d]).sum(1) * torch.tensor(dyf, dtype=torch.float64)).sum().backward()
+    want = round_bf16(ygt.grad.numpy().astype(np.float32).astype(np.float64))
+    s = src.astype(np.int64)
+    wrong_token = round_bf16((w.ravel()[s][:, None] * dyf[np.minimum(s, T - 1)]).astype(np.float64))
+    wrong_weight = round_bf16((w.ravel()[(s // k) * k][:, None] * dyf[s // k]).astype(np.float64))
+    right = round_bf16((w.ravel()[s][:, None] * dyf[s // k]).astype(np.float64))
+    assert np.array_equal(right, want)
+    assert not np.array_equal(wrong_token, want) and not np.array_equal(wrong_weight, want)
