@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--gw", action="store_true", help="config 2: add the BF16 wgrad variant")
+    ap.add_argument("--experts-only", action="store_true",
+                    help="configs 3-5: time only the expert GEMMs and their quantizations (synthetic operands), "
+                         "not the whole MoE layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--swiglu", action="store_true",
                     help="configs 3/4: also time the fused SwiGLU + rowwise quantization (forward and backward) "
@@ -100,6 +103,7 @@ class Step:
         self.items = []
         self.rot = [0]
         self.specs = {}
+        self.outputs = {}
 
     def add(self, name, kind, fn, work, hbm=None, spec=None):
         self.items.append((name, kind, fn, work, work if hbm is None else hbm))
@@ -112,10 +116,14 @@ class Step:
 
 
 def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_ROTATE, keep_host: bool = False,
-               dev: str = "cuda:0"):
+               dev: str = "cuda:0", experts_only: bool = False):
     """The layer step of workload `cfg` on preallocated device buffers.  Returns (step, host): host
     holds the bf16 inputs as numpy bit patterns (X, DY and W always; with keep_host every input,
-    named as in Step.specs)."""
+    named as in Step.specs).
+
+    For the MoE workloads (3, 4, 5) the step is the whole MoE layer, forward and backward, from
+    the tokens' expert ids to the tokens' input gradient (see moe_layer below); experts_only keeps
+    only the expert GEMMs and their quantizations, on synthetic inputs for every operand."""
     import torch
     import mxfp8_quantized_moe_amd as fm
     from mxfp8_quantized_moe_amd import synth
@@ -186,6 +194,164 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                  spec=dict(op="g_k", qa=qa, sa=sa, qb=qb, sb=sb, sk=sk, offs=offs_np if offs_t is None else offs_t,
                            M=Mc, N=N, K=K, out=o))
         return o
+
+    # MXFP8: e8m0 scales written by the quantizer in the K4 layout the GEMM reads per stage
+    rule = fm.MX_FLOOR_OCP
+    Mp = fm.quantize_mx_rows_bound(M, E)
+    K4 = fm.MX_LAYOUT_K4
+
+    def mx_last(name, src, x, rows, cols):
+        q, s = u8(rows, cols), u8(*fm.mx_k4_shape(rows, cols // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx(x().view(rows, cols), axis=1, rule=rule, q=q, scale=s,
+                                                       layout=K4),
+                 qbytes(rows * cols, rows * cols // 32, 1),
+                 spec=dict(op="mx_last", src=src, shape=(rows, cols), rule=rule, q=q, s=s))
+        return q, s
+
+    def mx_rows_b(name, src, x, B, R, C):
+        q, s = u8(B, C, R), u8(*fm.mx_k4_shape(B * C, R // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, rule=rule, q=q, scale=s, layout=K4),
+                 qbytes(B * R * C, B * C * R // 32, 1),
+                 spec=dict(op="mx_rows_b", src=src, shape=(B, R, C), rule=rule, q=q, s=s))
+        return q, s
+
+    op = torch.empty(E, dtype=torch.int32, device=dev)
+
+    def mx_rows_g(name, src, x, rows, cols):
+        q, s = u8(cols, Mp), u8(*fm.mx_k4_shape(cols, Mp // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
+                                                       offs_pad=op, layout=K4),
+                 qbytes(rows * cols, cols * rows // 32, 1),
+                 spec=dict(op="mx_rows_g", src=src, offs=offs_np, rows_pad=Mp, rule=rule, q=q, s=s, offs_pad=op))
+        return q, s
+
+    def moe_layer():
+        """The MoE layer as one stream-ordered step with no host synchronisation [P1 Details, MoE
+        paragraph; P4 "MoE"]: route the tokens' expert ids into offsets, gather the token rows into
+        the grouped layout (with the FP8 rowwise recipe quantized in the same pass), W1, SwiGLU
+        (fused with the next quantization), W2, the weighted combine back to tokens; then the
+        mirror backward: combine's backward (routed-row gradients, fused with their rowwise
+        quantization, and the router weights' gradients), dgrad and wgrad of W2, SwiGLU's backward,
+        dgrad and wgrad of W1, and the sum of each token's routed input gradients.  Every GEMM
+        reads the device-computed offsets; intermediate tensors are the previous launches' own
+        outputs.  Kind 'moe' marks the memory-bound launches that are not quantizations alone."""
+        nonlocal offs
+        F, F2 = w.F, w.F2
+        T, k = synth.tokens_topk(cfg)
+        ids, RW = synth.routing_ids(cfg), synth.router_weights(cfg)
+        S = T * k
+        rows = fm.moe_route_rows_bound(S, E, 1)
+        assert rows == M, "the routing reproduces the workload's routed rows"
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(4) as ex:
+            X, DY, W1, W2 = ex.map(lambda f: f(w), [synth.make_tokens, synth.make_dy_tokens, synth.make_w1,
+                                                    synth.make_w2])
+        host.update(X=X, DY=DY, W=W1.reshape(E * F2, H), IDS=ids, RW=RW)
+        if keep_host:
+            host.update(W1=W1, W2=W2)
+        Xd, DYd, W1d, W2d = dv(X), dv(DY), dv(W1), dv(W2)
+        idsd = torch.from_numpy(ids).to(dev)
+        rwd = torch.from_numpy(RW).to(dev)
+        i32 = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+        r_counts, r_offs, r_dest, r_src = i32(E), i32(E), i32(S), i32(rows)
+        ws = u8(max(fm.moe_route_workspace_bytes(S, E), 1))
+        offs = r_offs                        # every launch below reads the routed offsets
+        step.add("route", "moe",
+                 lambda: fm.moe_route(idsd, E, 1, out=(r_counts, r_offs, r_dest, r_src), workspace=ws),
+                 4 * S + 4 * S + 4 * rows + 8 * E,
+                 spec=dict(op="route", ids="IDS", E=E, pad=1, out=(r_counts, r_offs, r_dest, r_src)))
+        xg = bf(rows, H)
+        if w.mx:
+            step.add("permute X", "moe", lambda: fm.moe_permute(Xd(), r_src, k, xg=xg), 4 * rows * H + 4 * rows,
+                     spec=dict(op="permute", src="X", topk=k, rsrc=r_src, out=xg))
+            qx, sx = mx_last("mx Xg", xg, lambda: xg, rows, H)
+            qw1, sw1 = mx_last("mx W1", "W1", W1d, E * F2, H)
+            h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H, sk=fm.SCALE_E8M0_K4)
+        else:
+            qx, sx = u8(rows, H), f32(rows)
+            step.add("permute+q X", "moe",
+                     lambda: fm.moe_permute_rowwise(Xd(), r_src, k, 0, xg=xg, qg=qx, scale_g=sx),
+                     5 * rows * H + 8 * rows,
+                     spec=dict(op="permute_rowwise", src="X", topk=k, rsrc=r_src, xg=xg, q=qx, s=sx))
+            qw1, sw1 = q_row("q_row W1", "W1", W1d, E * F2, H)
+            h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H)
+        a2 = bf(rows, F)
+        if w.mx:
+            step.add("swiglu", "moe", lambda: fm.swiglu_quantize_rowwise(h1, 0, a2=a2, codes=False),
+                     2 * rows * F2 + 2 * rows * F, spec=dict(op="swiglu", h1=h1, F=F, a2=a2, q=None, s=None))
+            qa2, sa2 = mx_last("mx A2", a2, lambda: a2, rows, F)
+            qw2, sw2 = mx_last("mx W2", "W2", W2d, E * H, F)
+            yg = g_m("gemm fwd W2", qa2, sa2, qw2, sw2, rows, H, F, sk=fm.SCALE_E8M0_K4)
+        else:
+            qa2, sa2 = u8(rows, F), f32(rows)
+            step.add("swiglu+q", "moe", lambda: fm.swiglu_quantize_rowwise(h1, 0, a2=a2, q=qa2, scale=sa2),
+                     2 * rows * F2 + 3 * rows * F + 4 * rows,
+                     spec=dict(op="swiglu", h1=h1, F=F, a2=a2, q=qa2, s=sa2))
+            qw2, sw2 = q_row("q_row W2", "W2", W2d, E * H, F)
+            yg = g_m("gemm fwd W2", qa2, sa2, qw2, sw2, rows, H, F)
+        y = bf(T, H)
+        step.add("combine", "moe", lambda: fm.moe_combine(yg, r_dest, rwd, k, y=y), 2 * S * H + 2 * T * H + 8 * S,
+                 spec=dict(op="combine", yg=yg, dest=r_dest, w="RW", topk=k, out=y))
+        # backward
+        dyg, dw = bf(rows, H), f32(S)
+        if w.mx:
+            step.add("combine bwd", "moe",
+                     lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, codes=False, dyg=dyg,
+                                                     dweights=dw),
+                     2 * T * H + 4 * rows * H + 16 * S,
+                     spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=dyg,
+                               q=None, s=None, dw=dw))
+            qdy, sdy = mx_last("mx dYg", dyg, lambda: dyg, rows, H)
+            qw2t, sw2t = mx_rows_b("mx W2^T", "W2", W2d, E, H, F)
+            da2 = g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, rows, F, H, sk=fm.SCALE_E8M0_K4)
+            qdyt, sdyt = mx_rows_g("mx dYg^T", dyg, lambda: dyg, rows, H)
+            qa2t, sa2t = mx_rows_g("mx A2^T", a2, lambda: a2, rows, F)
+            g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0_K4, offs_t=op)
+        else:
+            qdy, sdy = u8(rows, H), f32(rows)
+            step.add("combine bwd+q", "moe",
+                     lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, dyg=dyg, q=qdy, scale=sdy,
+                                                     dweights=dw),
+                     2 * T * H + 5 * rows * H + 4 * rows + 16 * S,
+                     spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=dyg,
+                               q=qdy, s=sdy, dw=dw))
+            qw2t, sw2t = q_col_batched("q_col W2", "W2", W2d, E, H, F)
+            da2 = g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, rows, F, H)
+            qdyt, sdyt, ld = q_col_grouped("q_col dYg", dyg, lambda: dyg, rows, H)
+            qa2t, sa2t, _ = q_col_grouped("q_col A2", a2, lambda: a2, rows, F)
+            g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, ld, H, F)
+        dh1 = bf(rows, F2)
+        if w.mx:
+            step.add("swiglu bwd", "moe",
+                     lambda: fm.swiglu_backward_quantize_rowwise(da2, h1, 0, dh1=dh1, codes=False),
+                     2 * rows * F + 4 * rows * F2, spec=dict(op="swiglu_bwd", da2=da2, h1=h1, F=F, dh1=dh1, q=None,
+                                                            s=None))
+            qdh, sdh = mx_last("mx dH1", dh1, lambda: dh1, rows, F2)
+            qw1t, sw1t = mx_rows_b("mx W1^T", "W1", W1d, E, F2, H)
+            dxg = g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, rows, H, F2, sk=fm.SCALE_E8M0_K4)
+            qdht, sdht = mx_rows_g("mx dH1^T", dh1, lambda: dh1, rows, F2)
+            qxt, sxt = mx_rows_g("mx Xg^T", xg, lambda: xg, rows, H)
+            g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0_K4, offs_t=op)
+        else:
+            qdh, sdh = u8(rows, F2), f32(rows)
+            step.add("swiglu bwd+q", "moe",
+                     lambda: fm.swiglu_backward_quantize_rowwise(da2, h1, 0, dh1=dh1, q=qdh, scale=sdh),
+                     2 * rows * F + 5 * rows * F2 + 4 * rows,
+                     spec=dict(op="swiglu_bwd", da2=da2, h1=h1, F=F, dh1=dh1, q=qdh, s=sdh))
+            qw1t, sw1t = q_col_batched("q_col W1", "W1", W1d, E, F2, H)
+            dxg = g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, rows, H, F2)
+            qdht, sdht, _ = q_col_grouped("q_col dH1", dh1, lambda: dh1, rows, F2)
+            qxt, sxt, _ = q_col_grouped("q_col Xg", xg, lambda: xg, rows, H)
+            g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, ld, F2, H)
+        dx = bf(T, H)
+        step.add("combine dX", "moe", lambda: fm.moe_combine(dxg, r_dest, None, k, y=dx), 2 * S * H + 2 * T * H + 4 * S,
+                 spec=dict(op="combine", yg=dxg, dest=r_dest, w=None, topk=k, out=dx))
+        step.outputs = dict(y=y, dx=dx, dw=dw, xg=xg, h1=h1, a2=a2, yg=yg, dyg=dyg, da2=da2, dh1=dh1, dxg=dxg,
+                            route=(r_counts, r_offs, r_dest, r_src))
+        return step, host
+
+    if cfg in (3, 4, 5) and not experts_only:
+        return moe_layer()
 
     if cfg == 2 and tensorwise:
         # one scale per tensor: each of X, W, dY quantized once into both layouts, its scale broadcast
@@ -270,36 +436,7 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
         g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, ld, F2, H)
         return step, host
 
-    # cfg 5: MXFP8, e8m0 scales written by the quantizer in the K4 layout the GEMM reads per stage
-    rule = fm.MX_FLOOR_OCP
-    Mp = fm.quantize_mx_rows_bound(M, E)
-    K4 = fm.MX_LAYOUT_K4
-
-    def mx_last(name, src, x, rows, cols):
-        q, s = u8(rows, cols), u8(*fm.mx_k4_shape(rows, cols // 32))
-        step.add(name, "quant", lambda: fm.quantize_mx(x().view(rows, cols), axis=1, rule=rule, q=q, scale=s,
-                                                       layout=K4),
-                 qbytes(rows * cols, rows * cols // 32, 1),
-                 spec=dict(op="mx_last", src=src, shape=(rows, cols), rule=rule, q=q, s=s))
-        return q, s
-
-    def mx_rows_b(name, src, x, B, R, C):
-        q, s = u8(B, C, R), u8(*fm.mx_k4_shape(B * C, R // 32))
-        step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, rule=rule, q=q, scale=s, layout=K4),
-                 qbytes(B * R * C, B * C * R // 32, 1),
-                 spec=dict(op="mx_rows_b", src=src, shape=(B, R, C), rule=rule, q=q, s=s))
-        return q, s
-
-    op = torch.empty(E, dtype=torch.int32, device=dev)
-
-    def mx_rows_g(name, src, x, rows, cols):
-        q, s = u8(cols, Mp), u8(*fm.mx_k4_shape(cols, Mp // 32))
-        step.add(name, "quant", lambda: fm.quantize_mx(x(), axis=0, offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
-                                                       offs_pad=op, layout=K4),
-                 qbytes(rows * cols, cols * rows // 32, 1),
-                 spec=dict(op="mx_rows_g", src=src, offs=offs_np, rows_pad=Mp, rule=rule, q=q, s=s, offs_pad=op))
-        return q, s
-
+    # cfg 5: MXFP8
     qx, sx = mx_last("mx X", "X", Xd, M, H)
     qw1, sw1 = mx_last("mx W1", "W1", W1d, E * F2, H)
     g_m("gemm fwd W1", qx, sx, qw1, sw1, M, F2, H, sk=fm.SCALE_E8M0_K4)
@@ -347,8 +484,11 @@ def cpu_baseline(step, host: dict):
       * quantization: a slice of whole rows (rowwise, MX last-dim blocks) or whole columns (colwise,
         MX row blocks) of about 2M elements, single-threaded numpy;
       * GEMMs: a block of up to 1024 output rows x 4096 output columns of the largest group, over the
-        whole contraction, on the step's own operands copied to the host, fp64 BLAS; scaled by flops.
-    """
+        whole contraction, on the step's own operands copied to the host, fp64 BLAS; scaled by flops;
+      * the MoE layer's routing (whole), gathers, SwiGLU and combines: about 2M output elements of
+        whole rows (tokens for the combines), single-threaded numpy.
+    Inputs that the step computes (the MoE layer's intermediate tensors) are copied from the device
+    as the last step left them."""
     import oracle
     from threadpoolctl import threadpool_info, threadpool_limits
     total_us = 0.0
@@ -376,8 +516,16 @@ def cpu_baseline(step, host: dict):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
+    dev_cache = {}
+
     def src(name):
+        if not isinstance(name, str):               # a device tensor the step computes
+            if id(name) not in dev_cache:
+                dev_cache[id(name)] = h(name)
+            return dev_cache[id(name)]
         return host["W1"] if name == "W1" else host[name]
+
+    from oracle import route as o_route, swiglu as o_swiglu
 
     for name, kind, *_ in step.items:
         sp = step.specs.get(name)
@@ -444,6 +592,44 @@ def cpu_baseline(step, host: dict):
                 f = lambda: oracle.mm_grouped_k_mx(np.ascontiguousarray(qa), sa, np.ascontiguousarray(qb), sb, one)
             full = 2.0 * float((hi - lo).sum()) * N * K
             add(name, timed(f), full / (2.0 * n * k * float(hi[e] - lo[e])))
+        elif op == "route":
+            ids = host[sp["ids"]]
+            add(name, timed(lambda: o_route.route(ids, sp["E"], sp["pad"]), 1), 1.0)
+        elif op in ("permute", "permute_rowwise"):
+            x, rsrc = src(sp["src"]), src(sp["rsrc"])
+            R, C = rsrc.size, x.shape[1]
+            r = max(1, min(R, QS // max(C, 1)))
+            sub = rsrc[:r]
+            f = (lambda: o_route.permute(x, sub, sp["topk"])) if op == "permute" else \
+                (lambda: oracle.quantize_rowwise(o_route.permute(x, sub, sp["topk"]), 0))
+            add(name, timed(f, 1), R / r)
+        elif op in ("swiglu", "swiglu_bwd"):
+            h1 = src(sp["h1"])
+            R, F = h1.shape[0], sp["F"]
+            r = max(1, min(R, QS // max(2 * F, 1)))
+            if op == "swiglu":
+                f = (lambda: o_swiglu.swiglu_fwd(h1[:r], F)) if sp["q"] is None else \
+                    (lambda: o_swiglu.swiglu_quantize_rowwise(h1[:r], F, 0))
+            else:
+                da2 = src(sp["da2"])
+                f = (lambda: o_swiglu.swiglu_bwd(da2[:r], h1[:r], F)) if sp["q"] is None else \
+                    (lambda: o_swiglu.swiglu_backward_quantize_rowwise(da2[:r], h1[:r], F, 0))
+            add(name, timed(f, 1), R / r)
+        elif op in ("combine", "combine_bwd"):
+            yg, dest, k = src(sp["yg"]), src(sp["dest"]), sp["topk"]
+            T, C = dest.size // k, yg.shape[1]
+            t = max(1, min(T, QS // max(C * k, 1)))
+            d = dest[:t * k]
+            yg_sub = yg[np.clip(d, 0, None)]
+            d_sub = np.where(d >= 0, np.arange(t * k), -1).astype(np.int32)
+            wts = None if sp["w"] is None else host[sp["w"]][:t]
+            if op == "combine":
+                f = lambda: o_route.combine(yg_sub, d_sub, wts, t, k)
+            else:
+                dy = host[sp["dy"]][:t]
+                s_sub = np.arange(t * k, dtype=np.int32)
+                f = lambda: o_route.combine_backward(dy, yg_sub, s_sub, d_sub, wts, t, k)
+            add(name, timed(f, 1), T / t)
         elif op == "g_k_bf16":
             a, b = host[sp["a"]], host[sp["b"]]
             Mt, N = a.shape
@@ -791,7 +977,9 @@ def main():
     if args.tensorwise and args.config != 2:
         raise SystemExit("--tensorwise is built for config 2 (the Llama3-8B linear layer)")
     progress(f"config {args.config}: inputs")
-    step, host = build_step(args.config, args.gw, args.tensorwise, keep_host=not args.no_cpu_baseline)
+    step, host = build_step(args.config, args.gw, args.tensorwise, keep_host=not args.no_cpu_baseline,
+                            experts_only=args.experts_only)
+    layer = args.config in (3, 4, 5) and not args.experts_only
     progress(f"config {args.config}: {len(step.items)} launches; warm-up")
     stream = torch.cuda.current_stream()
     names = [it[0] for it in step.items]
@@ -828,13 +1016,15 @@ def main():
         per[name] = (kind, work, us, hbm)
     q_bytes = sum(v[1] for v in per.values() if v[0] == "quant")
     q_us = sum(v[2] for v in per.values() if v[0] == "quant")
+    m_bytes = sum(v[1] for v in per.values() if v[0] == "moe")
+    m_us = sum(v[2] for v in per.values() if v[0] == "moe")
     g_flops = sum(v[1] for v in per.values() if v[0] == "gemm")
     g_us = sum(v[2] for v in per.values() if v[0] == "gemm")
 
     def roof(kind, work, us, hbm):
         """(bound, achieved, peak, unit): a GEMM is HBM-bound when moving its algorithmic bytes at
         peak bandwidth takes longer than its flops at peak MFMA rate."""
-        if kind == "quant":
+        if kind in ("quant", "moe"):
             return "hbm", work / us / 1e3, PEAK_HBM_GBPS, "GB/s"
         peak_f = PEAK_BF16_TFLOPS if kind == "gemm_bf16" else PEAK_FP8_TFLOPS
         if hbm / PEAK_HBM_GBPS / 1e3 > work / peak_f / 1e6:
@@ -869,13 +1059,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "experts": w.E, "routed_rows": w.M, "hidden": w.H,
                    "w1_out": w.F2, "w2_in": w.F,
-                   "step": ("fwd" if args.config == 1 else "fwd+dgrad+wgrad") + ("+bf16 wgrad" if args.gw else ""),
+                   **({"tokens": synth.tokens_topk(args.config)[0], "topk": synth.tokens_topk(args.config)[1]}
+                      if layer else {}),
+                   "step": ("MoE layer fwd+bwd: route, permute, W1, SwiGLU, W2, combine; combine bwd, "
+                            "W2 dgrad+wgrad, SwiGLU bwd, W1 dgrad+wgrad, input-gradient combine" if layer else
+                            ("fwd" if args.config == 1 else "fwd+dgrad+wgrad") + ("+bf16 wgrad" if args.gw else "")),
                    "recipe": "mxfp8 (e8m0 per 1x32)" if w.mx else
                    "fp8 e4m3fn tensorwise (one scale per tensor)" if args.tensorwise else
                    "fp8 e4m3fn rowwise + colwise backward",
                    **({"only": args.only} if args.only else {})},
         "quant_GBps": round(q_bytes / q_us / 1e3, 1) if q_us else None,
         "quant_us": round(q_us, 1),
+        **({"moe_ops_GBps": round(m_bytes / m_us / 1e3, 1), "moe_ops_us": round(m_us, 1)} if m_us else {}),
         "gemm_TFLOPs": round(g_flops / g_us / 1e6, 1) if g_us else None,
         "gemm_us": round(g_us, 1),
         "kernels_us": {k: round(v[2], 1) for k, v in per.items()},

@@ -146,7 +146,9 @@ int quantize_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_
  *   h1     bf16 [rows][ld_h1]  W1's output: gate in columns [0, F), up in [F, 2F)
  *   a2     bf16 [rows][F]      bf16(silu(gate) * up), silu(g) = g / (1 + e^-g),
  *                              fp32 arithmetic, round to nearest even (written)
- *   q      u8   [rows][F]      FP8 codes of a2, as quantize_rowwise(a2) (written)
+ *   q      u8   [rows][F]      FP8 codes of a2, as quantize_rowwise(a2) (written), or
+ *                              NULL together with scale: a2 only (for a caller that
+ *                              quantizes a2 another way, e.g. MXFP8)
  *   scale  f32  [rows]         as quantize_rowwise(a2) (written)
  *   Requires: rows, F >= 0; ld_h1 >= 2F; F % 8 == 0; ld_h1 % 8 == 0; h1, a2 and
  *   q 16-byte aligned, scale 4-byte aligned.  The caller owns every buffer.
@@ -162,7 +164,8 @@ int swiglu_quantize_rowwise(const void *h1_bf16, int64_t rows, int64_t F, int64_
  *   h1     bf16 [rows][ld_h1]  as above
  *   dh1    bf16 [rows][2F]     [bf16(da2 up s (1 + g (1 - s))) | bf16(da2 g s)],
  *                              s = sigmoid(gate), fp32 arithmetic (written)
- *   q      u8   [rows][2F]     FP8 codes of dh1, as quantize_rowwise(dh1) (written)
+ *   q      u8   [rows][2F]     FP8 codes of dh1, as quantize_rowwise(dh1) (written), or
+ *                              NULL together with scale: dh1 only
  *   scale  f32  [rows]         as quantize_rowwise(dh1) (written)
  *   Requires: as swiglu_quantize_rowwise, and da2 16-byte aligned.
  */
@@ -360,13 +363,35 @@ int moe_permute_quantized(const void *q, const float *scale, int64_t tokens, int
                           void *qg, float *scale_g, void *stream);
 
 /*
+ * moe_permute_rowwise -- gather token rows into the grouped layout and
+ * quantize them rowwise in the same pass: one read of each routed token row
+ * gives the gathered bf16 row (kept for the backward's colwise operand) and
+ * its FP8 codes and scale for the forward GEMM.
+ *   [as moe_route; P1 Details, MoE paragraph, and P4 "Три уровня
+ *   оптимизации Triton-ядер": quantization fused into the kernel that
+ *   produces the operand, ahead of the grouped GEMM.]
+ *   x        bf16 [tokens][cols]
+ *   src      int32 [rows_out]      as written by moe_route
+ *   xg       bf16 [rows_out][cols] as moe_permute(x) (written), or NULL when not
+ *            wanted (then cols <= 16384: longer rows are cast from that copy)
+ *   qg       u8   [rows_out][cols] codes of quantize_rowwise(xg) (written)
+ *   scale_g  f32  [rows_out]       its row scales; a padding row takes fmax/1e-12f (written)
+ *   Requires: cols % 8 == 0; x, xg and qg 16-byte aligned, src and scale_g
+ *   4-byte aligned.  One kernel, no allocation.
+ */
+int moe_permute_rowwise(const void *x_bf16, int64_t tokens, int64_t cols, int32_t topk,
+                        const int32_t *src, int64_t rows_out, int codec, void *xg_bf16, void *qg,
+                        float *scale_g, void *stream);
+
+/*
  * moe_combine -- weighted sum of each token's expert outputs.
  *   [P4 "MoE" (the routed experts' outputs summed per token with the router's
  *   weights).]
  *   yg       bf16 [rows_in][cols]  expert outputs in the grouped layout
  *   dest     int32 [tokens*topk]   as written by moe_route; a slot whose dest
  *                                  is < 0 or >= rows_in contributes nothing
- *   weights  f32 [tokens][topk]
+ *   weights  f32 [tokens][topk], or NULL: every weight 1 (the backward's sum of a
+ *            token's routed input gradients)
  *   y        bf16 [tokens][cols]   y[t] = sum over j in order 0..topk-1 of
  *            weights[t][j] * yg[dest[t*topk+j]], each product and sum one fp32
  *            operation rounded to nearest, then rounded to bf16 (nearest even) (written)
@@ -375,6 +400,35 @@ int moe_permute_quantized(const void *q, const float *scale, int64_t tokens, int
 int moe_combine(const void *yg_bf16, int64_t rows_in, const int32_t *dest,
                 const float *weights, int64_t tokens, int32_t topk, int64_t cols,
                 void *y_bf16, void *stream);
+
+/*
+ * moe_combine_backward -- the gradients through moe_combine, for the loss
+ * gradient dy of its output: each routed row's gradient in the grouped layout
+ * (optionally quantized rowwise in the same pass, for the W2 dgrad GEMM) and
+ * each router weight's gradient.
+ *   [P4 "MoE" (the routed experts' outputs summed per token with the router's
+ *   weights); P1 Details, MoE paragraph (the backward's grouped GEMMs on
+ *   dynamically quantized operands).]
+ *   dy       bf16 [tokens][cols]   gradient of moe_combine's output
+ *   yg       bf16 [rows][cols]     the expert outputs moe_combine summed
+ *   dest     int32 [tokens*topk], src int32 [rows]  from one moe_route call
+ *   weights  f32  [tokens][topk]
+ *   dyg      bf16 [rows][cols]     for grouped row r holding slot s = src[r] of
+ *            token t = s / topk: bf16(weights[s] * dy[t]), one fp32 product
+ *            rounded to nearest even; zeros for a row holding no slot (written)
+ *   q        u8   [rows][cols]     codes of quantize_rowwise(dyg), or NULL (written)
+ *   scale    f32  [rows]           its row scales, NULL exactly when q is (written)
+ *   dweights f32  [tokens*topk]    sum over columns of dy[t] * yg[dest[s]] (exact
+ *            bf16 products, fp32 sums in an unspecified order); 0 for a slot whose
+ *            dest is < 0 or >= rows (written)
+ *   Requires: cols % 8 == 0 and cols <= 16384 (else FP8MOE_ERR_UNSUPPORTED);
+ *   dy, yg, dyg and q 16-byte aligned, the int32 and f32 arrays 4-byte
+ *   aligned.  One kernel, no allocation.
+ */
+int moe_combine_backward(const void *dy_bf16, const void *yg_bf16, int64_t rows,
+                         const int32_t *dest, const int32_t *src, const float *weights,
+                         int64_t tokens, int32_t topk, int64_t cols, int codec, void *dyg_bf16,
+                         void *q, float *scale, float *dweights, void *stream);
 
 /*
  * quantize_colwise -- one fp32 scale per (group, column), reduced over the

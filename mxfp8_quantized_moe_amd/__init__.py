@@ -21,7 +21,8 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
-           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_permute", "moe_combine",
+           "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_route_workspace_bytes", "moe_permute", "moe_combine",
+           "moe_permute_rowwise", "moe_combine_backward",
            "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise",
            "quantize_blockwise_tokens", "grouped_mm_blockwise_k"]
 
@@ -148,8 +149,9 @@ def grouped_mm_scaled(mode, a, a_fmt, a_scale, b, b_fmt, b_scale, scale_kind, of
     return out
 
 
-def swiglu_quantize_rowwise(h1, codec=E4M3FN, a2=None, q=None, scale=None, stream=None):
-    """h1 [R, 2F] bf16 (gate | up; row stride may exceed 2F) -> (a2 bf16 [R, F], q uint8 [R, F], scale f32 [R])."""
+def swiglu_quantize_rowwise(h1, codec=E4M3FN, a2=None, q=None, scale=None, stream=None, codes=True):
+    """h1 [R, 2F] bf16 (gate | up; row stride may exceed 2F) -> (a2 bf16 [R, F], q uint8 [R, F], scale f32 [R]);
+    with codes=False only a2 is computed and q, scale are None."""
     h1 = _bits(h1)
     R, F2 = h1.shape
     if F2 % 2 or (h1.numel() and h1.stride(1) != 1):
@@ -157,15 +159,19 @@ def swiglu_quantize_rowwise(h1, codec=E4M3FN, a2=None, q=None, scale=None, strea
     F = F2 // 2
     ld = h1.stride(0) if h1.numel() else F2
     a2 = torch.empty((R, F), dtype=torch.bfloat16, device=h1.device) if a2 is None else a2
-    q = torch.empty((R, F), dtype=torch.uint8, device=h1.device) if q is None else q
-    scale = torch.empty((R,), dtype=torch.float32, device=h1.device) if scale is None else scale
+    if codes:
+        q = torch.empty((R, F), dtype=torch.uint8, device=h1.device) if q is None else q
+        scale = torch.empty((R,), dtype=torch.float32, device=h1.device) if scale is None else scale
+    else:
+        q = scale = None
     _lib.check("swiglu_quantize_rowwise", _lib.lib().swiglu_quantize_rowwise(
         _ptr(h1), R, F, ld, codec, _ptr(a2), _ptr(q), _ptr(scale), _stream(stream)))
     return a2, q, scale
 
 
-def swiglu_backward_quantize_rowwise(da2, h1, codec=E4M3FN, dh1=None, q=None, scale=None, stream=None):
-    """da2 [R, F] bf16 and h1 [R, 2F] bf16 -> (dh1 bf16 [R, 2F], q uint8 [R, 2F], scale f32 [R])."""
+def swiglu_backward_quantize_rowwise(da2, h1, codec=E4M3FN, dh1=None, q=None, scale=None, stream=None, codes=True):
+    """da2 [R, F] bf16 and h1 [R, 2F] bf16 -> (dh1 bf16 [R, 2F], q uint8 [R, 2F], scale f32 [R]);
+    with codes=False only dh1 is computed and q, scale are None."""
     h1 = _bits(h1)
     da2 = _bits(da2).contiguous()
     R, F2 = h1.shape
@@ -174,8 +180,11 @@ def swiglu_backward_quantize_rowwise(da2, h1, codec=E4M3FN, dh1=None, q=None, sc
     F = F2 // 2
     ld = h1.stride(0) if h1.numel() else F2
     dh1 = torch.empty((R, F2), dtype=torch.bfloat16, device=h1.device) if dh1 is None else dh1
-    q = torch.empty((R, F2), dtype=torch.uint8, device=h1.device) if q is None else q
-    scale = torch.empty((R,), dtype=torch.float32, device=h1.device) if scale is None else scale
+    if codes:
+        q = torch.empty((R, F2), dtype=torch.uint8, device=h1.device) if q is None else q
+        scale = torch.empty((R,), dtype=torch.float32, device=h1.device) if scale is None else scale
+    else:
+        q = scale = None
     _lib.check("swiglu_backward_quantize_rowwise", _lib.lib().swiglu_backward_quantize_rowwise(
         _ptr(da2), _ptr(h1), R, F, ld, codec, _ptr(dh1), _ptr(q), _ptr(scale), _stream(stream)))
     return dh1, q, scale
@@ -259,6 +268,10 @@ def moe_route_rows_bound(slots: int, n_experts: int, pad: int = 1) -> int:
     return int(_lib.lib().moe_route_rows_bound(slots, n_experts, pad))
 
 
+def moe_route_workspace_bytes(slots: int, n_experts: int) -> int:
+    return int(_lib.lib().moe_route_workspace_bytes(slots, n_experts))
+
+
 def moe_route(expert_ids, n_experts, pad=1, out=None, workspace=None, stream=None):
     """expert_ids int32 [T, k] -> (counts [E], offs [E], dest [T*k], src [rows bound]), all int32."""
     ids = expert_ids.contiguous()
@@ -317,17 +330,63 @@ def moe_permute_quantized(q, scale, src, topk, codec=E4M3FN, qg=None, scale_g=No
 
 
 def moe_combine(yg, dest, weights, topk, y=None, stream=None):
-    """yg bf16 [R, C], dest int32 [T*k], weights f32 [T, k] -> y bf16 [T, C]."""
+    """yg bf16 [R, C], dest int32 [T*k], weights f32 [T, k] or None (every weight 1) -> y bf16 [T, C]."""
     yg = _bits(yg).contiguous()
     R, C = yg.shape
-    weights = weights.contiguous()
-    T = weights.shape[0]
-    if weights.dtype != torch.float32 or tuple(weights.shape) != (T, topk) or dest.numel() != T * topk:
-        raise ValueError("moe_combine: weights f32 [T, topk] and dest [T*topk]")
+    T = dest.numel() // topk
+    if weights is not None:
+        weights = weights.contiguous()
+        if weights.dtype != torch.float32 or tuple(weights.shape) != (T, topk):
+            raise ValueError("moe_combine: weights f32 [T, topk]")
+    if dest.numel() != T * topk:
+        raise ValueError("moe_combine: dest [T*topk]")
     y = torch.empty((T, C), dtype=yg.dtype, device=yg.device) if y is None else y
     _lib.check("moe_combine", _lib.lib().moe_combine(_ptr(yg), R, _ptr(dest), _ptr(weights), T, topk, C, _ptr(y),
                                                      _stream(stream)))
     return y
+
+
+def moe_permute_rowwise(x, src, topk, codec=E4M3FN, xg=None, qg=None, scale_g=None, keep_bf16=True, stream=None):
+    """x bf16 [T, C], src int32 [R] -> (xg bf16 [R, C] or None, qg u8 [R, C], scale_g f32 [R]): the gathered
+    rows and their rowwise codes in one pass (keep_bf16=False skips the bf16 copy)."""
+    x = _bits(x).contiguous()
+    T, C = x.shape
+    R = src.numel()
+    if keep_bf16:
+        xg = torch.empty((R, C), dtype=x.dtype, device=x.device) if xg is None else xg
+    else:
+        xg = None
+    qg = torch.empty((R, C), dtype=torch.uint8, device=x.device) if qg is None else qg
+    scale_g = torch.empty((R,), dtype=torch.float32, device=x.device) if scale_g is None else scale_g
+    _lib.check("moe_permute_rowwise", _lib.lib().moe_permute_rowwise(
+        _ptr(x), T, C, topk, _ptr(src), R, codec, _ptr(xg), _ptr(qg), _ptr(scale_g), _stream(stream)))
+    return xg, qg, scale_g
+
+
+def moe_combine_backward(dy, yg, dest, src, weights, topk, codec=E4M3FN, codes=True, dyg=None, q=None, scale=None,
+                         dweights=None, stream=None):
+    """dy bf16 [T, C], yg bf16 [R, C], dest int32 [T*k], src int32 [R], weights f32 [T, k] ->
+    (dyg bf16 [R, C], q u8 [R, C] or None, scale f32 [R] or None, dweights f32 [T*k])."""
+    dy = _bits(dy).contiguous()
+    yg = _bits(yg).contiguous()
+    T, C = dy.shape
+    R = yg.shape[0]
+    weights = weights.contiguous()
+    if weights.dtype != torch.float32 or tuple(weights.shape) != (T, topk) or dest.numel() != T * topk \
+            or src.numel() != R or yg.shape[1] != C:
+        raise ValueError("moe_combine_backward: dy [T, C], yg [R, C], weights f32 [T, topk], dest [T*topk], src [R]")
+    dev = dy.device
+    dyg = torch.empty((R, C), dtype=dy.dtype, device=dev) if dyg is None else dyg
+    if codes:
+        q = torch.empty((R, C), dtype=torch.uint8, device=dev) if q is None else q
+        scale = torch.empty((R,), dtype=torch.float32, device=dev) if scale is None else scale
+    else:
+        q = scale = None
+    dweights = torch.empty((T * topk,), dtype=torch.float32, device=dev) if dweights is None else dweights
+    _lib.check("moe_combine_backward", _lib.lib().moe_combine_backward(
+        _ptr(dy), _ptr(yg), R, _ptr(dest), _ptr(src), _ptr(weights), T, topk, C, codec, _ptr(dyg), _ptr(q),
+        _ptr(scale), _ptr(dweights), _stream(stream)))
+    return dyg, q, scale, dweights
 
 
 def encode_f32(y, codec=E4M3FN, q=None, stream=None):

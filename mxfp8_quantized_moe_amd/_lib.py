@@ -26,7 +26,8 @@ EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "moe_route_rows_bound", "moe_permute", "moe_combine", "quantize_tensorwise", "moe_permute_quantized",
            "quantize_blockwise", "grouped_mm_blockwise", "quantize_blockwise_tokens",
            "blockwise_token_blocks_bound", "grouped_mm_blockwise_k",
-           "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget", "moe_route_noalloc"]
+           "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget", "moe_route_noalloc",
+           "moe_permute_rowwise", "moe_combine_backward"]
 
 _lib = None
 
@@ -60,6 +61,9 @@ _SIGS = {
     "moe_permute": (_int, [_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp]),
     "moe_permute_quantized": (_int, [_vp, _vp, _i64, _i64, _i32, _vp, _i64, _int, _vp, _vp, _vp]),
     "moe_combine": (_int, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
+    "moe_permute_rowwise": (_int, [_vp, _i64, _i64, _i32, _vp, _i64, _int, _vp, _vp, _vp, _vp]),
+    "moe_combine_backward": (_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _i64, _int, _vp, _vp, _vp, _vp,
+                                    _vp]),
 }
 
 

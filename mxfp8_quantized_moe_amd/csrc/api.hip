@@ -179,6 +179,27 @@ int moe_combine(const void* yg_bf16, int64_t rows_in, const int32_t* dest, const
                                           cols, static_cast<uint16_t*>(y_bf16), as_stream(stream)));
 }
 
+int moe_permute_rowwise(const void* x_bf16, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                        int64_t rows_out, int codec, void* xg_bf16, void* qg, float* scale_g, void* stream) {
+  const int st = check_moe_permute_rowwise(x_bf16, tokens, cols, topk, src, rows_out, codec, xg_bf16, qg, scale_g);
+  if (st) return st;
+  return launch_status(launch_moe_permute_rowwise(static_cast<const uint16_t*>(x_bf16), tokens, cols, topk, src,
+                                                  rows_out, codec, static_cast<uint16_t*>(xg_bf16),
+                                                  static_cast<uint8_t*>(qg), scale_g, as_stream(stream)));
+}
+
+int moe_combine_backward(const void* dy_bf16, const void* yg_bf16, int64_t rows, const int32_t* dest,
+                         const int32_t* src, const float* weights, int64_t tokens, int32_t topk, int64_t cols,
+                         int codec, void* dyg_bf16, void* q, float* scale, float* dweights, void* stream) {
+  const int st = check_moe_combine_backward(dy_bf16, yg_bf16, rows, dest, src, weights, tokens, topk, cols, codec,
+                                            dyg_bf16, q, scale, dweights);
+  if (st) return st;
+  return launch_status(launch_moe_combine_backward(
+      static_cast<const uint16_t*>(dy_bf16), static_cast<const uint16_t*>(yg_bf16), rows, dest, src, weights, tokens,
+      topk, cols, codec, static_cast<uint16_t*>(dyg_bf16), static_cast<uint8_t*>(q), scale, dweights,
+      as_stream(stream)));
+}
+
 int quantize_colwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                      int32_t n_groups, int codec, void* q_t, int64_t ld_q, float* scale, void* stream) {
   const int st = check_quantize_colwise(x_bf16, batch, rows, cols, offs, n_groups, codec, q_t, ld_q, scale);
@@ -244,6 +265,6 @@ int fp8moe_default_codec(int hip_device, int* codec_out) {
 
 int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(polls); }
 
-int fp8moe_version(void) { return 103; }
+int fp8moe_version(void) { return 104; }
 
 }  // extern "C"

@@ -66,6 +66,13 @@ hipError_t launch_moe_permute_quantized(const uint8_t* q, const float* scale, in
                                         float* scale_g, hipStream_t st);
 hipError_t launch_moe_combine(const uint16_t* yg, int64_t rows_in, const int32_t* dest, const float* w,
                               int64_t tokens, int topk, int64_t cols, uint16_t* y, hipStream_t st);
+hipError_t launch_moe_permute_rowwise(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
+                                      int64_t rows_out, int codec, uint16_t* xg, uint8_t* qg, float* scale_g,
+                                      hipStream_t st);
+hipError_t launch_moe_combine_backward(const uint16_t* dy, const uint16_t* yg, int64_t rows, const int32_t* dest,
+                                       const int32_t* src, const float* w, int64_t tokens, int topk, int64_t cols,
+                                       int codec, uint16_t* dyg, uint8_t* q, float* scale, float* dw,
+                                       hipStream_t st);
 hipError_t launch_swiglu_quantize_rowwise(const uint16_t* h1, int64_t rows, int64_t F, int64_t ld_h1, int codec,
                                           uint16_t* a2, uint8_t* q, float* scale, hipStream_t st);
 hipError_t launch_swiglu_backward_quantize_rowwise(const uint16_t* da2, const uint16_t* h1, int64_t rows, int64_t F,

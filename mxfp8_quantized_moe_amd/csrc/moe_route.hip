@@ -227,8 +227,8 @@ typedef float rt_f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 rt_bf16x2 __attribute__((ext_vector_type(2)));
 
 // One workgroup per token: y[t] = sum_j w[t, j] * yg[dest[t, j]] in slot
-// order.  A thread loads its chunk of up to eight rows before summing (a
-// dropped slot loads row 0 and its result is not taken).
+// order (w null: every weight 1).  A thread loads its chunk of up to eight
+// rows before summing (a dropped slot loads row 0 and its result is not taken).
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ yg, int64_t rows_in,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ w, int topk, int64_t cols,
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int64_t t = blockIdx.x;
   const int64_t nc = cols >> 3;
   const int32_t* __restrict__ dt = dest + t * topk;
-  const float* __restrict__ wt = w + t * topk;
+  const float* __restrict__ wt = w != nullptr ? w + t * topk : nullptr;
   u32x4* __restrict__ out = reinterpret_cast<u32x4*>(y + t * cols);
   for (int64_t c = threadIdx.x; c < nc; c += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         if (j0 + u >= topk) break;
-        const float wj = wt[j0 + u];
+        const float wj = wt != nullptr ? wt[j0 + u] : 1.0f;
         const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -275,6 +275,121 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int k = 0; k < 4; ++k)
       o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rt_f32x2{acc[2 * k], acc[2 * k + 1]}, rt_bf16x2));
     out[c] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// Backward of the combine.  Workgroups [0, tokens) take one token each: the
+// token's gradient row dy[t] stays in registers (ITEMS 16-byte chunks per
+// thread, 256 threads), and for each of its slots s = t*topk + j, in order,
+// the workgroup writes the routed row's gradient dyg[dest[s]] = bf16(w[s] *
+// dy[t]) (one fp32 product, rounded to nearest even), reduces the router
+// weight's gradient dw[s] = <dy[t], yg[dest[s]]> (exact bf16 products, fp32
+// sums), and, with codes requested, quantizes the routed row rowwise from the
+// bf16 values it just wrote.  A dropped slot gets dw = 0.  Workgroups from
+// `tokens` on clear the grouped rows that hold no slot (padding): zeros, zero
+// codes and the all-zero row's scale.
+template <int CODEC, int ITEMS, bool QUANT>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dy,
+                                                          const uint16_t* __restrict__ yg, int64_t rows,
+                                                          const int32_t* __restrict__ dest,
+                                                          const int32_t* __restrict__ src,
+                                                          const float* __restrict__ w, int64_t tokens, int topk,
+                                                          int64_t cols, uint16_t* __restrict__ dyg,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                          float* __restrict__ dw, int zero_blocks) {
+  __shared__ float red_sum[2][4];
+  __shared__ uint32_t red_max[2][4];
+  const int tid = threadIdx.x;
+  const int64_t nc = cols >> 3;
+  const int64_t S = tokens * topk;
+  if ((int64_t)blockIdx.x >= tokens) {   // padding rows (no barrier on this side)
+    const float s0 = scale_from_amax(0.0f, CODEC);
+    for (int64_t r = (int64_t)blockIdx.x - tokens; r < rows; r += zero_blocks) {
+      const int sl = src[r];
+      if (sl >= 0 && (int64_t)sl < S) continue;
+      u32x4* __restrict__ o = reinterpret_cast<u32x4*>(dyg + r * cols);
+      for (int64_t c = tid; c < nc; c += 256) o[c] = u32x4{0, 0, 0, 0};
+      if constexpr (QUANT) {
+        u32x2* __restrict__ qo = reinterpret_cast<u32x2*>(q + r * cols);
+        for (int64_t c = tid; c < nc; c += 256) qo[c] = u32x2{0, 0};
+        if (tid == 0) scale[r] = s0;
+      }
+    }
+    return;
+  }
+  const int64_t t = blockIdx.x;
+  const u32x4* __restrict__ dr = reinterpret_cast<const u32x4*>(dy + t * cols);
+  u32x4 dv[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int64_t c = (int64_t)i * 256 + tid;
+    dv[i] = c < nc ? dr[c] : u32x4{0, 0, 0, 0};
+  }
+  int b = 0;   // reduction buffer of the next slot that reduces
+  for (int j = 0; j < topk; ++j) {   // uniform over the workgroup
+    const int64_t sl = t * topk + j;
+    const int d = dest[sl];
+    if (d < 0 || (int64_t)d >= rows) {
+      if (tid == 0) dw[sl] = 0.0f;
+      continue;
+    }
+    const float wj = w[sl];
+    const u32x4* __restrict__ yr = reinterpret_cast<const u32x4*>(yg + (int64_t)d * cols);
+    u32x4* __restrict__ gr = reinterpret_cast<u32x4*>(dyg + (int64_t)d * cols);
+    u32x4 gv[ITEMS];
+    float acc = 0.0f;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int64_t c = (int64_t)i * 256 + tid;
+      gv[i] = u32x4{0, 0, 0, 0};
+      if (c < nc) {
+        const u32x4 yv = yr[c];
+        const uint32_t dw4[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+        const uint32_t yw4[4] = {yv.x, yv.y, yv.z, yv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float d0 = bf16_lo(dw4[k]), d1 = bf16_hi(dw4[k]);
+          acc = fmaf(d0, bf16_lo(yw4[k]), acc);
+          acc = fmaf(d1, bf16_hi(yw4[k]), acc);
+          const float p0 = wj * d0, p1 = wj * d1;   // fp32 products, each rounded once
+          o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rt_f32x2{p0, p1}, rt_bf16x2));
+        }
+        gv[i] = u32x4{o[0], o[1], o[2], o[3]};
+        gr[c] = gv[i];
+      }
+      if constexpr (QUANT) {
+        m = pk_absmax_bf16(m, gv[i].x);
+        m = pk_absmax_bf16(m, gv[i].y);
+        m = pk_absmax_bf16(m, gv[i].z);
+        m = pk_absmax_bf16(m, gv[i].w);
+      }
+    }
+    // workgroup reductions: the buffers alternate between reducing slots, so one barrier per slot
+    // suffices (a buffer is rewritten only after the next slot's barrier, which every read precedes)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if constexpr (QUANT) m = wave_max_u32(pk_fold(m));
+    if ((tid & 63) == 0) {
+      red_sum[b][tid >> 6] = acc;
+      if constexpr (QUANT) red_max[b][tid >> 6] = m;
+    }
+    __syncthreads();
+    if (tid == 0) dw[sl] = (red_sum[b][0] + red_sum[b][1]) + (red_sum[b][2] + red_sum[b][3]);
+    if constexpr (QUANT) {
+      m = max(max(red_max[b][0], red_max[b][1]), max(red_max[b][2], red_max[b][3]));
+      const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
+      u32x2* __restrict__ qr = reinterpret_cast<u32x2*>(q + (int64_t)d * cols);
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int64_t c = (int64_t)i * 256 + tid;
+        if (c < nc)
+          qr[c] = u32x2{quant_bf16x4<CODEC>(gv[i].x, gv[i].y, s), quant_bf16x4<CODEC>(gv[i].z, gv[i].w, s)};
+      }
+      if (tid == 0) scale[d] = s;
+    }
+    b ^= 1;
   }
 }
 
@@ -366,6 +481,40 @@ hipError_t launch_moe_permute_quantized(const uint8_t* q, const float* scale, in
                                         float* scale_g, hipStream_t st) {
   if (rows_out == 0) return hipSuccess;
   return launch_permute(q, tokens, cols, topk, src, rows_out, qg, scale, scale_g, codec, st);
+}
+
+template <int CODEC, bool QUANT>
+static hipError_t combine_bwd_items(const uint16_t* dy, const uint16_t* yg, int64_t rows, const int32_t* dest,
+                                    const int32_t* src, const float* w, int64_t tokens, int topk, int64_t cols,
+                                    uint16_t* dyg, uint8_t* q, float* scale, float* dw, hipStream_t st) {
+  const int64_t items = ((cols >> 3) + 255) / 256;
+  const int zero_blocks = (int)std::min<int64_t>(rows, 1024);
+  const dim3 grid((unsigned)(tokens + zero_blocks));
+  auto go = [&](auto it_tag) -> hipError_t {
+    constexpr int IT = decltype(it_tag)::value;
+    hipLaunchKernelGGL((combine_bwd_kernel<CODEC, IT, QUANT>), grid, dim3(256), 0, st, dy, yg, rows, dest, src, w,
+                       tokens, topk, cols, dyg, q, scale, dw, zero_blocks);
+    return hipGetLastError();
+  };
+  if (items <= 1) return go(std::integral_constant<int, 1>{});
+  if (items <= 2) return go(std::integral_constant<int, 2>{});
+  if (items <= 4) return go(std::integral_constant<int, 4>{});
+  if (items <= 8) return go(std::integral_constant<int, 8>{});
+  return hipErrorInvalidValue;   // beyond the columns the ABI accepts
+}
+
+hipError_t launch_moe_combine_backward(const uint16_t* dy, const uint16_t* yg, int64_t rows, const int32_t* dest,
+                                       const int32_t* src, const float* w, int64_t tokens, int topk, int64_t cols,
+                                       int codec, uint16_t* dyg, uint8_t* q, float* scale, float* dw,
+                                       hipStream_t st) {
+  if (tokens == 0 && rows == 0) return hipSuccess;   // (no columns: the kernel reads nothing, dw is 0)
+  const bool quant = q != nullptr;
+  if (codec == 0)
+    return quant ? combine_bwd_items<0, true>(dy, yg, rows, dest, src, w, tokens, topk, cols, dyg, q, scale, dw, st)
+                 : combine_bwd_items<0, false>(dy, yg, rows, dest, src, w, tokens, topk, cols, dyg, q, scale, dw,
+                                               st);
+  return quant ? combine_bwd_items<1, true>(dy, yg, rows, dest, src, w, tokens, topk, cols, dyg, q, scale, dw, st)
+               : combine_bwd_items<1, false>(dy, yg, rows, dest, src, w, tokens, topk, cols, dyg, q, scale, dw, st);
 }
 
 hipError_t launch_moe_combine(const uint16_t* yg, int64_t rows_in, const int32_t* dest, const float* w,

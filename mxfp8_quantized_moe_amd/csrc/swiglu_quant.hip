@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t* __restr
   const u32x4* __restrict__ gr = reinterpret_cast<const u32x4*>(h1 + rr * ld_h1);
   const u32x4* __restrict__ ur = reinterpret_cast<const u32x4*>(h1 + rr * ld_h1 + F);
   u32x4* __restrict__ ar = reinterpret_cast<u32x4*>(a2 + rr * F);
-  u32x2* __restrict__ qr = reinterpret_cast<u32x2*>(q + rr * F);
+  u32x2* __restrict__ qr = reinterpret_cast<u32x2*>(q != nullptr ? q + rr * F : nullptr);
   uint32_t m = 0;
   if constexpr (ITEMS > 0) {
     u32x4 av[ITEMS];
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t* __restr
       }
       m = sw_absmax4(m, av[i]);
     }
+    if (q == nullptr) return;   // bf16 output only (uniform over the launch)
     m = sw_row_max<TPR>(pk_fold(m), red);
     const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
 #pragma unroll
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t* __restr
         m = sw_absmax4(m, a);
       }
     }
+    if (q == nullptr) return;
     m = sw_row_max<TPR>(pk_fold(m), red);
     const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
     if (valid) {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
   const u32x4* __restrict__ gr = reinterpret_cast<const u32x4*>(h1 + rr * ld_h1);
   const u32x4* __restrict__ ur = reinterpret_cast<const u32x4*>(h1 + rr * ld_h1 + F);
   u32x4* __restrict__ orow = reinterpret_cast<u32x4*>(dh1 + rr * 2 * F);
-  u32x2* __restrict__ qr = reinterpret_cast<u32x2*>(q + rr * 2 * F);
+  u32x2* __restrict__ qr = reinterpret_cast<u32x2*>(q != nullptr ? q + rr * 2 * F : nullptr);
   uint32_t m = 0;
   if constexpr (ITEMS > 0) {
     u32x4 gv[ITEMS], uv[ITEMS];
@@ -189,6 +191,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
       }
       m = sw_absmax4(sw_absmax4(m, gv[i]), uv[i]);
     }
+    if (q == nullptr) return;   // bf16 output only (uniform over the launch)
     m = sw_row_max<TPR>(pk_fold(m), red);
     const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
 #pragma unroll
@@ -210,6 +213,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
         m = sw_absmax4(sw_absmax4(m, a), b);
       }
     }
+    if (q == nullptr) return;
     m = sw_row_max<TPR>(pk_fold(m), red);
     const float s = scale_from_amax(__uint_as_float(m << 16), CODEC);
     if (valid) {

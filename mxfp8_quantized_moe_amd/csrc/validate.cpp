@@ -155,8 +155,8 @@ int check_swiglu(const void* h1, int64_t rows, int64_t F, int64_t ld_h1, int cod
   if (rows < 0 || F < 0 || rows > kI32Max * 256LL || F > kI32Max / 2 || ld_h1 < 2 * F) return FP8MOE_ERR_SHAPE;
   const int64_t n = mul(rows, 2 * F);
   if (n < 0 || mul(rows, ld_h1) < 0) return FP8MOE_ERR_SHAPE;
-  if (!need(h1, n) || !need(out_bf16, n) || !need(q, n) || !need(scale, rows) || (backward && !need(da2, n)))
-    return FP8MOE_ERR_NULL;
+  if ((q == nullptr) != (scale == nullptr)) return FP8MOE_ERR_NULL;   // codes and scales come together
+  if (!need(h1, n) || !need(out_bf16, n) || (backward && !need(da2, n))) return FP8MOE_ERR_NULL;
   if (F % 8 || ld_h1 % 8 || !aligned(h1, 16) || !aligned(out_bf16, 16) || !aligned(q, 16) || !aligned(scale, 4) ||
       (backward && !aligned(da2, 16)))
     return FP8MOE_ERR_ALIGN;
@@ -314,8 +314,42 @@ int check_moe_combine(const void* yg, int64_t rows_in, const int32_t* dest, cons
   const int64_t S = mul(tokens, topk), ny = mul(tokens, cols), ng = mul(rows_in, cols);
   if (S < 0 || S > kI32Max || ny < 0 || ng < 0) return FP8MOE_ERR_SHAPE;
   const int64_t work = cols ? S : 0;   // nothing is read when there are no columns
-  if (!need(yg, cols ? ng : 0) || !need(dest, work) || !need(w, work) || !need(y, ny)) return FP8MOE_ERR_NULL;
+  // w may be null: every weight 1
+  if (!need(yg, cols ? ng : 0) || !need(dest, work) || !need(y, ny)) return FP8MOE_ERR_NULL;
   if (cols % 8 || !aligned(yg, 16) || !aligned(y, 16) || !aligned(dest, 4) || !aligned(w, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_moe_permute_rowwise(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                              int64_t rows_out, int codec, const void* xg, const void* qg, const float* scale_g) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (tokens < 0 || cols < 0 || topk < 1 || rows_out < 0 || rows_out > kI32Max * 256LL || cols > kI32Max)
+    return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk), nx = mul(tokens, cols), ng = mul(rows_out, cols);
+  if (S < 0 || S > kI32Max || nx < 0 || ng < 0) return FP8MOE_ERR_SHAPE;
+  if (!need(x, nx) || !need(src, rows_out) || !need(qg, ng) || !need(scale_g, rows_out)) return FP8MOE_ERR_NULL;
+  if (xg == nullptr && cols > kRowwiseRegCols && rows_out > 0) return FP8MOE_ERR_NULL;
+  if (cols % 8 || !aligned(x, 16) || !aligned(xg, 16) || !aligned(qg, 16) || !aligned(src, 4) ||
+      !aligned(scale_g, 4))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
+int check_moe_combine_backward(const void* dy, const void* yg, int64_t rows, const int32_t* dest,
+                               const int32_t* src, const float* w, int64_t tokens, int32_t topk, int64_t cols,
+                               int codec, const void* dyg, const void* q, const float* scale, const float* dw) {
+  if (codec != FP8MOE_E4M3FN && codec != FP8MOE_E4M3FNUZ) return FP8MOE_ERR_ENUM;
+  if (tokens < 0 || cols < 0 || topk < 1 || rows < 0 || rows > kI32Max) return FP8MOE_ERR_SHAPE;
+  if (cols > kCombineBwdMaxCols) return FP8MOE_ERR_UNSUPPORTED;
+  const int64_t S = mul(tokens, topk), ny = mul(tokens, cols), ng = mul(rows, cols);
+  if (S < 0 || S > kI32Max || ny < 0 || ng < 0 || tokens > kI32Max - 1024) return FP8MOE_ERR_SHAPE;
+  if ((q == nullptr) != (scale == nullptr)) return FP8MOE_ERR_NULL;   // codes and scales come together
+  if (!need(dy, ny) || !need(yg, ng) || !need(dest, S) || !need(src, rows) || !need(w, S) || !need(dyg, ng) ||
+      !need(dw, S))
+    return FP8MOE_ERR_NULL;
+  if (cols % 8 || !aligned(dy, 16) || !aligned(yg, 16) || !aligned(dyg, 16) || !aligned(q, 16) ||
+      !aligned(dest, 4) || !aligned(src, 4) || !aligned(w, 4) || !aligned(scale, 4) || !aligned(dw, 4))
+    return FP8MOE_ERR_ALIGN;
   return FP8MOE_OK;
 }
 

@@ -63,5 +63,15 @@ int check_moe_permute_quantized(const void* q, const float* scale, int64_t token
                                 const float* scale_g);
 int check_moe_combine(const void* yg, int64_t rows_in, const int32_t* dest, const float* w, int64_t tokens,
                       int32_t topk, int64_t cols, const void* y);
+// Rowwise quantization holds rows of up to this many columns in registers (256 threads x 8 chunks of 8);
+// longer gathered rows are cast from the gathered bf16 copy, which must then be written.
+constexpr int64_t kRowwiseRegCols = 16384;
+int check_moe_permute_rowwise(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                              int64_t rows_out, int codec, const void* xg, const void* qg, const float* scale_g);
+// Combine's backward holds a token's gradient row in registers: at most this many columns.
+constexpr int64_t kCombineBwdMaxCols = 16384;
+int check_moe_combine_backward(const void* dy, const void* yg, int64_t rows, const int32_t* dest,
+                               const int32_t* src, const float* w, int64_t tokens, int32_t topk, int64_t cols,
+                               int codec, const void* dyg, const void* q, const float* scale, const float* dw);
 
 }  // namespace fp8moe

@@ -11,7 +11,8 @@ Recipe
 * Outliers: after the normals, ``mask = random(shape) < frac`` and masked values
   are multiplied by ``factor``.
 * fp32 -> bf16 by round-to-nearest-even on the bit pattern (inputs are finite).
-* Tensor seed = 100*cfg + t with t in {0: X, 1: W1/W, 2: W2, 3: dY, 4: A2, 5: dH1};
+* Tensor seed = 100*cfg + t with t in {0: X, 1: W1/W, 2: W2, 3: dY, 4: A2, 5: dH1,
+  6: token rows X of the full MoE layer, 7: its output gradient dY, 8: router logits};
   3D weights draw each expert from seed 1000*(100*cfg + t) + e so they can be
   generated one expert at a time.
 * Rows are generated already grouped by expert; ``offs`` is the inclusive
@@ -27,7 +28,7 @@ from __future__ import annotations
 import dataclasses
 import numpy as np
 
-T_X, T_W1, T_W2, T_DY, T_A2, T_DH1 = 0, 1, 2, 3, 4, 5
+T_X, T_W1, T_W2, T_DY, T_A2, T_DH1, T_XT, T_DYT, T_RW = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -97,9 +98,9 @@ def routing_counts(cfg: int) -> np.ndarray:
 
 def routing_ids(cfg: int):
     """Per-token expert ids [tokens, topk] (int32) whose per-expert counts are
-    routing_counts(cfg): config 3 keeps its Gumbel top-6 draw; config 4 places
-    its multinomial counts on 8192 tokens with one expert each, in a seeded
-    random token order."""
+    routing_counts(cfg): config 3 keeps its Gumbel top-6 draw; configs 4 and 5
+    place their multinomial counts on 8192 (16384) tokens with one expert each,
+    in a seeded random token order."""
     if cfg == 3:
         rng = np.random.Generator(np.random.PCG64(cfg))
         rank = rng.permutation(64) + 1
@@ -107,12 +108,32 @@ def routing_ids(cfg: int):
         p /= p.sum()
         g = rng.gumbel(size=(8192, 64))
         return np.argsort(-(np.log(p)[None, :] + g), axis=1)[:, :6].astype(np.int32)
-    if cfg == 4:
-        counts = routing_counts(4)
-        ids = np.repeat(np.arange(32, dtype=np.int32), counts)
+    if cfg in (4, 5):
+        counts = routing_counts(cfg)
+        ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
         rng = np.random.Generator(np.random.PCG64(10_000 + cfg))
         return rng.permutation(ids).reshape(-1, 1).astype(np.int32)
-    raise ValueError(f"per-token routing is generated for configs 3 and 4, not {cfg}")
+    raise ValueError(f"per-token routing is generated for configs 3, 4 and 5, not {cfg}")
+
+
+def tokens_topk(cfg: int):
+    """(tokens, experts per token) of the MoE workloads' routing."""
+    return {3: (8192, 6), 4: (8192, 1), 5: (16384, 1)}[cfg]
+
+
+def router_weights(cfg: int) -> np.ndarray:
+    """Router weights [tokens, topk] (fp32) of a token's chosen experts, from N(0, 1) logits (seed
+    100*cfg + 8): a softmax over the chosen experts' logits when topk > 1, the sigmoid of the
+    logit with one expert per token (fp64 arithmetic, rounded once to fp32)."""
+    T, k = tokens_topk(cfg)
+    rng = np.random.Generator(np.random.PCG64(tensor_seed(cfg, T_RW)))
+    z = rng.standard_normal((T, k))
+    if k == 1:
+        p = 1.0 / (1.0 + np.exp(-z))
+    else:
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+    return p.astype(np.float32)
 
 
 def offsets_from_counts(counts) -> np.ndarray:
@@ -186,6 +207,18 @@ def make_dy(w: Workload) -> np.ndarray:
 
 def make_dh1(w: Workload) -> np.ndarray:
     return normal_bf16(tensor_seed(w.cfg, T_DH1), (w.M, w.F2), 1e-3)
+
+
+def make_tokens(w: Workload) -> np.ndarray:
+    """Token rows entering the full MoE layer: [tokens, H], the activation recipe of X."""
+    T, _ = tokens_topk(w.cfg)
+    return normal_bf16(tensor_seed(w.cfg, T_XT), (T, w.H), 1.0, *w.x_outliers)
+
+
+def make_dy_tokens(w: Workload) -> np.ndarray:
+    """Gradient of the full MoE layer's output: [tokens, H], N(0, 1e-3)."""
+    T, _ = tokens_topk(w.cfg)
+    return normal_bf16(tensor_seed(w.cfg, T_DYT), (T, w.H), 1e-3)
 
 
 def make_w1(w: Workload) -> np.ndarray:

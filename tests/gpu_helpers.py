@@ -64,3 +64,31 @@ def e8m0_rows_to_k4(sc: np.ndarray) -> np.ndarray:
     padded = np.zeros((R, 4 * G), np.uint8)
     padded[:, :NB] = sc
     return np.ascontiguousarray(padded.reshape(R, G, 4).transpose(1, 0, 2))
+
+
+def ulp_key(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> integers ordered like the values (both zeros -> 0)."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def assert_within_one_ulp(got: np.ndarray, ref: np.ndarray, what: str) -> None:
+    """bf16 results of an fp32 evaluation with its own exponential against the exact values rounded
+    once: at most one bf16 ulp apart, on at most a fraction 2^-11 of the elements (at least one
+    allowed).  The fraction: the fp32 evaluation (exponential, add, divide and up to six products
+    and sums) stays within a relative error eps = 2^-20 of the exact value; an element flips only if
+    its exact value v lies within eps*v of a bf16 rounding midpoint, and with the bf16 spacing
+    h > v*2^-8 that happens for a fraction at most 2*eps*v/h < 2^-11 of values spread over the
+    spacing."""
+    import math
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    d = np.abs(ulp_key(got) - ulp_key(ref))
+    if d.size:
+        i = np.unravel_index(np.argmax(d), d.shape)
+        assert d.max() <= 1, f"{what}: {int((d > 1).sum())} elements beyond 1 bf16 ulp; worst at {i}: " \
+                             f"got {got[i]:#06x} ref {ref[i]:#06x}"
+        note(f"{what}: {int((d > 0).sum())} of {d.size} elements one bf16 ulp off ({(d > 0).mean():.3e})")
+        allowed = math.ceil(d.size * 2.0 ** -11)
+        assert int((d > 0).sum()) <= allowed, \
+            f"{what}: {int((d > 0).sum())} elements off by one ulp, more than {allowed} ({d.size} * 2^-11)"

@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 9):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 103
+    assert lib.fp8moe_version() == 104
 
 
 def test_rows_bound(lib):
@@ -216,12 +216,48 @@ def test_route_rejections(lib):
     assert c(P, 8, P, P, 4, 0, 16, P, None) == L.ERR_SHAPE
     assert c(None, 8, P, P, 4, 2, 16, P, None) == L.ERR_NULL
     assert c(P, 8, None, P, 4, 2, 16, P, None) == L.ERR_NULL
-    assert c(P, 8, P, None, 4, 2, 16, P, None) == L.ERR_NULL
+    # weights may be null (every weight 1): that call passes validation, so it is not made here
     assert c(P, 8, P, P, 4, 2, 16, None, None) == L.ERR_NULL
     assert c(P, 8, P, P, 4, 2, 12, P, None) == L.ERR_ALIGN
     assert c(MIS, 8, P, P, 4, 2, 16, P, None) == L.ERR_ALIGN
     assert c(P, 8, P, P + 2, 4, 2, 16, P, None) == L.ERR_ALIGN
     assert c(None, 0, None, None, 0, 2, 16, None, None) == L.OK    # nothing to do
+    pr = lib.moe_permute_rowwise   # (x, tokens, cols, topk, src, rows_out, codec, xg, qg, scale_g, stream)
+    assert pr(P, 4, 16, 2, P, 8, 7, P, P, P, None) == L.ERR_ENUM
+    assert pr(P, -1, 16, 2, P, 8, 0, P, P, P, None) == L.ERR_SHAPE
+    assert pr(P, 4, 16, 0, P, 8, 0, P, P, P, None) == L.ERR_SHAPE
+    assert pr(P, 4, 16, 2, P, -1, 0, P, P, P, None) == L.ERR_SHAPE
+    assert pr(None, 4, 16, 2, P, 8, 0, P, P, P, None) == L.ERR_NULL
+    assert pr(P, 4, 16, 2, None, 8, 0, P, P, P, None) == L.ERR_NULL
+    assert pr(P, 4, 16, 2, P, 8, 0, P, None, P, None) == L.ERR_NULL
+    assert pr(P, 4, 16, 2, P, 8, 0, P, P, None, None) == L.ERR_NULL
+    assert pr(P, 4, 16392, 2, P, 8, 0, None, P, P, None) == L.ERR_NULL   # long rows need the bf16 copy
+    assert pr(P, 4, 12, 2, P, 8, 0, P, P, P, None) == L.ERR_ALIGN        # cols % 8
+    assert pr(MIS, 4, 16, 2, P, 8, 0, P, P, P, None) == L.ERR_ALIGN
+    assert pr(P, 4, 16, 2, P, 8, 0, MIS, P, P, None) == L.ERR_ALIGN
+    assert pr(P, 4, 16, 2, P, 8, 0, P, MIS, P, None) == L.ERR_ALIGN
+    assert pr(P, 4, 16, 2, P, 8, 0, P, P, P + 2, None) == L.ERR_ALIGN
+    assert pr(None, 0, 16, 2, None, 0, 0, None, None, None, None) == L.OK   # nothing to do
+    cb = lib.moe_combine_backward
+    # (dy, yg, rows, dest, src, weights, tokens, topk, cols, codec, dyg, q, scale, dweights, stream)
+    assert cb(P, P, 8, P, P, P, 4, 2, 16, 7, P, P, P, P, None) == L.ERR_ENUM
+    assert cb(P, P, 8, P, P, P, -1, 2, 16, 0, P, P, P, P, None) == L.ERR_SHAPE
+    assert cb(P, P, -1, P, P, P, 4, 2, 16, 0, P, P, P, P, None) == L.ERR_SHAPE
+    assert cb(P, P, 8, P, P, P, 4, 0, 16, 0, P, P, P, P, None) == L.ERR_SHAPE
+    assert cb(P, P, 8, P, P, P, 4, 2, 16392, 0, P, P, P, P, None) == L.ERR_UNSUPPORTED
+    assert cb(P, P, 8, P, P, P, 4, 2, 16, 0, P, None, P, P, None) == L.ERR_NULL   # codes without scales
+    assert cb(P, P, 8, P, P, P, 4, 2, 16, 0, P, P, None, P, None) == L.ERR_NULL
+    for i in (0, 1, 3, 4, 5, 10, 13):
+        args = [P, P, 8, P, P, P, 4, 2, 16, 0, P, P, P, P, None]
+        args[i] = None
+        assert cb(*args) == L.ERR_NULL, i
+    assert cb(P, P, 8, P, P, P, 4, 2, 12, 0, P, P, P, P, None) == L.ERR_ALIGN    # cols % 8
+    for i, bad in ((0, MIS), (1, MIS), (10, MIS), (11, MIS), (3, P + 2), (4, P + 2), (5, P + 2), (12, P + 2),
+                   (13, P + 2)):
+        args = [P, P, 8, P, P, P, 4, 2, 16, 0, P, P, P, P, None]
+        args[i] = bad
+        assert cb(*args) == L.ERR_ALIGN, i
+    assert cb(None, None, 0, None, None, None, 0, 2, 16, 0, None, None, None, None, None) == L.OK
 
 
 def test_colwise_rejections(lib):

@@ -1,17 +1,26 @@
-"""GPU parity of the timed layer step: every launch of the step bench.py times, on all five workloads.
+"""GPU parity of the timed layer step: every launch of the step bench.py times, on all five workloads,
+and for the MoE workloads both the whole MoE layer (route, gather, W1, SwiGLU, W2, combine and the
+mirror backward) and the expert GEMMs alone.
 
 The step is built by bench.build_step itself (no copy of its wiring), run twice on the GPU, and each
-launch's outputs are checked against the oracle:
+launch's outputs are checked against the oracle, with the launch's own device inputs (for the MoE
+layer's intermediate tensors, the previous launches' outputs):
   * quantization: codes and scales bit-exact on 1/8 of the rows (rowwise, MX last-dim blocks) or of
     the columns (colwise, MX row blocks), strided so every tile and every column strip is hit, plus
     the padded offsets of the grouped MX calls;
   * grouped GEMMs at their real N and K, on the GPU's own (separately checked) operands: GROUPED_M on
     the first, last and random rows of every expert, GROUPED_K on sampled output rows of every expert
     (empty experts exact zeros).
+  * the MoE layer's routing bit-exact (and equal to the workload's routed counts); gathers, SwiGLU,
+    combines and their backward on sampled rows or tokens, as in their own tests;
+  * end to end, on sampled tokens: the layer's output, the tokens' input gradient and the router
+    weights' gradient against an fp64 layer with no quantization, within a relative error that
+    FP8 rounding explains, which a wrongly wired operand (another expert, another tensor) exceeds.
 This covers what no single-kernel test does: the padded row pitch of the grouped colwise outputs,
 the K4 e8m0 layout between quantizer and GEMM, the padded offsets the MX weight gradient runs on,
-and dgrad operands taken from the batched colwise quantizer.  [P1 Details, Level 2 result (the
-MoE layer is the measured unit); P4 "Три уровня оптимизации Triton-ядер".]
+dgrad operands taken from the batched colwise quantizer, and the MoE layer's dataflow.  [P1
+Details, Level 2 result (the MoE layer is the measured unit); P4 "Три уровня оптимизации
+Triton-ядер", "MoE".]
 """
 import concurrent.futures as cf
 import os
@@ -23,7 +32,8 @@ import torch
 
 import oracle
 import mxfp8_quantized_moe_amd as fm
-from gpu_helpers import note, host, bf16_bits_to_f64, assert_bytes_equal, assert_f32_bits_equal
+from oracle import route as o_route, swiglu as o_swiglu
+from gpu_helpers import note, host, bf16_bits_to_f64, assert_bytes_equal, assert_f32_bits_equal, assert_within_one_ulp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
@@ -43,21 +53,35 @@ LAUNCHES = {
         "mx dH1^T", "mx X^T"] + _FWD_BWD,
 }
 LAUNCHES[4] = LAUNCHES[3]
+LAYER = {
+    3: ["route", "permute+q X", "q_row W1", "gemm fwd W1", "swiglu+q", "q_row W2", "gemm fwd W2", "combine",
+        "combine bwd+q", "q_col W2", "gemm dgrad W2", "q_col dYg", "q_col A2", "gemm wgrad W2", "swiglu bwd+q",
+        "q_col W1", "gemm dgrad W1", "q_col dH1", "q_col Xg", "gemm wgrad W1", "combine dX"],
+    5: ["route", "permute X", "mx Xg", "mx W1", "gemm fwd W1", "swiglu", "mx A2", "mx W2", "gemm fwd W2", "combine",
+        "combine bwd", "mx dYg", "mx W2^T", "gemm dgrad W2", "mx dYg^T", "mx A2^T", "gemm wgrad W2", "swiglu bwd",
+        "mx dH1", "mx W1^T", "gemm dgrad W1", "mx dH1^T", "mx Xg^T", "gemm wgrad W1", "combine dX"],
+}
+LAYER[4] = LAYER[3]
+# (workload, variant): the experts-only steps of configs 3-5 and the whole MoE layer
+VARIANTS = {**{(c, "experts"): v for c, v in LAUNCHES.items()}, **{(c, "layer"): v for c, v in LAYER.items()}}
 SAMPLE = 8          # quantization: every 8th row or column
 POOL = 8            # host threads for the oracle (numpy releases the GIL on array work)
+_DEV_CACHE = {}     # host copies of the step's device tensors, per fixture
 
 
 @pytest.fixture(scope="module")
 def layer(request):
-    cfg = request.param
-    note(f"layer step cfg={cfg}: build")
-    step, hst = bench.build_step(cfg, gw=(cfg == 2), n_rotate=1, keep_host=True)
-    assert sorted(step.specs) == sorted(LAUNCHES[cfg]), sorted(step.specs)
+    cfg, variant = request.param
+    note(f"layer step cfg={cfg} {variant}: build")
+    step, hst = bench.build_step(cfg, gw=(cfg == 2), n_rotate=1, keep_host=True, experts_only=(variant == "experts"))
+    assert sorted(step.specs) == sorted(VARIANTS[(cfg, variant)]), sorted(step.specs)
     for i in range(2):
-        note(f"layer step cfg={cfg}: run {i}")
+        note(f"layer step cfg={cfg} {variant}: run {i}")
         step.run()
         torch.cuda.synchronize()
+    _DEV_CACHE.clear()
     yield cfg, step, hst
+    _DEV_CACHE.clear()
     del step
     torch.cuda.empty_cache()
 
@@ -65,6 +89,11 @@ def layer(request):
 # ------------------------------------------------------------------ helpers
 
 def _src(hst, name):
+    """A named host input, or a host copy of a device tensor the step computed."""
+    if not isinstance(name, str):
+        if id(name) not in _DEV_CACHE:
+            _DEV_CACHE[id(name)] = host(name)
+        return _DEV_CACHE[id(name)]
     return hst["W1"] if name == "W1" else hst[name]
 
 
@@ -267,16 +296,172 @@ def check_g_k_bf16(sp, hst, phase):
     _check_gemm(got[:, n_rows], ref, contract, tight, "bf16 weight gradient")
 
 
+# ------------------------------------------------------------------ MoE layer checks
+
+def check_route(sp, hst, phase):
+    ref = o_route.route(hst[sp["ids"]], sp["E"], sp["pad"])
+    for nm, g, r in zip(("counts", "offs", "dest", "src"), sp["out"], ref):
+        assert_bytes_equal(_src(hst, g), r, f"route {nm}")
+
+
+def _rows_sample(n, phase):
+    return _strided(n, phase)
+
+
+def check_permute(sp, hst, phase):
+    x, rsrc = _src(hst, sp["src"]), _src(hst, sp["rsrc"])
+    rows = _rows_sample(rsrc.size, phase)
+    assert_bytes_equal(_src(hst, sp["out"])[rows], o_route.permute(x, rsrc[rows], sp["topk"]), "gathered rows")
+
+
+def check_permute_rowwise(sp, hst, phase):
+    x, rsrc = _src(hst, sp["src"]), _src(hst, sp["rsrc"])
+    rows = _rows_sample(rsrc.size, phase)
+    xg = o_route.permute(x, rsrc[rows], sp["topk"])
+    assert_bytes_equal(_src(hst, sp["xg"])[rows], xg, "gathered rows")
+    q, s = oracle.quantize_rowwise(xg, 0)
+    assert_bytes_equal(_src(hst, sp["q"])[rows], q, "codes")
+    assert_f32_bits_equal(_src(hst, sp["s"])[rows], s, "scales")
+
+
+def check_swiglu(sp, hst, phase):
+    h1 = _src(hst, sp["h1"])
+    rows = _rows_sample(h1.shape[0], phase)
+    a2 = _src(hst, sp["a2"])[rows]
+    assert_within_one_ulp(a2, o_swiglu.swiglu_fwd(h1[rows], sp["F"]), "a2")
+    if sp["q"] is not None:
+        q, s = oracle.quantize_rowwise(a2, 0)
+        assert_bytes_equal(_src(hst, sp["q"])[rows], q, "a2 codes")
+        assert_f32_bits_equal(_src(hst, sp["s"])[rows], s, "a2 scales")
+
+
+def check_swiglu_bwd(sp, hst, phase):
+    h1, da2 = _src(hst, sp["h1"]), _src(hst, sp["da2"])
+    rows = _rows_sample(h1.shape[0], phase)
+    dh1 = _src(hst, sp["dh1"])[rows]
+    assert_within_one_ulp(dh1, o_swiglu.swiglu_bwd(da2[rows], h1[rows], sp["F"]), "dh1")
+    if sp["q"] is not None:
+        q, s = oracle.quantize_rowwise(dh1, 0)
+        assert_bytes_equal(_src(hst, sp["q"])[rows], q, "dh1 codes")
+        assert_f32_bits_equal(_src(hst, sp["s"])[rows], s, "dh1 scales")
+
+
+def _token_sample(T, phase):
+    return np.unique(np.concatenate([[0, T - 1], np.random.default_rng(400 + phase).choice(T, 255, replace=False)]))
+
+
+def _sub_routing(dest, toks, k):
+    """The grouped rows the sampled tokens use, renumbered: (rows to take, dest of the sub-problem)."""
+    d = dest.reshape(-1, k)[toks].ravel()
+    return np.clip(d, 0, None), np.where(d >= 0, np.arange(d.size), -1).astype(np.int32)
+
+
+def check_combine(sp, hst, phase):
+    yg, dest, k = _src(hst, sp["yg"]), _src(hst, sp["dest"]), sp["topk"]
+    T = dest.size // k
+    toks = _token_sample(T, phase)
+    take, d_sub = _sub_routing(dest, toks, k)
+    wts = None if sp["w"] is None else hst[sp["w"]][toks]
+    assert_bytes_equal(_src(hst, sp["out"])[toks], o_route.combine(yg[take], d_sub, wts, len(toks), k), "combined")
+
+
+def check_combine_bwd(sp, hst, phase):
+    yg, dest, rsrc, k = _src(hst, sp["yg"]), _src(hst, sp["dest"]), _src(hst, sp["src"]), sp["topk"]
+    dy, wts = hst[sp["dy"]], hst[sp["w"]]
+    T = dest.size // k
+    toks = _token_sample(T, phase)
+    take, d_sub = _sub_routing(dest, toks, k)
+    s_sub = np.arange(d_sub.size, dtype=np.int32)
+    dyg_ref, dw_ref = o_route.combine_backward(dy[toks], yg[take], s_sub, d_sub, wts[toks], len(toks), k)
+    dyg = _src(hst, sp["dyg"])
+    assert_bytes_equal(dyg[take], dyg_ref, "routed-row gradients")
+    if sp["q"] is not None:
+        q, s = oracle.quantize_rowwise(dyg_ref, 0)
+        assert_bytes_equal(_src(hst, sp["q"])[take], q, "codes")
+        assert_f32_bits_equal(_src(hst, sp["s"])[take], s, "scales")
+    slots = (toks[:, None] * k + np.arange(k)[None, :]).ravel()
+    dw = _src(hst, sp["dw"])[slots].astype(np.float64)
+    mag = np.einsum("sc,sc->s", np.abs(bf16_bits_to_f64(dy[toks]).repeat(k, axis=0)),
+                    np.abs(bf16_bits_to_f64(yg[take])))
+    assert np.all(np.abs(dw - dw_ref) <= dy.shape[1] * 2.0 ** -24 * mag), "router-weight gradients"
+    pad = rsrc < 0                                      # rows holding no slot are zeros
+    assert not dyg[pad].any()
+
+
 CHECKS = {"q_row": check_q_row, "q_col_grouped": check_q_col_grouped, "q_col_batched": check_q_col_batched,
           "mx_last": check_mx_last, "mx_rows_b": check_mx_rows_b, "mx_rows_g": check_mx_rows_g,
-          "g_m": check_g_m, "g_k": check_g_k, "g_k_bf16": check_g_k_bf16}
+          "g_m": check_g_m, "g_k": check_g_k, "g_k_bf16": check_g_k_bf16,
+          "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
+          "swiglu": check_swiglu, "swiglu_bwd": check_swiglu_bwd, "combine": check_combine,
+          "combine_bwd": check_combine_bwd}
 
 
-@pytest.mark.parametrize("layer,launch", [(c, n) for c in sorted(LAUNCHES) for n in LAUNCHES[c]],
-                         indirect=["layer"], scope="module", ids=[f"cfg{c}-{n.replace(' ', '_')}" for c in sorted(LAUNCHES)
-                                                  for n in LAUNCHES[c]])
+_CASES = [(v, n) for v in sorted(VARIANTS) for n in VARIANTS[v]]
+
+
+@pytest.mark.parametrize("layer,launch", _CASES, indirect=["layer"], scope="module",
+                         ids=[f"cfg{c}-{v}-{n.replace(' ', '_')}" for (c, v), n in _CASES])
 def test_layer_launch(layer, launch):
     cfg, step, hst = layer
     sp = step.specs[launch]
     note(f"layer step cfg={cfg}: check {launch} ({sp['op']})")
     CHECKS[sp["op"]](sp, hst, phase=cfg + len(launch))
+
+
+def _swiglu64(h, F):
+    g, u = h[:, :F], h[:, F:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+@pytest.mark.parametrize("layer", [(c, "layer") for c in sorted(LAYER)], indirect=True, scope="module",
+                         ids=[f"cfg{c}-layer" for c in sorted(LAYER)])
+def test_layer_end_to_end(layer):
+    """The MoE layer's output y, the tokens' input gradient dx and the router weights' gradient dw on
+    8 sampled tokens, against an fp64 layer with no quantization computed here from the host inputs:
+    y[t] = sum_j w[t,j] W2[e_j] swiglu(W1[e_j] x[t]), and its gradients for the loss <dy, y>.  FP8
+    keeps 3 significand bits: a quantized operand's elements carry a relative rounding error of at
+    most 2^-4 (about 0.036 root mean square), and a pass chains four quantized operands (x, W1, a2,
+    W2 forward), so the layer's relative error is about 2 x 0.036, 0.07; measured worst cases over
+    the sampled tokens are 0.07-0.11.  Bound 0.25.  A router-weight gradient is one dot product
+    <dy, y_e> whose exact value may sit near zero, so its error is taken against the size such a
+    product has, |dy| |y_e| / sqrt(H) (measured worst 0.13-0.17), bound 0.4.  Another expert's
+    weights, an unweighted combine or a transposed operand give errors of order 1 (another
+    expert: about sqrt(2))."""
+    cfg, step, hst = layer
+    k = hst["IDS"].shape[1]
+    X, DY, RW, IDS = hst["X"], hst["DY"], hst["RW"], hst["IDS"]
+    W1, W2 = hst["W1"], hst["W2"]
+    F2, H = W1.shape[1], W1.shape[2]
+    F = F2 // 2
+    out = step.outputs
+    y, dx, dw = host(out["y"]), host(out["dx"]), host(out["dw"])
+    toks = np.random.default_rng(cfg).choice(X.shape[0], 8, replace=False)
+    errs = {"y": [], "dx": [], "dw": []}
+    for t in toks:
+        x = bf16_bits_to_f64(X[t])
+        dyt = bf16_bits_to_f64(DY[t])
+        y_ref = np.zeros(H)
+        dx_ref = np.zeros(H)
+        dw_ref = np.zeros(k)
+        dw_scale = np.zeros(k)
+        for j in range(k):
+            e = int(IDS[t, j])
+            w1, w2 = bf16_bits_to_f64(W1[e]), bf16_bits_to_f64(W2[e])
+            h1 = w1 @ x                                   # [2F]
+            g, u = h1[:F], h1[F:]
+            sg = 1.0 / (1.0 + np.exp(-g))
+            a2 = g * sg * u
+            ye = w2 @ a2                                  # [H]
+            y_ref += float(RW[t, j]) * ye
+            dw_ref[j] = dyt @ ye
+            dw_scale[j] = np.linalg.norm(dyt) * np.linalg.norm(ye) / np.sqrt(H)
+            da2 = (float(RW[t, j]) * dyt) @ w2            # [F]
+            dh1 = np.concatenate([da2 * u * sg * (1.0 + g * (1.0 - sg)), da2 * g * sg])
+            dx_ref += dh1 @ w1
+        rel = lambda got, ref: float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+        errs["y"].append(rel(bf16_bits_to_f64(y[t]), y_ref))
+        errs["dx"].append(rel(bf16_bits_to_f64(dx[t]), dx_ref))
+        errs["dw"].append(float(np.max(np.abs(dw[t * k:(t + 1) * k].astype(np.float64) - dw_ref) / dw_scale)))
+    note(f"end to end cfg={cfg}: worst relative error " + ", ".join(f"{n} {max(v):.3e}" for n, v in errs.items()))
+    for n, bound in (("y", 0.25), ("dx", 0.25), ("dw", 0.4)):
+        assert max(errs[n]) < bound, f"{n}: relative error {max(errs[n]):.3e} on a sampled token"

@@ -1,8 +1,11 @@
-"""GPU parity of the routing kernels (moe_route, moe_permute, moe_combine)
-against the oracle (oracle/route.py).
+"""GPU parity of the routing kernels (moe_route, moe_permute, moe_permute_rowwise,
+moe_combine, moe_combine_backward) against the oracle (oracle/route.py).
 
 Everything here is integer or byte work, or an fp32 sum in a fixed order of
-round-to-nearest operations: all outputs must match the oracle bit for bit."""
+round-to-nearest operations: all outputs must match the oracle bit for bit.
+The one exception is the router-weight gradient of moe_combine_backward, an
+fp32 dot product in the kernel's own order, accepted within fp32 summation
+error of the exact sum."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +14,8 @@ import mxfp8_quantized_moe_amd as fm
 from mxfp8_quantized_moe_amd import synth
 from oracle import route as rt
 from oracle.swiglu import round_bf16
-from gpu_helpers import DEV, note, bf16_dev, i32_dev, host, assert_bytes_equal
+from gpu_helpers import (DEV, note, bf16_dev, i32_dev, host, assert_bytes_equal, assert_f32_bits_equal,
+                         filled_u8, filled_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +187,106 @@ def test_permute_quantized(codec, shape):
     assert_bytes_equal(host(sg).view(np.uint32), host(s2).view(np.uint32), "scale_g vs quantize after permute")
     q_or, s_or = oracle.quantize_rowwise(x, codec)
     assert_bytes_equal(host(q), q_or, "token codes")
+
+
+@pytest.mark.parametrize("codec", [fm.E4M3FN, fm.E4M3FNUZ])
+@pytest.mark.parametrize("shape,keep", [((9, 3, 5, 4, 32), True), ((1000, 6, 64, 32, 2048), True),
+                                        ((300, 1, 16, 128, 7168), False), ((40, 2, 3, 8, 16392), True),
+                                        ((77, 2, 4, 1, 136), False), ((0, 2, 4, 16, 64), True)])
+def test_permute_rowwise(codec, shape, keep):
+    """Fused gather + rowwise quantization: the gathered rows bit-exact against the oracle's permute, the
+    codes and scales against the oracle's rowwise quantizer of those rows (padding rows: zero codes and the
+    all-zero row's scale); rows of 16392 columns take the streaming cast."""
+    import oracle
+    T, k, E, pad, C = shape
+    rng = np.random.default_rng(T + C + codec + 11)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 10:
+        ids[rng.random((T, k)) < 0.02] = -1
+    x = bf16_random(rng, (T, C), 2.0)
+    if T > 5:
+        x[4] = 0                                                    # an all-zero token
+    counts, offs, dest, src = fm.moe_route(i32_dev(ids), E, pad)
+    R = src.numel()
+    xg0 = torch.full((R, C), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16) if keep else None
+    note(f"moe_permute_rowwise T={T} k={k} C={C} rows={R} codec={codec} keep={keep}")
+    xg, qg, sg = fm.moe_permute_rowwise(bf16_dev(x), src, k, codec, xg=xg0, keep_bf16=keep,
+                                        qg=filled_u8((R, C)), scale_g=filled_f32((R,)))
+    xg_ref = rt.permute(x, host(src), k)
+    if keep:
+        assert_bytes_equal(host(xg), xg_ref, "xg")
+    else:
+        assert xg is None
+    q_ref, s_ref = oracle.quantize_rowwise(xg_ref, codec)
+    assert_bytes_equal(host(qg), q_ref, "qg")
+    assert_f32_bits_equal(host(sg), s_ref, "scale_g")
+
+
+def check_combine_backward(ids, E, pad, C, codec, codes, seed, what):
+    import oracle
+    T, k = ids.shape
+    rng = np.random.default_rng(seed)
+    (counts, offs, dest, src), (_, _, dref, sref) = check_route(ids, E, pad, what)
+    R = src.numel()
+    dy = bf16_random(rng, (T, C), 1e-3)
+    yg = bf16_random(rng, (R, C), 2.0)
+    w = (rng.random((T, k)) + 0.05).astype(np.float32)
+    note(f"moe_combine_backward {what}: T={T} k={k} C={C} rows={R} codec={codec} codes={codes}")
+    dyg, q, s, dw = fm.moe_combine_backward(
+        bf16_dev(dy), bf16_dev(yg), dest, src, torch.from_numpy(w).to(DEV), k, codec, codes=codes,
+        dyg=torch.full((R, C), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16),
+        q=filled_u8((R, C)) if codes else None, scale=filled_f32((R,)) if codes else None,
+        dweights=filled_f32((T * k,)))
+    dyg_ref, dw_ref = rt.combine_backward(dy, yg, sref, dref, w, T, k)
+    assert_bytes_equal(host(dyg), dyg_ref, f"{what} dyg")
+    if codes:
+        q_ref, s_ref = oracle.quantize_rowwise(dyg_ref, codec)
+        assert_bytes_equal(host(q), q_ref, f"{what} codes")
+        assert_f32_bits_equal(host(s), s_ref, f"{what} scales")
+    else:
+        assert q is None and s is None
+    # dw: exact bf16 products, fp32 sums in the kernel's order: within C * 2^-24 * sum |products|
+    dyf = oracle.bf16_to_f32(dy).astype(np.float64)
+    ygf = oracle.bf16_to_f32(yg).astype(np.float64)
+    ok = dref >= 0
+    mag = np.zeros(T * k)
+    mag[ok] = np.einsum("sc,sc->s", np.abs(dyf[np.nonzero(ok)[0] // k]), np.abs(ygf[dref[ok]]))
+    err = np.abs(host(dw).astype(np.float64) - dw_ref)
+    bound = C * 2.0 ** -24 * mag
+    assert np.all(err <= bound), f"{what} dw: worst excess {np.max(err - bound):.3e}"
+    assert np.all(host(dw)[~ok] == 0.0), f"{what}: dropped slots must get dw = 0"
+
+
+@pytest.mark.parametrize("codec", [fm.E4M3FN, fm.E4M3FNUZ])
+@pytest.mark.parametrize("shape", [(7, 3, 5, 4, 8), (1000, 6, 64, 32, 2048), (300, 1, 16, 1, 7168),
+                                   (129, 8, 256, 16, 24), (50, 2, 3, 8, 16384), (0, 2, 4, 16, 64)])
+def test_combine_backward(codec, shape):
+    """Routed-row gradients bit-exact (and their rowwise codes), router-weight gradients within fp32 summation
+    error, padding rows zero, dropped slots zero."""
+    T, k, E, pad, C = shape
+    rng = np.random.default_rng(T + C + 3)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 10:
+        ids[rng.random((T, k)) < 0.02] = -1
+    check_combine_backward(ids, E, pad, C, codec, True, T + 7, f"random{shape}")
+    if C <= 2048:
+        check_combine_backward(ids, E, pad, C, codec, False, T + 8, f"random{shape} no codes")
+
+
+@pytest.mark.parametrize("cfg,E,C", [(3, 64, 2048), (4, 32, 7168)])
+def test_combine_backward_workload(cfg, E, C):
+    """The DeepSeek-MoE-16B and DeepSeek-V3-share routings at their hidden sizes."""
+    check_combine_backward(synth.routing_ids(cfg), E, 1, C, fm.E4M3FN, True, cfg, f"workload{cfg}")
+
+
+def test_combine_without_weights():
+    """Null weights sum a token's routed rows (the backward's input gradient), as the oracle's unit weights."""
+    rng = np.random.default_rng(21)
+    T, k, E, C = 500, 6, 64, 2048
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[3, 2] = -1
+    (counts, offs, dest, src), (_, _, dref, sref) = check_route(ids, E, 1, "unit weights")
+    yg = bf16_random(rng, (src.numel(), C), 3.0)
+    note("moe_combine without weights")
+    y = fm.moe_combine(bf16_dev(yg), dest, None, k)
+    assert_bytes_equal(host(y), rt.combine(yg, dref, None, T, k), "y")
