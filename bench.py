@@ -225,6 +225,26 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                  spec=dict(op="mx_rows_g", src=src, offs=offs_np, rows_pad=Mp, rule=rule, q=q, s=s, offs_pad=op))
         return q, s
 
+    def mx_dual_b(name, src, x, B, R, C):
+        """Both MX forms of a batched tensor (weights) from one read."""
+        q, s = u8(B * R, C), u8(*fm.mx_k4_shape(B * R, C // 32))
+        qt, st = u8(B, C, R), u8(*fm.mx_k4_shape(B * C, R // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx_dual(x(), rule=rule, q=q, scale=s, q_t=qt, scale_t=st, layout=K4),
+                 4 * B * R * C + 2 * (B * R * C // 32),
+                 spec=dict(op="mx_dual", src=src, shape=(B, R, C), rule=rule, q=q, s=s, qt=qt, st=st))
+        return q, s, qt, st
+
+    def mx_dual_g(name, src, x, rows, cols):
+        """Both MX forms of a grouped tensor (activations) from one read; row blocks padded per group."""
+        q, s = u8(rows, cols), u8(*fm.mx_k4_shape(rows, cols // 32))
+        qt, st = u8(cols, Mp), u8(*fm.mx_k4_shape(cols, Mp // 32))
+        step.add(name, "quant", lambda: fm.quantize_mx_dual(x(), offs=offs, rule=rule, rows_pad=Mp, q=q, scale=s,
+                                                            q_t=qt, scale_t=st, offs_pad=op, layout=K4),
+                 4 * rows * cols + 2 * (rows * cols // 32),
+                 spec=dict(op="mx_dual", src=src, shape=(rows, cols), offs=offs_np, rows_pad=Mp, rule=rule, q=q, s=s,
+                           qt=qt, st=st, offs_pad=op))
+        return q, s, qt, st
+
     def moe_layer():
         """The MoE layer as one stream-ordered step with no host synchronisation [P1 Details, MoE
         paragraph; P4 "MoE"]: route the tokens' expert ids into offsets, gather the token rows into
@@ -264,8 +284,8 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
         if w.mx:
             step.add("permute X", "moe", lambda: fm.moe_permute(Xd(), r_src, k, xg=xg), 4 * rows * H + 4 * rows,
                      spec=dict(op="permute", src="X", topk=k, rsrc=r_src, out=xg))
-            qx, sx = mx_last("mx Xg", xg, lambda: xg, rows, H)
-            qw1, sw1 = mx_last("mx W1", "W1", W1d, E * F2, H)
+            qx, sx, qxt, sxt = mx_dual_g("mx Xg (both forms)", xg, lambda: xg, rows, H)
+            qw1, sw1, qw1t, sw1t = mx_dual_b("mx W1 (both forms)", "W1", W1d, E, F2, H)
             h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H, sk=fm.SCALE_E8M0_K4)
         else:
             qx, sx = u8(rows, H), f32(rows)
@@ -279,8 +299,8 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
         if w.mx:
             step.add("swiglu", "moe", lambda: fm.swiglu_quantize_rowwise(h1, 0, a2=a2, codes=False),
                      2 * rows * F2 + 2 * rows * F, spec=dict(op="swiglu", h1=h1, F=F, a2=a2, q=None, s=None))
-            qa2, sa2 = mx_last("mx A2", a2, lambda: a2, rows, F)
-            qw2, sw2 = mx_last("mx W2", "W2", W2d, E * H, F)
+            qa2, sa2, qa2t, sa2t = mx_dual_g("mx A2 (both forms)", a2, lambda: a2, rows, F)
+            qw2, sw2, qw2t, sw2t = mx_dual_b("mx W2 (both forms)", "W2", W2d, E, H, F)
             yg = g_m("gemm fwd W2", qa2, sa2, qw2, sw2, rows, H, F, sk=fm.SCALE_E8M0_K4)
         else:
             qa2, sa2 = u8(rows, F), f32(rows)
@@ -301,11 +321,8 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                      2 * T * H + 4 * rows * H + 16 * S,
                      spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=dyg,
                                q=None, s=None, dw=dw))
-            qdy, sdy = mx_last("mx dYg", dyg, lambda: dyg, rows, H)
-            qw2t, sw2t = mx_rows_b("mx W2^T", "W2", W2d, E, H, F)
+            qdy, sdy, qdyt, sdyt = mx_dual_g("mx dYg (both forms)", dyg, lambda: dyg, rows, H)
             da2 = g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, rows, F, H, sk=fm.SCALE_E8M0_K4)
-            qdyt, sdyt = mx_rows_g("mx dYg^T", dyg, lambda: dyg, rows, H)
-            qa2t, sa2t = mx_rows_g("mx A2^T", a2, lambda: a2, rows, F)
             g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0_K4, offs_t=op)
         else:
             qdy, sdy = u8(rows, H), f32(rows)
@@ -326,11 +343,8 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                      lambda: fm.swiglu_backward_quantize_rowwise(da2, h1, 0, dh1=dh1, codes=False),
                      2 * rows * F + 4 * rows * F2, spec=dict(op="swiglu_bwd", da2=da2, h1=h1, F=F, dh1=dh1, q=None,
                                                             s=None))
-            qdh, sdh = mx_last("mx dH1", dh1, lambda: dh1, rows, F2)
-            qw1t, sw1t = mx_rows_b("mx W1^T", "W1", W1d, E, F2, H)
+            qdh, sdh, qdht, sdht = mx_dual_g("mx dH1 (both forms)", dh1, lambda: dh1, rows, F2)
             dxg = g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, rows, H, F2, sk=fm.SCALE_E8M0_K4)
-            qdht, sdht = mx_rows_g("mx dH1^T", dh1, lambda: dh1, rows, F2)
-            qxt, sxt = mx_rows_g("mx Xg^T", xg, lambda: xg, rows, H)
             g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0_K4, offs_t=op)
         else:
             qdh, sdh = u8(rows, F2), f32(rows)
@@ -592,6 +606,26 @@ def cpu_baseline(step, host: dict):
                 f = lambda: oracle.mm_grouped_k_mx(np.ascontiguousarray(qa), sa, np.ascontiguousarray(qb), sb, one)
             full = 2.0 * float((hi - lo).sum()) * N * K
             add(name, timed(f), full / (2.0 * n * k * float(hi[e] - lo[e])))
+        elif op == "mx_dual":
+            x = src(sp["src"])
+            if "offs" in sp:
+                M, C = sp["shape"]
+                x = x.reshape(M, C)
+                r = max(1, min(M, QS // max(C, 1)))
+                c = max(8, min(C, QS // max(M, 1)) // 32 * 32)
+                xs = np.ascontiguousarray(x[:, :c])
+                # the two halves scale differently: rows sampled for one, columns for the other
+                t_l = timed(lambda: oracle.quantize_mx_lastdim(x[:r], sp["rule"]), 1) * (M / r)
+                t_r = timed(lambda: oracle.quantize_mx_rows_grouped(xs, sp["offs"], sp["rule"], sp["rows_pad"]), 1) * (C / c)
+            else:
+                B, R, C = sp["shape"]
+                x = x.reshape(B, R, C)
+                r = max(1, min(B * R, QS // max(C, 1)))
+                c = max(8, min(C, QS // max(B * R, 1)) // 8 * 8)
+                xs = np.ascontiguousarray(x[:, :, :c])
+                t_l = timed(lambda: oracle.quantize_mx_lastdim(x.reshape(B * R, C)[:r], sp["rule"]), 1) * (B * R / r)
+                t_r = timed(lambda: oracle.quantize_mx_rows_batched(xs, sp["rule"]), 1) * (C / c)
+            add(name, t_l + t_r, 1.0)
         elif op == "route":
             ids = host[sp["ids"]]
             add(name, timed(lambda: o_route.route(ids, sp["E"], sp["pad"]), 1), 1.0)

@@ -494,6 +494,32 @@ int quantize_mx(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols, i
                 void *q, void *scale_e8m0, int64_t rows_pad, int32_t *offs_pad_out,
                 void *stream);
 
+/*
+ * quantize_mx_dual -- both MXFP8 forms of one tensor from a single read: the
+ * last-dim blocks (a weight's forward operand, an activation gradient's dgrad
+ * operand) and the row blocks (the same weight's dgrad operand, the wgrad
+ * operands).  Every 1x32 block is local to its 32 elements, so one pass over a
+ * tile of x gives both; HBM sees x read once instead of twice.
+ *   [as quantize_mx; P2 Details (the forward and both backward GEMMs take
+ *   MXFP8 operands blocked along their own contraction dimension); P4 "Три
+ *   уровня оптимизации Triton-ядер" (fused scale-and-cast, no second read).]
+ *   q, scale_e8m0     the outputs of quantize_mx(x, batch, rows, cols, axis = 1)
+ *                     over x viewed as [batch*rows][cols] (written).  With offs,
+ *                     only the rows inside groups (rows < offs[n_groups-1]) are
+ *                     written; rows past the last group are left untouched.
+ *   q_t, scale_t_e8m0 the outputs of quantize_mx(x, ..., axis = 0, offs, n_groups,
+ *                     rows_pad, offs_pad_out) (written)
+ *   Every other argument and every requirement is that of the two quantize_mx
+ *   calls (cols % 32 == 0; without offs, rows % 32 == 0); scale_layout applies
+ *   to both scale matrices; q 16-byte aligned.  One kernel (128 x 128 work
+ *   items, so every row's last-dim codes leave in whole 128-byte lines), no
+ *   allocation.
+ */
+int quantize_mx_dual(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
+                     const int32_t *offs, int32_t n_groups, int rule, int scale_layout, void *q,
+                     void *scale_e8m0, void *q_t, void *scale_t_e8m0, int64_t rows_pad,
+                     int32_t *offs_pad_out, void *stream);
+
 /* Host-side allocation bound for quantize_mx's padded rows: round_up(rows + 31*n_groups, 32).
  * Returns -1 for negative arguments. */
 int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups);

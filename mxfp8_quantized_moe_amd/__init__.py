@@ -20,7 +20,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "grouped_mm_scaled", "encode_f32", "default_codec", "E4M3FN", "E4M3FNUZ", "MX_FLOOR_OCP",
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
-           "mx_k4_shape", "Fp8MoeError", "swiglu_quantize_rowwise",
+           "mx_k4_shape", "quantize_mx_dual", "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_route_workspace_bytes", "moe_permute", "moe_combine",
            "moe_permute_rowwise", "moe_combine_backward",
            "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise",
@@ -133,6 +133,39 @@ def quantize_mx(x, axis=1, offs=None, rule=MX_FLOOR_OCP, rows_pad=None, q=None, 
                                 _ptr(offs_pad), _stream(stream))
     _lib.check("quantize_mx", st)
     return q, scale, offs_pad
+
+
+def quantize_mx_dual(x, offs=None, rule=MX_FLOOR_OCP, rows_pad=None, q=None, scale=None, q_t=None, scale_t=None,
+                     offs_pad=None, layout=MX_LAYOUT_ROWS, stream=None):
+    """Both MXFP8 forms from one read: (q, scale) as quantize_mx(x viewed [B*R, C], axis=1) and
+    (q_t, scale_t, offs_pad) as quantize_mx(x, axis=0, offs).  x is [B, R, C] without offs, [M, C] with."""
+    x = _bits(x).contiguous()
+    dev = x.device
+    k4 = layout == MX_LAYOUT_K4
+
+    def sc_empty(rows_major_shape, n_rows, n_blocks):
+        shape = mx_k4_shape(n_rows, n_blocks) if k4 else rows_major_shape
+        return torch.empty(shape, dtype=torch.uint8, device=dev)
+
+    if offs is None:
+        B, R, C = x.shape
+        E, rp, offs_pad = 0, R, None
+        q_t = torch.empty((B, C, R), dtype=torch.uint8, device=dev) if q_t is None else q_t
+        scale_t = sc_empty((B, C, R // 32), B * C, R // 32) if scale_t is None else scale_t
+    else:
+        (M, C), B = x.shape, 1
+        R = M
+        E = offs.numel()
+        rp = rows_pad or quantize_mx_rows_bound(M, E)
+        q_t = torch.empty((C, rp), dtype=torch.uint8, device=dev) if q_t is None else q_t
+        scale_t = sc_empty((C, rp // 32), C, rp // 32) if scale_t is None else scale_t
+        offs_pad = torch.empty((E,), dtype=torch.int32, device=dev) if offs_pad is None else offs_pad
+    q = torch.empty((B * R, C), dtype=torch.uint8, device=dev) if q is None else q
+    scale = sc_empty((B * R, C // 32), B * R, C // 32) if scale is None else scale
+    st = _lib.lib().quantize_mx_dual(_ptr(x), B, R, C, _ptr(offs), E, rule, layout, _ptr(q), _ptr(scale), _ptr(q_t),
+                                     _ptr(scale_t), rp, _ptr(offs_pad), _stream(stream))
+    _lib.check("quantize_mx_dual", st)
+    return q, scale, q_t, scale_t, offs_pad
 
 
 def grouped_mm_scaled(mode, a, a_fmt, a_scale, b, b_fmt, b_scale, scale_kind, offs, n_groups, M, N, K,

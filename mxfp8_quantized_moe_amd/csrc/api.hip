@@ -221,6 +221,19 @@ int quantize_mx(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, i
                                           as_stream(stream)));
 }
 
+int quantize_mx_dual(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+                     int32_t n_groups, int rule, int scale_layout, void* q, void* scale_e8m0, void* q_t,
+                     void* scale_t_e8m0, int64_t rows_pad, int32_t* offs_pad_out, void* stream) {
+  const int st = check_quantize_mx_dual(x_bf16, batch, rows, cols, offs, n_groups, rule, scale_layout, q, scale_e8m0,
+                                        q_t, scale_t_e8m0, rows_pad, offs_pad_out);
+  if (st) return st;
+  return launch_status(launch_quantize_mx_dual(static_cast<const uint16_t*>(x_bf16), batch, rows, cols, offs,
+                                               n_groups, rule, scale_layout, static_cast<uint8_t*>(q),
+                                               static_cast<uint8_t*>(scale_e8m0), static_cast<uint8_t*>(q_t),
+                                               static_cast<uint8_t*>(scale_t_e8m0), rows_pad, offs_pad_out,
+                                               as_stream(stream)));
+}
+
 int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups) { return mx_rows_bound(rows, n_groups); }
 
 int grouped_mm_scaled(int mode, const void* a, int a_fmt, const void* a_scale, const void* b, int b_fmt,
@@ -265,6 +278,6 @@ int fp8moe_default_codec(int hip_device, int* codec_out) {
 
 int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(polls); }
 
-int fp8moe_version(void) { return 104; }
+int fp8moe_version(void) { return 105; }
 
 }  // extern "C"

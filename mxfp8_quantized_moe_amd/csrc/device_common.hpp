@@ -197,6 +197,43 @@ __device__ __forceinline__ int mx_exponent_bf16(uint32_t a16, int rule) {
 // 2^-X for X in [-127, 119] (a normal fp32, no branch).
 __device__ __forceinline__ float exp2_neg_bf16(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
 
+// ------------------------------------------------------------------ MX cast on the scaled converter
+//
+// gfx950's v_cvt_scalef32_pk_fp8_bf16 converts two bf16 values to e4m3fn after
+// dividing them by 2^(e - 127), where e is the exponent field of its fp32
+// scale operand (the significand is ignored; e = 0 means 2^-127): given the
+// block's e8m0 code E = X + 127 in that field, it computes enc(x * 2^-X) with
+// round-to-nearest-even, the sign of a zero result kept.  The product is exact
+// (a power-of-two scaling of a bf16 value, except where it falls below 2^-126,
+// far under the smallest e4m3 step), so this equals the clamp-then-encode of
+// the software path for every |x * 2^-X| <= 448.  Above, the converter returns
+// 448 up to the rounding boundary 464 and the NaN code (0x7F, 0xFF) beyond;
+// e4m3fn has no other NaN or infinity, so replacing a NaN code by the largest
+// code of its sign (0x7E, 0xFE) gives the clamped result there too.  Checked
+// on every bf16 value under scales 2^-127 .. 2^127, and the MX kernels that use
+// it are checked bit for bit against the oracle.
+typedef short mx_v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_v2bf16 __attribute__((ext_vector_type(2)));
+
+// The scale operand carrying e8m0 code E (0..254).
+__device__ __forceinline__ float mx_scale_operand(int E) { return __uint_as_float((uint32_t)E << 23); }
+
+// Four codes (little-endian) of the bf16 pairs p0 = (x0, x1), p1 = (x2, x3) under one scale operand,
+// NaN codes replaced by +-448 (needed only when a value can exceed 448: the FLOOR rule).
+template <bool SAT>
+__device__ __forceinline__ uint32_t mx_cvt4(uint32_t p0, uint32_t p1, float sc) {
+  mx_v2i16 o = {0, 0};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, __builtin_bit_cast(mx_v2bf16, p0), sc, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, __builtin_bit_cast(mx_v2bf16, p1), sc, true);
+  uint32_t w = __builtin_bit_cast(uint32_t, o);
+  if constexpr (SAT) {
+    // a byte whose low 7 bits are all set (the NaN codes) gets its lowest bit cleared
+    const uint32_t u = (w & 0x7F7F7F7Fu) + 0x01010101u;
+    w ^= (u >> 7) & 0x01010101u;
+  }
+  return w;
+}
+
 // 2^-X as an fp32 for X in [-127, 127] (X = 127 gives the subnormal 2^-127 = 0x00400000).
 __device__ __forceinline__ float exp2_neg(int X) {
   const int be = 127 - X;  // biased exponent of 2^-X, in [0, 254]

@@ -24,6 +24,11 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, in
                               const int32_t* offs, int32_t n_groups, int rule, int scale_layout, uint8_t* q,
                               uint8_t* sc, int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st);
 
+hipError_t launch_quantize_mx_dual(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                   const int32_t* offs, int32_t n_groups, int rule, int scale_layout, uint8_t* q,
+                                   uint8_t* sc, uint8_t* q_t, uint8_t* sc_t, int64_t rows_pad,
+                                   int32_t* offs_pad_out, hipStream_t st);
+
 struct GemmArgs {
   int mode, a_fmt, b_fmt, scale_kind, out_dtype;
   const void* a;

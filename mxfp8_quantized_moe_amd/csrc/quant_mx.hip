@@ -6,17 +6,23 @@
 //
 // The scale factor 2^-X is a power of two, so x * 2^-X is exact in fp32 (bf16
 // inputs); the clamp to +-448 and the round-to-nearest-even encode follow.
+// The cast runs on gfx950's scaled converter, which takes the block's e8m0
+// code as its scale (mx_cvt4 in device_common.hpp states why it is exact).
 //
 // Two layouts:
 //  * blocks along the last dim (fwd/dgrad operands, K-contiguous): 4 lanes per
 //    block, 16 bytes each, a 2-step shuffle reduction.
-//  * blocks along rows (wgrad operands; weights for dgrad): the colwise tile
-//    (64 columns x 512 rows) with the output transposed through LDS.  A
+//  * blocks along rows (wgrad operands; weights for dgrad): a 64-column tile
+//    with the output transposed through LDS.  A
 //    32-row block is exactly the 8 row-slots of one wave in one iteration, so
 //    its reduction is three lane shuffles.  With group offsets, blocks restart
 //    at every group, each group is padded to a multiple of 32 rows with +0,
 //    groups sit back to back at padded offsets, and the columns past the last
 //    padded group are written with zero codes and zero scales.
+//
+// The dual form reads each tile once and writes both: the row-block output and
+// the last-dim blocks of the same rows (a weight's forward and dgrad operands,
+// or an activation's dgrad and wgrad operands, from one read).
 //
 // Scales go out row-major ([R][NB], NB blocks per row) or in the K4 layout
 // the GEMM reads one 128-wide stage at a time from: byte (r, b) at
@@ -65,8 +71,8 @@ __global__ __launch_bounds__(256) void mx_lastdim_kernel(const uint16_t* __restr
     m = pk_fold(pk_absmax_bf16(pk_absmax_bf16(m, v.z), v.w));
     m = lane_max_xor<2, false>(lane_max_xor<1, false>(m));
     const int X = mx_exponent_bf16(m, RULE);
-    const float s = exp2_neg_bf16(X);
-    reinterpret_cast<u32x2*>(q)[ci] = u32x2{quant_bf16x4<0>(v.x, v.y, s), quant_bf16x4<0>(v.z, v.w, s)};
+    const float s = mx_scale_operand(X + 127);
+    reinterpret_cast<u32x2*>(q)[ci] = u32x2{mx_cvt4<RULE == 0>(v.x, v.y, s), mx_cvt4<RULE == 0>(v.z, v.w, s)};
     if constexpr (K4) {
       // 16 lanes hold one stage's four blocks of one row when rows have whole
       // stages (chunks start at multiples of 256, rows at multiples of 16):
@@ -122,6 +128,33 @@ struct MxPad {
   __device__ int operator()(int lo, int hi) const { return (hi - lo + 31) & ~31; }
 };
 
+// Padded offsets of a grouped row-block call: inclusive cumulative sum of
+// ceil32 of each group's rows (one workgroup, 256 threads).
+__device__ __noinline__ void mx_write_offs_pad(const int32_t* __restrict__ offs, int n_groups, int rows,
+                                               int32_t* __restrict__ offs_pad_out) {
+  __shared__ int tmp[4];
+  __shared__ int s_hi[256];
+  __shared__ int s_tot[2];
+  const int t = threadIdx.x;
+  int carry = 0, pbase = 0;
+  for (int g0 = 0; g0 < n_groups; g0 += 256) {
+    const int e = g0 + t;
+    const int vv = e < n_groups ? clamp_off(offs[e], rows) : 0;
+    const int h = max(block_scan_max<256>(vv, tmp), carry);
+    s_hi[t] = h;
+    __syncthreads();
+    const int l = t == 0 ? carry : s_hi[t - 1];
+    const int pd = e < n_groups ? ((h - l + 31) & ~31) : 0;
+    const int pincl = block_scan_sum<256>(pd, tmp) + pbase;
+    if (e < n_groups) offs_pad_out[e] = pincl;
+    if (t == 255) { s_tot[0] = pincl; s_tot[1] = h; }
+    __syncthreads();
+    pbase = s_tot[0];
+    carry = s_tot[1];
+    __syncthreads();
+  }
+}
+
 template <int RULE, bool GROUPED, bool K4>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t batch, int rows,
                                                       int cols, const int32_t* __restrict__ offs, int n_groups,
@@ -142,29 +175,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
   int64_t srow0, s_rows;   // scale row of column 0 and scale rows in all
   int s_nb;                // blocks per scale row
   if constexpr (GROUPED) {
-    if (blockIdx.x == 0 && offs_pad_out != nullptr) {
-      // padded offsets: inclusive cumulative sum of ceil32 of each group's rows
-      __shared__ int tmp[4];
-      __shared__ int s_hi[256];
-      __shared__ int s_tot[2];
-      int carry = 0, pbase = 0;
-      for (int g0 = 0; g0 < n_groups; g0 += 256) {
-        const int e = g0 + t;
-        const int vv = e < n_groups ? clamp_off(offs[e], rows) : 0;
-        const int h = max(block_scan_max<256>(vv, tmp), carry);
-        s_hi[t] = h;
-        __syncthreads();
-        const int l = t == 0 ? carry : s_hi[t - 1];
-        const int pd = e < n_groups ? ((h - l + 31) & ~31) : 0;
-        const int pincl = block_scan_sum<256>(pd, tmp) + pbase;
-        if (e < n_groups) offs_pad_out[e] = pincl;
-        if (t == 255) { s_tot[0] = pincl; s_tot[1] = h; }
-        __syncthreads();
-        pbase = s_tot[0];
-        carry = s_tot[1];
-        __syncthreads();
-      }
-    }
+    if (blockIdx.x == 0 && offs_pad_out != nullptr) mx_write_offs_pad(offs, n_groups, rows, offs_pad_out);
     const Unit un = find_unit<256>(offs, n_groups, rows, u, MxChunks{}, MxPad{});
     if (un.e >= 0) {
       lo = un.lo; hi = un.hi; plo = un.pbase; phi = plo + ((hi - lo + 31) & ~31); j = un.j;
@@ -232,13 +243,21 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
     for (int k = 0; k < 8; ++k) {
       const uint32_t a16 = (m[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
       const int X = mx_exponent_bf16(a16, RULE);
-      s[k] = exp2_neg_bf16(X);
+      s[k] = mx_scale_operand(X + 127);
       if (lane < 8) s_x[(cc * 8 + k) * (kMxRows / 32) + 4 * i + w] = (uint8_t)(X + 127);
     }
+    // column k of rows 0..3: the bf16 pairs (row 0, row 1) and (row 2, row 3) of that column, built
+    // with byte permutes, give the column's four codes in row order, one word for the tile
+    const uint32_t r0[4] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w};
+    const uint32_t r1[4] = {v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+    const uint32_t r2[4] = {v[i][2].x, v[i][2].y, v[i][2].z, v[i][2].w};
+    const uint32_t r3[4] = {v[i][3].x, v[i][3].y, v[i][3].z, v[i][3].w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t word = quant4<0>(col_of(v[i][0], k), col_of(v[i][1], k), col_of(v[i][2], k),
-                                      col_of(v[i][3], k), s[k]);
+      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;   // high or low bf16 of each word
+      const uint32_t p01 = __builtin_amdgcn_perm(r1[k >> 1], r0[k >> 1], sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(r3[k >> 1], r2[k >> 1], sel);
+      const uint32_t word = mx_cvt4<RULE == 0>(p01, p23, s[k]);
       *reinterpret_cast<uint32_t*>(tile + mx_tile_off(cc * 8 + k, 128 * i + 4 * rs)) = word;
     }
   }
@@ -341,6 +360,257 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, in
                                     n_strips, st)
                    : launch_rows<1>(x, batch, rows, cols, offs, n_groups, k4, q, sc, rows_pad, offs_pad_out, grid,
                                     n_strips, st);
+}
+
+// ------------------------------------------------------------ both forms from one read
+//
+// Work items are 128 columns x 128 rows.  Thread t holds the 16-column slice
+// cc = t & 7 of rows 4 rs .. 4 rs + 3 (rs = t >> 3), so a wave's 8 row slots
+// are one 32-row block (three lane exchanges give a column's block maximum)
+// and a 32-column last-dim block is the slices of two adjacent lanes (one
+// exchange).  Every row's 128 last-dim codes leave as one whole cache line
+// (eight 16-byte stores) and its four e8m0 bytes as one word; the row-block
+// codes are transposed through a 16 KiB LDS tile and leave as 128-byte column
+// segments.  Narrower items than the row-block kernel's 64 x 256: with 64
+// columns, each workgroup wrote half of every row's line and the two halves
+// met only in memory.
+constexpr int kDualRows = 128, kDualCols = 128;
+
+// Column c, row r of the codes tile: 8 segments of 16 rows per column, the
+// segment index XOR-ed with the 16-column slice so a wave's 4-row writes of
+// one slice column spread over 32 banks.
+__device__ __forceinline__ int mx_dual_off(int c, int r) {
+  return c * kDualRows + ((((r >> 4) ^ (c >> 4)) & 7) << 4) + (r & 15);
+}
+
+__device__ __forceinline__ int mx_dual_chunks(int lo, int hi) {
+  return (((hi - lo + 31) & ~31) + kDualRows - 1) / kDualRows;
+}
+struct MxDualChunks {
+  __device__ int operator()(int lo, int hi) const { return mx_dual_chunks(lo, hi); }
+};
+
+template <int RULE, bool GROUPED, bool K4>
+__global__ __launch_bounds__(256) void mx_dual_kernel(const uint16_t* __restrict__ x, int64_t batch, int rows,
+                                                      int cols, const int32_t* __restrict__ offs, int n_groups,
+                                                      uint8_t* __restrict__ ql, uint8_t* __restrict__ scl,
+                                                      int64_t l_rows, uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ sc, int64_t rows_pad,
+                                                      int32_t* __restrict__ offs_pad_out, int n_strips) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kDualCols * kDualRows];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[kDualCols * (kDualRows / 32)];   // [column][block]
+
+  const int strip = blockIdx.x % n_strips;
+  const int u = blockIdx.x / n_strips;
+  const int t = threadIdx.x, cc = t & 7, rs = t >> 3, lane = t & 63, w = t >> 6;
+
+  // geometry, as the row-block kernel: input rows [lo, hi) -> padded output rows [plo, phi)
+  int lo, hi, plo, phi, j;
+  int64_t ld_q;
+  uint8_t* qb;
+  int64_t srow0, s_rows;   // row-block scales: row of column 0, rows in all
+  int s_nb;                // row-block scales: blocks per row
+  int64_t lrow0 = 0;       // last-dim output row of input row 0
+  if constexpr (GROUPED) {
+    if (blockIdx.x == 0 && offs_pad_out != nullptr) mx_write_offs_pad(offs, n_groups, rows, offs_pad_out);
+    const Unit un = find_unit<256>(offs, n_groups, rows, u, MxDualChunks{}, MxPad{});
+    if (un.e >= 0) {
+      lo = un.lo; hi = un.hi; plo = un.pbase; phi = plo + ((hi - lo + 31) & ~31); j = un.j;
+    } else {
+      lo = hi = 0; plo = un.pbase; phi = (int)rows_pad; j = un.j;
+      if (plo + j * kDualRows >= phi) return;
+    }
+    ld_q = rows_pad; qb = q;
+    srow0 = 0; s_rows = cols; s_nb = (int)(rows_pad / 32);
+  } else {
+    const int upb = mx_dual_chunks(0, rows);
+    const int64_t b = upb ? u / upb : batch;
+    if (b >= batch) return;
+    j = u % upb;
+    lo = 0; hi = rows; plo = 0; phi = rows;
+    ld_q = rows;
+    qb = q + b * cols * (int64_t)rows;
+    srow0 = b * cols; s_rows = batch * cols; s_nb = rows / 32;
+    x += b * (int64_t)rows * cols;
+    lrow0 = b * (int64_t)rows;
+  }
+
+  const int A = plo + j * kDualRows;               // output row of tile row 0 (multiple of 32)
+  const int r_end = min(A + kDualRows, phi);
+  const int c0 = strip * kDualCols;
+  const int col = c0 + cc * 16;
+  const bool col_ok = col < cols;                  // cols % 32 == 0: a slice is wholly in or out
+  const bool full = c0 + kDualCols <= cols && A + kDualRows <= r_end && lo + (A + kDualRows - plo) <= hi;
+  u32x4 v[4][2];
+  if (full) {
+    const uint16_t* xr = x + (int64_t)(lo + A - plo + 4 * rs) * cols + col;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k][0] = *reinterpret_cast<const u32x4*>(xr + (int64_t)k * cols);
+      v[k][1] = *reinterpret_cast<const u32x4*>(xr + (int64_t)k * cols + 8);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = A + 4 * rs + k, in = lo + (r - plo);
+      const bool ok = col_ok && r < r_end && in < hi;
+      const uint16_t* xr = x + (int64_t)in * cols + col;
+      v[k][0] = ok ? *reinterpret_cast<const u32x4*>(xr) : u32x4{0, 0, 0, 0};
+      v[k][1] = ok ? *reinterpret_cast<const u32x4*>(xr + 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // last-dim blocks: per row, the 32 columns of lanes cc and cc ^ 1
+  {
+    const int nb = cols >> 5, b0 = c0 >> 5;              // b0 % 4 == 0: a tile row is one K4 word
+    const int nvalid = min(4, nb - b0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t m = 0;
+      m = pk_absmax_bf16(m, v[k][0].x); m = pk_absmax_bf16(m, v[k][0].y);
+      m = pk_absmax_bf16(m, v[k][0].z); m = pk_absmax_bf16(m, v[k][0].w);
+      m = pk_absmax_bf16(m, v[k][1].x); m = pk_absmax_bf16(m, v[k][1].y);
+      m = pk_absmax_bf16(m, v[k][1].z); m = pk_absmax_bf16(m, v[k][1].w);
+      m = lane_max_xor<1, false>(pk_fold(m));
+      const int X = mx_exponent_bf16(m, RULE);
+      const float so = mx_scale_operand(X + 127);
+      const uint32_t e = (uint32_t)(X + 127);
+      const uint32_t e1 = (uint32_t)__shfl((int)e, lane + 2, 64);   // blocks 1..3 of the row (lanes cc 2, 4, 6)
+      const uint32_t e2 = (uint32_t)__shfl((int)e, lane + 4, 64);
+      const uint32_t e3 = (uint32_t)__shfl((int)e, lane + 6, 64);
+      const int r = A + 4 * rs + k, in = lo + (r - plo);
+      if (full || (r < r_end && in < hi)) {
+        const int64_t grow = lrow0 + in;
+        if (col_ok)
+          *reinterpret_cast<u32x4*>(ql + grow * cols + col) =
+              u32x4{mx_cvt4<RULE == 0>(v[k][0].x, v[k][0].y, so), mx_cvt4<RULE == 0>(v[k][0].z, v[k][0].w, so),
+                    mx_cvt4<RULE == 0>(v[k][1].x, v[k][1].y, so), mx_cvt4<RULE == 0>(v[k][1].z, v[k][1].w, so)};
+        if (cc == 0) {
+          // the blocks past the row's last (K4: up to the stage's four) are zero
+          const uint32_t word = (e | (e1 << 8) | (e2 << 16) | (e3 << 24)) &
+                                (nvalid >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nvalid)) - 1u));
+          if constexpr (K4) {
+            *reinterpret_cast<uint32_t*>(scl + k4_index(grow, b0, l_rows)) = word;
+          } else if (nvalid == 4 && ((grow * nb + b0) & 3) == 0) {
+            *reinterpret_cast<uint32_t*>(scl + grow * nb + b0) = word;
+          } else {
+            for (int i = 0; i < nvalid; ++i) scl[grow * nb + b0 + i] = (uint8_t)(word >> (8 * i));
+          }
+        }
+      }
+    }
+  }
+
+  // row blocks: the wave's 32 rows of each of the thread's 16 columns
+  {
+    uint32_t m[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      m[4 * h + 0] = m[4 * h + 1] = m[4 * h + 2] = m[4 * h + 3] = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        m[4 * h + 0] = pk_absmax_bf16(m[4 * h + 0], v[k][h].x);
+        m[4 * h + 1] = pk_absmax_bf16(m[4 * h + 1], v[k][h].y);
+        m[4 * h + 2] = pk_absmax_bf16(m[4 * h + 2], v[k][h].z);
+        m[4 * h + 3] = pk_absmax_bf16(m[4 * h + 3], v[k][h].w);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) m[p] = lane_max_xor<32, true>(lane_max_xor<16, true>(lane_max_xor<8, true>(m[p])));
+#pragma unroll
+    for (int jc = 0; jc < 16; ++jc) {
+      const uint32_t a16 = (m[jc >> 1] >> (16 * (jc & 1))) & 0xFFFFu;
+      const int X = mx_exponent_bf16(a16, RULE);
+      if (lane < 8) s_x[(cc * 16 + jc) * (kDualRows / 32) + w] = (uint8_t)(X + 127);
+      const int h = jc >> 3, wi = (jc >> 1) & 3;
+      auto word_of = [&](int k) {
+        const u32x4& q4 = v[k][h];
+        return wi == 0 ? q4.x : wi == 1 ? q4.y : wi == 2 ? q4.z : q4.w;
+      };
+      const uint32_t sel = (jc & 1) ? 0x07060302u : 0x05040100u;   // high or low bf16 of each word
+      const uint32_t p01 = __builtin_amdgcn_perm(word_of(1), word_of(0), sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(word_of(3), word_of(2), sel);
+      *reinterpret_cast<uint32_t*>(tile + mx_dual_off(cc * 16 + jc, 4 * rs)) =
+          mx_cvt4<RULE == 0>(p01, p23, mx_scale_operand(X + 127));
+    }
+  }
+  __syncthreads();
+
+  // transposed codes: 4 passes of 32 columns x 8 segments of 16 rows
+#pragma unroll
+  for (int p = 0; p < kDualCols / 32; ++p) {
+    const int ci = p * 32 + (t >> 3), sg = t & 7;
+    const int c = c0 + ci, R0 = A + 16 * sg;
+    const u32x4 d = *reinterpret_cast<const u32x4*>(tile + mx_dual_off(ci, 16 * sg));
+    if (full || (c < cols && R0 < r_end)) *reinterpret_cast<u32x4*>(qb + (int64_t)c * ld_q + R0) = d;
+  }
+  // row-block scales: column t's (up to) four blocks of this item
+  if (t < kDualCols) {
+    const int ci = t, c = c0 + ci;
+    const int nbt = (r_end - A) >> 5;
+    if (c < cols) {
+      const int64_t srow = srow0 + c;
+      const int blk0 = A >> 5;
+      if (nbt == 4 && (blk0 & 3) == 0 && (K4 || (s_nb & 3) == 0)) {
+        const uint32_t wv = *reinterpret_cast<const uint32_t*>(s_x + ci * 4);
+        *reinterpret_cast<uint32_t*>(sc + (K4 ? k4_index(srow, blk0, s_rows) : srow * s_nb + blk0)) = wv;
+      } else {
+        for (int b = 0; b < nbt; ++b) {
+          const int blk = blk0 + b;
+          if constexpr (K4) {
+            uint8_t* d = sc + k4_index(srow, blk, s_rows);
+            d[0] = s_x[ci * 4 + b];
+            if (blk == s_nb - 1)
+              for (int e = 1; (blk + e) & 3; ++e) d[e] = 0;   // pad to the stage's four blocks
+          } else {
+            sc[srow * s_nb + blk] = s_x[ci * 4 + b];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int RULE>
+static hipError_t launch_dual(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+                              int32_t n_groups, bool k4, uint8_t* ql, uint8_t* scl, uint8_t* q, uint8_t* sc,
+                              int64_t rows_pad, int32_t* offs_pad_out, dim3 grid, int n_strips, hipStream_t st) {
+  const int64_t l_rows = batch * rows;
+  if (offs) {
+    auto k = k4 ? mx_dual_kernel<RULE, true, true> : mx_dual_kernel<RULE, true, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, (int64_t)1, (int)rows, (int)cols, offs, n_groups, ql, scl,
+                       l_rows, q, sc, rows_pad, offs_pad_out, n_strips);
+  } else {
+    auto k = k4 ? mx_dual_kernel<RULE, false, true> : mx_dual_kernel<RULE, false, false>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, batch, (int)rows, (int)cols, nullptr, 0, ql, scl, l_rows, q,
+                       sc, rows, nullptr, n_strips);
+  }
+  return hipGetLastError();
+}
+
+int64_t mx_dual_grid_bound(int64_t batch, int64_t rows, int64_t cols, bool grouped, int32_t n_groups,
+                           int64_t rows_pad) {
+  const int64_t units = grouped ? (rows_pad + kDualRows - 1) / kDualRows + n_groups + 1
+                                : batch * ((rows + kDualRows - 1) / kDualRows);
+  return units * std::max<int64_t>((cols + kDualCols - 1) / kDualCols, 1);
+}
+
+hipError_t launch_quantize_mx_dual(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                   const int32_t* offs, int32_t n_groups, int rule, int scale_layout, uint8_t* q,
+                                   uint8_t* sc, uint8_t* q_t, uint8_t* sc_t, int64_t rows_pad,
+                                   int32_t* offs_pad_out, hipStream_t st) {
+  const bool k4 = scale_layout == 1;
+  if (cols == 0) {
+    if (offs == nullptr || offs_pad_out == nullptr) return hipSuccess;
+  }
+  const int n_strips = (int)std::max<int64_t>((cols + kDualCols - 1) / kDualCols, 1);
+  const int64_t blocks = mx_dual_grid_bound(batch, rows, cols, offs != nullptr, n_groups, rows_pad);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
+  return rule == 0 ? launch_dual<0>(x, batch, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                    offs_pad_out, grid, n_strips, st)
+                   : launch_dual<1>(x, batch, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                    offs_pad_out, grid, n_strips, st);
 }
 
 }  // namespace fp8moe

@@ -102,6 +102,21 @@ int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, 
   return FP8MOE_OK;
 }
 
+int check_quantize_mx_dual(const void* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+                           int32_t n_groups, int rule, int scale_layout, const void* q, const void* sc,
+                           const void* q_t, const void* sc_t, int64_t rows_pad, const int32_t* offs_pad_out) {
+  int st = check_quantize_mx(x, batch, rows, cols, 1, nullptr, 0, rule, scale_layout, q, sc, 0, nullptr);
+  if (st) return st;
+  st = check_quantize_mx(x, batch, rows, cols, 0, offs, n_groups, rule, scale_layout, q_t, sc_t, rows_pad,
+                         offs_pad_out);
+  if (st) return st;
+  // one workgroup per 128 x 128 item: the grid must fit a 1D launch
+  const int64_t units = offs ? (rows_pad + 127) / 128 + n_groups + 1 : mul(batch, (rows + 127) / 128);
+  const int64_t grid = mul(units, (cols + 127) / 128 > 0 ? (cols + 127) / 128 : 1);
+  if (units < 0 || grid < 0 || grid > kI32Max) return FP8MOE_ERR_SHAPE;
+  return FP8MOE_OK;
+}
+
 int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const void* b, int b_fmt,
                      const void* sb, int scale_kind, const int32_t* offs, int32_t n_groups, int64_t M,
                      int64_t N, int64_t K, const void* out, int out_dtype) {

@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 9):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 104
+    assert lib.fp8moe_version() == 105
 
 
 def test_rows_bound(lib):
@@ -289,6 +289,24 @@ def test_mx_rejections(lib):
     assert f(P, 1, 75, 64, 0, P, 4, 0, 1, P, None, 224, P, None) == L.ERR_NULL        # K4 scales missing
     # K4 scale tensors are addressed with 32-bit offsets: at most 2^31 - 1 bytes
     assert f(P, 1, 1 << 29, 2048, 1, None, 0, 0, 1, P, P, 0, None, None) == L.ERR_SHAPE
+
+
+def test_mx_dual_rejections(lib):
+    d = lib.quantize_mx_dual
+    # (x, batch, rows, cols, offs, n_groups, rule, layout, q, sc, q_t, sc_t, rows_pad, offs_pad, stream)
+    assert d(P, 1, 64, 64, None, 0, 5, 0, P, P, P, P, 64, None, None) == L.ERR_ENUM          # rule
+    assert d(P, 1, 64, 64, None, 0, 0, 2, P, P, P, P, 64, None, None) == L.ERR_ENUM          # scale layout
+    assert d(P, 1, 64, 48, None, 0, 0, 0, P, P, P, P, 64, None, None) == L.ERR_ALIGN         # cols % 32
+    assert d(P, 2, 40, 64, None, 0, 0, 0, P, P, P, P, 40, None, None) == L.ERR_ALIGN         # rows % 32 (batched)
+    assert d(P, 1, 75, 64, P, 4, 0, 0, P, P, P, P, 192, P, None) == L.ERR_SHAPE              # rows_pad < bound
+    assert d(P, 2, 75, 64, P, 4, 0, 0, P, P, P, P, 224, P, None) == L.ERR_SHAPE              # batch with offs
+    assert d(P, 1, 64, 64, None, 0, 0, 0, None, P, P, P, 64, None, None) == L.ERR_NULL       # last-dim codes
+    assert d(P, 1, 64, 64, None, 0, 0, 0, P, None, P, P, 64, None, None) == L.ERR_NULL       # last-dim scales
+    assert d(P, 1, 64, 64, None, 0, 0, 0, P, P, None, P, 64, None, None) == L.ERR_NULL       # row-block codes
+    assert d(P, 1, 64, 64, None, 0, 0, 1, P, P, P, None, 64, None, None) == L.ERR_NULL       # row-block scales
+    assert d(MIS, 1, 64, 64, None, 0, 0, 0, P, P, P, P, 64, None, None) == L.ERR_ALIGN
+    assert d(P, 1, 64, 64, None, 0, 0, 0, MIS, P, P, P, 64, None, None) == L.ERR_ALIGN
+    assert d(P, 1, 64, 64, None, 0, 0, 0, P, P, MIS, P, 64, None, None) == L.ERR_ALIGN
 
 
 def test_gemm_rejections(lib):

@@ -57,9 +57,10 @@ LAYER = {
     3: ["route", "permute+q X", "q_row W1", "gemm fwd W1", "swiglu+q", "q_row W2", "gemm fwd W2", "combine",
         "combine bwd+q", "q_col W2", "gemm dgrad W2", "q_col dYg", "q_col A2", "gemm wgrad W2", "swiglu bwd+q",
         "q_col W1", "gemm dgrad W1", "q_col dH1", "q_col Xg", "gemm wgrad W1", "combine dX"],
-    5: ["route", "permute X", "mx Xg", "mx W1", "gemm fwd W1", "swiglu", "mx A2", "mx W2", "gemm fwd W2", "combine",
-        "combine bwd", "mx dYg", "mx W2^T", "gemm dgrad W2", "mx dYg^T", "mx A2^T", "gemm wgrad W2", "swiglu bwd",
-        "mx dH1", "mx W1^T", "gemm dgrad W1", "mx dH1^T", "mx Xg^T", "gemm wgrad W1", "combine dX"],
+    5: ["route", "permute X", "mx Xg (both forms)", "mx W1 (both forms)", "gemm fwd W1", "swiglu",
+        "mx A2 (both forms)", "mx W2 (both forms)", "gemm fwd W2", "combine", "combine bwd", "mx dYg (both forms)",
+        "gemm dgrad W2", "gemm wgrad W2", "swiglu bwd", "mx dH1 (both forms)", "gemm dgrad W1", "gemm wgrad W1",
+        "combine dX"],
 }
 LAYER[4] = LAYER[3]
 # (workload, variant): the experts-only steps of configs 3-5 and the whole MoE layer
@@ -217,6 +218,22 @@ def check_mx_rows_g(sp, hst, phase):
     assert_bytes_equal(q[cols], np.concatenate([a for a, _, _ in res]), "codes (transposed, padded)")
     assert_bytes_equal(sc[cols], np.concatenate([b for _, b, _ in res]), "e8m0")
     assert_bytes_equal(host(sp["offs_pad"]), res[0][2], "padded offsets")
+
+
+def check_mx_dual(sp, hst, phase):
+    """Both MX forms from one read: the last-dim half as check_mx_last, the row-block half as
+    check_mx_rows_b (batched) or check_mx_rows_g (grouped)."""
+    last = dict(src=sp["src"], rule=sp["rule"], q=sp["q"], s=sp["s"])
+    if "offs" in sp:
+        last["shape"] = sp["shape"]
+        check_mx_last(last, hst, phase)
+        check_mx_rows_g(dict(src=sp["src"], offs=sp["offs"], rows_pad=sp["rows_pad"], rule=sp["rule"], q=sp["qt"],
+                             s=sp["st"], offs_pad=sp["offs_pad"]), hst, phase)
+    else:
+        B, R, C = sp["shape"]
+        last["shape"] = (B * R, C)
+        check_mx_last(last, hst, phase)
+        check_mx_rows_b(dict(src=sp["src"], shape=sp["shape"], rule=sp["rule"], q=sp["qt"], s=sp["st"]), hst, phase)
 
 
 # ------------------------------------------------------------------ GEMM checks
@@ -391,7 +408,7 @@ def check_combine_bwd(sp, hst, phase):
 CHECKS = {"q_row": check_q_row, "q_col_grouped": check_q_col_grouped, "q_col_batched": check_q_col_batched,
           "mx_last": check_mx_last, "mx_rows_b": check_mx_rows_b, "mx_rows_g": check_mx_rows_g,
           "g_m": check_g_m, "g_k": check_g_k, "g_k_bf16": check_g_k_bf16,
-          "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
+          "mx_dual": check_mx_dual, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
           "swiglu": check_swiglu, "swiglu_bwd": check_swiglu_bwd, "combine": check_combine,
           "combine_bwd": check_combine_bwd}
 

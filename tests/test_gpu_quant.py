@@ -243,6 +243,146 @@ def test_mx_rows_grouped_k4_layout(case):
     assert_bytes_equal(host(sc), e8m0_rows_to_k4(sr), "e8m0 K4")
 
 
+@pytest.mark.parametrize("rule", [0, 1])
+def test_mx_cast_every_bf16_value(rule):
+    """The MX cast runs on gfx950's scaled converter.  For block exponents X across the whole range
+    (-127 .. 119: the e8m0 extremes, the subnormal-maximum clamp, both sides of 0, the largest bf16), every
+    bf16 magnitude up to the block maximum, with both signs, is cast in blocks whose first element pins
+    that maximum; this covers the values that land in (448, 512) under the FLOOR rule (the converter's NaN
+    range, mapped back to +-448), subnormal results and signed zeros.  Bit-exact against the oracle."""
+    Xs = [-127, -126, -125, -120, -100, -60, -20, -9, -8, -1, 0, 1, 8, 30, 60, 100, 117, 118, 119]
+    blocks = []
+    for X in Xs:
+        field = X + 135
+        if field < 1:
+            continue
+        # FLOOR: any significand gives X; CEIL: a significand up to 0x60 (1.75) keeps X
+        pilot = (field << 7) | (0x7F if rule == 0 else 0x60)
+        mags = np.arange(0, pilot + 1, dtype=np.uint16)
+        vals = np.concatenate([mags, mags | 0x8000])
+        n = (vals.size + 30) // 31
+        body = np.zeros(n * 31, np.uint16)
+        body[:vals.size] = vals
+        blk = np.empty((n, 32), np.uint16)
+        blk[:, 0] = pilot
+        blk[:, 1:] = body.reshape(n, 31)
+        blocks.append(blk)
+    allb = np.concatenate(blocks)
+    allb = np.concatenate([allb, np.zeros(((-allb.shape[0]) % 4, 32), np.uint16)])   # whole rows of 4 blocks
+    x = allb.reshape(-1, 128)
+    note(f"mx cast sweep rule={rule}: {x.size} values")
+    q, sc, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule)
+    qr, sr = oracle.quantize_mx_lastdim(x, rule)
+    assert_bytes_equal(host(sc), sr, "e8m0")
+    assert_bytes_equal(host(q), qr, "codes")
+    note(f"mx cast sweep rule={rule}: row blocks")
+    xt = np.ascontiguousarray(x[: x.shape[0] // 32 * 32].reshape(-1, 32, 128)[:4].transpose(0, 2, 1))   # blocks down columns
+    qt, sct, _ = fm.quantize_mx(bf16_dev(xt), axis=0, rule=rule)
+    qtr, strr = oracle.quantize_mx_rows_batched(xt, rule)
+    assert_bytes_equal(host(sct), strr, "row-block e8m0")
+    assert_bytes_equal(host(qt), qtr, "row-block codes")
+
+
+# ------------------------------------------------------------------- MXFP8, both forms from one read
+
+def _dual_check(x, xq, offs, rule, layout, rows_pad, what):
+    """quantize_mx_dual against the oracle's last-dim and row-block quantizers (and so against the two
+    quantize_mx calls it stands for), with sentinels in every output."""
+    k4 = layout == fm.MX_LAYOUT_K4
+    if offs is None:
+        B, R, C = x.shape
+        rows_total, scale_t_rows, nb_t = B * R, B * C, R // 32
+        q_t = filled_u8((B, C, R))
+    else:
+        (R, C), B = x.shape, 1
+        rows_total, scale_t_rows, nb_t = R, C, rows_pad // 32
+        q_t = filled_u8((C, rows_pad))
+    q = filled_u8((rows_total, C))
+    sc = filled_u8(fm.mx_k4_shape(rows_total, C // 32) if k4 else (rows_total, C // 32))
+    sc_t = filled_u8(fm.mx_k4_shape(scale_t_rows, nb_t) if k4 else (scale_t_rows, nb_t))
+    note(f"mx dual {what} rule={rule} layout={layout} shape={x.shape}")
+    q, sc, q_t, sc_t, op = fm.quantize_mx_dual(xq, None if offs is None else i32_dev(offs), rule=rule,
+                                               rows_pad=rows_pad, q=q, scale=sc, q_t=q_t, scale_t=sc_t,
+                                               layout=layout)
+    x2 = x.reshape(rows_total, C)
+    if offs is None:
+        covered = rows_total
+        qtr, str_ = oracle.quantize_mx_rows_batched(x, rule)
+        str_ = str_.reshape(scale_t_rows, nb_t)
+    else:
+        covered = int(min(max(int(np.clip(offs, 0, R).max()), 0), R))
+        qtr, str_, opr = oracle.quantize_mx_rows_grouped(x, offs, rule, rows_pad)
+        assert_bytes_equal(host(op), opr, f"{what} padded offsets")
+    assert_bytes_equal(host(q_t), qtr, f"{what} row-block codes")
+    assert_bytes_equal(host(sc_t), e8m0_rows_to_k4(str_) if k4 else str_, f"{what} row-block e8m0")
+    ql, sl = oracle.quantize_mx_lastdim(x2[:covered], rule)
+    qh = host(q)
+    assert_bytes_equal(qh[:covered], ql, f"{what} last-dim codes")
+    assert np.all(qh[covered:] == 0xA5), f"{what}: rows past the last group must stay untouched"
+    if k4:
+        full = np.full((rows_total, C // 32), 0xA5, np.uint8)
+        full[:covered] = sl.reshape(covered, C // 32)
+        want = e8m0_rows_to_k4(full)
+        got = host(sc)
+        if covered < rows_total:          # the untouched rows' K4 bytes, padding included, keep the sentinel
+            want[:, covered:, :] = 0xA5
+        assert_bytes_equal(got, want, f"{what} last-dim e8m0 K4")
+    else:
+        assert_bytes_equal(host(sc)[:covered], sl.reshape(covered, C // 32), f"{what} last-dim e8m0")
+        assert np.all(host(sc)[covered:] == 0xA5)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("layout", [fm.MX_LAYOUT_ROWS, fm.MX_LAYOUT_K4])
+@pytest.mark.parametrize("shape", [(2, 64, 96), (3, 288, 160), (1, 32, 32), (2, 544, 224), (4, 1024, 512)])
+def test_mx_dual_batched(rule, layout, shape):
+    """Batched (weights): last-dim blocks of x viewed [B*R, C] and row blocks per batch item.  Widths give
+    1 to 16 blocks per row, odd block counts (a tile's second block past the end) and block counts of 1, 2
+    and 3 modulo 4 (the K4 stage padding)."""
+    x = special_input(7000 + sum(shape), shape, 0.01, 30.0)
+    _dual_check(x, bf16_dev(x), None, rule, layout, None, "batched")
+
+
+MX_DUAL_GROUP_CASES = {
+    "ragged": (1300, 160, synth.offsets_from_counts(synth.random_counts(8, 1290, 7))),   # 10 rows in no group
+    "cfg1": (512, 256, synth.offsets_from_counts(synth.routing_counts(1))),
+    "malformed": (300, 64, np.array([40, 20, 300, 500], np.int32)),
+    "one_row": (1, 32, np.array([1], np.int32)),
+    "wide": (700, 5120, synth.offsets_from_counts(synth.random_counts(9, 700, 16))),
+}
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("layout", [fm.MX_LAYOUT_ROWS, fm.MX_LAYOUT_K4])
+@pytest.mark.parametrize("case", list(MX_DUAL_GROUP_CASES))
+def test_mx_dual_grouped(rule, layout, case):
+    """Grouped (activations): last-dim blocks of the rows inside groups and padded row blocks per group."""
+    M, C, offs = MX_DUAL_GROUP_CASES[case]
+    x = special_input(7100 + M + C, (M, C), 0.01, 30.0)
+    rows_pad = fm.quantize_mx_rows_bound(M, len(offs)) + 32
+    _dual_check(x, bf16_dev(x), offs, rule, layout, rows_pad, case)
+
+
+def test_mx_dual_llama4_scout_weights_sampled():
+    """W2 of the Llama4-Scout layer ([16, 5120, 8192]) in the dual form, against the two quantize_mx calls
+    it replaces (bit for bit, whole tensors) and the oracle on sampled rows and columns."""
+    w = synth.WORKLOADS[5]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    x = (torch.randn(w.E, w.H, w.F, device=DEV, generator=gen) * 0.02).to(torch.bfloat16)
+    note("mx dual Llama4-Scout W2 full size")
+    q, sc, q_t, sc_t, _ = fm.quantize_mx_dual(x, layout=fm.MX_LAYOUT_K4)
+    q1, s1, _ = fm.quantize_mx(x.view(w.E * w.H, w.F), axis=1, layout=fm.MX_LAYOUT_K4)
+    q2, s2, _ = fm.quantize_mx(x, axis=0, layout=fm.MX_LAYOUT_K4)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(sc, s1), "last-dim form differs from quantize_mx(axis=1)"
+    assert torch.equal(q_t, q2) and torch.equal(sc_t, s2), "row-block form differs from quantize_mx(axis=0)"
+    xh = host(x)
+    rows = _sample(w.E * w.H, 64, 11)
+    ql, sl = oracle.quantize_mx_lastdim(xh.reshape(-1, w.F)[rows], 0)
+    assert_bytes_equal(host(q)[rows], ql, "last-dim codes sampled")
+
+
 # ------------------------------------------------------------------- full-size, sampled
 
 def _sample(n, k, seed):
