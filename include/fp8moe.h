@@ -48,8 +48,9 @@
  *     threads.  The only mutable library state is the device array the
  *     single-pass colwise quantizer exchanges column maxima through (see
  *     quantize_colwise: its values are tagged per call, so overlapping calls
- *     stay correct) and that quantizer's poll budget, a test hook
- *     (fp8moe_set_colwise_poll_budget).  Everything else a call needs is in
+ *     stay correct) and that quantizer's poll budget and chunk height, test
+ *     hooks (fp8moe_set_colwise_poll_budget, fp8moe_set_colwise_chunk_rows).
+ *     Everything else a call needs is in
  *     its arguments.
  */
 #ifndef FP8MOE_H
@@ -449,15 +450,17 @@ int moe_combine_backward(const void *dy_bf16, const void *yg_bf16, int64_t rows,
  *     scale f32  [batch][cols]
  *   Requires: batch >= 1 (== 1 with offs), n_groups >= 1 with offs, rows, cols >= 0,
  *   ld_q >= rows, cols % 8 == 0, ld_q % 16 == 0, x and q_t 16-byte aligned.
- *   Normally the call enqueues one kernel: every 512-row x 64-column chunk is
- *   read once into registers, and the chunks of a group exchange their column
+ *   Normally the call enqueues one kernel: every 64-column chunk of 512 rows
+ *   (128 rows when the groups or batch items average at most 512 rows, so a
+ *   short group does not occupy a mostly empty chunk) is read once into
+ *   registers, and the chunks of a group exchange their column
  *   maxima through a fixed library-owned device array (32768 chunk slots, no
  *   allocation) before casting from registers.  Values in that array carry a
  *   per-call tag (a host counter), so calls need no reset and leave nothing
  *   behind.  Calls that overlap on one device (other streams) stay correct: a
  *   chunk whose peers do not all publish within a bounded number of polls
  *   recomputes the maxima from x itself, at the cost of a second read.  A
- *   group taller than 128 chunks, a call with more than 32768 chunks, or a
+ *   group taller than 128 chunks of 512 rows, a call with more than 32768 chunks, or a
  *   call made while `stream` is being captured into a graph (where a replay
  *   would repeat the tag) instead takes three kernels (amax reset, partial
  *   amax, cast): x is read twice, and no state carries between launches.
@@ -591,6 +594,16 @@ int fp8moe_version(void);
  * after it returns.  Returns the previous budget.  Host only, no HIP call.
  */
 int fp8moe_set_colwise_poll_budget(int polls);
+
+/*
+ * fp8moe_set_colwise_chunk_rows -- test and tuning hook: the chunk height of
+ * the single-pass colwise quantizer (128 or 512 rows: forced; any other value:
+ * chosen per call, 128 rows when the groups or batch items average at most 512
+ * rows, else 512).  A forced height that a call cannot use (too many chunks)
+ * falls back to 512 rows, then to the two-pass path.  Results do not depend on
+ * it.  Process-wide; returns the previous setting (0 for per-call choice).
+ */
+int fp8moe_set_colwise_chunk_rows(int rows);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "moe_route_rows_bound", "moe_permute", "moe_combine", "quantize_tensorwise", "moe_permute_quantized",
            "quantize_blockwise", "grouped_mm_blockwise", "quantize_blockwise_tokens",
            "blockwise_token_blocks_bound", "grouped_mm_blockwise_k",
-           "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget", "moe_route_noalloc",
+           "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget", "fp8moe_set_colwise_chunk_rows", "moe_route_noalloc",
            "moe_permute_rowwise", "moe_combine_backward", "quantize_mx_dual"]
 
 _lib = None
@@ -45,6 +45,7 @@ _SIGS = {
     "fp8moe_default_codec": (_int, [_int, ctypes.POINTER(_int)]),
     "fp8moe_version": (_int, []),
     "fp8moe_set_colwise_poll_budget": (_int, [_int]),
+    "fp8moe_set_colwise_chunk_rows": (_int, [_int]),
     "swiglu_quantize_rowwise": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
     "swiglu_backward_quantize_rowwise": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
     "quantize_tensorwise": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),

@@ -278,6 +278,8 @@ int fp8moe_default_codec(int hip_device, int* codec_out) {
 
 int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(polls); }
 
+int fp8moe_set_colwise_chunk_rows(int rows) { return set_colwise_chunk_rows(rows); }
+
 int fp8moe_version(void) { return 105; }
 
 }  // extern "C"

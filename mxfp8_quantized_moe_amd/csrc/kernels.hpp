@@ -45,6 +45,8 @@ hipError_t launch_grouped_mm(const GemmArgs& g, hipStream_t st);
 
 // Poll budget of the single-pass colwise exchange (negative: the default); returns the previous one.
 int set_colwise_poll_budget(int polls);
+// Chunk height of the single-pass colwise quantizer (128 or 512: forced; else per call); returns the previous one.
+int set_colwise_chunk_rows(int rows);
 
 hipError_t launch_encode_f32(const float* y, int64_t n, int codec, uint8_t* q, hipStream_t st);
 hipError_t launch_quantize_blockwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,

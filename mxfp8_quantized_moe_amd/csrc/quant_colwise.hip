@@ -36,13 +36,16 @@ constexpr int kCwThreads = 256;
 constexpr int kCwIters = kTileRows / 128;   // 4 iterations of 128 rows
 constexpr uint32_t kTag = 0x80000000u;      // marks a merged |x| max (not yet a scale)
 
+// Chunks of CR rows (512, or 128 for calls whose groups are short on average).
+template <int CR = kTileRows>
 __device__ __forceinline__ int cw_chunks(int lo, int hi) {
   if (hi <= lo) return 1;                    // an empty group still owns one unit: its scale
   const int a = lo & ~15;
-  return (hi - a + kTileRows - 1) / kTileRows;
+  return (hi - a + CR - 1) / CR;
 }
+template <int CR = kTileRows>
 struct CwChunks {
-  __device__ int operator()(int lo, int hi) const { return cw_chunks(lo, hi); }
+  __device__ int operator()(int lo, int hi) const { return cw_chunks<CR>(lo, hi); }
 };
 struct NoPad {
   __device__ int operator()(int, int) const { return 0; }
@@ -61,20 +64,20 @@ struct CwGeom {
   bool ok;
 };
 
-template <bool GROUPED>
+template <bool GROUPED, int CR = kTileRows>
 __device__ __forceinline__ CwGeom cw_geom(int u, int64_t batch, int rows, int cols,
                                           const int32_t* offs, int n_groups, uint8_t* q_t,
                                           int64_t ld_q, float* scale) {
   CwGeom g;
   if constexpr (GROUPED) {
-    const Unit un = find_unit<kCwThreads>(offs, n_groups, rows, u, CwChunks{}, NoPad{});
+    const Unit un = find_unit<kCwThreads>(offs, n_groups, rows, u, CwChunks<CR>{}, NoPad{});
     g.ok = un.e >= 0;
     g.e = un.e; g.j = un.j; g.olo = un.lo; g.ohi = un.hi;
     g.in_base = 0;
     g.q = q_t;
     g.s = scale + (int64_t)max(un.e, 0) * cols;
   } else {
-    const int upb = cw_chunks(0, rows);
+    const int upb = cw_chunks<CR>(0, rows);
     const int64_t b = u / upb;
     g.ok = b < batch;
     g.e = (int)b; g.j = u % upb; g.olo = 0; g.ohi = rows;
@@ -278,36 +281,37 @@ __device__ __forceinline__ bool cw_gather(const unsigned long long* __restrict__
   return k >= nch;
 }
 
-template <int CODEC, bool GROUPED>
+template <int CODEC, bool GROUPED, int CR>
 __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __restrict__ x, int64_t batch,
                                                              int rows, int cols, const int32_t* __restrict__ offs,
                                                              int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
                                                              float* __restrict__ scale, int units, uint32_t gen,
                                                              int max_polls) {
+  constexpr int kIters = CR / 128;
   __shared__ uint32_t red[4 * 8 * 4];
   __shared__ uint32_t s_amax[64];
   __shared__ float s_scale[64];
   __shared__ int s_ok;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileCols * CR];
   const int t = threadIdx.x, cc = t & 7, rs = t >> 3;
   const int strip = blockIdx.x / units, u = blockIdx.x % units;
-  const CwGeom g = cw_geom<GROUPED>(u, batch, rows, cols, offs, n_groups, q_t, ld_q, scale);
+  const CwGeom g = cw_geom<GROUPED, CR>(u, batch, rows, cols, offs, n_groups, q_t, ld_q, scale);
   if (!g.ok) return;
   const int c0 = strip * kTileCols;
   if (g.ohi <= g.olo) {   // the scale of an empty group (no rows, no data)
     if (t < 64 && c0 + t < cols) g.s[c0 + t] = scale_from_amax(0.0f, CODEC);
     return;
   }
-  const int nch = cw_chunks(g.olo, g.ohi);
-  const int A = (g.olo & ~15) + g.j * kTileRows;          // output row of tile row 0
-  const int r_begin = max(A, g.olo), r_end = min(A + kTileRows, g.ohi);
+  const int nch = cw_chunks<CR>(g.olo, g.ohi);
+  const int A = (g.olo & ~15) + g.j * CR;                  // output row of tile row 0
+  const int r_begin = max(A, g.olo), r_end = min(A + CR, g.ohi);
   const int col = c0 + cc * 8;
   const bool col_ok = col < cols;
 
-  u32x4 v[kCwIters][4];
+  u32x4 v[kIters][4];
   uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < kCwIters; ++i) {
+  for (int i = 0; i < kIters; ++i) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = A + 128 * i + 4 * rs + k;
@@ -340,22 +344,23 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
 #pragma unroll
   for (int k = 0; k < 8; ++k) sc[k] = s_scale[cc * 8 + k];
 #pragma unroll
-  for (int i = 0; i < kCwIters; ++i) {
+  for (int i = 0; i < kIters; ++i) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t w = quant4<CODEC>(col_of(v[i][0], k), col_of(v[i][1], k), col_of(v[i][2], k),
                                        col_of(v[i][3], k), sc[k]);
-      tile_put4(tile, cc * 8 + k, 128 * i + 4 * rs, w);
+      *reinterpret_cast<uint32_t*>(tile + tile_off_r<CR>(cc * 8 + k, 128 * i + 4 * rs)) = w;
     }
   }
   __syncthreads();
-  // transposed store: each pass writes 8 columns x 32 segments of 16 rows
+  // transposed store: each pass writes 256 / (CR / 16) columns x CR / 16 segments of 16 rows
+  constexpr int kSegs = CR / 16, kColsPerPass = 256 / kSegs;
 #pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    const int ci = pp * 8 + (t >> 5), sg = t & 31;
+  for (int pp = 0; pp < kTileCols / kColsPerPass; ++pp) {
+    const int ci = pp * kColsPerPass + t / kSegs, sg = t % kSegs;
     const int c = c0 + ci, R0 = A + 16 * sg;
     if (c < cols && R0 < r_end && R0 + 16 > r_begin) {
-      const u32x4 d = tile_get16(tile, ci, 16 * sg);
+      const u32x4 d = *reinterpret_cast<const u32x4*>(tile + tile_off_r<CR>(ci, 16 * sg));
       store_segment(g.q + (int64_t)c * ld_q + R0, R0, r_begin, r_end, d);
     }
   }
@@ -368,16 +373,27 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
 // reset is an ordinary kernel and which keeps no state between launches.
 static std::atomic<uint32_t> g_generation{0};
 static std::atomic<int> g_poll_budget{kPolls};
+static std::atomic<int> g_chunk_rows{0};   // 0: chosen per call; 128 or 512: forced (a test hook)
 static uint32_t next_generation() {
   uint32_t g = g_generation.fetch_add(1) + 1;
   if (g == 0) g = g_generation.fetch_add(1) + 1;
   return g;
 }
 
-int64_t colwise_units_bound(int64_t batch, int64_t rows, const int32_t* offs, int32_t n_groups) {
-  if (offs) return (rows + 16LL * n_groups + kTileRows - 1) / kTileRows + n_groups;
-  const int64_t upb = rows > 0 ? (rows + kTileRows - 1) / kTileRows : 1;
+int64_t colwise_units_bound(int64_t batch, int64_t rows, const int32_t* offs, int32_t n_groups,
+                            int64_t cr = kTileRows) {
+  if (offs) return (rows + 16LL * n_groups + cr - 1) / cr + n_groups;
+  const int64_t upb = rows > 0 ? (rows + cr - 1) / cr : 1;
   return batch * upb;
+}
+
+// Chunk height of a single-pass call: 128 rows when its groups (or batch items)
+// average at most 512 rows (a 512-row chunk of a short group is mostly
+// padding), else 512; a forced height from the test hook wins.
+static int colwise_chunk_rows(int64_t rows, int64_t groups) {
+  const int forced = g_chunk_rows.load();
+  if (forced == 128 || forced == kTileRows) return forced;
+  return rows <= 512 * std::max<int64_t>(groups, 1) ? 128 : kTileRows;
 }
 
 template <int CODEC, bool GROUPED>
@@ -387,19 +403,25 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
   const int64_t n_scale = (GROUPED ? n_groups : batch) * cols;
   if (n_scale == 0) return hipSuccess;
   const int n_strips = (int)((cols + kTileCols - 1) / kTileCols);
-  const int64_t units = colwise_units_bound(batch, rows, offs, n_groups);
-  const int64_t items = units * n_strips;
-  // most chunks one group can span: a grouped group may start 15 rows past a 16-row anchor
-  const int64_t nch_bound = ((GROUPED ? rows + 15 : rows) + kTileRows - 1) / kTileRows;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cap) != hipSuccess) return hipGetLastError();
   const bool capturing = cap != hipStreamCaptureStatusNone;
-  if (!capturing && nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
-    hipLaunchKernelGGL((colwise_single_kernel<CODEC, GROUPED>), dim3((unsigned)items), dim3(256), 0, st, x,
-                       batch, (int)rows, (int)cols, offs, n_groups, q_t, ld_q, scale, (int)units,
-                       next_generation(), g_poll_budget.load());
-    return hipGetLastError();
+  // the single pass, at the chosen chunk height or else at 512 rows
+  const int pref = colwise_chunk_rows(rows, GROUPED ? n_groups : 1);
+  for (int cr : {pref, kTileRows}) {
+    const int64_t units = colwise_units_bound(batch, rows, offs, n_groups, cr);
+    const int64_t items = units * n_strips;
+    // most chunks one group can span: a grouped group may start 15 rows past a 16-row anchor
+    const int64_t nch_bound = ((GROUPED ? rows + 15 : rows) + cr - 1) / cr;
+    if (!capturing && nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
+      auto k = cr == 128 ? colwise_single_kernel<CODEC, GROUPED, 128> : colwise_single_kernel<CODEC, GROUPED, kTileRows>;
+      hipLaunchKernelGGL(k, dim3((unsigned)items), dim3(256), 0, st, x, batch, (int)rows, (int)cols, offs, n_groups,
+                         q_t, ld_q, scale, (int)units, next_generation(), g_poll_budget.load());
+      return hipGetLastError();
+    }
+    if (cr == kTileRows) break;
   }
+  const int64_t units = colwise_units_bound(batch, rows, offs, n_groups);
   hipLaunchKernelGGL(colwise_reset_kernel, dim3((unsigned)((n_scale + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint32_t*>(scale), n_scale);
   const dim3 grid((unsigned)(units * n_strips));
@@ -411,6 +433,8 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
 }
 
 int set_colwise_poll_budget(int polls) { return g_poll_budget.exchange(polls < 0 ? kPolls : polls); }
+
+int set_colwise_chunk_rows(int rows) { return g_chunk_rows.exchange(rows == 128 || rows == kTileRows ? rows : 0); }
 
 hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                    const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,

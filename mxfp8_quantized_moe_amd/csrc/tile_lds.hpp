@@ -29,6 +29,20 @@ __device__ __forceinline__ int tile_off(int c, int r) {
   return c * kTileRows + ((((r >> 4) ^ (2 * (c >> 3))) & 31) << 4) + (r & 15);
 }
 
+// The same layout for a tile of TR rows (TR / 16 segments per column).  For
+// TR = 128 the segment is XOR-ed with the 8-column slice index (8 values over
+// 8 segments), which keeps a wave's 4-row writes of one slice column on 32
+// distinct banks and a quarter-wave's 16-byte reads (two columns) on all 64.
+template <int TR>
+__device__ __forceinline__ int tile_off_r(int c, int r) {
+  if constexpr (TR == kTileRows) {
+    return tile_off(c, r);
+  } else {
+    static_assert(TR == 128, "tile heights: 512 or 128 rows");
+    return c * TR + ((((r >> 4) ^ (c >> 3)) & 7) << 4) + (r & 15);
+  }
+}
+
 // Codes of 4 consecutive rows (r..r+3, r % 4 == 0) of one column.
 __device__ __forceinline__ void tile_put4(uint8_t* tile, int c, int r, uint32_t word) {
   *reinterpret_cast<uint32_t*>(tile + tile_off(c, r)) = word;

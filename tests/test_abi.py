@@ -372,6 +372,18 @@ def test_colwise_poll_budget_hook(lib):
         f(first)
 
 
+def test_colwise_chunk_rows_hook(lib):
+    """Host-only tuning hook: 128 or 512 force a chunk height, anything else selects per call (0)."""
+    f = lib.fp8moe_set_colwise_chunk_rows
+    first = f(128)
+    try:
+        assert f(512) == 128
+        assert f(300) == 512
+        assert f(0) == 0
+    finally:
+        f(first)
+
+
 def test_route_noalloc_rejections(lib):
     """Host-side checks of the allocation-free routing (no HIP call is reached)."""
     r = lib.moe_route_noalloc   # (ids, tokens, topk, E, pad, counts, offs, dest, src, stream)

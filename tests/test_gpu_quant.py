@@ -96,13 +96,22 @@ GROUP_CASES = {
 }
 
 
+@pytest.fixture(params=[0, 128, 512], ids=["chunks_auto", "chunks128", "chunks512"])
+def chunk_rows(request):
+    """The single-pass colwise chunk height: chosen per call, or forced to 128 or 512 rows."""
+    f = fm._lib.lib().fp8moe_set_colwise_chunk_rows
+    prev = f(request.param)
+    yield request.param
+    f(prev)
+
+
 @pytest.mark.parametrize("codec", CODECS)
 @pytest.mark.parametrize("case", list(GROUP_CASES))
-def test_colwise_grouped_parity(codec, case):
+def test_colwise_grouped_parity(codec, case, chunk_rows):
     M, C, offs = GROUP_CASES[case]
     x = special_input(2000 + M, (M, C))
     ld_q = (M + 16 + 15) // 16 * 16
-    note(f"colwise grouped codec={codec} case={case}")
+    note(f"colwise grouped codec={codec} case={case} chunk rows={chunk_rows}")
     q_t = filled_u8((C, ld_q))
     sc = filled_f32((len(offs), C))
     fm.quantize_colwise(bf16_dev(x), i32_dev(offs), codec, q_t=q_t, scale=sc, ld_q=ld_q)
@@ -115,11 +124,11 @@ def test_colwise_grouped_parity(codec, case):
 @pytest.mark.parametrize("codec", CODECS)
 @pytest.mark.parametrize("shape", [(3, 700, 72), (4, 100, 64), (2, 1, 8), (1, 1030, 136),
                                    (2, 4096, 72), (2, 4097, 72), (5, 1536, 200), (1, 65600, 16)])
-def test_colwise_batched_parity(codec, shape):
+def test_colwise_batched_parity(codec, shape, chunk_rows):
     x = special_input(3000 + sum(shape), shape)
     B, R, C = shape
     ld_q = (R + 15) // 16 * 16 + 16
-    note(f"colwise batched codec={codec} shape={shape}")
+    note(f"colwise batched codec={codec} shape={shape} chunk rows={chunk_rows}")
     q_t = filled_u8((B, C, ld_q))
     sc = filled_f32((B, C))
     fm.quantize_colwise(bf16_dev(x), None, codec, q_t=q_t, scale=sc, ld_q=ld_q)
@@ -493,7 +502,7 @@ def test_mx_all_subnormal_blocks(rule):
 
 
 @pytest.mark.parametrize("codec", CODECS)
-def test_colwise_wait_fallback_bit_exact(codec):
+def test_colwise_wait_fallback_bit_exact(codec, chunk_rows):
     """With a poll budget of 0 every chunk of a multi-chunk group recomputes its group's column
     maxima from x (the path a chunk takes when its peers do not publish in time); every kernel
     still exits normally and the result is the same, bit for bit."""
