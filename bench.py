@@ -295,14 +295,20 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                      spec=dict(op="permute_rowwise", src="X", topk=k, rsrc=r_src, xg=xg, q=qx, s=sx))
             qw1, sw1 = q_row("q_row W1", "W1", W1d, E * F2, H)
             h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H)
-        a2 = bf(rows, F)
         if w.mx:
-            step.add("swiglu", "moe", lambda: fm.swiglu_quantize_rowwise(h1, 0, a2=a2, codes=False),
-                     2 * rows * F2 + 2 * rows * F, spec=dict(op="swiglu", h1=h1, F=F, a2=a2, q=None, s=None))
-            qa2, sa2, qa2t, sa2t = mx_dual_g("mx A2 (both forms)", a2, lambda: a2, rows, F)
+            # SwiGLU computed inside the quantizer: A2 itself never goes to memory
+            qa2, sa2 = u8(rows, F), u8(*fm.mx_k4_shape(rows, F // 32))
+            qa2t, sa2t = u8(F, Mp), u8(*fm.mx_k4_shape(F, Mp // 32))
+            step.add("swiglu+mx A2 (both forms)", "quant",
+                     lambda: fm.swiglu_quantize_mx_dual(h1, offs, rule=rule, rows_pad=Mp, q=qa2, scale=sa2, q_t=qa2t,
+                                                        scale_t=sa2t, offs_pad=op, layout=K4),
+                     2 * rows * F2 + 2 * rows * F + 2 * (rows * F // 32),
+                     spec=dict(op="swiglu_mx", h1=h1, da2=None, F=F, offs=offs_np, rows_pad=Mp, rule=rule, q=qa2,
+                               s=sa2, qt=qa2t, st=sa2t, offs_pad=op))
             qw2, sw2, qw2t, sw2t = mx_dual_b("mx W2 (both forms)", "W2", W2d, E, H, F)
             yg = g_m("gemm fwd W2", qa2, sa2, qw2, sw2, rows, H, F, sk=fm.SCALE_E8M0_K4)
         else:
+            a2 = bf(rows, F)
             qa2, sa2 = u8(rows, F), f32(rows)
             step.add("swiglu+q", "moe", lambda: fm.swiglu_quantize_rowwise(h1, 0, a2=a2, q=qa2, scale=sa2),
                      2 * rows * F2 + 3 * rows * F + 4 * rows,
@@ -337,16 +343,20 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
             qdyt, sdyt, ld = q_col_grouped("q_col dYg", dyg, lambda: dyg, rows, H)
             qa2t, sa2t, _ = q_col_grouped("q_col A2", a2, lambda: a2, rows, F)
             g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, ld, H, F)
-        dh1 = bf(rows, F2)
         if w.mx:
-            step.add("swiglu bwd", "moe",
-                     lambda: fm.swiglu_backward_quantize_rowwise(da2, h1, 0, dh1=dh1, codes=False),
-                     2 * rows * F + 4 * rows * F2, spec=dict(op="swiglu_bwd", da2=da2, h1=h1, F=F, dh1=dh1, q=None,
-                                                            s=None))
-            qdh, sdh, qdht, sdht = mx_dual_g("mx dH1 (both forms)", dh1, lambda: dh1, rows, F2)
+            qdh, sdh = u8(rows, F2), u8(*fm.mx_k4_shape(rows, F2 // 32))
+            qdht, sdht = u8(F2, Mp), u8(*fm.mx_k4_shape(F2, Mp // 32))
+            step.add("swiglu bwd+mx dH1 (both forms)", "quant",
+                     lambda: fm.swiglu_backward_quantize_mx_dual(da2, h1, offs, rule=rule, rows_pad=Mp, q=qdh,
+                                                                 scale=sdh, q_t=qdht, scale_t=sdht, offs_pad=op,
+                                                                 layout=K4),
+                     2 * rows * F + 2 * rows * F2 + 2 * rows * F2 + 2 * (rows * F2 // 32),
+                     spec=dict(op="swiglu_mx", h1=h1, da2=da2, F=F, offs=offs_np, rows_pad=Mp, rule=rule, q=qdh,
+                               s=sdh, qt=qdht, st=sdht, offs_pad=op))
             dxg = g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, rows, H, F2, sk=fm.SCALE_E8M0_K4)
             g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, Mp, F2, H, sk=fm.SCALE_E8M0_K4, offs_t=op)
         else:
+            dh1 = bf(rows, F2)
             qdh, sdh = u8(rows, F2), f32(rows)
             step.add("swiglu bwd+q", "moe",
                      lambda: fm.swiglu_backward_quantize_rowwise(da2, h1, 0, dh1=dh1, q=qdh, scale=sdh),
@@ -360,7 +370,7 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
         dx = bf(T, H)
         step.add("combine dX", "moe", lambda: fm.moe_combine(dxg, r_dest, None, k, y=dx), 2 * S * H + 2 * T * H + 4 * S,
                  spec=dict(op="combine", yg=dxg, dest=r_dest, w=None, topk=k, out=dx))
-        step.outputs = dict(y=y, dx=dx, dw=dw, xg=xg, h1=h1, a2=a2, yg=yg, dyg=dyg, da2=da2, dh1=dh1, dxg=dxg,
+        step.outputs = dict(y=y, dx=dx, dw=dw, xg=xg, h1=h1, yg=yg, dyg=dyg, da2=da2, dxg=dxg,
                             route=(r_counts, r_offs, r_dest, r_src))
         return step, host
 
@@ -626,6 +636,18 @@ def cpu_baseline(step, host: dict):
                 t_l = timed(lambda: oracle.quantize_mx_lastdim(x.reshape(B * R, C)[:r], sp["rule"]), 1) * (B * R / r)
                 t_r = timed(lambda: oracle.quantize_mx_rows_batched(xs, sp["rule"]), 1) * (C / c)
             add(name, t_l + t_r, 1.0)
+        elif op == "swiglu_mx":
+            h1 = src(sp["h1"])
+            R, F = h1.shape[0], sp["F"]
+            C = F if sp["da2"] is None else 2 * F
+            r = max(1, min(R, QS // max(C, 1)))
+            if sp["da2"] is None:
+                t_r = timed(lambda: oracle.quantize_mx_lastdim(o_swiglu.swiglu_fwd(h1[:r], F), sp["rule"]), 1)
+            else:
+                da2 = src(sp["da2"])
+                t_r = timed(lambda: oracle.quantize_mx_lastdim(o_swiglu.swiglu_bwd(da2[:r], h1[:r], F), sp["rule"]), 1)
+            # the row-block form costs what the last-dim form does per element (one more pass over the tensor)
+            add(name, 2.0 * t_r, R / r)
         elif op == "route":
             ids = host[sp["ids"]]
             add(name, timed(lambda: o_route.route(ids, sp["E"], sp["pad"]), 1), 1.0)

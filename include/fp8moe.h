@@ -523,6 +523,46 @@ int quantize_mx_dual(const void *x_bf16, int64_t batch, int64_t rows, int64_t co
                      void *scale_e8m0, void *q_t, void *scale_t_e8m0, int64_t rows_pad,
                      int32_t *offs_pad_out, void *stream);
 
+/*
+ * swiglu_quantize_mx_dual -- the SwiGLU between the two expert GEMMs fused with
+ * both MXFP8 forms of its output (the W2 forward operand and the W2 wgrad
+ * operand): A2 = bf16(silu(gate) * up) is computed from W1's output as
+ * swiglu_quantize_rowwise computes it and quantized as quantize_mx_dual(A2)
+ * would, without A2 ever going to memory.
+ *   [P1 Details and P4 "Три уровня оптимизации Triton-ядер": quantization
+ *   fused into the kernel that produces the tensor; P2 Details: MXFP8 operands
+ *   blocked along each GEMM's contraction dimension.]
+ *   h1      bf16 [rows][ld_h1]  gate in columns [0, F), up in [F, 2F)
+ *   a2      bf16 [rows][F]      optional copy of A2 (NULL: not written)
+ *   q, scale_e8m0, q_t, scale_t_e8m0, offs, n_groups, rows_pad, offs_pad_out,
+ *   rule, scale_layout: as quantize_mx_dual of A2 ([rows][F], so with offs
+ *   only the rows inside groups get last-dim codes).
+ *   Requires: F % 32 == 0; ld_h1 >= 2F, ld_h1 % 8 == 0; h1, a2 and q 16-byte
+ *   aligned; the rest as quantize_mx_dual.  One kernel, no allocation.
+ */
+int swiglu_quantize_mx_dual(const void *h1_bf16, int64_t rows, int64_t F, int64_t ld_h1,
+                            const int32_t *offs, int32_t n_groups, int rule, int scale_layout,
+                            void *a2_bf16, void *q, void *scale_e8m0, void *q_t, void *scale_t_e8m0,
+                            int64_t rows_pad, int32_t *offs_pad_out, void *stream);
+
+/*
+ * swiglu_backward_quantize_mx_dual -- SwiGLU's backward fused with both MXFP8
+ * forms of its result (the W1 dgrad operand and the W1 wgrad operand): dH1 =
+ * [d gate | d up] ([rows][2F]) as swiglu_backward_quantize_rowwise computes it,
+ * quantized as quantize_mx_dual(dH1) would, without dH1 going to memory.
+ *   [as swiglu_quantize_mx_dual]
+ *   da2     bf16 [rows][F]      gradient of A2
+ *   dh1     bf16 [rows][2F]     optional copy of dH1 (NULL: not written)
+ *   The rest as swiglu_quantize_mx_dual, for the [rows][2F] tensor dH1, except
+ *   that F % 128 == 0 (each work item evaluates the product rule once for 128
+ *   columns of F and emits the matching d gate and d up tiles).
+ */
+int swiglu_backward_quantize_mx_dual(const void *da2_bf16, const void *h1_bf16, int64_t rows,
+                                     int64_t F, int64_t ld_h1, const int32_t *offs, int32_t n_groups,
+                                     int rule, int scale_layout, void *dh1_bf16, void *q,
+                                     void *scale_e8m0, void *q_t, void *scale_t_e8m0, int64_t rows_pad,
+                                     int32_t *offs_pad_out, void *stream);
+
 /* Host-side allocation bound for quantize_mx's padded rows: round_up(rows + 31*n_groups, 32).
  * Returns -1 for negative arguments. */
 int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups);

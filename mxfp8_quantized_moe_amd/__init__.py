@@ -20,7 +20,8 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "grouped_mm_scaled", "encode_f32", "default_codec", "E4M3FN", "E4M3FNUZ", "MX_FLOOR_OCP",
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
-           "mx_k4_shape", "quantize_mx_dual", "Fp8MoeError", "swiglu_quantize_rowwise",
+           "mx_k4_shape", "quantize_mx_dual", "swiglu_quantize_mx_dual", "swiglu_backward_quantize_mx_dual",
+           "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_route_workspace_bytes", "moe_permute", "moe_combine",
            "moe_permute_rowwise", "moe_combine_backward",
            "quantize_tensorwise", "moe_permute_quantized", "quantize_blockwise", "grouped_mm_blockwise",
@@ -166,6 +167,57 @@ def quantize_mx_dual(x, offs=None, rule=MX_FLOOR_OCP, rows_pad=None, q=None, sca
                                      _ptr(scale_t), rp, _ptr(offs_pad), _stream(stream))
     _lib.check("quantize_mx_dual", st)
     return q, scale, q_t, scale_t, offs_pad
+
+
+def _mx_dual_outputs(R, C, offs, rows_pad, q, scale, q_t, scale_t, offs_pad, layout, dev):
+    k4 = layout == MX_LAYOUT_K4
+    E = offs.numel()
+    rp = rows_pad or quantize_mx_rows_bound(R, E)
+    sc_shape = lambda rows_major, n_rows, n_blocks: mx_k4_shape(n_rows, n_blocks) if k4 else rows_major
+    q = torch.empty((R, C), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty(sc_shape((R, C // 32), R, C // 32), dtype=torch.uint8, device=dev) if scale is None else scale
+    q_t = torch.empty((C, rp), dtype=torch.uint8, device=dev) if q_t is None else q_t
+    scale_t = torch.empty(sc_shape((C, rp // 32), C, rp // 32), dtype=torch.uint8, device=dev) \
+        if scale_t is None else scale_t
+    offs_pad = torch.empty((E,), dtype=torch.int32, device=dev) if offs_pad is None else offs_pad
+    return rp, q, scale, q_t, scale_t, offs_pad
+
+
+def swiglu_quantize_mx_dual(h1, offs, rule=MX_FLOOR_OCP, rows_pad=None, a2=None, q=None, scale=None, q_t=None,
+                            scale_t=None, offs_pad=None, layout=MX_LAYOUT_K4, stream=None):
+    """h1 [R, 2F] bf16 (gate | up), offs int32 [E] -> (a2 or None, q [R, F], scale, q_t [F, rows_pad], scale_t,
+    offs_pad): both MX forms of bf16(silu(gate) * up); a2 (bf16 [R, F]) is written only if passed."""
+    h1 = _bits(h1)
+    R, F2 = h1.shape
+    if F2 % 2 or (h1.numel() and h1.stride(1) != 1):
+        raise ValueError("swiglu_quantize_mx_dual needs an even column count and unit column stride")
+    F = F2 // 2
+    ld = h1.stride(0) if h1.numel() else F2
+    rp, q, scale, q_t, scale_t, offs_pad = _mx_dual_outputs(R, F, offs, rows_pad, q, scale, q_t, scale_t, offs_pad,
+                                                            layout, h1.device)
+    _lib.check("swiglu_quantize_mx_dual", _lib.lib().swiglu_quantize_mx_dual(
+        _ptr(h1), R, F, ld, _ptr(offs), offs.numel(), rule, layout, _ptr(a2), _ptr(q), _ptr(scale), _ptr(q_t),
+        _ptr(scale_t), rp, _ptr(offs_pad), _stream(stream)))
+    return a2, q, scale, q_t, scale_t, offs_pad
+
+
+def swiglu_backward_quantize_mx_dual(da2, h1, offs, rule=MX_FLOOR_OCP, rows_pad=None, dh1=None, q=None, scale=None,
+                                     q_t=None, scale_t=None, offs_pad=None, layout=MX_LAYOUT_K4, stream=None):
+    """da2 [R, F], h1 [R, 2F] bf16, offs int32 [E] -> (dh1 or None, q [R, 2F], scale, q_t [2F, rows_pad], scale_t,
+    offs_pad): both MX forms of SwiGLU's input gradient; dh1 (bf16 [R, 2F]) is written only if passed."""
+    h1 = _bits(h1)
+    da2 = _bits(da2).contiguous()
+    R, F2 = h1.shape
+    if F2 % 2 or (h1.numel() and h1.stride(1) != 1) or tuple(da2.shape) != (R, F2 // 2):
+        raise ValueError("swiglu_backward_quantize_mx_dual: h1 [R, 2F] with unit column stride, da2 [R, F]")
+    F = F2 // 2
+    ld = h1.stride(0) if h1.numel() else F2
+    rp, q, scale, q_t, scale_t, offs_pad = _mx_dual_outputs(R, F2, offs, rows_pad, q, scale, q_t, scale_t, offs_pad,
+                                                            layout, h1.device)
+    _lib.check("swiglu_backward_quantize_mx_dual", _lib.lib().swiglu_backward_quantize_mx_dual(
+        _ptr(da2), _ptr(h1), R, F, ld, _ptr(offs), offs.numel(), rule, layout, _ptr(dh1), _ptr(q), _ptr(scale),
+        _ptr(q_t), _ptr(scale_t), rp, _ptr(offs_pad), _stream(stream)))
+    return dh1, q, scale, q_t, scale_t, offs_pad
 
 
 def grouped_mm_scaled(mode, a, a_fmt, a_scale, b, b_fmt, b_scale, scale_kind, offs, n_groups, M, N, K,

@@ -234,6 +234,32 @@ int quantize_mx_dual(const void* x_bf16, int64_t batch, int64_t rows, int64_t co
                                                as_stream(stream)));
 }
 
+int swiglu_quantize_mx_dual(const void* h1_bf16, int64_t rows, int64_t F, int64_t ld_h1, const int32_t* offs,
+                            int32_t n_groups, int rule, int scale_layout, void* a2_bf16, void* q, void* scale_e8m0,
+                            void* q_t, void* scale_t_e8m0, int64_t rows_pad, int32_t* offs_pad_out, void* stream) {
+  const int st = check_swiglu_mx_dual(h1_bf16, nullptr, false, rows, F, ld_h1, offs, n_groups, rule, scale_layout,
+                                      a2_bf16, q, scale_e8m0, q_t, scale_t_e8m0, rows_pad, offs_pad_out);
+  if (st) return st;
+  return launch_status(launch_swiglu_mx_dual(
+      static_cast<const uint16_t*>(h1_bf16), nullptr, rows, F, ld_h1, offs, n_groups, rule, scale_layout,
+      static_cast<uint16_t*>(a2_bf16), static_cast<uint8_t*>(q), static_cast<uint8_t*>(scale_e8m0),
+      static_cast<uint8_t*>(q_t), static_cast<uint8_t*>(scale_t_e8m0), rows_pad, offs_pad_out, as_stream(stream)));
+}
+
+int swiglu_backward_quantize_mx_dual(const void* da2_bf16, const void* h1_bf16, int64_t rows, int64_t F,
+                                     int64_t ld_h1, const int32_t* offs, int32_t n_groups, int rule,
+                                     int scale_layout, void* dh1_bf16, void* q, void* scale_e8m0, void* q_t,
+                                     void* scale_t_e8m0, int64_t rows_pad, int32_t* offs_pad_out, void* stream) {
+  const int st = check_swiglu_mx_dual(h1_bf16, da2_bf16, true, rows, F, ld_h1, offs, n_groups, rule, scale_layout,
+                                      dh1_bf16, q, scale_e8m0, q_t, scale_t_e8m0, rows_pad, offs_pad_out);
+  if (st) return st;
+  return launch_status(launch_swiglu_mx_dual(
+      static_cast<const uint16_t*>(h1_bf16), static_cast<const uint16_t*>(da2_bf16), rows, F, ld_h1, offs, n_groups,
+      rule, scale_layout, static_cast<uint16_t*>(dh1_bf16), static_cast<uint8_t*>(q),
+      static_cast<uint8_t*>(scale_e8m0), static_cast<uint8_t*>(q_t), static_cast<uint8_t*>(scale_t_e8m0), rows_pad,
+      offs_pad_out, as_stream(stream)));
+}
+
 int64_t quantize_mx_rows_bound(int64_t rows, int32_t n_groups) { return mx_rows_bound(rows, n_groups); }
 
 int grouped_mm_scaled(int mode, const void* a, int a_fmt, const void* a_scale, const void* b, int b_fmt,
@@ -280,6 +306,6 @@ int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(p
 
 int fp8moe_set_colwise_chunk_rows(int rows) { return set_colwise_chunk_rows(rows); }
 
-int fp8moe_version(void) { return 105; }
+int fp8moe_version(void) { return 106; }
 
 }  // extern "C"

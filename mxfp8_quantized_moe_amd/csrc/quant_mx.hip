@@ -30,6 +30,7 @@
 // (up to the next multiple of four) written as 0.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "swiglu_common.hpp"
 #include "tile_lds.hpp"
 
 namespace fp8moe {
@@ -376,6 +377,50 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t batch, int64_t rows, in
 // met only in memory.
 constexpr int kDualRows = 128, kDualCols = 128;
 
+// Where the dual kernel's tensor comes from.  PROD 0: read as is.  PROD 1: the
+// SwiGLU output bf16(silu(gate) * up) computed from W1's output h1 (gate in
+// columns [0, F), up in [F, 2F)).  PROD 2: SwiGLU's input gradient [d gate |
+// d up] (2F columns) computed from dA2 and h1.  The tensor then never exists
+// in memory unless `out` asks for a bf16 copy.  Columns of a 16-column slice
+// never straddle F (F % 16 == 0).
+struct DualSrc {
+  const uint16_t* x;      // PROD 0: [rows][cols]
+  const uint16_t* h1;     // PROD 1, 2: [rows][ld_h1]
+  const uint16_t* da2;    // PROD 2: [rows][F]
+  int64_t ld_h1;
+  int F;
+  uint16_t* out;          // optional bf16 copy of the tensor, [rows][cols]
+};
+
+// The 16 columns [col, col + 16) of tensor row `row` (cols columns) as two 8-column chunks.
+template <int PROD>
+__device__ __forceinline__ void dual_load(const DualSrc& sr, int64_t row, int col, int cols, u32x4& v0, u32x4& v1) {
+  if constexpr (PROD == 0) {
+    const uint16_t* p = sr.x + row * cols + col;
+    v0 = *reinterpret_cast<const u32x4*>(p);
+    v1 = *reinterpret_cast<const u32x4*>(p + 8);
+  } else if constexpr (PROD == 1) {
+    const uint16_t* g = sr.h1 + row * sr.ld_h1 + col;
+    const u32x4 g0 = *reinterpret_cast<const u32x4*>(g), g1 = *reinterpret_cast<const u32x4*>(g + 8);
+    const u32x4 u0 = *reinterpret_cast<const u32x4*>(g + sr.F), u1 = *reinterpret_cast<const u32x4*>(g + sr.F + 8);
+    v0 = sw_fwd_chunk(g0, u0);
+    v1 = sw_fwd_chunk(g1, u1);
+  } else {
+    const bool up = col >= sr.F;
+    const int cf = up ? col - sr.F : col;
+    const uint16_t* d = sr.da2 + row * sr.F + cf;
+    const uint16_t* g = sr.h1 + row * sr.ld_h1 + cf;
+    const u32x4 d0 = *reinterpret_cast<const u32x4*>(d), d1 = *reinterpret_cast<const u32x4*>(d + 8);
+    const u32x4 g0 = *reinterpret_cast<const u32x4*>(g), g1 = *reinterpret_cast<const u32x4*>(g + 8);
+    const u32x4 u0 = *reinterpret_cast<const u32x4*>(g + sr.F), u1 = *reinterpret_cast<const u32x4*>(g + sr.F + 8);
+    u32x4 dg, du;
+    sw_bwd_chunk(d0, g0, u0, dg, du);
+    v0 = up ? du : dg;
+    sw_bwd_chunk(d1, g1, u1, dg, du);
+    v1 = up ? du : dg;
+  }
+}
+
 // Column c, row r of the codes tile: 8 segments of 16 rows per column, the
 // segment index XOR-ed with the 16-column slice so a wave's 4-row writes of
 // one slice column spread over 32 banks.
@@ -390,8 +435,8 @@ struct MxDualChunks {
   __device__ int operator()(int lo, int hi) const { return mx_dual_chunks(lo, hi); }
 };
 
-template <int RULE, bool GROUPED, bool K4>
-__global__ __launch_bounds__(256) void mx_dual_kernel(const uint16_t* __restrict__ x, int64_t batch, int rows,
+template <int RULE, bool GROUPED, bool K4, int PROD>
+__global__ __launch_bounds__(256) void mx_dual_kernel(DualSrc sr, int64_t batch, int rows,
                                                       int cols, const int32_t* __restrict__ offs, int n_groups,
                                                       uint8_t* __restrict__ ql, uint8_t* __restrict__ scl,
                                                       int64_t l_rows, uint8_t* __restrict__ q,
@@ -431,38 +476,59 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const uint16_t* __restrict
     ld_q = rows;
     qb = q + b * cols * (int64_t)rows;
     srow0 = b * cols; s_rows = batch * cols; s_nb = rows / 32;
-    x += b * (int64_t)rows * cols;
-    lrow0 = b * (int64_t)rows;
+    lrow0 = b * (int64_t)rows;                     // tensor rows of batch item b start here
   }
 
   const int A = plo + j * kDualRows;               // output row of tile row 0 (multiple of 32)
   const int r_end = min(A + kDualRows, phi);
+  // Items stride over the columns of the tensor, except for SwiGLU's backward, whose items stride
+  // over F and emit both the d gate tile (columns c0 ..) and the d up tile (F + c0 ..) of dH1 from one
+  // evaluation of the product rule (F % 128 == 0, so those tiles are whole).
+  const int cols_i = PROD == 2 ? sr.F : cols;
   const int c0 = strip * kDualCols;
   const int col = c0 + cc * 16;
-  const bool col_ok = col < cols;                  // cols % 32 == 0: a slice is wholly in or out
-  const bool full = c0 + kDualCols <= cols && A + kDualRows <= r_end && lo + (A + kDualRows - plo) <= hi;
-  u32x4 v[4][2];
-  if (full) {
-    const uint16_t* xr = x + (int64_t)(lo + A - plo + 4 * rs) * cols + col;
+  const bool col_ok = col < cols_i;                // cols % 32 == 0: a slice is wholly in or out
+  const bool full = c0 + kDualCols <= cols_i && A + kDualRows <= r_end && lo + (A + kDualRows - plo) <= hi;
+  u32x4 v[4][2], vu[PROD == 2 ? 4 : 1][2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k][0] = *reinterpret_cast<const u32x4*>(xr + (int64_t)k * cols);
-      v[k][1] = *reinterpret_cast<const u32x4*>(xr + (int64_t)k * cols + 8);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = A + 4 * rs + k, in = lo + (r - plo);
-      const bool ok = col_ok && r < r_end && in < hi;
-      const uint16_t* xr = x + (int64_t)in * cols + col;
-      v[k][0] = ok ? *reinterpret_cast<const u32x4*>(xr) : u32x4{0, 0, 0, 0};
-      v[k][1] = ok ? *reinterpret_cast<const u32x4*>(xr + 8) : u32x4{0, 0, 0, 0};
+  for (int k = 0; k < 4; ++k) {
+    const int r = A + 4 * rs + k, in = lo + (r - plo);
+    v[k][0] = v[k][1] = u32x4{0, 0, 0, 0};
+    if constexpr (PROD == 2) vu[k][0] = vu[k][1] = u32x4{0, 0, 0, 0};
+    if (full || (col_ok && r < r_end && in < hi)) {
+      if constexpr (PROD == 2) {
+        const int64_t row = lrow0 + in;
+        const uint16_t* d = sr.da2 + row * sr.F + col;
+        const uint16_t* g = sr.h1 + row * sr.ld_h1 + col;
+        const u32x4 d0 = *reinterpret_cast<const u32x4*>(d), d1 = *reinterpret_cast<const u32x4*>(d + 8);
+        const u32x4 g0 = *reinterpret_cast<const u32x4*>(g), g1 = *reinterpret_cast<const u32x4*>(g + 8);
+        const u32x4 u0 = *reinterpret_cast<const u32x4*>(g + sr.F), u1 = *reinterpret_cast<const u32x4*>(g + sr.F + 8);
+        sw_bwd_chunk(d0, g0, u0, v[k][0], vu[k][0]);
+        sw_bwd_chunk(d1, g1, u1, v[k][1], vu[k][1]);
+        if (sr.out != nullptr) {
+          uint16_t* o = sr.out + row * cols + col;
+          *reinterpret_cast<u32x4*>(o) = v[k][0];
+          *reinterpret_cast<u32x4*>(o + 8) = v[k][1];
+          *reinterpret_cast<u32x4*>(o + sr.F) = vu[k][0];
+          *reinterpret_cast<u32x4*>(o + sr.F + 8) = vu[k][1];
+        }
+      } else {
+        dual_load<PROD>(sr, lrow0 + in, col, cols, v[k][0], v[k][1]);
+        if (sr.out != nullptr) {
+          uint16_t* o = sr.out + (lrow0 + in) * cols + col;
+          *reinterpret_cast<u32x4*>(o) = v[k][0];
+          *reinterpret_cast<u32x4*>(o + 8) = v[k][1];
+        }
+      }
     }
   }
 
+  // Both MX forms of the 128 x 128 register tile `v`, whose column 0 is tensor column c0o.
+  auto emit = [&](const u32x4 (&v)[4][2], const int c0o) {
+  const int col = c0o + cc * 16;
   // last-dim blocks: per row, the 32 columns of lanes cc and cc ^ 1
   {
-    const int nb = cols >> 5, b0 = c0 >> 5;              // b0 % 4 == 0: a tile row is one K4 word
+    const int nb = cols >> 5, b0 = c0o >> 5;             // b0 % 4 == 0: a tile row is one K4 word
     const int nvalid = min(4, nb - b0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -540,13 +606,13 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int p = 0; p < kDualCols / 32; ++p) {
     const int ci = p * 32 + (t >> 3), sg = t & 7;
-    const int c = c0 + ci, R0 = A + 16 * sg;
+    const int c = c0o + ci, R0 = A + 16 * sg;
     const u32x4 d = *reinterpret_cast<const u32x4*>(tile + mx_dual_off(ci, 16 * sg));
     if (full || (c < cols && R0 < r_end)) *reinterpret_cast<u32x4*>(qb + (int64_t)c * ld_q + R0) = d;
   }
   // row-block scales: column t's (up to) four blocks of this item
   if (t < kDualCols) {
-    const int ci = t, c = c0 + ci;
+    const int ci = t, c = c0o + ci;
     const int nbt = (r_end - A) >> 5;
     if (c < cols) {
       const int64_t srow = srow0 + c;
@@ -569,20 +635,27 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const uint16_t* __restrict
       }
     }
   }
+  };
+
+  emit(v, c0);
+  if constexpr (PROD == 2) {
+    __syncthreads();   // the codes tile and the block exponents are reused
+    emit(vu, sr.F + c0);
+  }
 }
 
-template <int RULE>
-static hipError_t launch_dual(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
+template <int RULE, int PROD>
+static hipError_t launch_dual(const DualSrc& sr, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                               int32_t n_groups, bool k4, uint8_t* ql, uint8_t* scl, uint8_t* q, uint8_t* sc,
                               int64_t rows_pad, int32_t* offs_pad_out, dim3 grid, int n_strips, hipStream_t st) {
   const int64_t l_rows = batch * rows;
   if (offs) {
-    auto k = k4 ? mx_dual_kernel<RULE, true, true> : mx_dual_kernel<RULE, true, false>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, (int64_t)1, (int)rows, (int)cols, offs, n_groups, ql, scl,
+    auto k = k4 ? mx_dual_kernel<RULE, true, true, PROD> : mx_dual_kernel<RULE, true, false, PROD>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, sr, (int64_t)1, (int)rows, (int)cols, offs, n_groups, ql, scl,
                        l_rows, q, sc, rows_pad, offs_pad_out, n_strips);
   } else {
-    auto k = k4 ? mx_dual_kernel<RULE, false, true> : mx_dual_kernel<RULE, false, false>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, x, batch, (int)rows, (int)cols, nullptr, 0, ql, scl, l_rows, q,
+    auto k = k4 ? mx_dual_kernel<RULE, false, true, PROD> : mx_dual_kernel<RULE, false, false, PROD>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, st, sr, batch, (int)rows, (int)cols, nullptr, 0, ql, scl, l_rows, q,
                        sc, rows, nullptr, n_strips);
   }
   return hipGetLastError();
@@ -607,10 +680,35 @@ hipError_t launch_quantize_mx_dual(const uint16_t* x, int64_t batch, int64_t row
   const int64_t blocks = mx_dual_grid_bound(batch, rows, cols, offs != nullptr, n_groups, rows_pad);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
-  return rule == 0 ? launch_dual<0>(x, batch, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
-                                    offs_pad_out, grid, n_strips, st)
-                   : launch_dual<1>(x, batch, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
-                                    offs_pad_out, grid, n_strips, st);
+  const DualSrc sr{x, nullptr, nullptr, 0, 0, nullptr};
+  return rule == 0 ? launch_dual<0, 0>(sr, batch, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                       offs_pad_out, grid, n_strips, st)
+                   : launch_dual<1, 0>(sr, batch, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                       offs_pad_out, grid, n_strips, st);
+}
+
+hipError_t launch_swiglu_mx_dual(const uint16_t* h1, const uint16_t* da2, int64_t rows, int64_t F, int64_t ld_h1,
+                                 const int32_t* offs, int32_t n_groups, int rule, int scale_layout, uint16_t* out,
+                                 uint8_t* q, uint8_t* sc, uint8_t* q_t, uint8_t* sc_t, int64_t rows_pad,
+                                 int32_t* offs_pad_out, hipStream_t st) {
+  const bool k4 = scale_layout == 1, bwd = da2 != nullptr;
+  const int64_t cols = bwd ? 2 * F : F;
+  if (cols == 0 && offs_pad_out == nullptr) return hipSuccess;
+  const int64_t cols_i = bwd ? F : cols;   // the backward's items stride over F (two output tiles each)
+  const int n_strips = (int)std::max<int64_t>((cols_i + kDualCols - 1) / kDualCols, 1);
+  const int64_t blocks = mx_dual_grid_bound(1, rows, cols_i, offs != nullptr, n_groups, rows_pad);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
+  const DualSrc sr{nullptr, h1, da2, ld_h1, (int)F, out};
+  if (bwd)
+    return rule == 0 ? launch_dual<0, 2>(sr, 1, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                         offs_pad_out, grid, n_strips, st)
+                     : launch_dual<1, 2>(sr, 1, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                         offs_pad_out, grid, n_strips, st);
+  return rule == 0 ? launch_dual<0, 1>(sr, 1, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                       offs_pad_out, grid, n_strips, st)
+                   : launch_dual<1, 1>(sr, 1, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
+                                       offs_pad_out, grid, n_strips, st);
 }
 
 }  // namespace fp8moe

@@ -117,6 +117,23 @@ int check_quantize_mx_dual(const void* x, int64_t batch, int64_t rows, int64_t c
   return FP8MOE_OK;
 }
 
+int check_swiglu_mx_dual(const void* h1, const void* da2, bool backward, int64_t rows, int64_t F, int64_t ld_h1,
+                         const int32_t* offs, int32_t n_groups, int rule, int scale_layout, const void* out,
+                         const void* q, const void* sc, const void* q_t, const void* sc_t, int64_t rows_pad,
+                         const int32_t* offs_pad_out) {
+  if (rows < 0 || F < 0 || F > kI32Max / 4 || ld_h1 < 2 * F || mul(rows, ld_h1) < 0) return FP8MOE_ERR_SHAPE;
+  const int64_t cols = backward ? 2 * F : F;
+  // the tensor the MX forms are taken of: its shape, pointer and alignment stand in for x
+  const int st = check_quantize_mx_dual(rows && cols ? h1 : nullptr, 1, rows, cols, offs, n_groups, rule,
+                                        scale_layout, q, sc, q_t, sc_t, rows_pad, offs_pad_out);
+  if (st) return st;
+  const int64_t n = mul(rows, F);
+  if (!need(h1, n) || (backward && !need(da2, n))) return FP8MOE_ERR_NULL;
+  if (F % (backward ? 128 : 32) || ld_h1 % 8 || !aligned(h1, 16) || !aligned(da2, 16) || !aligned(out, 16))
+    return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_grouped_mm(int mode, const void* a, int a_fmt, const void* sa, const void* b, int b_fmt,
                      const void* sb, int scale_kind, const int32_t* offs, int32_t n_groups, int64_t M,
                      int64_t N, int64_t K, const void* out, int out_dtype) {

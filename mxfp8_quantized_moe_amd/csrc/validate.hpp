@@ -16,6 +16,10 @@ int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, 
 int check_quantize_mx_dual(const void* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                            int32_t n_groups, int rule, int scale_layout, const void* q, const void* sc,
                            const void* q_t, const void* sc_t, int64_t rows_pad, const int32_t* offs_pad_out);
+int check_swiglu_mx_dual(const void* h1, const void* da2, bool backward, int64_t rows, int64_t F, int64_t ld_h1,
+                         const int32_t* offs, int32_t n_groups, int rule, int scale_layout, const void* out,
+                         const void* q, const void* sc, const void* q_t, const void* sc_t, int64_t rows_pad,
+                         const int32_t* offs_pad_out);
 // Bytes of an e8m0 scale matrix of `rows` rows and `nb` 32-blocks per row in
 // the K4 layout (nb rounded up to whole 128-wide stages), or -1 on overflow.
 int64_t mx_k4_bytes(int64_t rows, int64_t nb);

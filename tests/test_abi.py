@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 9):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 105
+    assert lib.fp8moe_version() == 106
 
 
 def test_rows_bound(lib):
@@ -307,6 +307,38 @@ def test_mx_dual_rejections(lib):
     assert d(MIS, 1, 64, 64, None, 0, 0, 0, P, P, P, P, 64, None, None) == L.ERR_ALIGN
     assert d(P, 1, 64, 64, None, 0, 0, 0, MIS, P, P, P, 64, None, None) == L.ERR_ALIGN
     assert d(P, 1, 64, 64, None, 0, 0, 0, P, P, MIS, P, 64, None, None) == L.ERR_ALIGN
+
+
+def test_swiglu_mx_dual_rejections(lib):
+    f = lib.swiglu_quantize_mx_dual
+    # (h1, rows, F, ld_h1, offs, n_groups, rule, layout, a2, q, sc, q_t, sc_t, rows_pad, offs_pad, stream)
+    ok = [P, 64, 64, 128, P, 4, 0, 1, None, P, P, P, P, 64 + 128, P, None]
+    def call(fn, args, i=None, v=None):
+        a = list(args)
+        if i is not None:
+            a[i] = v
+        return fn(*a)
+    assert call(f, ok, 6, 5) == L.ERR_ENUM                 # rule
+    assert call(f, ok, 7, 2) == L.ERR_ENUM                 # scale layout
+    assert call(f, ok, 3, 100) == L.ERR_SHAPE              # ld_h1 < 2F
+    assert call(f, ok, 1, -1) == L.ERR_SHAPE
+    assert call(f, ok, 13, 64) == L.ERR_SHAPE              # rows_pad below the bound
+    assert call(f, ok, 0, None) == L.ERR_NULL
+    assert call(f, ok, 9, None) == L.ERR_NULL
+    assert call(f, ok, 11, None) == L.ERR_NULL
+    assert call(f, ok, 2, 48) == L.ERR_ALIGN               # F % 32
+    assert call(f, ok, 3, 132) == L.ERR_ALIGN              # ld_h1 % 8
+    assert call(f, ok, 0, MIS) == L.ERR_ALIGN
+    assert call(f, ok, 8, MIS) == L.ERR_ALIGN              # the optional bf16 copy
+    b = lib.swiglu_backward_quantize_mx_dual
+    okb = [P, P, 64, 128, 256, P, 4, 0, 1, None, P, P, P, P, 64 + 128, P, None]
+    assert call(b, okb, 7, 5) == L.ERR_ENUM
+    assert call(b, okb, 4, 200) == L.ERR_SHAPE
+    assert call(b, okb, 0, None) == L.ERR_NULL             # da2
+    assert call(b, okb, 1, None) == L.ERR_NULL             # h1
+    assert call(b, okb, 3, 48) == L.ERR_ALIGN
+    assert call(b, [P, P, 64, 96, 192, P, 4, 0, 1, None, P, P, P, P, 192, P, None]) == L.ERR_ALIGN   # F % 128
+    assert call(b, okb, 0, MIS) == L.ERR_ALIGN
 
 
 def test_gemm_rejections(lib):

@@ -57,10 +57,9 @@ LAYER = {
     3: ["route", "permute+q X", "q_row W1", "gemm fwd W1", "swiglu+q", "q_row W2", "gemm fwd W2", "combine",
         "combine bwd+q", "q_col W2", "gemm dgrad W2", "q_col dYg", "q_col A2", "gemm wgrad W2", "swiglu bwd+q",
         "q_col W1", "gemm dgrad W1", "q_col dH1", "q_col Xg", "gemm wgrad W1", "combine dX"],
-    5: ["route", "permute X", "mx Xg (both forms)", "mx W1 (both forms)", "gemm fwd W1", "swiglu",
-        "mx A2 (both forms)", "mx W2 (both forms)", "gemm fwd W2", "combine", "combine bwd", "mx dYg (both forms)",
-        "gemm dgrad W2", "gemm wgrad W2", "swiglu bwd", "mx dH1 (both forms)", "gemm dgrad W1", "gemm wgrad W1",
-        "combine dX"],
+    5: ["route", "permute X", "mx Xg (both forms)", "mx W1 (both forms)", "gemm fwd W1", "swiglu+mx A2 (both forms)",
+        "mx W2 (both forms)", "gemm fwd W2", "combine", "combine bwd", "mx dYg (both forms)", "gemm dgrad W2",
+        "gemm wgrad W2", "swiglu bwd+mx dH1 (both forms)", "gemm dgrad W1", "gemm wgrad W1", "combine dX"],
 }
 LAYER[4] = LAYER[3]
 # (workload, variant): the experts-only steps of configs 3-5 and the whole MoE layer
@@ -236,6 +235,36 @@ def check_mx_dual(sp, hst, phase):
         check_mx_rows_b(dict(src=sp["src"], shape=sp["shape"], rule=sp["rule"], q=sp["qt"], s=sp["st"]), hst, phase)
 
 
+def check_swiglu_mx(sp, hst, phase):
+    """SwiGLU (or its backward) fused with both MX forms: the launch's outputs equal those of the same entry
+    point asked to also write the bf16 tensor it quantizes, and that tensor is checked against the oracle
+    (within one bf16 ulp on sampled rows, then both MX forms bit-exact against the oracle's quantizers of it)."""
+    h1 = sp["h1"]
+    offs_d = torch.from_numpy(np.asarray(sp["offs"], np.int32)).to(h1.device)
+    F = sp["F"]
+    R = h1.shape[0]
+    C = F if sp["da2"] is None else 2 * F
+    copy = torch.empty(R, C, dtype=torch.bfloat16, device=h1.device)
+    if sp["da2"] is None:
+        r = fm.swiglu_quantize_mx_dual(h1, offs_d, rule=sp["rule"], rows_pad=sp["rows_pad"], a2=copy)
+    else:
+        r = fm.swiglu_backward_quantize_mx_dual(sp["da2"], h1, offs_d, rule=sp["rule"], rows_pad=sp["rows_pad"],
+                                                dh1=copy)
+    for got, want, what in zip((sp["q"], sp["s"], sp["qt"], sp["st"], sp["offs_pad"]), r[1:],
+                               ("last-dim codes", "last-dim e8m0", "row-block codes", "row-block e8m0",
+                                "padded offsets")):
+        assert torch.equal(got, want), f"{what} differ from the run that writes the bf16 tensor"
+    rows = _strided(R, phase)[::4]
+    h1h = _src(hst, h1)[rows]
+    t = host(copy)
+    ref = o_swiglu.swiglu_fwd(h1h, F) if sp["da2"] is None else o_swiglu.swiglu_bwd(_src(hst, sp["da2"])[rows], h1h, F)
+    assert_within_one_ulp(t[rows], ref, "bf16 tensor")
+    _DEV_CACHE[id(copy)] = t
+    check_mx_dual(dict(src=copy, shape=(R, C), offs=sp["offs"], rows_pad=sp["rows_pad"], rule=sp["rule"],
+                       q=sp["q"], s=sp["s"], qt=sp["qt"], st=sp["st"], offs_pad=sp["offs_pad"]), hst, phase)
+    del _DEV_CACHE[id(copy)]
+
+
 # ------------------------------------------------------------------ GEMM checks
 
 def _mx(sp):
@@ -408,7 +437,7 @@ def check_combine_bwd(sp, hst, phase):
 CHECKS = {"q_row": check_q_row, "q_col_grouped": check_q_col_grouped, "q_col_batched": check_q_col_batched,
           "mx_last": check_mx_last, "mx_rows_b": check_mx_rows_b, "mx_rows_g": check_mx_rows_g,
           "g_m": check_g_m, "g_k": check_g_k, "g_k_bf16": check_g_k_bf16,
-          "mx_dual": check_mx_dual, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
+          "mx_dual": check_mx_dual, "swiglu_mx": check_swiglu_mx, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
           "swiglu": check_swiglu, "swiglu_bwd": check_swiglu_bwd, "combine": check_combine,
           "combine_bwd": check_combine_bwd}
 

@@ -17,7 +17,7 @@ import torch
 import mxfp8_quantized_moe_amd as fm
 import oracle
 from oracle import swiglu as sw
-from gpu_helpers import (DEV, note, bf16_dev, host, assert_bytes_equal, assert_f32_bits_equal,
+from gpu_helpers import (DEV, note, bf16_dev, i32_dev, host, assert_bytes_equal, assert_f32_bits_equal,
                          assert_within_one_ulp)
 
 pytestmark = pytest.mark.gpu
@@ -131,3 +131,105 @@ def test_swiglu_full_size_sampled():
     qr, sr = oracle.quantize_rowwise(dh1h, fm.E4M3FN)
     assert_bytes_equal(host(qb)[rows], qr, "dh1 codes sampled")
     assert_f32_bits_equal(host(sb)[rows], sr, "dh1 scales sampled")
+
+
+# ----------------------------------------------------------- SwiGLU fused with both MX forms
+
+def _k4_rows(k4, R, NB):
+    G = k4.shape[0]
+    return np.ascontiguousarray(k4.transpose(1, 0, 2).reshape(R, 4 * G)[:, :NB])
+
+
+def _check_mx_forms(t_bits, offs, rule, rows_pad, q, sc, q_t, sc_t, op, what):
+    """Both MX forms of the bf16 tensor t (the kernel's own copy) against the oracle: last-dim blocks of the
+    rows inside groups, padded row blocks per group (K4 scale layout)."""
+    R, C = t_bits.shape
+    covered = int(min(max(int(np.clip(offs, 0, R).max()), 0), R))
+    ql, sl = oracle.quantize_mx_lastdim(t_bits[:covered], rule)
+    assert_bytes_equal(host(q)[:covered], ql, f"{what} last-dim codes")
+    assert_bytes_equal(_k4_rows(host(sc), R, C // 32)[:covered], sl.reshape(covered, C // 32), f"{what} last-dim e8m0")
+    qt, st, opr = oracle.quantize_mx_rows_grouped(t_bits, offs, rule, rows_pad)
+    assert_bytes_equal(host(op), opr, f"{what} padded offsets")
+    assert_bytes_equal(host(q_t), qt, f"{what} row-block codes")
+    assert_bytes_equal(_k4_rows(host(sc_t), C, rows_pad // 32), st, f"{what} row-block e8m0")
+
+
+SW_MX_CASES = {
+    "ragged": (700, 128, np.array([100, 100, 350, 690], np.int32)),       # an empty group, 10 rows in no group
+    "wide": (300, 1408 + 128, np.array([37, 200, 300], np.int32)),
+    "one_group": (96, 256, np.array([96], np.int32)),
+}
+# the forward also takes widths that are not a multiple of 128 (partial column tiles)
+SW_MX_FWD_CASES = {**SW_MX_CASES, "narrow": (200, 32, np.array([70, 200], np.int32)),
+                   "partial": (130, 1408 + 32, np.array([130], np.int32))}
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("case", list(SW_MX_FWD_CASES))
+def test_swiglu_mx_dual_forward(rule, case):
+    """A2 computed on the fly: its optional bf16 copy within one ulp of the exact value, both MX forms bit-exact
+    against the oracle's quantizers of that copy, and the same codes when no copy is written."""
+    R, F, offs = SW_MX_FWD_CASES[case]
+    h1 = make_h1(40 + R + F, R, F)
+    rows_pad = fm.quantize_mx_rows_bound(R, len(offs)) + 32
+    a2 = torch.full((R, F), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    note(f"swiglu fwd + MX dual rule={rule} case={case}")
+    _, q, sc, q_t, sc_t, op = fm.swiglu_quantize_mx_dual(bf16_dev(h1), i32_dev(offs), rule=rule, rows_pad=rows_pad,
+                                                         a2=a2)
+    covered = int(np.clip(offs, 0, R).max())
+    a2h = host(a2)
+    assert_within_one_ulp(a2h[:covered], sw.swiglu_fwd(h1[:covered], F), "a2 copy")
+    assert np.all(a2h[covered:].view(np.int16) == 0x5A5A), "rows in no group must stay untouched"
+    _check_mx_forms(a2h, offs, rule, rows_pad, q, sc, q_t, sc_t, op, "a2")
+    note(f"swiglu fwd + MX dual without the copy rule={rule} case={case}")
+    _, q2, sc2, qt2, sct2, _ = fm.swiglu_quantize_mx_dual(bf16_dev(h1), i32_dev(offs), rule=rule, rows_pad=rows_pad)
+    assert_bytes_equal(host(q2)[:covered], host(q)[:covered], "without the copy: last-dim codes")
+    assert_bytes_equal(_k4_rows(host(sc2), R, F // 32)[:covered], _k4_rows(host(sc), R, F // 32)[:covered],
+                       "without the copy: last-dim e8m0")
+    assert_bytes_equal(host(qt2), host(q_t), "without the copy: row-block codes")
+    assert_bytes_equal(host(sct2), host(sc_t), "without the copy: row-block e8m0")
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("case", list(SW_MX_CASES))
+def test_swiglu_mx_dual_backward(rule, case):
+    R, F, offs = SW_MX_CASES[case]
+    h1 = make_h1(50 + R + F, R, F)
+    da2 = make_da2(60 + R + F, R, F)
+    rows_pad = fm.quantize_mx_rows_bound(R, len(offs)) + 32
+    dh1 = torch.full((R, 2 * F), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    note(f"swiglu bwd + MX dual rule={rule} case={case}")
+    _, q, sc, q_t, sc_t, op = fm.swiglu_backward_quantize_mx_dual(bf16_dev(da2), bf16_dev(h1), i32_dev(offs), rule=rule,
+                                                                  rows_pad=rows_pad, dh1=dh1)
+    covered = int(np.clip(offs, 0, R).max())
+    dh1h = host(dh1)
+    assert_within_one_ulp(dh1h[:covered], sw.swiglu_bwd(da2[:covered], h1[:covered], F), "dh1 copy")
+    _check_mx_forms(dh1h, offs, rule, rows_pad, q, sc, q_t, sc_t, op, "dh1")
+
+
+def test_swiglu_mx_dual_llama4_scout_sampled():
+    """The Llama4-Scout layer's shapes (16384 routed rows, F = 8192, 16 groups): the fused forward and backward
+    against swiglu (bf16 copy, sampled rows) and the separate dual quantizer applied to that copy (whole
+    tensors, bit for bit)."""
+    from mxfp8_quantized_moe_amd import synth
+    w = synth.WORKLOADS[5]
+    offs = i32_dev(w.offs)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(55)
+    h1 = (torch.randn(w.M, w.F2, device=DEV, generator=gen) * 0.5).to(torch.bfloat16)
+    da2 = (torch.randn(w.M, w.F, device=DEV, generator=gen) * 1e-3).to(torch.bfloat16)
+    a2 = torch.empty(w.M, w.F, dtype=torch.bfloat16, device=DEV)
+    dh1 = torch.empty(w.M, w.F2, dtype=torch.bfloat16, device=DEV)
+    note("swiglu + MX dual, Llama4-Scout shapes")
+    _, q, sc, qt, sct, _ = fm.swiglu_quantize_mx_dual(h1, offs, a2=a2)
+    r = fm.quantize_mx_dual(a2, offs=offs, layout=fm.MX_LAYOUT_K4)
+    for g_, w_, n_ in zip((q, sc, qt, sct), r[:4], ("q", "scale", "q_t", "scale_t")):
+        assert torch.equal(g_, w_), f"forward {n_} differs from quantize_mx_dual of the copy"
+    _, q, sc, qt, sct, _ = fm.swiglu_backward_quantize_mx_dual(da2, h1, offs, dh1=dh1)
+    r = fm.quantize_mx_dual(dh1, offs=offs, layout=fm.MX_LAYOUT_K4)
+    for g_, w_, n_ in zip((q, sc, qt, sct), r[:4], ("q", "scale", "q_t", "scale_t")):
+        assert torch.equal(g_, w_), f"backward {n_} differs from quantize_mx_dual of the copy"
+    rows = np.random.default_rng(5).choice(w.M, 64, replace=False)
+    h1h, dah = host(h1)[rows], host(da2)[rows]
+    assert_within_one_ulp(host(a2)[rows], sw.swiglu_fwd(h1h, w.F), "a2 sampled")
+    assert_within_one_ulp(host(dh1)[rows], sw.swiglu_bwd(dah, h1h, w.F), "dh1 sampled")
