@@ -1139,24 +1139,33 @@ void gemm_fp8_pipe(KParams p) {
     const uint32_t stg_l = lds_off(stg), sinv_l = lds_off(sinv);
     const bool full = p_valid == BM && q_valid == BN;
     const int rr = lane >> 3, k = lane & 7;     // read-back: staged row 8 itr + rr, chunk k
-    lds_u4 dv[2][4];                            // read-back pieces of the last two passes
-    // Stores of pass n (32-row block n % TM, columns PC (n / TM) ..), once its
-    // read-back has landed.
+    constexpr int NP = TM * (TN / JPP);         // passes
+    // GROUPED_M with bf16 output: the read-back pieces of every pass are held
+    // (128 registers, where the dead MFMA fragments were) and stored together
+    // once the next tile's stages have landed.  Otherwise (measured slower for
+    // the short weight-gradient tiles, whose next k step then waits for the
+    // whole burst of stores; too many registers for fp32) the pieces of the
+    // last two passes, each pass's stores issued behind the next one's LDS work.
+    constexpr bool HOLD = MODE == 0 && NP <= 8;
+    constexpr int ND_ = HOLD ? NP : 2;
+    lds_u4 dv[ND_][4];
+    // Stores of pass n (32-row block n % TM, columns PC (n / TM) ..), once
+    // its read-back has landed.  All pre-issued stages of the next tile (this
+    // wave's part) land before the first store: until then only loads are in
+    // flight, and they complete in order.
     auto store_pass = [&](auto nc) {
       constexpr int n = decltype(nc)::value, i = n % TM, jp = n / TM;
+      constexpr int d = HOLD ? n : (n & 1);
 #pragma unroll
-      for (int itr = 0; itr < 4; ++itr) lds_ready(dv[n & 1][itr]);
-      // All pre-issued stages of the next tile (this wave's part) land before
-      // the first store: until then only loads are in flight, and they
-      // complete in order.
-      if constexpr (n == 0) wait_vmcnt<0>();
+      for (int itr = 0; itr < 4; ++itr) lds_ready(dv[d][itr]);
+      if constexpr (!HOLD && n == 0) wait_vmcnt<0>();
       const int c = wn * WN + PC * jp + VEC * k;
       uint8_t* const row0 = static_cast<uint8_t*>(p.out) +
                             (out_base + (int64_t)(wm * WM + 32 * i + rr) * out_ld + c) * ELEM;
       if (full) {
 #pragma unroll
         for (int itr = 0; itr < 4; ++itr)
-          store_stream16(row0 + (int64_t)itr * 8 * out_ld * ELEM, __builtin_bit_cast(u32x4, dv[n & 1][itr]));
+          store_stream16(row0 + (int64_t)itr * 8 * out_ld * ELEM, __builtin_bit_cast(u32x4, dv[d][itr]));
         return;
       }
 #pragma unroll
@@ -1164,11 +1173,11 @@ void gemm_fp8_pipe(KParams p) {
         const int r = wm * WM + 32 * i + 8 * itr + rr;
         if (r >= p_valid) continue;
         uint8_t* dst = row0 + (int64_t)itr * 8 * out_ld * ELEM;
-        const lds_u4 d = dv[n & 1][itr];
+        const lds_u4 dd = dv[d][itr];
         if (c + VEC <= q_valid) {
-          store_stream16(dst, __builtin_bit_cast(u32x4, d));
+          store_stream16(dst, __builtin_bit_cast(u32x4, dd));
         } else {
-          const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+          const uint32_t w[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             if (c + e >= q_valid) break;
@@ -1249,17 +1258,27 @@ void gemm_fp8_pipe(KParams p) {
         for (int itr = 0; itr < 4; ++itr) {
           const int lr = 8 * itr + rr;
           const int pc = OUT == 0 ? (k ^ ((lr & 14) >> 1)) : (k ^ (lr & 7));
-          dv[n & 1][itr] = lds_read16(stg_l + lr * 128 + (pc << 4));
+          if constexpr (HOLD)
+            dv[n][itr] = *reinterpret_cast<const lds_u4*>(stg + lr * 128 + (pc << 4));
+          else
+            dv[n & 1][itr] = lds_read16(stg_l + lr * 128 + (pc << 4));
         }
-        // the previous pass's pieces leave now, behind this pass's LDS work
-        if constexpr (n > 0) {
+        // fp32: the previous pass's pieces leave now, behind this pass's LDS work
+        if constexpr (!HOLD && n > 0) {
           wait_lgkmcnt<4 * JPP + 4>();
           store_pass(std::integral_constant<int, n - 1>{});
         }
       });
     });
     wait_lgkmcnt<0>();
-    store_pass(std::integral_constant<int, TM * (TN / JPP) - 1>{});
+    if constexpr (HOLD) {
+      // bf16: every pass was staged and read back before the first store, so
+      // the conversion ran while the next tile's stages were still landing.
+      wait_vmcnt<0>();
+      static_for<NP>([&](auto nc) { store_pass(nc); });
+    } else {
+      store_pass(std::integral_constant<int, NP - 1>{});
+    }
   } else {
     // Output rows not 16-byte aligned: element stores straight from registers.
     wait_vmcnt<0>();   // the next tile's pre-issued stages (older than any store below)
