@@ -528,6 +528,53 @@ def test_grouped_m_mx_k4(rule, K):
     check(got, ref, contract, tight, f"GROUPED_M MX K4 K={K}")
 
 
+# Groups averaging at least 512 rows take 256-row tiles.  These sizes put a group's last tile at every
+# boundary: remainders (mod 256) of 0, 1, 127, 128, 129, 255, groups under one tile, an empty group,
+# one row.
+SPLIT_COUNTS = np.array([256, 257, 383, 385, 511, 512, 513, 640, 767, 900, 0, 1, 100, 1023, 2000], np.int64)
+
+
+def test_grouped_m_last_tile_sizes():
+    offs = synth.offsets_from_counts(SPLIT_COUNTS)
+    M = int(offs[-1]) + 37                          # rows past the last group keep their sentinel
+    x = synth.normal_bf16(81, (M, 512), 1.0, 0.01, 50.0)
+    w = synth.normal_bf16(82, (len(SPLIT_COUNTS), 320, 512), 0.02)
+    assert M // len(SPLIT_COUNTS) >= 512
+    gm_case(x, w, offs, name="tile boundaries")
+
+
+
+def test_grouped_m_last_tile_sizes_malformed_offsets():
+    """A decreasing offset (an empty group) and one past M (clamped), with 256-row tiles."""
+    x = synth.normal_bf16(85, (3000, 384), 1.0)
+    w = synth.normal_bf16(86, (4, 300, 384), 0.02)
+    gm_case(x, w, np.array([1000, 600, 2300, 99999], np.int32), name="tile boundaries, malformed offsets")
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_grouped_m_mx_k4_last_tile_sizes(rule):
+    offs = synth.offsets_from_counts(SPLIT_COUNTS)
+    M, K = int(offs[-1]), 640
+    E, N = len(SPLIT_COUNTS), 288
+    x = synth.normal_bf16(83, (M, K), 1.0, 0.01, 30.0)
+    w = synth.normal_bf16(84, (E, N, K), 0.02)
+    note(f"GROUPED_M MX K4 last tile sizes rule={rule}")
+    qa, xa, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule)
+    qb, xb, _ = fm.quantize_mx(bf16_dev(w.reshape(E * N, K)), axis=1, rule=rule)
+    _, ya, _ = fm.quantize_mx(bf16_dev(x), axis=1, rule=rule, layout=fm.MX_LAYOUT_K4)
+    _, yb, _ = fm.quantize_mx(bf16_dev(w.reshape(E * N, K)), axis=1, rule=rule, layout=fm.MX_LAYOUT_K4)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(SENT_BF16)
+    fm.grouped_mm_scaled(fm.GROUPED_M, qa, 0, ya, qb, 0, yb, fm.SCALE_E8M0_K4, i32_dev(offs), E, M, N, K, out=out)
+    raw, got = _out_host(out)
+    qa_h, xa_h = host(qa), host(xa)
+    qb_h, xb3 = host(qb).reshape(E, N, K), host(xb).reshape(E, N, K // 32)
+    ref = oracle.mm_grouped_m_mx(qa_h, xa_h, qb_h, xb3, offs)
+    A = oracle.decode(qa_h, 0) * np.repeat(oracle.e8m0_decode(xa_h), 32, axis=-1)
+    B = oracle.decode(qb_h, 0) * np.repeat(oracle.e8m0_decode(xb3), 32, axis=-1)
+    contract, tight = oracle.error_bounds_m(A, B, offs, oracle.ACC_FP8_MFMA)
+    check(got, ref, contract, tight, "GROUPED_M MX K4 last tile sizes")
+
+
 @pytest.mark.parametrize("case", ["unaligned", "aligned", "small-groups"])
 def test_grouped_k_mx_k4(case):
     if case == "unaligned":       # rows_pad = 1216: the last stage holds one real 32-block
