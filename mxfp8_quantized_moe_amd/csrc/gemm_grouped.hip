@@ -581,8 +581,9 @@ void gemm_fp8_pipe(KParams p) {
   // ---------------------------------------------------------------- tiles
   // Persistent: the grid is at most one workgroup per CU and each walks the
   // tiles with a stride of the grid.  Round k gives XCD x (dispatch is
-  // round-robin over 8) the contiguous logical tiles [G k + G/8 x, + G/8), so
-  // the tiles one XCD runs together share operand rows in its L2; logical
+  // round-robin over 8) the contiguous logical tiles [G k + G/8 x, + G/8)
+  // (for a skewed GROUPED_K, odd rounds backwards: [G k + G/8 (7 - x), ...)),
+  // so the tiles one XCD runs together share operand rows in its L2; logical
   // tiles run in bands of kBandRows row tiles.  GROUPED_M counts its real row
   // tiles on the device (the host knows only a bound), so no round is spent
   // on empty tiles.
@@ -607,6 +608,7 @@ void gemm_fp8_pipe(KParams p) {
   __shared__ int g_hi[kTableGroups];
   __shared__ int g_pre[kTableGroups + 1];
   const bool table = p.E <= kTableGroups;
+  int skewed = 0;   // GROUPED_K: groups sorted by size, every other round backwards
   if (table) {
     __shared__ int s_tmp[4];
     const int t = threadIdx.x;
@@ -621,8 +623,35 @@ void gemm_fp8_pipe(KParams p) {
       if (t < p.E) g_pre[t + 1] = incl;
       if (t == 0) g_pre[0] = 0;
       __syncthreads();
+    } else {
+      // GROUPED_K: a tile's cost grows with its group's token count.  When the
+      // largest group holds more than twice the mean of the non-empty ones,
+      // g_pre[r] = the group of rank r in decreasing token count (ties: lower
+      // index first); tiles run in that order and the grid stride below runs
+      // every other round backwards, so the long contractions come first and
+      // even out across the CUs.  Otherwise g_pre[r] = r.
+      __shared__ int s_skew;
+      const int c = t < p.E ? hi - (t == 0 ? 0 : g_hi[t - 1]) : 0;
+      const int cmax = block_scan_max<256>(c, s_tmp);
+      const int nz = block_scan_sum<256>(c > 0 ? 1 : 0, s_tmp);
+      if (t == 255) s_skew = (int64_t)cmax * nz > 2 * (int64_t)g_hi[p.E - 1] ? 1 : 0;
+      __syncthreads();
+      skewed = s_skew;
+      if (t < p.E) {
+        int rank = t;
+        if (skewed) {
+          rank = 0;
+          for (int j = 0; j < p.E; ++j) {
+            const int cj = g_hi[j] - (j == 0 ? 0 : g_hi[j - 1]);
+            rank += cj > c || (cj == c && j < t) ? 1 : 0;
+          }
+        }
+        g_pre[rank] = t;
+      }
+      __syncthreads();
     }
   }
+  skewed = __builtin_amdgcn_readfirstlane(skewed);
   int row_units = p.row_units;
   if constexpr (MODE == 0) {
     constexpr int kFar = 1 << 30;
@@ -632,7 +661,9 @@ void gemm_fp8_pipe(KParams p) {
   const int ntiles = row_units * p.col_tiles;
   const int G = gridDim.x;
   auto tile_of = [&](int it) {
-    return (G & 7) == 0 ? G * it + (G >> 3) * (blockIdx.x & 7) + (blockIdx.x >> 3) : G * it + blockIdx.x;
+    int pos = (G & 7) == 0 ? (G >> 3) * (int)(blockIdx.x & 7) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+    if (skewed && (it & 1)) pos = G - 1 - pos;   // XCD x takes chunk 7 - x: still contiguous
+    return G * it + pos;
   };
   // Contraction-contiguous row stride of both operands, output row stride and
   // e8m0 row length: fixed per launch.
@@ -709,7 +740,7 @@ void gemm_fp8_pipe(KParams p) {
       qsf = static_cast<const float*>(p.sb) + (int64_t)e * p.N + n0;
     } else {
       const int ntn = (p.N + BM - 1) / BM;
-      const int e = ru / ntn;
+      const int e = table ? g_pre[ru / ntn] : ru / ntn;
       const int n0 = (ru % ntn) * BM, k0 = ct * BN;
       // group range of e: lo = max over j < e of clamp(offs[j]); hi = max(lo, clamp(offs[e]))
       int lo, hi;

@@ -429,6 +429,18 @@ def test_grouped_k_small_and_empty_groups():
     gk_case(dy, x, synth.offsets_from_counts(counts), name="small-groups")
 
 
+
+def test_grouped_k_skewed_groups():
+    """One group far above the mean (the kernel then runs the groups in decreasing size, every other
+    round of the grid backwards), equal sizes (ties keep index order) and empty groups; more tiles
+    than one round of the grid."""
+    counts = np.array([64, 3000, 0, 64, 130, 1, 700, 64, 0, 2, 300, 33], np.int64)
+    assert counts.max() * (counts > 0).sum() > 2 * counts.sum()
+    M = (int(counts.sum()) + 15) // 16 * 16        # a multiple of 16; rows past the last group are ignored
+    dy = synth.normal_bf16(48, (M, 2104), 1e-3)      # 12 x 9 x 6 tiles of 256: three rounds of 256 CUs
+    x = synth.normal_bf16(49, (M, 1400), 1.0, 0.01, 30.0)
+    gk_case(dy, x, synth.offsets_from_counts(counts), name="skewed")
+
 def test_grouped_k_f32_out():
     dy, x, offs = GK_CASES["ragged"]()
     gk_case(dy, x, offs, out_dtype=1, name="f32out")
