@@ -39,9 +39,11 @@
 //    ring, e8m0 scales loaded a byte at a time.
 //  * Small groups (average rows per group below 512) use BM = 128 to waste
 //    less of each tile on padding rows.
-//  * Tiles are ordered in bands of 8 row tiles, and each XCD (dispatch is
-//    round-robin over 8) gets a contiguous range of them, so the tiles running
-//    together on one XCD share operand rows in its L2.
+//  * Tiles are ordered in bands of 8 row tiles (GROUPED_M: cut at group
+//    boundaries, so a band's tiles share one expert's weight panels), and
+//    each XCD (dispatch is round-robin over 8) gets a contiguous range of
+//    them, so the tiles running together on one XCD share operand rows in its
+//    L2.
 #include "device_common.hpp"
 #include "gemm_common.hpp"
 #include "kernels.hpp"
@@ -70,6 +72,7 @@ struct KParams {
   // ceil(2^32 / (kBandRows * col_tiles)): band = umulhi(L, band_magic) for
   // every logical tile L (exact while L * kBandRows * col_tiles < 2^32).
   uint32_t band_magic;
+  uint32_t col_magic;   // ceil(2^32 / col_tiles) (col_tiles >= 2): L / col_tiles = umulhi(L, col_magic)
 };
 
 // Each XCD gets a contiguous range of logical tile ids (dispatch is round-robin).
@@ -698,29 +701,51 @@ void gemm_fp8_pipe(KParams p) {
     // value in the common case (a loop-invariant reciprocal would occupy a
     // register across the whole tile loop)
     static_assert((kBandRows & (kBandRows - 1)) == 0, "band rows: a power of two");
-    const int band = (int)__umulhi((uint32_t)L, p.band_magic);
-    const int first = band * kBandRows;
-    const int gsz = min(row_units - first, kBandRows);
-    const int inband = L - band * (kBandRows * p.col_tiles);
-    int ru, ct;
-    if (gsz == kBandRows) {
-      ru = first + (inband & (kBandRows - 1));
-      ct = inband / kBandRows;
+    int ru, ct, grp = -1;
+    if (MODE == 0 && table) {
+      // GROUPED_M bands do not cross groups: a group's row tiles form bands
+      // of kBandRows from its first one (the last band of a group shorter), so
+      // the tiles an XCD runs together share one expert's weight panels.
+      // Band [b0, b1) holds the logical tiles [b0 C, b1 C) (C column tiles).
+      const int C = p.col_tiles;
+      // L / C: a row unit of L's band (the magic needs C >= 2)
+      const int u = C == 1 ? L : (int)__umulhi((uint32_t)L, p.col_magic);
+      int a = 0, b = p.E;   // g_pre[a] <= u < g_pre[b]
+      while (b - a > 1) {
+        const int mid = (a + b) >> 1;
+        if (g_pre[mid] <= u) a = mid;
+        else b = mid;
+      }
+      const int b0 = g_pre[a] + ((u - g_pre[a]) & ~(kBandRows - 1));
+      const int gsz = min(g_pre[a + 1] - b0, kBandRows);
+      const int inband = L - b0 * C;
+      if (gsz == kBandRows) {
+        ru = b0 + (inband & (kBandRows - 1));
+        ct = inband / kBandRows;
+      } else {
+        ru = b0 + inband % gsz;
+        ct = inband / gsz;
+      }
+      grp = a;
     } else {
-      ru = first + inband % gsz;
-      ct = inband / gsz;
+      const int band = (int)__umulhi((uint32_t)L, p.band_magic);
+      const int first = band * kBandRows;
+      const int gsz = min(row_units - first, kBandRows);
+      const int inband = L - band * (kBandRows * p.col_tiles);
+      if (gsz == kBandRows) {
+        ru = first + (inband & (kBandRows - 1));
+        ct = inband / kBandRows;
+      } else {
+        ru = first + inband % gsz;
+        ct = inband / gsz;
+      }
     }
     const float* psf = nullptr;   // fp32 scales of the tile's rows / columns
     const float* qsf = nullptr;
     if constexpr (MODE == 0) {
       Unit un;
       if (table) {
-        int a = 0, b = p.E;   // g_pre[a] <= ru < g_pre[b]
-        while (b - a > 1) {
-          const int mid = (a + b) >> 1;
-          if (g_pre[mid] <= ru) a = mid;
-          else b = mid;
-        }
+        const int a = grp;
         un = Unit{a, ru - g_pre[a], a == 0 ? 0 : g_hi[a - 1], g_hi[a], 0};
       } else {
         un = find_unit<256>(p.offs, p.E, p.M, ru, Ch{}, NoPad{});
@@ -1375,6 +1400,8 @@ static void fill_params(KParams& p, const GemmArgs& g, int BM, int BN) {
   }
   const uint64_t band_tiles = (uint64_t)kBandRows * (uint64_t)std::max(p.col_tiles, 1);
   p.band_magic = (uint32_t)(((1ull << 32) + band_tiles - 1) / band_tiles);
+  const uint64_t ct = (uint64_t)p.col_tiles;
+  p.col_magic = ct >= 2 ? (uint32_t)(((1ull << 32) + ct - 1) / ct) : 0u;   // unused below 2
 }
 
 // The band magic is exact for every tile index below 2^32 / (kBandRows * col_tiles).

@@ -546,13 +546,14 @@ def test_grouped_m_mx_k4(rule, K):
 SPLIT_COUNTS = np.array([256, 257, 383, 385, 511, 512, 513, 640, 767, 900, 0, 1, 100, 1023, 2000], np.int64)
 
 
-def test_grouped_m_last_tile_sizes():
+@pytest.mark.parametrize("N", [320, 200])           # two column tiles, one
+def test_grouped_m_last_tile_sizes(N):
     offs = synth.offsets_from_counts(SPLIT_COUNTS)
     M = int(offs[-1]) + 37                          # rows past the last group keep their sentinel
     x = synth.normal_bf16(81, (M, 512), 1.0, 0.01, 50.0)
-    w = synth.normal_bf16(82, (len(SPLIT_COUNTS), 320, 512), 0.02)
+    w = synth.normal_bf16(82, (len(SPLIT_COUNTS), N, 512), 0.02)
     assert M // len(SPLIT_COUNTS) >= 512
-    gm_case(x, w, offs, name="tile boundaries")
+    gm_case(x, w, offs, name=f"tile boundaries N={N}")
 
 
 
