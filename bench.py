@@ -280,14 +280,28 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                  lambda: fm.moe_route(idsd, E, 1, out=(r_counts, r_offs, r_dest, r_src), workspace=ws),
                  4 * S + 4 * S + 4 * rows + 8 * E,
                  spec=dict(op="route", ids="IDS", E=E, pad=1, out=(r_counts, r_offs, r_dest, r_src)))
-        xg = bf(rows, H)
+        def mx_gather(name, x, x_name, wts, w_name):
+            """Both MX forms of the token rows x gathered into the grouped layout (times the router
+            weights when given) in one launch: the gathered tensor never goes to memory."""
+            q, s = u8(rows, H), u8(*fm.mx_k4_shape(rows, H // 32))
+            qt, st = u8(H, Mp), u8(*fm.mx_k4_shape(H, Mp // 32))
+            step.add(name, "quant",
+                     lambda: fm.moe_permute_quantize_mx_dual(x(), r_src, k, offs, weights=wts, rule=rule,
+                                                             rows_pad=Mp, q=q, scale=s, q_t=qt, scale_t=st,
+                                                             offs_pad=op, layout=K4),
+                     2 * T * H + 2 * rows * H + 2 * (rows * H // 32) + 4 * rows + (4 * S if wts is not None else 0),
+                     spec=dict(op="permute_mx_dual", x=x_name, rsrc=r_src, dest=r_dest, topk=k, w=w_name,
+                               shape=(rows, H), offs=offs_np, rows_pad=Mp, rule=rule, q=q, s=s, qt=qt, st=st,
+                               offs_pad=op))
+            return q, s, qt, st
+
+        xg = dyg = None                      # the gathered bf16 rows (the MX path never forms them)
         if w.mx:
-            step.add("permute X", "moe", lambda: fm.moe_permute(Xd(), r_src, k, xg=xg), 4 * rows * H + 4 * rows,
-                     spec=dict(op="permute", src="X", topk=k, rsrc=r_src, out=xg))
-            qx, sx, qxt, sxt = mx_dual_g("mx Xg (both forms)", xg, lambda: xg, rows, H)
+            qx, sx, qxt, sxt = mx_gather("permute+mx Xg (both forms)", Xd, "X", None, None)
             qw1, sw1, qw1t, sw1t = mx_dual_b("mx W1 (both forms)", "W1", W1d, E, F2, H)
             h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H, sk=fm.SCALE_E8M0_K4)
         else:
+            xg = bf(rows, H)
             qx, sx = u8(rows, H), f32(rows)
             step.add("permute+q X", "moe",
                      lambda: fm.moe_permute_rowwise(Xd(), r_src, k, 0, xg=xg, qg=qx, scale_g=sx),
@@ -319,18 +333,20 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
         step.add("combine", "moe", lambda: fm.moe_combine(yg, r_dest, rwd, k, y=y), 2 * S * H + 2 * T * H + 8 * S,
                  spec=dict(op="combine", yg=yg, dest=r_dest, w="RW", topk=k, out=y))
         # backward
-        dyg, dw = bf(rows, H), f32(S)
+        dw = f32(S)
         if w.mx:
-            step.add("combine bwd", "moe",
-                     lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, codes=False, dyg=dyg,
-                                                     dweights=dw),
-                     2 * T * H + 4 * rows * H + 16 * S,
-                     spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=dyg,
+            # the router weights' gradients only; the routed-row gradients are formed inside the quantizer
+            step.add("combine bwd (dw)", "moe",
+                     lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, codes=False,
+                                                     rows_out=False, dweights=dw),
+                     2 * T * H + 2 * rows * H + 16 * S,
+                     spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=None,
                                q=None, s=None, dw=dw))
-            qdy, sdy, qdyt, sdyt = mx_dual_g("mx dYg (both forms)", dyg, lambda: dyg, rows, H)
+            qdy, sdy, qdyt, sdyt = mx_gather("permute+mx dYg (both forms)", DYd, "DY", rwd, "RW")
             da2 = g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, rows, F, H, sk=fm.SCALE_E8M0_K4)
             g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0_K4, offs_t=op)
         else:
+            dyg = bf(rows, H)
             qdy, sdy = u8(rows, H), f32(rows)
             step.add("combine bwd+q", "moe",
                      lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, dyg=dyg, q=qdy, scale=sdy,
@@ -635,6 +651,24 @@ def cpu_baseline(step, host: dict):
                 xs = np.ascontiguousarray(x[:, :, :c])
                 t_l = timed(lambda: oracle.quantize_mx_lastdim(x.reshape(B * R, C)[:r], sp["rule"]), 1) * (B * R / r)
                 t_r = timed(lambda: oracle.quantize_mx_rows_batched(xs, sp["rule"]), 1) * (C / c)
+            add(name, t_l + t_r, 1.0)
+        elif op == "permute_mx_dual":
+            x, rsrc, k = host[sp["x"]], src(sp["rsrc"]), sp["topk"]
+            M, C = sp["shape"]
+            T = x.shape[0]
+            r = max(1, min(M, QS // max(C, 1)))
+            c = max(32, min(C, QS // max(M, 1)) // 32 * 32)
+            no_dest = np.full(T * k, -1, np.int32)
+
+            def gather(s_rows, cols):
+                xs = np.ascontiguousarray(x[:, :cols])
+                if sp["w"] is None:
+                    return o_route.permute(xs, s_rows, k)
+                return o_route.combine_backward(xs, np.zeros((s_rows.size, cols), np.uint16), s_rows, no_dest,
+                                                host[sp["w"]], T, k)[0]
+            t_l = timed(lambda: oracle.quantize_mx_lastdim(gather(rsrc[:r], C), sp["rule"]), 1) * (M / r)
+            t_r = timed(lambda: oracle.quantize_mx_rows_grouped(gather(rsrc, c), sp["offs"], sp["rule"],
+                                                                sp["rows_pad"]), 1) * (C / c)
             add(name, t_l + t_r, 1.0)
         elif op == "swiglu_mx":
             h1 = src(sp["h1"])

@@ -416,7 +416,9 @@ int moe_combine(const void *yg_bf16, int64_t rows_in, const int32_t *dest,
  *   weights  f32  [tokens][topk]
  *   dyg      bf16 [rows][cols]     for grouped row r holding slot s = src[r] of
  *            token t = s / topk: bf16(weights[s] * dy[t]), one fp32 product
- *            rounded to nearest even; zeros for a row holding no slot (written)
+ *            rounded to nearest even; zeros for a row holding no slot (written),
+ *            or NULL: not written (moe_permute_quantize_mx_dual forms the same
+ *            rows from dy itself)
  *   q        u8   [rows][cols]     codes of quantize_rowwise(dyg), or NULL (written)
  *   scale    f32  [rows]           its row scales, NULL exactly when q is (written)
  *   dweights f32  [tokens*topk]    sum over columns of dy[t] * yg[dest[s]] (exact
@@ -522,6 +524,37 @@ int quantize_mx_dual(const void *x_bf16, int64_t batch, int64_t rows, int64_t co
                      const int32_t *offs, int32_t n_groups, int rule, int scale_layout, void *q,
                      void *scale_e8m0, void *q_t, void *scale_t_e8m0, int64_t rows_pad,
                      int32_t *offs_pad_out, void *stream);
+
+/*
+ * moe_permute_quantize_mx_dual -- the gather of token rows into moe_route's
+ * grouped layout fused with both MXFP8 forms of the gathered tensor: the rows
+ * are formed at load time and never go to memory (an optional bf16 copy
+ * exists).  With router weights it forms, the same way, the routed-row
+ * gradients of moe_combine_backward from the output gradient dy.
+ *   [P1 Details, MoE paragraph (the routed rows quantized by a fused kernel
+ *   ahead of the grouped GEMM); P2 Details (MXFP8 operands blocked along each
+ *   GEMM's contraction dimension); P4 "MoE" (the experts' outputs summed with
+ *   the router's weights, whose backward scales each routed row).]
+ *   x        bf16 [tokens][cols]  token rows (or dy)
+ *   src      int32 [rows]         from moe_route: grouped row r holds slot
+ *                                 s = src[r] of token s / topk; a row whose
+ *                                 src is < 0 or >= tokens*topk is zeros
+ *   weights  f32 [tokens*topk], or NULL: row r = bf16(weights[s] * x[s / topk]),
+ *            one fp32 product rounded to nearest even; NULL: row r = x[s / topk]
+ *   xg       bf16 [rows][cols]    optional copy of the gathered rows (NULL: not
+ *                                 written); rows past the last group untouched
+ *   q, scale_e8m0, q_t, scale_t_e8m0, offs, n_groups, rows_pad, offs_pad_out,
+ *   rule, scale_layout: as quantize_mx_dual of the gathered [rows][cols] tensor
+ *   with offs (required, non-NULL).
+ *   Requires: tokens*topk <= INT32_MAX; x, xg and q 16-byte aligned, src and
+ *   weights 4-byte aligned; the rest as quantize_mx_dual.  One kernel, no
+ *   allocation.
+ */
+int moe_permute_quantize_mx_dual(const void *x_bf16, int64_t tokens, int64_t cols, int32_t topk,
+                                 const int32_t *src, const float *weights, int64_t rows,
+                                 const int32_t *offs, int32_t n_groups, int rule, int scale_layout,
+                                 void *xg_bf16, void *q, void *scale_e8m0, void *q_t, void *scale_t_e8m0,
+                                 int64_t rows_pad, int32_t *offs_pad_out, void *stream);
 
 /*
  * swiglu_quantize_mx_dual -- the SwiGLU between the two expert GEMMs fused with

@@ -21,6 +21,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "quantize_mx_dual", "swiglu_quantize_mx_dual", "swiglu_backward_quantize_mx_dual",
+           "moe_permute_quantize_mx_dual",
            "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_route_workspace_bytes", "moe_permute", "moe_combine",
            "moe_permute_rowwise", "moe_combine_backward",
@@ -181,6 +182,28 @@ def _mx_dual_outputs(R, C, offs, rows_pad, q, scale, q_t, scale_t, offs_pad, lay
         if scale_t is None else scale_t
     offs_pad = torch.empty((E,), dtype=torch.int32, device=dev) if offs_pad is None else offs_pad
     return rp, q, scale, q_t, scale_t, offs_pad
+
+
+def moe_permute_quantize_mx_dual(x, src, topk, offs, weights=None, rule=MX_FLOOR_OCP, rows_pad=None, xg=None,
+                                 q=None, scale=None, q_t=None, scale_t=None, offs_pad=None, layout=MX_LAYOUT_K4,
+                                 stream=None):
+    """x bf16 [T, C] (token rows, or the output gradient dy), src int32 [R], offs int32 [E] from moe_route,
+    weights f32 [T, topk] or None -> (xg or None, q [R, C], scale, q_t [C, rows_pad], scale_t, offs_pad): both
+    MX forms of the gathered rows x[src[r] // topk] (times weights[src[r]] when given, rounded to bf16);
+    xg (bf16 [R, C]) is written only if passed."""
+    x = _bits(x).contiguous()
+    T, C = x.shape
+    R = src.numel()
+    if weights is not None:
+        weights = weights.contiguous()
+        if weights.dtype != torch.float32 or weights.numel() != T * topk:
+            raise ValueError("moe_permute_quantize_mx_dual: weights f32 [T, topk]")
+    rp, q, scale, q_t, scale_t, offs_pad = _mx_dual_outputs(R, C, offs, rows_pad, q, scale, q_t, scale_t, offs_pad,
+                                                            layout, x.device)
+    _lib.check("moe_permute_quantize_mx_dual", _lib.lib().moe_permute_quantize_mx_dual(
+        _ptr(x), T, C, topk, _ptr(src), _ptr(weights), R, _ptr(offs), offs.numel(), rule, layout, _ptr(xg), _ptr(q),
+        _ptr(scale), _ptr(q_t), _ptr(scale_t), rp, _ptr(offs_pad), _stream(stream)))
+    return xg, q, scale, q_t, scale_t, offs_pad
 
 
 def swiglu_quantize_mx_dual(h1, offs, rule=MX_FLOOR_OCP, rows_pad=None, a2=None, q=None, scale=None, q_t=None,
@@ -449,9 +472,10 @@ def moe_permute_rowwise(x, src, topk, codec=E4M3FN, xg=None, qg=None, scale_g=No
 
 
 def moe_combine_backward(dy, yg, dest, src, weights, topk, codec=E4M3FN, codes=True, dyg=None, q=None, scale=None,
-                         dweights=None, stream=None):
+                         dweights=None, stream=None, rows_out=True):
     """dy bf16 [T, C], yg bf16 [R, C], dest int32 [T*k], src int32 [R], weights f32 [T, k] ->
-    (dyg bf16 [R, C], q u8 [R, C] or None, scale f32 [R] or None, dweights f32 [T*k])."""
+    (dyg bf16 [R, C] or None, q u8 [R, C] or None, scale f32 [R] or None, dweights f32 [T*k]).
+    rows_out=False: the routed-row gradients are not written (dyg is None)."""
     dy = _bits(dy).contiguous()
     yg = _bits(yg).contiguous()
     T, C = dy.shape
@@ -461,7 +485,10 @@ def moe_combine_backward(dy, yg, dest, src, weights, topk, codec=E4M3FN, codes=T
             or src.numel() != R or yg.shape[1] != C:
         raise ValueError("moe_combine_backward: dy [T, C], yg [R, C], weights f32 [T, topk], dest [T*topk], src [R]")
     dev = dy.device
-    dyg = torch.empty((R, C), dtype=dy.dtype, device=dev) if dyg is None else dyg
+    if rows_out:
+        dyg = torch.empty((R, C), dtype=dy.dtype, device=dev) if dyg is None else dyg
+    else:
+        dyg = None
     if codes:
         q = torch.empty((R, C), dtype=torch.uint8, device=dev) if q is None else q
         scale = torch.empty((R,), dtype=torch.float32, device=dev) if scale is None else scale

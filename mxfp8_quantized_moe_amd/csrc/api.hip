@@ -234,6 +234,20 @@ int quantize_mx_dual(const void* x_bf16, int64_t batch, int64_t rows, int64_t co
                                                as_stream(stream)));
 }
 
+int moe_permute_quantize_mx_dual(const void* x_bf16, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                                 const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups, int rule,
+                                 int scale_layout, void* xg_bf16, void* q, void* scale_e8m0, void* q_t,
+                                 void* scale_t_e8m0, int64_t rows_pad, int32_t* offs_pad_out, void* stream) {
+  const int st = check_moe_permute_mx_dual(x_bf16, tokens, cols, topk, src, weights, rows, offs, n_groups, rule,
+                                           scale_layout, xg_bf16, q, scale_e8m0, q_t, scale_t_e8m0, rows_pad,
+                                           offs_pad_out);
+  if (st) return st;
+  return launch_status(launch_moe_permute_mx_dual(
+      static_cast<const uint16_t*>(x_bf16), tokens, cols, topk, src, weights, rows, offs, n_groups, rule,
+      scale_layout, static_cast<uint16_t*>(xg_bf16), static_cast<uint8_t*>(q), static_cast<uint8_t*>(scale_e8m0),
+      static_cast<uint8_t*>(q_t), static_cast<uint8_t*>(scale_t_e8m0), rows_pad, offs_pad_out, as_stream(stream)));
+}
+
 int swiglu_quantize_mx_dual(const void* h1_bf16, int64_t rows, int64_t F, int64_t ld_h1, const int32_t* offs,
                             int32_t n_groups, int rule, int scale_layout, void* a2_bf16, void* q, void* scale_e8m0,
                             void* q_t, void* scale_t_e8m0, int64_t rows_pad, int32_t* offs_pad_out, void* stream) {
@@ -306,6 +320,6 @@ int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(p
 
 int fp8moe_set_colwise_chunk_rows(int rows) { return set_colwise_chunk_rows(rows); }
 
-int fp8moe_version(void) { return 106; }
+int fp8moe_version(void) { return 107; }
 
 }  // extern "C"

@@ -30,6 +30,10 @@ hipError_t launch_quantize_mx_dual(const uint16_t* x, int64_t batch, int64_t row
                                    int32_t* offs_pad_out, hipStream_t st);
 
 // SwiGLU (da2 null) or its backward (da2 given) computed on the fly and quantized into both MX forms.
+hipError_t launch_moe_permute_mx_dual(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
+                                     const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups,
+                                     int rule, int scale_layout, uint16_t* xg, uint8_t* q, uint8_t* sc, uint8_t* q_t,
+                                     uint8_t* sc_t, int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st);
 hipError_t launch_swiglu_mx_dual(const uint16_t* h1, const uint16_t* da2, int64_t rows, int64_t F, int64_t ld_h1,
                                  const int32_t* offs, int32_t n_groups, int rule, int scale_layout, uint16_t* out,
                                  uint8_t* q, uint8_t* sc, uint8_t* q_t, uint8_t* sc_t, int64_t rows_pad,

@@ -281,13 +281,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // Backward of the combine.  Workgroups [0, tokens) take one token each: the
 // token's gradient row dy[t] stays in registers (ITEMS 16-byte chunks per
 // thread, 256 threads), and for each of its slots s = t*topk + j, in order,
-// the workgroup writes the routed row's gradient dyg[dest[s]] = bf16(w[s] *
-// dy[t]) (one fp32 product, rounded to nearest even), reduces the router
-// weight's gradient dw[s] = <dy[t], yg[dest[s]]> (exact bf16 products, fp32
-// sums), and, with codes requested, quantizes the routed row rowwise from the
-// bf16 values it just wrote.  A dropped slot gets dw = 0.  Workgroups from
-// `tokens` on clear the grouped rows that hold no slot (padding): zeros, zero
-// codes and the all-zero row's scale.
+// the workgroup forms the routed row's gradient dyg[dest[s]] = bf16(w[s] *
+// dy[t]) (one fp32 product, rounded to nearest even; written unless dyg is
+// null), reduces the router weight's gradient dw[s] = <dy[t], yg[dest[s]]>
+// (exact bf16 products, fp32 sums), and, with codes requested, quantizes the
+// routed row rowwise from those bf16 values.  A dropped slot gets dw = 0.
+// Workgroups from `tokens` on clear the grouped rows that hold no slot
+// (padding): zeros, zero codes and the all-zero row's scale.
 template <int CODEC, int ITEMS, bool QUANT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dy,
                                                           const uint16_t* __restrict__ yg, int64_t rows,
@@ -307,8 +307,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
     for (int64_t r = (int64_t)blockIdx.x - tokens; r < rows; r += zero_blocks) {
       const int sl = src[r];
       if (sl >= 0 && (int64_t)sl < S) continue;
-      u32x4* __restrict__ o = reinterpret_cast<u32x4*>(dyg + r * cols);
-      for (int64_t c = tid; c < nc; c += 256) o[c] = u32x4{0, 0, 0, 0};
+      if (dyg != nullptr) {
+        u32x4* __restrict__ o = reinterpret_cast<u32x4*>(dyg + r * cols);
+        for (int64_t c = tid; c < nc; c += 256) o[c] = u32x4{0, 0, 0, 0};
+      }
       if constexpr (QUANT) {
         u32x2* __restrict__ qo = reinterpret_cast<u32x2*>(q + r * cols);
         for (int64_t c = tid; c < nc; c += 256) qo[c] = u32x2{0, 0};
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
     }
     const float wj = w[sl];
     const u32x4* __restrict__ yr = reinterpret_cast<const u32x4*>(yg + (int64_t)d * cols);
-    u32x4* __restrict__ gr = reinterpret_cast<u32x4*>(dyg + (int64_t)d * cols);
+    u32x4* __restrict__ gr = dyg != nullptr ? reinterpret_cast<u32x4*>(dyg + (int64_t)d * cols) : nullptr;
     u32x4 gv[ITEMS];
     float acc = 0.0f;
     uint32_t m = 0;
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
           o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rt_f32x2{p0, p1}, rt_bf16x2));
         }
         gv[i] = u32x4{o[0], o[1], o[2], o[3]};
-        gr[c] = gv[i];
+        if (gr != nullptr) gr[c] = gv[i];
       }
       if constexpr (QUANT) {
         m = pk_absmax_bf16(m, gv[i].x);
@@ -488,7 +490,9 @@ static hipError_t combine_bwd_items(const uint16_t* dy, const uint16_t* yg, int6
                                     const int32_t* src, const float* w, int64_t tokens, int topk, int64_t cols,
                                     uint16_t* dyg, uint8_t* q, float* scale, float* dw, hipStream_t st) {
   const int64_t items = ((cols >> 3) + 255) / 256;
-  const int zero_blocks = (int)std::min<int64_t>(rows, 1024);
+  // padding rows are cleared by workgroups past `tokens`: none when nothing is written for them
+  const int zero_blocks = dyg == nullptr && !QUANT ? 0 : (int)std::min<int64_t>(rows, 1024);
+  if (tokens + zero_blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)(tokens + zero_blocks));
   auto go = [&](auto it_tag) -> hipError_t {
     constexpr int IT = decltype(it_tag)::value;

@@ -384,13 +384,23 @@ constexpr int kDualRows = 128, kDualCols = 128;
 // in memory unless `out` asks for a bf16 copy.  Columns of a 16-column slice
 // never straddle F (F % 16 == 0).
 struct DualSrc {
-  const uint16_t* x;      // PROD 0: [rows][cols]
+  const uint16_t* x;      // PROD 0: [rows][cols]; PROD 3: token rows [tokens][cols]
   const uint16_t* h1;     // PROD 1, 2: [rows][ld_h1]
   const uint16_t* da2;    // PROD 2: [rows][F]
   int64_t ld_h1;
   int F;
   uint16_t* out;          // optional bf16 copy of the tensor, [rows][cols]
+  const int32_t* src;     // PROD 3: [rows] routing slot of each grouped row
+  const float* gw;        // PROD 3: [slots] router weights, or null
+  int topk;               // PROD 3: slots per token
+  int64_t slots;          // PROD 3: tokens * topk
 };
+
+// Eight bf16 values times w, each product one fp32 operation rounded to bf16 (nearest even).
+__device__ __forceinline__ u32x4 scale_bf16x8(const u32x4& v, float w) {
+  return u32x4{sw_pack(w * bf16_lo(v.x), w * bf16_hi(v.x)), sw_pack(w * bf16_lo(v.y), w * bf16_hi(v.y)),
+               sw_pack(w * bf16_lo(v.z), w * bf16_hi(v.z)), sw_pack(w * bf16_lo(v.w), w * bf16_hi(v.w))};
+}
 
 // The 16 columns [col, col + 16) of tensor row `row` (cols columns) as two 8-column chunks.
 template <int PROD>
@@ -399,6 +409,22 @@ __device__ __forceinline__ void dual_load(const DualSrc& sr, int64_t row, int co
     const uint16_t* p = sr.x + row * cols + col;
     v0 = *reinterpret_cast<const u32x4*>(p);
     v1 = *reinterpret_cast<const u32x4*>(p + 8);
+  } else if constexpr (PROD == 3) {
+    // grouped row `row` holds routing slot s = src[row] of token s / topk (a zero row for no slot),
+    // times the slot's router weight when weights are given
+    const int sl = sr.src[row];
+    if (sl < 0 || (int64_t)sl >= sr.slots) {
+      v0 = v1 = u32x4{0, 0, 0, 0};
+      return;
+    }
+    const uint16_t* p = sr.x + (int64_t)(sl / sr.topk) * cols + col;
+    v0 = *reinterpret_cast<const u32x4*>(p);
+    v1 = *reinterpret_cast<const u32x4*>(p + 8);
+    if (sr.gw != nullptr) {
+      const float wj = sr.gw[sl];
+      v0 = scale_bf16x8(v0, wj);
+      v1 = scale_bf16x8(v1, wj);
+    }
   } else if constexpr (PROD == 1) {
     const uint16_t* g = sr.h1 + row * sr.ld_h1 + col;
     const u32x4 g0 = *reinterpret_cast<const u32x4*>(g), g1 = *reinterpret_cast<const u32x4*>(g + 8);
@@ -709,6 +735,24 @@ hipError_t launch_swiglu_mx_dual(const uint16_t* h1, const uint16_t* da2, int64_
                                        offs_pad_out, grid, n_strips, st)
                    : launch_dual<1, 1>(sr, 1, rows, cols, offs, n_groups, k4, q, sc, q_t, sc_t, rows_pad,
                                        offs_pad_out, grid, n_strips, st);
+}
+
+hipError_t launch_moe_permute_mx_dual(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
+                                     const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups,
+                                     int rule, int scale_layout, uint16_t* xg, uint8_t* q, uint8_t* sc, uint8_t* q_t,
+                                     uint8_t* sc_t, int64_t rows_pad, int32_t* offs_pad_out, hipStream_t st) {
+  const bool k4 = scale_layout == 1;
+  if (cols == 0 && offs_pad_out == nullptr) return hipSuccess;
+  const int n_strips = (int)std::max<int64_t>((cols + kDualCols - 1) / kDualCols, 1);
+  const int64_t blocks = mx_dual_grid_bound(1, rows, cols, true, n_groups, rows_pad);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
+  const DualSrc sr{x, nullptr, nullptr, 0, 0, xg, src, weights, topk, tokens * topk};
+  auto kern = rule == 0 ? (k4 ? mx_dual_kernel<0, true, true, 3> : mx_dual_kernel<0, true, false, 3>)
+                        : (k4 ? mx_dual_kernel<1, true, true, 3> : mx_dual_kernel<1, true, false, 3>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, sr, (int64_t)1, (int)rows, (int)cols, offs, n_groups, q, sc, rows,
+                     q_t, sc_t, rows_pad, offs_pad_out, n_strips);
+  return hipGetLastError();
 }
 
 }  // namespace fp8moe

@@ -117,6 +117,23 @@ int check_quantize_mx_dual(const void* x, int64_t batch, int64_t rows, int64_t c
   return FP8MOE_OK;
 }
 
+int check_moe_permute_mx_dual(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                              const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups, int rule,
+                              int scale_layout, const void* xg, const void* q, const void* sc, const void* q_t,
+                              const void* sc_t, int64_t rows_pad, const int32_t* offs_pad_out) {
+  if (tokens < 0 || cols < 0 || topk < 1 || rows < 0 || cols > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk), nx = mul(tokens, cols);
+  if (S < 0 || S > kI32Max || nx < 0) return FP8MOE_ERR_SHAPE;
+  if (offs == nullptr) return FP8MOE_ERR_NULL;   // the grouped layout of moe_route
+  // the gathered [rows][cols] tensor: q stands in for its pointer and alignment
+  const int st = check_quantize_mx_dual(rows && cols ? q : nullptr, 1, rows, cols, offs, n_groups, rule, scale_layout,
+                                        q, sc, q_t, sc_t, rows_pad, offs_pad_out);
+  if (st) return st;
+  if (!need(x, nx) || !need(src, rows)) return FP8MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xg, 16) || !aligned(src, 4) || !aligned(weights, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int check_swiglu_mx_dual(const void* h1, const void* da2, bool backward, int64_t rows, int64_t F, int64_t ld_h1,
                          const int32_t* offs, int32_t n_groups, int rule, int scale_layout, const void* out,
                          const void* q, const void* sc, const void* q_t, const void* sc_t, int64_t rows_pad,
@@ -376,8 +393,7 @@ int check_moe_combine_backward(const void* dy, const void* yg, int64_t rows, con
   const int64_t S = mul(tokens, topk), ny = mul(tokens, cols), ng = mul(rows, cols);
   if (S < 0 || S > kI32Max || ny < 0 || ng < 0 || tokens > kI32Max - 1024) return FP8MOE_ERR_SHAPE;
   if ((q == nullptr) != (scale == nullptr)) return FP8MOE_ERR_NULL;   // codes and scales come together
-  if (!need(dy, ny) || !need(yg, ng) || !need(dest, S) || !need(src, rows) || !need(w, S) || !need(dyg, ng) ||
-      !need(dw, S))
+  if (!need(dy, ny) || !need(yg, ng) || !need(dest, S) || !need(src, rows) || !need(w, S) || !need(dw, S))
     return FP8MOE_ERR_NULL;
   if (cols % 8 || !aligned(dy, 16) || !aligned(yg, 16) || !aligned(dyg, 16) || !aligned(q, 16) ||
       !aligned(dest, 4) || !aligned(src, 4) || !aligned(w, 4) || !aligned(scale, 4) || !aligned(dw, 4))

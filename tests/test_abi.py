@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 9):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 106
+    assert lib.fp8moe_version() == 107
 
 
 def test_rows_bound(lib):
@@ -247,7 +247,7 @@ def test_route_rejections(lib):
     assert cb(P, P, 8, P, P, P, 4, 2, 16392, 0, P, P, P, P, None) == L.ERR_UNSUPPORTED
     assert cb(P, P, 8, P, P, P, 4, 2, 16, 0, P, None, P, P, None) == L.ERR_NULL   # codes without scales
     assert cb(P, P, 8, P, P, P, 4, 2, 16, 0, P, P, None, P, None) == L.ERR_NULL
-    for i in (0, 1, 3, 4, 5, 10, 13):
+    for i in (0, 1, 3, 4, 5, 13):       # (dyg, index 10, may be NULL: the rows are then not written)
         args = [P, P, 8, P, P, P, 4, 2, 16, 0, P, P, P, P, None]
         args[i] = None
         assert cb(*args) == L.ERR_NULL, i
@@ -307,6 +307,30 @@ def test_mx_dual_rejections(lib):
     assert d(MIS, 1, 64, 64, None, 0, 0, 0, P, P, P, P, 64, None, None) == L.ERR_ALIGN
     assert d(P, 1, 64, 64, None, 0, 0, 0, MIS, P, P, P, 64, None, None) == L.ERR_ALIGN
     assert d(P, 1, 64, 64, None, 0, 0, 0, P, P, MIS, P, 64, None, None) == L.ERR_ALIGN
+
+
+def test_moe_permute_mx_dual_rejections(lib):
+    f = lib.moe_permute_quantize_mx_dual
+    # (x, tokens, cols, topk, src, weights, rows, offs, n_groups, rule, layout, xg, q, sc, q_t, sc_t, rows_pad,
+    #  offs_pad, stream)
+    ok = [P, 32, 64, 2, P, None, 64, P, 4, 0, 1, None, P, P, P, P, 64 + 128, P, None]
+    def call(args, i=None, v=None):
+        a = list(args)
+        if i is not None:
+            a[i] = v
+        return f(*a)
+    assert call(ok, 9, 5) == L.ERR_ENUM                   # rule
+    assert call(ok, 10, 2) == L.ERR_ENUM                  # scale layout
+    assert call(ok, 3, 0) == L.ERR_SHAPE                  # topk
+    assert call(ok, 1, -1) == L.ERR_SHAPE                 # tokens
+    assert call(ok, 1, 1 << 31) == L.ERR_SHAPE            # tokens * topk past int32
+    assert call(ok, 16, 64) == L.ERR_SHAPE                # rows_pad below the bound
+    assert call(ok, 7, None) == L.ERR_NULL                # offs: the grouped layout is required
+    for i in (0, 4, 12, 13, 14, 15):                      # x, src, both codes and both scales
+        assert call(ok, i, None) == L.ERR_NULL, i
+    assert call(ok, 2, 48) == L.ERR_ALIGN                 # cols % 32
+    for i, bad in ((0, MIS), (11, MIS), (12, MIS), (4, P + 2), (5, P + 2)):
+        assert call(ok, i, bad) == L.ERR_ALIGN, i
 
 
 def test_swiglu_mx_dual_rejections(lib):

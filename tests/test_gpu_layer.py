@@ -57,8 +57,9 @@ LAYER = {
     3: ["route", "permute+q X", "q_row W1", "gemm fwd W1", "swiglu+q", "q_row W2", "gemm fwd W2", "combine",
         "combine bwd+q", "q_col W2", "gemm dgrad W2", "q_col dYg", "q_col A2", "gemm wgrad W2", "swiglu bwd+q",
         "q_col W1", "gemm dgrad W1", "q_col dH1", "q_col Xg", "gemm wgrad W1", "combine dX"],
-    5: ["route", "permute X", "mx Xg (both forms)", "mx W1 (both forms)", "gemm fwd W1", "swiglu+mx A2 (both forms)",
-        "mx W2 (both forms)", "gemm fwd W2", "combine", "combine bwd", "mx dYg (both forms)", "gemm dgrad W2",
+    5: ["route", "permute+mx Xg (both forms)", "mx W1 (both forms)", "gemm fwd W1", "swiglu+mx A2 (both forms)",
+        "mx W2 (both forms)", "gemm fwd W2", "combine", "combine bwd (dw)", "permute+mx dYg (both forms)",
+        "gemm dgrad W2",
         "gemm wgrad W2", "swiglu bwd+mx dH1 (both forms)", "gemm dgrad W1", "gemm wgrad W1", "combine dX"],
 }
 LAYER[4] = LAYER[3]
@@ -89,7 +90,9 @@ def layer(request):
 # ------------------------------------------------------------------ helpers
 
 def _src(hst, name):
-    """A named host input, or a host copy of a device tensor the step computed."""
+    """A named host input, a host array, or a host copy of a device tensor the step computed."""
+    if isinstance(name, np.ndarray):
+        return name
     if not isinstance(name, str):
         if id(name) not in _DEV_CACHE:
             _DEV_CACHE[id(name)] = host(name)
@@ -233,6 +236,20 @@ def check_mx_dual(sp, hst, phase):
         last["shape"] = (B * R, C)
         check_mx_last(last, hst, phase)
         check_mx_rows_b(dict(src=sp["src"], shape=sp["shape"], rule=sp["rule"], q=sp["qt"], s=sp["st"]), hst, phase)
+
+
+def check_permute_mx_dual(sp, hst, phase):
+    """The gather into the grouped layout fused with both MX forms: the gathered rows (times the router
+    weights for the routed-row gradients) are formed here by the oracle's permute (or combine backward)
+    from the step's own routing, then checked as check_mx_dual checks a tensor in memory."""
+    x, rsrc, dest, k = hst[sp["x"]], _src(hst, sp["rsrc"]), _src(hst, sp["dest"]), sp["topk"]
+    T, C = x.shape
+    if sp["w"] is None:
+        g = o_route.permute(x, rsrc, k)
+    else:
+        g, _ = o_route.combine_backward(x, np.zeros((rsrc.size, C), np.uint16), rsrc, dest, hst[sp["w"]], T, k)
+    check_mx_dual(dict(src=g, shape=sp["shape"], offs=sp["offs"], rows_pad=sp["rows_pad"], rule=sp["rule"],
+                       q=sp["q"], s=sp["s"], qt=sp["qt"], st=sp["st"], offs_pad=sp["offs_pad"]), hst, phase)
 
 
 def check_swiglu_mx(sp, hst, phase):
@@ -419,8 +436,9 @@ def check_combine_bwd(sp, hst, phase):
     take, d_sub = _sub_routing(dest, toks, k)
     s_sub = np.arange(d_sub.size, dtype=np.int32)
     dyg_ref, dw_ref = o_route.combine_backward(dy[toks], yg[take], s_sub, d_sub, wts[toks], len(toks), k)
-    dyg = _src(hst, sp["dyg"])
-    assert_bytes_equal(dyg[take], dyg_ref, "routed-row gradients")
+    dyg = _src(hst, sp["dyg"]) if sp["dyg"] is not None else None     # None: router-weight gradients only
+    if dyg is not None:
+        assert_bytes_equal(dyg[take], dyg_ref, "routed-row gradients")
     if sp["q"] is not None:
         q, s = oracle.quantize_rowwise(dyg_ref, 0)
         assert_bytes_equal(_src(hst, sp["q"])[take], q, "codes")
@@ -430,14 +448,15 @@ def check_combine_bwd(sp, hst, phase):
     mag = np.einsum("sc,sc->s", np.abs(bf16_bits_to_f64(dy[toks]).repeat(k, axis=0)),
                     np.abs(bf16_bits_to_f64(yg[take])))
     assert np.all(np.abs(dw - dw_ref) <= dy.shape[1] * 2.0 ** -24 * mag), "router-weight gradients"
-    pad = rsrc < 0                                      # rows holding no slot are zeros
-    assert not dyg[pad].any()
+    if dyg is not None:
+        pad = rsrc < 0                                  # rows holding no slot are zeros
+        assert not dyg[pad].any()
 
 
 CHECKS = {"q_row": check_q_row, "q_col_grouped": check_q_col_grouped, "q_col_batched": check_q_col_batched,
           "mx_last": check_mx_last, "mx_rows_b": check_mx_rows_b, "mx_rows_g": check_mx_rows_g,
           "g_m": check_g_m, "g_k": check_g_k, "g_k_bf16": check_g_k_bf16,
-          "mx_dual": check_mx_dual, "swiglu_mx": check_swiglu_mx, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
+          "mx_dual": check_mx_dual, "permute_mx_dual": check_permute_mx_dual, "swiglu_mx": check_swiglu_mx, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
           "swiglu": check_swiglu, "swiglu_bwd": check_swiglu_bwd, "combine": check_combine,
           "combine_bwd": check_combine_bwd}
 

@@ -297,22 +297,41 @@ def test_mx_cast_every_bf16_value(rule):
 def _dual_check(x, xq, offs, rule, layout, rows_pad, what):
     """quantize_mx_dual against the oracle's last-dim and row-block quantizers (and so against the two
     quantize_mx calls it stands for), with sentinels in every output."""
+    q, sc, q_t, sc_t = _dual_outputs(x.shape, offs is not None, layout, rows_pad)
+    note(f"mx dual {what} rule={rule} layout={layout} shape={x.shape}")
+    outs = fm.quantize_mx_dual(xq, None if offs is None else i32_dev(offs), rule=rule, rows_pad=rows_pad, q=q,
+                               scale=sc, q_t=q_t, scale_t=sc_t, layout=layout)
+    _dual_verify(x, offs, rule, layout, rows_pad, outs, what)
+
+
+def _dual_outputs(x_shape, grouped, layout, rows_pad):
+    """Sentinel-filled outputs of the dual MX quantizers for a [B, R, C] (not grouped) or [R, C] tensor."""
     k4 = layout == fm.MX_LAYOUT_K4
-    if offs is None:
-        B, R, C = x.shape
+    if not grouped:
+        B, R, C = x_shape
         rows_total, scale_t_rows, nb_t = B * R, B * C, R // 32
         q_t = filled_u8((B, C, R))
     else:
-        (R, C), B = x.shape, 1
+        (R, C), B = x_shape, 1
         rows_total, scale_t_rows, nb_t = R, C, rows_pad // 32
         q_t = filled_u8((C, rows_pad))
     q = filled_u8((rows_total, C))
     sc = filled_u8(fm.mx_k4_shape(rows_total, C // 32) if k4 else (rows_total, C // 32))
     sc_t = filled_u8(fm.mx_k4_shape(scale_t_rows, nb_t) if k4 else (scale_t_rows, nb_t))
-    note(f"mx dual {what} rule={rule} layout={layout} shape={x.shape}")
-    q, sc, q_t, sc_t, op = fm.quantize_mx_dual(xq, None if offs is None else i32_dev(offs), rule=rule,
-                                               rows_pad=rows_pad, q=q, scale=sc, q_t=q_t, scale_t=sc_t,
-                                               layout=layout)
+    return q, sc, q_t, sc_t
+
+
+def _dual_verify(x, offs, rule, layout, rows_pad, outs, what):
+    """Both MX forms `outs` = (q, sc, q_t, sc_t, offs_pad) of the host tensor x against the oracle's last-dim
+    and row-block quantizers; last-dim rows past the last group must keep their sentinel."""
+    q, sc, q_t, sc_t, op = outs
+    k4 = layout == fm.MX_LAYOUT_K4
+    if offs is None:
+        B, R, C = x.shape
+        rows_total, scale_t_rows, nb_t = B * R, B * C, R // 32
+    else:
+        (R, C), B = x.shape, 1
+        rows_total, scale_t_rows, nb_t = R, C, rows_pad // 32
     x2 = x.reshape(rows_total, C)
     if offs is None:
         covered = rows_total
@@ -390,6 +409,43 @@ def test_mx_dual_llama4_scout_weights_sampled():
     rows = _sample(w.E * w.H, 64, 11)
     ql, sl = oracle.quantize_mx_lastdim(xh.reshape(-1, w.F)[rows], 0)
     assert_bytes_equal(host(q)[rows], ql, "last-dim codes sampled")
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("rule,layout", [(0, fm.MX_LAYOUT_K4), (1, fm.MX_LAYOUT_ROWS)])
+@pytest.mark.parametrize("shape", [(700, 2, 5, 320), (96, 1, 3, 32), (0, 2, 4, 64)])
+def test_moe_permute_mx_dual(weighted, rule, layout, shape):
+    """The gather into moe_route's grouped layout fused with both MX forms: the same bytes as the oracle's
+    gather (or, with router weights, the routed-row gradients of the oracle's combine backward) quantized by
+    the oracle's MX quantizers; the optional bf16 copy equals the gathered rows; rows past the last group
+    keep their sentinels.  Dropped slots (ids -1) leave zero rows."""
+    from oracle import route as rt
+    T, k, E, C = shape
+    rng = np.random.default_rng(T + 7 * k + C + 2 * weighted)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 10:
+        ids[rng.random((T, k)) < 0.03] = -1
+    x = synth.normal_bf16(9100 + T + C, (T, C), 1.0, 0.01, 30.0)
+    counts, offs, dest, src = fm.moe_route(i32_dev(ids), E, 1)
+    R = src.numel()
+    w = (rng.random((T, k)) + 0.05).astype(np.float32) if weighted else None
+    rows_pad = fm.quantize_mx_rows_bound(R, E) + 32
+    q, sc, q_t, sc_t = _dual_outputs((R, C), True, layout, rows_pad)
+    xg = torch.full((R, C), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    note(f"moe_permute_quantize_mx_dual T={T} k={k} E={E} C={C} rows={R} weighted={weighted} rule={rule}")
+    got = fm.moe_permute_quantize_mx_dual(bf16_dev(x), src, k, offs, weights=None if w is None else
+                                          torch.from_numpy(w).to(DEV), rule=rule, rows_pad=rows_pad, xg=xg, q=q,
+                                          scale=sc, q_t=q_t, scale_t=sc_t, layout=layout)
+    src_h, dest_h, offs_h = host(src), host(dest), host(offs)
+    if w is None:
+        ref = rt.permute(x, src_h, k)
+    else:
+        ref, _ = rt.combine_backward(x, np.zeros((R, C), np.uint16), src_h, dest_h, w, T, k)
+    covered = int(offs_h[-1]) if E else 0
+    xg_h = host(got[0])
+    assert_bytes_equal(xg_h[:covered], ref[:covered], "gathered rows (bf16 copy)")
+    assert np.all(xg_h.view(np.uint16)[covered:] == 0x5A5A), "copy rows past the last group untouched"
+    _dual_verify(ref, offs_h, rule, layout, rows_pad, got[1:], f"permute mx dual weighted={weighted}")
 
 
 # ------------------------------------------------------------------- full-size, sampled
