@@ -295,18 +295,32 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
                                offs_pad=op))
             return q, s, qt, st
 
-        xg = dyg = None                      # the gathered bf16 rows (the MX path never forms them)
+        xg = dyg = None                      # the gathered bf16 rows: neither recipe forms them in memory
+
+        def q_col_gathered(name, x, x_name, wts, w_name):
+            """The colwise quantization of the token rows x gathered into the grouped layout (times the
+            router weights when given): the gathered rows are formed at load time."""
+            ld = (rows + 15) // 16 * 16
+            q, s = u8(H, ld), f32(E, H)
+            step.add(name, "quant",
+                     lambda: fm.moe_permute_quantize_colwise(x(), r_src, k, offs, weights=wts, codec=0, q_t=q,
+                                                             scale=s, ld_q=ld),
+                     2 * T * H + rows * H + 4 * E * H + 4 * rows + (4 * S if wts is not None else 0),
+                     spec=dict(op="permute_q_col", x=x_name, rsrc=r_src, dest=r_dest, topk=k, w=w_name, offs=offs_np,
+                               q=q, s=s))
+            return q, s, ld
+
         if w.mx:
             qx, sx, qxt, sxt = mx_gather("permute+mx Xg (both forms)", Xd, "X", None, None)
             qw1, sw1, qw1t, sw1t = mx_dual_b("mx W1 (both forms)", "W1", W1d, E, F2, H)
             h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H, sk=fm.SCALE_E8M0_K4)
         else:
-            xg = bf(rows, H)
+            # the gathered rows' bf16 copy is not kept: the weight gradient's colwise operand is gathered again
             qx, sx = u8(rows, H), f32(rows)
             step.add("permute+q X", "moe",
-                     lambda: fm.moe_permute_rowwise(Xd(), r_src, k, 0, xg=xg, qg=qx, scale_g=sx),
-                     5 * rows * H + 8 * rows,
-                     spec=dict(op="permute_rowwise", src="X", topk=k, rsrc=r_src, xg=xg, q=qx, s=sx))
+                     lambda: fm.moe_permute_rowwise(Xd(), r_src, k, 0, keep_bf16=False, qg=qx, scale_g=sx),
+                     3 * rows * H + 8 * rows,
+                     spec=dict(op="permute_rowwise", src="X", topk=k, rsrc=r_src, xg=None, q=qx, s=sx))
             qw1, sw1 = q_row("q_row W1", "W1", W1d, E * F2, H)
             h1 = g_m("gemm fwd W1", qx, sx, qw1, sw1, rows, F2, H)
         if w.mx:
@@ -346,17 +360,18 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
             da2 = g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, rows, F, H, sk=fm.SCALE_E8M0_K4)
             g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, Mp, H, F, sk=fm.SCALE_E8M0_K4, offs_t=op)
         else:
-            dyg = bf(rows, H)
+            # routed-row gradients quantized rowwise in the combine backward; their colwise operand is
+            # gathered from dY again, so the grouped bf16 dYg never goes to memory
             qdy, sdy = u8(rows, H), f32(rows)
             step.add("combine bwd+q", "moe",
-                     lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, dyg=dyg, q=qdy, scale=sdy,
-                                                     dweights=dw),
-                     2 * T * H + 5 * rows * H + 4 * rows + 16 * S,
-                     spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=dyg,
+                     lambda: fm.moe_combine_backward(DYd(), yg, r_dest, r_src, rwd, k, 0, rows_out=False, q=qdy,
+                                                     scale=sdy, dweights=dw),
+                     2 * T * H + 3 * rows * H + 4 * rows + 16 * S,
+                     spec=dict(op="combine_bwd", dy="DY", yg=yg, dest=r_dest, src=r_src, w="RW", topk=k, dyg=None,
                                q=qdy, s=sdy, dw=dw))
             qw2t, sw2t = q_col_batched("q_col W2", "W2", W2d, E, H, F)
             da2 = g_m("gemm dgrad W2", qdy, sdy, qw2t, sw2t, rows, F, H)
-            qdyt, sdyt, ld = q_col_grouped("q_col dYg", dyg, lambda: dyg, rows, H)
+            qdyt, sdyt, ld = q_col_gathered("q_col dYg (gathered)", DYd, "DY", rwd, "RW")
             qa2t, sa2t, _ = q_col_grouped("q_col A2", a2, lambda: a2, rows, F)
             g_k("gemm wgrad W2", qdyt, sdyt, qa2t, sa2t, ld, H, F)
         if w.mx:
@@ -381,7 +396,7 @@ def build_step(cfg: int, gw: bool, tensorwise: bool = False, n_rotate: int = N_R
             qw1t, sw1t = q_col_batched("q_col W1", "W1", W1d, E, F2, H)
             dxg = g_m("gemm dgrad W1", qdh, sdh, qw1t, sw1t, rows, H, F2)
             qdht, sdht, _ = q_col_grouped("q_col dH1", dh1, lambda: dh1, rows, F2)
-            qxt, sxt, _ = q_col_grouped("q_col Xg", xg, lambda: xg, rows, H)
+            qxt, sxt, _ = q_col_gathered("q_col Xg (gathered)", Xd, "X", None, None)
             g_k("gemm wgrad W1", qdht, sdht, qxt, sxt, ld, F2, H)
         dx = bf(T, H)
         step.add("combine dX", "moe", lambda: fm.moe_combine(dxg, r_dest, None, k, y=dx), 2 * S * H + 2 * T * H + 4 * S,
@@ -567,6 +582,16 @@ def cpu_baseline(step, host: dict):
 
     from oracle import route as o_route, swiglu as o_swiglu
 
+    def gathered(sp, x, s_rows, cols):
+        """The oracle's gather of rows s_rows (first `cols` columns) of the token rows x, or with router
+        weights the routed-row gradients of its combine backward."""
+        xs, k = np.ascontiguousarray(x[:, :cols]), sp["topk"]
+        if sp["w"] is None:
+            return o_route.permute(xs, s_rows, k)
+        T = x.shape[0]
+        return o_route.combine_backward(xs, np.zeros((s_rows.size, cols), np.uint16), s_rows,
+                                        np.full(T * k, -1, np.int32), host[sp["w"]], T, k)[0]
+
     for name, kind, *_ in step.items:
         sp = step.specs.get(name)
         if sp is None:
@@ -653,23 +678,20 @@ def cpu_baseline(step, host: dict):
                 t_r = timed(lambda: oracle.quantize_mx_rows_batched(xs, sp["rule"]), 1) * (C / c)
             add(name, t_l + t_r, 1.0)
         elif op == "permute_mx_dual":
-            x, rsrc, k = host[sp["x"]], src(sp["rsrc"]), sp["topk"]
+            x, rsrc = host[sp["x"]], src(sp["rsrc"])
             M, C = sp["shape"]
-            T = x.shape[0]
             r = max(1, min(M, QS // max(C, 1)))
             c = max(32, min(C, QS // max(M, 1)) // 32 * 32)
-            no_dest = np.full(T * k, -1, np.int32)
-
-            def gather(s_rows, cols):
-                xs = np.ascontiguousarray(x[:, :cols])
-                if sp["w"] is None:
-                    return o_route.permute(xs, s_rows, k)
-                return o_route.combine_backward(xs, np.zeros((s_rows.size, cols), np.uint16), s_rows, no_dest,
-                                                host[sp["w"]], T, k)[0]
-            t_l = timed(lambda: oracle.quantize_mx_lastdim(gather(rsrc[:r], C), sp["rule"]), 1) * (M / r)
-            t_r = timed(lambda: oracle.quantize_mx_rows_grouped(gather(rsrc, c), sp["offs"], sp["rule"],
+            t_l = timed(lambda: oracle.quantize_mx_lastdim(gathered(sp, x, rsrc[:r], C), sp["rule"]), 1) * (M / r)
+            t_r = timed(lambda: oracle.quantize_mx_rows_grouped(gathered(sp, x, rsrc, c), sp["offs"], sp["rule"],
                                                                 sp["rows_pad"]), 1) * (C / c)
             add(name, t_l + t_r, 1.0)
+        elif op == "permute_q_col":
+            x, rsrc = host[sp["x"]], src(sp["rsrc"])
+            M, C = rsrc.size, x.shape[1]
+            c = max(8, min(C, QS // max(M, 1)) // 8 * 8)
+            add(name, timed(lambda: oracle.quantize_colwise_grouped(gathered(sp, x, rsrc, c), sp["offs"], 0), 1),
+                C / c)
         elif op == "swiglu_mx":
             h1 = src(sp["h1"])
             R, F = h1.shape[0], sp["F"]

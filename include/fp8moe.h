@@ -472,6 +472,34 @@ int quantize_colwise(const void *x_bf16, int64_t batch, int64_t rows, int64_t co
                      void *q_t, int64_t ld_q, float *scale, void *stream);
 
 /*
+ * moe_permute_quantize_colwise -- the gather of token rows into moe_route's
+ * grouped layout fused with quantize_colwise of the gathered tensor: the rows
+ * are formed at load time and never go to memory.  With router weights it
+ * forms, the same way, the routed-row gradients of moe_combine_backward from
+ * the output gradient dy (the weight gradient's colwise operand; the rowwise
+ * one comes from moe_combine_backward in the same backward pass).
+ *   [as quantize_colwise; P1 Details, MoE paragraph (the routed rows quantized
+ *   by a fused kernel ahead of the grouped GEMM); P4 "MoE" (the experts' outputs
+ *   summed with the router's weights); P4 "Три уровня оптимизации
+ *   Triton-ядер" (fused backward scale-and-cast).]
+ *   x        bf16 [tokens][cols]  token rows (or dy)
+ *   src      int32 [rows]         from moe_route: grouped row r holds slot
+ *                                 s = src[r] of token s / topk; a row whose
+ *                                 src is < 0 or >= tokens*topk is zeros
+ *   weights  f32 [tokens*topk], or NULL: row r = bf16(weights[s] * x[s / topk]),
+ *            one fp32 product rounded to nearest even; NULL: row r = x[s / topk]
+ *   q_t, ld_q, scale, offs, n_groups, codec: as quantize_colwise of the gathered
+ *   [rows][cols] tensor in its grouped form (offs required, non-NULL); the same
+ *   kernels, paths and shared-state rules.
+ *   Requires: tokens*topk <= INT32_MAX; x 16-byte aligned, src and weights
+ *   4-byte aligned; the rest as quantize_colwise.  No allocation.
+ */
+int moe_permute_quantize_colwise(const void *x_bf16, int64_t tokens, int64_t cols, int32_t topk,
+                                 const int32_t *src, const float *weights, int64_t rows,
+                                 const int32_t *offs, int32_t n_groups, int codec, void *q_t,
+                                 int64_t ld_q, float *scale, void *stream);
+
+/*
  * quantize_mx -- MXFP8: e4m3fn codes with one e8m0 scale per 1x32 block.
  *   [P2 Details: _to_mxfp8_then_scaled_grouped_mm quantizes activations and
  *   weights dynamically; MXFP8 data/scale layout diagram; wgrad quantized along

@@ -21,7 +21,7 @@ __all__ = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "MX_CEIL", "MX_LAYOUT_ROWS", "MX_LAYOUT_K4", "GROUPED_M", "GROUPED_K", "OPD_E4M3FN", "OPD_E4M3FNUZ",
            "OPD_BF16", "SCALE_F32", "SCALE_E8M0", "SCALE_NONE", "SCALE_E8M0_K4", "OUT_BF16", "OUT_F32",
            "mx_k4_shape", "quantize_mx_dual", "swiglu_quantize_mx_dual", "swiglu_backward_quantize_mx_dual",
-           "moe_permute_quantize_mx_dual",
+           "moe_permute_quantize_mx_dual", "moe_permute_quantize_colwise",
            "Fp8MoeError", "swiglu_quantize_rowwise",
            "swiglu_backward_quantize_rowwise", "moe_route", "moe_route_noalloc", "moe_route_rows_bound", "moe_route_workspace_bytes", "moe_permute", "moe_combine",
            "moe_permute_rowwise", "moe_combine_backward",
@@ -80,6 +80,27 @@ def quantize_colwise(x, offs=None, codec=E4M3FN, q_t=None, scale=None, ld_q=None
         scale = torch.empty((B, C), dtype=torch.float32, device=x.device) if scale is None else scale
     _lib.check("quantize_colwise", _lib.lib().quantize_colwise(
         _ptr(x), B, R, C, _ptr(offs), E, codec, _ptr(q_t), ld_q, _ptr(scale), _stream(stream)))
+    return q_t, scale
+
+
+def moe_permute_quantize_colwise(x, src, topk, offs, weights=None, codec=E4M3FN, q_t=None, scale=None, ld_q=None,
+                                 stream=None):
+    """x bf16 [T, C] (token rows, or the output gradient dy), src int32 [R], offs int32 [E] from moe_route,
+    weights f32 [T, topk] or None -> (q_t uint8 phys [C, ld_q], scale [E, C]): quantize_colwise of the gathered
+    rows x[src[r] // topk] (times weights[src[r]] when given, rounded to bf16), which never go to memory."""
+    x = _bits(x).contiguous()
+    T, C = x.shape
+    R, E = src.numel(), offs.numel()
+    if weights is not None:
+        weights = weights.contiguous()
+        if weights.dtype != torch.float32 or weights.numel() != T * topk:
+            raise ValueError("moe_permute_quantize_colwise: weights f32 [T, topk]")
+    ld_q = ld_q or (R + 15) // 16 * 16
+    q_t = torch.empty((C, ld_q), dtype=torch.uint8, device=x.device) if q_t is None else q_t
+    scale = torch.empty((E, C), dtype=torch.float32, device=x.device) if scale is None else scale
+    _lib.check("moe_permute_quantize_colwise", _lib.lib().moe_permute_quantize_colwise(
+        _ptr(x), T, C, topk, _ptr(src), _ptr(weights), R, _ptr(offs), E, codec, _ptr(q_t), ld_q, _ptr(scale),
+        _stream(stream)))
     return q_t, scale
 
 

@@ -28,7 +28,7 @@ EXPORTS = ["quantize_rowwise", "quantize_colwise", "quantize_mx", "quantize_mx_r
            "blockwise_token_blocks_bound", "grouped_mm_blockwise_k",
            "quantize_tensorwise_workspace_bytes", "fp8moe_set_colwise_poll_budget", "fp8moe_set_colwise_chunk_rows", "moe_route_noalloc",
            "moe_permute_rowwise", "moe_combine_backward", "quantize_mx_dual", "swiglu_quantize_mx_dual",
-           "swiglu_backward_quantize_mx_dual", "moe_permute_quantize_mx_dual"]
+           "swiglu_backward_quantize_mx_dual", "moe_permute_quantize_mx_dual", "moe_permute_quantize_colwise"]
 
 _lib = None
 
@@ -37,6 +37,8 @@ _vp, _i64, _i32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.
 _SIGS = {
     "quantize_rowwise": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),
     "quantize_colwise": (_int, [_vp, _i64, _i64, _i64, _vp, _i32, _int, _vp, _i64, _vp, _vp]),
+    "moe_permute_quantize_colwise": (_int, [_vp, _i64, _i64, _i32, _vp, _vp, _i64, _vp, _i32, _int, _vp, _i64, _vp,
+                                            _vp]),
     "quantize_mx": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i32, _int, _int, _vp, _vp, _i64, _vp, _vp]),
     "quantize_mx_rows_bound": (_i64, [_i64, _i32]),
     "grouped_mm_scaled": (_int, [_int, _vp, _int, _vp, _vp, _int, _vp, _int, _vp, _i32, _i64, _i64, _i64,

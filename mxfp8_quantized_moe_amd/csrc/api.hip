@@ -209,6 +209,17 @@ int quantize_colwise(const void* x_bf16, int64_t batch, int64_t rows, int64_t co
                                                as_stream(stream)));
 }
 
+int moe_permute_quantize_colwise(const void* x_bf16, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                                 const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups, int codec,
+                                 void* q_t, int64_t ld_q, float* scale, void* stream) {
+  const int st = check_moe_permute_colwise(x_bf16, tokens, cols, topk, src, weights, rows, offs, n_groups, codec, q_t,
+                                           ld_q, scale);
+  if (st) return st;
+  return launch_status(launch_moe_permute_colwise(static_cast<const uint16_t*>(x_bf16), tokens, cols, topk, src,
+                                                  weights, rows, offs, n_groups, codec, static_cast<uint8_t*>(q_t),
+                                                  ld_q, scale, as_stream(stream)));
+}
+
 int quantize_mx(const void* x_bf16, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,
                 int32_t n_groups, int rule, int scale_layout, void* q, void* scale_e8m0, int64_t rows_pad,
                 int32_t* offs_pad_out, void* stream) {
@@ -320,6 +331,6 @@ int fp8moe_set_colwise_poll_budget(int polls) { return set_colwise_poll_budget(p
 
 int fp8moe_set_colwise_chunk_rows(int rows) { return set_colwise_chunk_rows(rows); }
 
-int fp8moe_version(void) { return 107; }
+int fp8moe_version(void) { return 108; }
 
 }  // extern "C"

@@ -26,6 +26,40 @@ struct alignas(8) u32x2 { uint32_t x, y; };
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
+// Eight packed bf16 values times w: each product one fp32 operation, rounded to
+// bf16 (nearest even) -- the combine backward's routed-row gradient w * dy.
+typedef float dc_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 dc_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_times(uint32_t v, float w) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(dc_f32x2{w * bf16_lo(v), w * bf16_hi(v)}, dc_bf16x2));
+}
+__device__ __forceinline__ u32x4 bf16x8_times(const u32x4& v, float w) {
+  return u32x4{bf16x2_times(v.x, w), bf16x2_times(v.y, w), bf16x2_times(v.z, w), bf16x2_times(v.w, w)};
+}
+
+// Row r of a tensor of `cols` bf16 columns, 8 columns from `col`: x row r, or
+// (gathered into moe_route's grouped layout, src non-null) token row
+// src[r] / topk of x, times the slot's router weight w[src[r]] when w is
+// non-null, and zeros for a row whose slot is < 0 or >= slots.
+struct RowSrc {
+  const uint16_t* x;
+  const int32_t* src;
+  const float* w;
+  int topk;
+  int64_t slots;
+};
+template <bool GATHER>
+__device__ __forceinline__ u32x4 row_load8(const RowSrc& s, int64_t r, int64_t cols, int col) {
+  if constexpr (!GATHER) {
+    return *reinterpret_cast<const u32x4*>(s.x + r * cols + col);
+  } else {
+    const int sl = s.src[r];
+    if (sl < 0 || (int64_t)sl >= s.slots) return u32x4{0, 0, 0, 0};
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s.x + (int64_t)(sl / s.topk) * cols + col);
+    return s.w != nullptr ? bf16x8_times(v, s.w[sl]) : v;
+  }
+}
+
 // Two independent 16-bit maxima packed in a u32 (v_pk_max_u16: one instruction).
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {

@@ -16,6 +16,9 @@ int device_cu_count();
 hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int codec,
                                    uint8_t* q, float* scale, hipStream_t st);
 
+hipError_t launch_moe_permute_colwise(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
+                                      const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups,
+                                      int codec, uint8_t* q_t, int64_t ld_q, float* scale, hipStream_t st);
 hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                    const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,
                                    int64_t ld_q, float* scale, hipStream_t st);

@@ -24,6 +24,9 @@
 //     scale (a reader sees either the tagged max or the final scale, and both
 //     give the same scale).  The cast kernel visits units in reverse order so
 //     its second read starts with the data the partial-max kernel touched last.
+// The gathered form (GATHER) reads the grouped rows through moe_route's
+// routing (row r = token row src[r] / topk, optionally times the slot's router
+// weight), so the grouped bf16 tensor is never written (row_load8).
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "tile_lds.hpp"
@@ -112,8 +115,8 @@ __device__ __forceinline__ void cw_reduce_cols(uint32_t m[4], uint32_t* red /* [
 
 // PHASE 0: partial maxima of multi-chunk groups.  PHASE 1: cast (and the whole
 // job for single-chunk and empty groups).
-template <int CODEC, bool GROUPED, int PHASE>
-__global__ __launch_bounds__(256) void colwise_kernel(const uint16_t* __restrict__ x, int64_t batch,
+template <int CODEC, bool GROUPED, int PHASE, bool GATHER>
+__global__ __launch_bounds__(256) void colwise_kernel(RowSrc xs, int64_t batch,
                                                       int rows, int cols, const int32_t* __restrict__ offs,
                                                       int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
                                                       float* __restrict__ scale, int n_strips, int units) {
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(256) void colwise_kernel(const uint16_t* __restrict
     for (int k = 0; k < 4; ++k) {
       const int r = A + 128 * i + 4 * rs + k;
       const bool ok = col_ok && r >= r_begin && r < r_end;
-      v[i][k] = ok ? *reinterpret_cast<const u32x4*>(x + (g.in_base + r) * cols + col) : u32x4{0, 0, 0, 0};
+      v[i][k] = ok ? row_load8<GATHER>(xs, g.in_base + r, cols, col) : u32x4{0, 0, 0, 0};
       m[0] = pk_absmax_bf16(m[0], v[i][k].x);
       m[1] = pk_absmax_bf16(m[1], v[i][k].y);
       m[2] = pk_absmax_bf16(m[2], v[i][k].z);
@@ -233,14 +236,15 @@ __device__ unsigned long long g_cw_part[kSlotItems][kTileCols];
 
 // Maxima of 64 columns over rows [lo, hi) of group rows in_base + r, read
 // again from global memory (the fallback of a wait that ran out).
-__device__ __forceinline__ void cw_column_max(const uint16_t* __restrict__ x, int64_t in_base, int lo, int hi,
+template <bool GATHER>
+__device__ __forceinline__ void cw_column_max(const RowSrc& xs, int64_t in_base, int lo, int hi,
                                               int cols, int c0, uint32_t* red, uint32_t* out) {
   const int t = threadIdx.x, cc = t & 7, rs = t >> 3;
   const int col = c0 + cc * 8;
   uint32_t m[4] = {0, 0, 0, 0};
   if (col < cols) {
     for (int r = lo + rs; r < hi; r += 32) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (in_base + r) * cols + col);
+      const u32x4 v = row_load8<GATHER>(xs, in_base + r, cols, col);
       m[0] = pk_absmax_bf16(m[0], v.x);
       m[1] = pk_absmax_bf16(m[1], v.y);
       m[2] = pk_absmax_bf16(m[2], v.z);
@@ -281,8 +285,8 @@ __device__ __forceinline__ bool cw_gather(const unsigned long long* __restrict__
   return k >= nch;
 }
 
-template <int CODEC, bool GROUPED, int CR>
-__global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __restrict__ x, int64_t batch,
+template <int CODEC, bool GROUPED, int CR, bool GATHER>
+__global__ __launch_bounds__(256) void colwise_single_kernel(RowSrc xs, int64_t batch,
                                                              int rows, int cols, const int32_t* __restrict__ offs,
                                                              int n_groups, uint8_t* __restrict__ q_t, int64_t ld_q,
                                                              float* __restrict__ scale, int units, uint32_t gen,
@@ -308,6 +312,30 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
   const int col = c0 + cc * 8;
   const bool col_ok = col < cols;
 
+  // Gathered rows: the chunk's token rows and weights are looked up once, with
+  // coalesced loads, into LDS (the front of the codes tile, which is written
+  // only after the column reduction's barriers), so each row's data load waits
+  // for an LDS read rather than a dependent global one.
+  int* const s_tok = reinterpret_cast<int*>(tile);
+  float* const s_w = reinterpret_cast<float*>(tile) + CR;
+  static_assert(!GATHER || 8 * CR <= kTileCols * CR, "token table fits the tile");
+  if constexpr (GATHER) {
+    for (int i = t; i < CR; i += 256) {
+      const int r = A + i;
+      int tk = -1;
+      float wv = 1.0f;
+      if (r >= r_begin && r < r_end) {
+        const int sl = xs.src[r];
+        if (sl >= 0 && (int64_t)sl < xs.slots) {
+          tk = sl / xs.topk;
+          if (xs.w != nullptr) wv = xs.w[sl];
+        }
+      }
+      s_tok[i] = tk;
+      s_w[i] = wv;
+    }
+    __syncthreads();
+  }
   u32x4 v[kIters][4];
   uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -316,7 +344,14 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
     for (int k = 0; k < 4; ++k) {
       const int r = A + 128 * i + 4 * rs + k;
       const bool ok = col_ok && r >= r_begin && r < r_end;
-      v[i][k] = ok ? *reinterpret_cast<const u32x4*>(x + (g.in_base + r) * cols + col) : u32x4{0, 0, 0, 0};
+      if constexpr (GATHER) {
+        const int tk = s_tok[128 * i + 4 * rs + k];
+        v[i][k] = ok && tk >= 0 ? *reinterpret_cast<const u32x4*>(xs.x + (int64_t)tk * cols + col)
+                                : u32x4{0, 0, 0, 0};
+        if (xs.w != nullptr) v[i][k] = bf16x8_times(v[i][k], s_w[128 * i + 4 * rs + k]);
+      } else {
+        v[i][k] = ok ? row_load8<false>(xs, g.in_base + r, cols, col) : u32x4{0, 0, 0, 0};
+      }
       m[0] = pk_absmax_bf16(m[0], v[i][k].x);
       m[1] = pk_absmax_bf16(m[1], v[i][k].y);
       m[2] = pk_absmax_bf16(m[2], v[i][k].z);
@@ -333,7 +368,7 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(const uint16_t* __r
       if (t == 0) s_ok = ok;
     }
     __syncthreads();
-    if (!s_ok) cw_column_max(x, g.in_base, g.olo, g.ohi, cols, c0, red, s_amax);
+    if (!s_ok) cw_column_max<GATHER>(xs, g.in_base, g.olo, g.ohi, cols, c0, red, s_amax);
   }
   if (t < 64) s_scale[t] = scale_from_amax(__uint_as_float(s_amax[t] << 16), CODEC);
   __syncthreads();
@@ -396,8 +431,8 @@ static int colwise_chunk_rows(int64_t rows, int64_t groups) {
   return rows <= 512 * std::max<int64_t>(groups, 1) ? 128 : kTileRows;
 }
 
-template <int CODEC, bool GROUPED>
-static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+template <int CODEC, bool GROUPED, bool GATHER = false>
+static hipError_t launch_cw(const RowSrc& xs, int64_t batch, int64_t rows, int64_t cols,
                             const int32_t* offs, int32_t n_groups, uint8_t* q_t, int64_t ld_q, float* scale,
                             hipStream_t st) {
   const int64_t n_scale = (GROUPED ? n_groups : batch) * cols;
@@ -414,8 +449,9 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
     // most chunks one group can span: a grouped group may start 15 rows past a 16-row anchor
     const int64_t nch_bound = ((GROUPED ? rows + 15 : rows) + cr - 1) / cr;
     if (!capturing && nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
-      auto k = cr == 128 ? colwise_single_kernel<CODEC, GROUPED, 128> : colwise_single_kernel<CODEC, GROUPED, kTileRows>;
-      hipLaunchKernelGGL(k, dim3((unsigned)items), dim3(256), 0, st, x, batch, (int)rows, (int)cols, offs, n_groups,
+      auto k = cr == 128 ? colwise_single_kernel<CODEC, GROUPED, 128, GATHER>
+                         : colwise_single_kernel<CODEC, GROUPED, kTileRows, GATHER>;
+      hipLaunchKernelGGL(k, dim3((unsigned)items), dim3(256), 0, st, xs, batch, (int)rows, (int)cols, offs, n_groups,
                          q_t, ld_q, scale, (int)units, next_generation(), g_poll_budget.load());
       return hipGetLastError();
     }
@@ -425,9 +461,9 @@ static hipError_t launch_cw(const uint16_t* x, int64_t batch, int64_t rows, int6
   hipLaunchKernelGGL(colwise_reset_kernel, dim3((unsigned)((n_scale + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint32_t*>(scale), n_scale);
   const dim3 grid((unsigned)(units * n_strips));
-  hipLaunchKernelGGL((colwise_kernel<CODEC, GROUPED, 0>), grid, dim3(256), 0, st, x, batch, (int)rows,
+  hipLaunchKernelGGL((colwise_kernel<CODEC, GROUPED, 0, GATHER>), grid, dim3(256), 0, st, xs, batch, (int)rows,
                      (int)cols, offs, n_groups, q_t, ld_q, scale, n_strips, (int)units);
-  hipLaunchKernelGGL((colwise_kernel<CODEC, GROUPED, 1>), grid, dim3(256), 0, st, x, batch, (int)rows,
+  hipLaunchKernelGGL((colwise_kernel<CODEC, GROUPED, 1, GATHER>), grid, dim3(256), 0, st, xs, batch, (int)rows,
                      (int)cols, offs, n_groups, q_t, ld_q, scale, n_strips, (int)units);
   return hipGetLastError();
 }
@@ -440,12 +476,22 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t row
                                    const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,
                                    int64_t ld_q, float* scale, hipStream_t st) {
   if (cols == 0) return hipSuccess;
+  const RowSrc xs{x, nullptr, nullptr, 1, 0};
   if (offs) {
-    return codec == 0 ? launch_cw<0, true>(x, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st)
-                      : launch_cw<1, true>(x, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st);
+    return codec == 0 ? launch_cw<0, true>(xs, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st)
+                      : launch_cw<1, true>(xs, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st);
   }
-  return codec == 0 ? launch_cw<0, false>(x, batch, rows, cols, nullptr, 0, q_t, ld_q, scale, st)
-                    : launch_cw<1, false>(x, batch, rows, cols, nullptr, 0, q_t, ld_q, scale, st);
+  return codec == 0 ? launch_cw<0, false>(xs, batch, rows, cols, nullptr, 0, q_t, ld_q, scale, st)
+                    : launch_cw<1, false>(xs, batch, rows, cols, nullptr, 0, q_t, ld_q, scale, st);
+}
+
+hipError_t launch_moe_permute_colwise(const uint16_t* x, int64_t tokens, int64_t cols, int topk, const int32_t* src,
+                                      const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups,
+                                      int codec, uint8_t* q_t, int64_t ld_q, float* scale, hipStream_t st) {
+  if (cols == 0) return hipSuccess;
+  const RowSrc xs{x, src, weights, topk, tokens * topk};
+  return codec == 0 ? launch_cw<0, true, true>(xs, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st)
+                    : launch_cw<1, true, true>(xs, 1, rows, cols, offs, n_groups, q_t, ld_q, scale, st);
 }
 
 }  // namespace fp8moe

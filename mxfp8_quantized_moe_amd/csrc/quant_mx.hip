@@ -396,11 +396,6 @@ struct DualSrc {
   int64_t slots;          // PROD 3: tokens * topk
 };
 
-// Eight bf16 values times w, each product one fp32 operation rounded to bf16 (nearest even).
-__device__ __forceinline__ u32x4 scale_bf16x8(const u32x4& v, float w) {
-  return u32x4{sw_pack(w * bf16_lo(v.x), w * bf16_hi(v.x)), sw_pack(w * bf16_lo(v.y), w * bf16_hi(v.y)),
-               sw_pack(w * bf16_lo(v.z), w * bf16_hi(v.z)), sw_pack(w * bf16_lo(v.w), w * bf16_hi(v.w))};
-}
 
 // The 16 columns [col, col + 16) of tensor row `row` (cols columns) as two 8-column chunks.
 template <int PROD>
@@ -422,8 +417,8 @@ __device__ __forceinline__ void dual_load(const DualSrc& sr, int64_t row, int co
     v1 = *reinterpret_cast<const u32x4*>(p + 8);
     if (sr.gw != nullptr) {
       const float wj = sr.gw[sl];
-      v0 = scale_bf16x8(v0, wj);
-      v1 = scale_bf16x8(v1, wj);
+      v0 = bf16x8_times(v0, wj);
+      v1 = bf16x8_times(v1, wj);
     }
   } else if constexpr (PROD == 1) {
     const uint16_t* g = sr.h1 + row * sr.ld_h1 + col;

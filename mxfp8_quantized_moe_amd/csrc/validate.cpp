@@ -59,6 +59,22 @@ int check_quantize_colwise(const void* x, int64_t batch, int64_t rows, int64_t c
   return FP8MOE_OK;
 }
 
+int check_moe_permute_colwise(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                              const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups, int codec,
+                              const void* q_t, int64_t ld_q, const void* scale) {
+  if (tokens < 0 || cols < 0 || topk < 1 || rows < 0 || cols > kI32Max) return FP8MOE_ERR_SHAPE;
+  const int64_t S = mul(tokens, topk), nx = mul(tokens, cols);
+  if (S < 0 || S > kI32Max || nx < 0) return FP8MOE_ERR_SHAPE;
+  if (offs == nullptr) return FP8MOE_ERR_NULL;   // the grouped layout of moe_route
+  // the gathered [rows][cols] tensor: q_t stands in for its pointer and alignment
+  const int st = check_quantize_colwise(rows && cols ? q_t : nullptr, 1, rows, cols, offs, n_groups, codec, q_t,
+                                        ld_q, scale);
+  if (st) return st;
+  if (!need(x, nx) || !need(src, rows)) return FP8MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(src, 4) || !aligned(weights, 4)) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
+}
+
 int64_t mx_k4_bytes(int64_t rows, int64_t nb) { return mul(mul(rows, (nb + 3) / 4), 4); }
 
 int check_quantize_mx(const void* x, int64_t batch, int64_t rows, int64_t cols, int axis, const int32_t* offs,

@@ -17,6 +17,9 @@ int check_moe_permute_mx_dual(const void* x, int64_t tokens, int64_t cols, int32
                               const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups, int rule,
                               int scale_layout, const void* xg, const void* q, const void* sc, const void* q_t,
                               const void* sc_t, int64_t rows_pad, const int32_t* offs_pad_out);
+int check_moe_permute_colwise(const void* x, int64_t tokens, int64_t cols, int32_t topk, const int32_t* src,
+                              const float* weights, int64_t rows, const int32_t* offs, int32_t n_groups, int codec,
+                              const void* q_t, int64_t ld_q, const void* scale);
 int check_quantize_mx_dual(const void* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* offs,
                            int32_t n_groups, int rule, int scale_layout, const void* q, const void* sc,
                            const void* q_t, const void* sc_t, int64_t rows_pad, const int32_t* offs_pad_out);

@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
     for s in range(1, 9):
         assert lib.fp8moe_status_string(s) not in (b"ok", b"unknown status")
     assert lib.fp8moe_status_string(99) == b"unknown status"
-    assert lib.fp8moe_version() == 107
+    assert lib.fp8moe_version() == 108
 
 
 def test_rows_bound(lib):
@@ -331,6 +331,29 @@ def test_moe_permute_mx_dual_rejections(lib):
     assert call(ok, 2, 48) == L.ERR_ALIGN                 # cols % 32
     for i, bad in ((0, MIS), (11, MIS), (12, MIS), (4, P + 2), (5, P + 2)):
         assert call(ok, i, bad) == L.ERR_ALIGN, i
+
+
+def test_moe_permute_colwise_rejections(lib):
+    f = lib.moe_permute_quantize_colwise
+    # (x, tokens, cols, topk, src, weights, rows, offs, n_groups, codec, q_t, ld_q, scale, stream)
+    ok = [P, 32, 64, 2, P, None, 64, P, 4, 0, P, 64, P, None]
+    def call(i=None, v=None):
+        a = list(ok)
+        if i is not None:
+            a[i] = v
+        return f(*a)
+    assert call(9, 7) == L.ERR_ENUM                       # codec
+    assert call(3, 0) == L.ERR_SHAPE                      # topk
+    assert call(1, -1) == L.ERR_SHAPE                     # tokens
+    assert call(1, 1 << 31) == L.ERR_SHAPE                # tokens * topk past int32
+    assert call(11, 48) == L.ERR_SHAPE                    # ld_q < rows
+    assert call(7, None) == L.ERR_NULL                    # offs: the grouped layout is required
+    for i in (0, 4, 10, 12):                              # x, src, codes, scales
+        assert call(i, None) == L.ERR_NULL, i
+    assert call(2, 60) == L.ERR_ALIGN                     # cols % 8
+    assert call(11, 72) == L.ERR_ALIGN                    # ld_q % 16
+    for i, bad in ((0, MIS), (10, MIS), (4, P + 2), (5, P + 2)):
+        assert call(i, bad) == L.ERR_ALIGN, i
 
 
 def test_swiglu_mx_dual_rejections(lib):

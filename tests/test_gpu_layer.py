@@ -55,8 +55,9 @@ LAUNCHES = {
 LAUNCHES[4] = LAUNCHES[3]
 LAYER = {
     3: ["route", "permute+q X", "q_row W1", "gemm fwd W1", "swiglu+q", "q_row W2", "gemm fwd W2", "combine",
-        "combine bwd+q", "q_col W2", "gemm dgrad W2", "q_col dYg", "q_col A2", "gemm wgrad W2", "swiglu bwd+q",
-        "q_col W1", "gemm dgrad W1", "q_col dH1", "q_col Xg", "gemm wgrad W1", "combine dX"],
+        "combine bwd+q", "q_col W2", "gemm dgrad W2", "q_col dYg (gathered)", "q_col A2", "gemm wgrad W2",
+        "swiglu bwd+q", "q_col W1", "gemm dgrad W1", "q_col dH1", "q_col Xg (gathered)", "gemm wgrad W1",
+        "combine dX"],
     5: ["route", "permute+mx Xg (both forms)", "mx W1 (both forms)", "gemm fwd W1", "swiglu+mx A2 (both forms)",
         "mx W2 (both forms)", "gemm fwd W2", "combine", "combine bwd (dw)", "permute+mx dYg (both forms)",
         "gemm dgrad W2",
@@ -172,6 +173,22 @@ def check_q_col_grouped(sp, hst, phase):
     assert_f32_bits_equal(s[:, cols], np.concatenate([b for _, b in res], axis=1), "scales")
 
 
+def _gathered(sp, hst):
+    """The grouped rows a gathered launch forms from token rows: the oracle's gather, or with router
+    weights the routed-row gradients of its combine backward, on the step's own routing."""
+    x, rsrc, dest, k = hst[sp["x"]], _src(hst, sp["rsrc"]), _src(hst, sp["dest"]), sp["topk"]
+    T, C = x.shape
+    if sp["w"] is None:
+        return o_route.permute(x, rsrc, k)
+    return o_route.combine_backward(x, np.zeros((rsrc.size, C), np.uint16), rsrc, dest, hst[sp["w"]], T, k)[0]
+
+
+def check_permute_q_col(sp, hst, phase):
+    """The gather fused with the grouped colwise quantizer, checked as check_q_col_grouped checks a tensor
+    in memory."""
+    check_q_col_grouped(dict(src=_gathered(sp, hst), offs=sp["offs"], q=sp["q"], s=sp["s"]), hst, phase)
+
+
 def check_q_col_batched(sp, hst, phase):
     B, R, C = sp["shape"]
     x = _src(hst, sp["src"]).reshape(B, R, C)
@@ -242,12 +259,7 @@ def check_permute_mx_dual(sp, hst, phase):
     """The gather into the grouped layout fused with both MX forms: the gathered rows (times the router
     weights for the routed-row gradients) are formed here by the oracle's permute (or combine backward)
     from the step's own routing, then checked as check_mx_dual checks a tensor in memory."""
-    x, rsrc, dest, k = hst[sp["x"]], _src(hst, sp["rsrc"]), _src(hst, sp["dest"]), sp["topk"]
-    T, C = x.shape
-    if sp["w"] is None:
-        g = o_route.permute(x, rsrc, k)
-    else:
-        g, _ = o_route.combine_backward(x, np.zeros((rsrc.size, C), np.uint16), rsrc, dest, hst[sp["w"]], T, k)
+    g = _gathered(sp, hst)
     check_mx_dual(dict(src=g, shape=sp["shape"], offs=sp["offs"], rows_pad=sp["rows_pad"], rule=sp["rule"],
                        q=sp["q"], s=sp["s"], qt=sp["qt"], st=sp["st"], offs_pad=sp["offs_pad"]), hst, phase)
 
@@ -381,7 +393,8 @@ def check_permute_rowwise(sp, hst, phase):
     x, rsrc = _src(hst, sp["src"]), _src(hst, sp["rsrc"])
     rows = _rows_sample(rsrc.size, phase)
     xg = o_route.permute(x, rsrc[rows], sp["topk"])
-    assert_bytes_equal(_src(hst, sp["xg"])[rows], xg, "gathered rows")
+    if sp["xg"] is not None:                            # the bf16 copy is optional
+        assert_bytes_equal(_src(hst, sp["xg"])[rows], xg, "gathered rows")
     q, s = oracle.quantize_rowwise(xg, 0)
     assert_bytes_equal(_src(hst, sp["q"])[rows], q, "codes")
     assert_f32_bits_equal(_src(hst, sp["s"])[rows], s, "scales")
@@ -456,7 +469,7 @@ def check_combine_bwd(sp, hst, phase):
 CHECKS = {"q_row": check_q_row, "q_col_grouped": check_q_col_grouped, "q_col_batched": check_q_col_batched,
           "mx_last": check_mx_last, "mx_rows_b": check_mx_rows_b, "mx_rows_g": check_mx_rows_g,
           "g_m": check_g_m, "g_k": check_g_k, "g_k_bf16": check_g_k_bf16,
-          "mx_dual": check_mx_dual, "permute_mx_dual": check_permute_mx_dual, "swiglu_mx": check_swiglu_mx, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
+          "mx_dual": check_mx_dual, "permute_mx_dual": check_permute_mx_dual, "permute_q_col": check_permute_q_col, "swiglu_mx": check_swiglu_mx, "route": check_route, "permute": check_permute, "permute_rowwise": check_permute_rowwise,
           "swiglu": check_swiglu, "swiglu_bwd": check_swiglu_bwd, "combine": check_combine,
           "combine_bwd": check_combine_bwd}
 

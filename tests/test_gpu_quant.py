@@ -583,6 +583,78 @@ def test_colwise_wait_fallback_bit_exact(codec, chunk_rows):
     assert_f32_bits_equal(host(sb), sbr, "batched scales")
 
 
+def _routed(T, k, E, C, seed, drop=0.03, one_expert=False):
+    """Token rows, their routing (GPU moe_route, pad 1) and router weights for the gathered quantizers."""
+    rng = np.random.default_rng(seed)
+    ids = (np.zeros((T, k)) if one_expert else rng.integers(0, E, size=(T, k))).astype(np.int32)
+    if T > 10 and drop:
+        ids[rng.random((T, k)) < drop] = -1
+    x = synth.normal_bf16(seed + 1, (T, C), 1.0, 0.01, 30.0)
+    w = (rng.random((T, k)) + 0.05).astype(np.float32)
+    return x, w, fm.moe_route(i32_dev(ids), E, 1)
+
+
+def _gathered_ref(x, w, src, dest, k):
+    from oracle import route as rt
+    T, C = x.shape
+    if w is None:
+        return rt.permute(x, src, k)
+    return rt.combine_backward(x, np.zeros((src.size, C), np.uint16), src, dest, w, T, k)[0]
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("shape", [(700, 2, 5, 136), (3000, 1, 4, 64), (96, 6, 8, 200)])
+def test_moe_permute_colwise(weighted, codec, shape, chunk_rows):
+    """The gather into moe_route's grouped layout fused with the colwise quantizer: the same bytes as the
+    oracle's gather (with router weights: the routed-row gradients of its combine backward) followed by
+    its grouped colwise quantizer, on every single-pass chunk height."""
+    T, k, E, C = shape
+    x, w, (counts, offs, dest, src) = _routed(T, k, E, C, 9300 + T + C + codec)
+    R = src.numel()
+    ld_q = (R + 15) // 16 * 16 + 16
+    note(f"moe_permute_quantize_colwise T={T} k={k} E={E} C={C} weighted={weighted} codec={codec} "
+         f"chunk rows={chunk_rows}")
+    q_t, sc = filled_u8((C, ld_q)), filled_f32((E, C))
+    fm.moe_permute_quantize_colwise(bf16_dev(x), src, k, offs, weights=torch.from_numpy(w).to(DEV) if weighted
+                                    else None, codec=codec, q_t=q_t, scale=sc, ld_q=ld_q)
+    g = _gathered_ref(x, w if weighted else None, host(src), host(dest), k)
+    qr, sr = oracle.quantize_colwise_grouped(g, host(offs), codec, q_init=np.full((C, ld_q), 0xA5, np.uint8),
+                                             ld_q=ld_q)
+    assert_bytes_equal(host(q_t), qr, "codes")
+    assert_f32_bits_equal(host(sc), sr, "scales")
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_moe_permute_colwise_other_paths(weighted):
+    """The gathered colwise quantizer on its other paths, bit for bit: the fallback a chunk takes when its
+    peers do not publish in time (poll budget 0, so every multi-chunk group re-reads its rows through the
+    gather) and the two-pass kernels (one group of 70000 rows, more than 128 chunks)."""
+    lib = fm._lib.lib()
+    x, w, (counts, offs, dest, src) = _routed(3000, 2, 3, 72, 9400)
+    ref = oracle.quantize_colwise_grouped(_gathered_ref(x, w if weighted else None, host(src), host(dest), 2),
+                                          host(offs), 0)
+    wd = torch.from_numpy(w).to(DEV) if weighted else None
+    prev = lib.fp8moe_set_colwise_poll_budget(0)
+    try:
+        note(f"moe_permute_quantize_colwise with no polls weighted={weighted}")
+        q, s = fm.moe_permute_quantize_colwise(bf16_dev(x), src, 2, offs, weights=wd)
+        qh, sh = host(q), host(s)
+    finally:
+        lib.fp8moe_set_colwise_poll_budget(prev)
+    used = int(host(offs)[-1])
+    assert_bytes_equal(qh[:, :used], ref[0][:, :used], "codes (fallback)")
+    assert_f32_bits_equal(sh, ref[1], "scales (fallback)")
+    xt, wt, (ct, ot, dt, st_) = _routed(70000, 1, 1, 64, 9500, drop=0.0, one_expert=True)
+    note(f"moe_permute_quantize_colwise two-pass weighted={weighted}")
+    q, s = fm.moe_permute_quantize_colwise(bf16_dev(xt), st_, 1, ot, weights=torch.from_numpy(wt).to(DEV)
+                                           if weighted else None)
+    qr, sr = oracle.quantize_colwise_grouped(_gathered_ref(xt, wt if weighted else None, host(st_), host(dt), 1),
+                                             host(ot), 0)
+    assert_bytes_equal(host(q)[:, :70000], qr[:, :70000], "codes (two-pass)")
+    assert_f32_bits_equal(host(s), sr, "scales (two-pass)")
+
+
 def test_colwise_graph_replays():
     """A call captured into a HIP graph and replayed with new inputs (eager calls in between, which
     advance the single-pass kernel's tag) gives the oracle's result on every replay."""
