@@ -942,6 +942,13 @@ void gemm_fp8_pipe(KParams p) {
   }
 
   for (int it = 0;; ++it) {
+  // A GROUPED_M tile with at most BM / 2 valid rows (a group's last, short
+  // tile) runs HALF: the four waves share its first BM / 2 rows and each takes
+  // a quarter of the columns, so no MFMA is spent on its padding rows.
+  auto tile_body = [&](auto half_tag) -> bool {
+  constexpr bool HALF = decltype(half_tag)::value;
+  constexpr int TNE = HALF ? TN / 2 : TN, WNE = HALF ? WN / 2 : WN;   // column blocks and columns per wave
+  constexpr int NME = TM * TNE, NDE = 2 * (TM + TNE), ND0E = NDE + (E8 ? TM + TNE : 0);
   // Thread indices pass through an opaque copy each tile, so the compiler
   // derives per-lane addresses inside the tile instead of hoisting (and
   // spilling) all of them across the tile loop.
@@ -949,7 +956,7 @@ void gemm_fp8_pipe(KParams p) {
   asm volatile("" : "+v"(t_opq));
   const int t = t_opq, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: scalar registers
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = HALF ? 0 : wave >> 1, wn = HALF ? wave : wave & 1;
   const int c_lo = cur.c_lo, c_hi = cur.c_hi, c_start = cur.c_start, nk = cur.nk;
   const float* const sinv = s_inv[it & 1];
   uint32_t soff[E8 ? SC_DMA : 1];
@@ -968,17 +975,17 @@ void gemm_fp8_pipe(KParams p) {
     raw_barrier();
   };
 
-  v16f acc[TM][TN];
+  v16f acc[TM][TNE];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TNE; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int g = lane >> 5, lrow = lane & 31;
   // Two register sets of MFMA fragments (one 64-byte k step each).
-  v8i fa[2][TM], fb[2][TN];
+  v8i fa[2][TM], fb[2][TNE];
   // e8m0 scale operands: byte i of ea[set] is fragment i's scale (the MFMA
   // picks it with op_sel), likewise eb.  In LDS a tile row's four scale bytes
   // of a stage are one word, byte 2 h + b for 32-block b of k step h, and the
@@ -986,7 +993,7 @@ void gemm_fp8_pipe(KParams p) {
   // word of each fragment row once (ahead of that step's fragment reads) and
   // packs the bytes of both k steps with byte permutes; the second k step's
   // operands wait in ea_n / eb_n.
-  static_assert(TM <= 4 && TN <= 4 && (TM == 4 || TM == 2) && TN == 4, "four scale bytes per register");
+  static_assert((TM == 4 || TM == 2) && (TNE == 4 || TNE == 2), "at most four scale bytes per register");
   int ea[2], eb[2], ea_n = 0, eb_n = 0;
   // byte selectors: t = [w0.b(g), w1.b(g), w0.b(2+g), w1.b(2+g)] from words w0 (low), w1
   const uint32_t sel_pair = 0x06020400u + 0x01010101u * (uint32_t)g;
@@ -1012,8 +1019,8 @@ void gemm_fp8_pipe(KParams p) {
         for (int i = 0; i < TM; ++i)
           wa[i] = *reinterpret_cast<const uint32_t*>(sc + 4 * (wm * WM + 32 * i + lrow));
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          wb[j] = *reinterpret_cast<const uint32_t*>(sc + 4 * (BM + wn * WN + 32 * j + lrow));
+        for (int j = 0; j < TNE; ++j)
+          wb[j] = *reinterpret_cast<const uint32_t*>(sc + 4 * (BM + wn * WNE + 32 * j + lrow));
       }
     }
 #pragma unroll
@@ -1024,8 +1031,8 @@ void gemm_fp8_pipe(KParams p) {
       fa[SET][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wn * WN + 32 * j + lrow;
+    for (int j = 0; j < TNE; ++j) {
+      const int r = wn * WNE + 32 * j + lrow;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + g));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(st + A_BYTES + R::off(r, 4 * h + 2 + g));
       fb[SET][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -1034,7 +1041,8 @@ void gemm_fp8_pipe(KParams p) {
       if (h == 0) {
         if constexpr (TM == 4) pack4(wa, ea[SET], ea_n);
         else pack2(wa, ea[SET], ea_n);
-        pack4(wb, eb[SET], eb_n);
+        if constexpr (TNE == 4) pack4(wb, eb[SET], eb_n);
+        else pack2(wb, eb[SET], eb_n);
       } else {
         ea[SET] = ea_n;
         eb[SET] = eb_n;
@@ -1045,7 +1053,7 @@ void gemm_fp8_pipe(KParams p) {
     constexpr int SET = decltype(set_tag)::value;
     static_for<TM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      static_for<TN>([&](auto jc) {
+      static_for<TNE>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         // B fragment first: the 32x32 result then holds output row (lane & 31)
         // and output columns 8 (v / 4) + 4 (lane >> 5) + v % 4 in register v,
@@ -1068,7 +1076,7 @@ void gemm_fp8_pipe(KParams p) {
       constexpr int CUR = (S * KS) & 1;
       rd(std::integral_constant<int, 1 - CUR>{}, slot_data[S], slot_scale[S], 1);
       mma(std::integral_constant<int, CUR>{});
-      interleave<NM, ND, 0>();
+      interleave<NME, NDE, 0>();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1102,7 +1110,7 @@ void gemm_fp8_pipe(KParams p) {
     issue_stage(cur, slot_tag, stage_of(min(kt + SLOTS, nk - 1)), Checked{}, soff);
     rd(std::integral_constant<int, 1 - CUR>{}, slot_data[NS], slot_scale[NS], 0);
     mma(std::integral_constant<int, CUR>{});
-    interleave<NM, ND0, LPS>();
+    interleave<NME, ND0E, LPS>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -1195,7 +1203,7 @@ void gemm_fp8_pipe(KParams p) {
     const uint32_t stg_l = lds_off(stg), sinv_l = lds_off(sinv);
     const bool full = p_valid == BM && q_valid == BN;
     const int rr = lane >> 3, k = lane & 7;     // read-back: staged row 8 itr + rr, chunk k
-    constexpr int NP = TM * (TN / JPP);         // passes
+    constexpr int NP = TM * (TNE / JPP);         // passes
     // GROUPED_M with bf16 output: the read-back pieces of every pass are held
     // (128 registers, where the dead MFMA fragments were) and stored together
     // once the next tile's stages have landed.  Otherwise (measured slower for
@@ -1215,7 +1223,7 @@ void gemm_fp8_pipe(KParams p) {
 #pragma unroll
       for (int itr = 0; itr < 4; ++itr) lds_ready(dv[d][itr]);
       if constexpr (!HOLD && n == 0) wait_vmcnt<0>();
-      const int c = wn * WN + PC * jp + VEC * k;
+      const int c = wn * WNE + PC * jp + VEC * k;
       uint8_t* const row0 = static_cast<uint8_t*>(p.out) +
                             (out_base + (int64_t)(wm * WM + 32 * i + rr) * out_ld + c) * ELEM;
       if (full) {
@@ -1245,7 +1253,7 @@ void gemm_fp8_pipe(KParams p) {
         }
       }
     };
-    static_for<TN / JPP>([&](auto jpc) {
+    static_for<TNE / JPP>([&](auto jpc) {
       constexpr int jp = decltype(jpc)::value;
       // reciprocals of the lane's columns in this pass (register quad q of
       // block jj: columns 32 jj + 8 q + 4 g + e of the pass) and of its rows
@@ -1258,7 +1266,7 @@ void gemm_fp8_pipe(KParams p) {
         for (int jj = 0; jj < JPP; ++jj)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            rq[jj][q] = lds_read16(sinv_l + 4 * (BM + wn * WN + 32 * (JPP * jp + jj) + 8 * q + 4 * g));
+            rq[jj][q] = lds_read16(sinv_l + 4 * (BM + wn * WNE + 32 * (JPP * jp + jj) + 8 * q + 4 * g));
 #pragma unroll
         for (int i = 0; i < TM; ++i) rp[i] = lds_read4(sinv_l + 4 * (wm * WM + 32 * i + lrow));
         lds_wait();
@@ -1345,13 +1353,13 @@ void gemm_fp8_pipe(KParams p) {
       return v;
     };
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TNE; ++j) {
       float inv_q[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int cc = min(wn * WN + 32 * j + 8 * q + 4 * g + e, BN - 1);
+          const int cc = min(wn * WNE + 32 * j + 8 * q + 4 * g + e, BN - 1);
           inv_q[4 * q + e] = (SK == 0 ? sinv[BM + cc] : 1.0f) * keep;
         }
 #pragma unroll
@@ -1363,7 +1371,7 @@ void gemm_fp8_pipe(KParams p) {
           const f32x4 v = quad(i, j, q, inv_p, inv_q);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int c = wn * WN + 32 * j + 8 * q + 4 * g + e;
+            const int c = wn * WNE + 32 * j + 8 * q + 4 * g + e;
             if (r >= p_valid || c >= q_valid) continue;
             const int64_t o = out_base + (int64_t)r * out_ld + c;
             if constexpr (OUT == 0)
@@ -1374,6 +1382,15 @@ void gemm_fp8_pipe(KParams p) {
         }
       }
     }
+  }
+  return has_next;
+  };
+  bool has_next;
+  if constexpr (MODE == 0 && BM == 256) {
+    if (cur.pv <= BM / 2) has_next = tile_body(std::true_type{});
+    else has_next = tile_body(std::false_type{});
+  } else {
+    has_next = tile_body(std::false_type{});
   }
   if (!has_next) break;
   cur = nxt;
