@@ -298,7 +298,22 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(RowSrc xs, int64_t 
   __shared__ int s_ok;
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileCols * CR];
   const int t = threadIdx.x, cc = t & 7, rs = t >> 3;
-  const int strip = blockIdx.x / units, u = blockIdx.x % units;
+  // The chunks of one (group or batch item, strip) job are consecutive
+  // workgroups (the exchange relies on it).  Batched tensors (weights) run
+  // their jobs in bands of 8 strips per batch item, so the workgroups running
+  // together read 1 KiB of each row instead of 128 bytes.
+  int strip, u;
+  if constexpr (GROUPED) {
+    strip = blockIdx.x / units;
+    u = blockIdx.x % units;
+  } else {
+    const int n_strips = (int)(gridDim.x / units), upb = (int)(units / batch);
+    const int per_b = n_strips * upb;
+    const int b = (int)blockIdx.x / per_b, r = (int)blockIdx.x % per_b;
+    const int band = r / (8 * upb), r2 = r % (8 * upb);
+    strip = 8 * band + r2 / upb;
+    u = b * upb + r2 % upb;
+  }
   const CwGeom g = cw_geom<GROUPED, CR>(u, batch, rows, cols, offs, n_groups, q_t, ld_q, scale);
   if (!g.ok) return;
   const int c0 = strip * kTileCols;
