@@ -1386,7 +1386,7 @@ void gemm_fp8_pipe(KParams p) {
   return has_next;
   };
   bool has_next;
-  if constexpr (MODE == 0 && BM == 256) {
+  if constexpr (MODE == 0) {
     if (cur.pv <= BM / 2) has_next = tile_body(std::true_type{});
     else has_next = tile_body(std::false_type{});
   } else {
