@@ -12,11 +12,12 @@ namespace fp8moe {
 typedef float sw_f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 sw_bf16x2 __attribute__((ext_vector_type(2)));
 
-// sigmoid(g) in fp32, in the form whose exponential never overflows.
+// sigmoid(g) in fp32, in the form whose exponential never overflows:
+// 1 / (1 + e^-g) for g >= 0 and e^g / (1 + e^g) below, both from the one
+// exponential e^-|g| (a wave whose lanes take both signs evaluates it once).
 __device__ __forceinline__ float sw_sigmoid(float g) {
-  if (g >= 0.0f) return 1.0f / (1.0f + expf(-g));
-  const float e = expf(g);
-  return e / (1.0f + e);
+  const float e = expf(-fabsf(g));
+  return (g >= 0.0f ? 1.0f : e) / (1.0f + e);
 }
 
 // Two fp32 values -> one word of two bf16 (round to nearest even).
