@@ -15,9 +15,13 @@ typedef __bf16 sw_bf16x2 __attribute__((ext_vector_type(2)));
 // sigmoid(g) in fp32, in the form whose exponential never overflows:
 // 1 / (1 + e^-g) for g >= 0 and e^g / (1 + e^g) below, both from the one
 // exponential e^-|g| (a wave whose lanes take both signs evaluates it once).
+// The denominator lies in [1, 2], so the hardware reciprocal (1 ulp) times the
+// numerator stands in for the division (within 2 ulp; the kernels that use it
+// are bound by their arithmetic, and the division's exact-rounding sequence
+// was a fifth of it).
 __device__ __forceinline__ float sw_sigmoid(float g) {
   const float e = expf(-fabsf(g));
-  return (g >= 0.0f ? 1.0f : e) / (1.0f + e);
+  return (g >= 0.0f ? 1.0f : e) * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Two fp32 values -> one word of two bf16 (round to nearest even).
