@@ -1078,10 +1078,16 @@ def main():
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
-        for _ in range(3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        for i in range(3):
             dst.copy_(src)
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(1, 3)]   # the first launch warms up
+        gbs = 2 * n / (sum(us) / len(us) * 1e-6) / 1e9                    # n bytes read + n written
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3, "us_per_copy": round(sum(us) / len(us), 1),
+                          "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / 8000.0, 3)}), flush=True)
         return
     import mxfp8_quantized_moe_amd  # noqa: F401  (fails loudly if the HIP library is missing)
     from mxfp8_quantized_moe_amd import synth
