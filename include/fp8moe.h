@@ -698,9 +698,10 @@ int fp8moe_set_colwise_poll_budget(int polls);
 
 /*
  * fp8moe_set_colwise_chunk_rows -- test and tuning hook: the chunk height of
- * the single-pass colwise quantizer (128 or 512 rows: forced; any other value:
- * chosen per call, 128 rows when the groups or batch items average at most 512
- * rows, else 512).  A forced height that a call cannot use (too many chunks)
+ * the single-pass colwise quantizer (128, 256 or 512 rows: forced; any other
+ * value: chosen per call from the average rows per group or batch item, 128
+ * rows up to 128, 256 rows up to 512, else 512).  A forced height that a call
+ * cannot use (too many chunks)
  * falls back to 512 rows, then to the two-pass path.  Results do not depend on
  * it.  Process-wide; returns the previous setting (0 for per-call choice).
  */

@@ -7,7 +7,8 @@
 // оптимизации Triton-ядер" (removal of the .t().contiguous().t() copy; fused
 // scale-and-cast; relaxed atomic ordering for commutative reductions).]
 //
-// Work units: a 64-column strip x a chunk of up to 512 rows of one group.
+// Work units: a 64-column strip x a chunk of up to 512 rows of one group (256
+// or 128 rows when the groups are short on average).
 // Chunks of group e are anchored at floor16(lo(e)) so every 16-row output
 // segment is 16-byte aligned; the (rare) segments shared with a neighbouring
 // group are stored byte by byte.
@@ -39,7 +40,7 @@ constexpr int kCwThreads = 256;
 constexpr int kCwIters = kTileRows / 128;   // 4 iterations of 128 rows
 constexpr uint32_t kTag = 0x80000000u;      // marks a merged |x| max (not yet a scale)
 
-// Chunks of CR rows (512, or 128 for calls whose groups are short on average).
+// Chunks of CR rows (512, or 256 or 128 for calls whose groups are short on average).
 template <int CR = kTileRows>
 __device__ __forceinline__ int cw_chunks(int lo, int hi) {
   if (hi <= lo) return 1;                    // an empty group still owns one unit: its scale
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(256) void colwise_single_kernel(RowSrc xs, int64_t 
 // reset is an ordinary kernel and which keeps no state between launches.
 static std::atomic<uint32_t> g_generation{0};
 static std::atomic<int> g_poll_budget{kPolls};
-static std::atomic<int> g_chunk_rows{0};   // 0: chosen per call; 128 or 512: forced (a test hook)
+static std::atomic<int> g_chunk_rows{0};   // 0: chosen per call; 128, 256 or 512: forced (a test hook)
 static uint32_t next_generation() {
   uint32_t g = g_generation.fetch_add(1) + 1;
   if (g == 0) g = g_generation.fetch_add(1) + 1;
@@ -437,13 +438,16 @@ int64_t colwise_units_bound(int64_t batch, int64_t rows, const int32_t* offs, in
   return batch * upb;
 }
 
-// Chunk height of a single-pass call: 128 rows when its groups (or batch items)
-// average at most 512 rows (a 512-row chunk of a short group is mostly
-// padding), else 512; a forced height from the test hook wins.
+// Chunk height of a single-pass call from the average rows per group (or batch
+// item): at most 128 -> 128-row chunks, at most 512 -> 256, else 512.  A
+// 512-row chunk of a short group is mostly padding; for groups of a few hundred
+// rows 256-row chunks beat 128 (half as many chunks exchange maxima, with the
+// same eight workgroups per CU).  A forced height from the test hook wins.
 static int colwise_chunk_rows(int64_t rows, int64_t groups) {
   const int forced = g_chunk_rows.load();
-  if (forced == 128 || forced == kTileRows) return forced;
-  return rows <= 512 * std::max<int64_t>(groups, 1) ? 128 : kTileRows;
+  if (forced == 128 || forced == 256 || forced == kTileRows) return forced;
+  const int64_t g = std::max<int64_t>(groups, 1);
+  return rows <= 128 * g ? 128 : rows <= 512 * g ? 256 : kTileRows;
 }
 
 template <int CODEC, bool GROUPED, bool GATHER = false>
@@ -464,8 +468,9 @@ static hipError_t launch_cw(const RowSrc& xs, int64_t batch, int64_t rows, int64
     // most chunks one group can span: a grouped group may start 15 rows past a 16-row anchor
     const int64_t nch_bound = ((GROUPED ? rows + 15 : rows) + cr - 1) / cr;
     if (!capturing && nch_bound <= kMaxChunks && (nch_bound <= 1 || items <= kSlotItems) && items < (1LL << 31)) {
-      auto k = cr == 128 ? colwise_single_kernel<CODEC, GROUPED, 128, GATHER>
-                         : colwise_single_kernel<CODEC, GROUPED, kTileRows, GATHER>;
+      auto k = cr == 128   ? colwise_single_kernel<CODEC, GROUPED, 128, GATHER>
+               : cr == 256 ? colwise_single_kernel<CODEC, GROUPED, 256, GATHER>
+                           : colwise_single_kernel<CODEC, GROUPED, kTileRows, GATHER>;
       hipLaunchKernelGGL(k, dim3((unsigned)items), dim3(256), 0, st, xs, batch, (int)rows, (int)cols, offs, n_groups,
                          q_t, ld_q, scale, (int)units, next_generation(), g_poll_budget.load());
       return hipGetLastError();
@@ -485,7 +490,9 @@ static hipError_t launch_cw(const RowSrc& xs, int64_t batch, int64_t rows, int64
 
 int set_colwise_poll_budget(int polls) { return g_poll_budget.exchange(polls < 0 ? kPolls : polls); }
 
-int set_colwise_chunk_rows(int rows) { return g_chunk_rows.exchange(rows == 128 || rows == kTileRows ? rows : 0); }
+int set_colwise_chunk_rows(int rows) {
+  return g_chunk_rows.exchange(rows == 128 || rows == 256 || rows == kTileRows ? rows : 0);
+}
 
 hipError_t launch_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                    const int32_t* offs, int32_t n_groups, int codec, uint8_t* q_t,

@@ -33,13 +33,15 @@ __device__ __forceinline__ int tile_off(int c, int r) {
 // TR = 128 the segment is XOR-ed with the 8-column slice index (8 values over
 // 8 segments), which keeps a wave's 4-row writes of one slice column on 32
 // distinct banks and a quarter-wave's 16-byte reads (two columns) on all 64.
+// TR = 256 takes the same XOR within its 16 segments: the writes again reach
+// 32 banks, and a quarter-wave's reads (16 segments of one column) all 64.
 template <int TR>
 __device__ __forceinline__ int tile_off_r(int c, int r) {
   if constexpr (TR == kTileRows) {
     return tile_off(c, r);
   } else {
-    static_assert(TR == 128, "tile heights: 512 or 128 rows");
-    return c * TR + ((((r >> 4) ^ (c >> 3)) & 7) << 4) + (r & 15);
+    static_assert(TR == 128 || TR == 256, "tile heights: 512, 256 or 128 rows");
+    return c * TR + ((((r >> 4) ^ (c >> 3)) & (TR / 16 - 1)) << 4) + (r & 15);
   }
 }
 

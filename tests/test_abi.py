@@ -452,12 +452,14 @@ def test_colwise_poll_budget_hook(lib):
 
 
 def test_colwise_chunk_rows_hook(lib):
-    """Host-only tuning hook: 128 or 512 force a chunk height, anything else selects per call (0)."""
+    """Host-only tuning hook: 128, 256 or 512 force a chunk height, anything else selects per call (0)."""
     f = lib.fp8moe_set_colwise_chunk_rows
     first = f(128)
     try:
-        assert f(512) == 128
+        assert f(256) == 128
+        assert f(512) == 256
         assert f(300) == 512
+        assert f(1024) == 0
         assert f(0) == 0
     finally:
         f(first)

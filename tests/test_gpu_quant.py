@@ -96,9 +96,9 @@ GROUP_CASES = {
 }
 
 
-@pytest.fixture(params=[0, 128, 512], ids=["chunks_auto", "chunks128", "chunks512"])
+@pytest.fixture(params=[0, 128, 256, 512], ids=["chunks_auto", "chunks128", "chunks256", "chunks512"])
 def chunk_rows(request):
-    """The single-pass colwise chunk height: chosen per call, or forced to 128 or 512 rows."""
+    """The single-pass colwise chunk height: chosen per call, or forced to 128, 256 or 512 rows."""
     f = fm._lib.lib().fp8moe_set_colwise_chunk_rows
     prev = f(request.param)
     yield request.param
