@@ -367,4 +367,52 @@ __device__ __forceinline__ Unit find_unit(const int32_t* __restrict__ offs, int 
   return r;
 }
 
+// find_unit for at most 64 groups, by one wave with no shared memory and no
+// barrier: lane e holds group e, running maximum and sums by lane shuffles, the
+// owning lane found by a ballot.  Every wave of a workgroup computes the same
+// result on its own.  The same unit as find_unit (whose scans take about ten
+// workgroup barriers before a quantizer workgroup can issue its first load).
+template <typename ChunkFn, typename PadFn>
+__device__ __forceinline__ Unit find_unit_wave(const int32_t* __restrict__ offs, int n_groups, int rows, int u,
+                                               ChunkFn chunks, PadFn pad) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < n_groups;
+  int hi = in ? clamp_off(offs[lane], rows) : 0;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(hi, d, 64);
+    if (lane >= d) hi = max(hi, o);
+  }
+  int lo = __shfl_up(hi, 1, 64);
+  if (lane == 0) lo = 0;
+  const int cnt = in ? chunks(lo, hi) : 0;
+  const int pd = in ? pad(lo, hi) : 0;
+  int incl = cnt, pincl = pd;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64), po = __shfl_up(pincl, d, 64);
+    if (lane >= d) {
+      incl += o;
+      pincl += po;
+    }
+  }
+  const int excl = incl - cnt;
+  const unsigned long long hit = __ballot(in && u >= excl && u < incl);
+  if (hit != 0ull) {
+    const int src = __ffsll(hit) - 1;
+    return Unit{src, u - __shfl(excl, src, 64), __shfl(lo, src, 64), __shfl(hi, src, 64),
+                __shfl(pincl - pd, src, 64)};
+  }
+  return Unit{-1, u - __shfl(incl, 63, 64), 0, 0, __shfl(pincl, 63, 64)};
+}
+
+// The group lookup of the quantizers: one wave each for at most 64 groups,
+// else the workgroup scan (a workgroup-uniform choice).
+template <int NT, typename ChunkFn, typename PadFn>
+__device__ __forceinline__ Unit find_unit_quant(const int32_t* __restrict__ offs, int n_groups, int rows, int u,
+                                                ChunkFn chunks, PadFn pad) {
+  if (offs != nullptr && n_groups <= 64) return find_unit_wave(offs, n_groups, rows, u, chunks, pad);
+  return find_unit<NT>(offs, n_groups, rows, u, chunks, pad);
+}
+
 }  // namespace fp8moe

@@ -74,7 +74,7 @@ __device__ __forceinline__ CwGeom cw_geom(int u, int64_t batch, int rows, int co
                                           int64_t ld_q, float* scale) {
   CwGeom g;
   if constexpr (GROUPED) {
-    const Unit un = find_unit<kCwThreads>(offs, n_groups, rows, u, CwChunks<CR>{}, NoPad{});
+    const Unit un = find_unit_quant<kCwThreads>(offs, n_groups, rows, u, CwChunks<CR>{}, NoPad{});
     g.ok = un.e >= 0;
     g.e = un.e; g.j = un.j; g.olo = un.lo; g.ohi = un.hi;
     g.in_base = 0;

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict
   int s_nb;                // blocks per scale row
   if constexpr (GROUPED) {
     if (blockIdx.x == 0 && offs_pad_out != nullptr) mx_write_offs_pad(offs, n_groups, rows, offs_pad_out);
-    const Unit un = find_unit<256>(offs, n_groups, rows, u, MxChunks{}, MxPad{});
+    const Unit un = find_unit_quant<256>(offs, n_groups, rows, u, MxChunks{}, MxPad{});
     if (un.e >= 0) {
       lo = un.lo; hi = un.hi; plo = un.pbase; phi = plo + ((hi - lo + 31) & ~31); j = un.j;
     } else {
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(DualSrc sr, int64_t batch,
   int64_t lrow0 = 0;       // last-dim output row of input row 0
   if constexpr (GROUPED) {
     if (blockIdx.x == 0 && offs_pad_out != nullptr) mx_write_offs_pad(offs, n_groups, rows, offs_pad_out);
-    const Unit un = find_unit<256>(offs, n_groups, rows, u, MxDualChunks{}, MxPad{});
+    const Unit un = find_unit_quant<256>(offs, n_groups, rows, u, MxDualChunks{}, MxPad{});
     if (un.e >= 0) {
       lo = un.lo; hi = un.hi; plo = un.pbase; phi = plo + ((hi - lo + 31) & ~31); j = un.j;
     } else {
