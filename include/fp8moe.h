@@ -453,8 +453,9 @@ int moe_combine_backward(const void *dy_bf16, const void *yg_bf16, int64_t rows,
  *   Requires: batch >= 1 (== 1 with offs), n_groups >= 1 with offs, rows, cols >= 0,
  *   ld_q >= rows, cols % 8 == 0, ld_q % 16 == 0, x and q_t 16-byte aligned.
  *   Normally the call enqueues one kernel: every 64-column chunk of 512 rows
- *   (128 rows when the groups or batch items average at most 512 rows, so a
- *   short group does not occupy a mostly empty chunk) is read once into
+ *   (256 rows when the groups or batch items average at most 512 rows, 128
+ *   when at most 128, so a short group does not occupy a mostly empty chunk)
+ *   is read once into
  *   registers, and the chunks of a group exchange their column
  *   maxima through a fixed library-owned device array (32768 chunk slots, no
  *   allocation) before casting from registers.  Values in that array carry a
