@@ -81,6 +81,22 @@ def test_rowwise_strided_rows(codec):
     assert_f32_bits_equal(host(s), sr, "scales")
 
 
+def _lookup_edge_offsets():
+    """Offsets at the boundary of the quantizers' group lookup: one wave handles at most 64 groups, a
+    workgroup scan more.  64 and 65 ragged groups with empty ones, and 64 malformed offsets (a decrease,
+    one past the rows, one negative)."""
+    g64 = synth.offsets_from_counts(synth.random_counts(11, 1900, 64, 0.25))
+    g65 = synth.offsets_from_counts(synth.random_counts(12, 1900, 65, 0.25))
+    bad = g64.copy()
+    bad[10] = bad[9] - 5
+    bad[30] = 2100
+    bad[40] = -1
+    return {"groups64": (2000, 136, g64), "groups65": (2000, 136, g65), "groups64_malformed": (2000, 136, bad)}
+
+
+LOOKUP_EDGE_CASES = _lookup_edge_offsets()
+
+
 # ------------------------------------------------------------------- colwise
 
 GROUP_CASES = {
@@ -93,6 +109,7 @@ GROUP_CASES = {
     "very_tall": (70000, 64, np.array([70000], np.int32)),
     # more chunk slots than the single pass holds (2000 mostly empty groups): the two-pass kernels
     "many_groups": (1024, 1024, synth.offsets_from_counts(synth.random_counts(6, 1024, 2000, 0.5))),
+    **LOOKUP_EDGE_CASES,
 }
 
 
@@ -217,6 +234,7 @@ MX_GROUP_CASES = {
     "cfg1": (512, 256, synth.offsets_from_counts(synth.routing_counts(1))),
     "malformed": (300, 64, np.array([40, 20, 300, 500], np.int32)),
     "one_row": (1, 8, np.array([1], np.int32)),
+    **LOOKUP_EDGE_CASES,
 }
 
 
@@ -377,6 +395,7 @@ MX_DUAL_GROUP_CASES = {
     "malformed": (300, 64, np.array([40, 20, 300, 500], np.int32)),
     "one_row": (1, 32, np.array([1], np.int32)),
     "wide": (700, 5120, synth.offsets_from_counts(synth.random_counts(9, 700, 16))),
+    **{k: (M, 160, o) for k, (M, C, o) in LOOKUP_EDGE_CASES.items()},
 }
 
 
