@@ -274,7 +274,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rt_f32x2{acc[2 * k], acc[2 * k + 1]}, rt_bf16x2));
-    out[c] = u32x4{o[0], o[1], o[2], o[3]};
+    // streamed (non-temporal): the layer's output is not read again by the layer's own launches, and its
+    // dirty lines otherwise drain during the next launch (Llama4-Scout: the router weights' gradient that
+    // follows took 80 us instead of 54 us alone)
+    typedef unsigned int nt_v4u __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(nt_v4u{o[0], o[1], o[2], o[3]}, reinterpret_cast<nt_v4u*>(out + c));
   }
 }
 
