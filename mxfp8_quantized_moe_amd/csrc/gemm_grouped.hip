@@ -944,11 +944,14 @@ void gemm_fp8_pipe(KParams p) {
   for (int it = 0;; ++it) {
   // A GROUPED_M tile with at most BM / 2 valid rows (a group's last, short
   // tile) runs HALF: the four waves share its first BM / 2 rows and each takes
-  // a quarter of the columns, so no MFMA is spent on its padding rows.
-  auto tile_body = [&](auto half_tag) -> bool {
-  constexpr bool HALF = decltype(half_tag)::value;
+  // a quarter of the columns, so no MFMA is spent on its padding rows; with at
+  // most BM / 4 valid rows (256-row tiles) the waves share the first BM / 4.
+  auto tile_body = [&](auto lay_tag) -> bool {
+  constexpr int LAY = decltype(lay_tag)::value;
+  constexpr bool HALF = LAY > 0;
+  constexpr int TME = LAY == 2 ? TM / 2 : TM;                          // 32-row blocks per wave
   constexpr int TNE = HALF ? TN / 2 : TN, WNE = HALF ? WN / 2 : WN;   // column blocks and columns per wave
-  constexpr int NME = TM * TNE, NDE = 2 * (TM + TNE), ND0E = NDE + (E8 ? TM + TNE : 0);
+  constexpr int NME = TME * TNE, NDE = 2 * (TME + TNE), ND0E = NDE + (E8 ? TME + TNE : 0);
   // Thread indices pass through an opaque copy each tile, so the compiler
   // derives per-lane addresses inside the tile instead of hoisting (and
   // spilling) all of them across the tile loop.
@@ -975,9 +978,9 @@ void gemm_fp8_pipe(KParams p) {
     raw_barrier();
   };
 
-  v16f acc[TM][TNE];
+  v16f acc[TME][TNE];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TME; ++i)
 #pragma unroll
     for (int j = 0; j < TNE; ++j)
 #pragma unroll
@@ -985,7 +988,7 @@ void gemm_fp8_pipe(KParams p) {
 
   const int g = lane >> 5, lrow = lane & 31;
   // Two register sets of MFMA fragments (one 64-byte k step each).
-  v8i fa[2][TM], fb[2][TNE];
+  v8i fa[2][TME], fb[2][TNE];
   // e8m0 scale operands: byte i of ea[set] is fragment i's scale (the MFMA
   // picks it with op_sel), likewise eb.  In LDS a tile row's four scale bytes
   // of a stage are one word, byte 2 h + b for 32-block b of k step h, and the
@@ -993,7 +996,7 @@ void gemm_fp8_pipe(KParams p) {
   // word of each fragment row once (ahead of that step's fragment reads) and
   // packs the bytes of both k steps with byte permutes; the second k step's
   // operands wait in ea_n / eb_n.
-  static_assert((TM == 4 || TM == 2) && (TNE == 4 || TNE == 2), "at most four scale bytes per register");
+  static_assert((TME == 4 || TME == 2) && (TNE == 4 || TNE == 2), "at most four scale bytes per register");
   int ea[2], eb[2], ea_n = 0, eb_n = 0;
   // byte selectors: t = [w0.b(g), w1.b(g), w0.b(2+g), w1.b(2+g)] from words w0 (low), w1
   const uint32_t sel_pair = 0x06020400u + 0x01010101u * (uint32_t)g;
@@ -1016,7 +1019,7 @@ void gemm_fp8_pipe(KParams p) {
     if constexpr (E8) {
       if (h == 0) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TME; ++i)
           wa[i] = *reinterpret_cast<const uint32_t*>(sc + 4 * (wm * WM + 32 * i + lrow));
 #pragma unroll
         for (int j = 0; j < TNE; ++j)
@@ -1024,7 +1027,7 @@ void gemm_fp8_pipe(KParams p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TME; ++i) {
       const int r = wm * WM + 32 * i + lrow;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + g));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(st + R::off(r, 4 * h + 2 + g));
@@ -1039,7 +1042,7 @@ void gemm_fp8_pipe(KParams p) {
     }
     if constexpr (E8) {
       if (h == 0) {
-        if constexpr (TM == 4) pack4(wa, ea[SET], ea_n);
+        if constexpr (TME == 4) pack4(wa, ea[SET], ea_n);
         else pack2(wa, ea[SET], ea_n);
         if constexpr (TNE == 4) pack4(wb, eb[SET], eb_n);
         else pack2(wb, eb[SET], eb_n);
@@ -1051,7 +1054,7 @@ void gemm_fp8_pipe(KParams p) {
   };
   auto mma = [&](auto set_tag) {
     constexpr int SET = decltype(set_tag)::value;
-    static_for<TM>([&](auto ic) {
+    static_for<TME>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       static_for<TNE>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
@@ -1203,7 +1206,7 @@ void gemm_fp8_pipe(KParams p) {
     const uint32_t stg_l = lds_off(stg), sinv_l = lds_off(sinv);
     const bool full = p_valid == BM && q_valid == BN;
     const int rr = lane >> 3, k = lane & 7;     // read-back: staged row 8 itr + rr, chunk k
-    constexpr int NP = TM * (TNE / JPP);         // passes
+    constexpr int NP = TME * (TNE / JPP);         // passes
     // GROUPED_M with bf16 output: the read-back pieces of every pass are held
     // (128 registers, where the dead MFMA fragments were) and stored together
     // once the next tile's stages have landed.  Otherwise (measured slower for
@@ -1213,12 +1216,12 @@ void gemm_fp8_pipe(KParams p) {
     constexpr bool HOLD = MODE == 0 && NP <= 8;
     constexpr int ND_ = HOLD ? NP : 2;
     lds_u4 dv[ND_][4];
-    // Stores of pass n (32-row block n % TM, columns PC (n / TM) ..), once
+    // Stores of pass n (32-row block n % TME, columns PC (n / TME) ..), once
     // its read-back has landed.  All pre-issued stages of the next tile (this
     // wave's part) land before the first store: until then only loads are in
     // flight, and they complete in order.
     auto store_pass = [&](auto nc) {
-      constexpr int n = decltype(nc)::value, i = n % TM, jp = n / TM;
+      constexpr int n = decltype(nc)::value, i = n % TME, jp = n / TME;
       constexpr int d = HOLD ? n : (n & 1);
 #pragma unroll
       for (int itr = 0; itr < 4; ++itr) lds_ready(dv[d][itr]);
@@ -1258,17 +1261,17 @@ void gemm_fp8_pipe(KParams p) {
       // reciprocals of the lane's columns in this pass (register quad q of
       // block jj: columns 32 jj + 8 q + 4 g + e of the pass) and of its rows
       f32x4 inv_q[JPP][4];
-      float inv_p[TM];
+      float inv_p[TME];
       if constexpr (SK == 0) {
         lds_u4 rq[JPP][4];
-        uint32_t rp[TM];
+        uint32_t rp[TME];
 #pragma unroll
         for (int jj = 0; jj < JPP; ++jj)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             rq[jj][q] = lds_read16(sinv_l + 4 * (BM + wn * WNE + 32 * (JPP * jp + jj) + 8 * q + 4 * g));
 #pragma unroll
-        for (int i = 0; i < TM; ++i) rp[i] = lds_read4(sinv_l + 4 * (wm * WM + 32 * i + lrow));
+        for (int i = 0; i < TME; ++i) rp[i] = lds_read4(sinv_l + 4 * (wm * WM + 32 * i + lrow));
         lds_wait();
 #pragma unroll
         for (int jj = 0; jj < JPP; ++jj)
@@ -1278,7 +1281,7 @@ void gemm_fp8_pipe(KParams p) {
             inv_q[jj][q] = __builtin_bit_cast(f32x4, rq[jj][q]) * keep;
           }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TME; ++i) {
           lds_ready(rp[i]);
           inv_p[i] = __builtin_bit_cast(float, rp[i]) * keep;
         }
@@ -1288,10 +1291,10 @@ void gemm_fp8_pipe(KParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) inv_q[jj][q] = f32x4{keep, keep, keep, keep};
 #pragma unroll
-        for (int i = 0; i < TM; ++i) inv_p[i] = 1.0f;
+        for (int i = 0; i < TME; ++i) inv_p[i] = 1.0f;
       }
-      static_for<TM>([&](auto ic) {
-        constexpr int i = decltype(ic)::value, n = TM * jp + i;   // pass n
+      static_for<TME>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, n = TME * jp + i;   // pass n
         // stage: block (i, JPP jp + jj), quad q -> staged row lrow
 #pragma unroll
         for (int jj = 0; jj < JPP; ++jj) {
@@ -1363,7 +1366,7 @@ void gemm_fp8_pipe(KParams p) {
           inv_q[4 * q + e] = (SK == 0 ? sinv[BM + cc] : 1.0f) * keep;
         }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TME; ++i) {
         const int r = wm * WM + 32 * i + lrow;
         const float inv_p = (SK == 0 ? sinv[r] : 1.0f) * keep;
 #pragma unroll
@@ -1387,10 +1390,17 @@ void gemm_fp8_pipe(KParams p) {
   };
   bool has_next;
   if constexpr (MODE == 0) {
-    if (cur.pv <= BM / 2) has_next = tile_body(std::true_type{});
-    else has_next = tile_body(std::false_type{});
+    bool quarter = false;
+    if constexpr (TM == 4) {
+      quarter = cur.pv <= BM / 4;
+      if (quarter) has_next = tile_body(std::integral_constant<int, 2>{});
+    }
+    if (!quarter) {
+      if (cur.pv <= BM / 2) has_next = tile_body(std::integral_constant<int, 1>{});
+      else has_next = tile_body(std::integral_constant<int, 0>{});
+    }
   } else {
-    has_next = tile_body(std::false_type{});
+    has_next = tile_body(std::integral_constant<int, 0>{});
   }
   if (!has_next) break;
   cur = nxt;

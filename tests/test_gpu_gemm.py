@@ -541,9 +541,10 @@ def test_grouped_m_mx_k4(rule, K):
 
 
 # Groups averaging at least 512 rows take 256-row tiles.  These sizes put a group's last tile at every
-# boundary: remainders (mod 256) of 0, 1, 127, 128, 129, 255, groups under one tile, an empty group,
-# one row.
-SPLIT_COUNTS = np.array([256, 257, 383, 385, 511, 512, 513, 640, 767, 900, 0, 1, 100, 1023, 2000], np.int64)
+# boundary: remainders (mod 256) of 0, 1, 64, 65, 127, 128, 129, 255, groups under one tile, an empty
+# group, one row.
+SPLIT_COUNTS = np.array([256, 257, 383, 385, 511, 512, 513, 640, 767, 900, 0, 1, 100, 1023, 2000, 320, 321],
+                        np.int64)
 
 
 @pytest.mark.parametrize("N", [320, 200])           # two column tiles, one
