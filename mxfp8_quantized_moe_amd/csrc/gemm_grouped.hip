@@ -945,7 +945,7 @@ void gemm_fp8_pipe(KParams p) {
   // A GROUPED_M tile with at most BM / 2 valid rows (a group's last, short
   // tile) runs HALF: the four waves share its first BM / 2 rows and each takes
   // a quarter of the columns, so no MFMA is spent on its padding rows; with at
-  // most BM / 4 valid rows (256-row tiles) the waves share the first BM / 4.
+  // most BM / 4 valid rows (256-row MX tiles) the waves share the first BM / 4.
   auto tile_body = [&](auto lay_tag) -> bool {
   constexpr int LAY = decltype(lay_tag)::value;
   constexpr bool HALF = LAY > 0;
@@ -1390,8 +1390,10 @@ void gemm_fp8_pipe(KParams p) {
   };
   bool has_next;
   if constexpr (MODE == 0) {
+    // Quarter layout for MX operands only: the FP8 kernels measured slower
+    // with the third tile body beside the other two.
     bool quarter = false;
-    if constexpr (TM == 4) {
+    if constexpr (TM == 4 && E8) {
       quarter = cur.pv <= BM / 4;
       if (quarter) has_next = tile_body(std::integral_constant<int, 2>{});
     }
